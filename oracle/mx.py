@@ -1,0 +1,111 @@
+"""MXFP8 block quantisation (oracle).
+
+[AREX] closing paragraph of the design section and [AIGWX] "详细发生了什么":
+the layer has a BF16 mode and an MXFP8 mode; in MXFP8 mode the weights are
+quantised ahead of time and the activations are quantised inside dispatch,
+the expert GEMM and SwiGLU.  [ALPHA] section 三: weight quantisation happens
+outside the timed region.
+
+The pages name the format only.  The rule below is the OCP Microscaling (MX)
+v1.0 specification's, for the MXFP8 (E4M3) element type:
+  * blocks of 32 consecutive elements along the GEMM's reduction axis share one
+    scale X = 2**s stored as E8M0 (biased exponent s + 127);
+  * s = floor(log2(amax)) - 8, where 8 is the largest exponent of a normal E4M3
+    value, clamped to [-127, 127]; an all-zero block gets s = -127;
+  * each element is v / X rounded to nearest-even on the E4M3 grid and
+    saturated to +-448 (E4M3 has no infinity; its one NaN code is never made).
+A trailing partial block behaves as if zero-padded (zeros do not change amax).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+MX_BLOCK = 32
+E4M3_MAX = 448.0
+E4M3_EMAX = 8          # exponent of the largest normal E4M3 value (1.75 * 2**8)
+E4M3_EMIN = -6         # exponent of the smallest normal E4M3 value
+E4M3_MBITS = 3
+
+
+def e4m3_round(v):
+    """Round float64 values to the nearest-even E4M3 value, saturating at 448."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, q = np.frexp(a)                      # a = f * 2**q, f in [0.5, 1)
+    e = np.maximum(q - 1, E4M3_EMIN)        # subnormals share the quantum of the min normal
+    quantum = np.ldexp(1.0, e - E4M3_MBITS)
+    r = np.round(a / quantum) * quantum     # np.round rounds halves to even
+    r = np.minimum(r, E4M3_MAX)
+    return np.copysign(r, v)
+
+
+def e4m3_encode(r):
+    """Bit pattern (uint8) of E4M3 values r (which must lie on the grid)."""
+    r = np.asarray(r, dtype=np.float64)
+    sign = np.signbit(r).astype(np.uint8) << 7
+    a = np.abs(r)
+    _, q = np.frexp(a)
+    e = q - 1
+    normal = a >= 2.0 ** E4M3_EMIN
+    exp_field = np.where(normal, e + 7, 0)
+    mant = np.where(normal, (a / np.ldexp(1.0, e) - 1.0) * 8.0, a / 2.0 ** (E4M3_EMIN - E4M3_MBITS))
+    if not np.all(mant == np.round(mant)):
+        raise ValueError("value not on the E4M3 grid")
+    code = (exp_field.astype(np.int64) << 3) | mant.astype(np.int64)
+    return sign | code.astype(np.uint8)
+
+
+def e4m3_decode(code):
+    """float64 values of E4M3 bit patterns (0x7F / 0xFF, the NaN codes, decode to NaN)."""
+    c = np.asarray(code, dtype=np.int64)
+    s = np.where(c & 0x80, -1.0, 1.0)
+    ef = (c >> 3) & 0xF
+    m = c & 0x7
+    val = np.where(ef == 0, m * 2.0 ** (E4M3_EMIN - E4M3_MBITS), (1.0 + m / 8.0) * np.ldexp(1.0, ef - 7))
+    val = np.where((c & 0x7F) == 0x7F, np.nan, val)
+    return s * val
+
+
+def _blocks_last(v):
+    n = v.shape[-1]
+    nb = -(-n // MX_BLOCK)
+    pad = nb * MX_BLOCK - n
+    if pad:
+        v = np.concatenate([v, np.zeros(v.shape[:-1] + (pad,), v.dtype)], axis=-1)
+    return v.reshape(v.shape[:-1] + (nb, MX_BLOCK)), n
+
+
+def mx_quantize(v, axis: int = -1):
+    """Quantise v along `axis` in blocks of 32.
+
+    Returns (codes uint8, same shape as v; scales uint8 E8M0, with the axis
+    length replaced by the number of blocks).
+    """
+    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
+    b, n = _blocks_last(v)
+    amax = np.max(np.abs(b), axis=-1)
+    _, q = np.frexp(amax)
+    s = np.where(amax > 0, (q - 1) - E4M3_EMAX, -127)
+    s = np.clip(s, -127, 127)
+    X = np.ldexp(1.0, s)[..., None]
+    r = e4m3_round(b / X)
+    codes = e4m3_encode(r).reshape(b.shape[:-2] + (-1,))[..., :n]
+    scales = (s + 127).astype(np.uint8)
+    return np.moveaxis(codes, -1, axis), np.moveaxis(scales, -1, axis)
+
+
+def mx_dequantize(codes, scales, axis: int = -1):
+    """float64 values of an MX tensor (inverse of the layout of mx_quantize)."""
+    c = np.moveaxis(np.asarray(codes), axis, -1)
+    sc = np.moveaxis(np.asarray(scales), axis, -1).astype(np.int64)
+    n = c.shape[-1]
+    val = e4m3_decode(c)
+    X = np.ldexp(1.0, sc - 127)
+    Xe = np.repeat(X, MX_BLOCK, axis=-1)[..., :n]
+    return np.moveaxis(val * Xe, -1, axis)
+
+
+def mx_roundtrip(v, axis: int = -1):
+    """Quantise then dequantise v along `axis` (float64 result)."""
+    c, s = mx_quantize(v, axis)
+    return mx_dequantize(c, s, axis)
