@@ -1,0 +1,230 @@
+#!/usr/bin/env python3
+"""Throughput of one MoE layer step (schedule + forward + backward) on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole layer over one batch of synthetic input:
+top-k routing and the schedule, dispatch, the expert-grouped SwiGLU FFN and
+the weighted combine, then the backward (reverse-combine, SwiGLU backward with
+the router-weight gradient, expert dgrad/wgrad, reverse-dispatch, softmax
+backward).  Inputs are resident in HBM before timing starts.
+
+FLOPs per step follow the usual MoE convention: 6*H*I per routed token-slot
+forward and 12*H*I backward (routing, softmax and elementwise work excluded).
+
+Prints one JSON line.  It carries the layer throughput, a roofline entry for
+the kernel with the largest share of the step (its algorithmic bytes per
+launch over its average duration, timed with HIP events on the launch stream),
+and the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+WORKLOADS = ("e512_t2048",)
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="e512_t2048", choices=WORKLOADS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=8,
+                    help="tokens in the CPU oracle's sample (forward + input gradients)")
+    ap.add_argument("--cpu-experts", type=int, default=2,
+                    help="experts in the CPU oracle's sample (weight gradients)")
+    return ap.parse_args()
+
+
+def kernel_bytes(shape, counts: np.ndarray) -> dict:
+    """Algorithmic HBM bytes per launch of each kernel (unique data it must move)."""
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    S = T * k
+    used = int(np.count_nonzero(counts))
+    P = I // 128
+    w_gu = used * 2 * I * H * 2
+    w_d = used * H * I * 2
+    return {
+        "topk_route": T * E * 4 + S * 8,
+        "dispatch": T * H * 2 + S * H * 2,
+        "gemm_gate_up": w_gu + S * H * 2 + 3 * S * I * 2,
+        "gemm_down": w_d + S * I * 2 + S * H * 2,
+        "combine": S * H * 2 + T * H * 2 + S * 8,
+        "gemm_down_dgrad": w_d + T * H * 2 + 2 * S * I * 2 + 3 * S * I * 2 + S * P * 4,
+        "gemm_gu_dgrad": w_gu + S * 2 * I * 2 + S * H * 2,
+        "wgrad_down": E * H * I * 2 + T * H * 2 + S * I * 2,
+        "wgrad_gate_up": E * 2 * I * H * 2 + T * H * 2 + S * 2 * I * 2,
+        "rd_reduce": S * H * 2 + T * H * 2,
+        "softmax_bwd": S * P * 4 + T * E * 4 + S * 12,
+    }
+
+
+def cpu_baseline(case, idx, w, n_tokens: int, n_experts: int):
+    """Time the oracle on a bounded sample of the same workload."""
+    import oracle
+    from threadpoolctl import threadpool_info
+
+    shape = case.shape
+    H, I, k = shape.H, shape.I, shape.k
+    rng = np.random.default_rng(0)
+    tokens = np.sort(rng.choice(shape.T, size=n_tokens, replace=False))
+    counts = np.bincount(idx.reshape(-1), minlength=shape.E)
+    experts = [int(e) for e in rng.choice(np.nonzero(counts)[0], size=n_experts, replace=False)]
+    need = sorted(set(idx[tokens].reshape(-1).tolist()) | set(experts))
+    # host copies of the weights the sample touches (fetched before timing)
+    wg = {e: case.wg[e].float().cpu().numpy() for e in need}
+    wu = {e: case.wu[e].float().cpu().numpy() for e in need}
+    wd = {e: case.wd[e].float().cpu().numpy() for e in need}
+    x = case.x.float().cpu().numpy()
+    dy = case.dy.float().cpu().numpy()
+    t0 = time.perf_counter()
+    oracle.forward(x, wg, wu, wd, idx, w, tokens=tokens)
+    oracle.backward(x, wg, wu, wd, idx, w, dy, tokens=tokens, experts=experts)
+    dt = time.perf_counter() - t0
+    rows = int(sum(counts[e] for e in experts))
+    flops = 12.0 * H * I * k * n_tokens + 6.0 * H * I * rows
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {
+        "value": flops / dt / 1e12,
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"float64 NumPy oracle: forward + input-gradient backward of {n_tokens} tokens "
+                   f"({n_tokens * k} slots) and the weight gradients of {n_experts} experts "
+                   f"({rows} rows) of the {shape.name} workload; {dt:.1f} s"),
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the layer is "
+              "built for a single MI355X and has no multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    import synth_inputs as si
+    from mixture_experts_layer_dispatch_amd import binding as B
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if not B.device_supported():
+        print("the library requires gfx950 (MI355X)", file=sys.stderr)
+        sys.exit(1)
+
+    shape = si.SHAPES[args.workload]
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    cfg = B.Config(T=T, H=H, I=I, E=E, k=k, n_shared=shape.n_shared,
+                   macrobatch=shape.macrobatch, minibatch=shape.minibatch)
+
+    class Case:
+        pass
+
+    case = Case()
+    case.shape = shape
+    case.logits = si.logits(shape, "cuda")
+    case.x = si.tokens(shape, "cuda")
+    case.dy = si.grad_out(shape, "cuda")
+    case.wg, case.wu, case.wd = si.all_expert_weights(shape, "cuda")
+    weights = {"w_gate": case.wg, "w_up": case.wu, "w_down": case.wd}
+    ws = B.alloc_workspace(cfg)
+    sched = B.alloc_schedule(cfg)
+    saved = B.alloc_saved(cfg)
+    grads = B.alloc_grads(cfg)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty_like(y)
+    dw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    dlog = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        B.moe_schedule(cfg, case.logits, sched, ws, stream)
+        B.moe_forward(cfg, sched, case.x, weights, y, saved, ws, stream)
+        B.moe_backward(cfg, sched, saved, case.x, weights, case.dy, dx, grads, dw, dlog, ws, stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    print(f"[bench] {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    assert B.moe_check_device_error(ws, stream) == 0
+
+    S = T * k
+    flops = 18.0 * H * I * S + (18.0 * H * I * T if shape.n_shared else 0.0)
+    value = flops / (ms * 1e-3) / 1e12
+
+    # per-kernel durations: HIP events around each launch, on the launch stream
+    B.profile_reset()
+    B.profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    B.profile_collect()
+    B.profile_enable(False)
+    stats = B.profile_stats()
+    counts = sched["counts"].cpu().numpy().sum(0)
+    kb = kernel_bytes(shape, counts)
+    kernels = {}
+    for name, (n, tot) in stats.items():
+        avg = tot / max(n, 1)
+        entry = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4)}
+        if name in kb:
+            entry["GB/s"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
+        kernels[name] = entry
+    dom = max(stats, key=lambda n: stats[n][1])
+    dom_avg = stats[dom][1] / stats[dom][0]
+    achieved = kb[dom] / (dom_avg * 1e-3) / 1e9
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": None, "avg_ms": round(dom_avg, 4), "bytes_per_launch": kb[dom]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        idx = sched["topk_idx"].cpu().numpy()
+        wts = sched["topk_w"].cpu().numpy().astype(np.float64)
+        import oracle  # noqa: F401  (test infrastructure: the CPU baseline only)
+        cpu = cpu_baseline(case, idx, wts, args.cpu_tokens, args.cpu_experts)
+
+    out = {
+        "metric": "MoE layer TFLOP/s fwd+bwd (bf16, MXFP8) at 512E H4096 I1024 top-10",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{shape.name}: T={T} H={H} I={I} E={E} top-{k}, bf16, "
+                               "schedule+forward+backward",
+                   "T": T, "H": H, "I": I, "E": E, "k": k, "parallelism": "none (1 GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

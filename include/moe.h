@@ -1,0 +1,218 @@
+/*
+ * moe.h — C ABI of a single-GPU Mixture-of-Experts layer for AMD Instinct
+ * MI355X (gfx950): top-k routing, the dispatch schedule, dispatch, the
+ * expert-grouped SwiGLU FFN, the router-weighted combine, and the backward.
+ *
+ * Sources (the pages that describe the method; cited by title and section):
+ *   [AREX]  arex-research.com, "Cursor 放出 MoK：NVL72 训练提速 2.37 倍",
+ *           section "pull 代替 push，ring buffer 踢掉 CPU：三个决定性的设计选择"
+ *           (first decision: one schedule table serves dispatch, combine,
+ *           reverse-combine and reverse-dispatch; second: a fixed-size ring
+ *           buffer of tokens, the macrobatch, recycled per minibatch, so no
+ *           token is dropped and no count goes back to the CPU; third: the
+ *           minibatch size is a tunable; closing paragraph: BF16 and MXFP8
+ *           modes, and the router-weight gradient fused into the SwiGLU
+ *           backward).
+ *   [AIGWX] aigwx.org, "Cursor 开源 MoK：面向 GB300 NVL72 的确定性 MoE 训练内核",
+ *           section "详细发生了什么".
+ *   [ALPHA] alphalab.site, "Mixture-of-Kittens" review: section 一 (what the
+ *           layer fuses), section 二 (router projection outside the layer;
+ *           the final router-weighted reduction; run-to-run bitwise
+ *           determinism from a fixed accumulation order), section 三 (what
+ *           the benchmark times; MXFP8 weights quantised outside timing),
+ *           section 四 (synthetic Gaussian logits with top-k; tunables).
+ *
+ * Conventions
+ *   - Token t has k slots s = t*k + j, j = 0..k-1, in the order the router
+ *     picked them (descending logit, ties to the lower expert index).
+ *   - Tokens are processed in macrobatches of `macrobatch` tokens.  The rows
+ *     of macrobatch m are the global rows [m*M*k, (m+1)*M*k); inside a
+ *     macrobatch they are grouped by expert (expert 0 first) and, within an
+ *     expert, ordered by ascending slot id.
+ *   - bf16 tensors are passed as pointers to 16-bit bf16 bit patterns.
+ *     Weights use the [out, in] row-major convention: W_gate, W_up [E, I, H],
+ *     W_down [E, H, I]; activations are row-major [tokens, H].
+ *   - Every device pointer must be 16-byte aligned.  The caller owns every
+ *     buffer; the library never allocates, frees, copies to the host or
+ *     synchronises, and keeps no state between calls (reentrant).
+ *   - Every call validates its arguments on the host first and returns a
+ *     nonzero moe_status before anything is enqueued if they are wrong.
+ *     Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously.
+ *   - Results are bit-identical across runs for the same inputs and config:
+ *     no floating-point atomics; every sum has a fixed order.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define MOE_API __attribute__((visibility("default")))
+#else
+#define MOE_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,        /* bad shape, null or misaligned pointer, bad enum */
+    MOE_ERR_UNSUPPORTED_DEVICE = 2, /* current device is not gfx950 (or no device)     */
+    MOE_ERR_CAPACITY = 3,           /* ring capacity below one macrobatch's rows        */
+    MOE_ERR_WORKSPACE = 4,          /* workspace null or smaller than required          */
+    MOE_ERR_HIP = 5,                /* a HIP launch or query failed                     */
+    MOE_ERR_UNSUPPORTED = 6         /* a valid request this build does not implement    */
+} moe_status;
+
+typedef enum moe_precision {
+    MOE_PREC_BF16 = 0,   /* bf16 operands, fp32 accumulation                             */
+    MOE_PREC_MXFP8 = 1   /* E4M3 operands with E8M0 scales per 32 elements along K       */
+} moe_precision;
+
+/* Layer shape and the tunables of [AREX] (third decision) / [ALPHA] 四, minus
+ * the communication ones (there is no cross-GPU traffic on one GPU). */
+typedef struct moe_config {
+    int32_t T;             /* tokens                                                  */
+    int32_t H;             /* hidden size, multiple of 128                            */
+    int32_t I;             /* expert intermediate size, multiple of 128               */
+    int32_t E;             /* routed experts, 1..1024                                 */
+    int32_t k;             /* experts per token, 1..min(E, 32)                        */
+    int32_t n_shared;      /* always-on shared experts: 0 or 1                        */
+    int32_t macrobatch;    /* tokens per macrobatch (ring refill unit); 0 = T         */
+    int32_t minibatch;     /* tokens per minibatch (fill granularity); 0 = macrobatch */
+    int64_t capacity_rows; /* ring-buffer rows; 0 = the minimum (see moe_ring_rows)   */
+    int32_t precision;     /* moe_precision                                           */
+    int32_t reserved;      /* must be 0                                               */
+} moe_config;
+
+/* The schedule table ([AREX] first decision): written by moe_schedule, read by
+ * moe_forward and moe_backward.  n_macro = T / macrobatch,
+ * n_mini = macrobatch / minibatch, S = T * k. */
+typedef struct moe_sched {
+    int32_t* topk_idx;     /* [T, k]  chosen experts                                  */
+    float*   topk_w;       /* [T, k]  softmax of the chosen logits (fp32)             */
+    int32_t* counts;       /* [n_macro, E]  rows per expert                           */
+    int32_t* offsets;      /* [n_macro, E+1] exclusive scan of counts (local rows)    */
+    int32_t* mini_counts;  /* [n_macro, E, n_mini] rows per expert per minibatch      */
+    int32_t* row_of_slot;  /* [S]  global row of slot s                               */
+    int32_t* slot_of_row;  /* [S]  inverse permutation                                */
+} moe_sched;
+
+/* bf16 weights.  The shared expert's pointers are read only if n_shared. */
+typedef struct moe_weights {
+    const void* w_gate;    /* [E, I, H] */
+    const void* w_up;      /* [E, I, H] */
+    const void* w_down;    /* [E, H, I] */
+    const void* s_gate;    /* [I, H]    */
+    const void* s_up;      /* [I, H]    */
+    const void* s_down;    /* [H, I]    */
+} moe_weights;
+
+/* What the forward keeps for the backward (bf16, rows in schedule row order). */
+typedef struct moe_saved {
+    void* g;               /* [S, I]  gate pre-activations                            */
+    void* u;               /* [S, I]  up projections                                  */
+    void* sg;              /* [T, I]  shared expert gate (if n_shared)                */
+    void* su;              /* [T, I]  shared expert up   (if n_shared)                */
+} moe_saved;
+
+/* Parameter gradients (bf16, same layouts as the weights; overwritten). */
+typedef struct moe_grads {
+    void* d_w_gate;        /* [E, I, H] */
+    void* d_w_up;          /* [E, I, H] */
+    void* d_w_down;        /* [E, H, I] */
+    void* d_s_gate;        /* [I, H]    (if n_shared) */
+    void* d_s_up;          /* [I, H]    (if n_shared) */
+    void* d_s_down;        /* [H, I]    (if n_shared) */
+} moe_grads;
+
+/* Human-readable name of a status code (static string, never NULL). */
+MOE_API const char* moe_status_string(moe_status s);
+
+/* Host-only: checks a config ([ALPHA] 四 tunables; T divisible by macrobatch,
+ * macrobatch by minibatch; capacity).  Touches no device. */
+MOE_API moe_status moe_validate_config(const moe_config* cfg);
+
+/* Host-only: rows of the ring buffer that carries dispatched rows of one
+ * macrobatch while the next is being filled ([AREX] second decision):
+ * capacity_rows if set, else macrobatch*k when there is one macrobatch and
+ * 2*macrobatch*k otherwise. */
+MOE_API moe_status moe_ring_rows(const moe_config* cfg, int64_t* rows);
+
+/* Host-only: bytes of device workspace that moe_schedule, moe_forward and
+ * moe_backward need (one workspace serves all three; it holds the ring
+ * buffer and per-call scratch, nothing that must survive between calls). */
+MOE_API moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Host-only: 1 if the current HIP device is gfx950, else 0 (also 0 when no
+ * device is visible).  The library refuses other devices, as the reference
+ * layer refuses GPUs other than the one it was written for ([ALPHA] 四). */
+MOE_API int moe_device_supported(void);
+
+/* Routing and schedule ([ALPHA] 一 and 四: top-k over the router logits;
+ * [AREX] first decision: one schedule table for all four data movements).
+ *   logits [T, E] fp32 (finite), device.  Writes every array of *sched.
+ * The router projection that produces the logits is outside the layer, as in
+ * [ALPHA] 二. */
+MOE_API moe_status moe_schedule(const moe_config* cfg, const float* logits, const moe_sched* sched,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Forward ([ALPHA] 一: dispatch, expert SwiGLU FFN, combine; 二: the
+ * router-weighted reduction in a fixed order).
+ *   x [T, H] bf16; y [T, H] bf16 (written);
+ *   y_t = FFN_shared(x_t) + sum_{j=0..k-1} w[t,j] * o_(t,j), accumulated in
+ *   fp32 in that order and rounded to bf16 once.
+ *   saved: g, u written for the backward.
+ * Macrobatches are processed in order through the ring buffer; every
+ * dynamic size stays on the device ([AREX] second decision). */
+MOE_API moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void* x,
+                       const moe_weights* w, void* y, const moe_saved* saved,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Backward ([AREX] first decision: reverse-combine and reverse-dispatch reuse
+ * the schedule; closing paragraph: the router-weight gradient is fused into
+ * the SwiGLU backward; [ALPHA] 一: expert gradients).  Macrobatches are walked
+ * in reverse order ([AREX] second decision).
+ *   dy [T, H] bf16; dx [T, H] bf16 (written);
+ *   grads: every weight gradient (overwritten, not accumulated);
+ *   dw [T, k] fp32: gradient of the combine weights (written);
+ *   d_logits [T, E] fp32: gradient of the logits through the top-k softmax,
+ *   zero for experts a token did not choose (written; may be NULL). */
+MOE_API moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe_saved* saved,
+                        const void* x, const moe_weights* w, const void* dy, void* dx,
+                        const moe_grads* grads, float* dw, float* d_logits,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Reads and clears the sticky device error word that kernels set when a
+ * caller-built schedule holds an out-of-range expert, slot or row (those
+ * entries are skipped, never dereferenced).  Synchronises `stream`; meant for
+ * tests.  *flags = 0 when nothing was found. */
+MOE_API moe_status moe_check_device_error(void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t* flags);
+
+/* ------------------------------------------------------------------------
+ * Kernel timing (diagnostics; not part of the layer).  While enabled, every
+ * kernel launch made by the calls above is bracketed by two HIP events
+ * recorded on the launch stream.  moe_profile_collect waits for the pending
+ * events and adds each kernel's elapsed time to a per-name total;
+ * moe_profile_query reads it.  Process-wide state guarded by a mutex; off by
+ * default, and free of cost while off.  Names are the kernels' short names
+ * (e.g. "gemm_gate_up").
+ * ------------------------------------------------------------------------ */
+MOE_API moe_status moe_profile_enable(int on);
+MOE_API moe_status moe_profile_collect(void);
+MOE_API moe_status moe_profile_query(const char* name, int64_t* launches, double* total_ms);
+/* Writes up to `cap` bytes of a newline-separated list of the kernel names
+ * seen so far into buf (NUL-terminated). */
+MOE_API moe_status moe_profile_names(char* buf, size_t cap);
+MOE_API moe_status moe_profile_reset(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,297 @@
+"""ctypes binding of the MoE layer's C ABI (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the HIP library
+``libmoe_mi355x.so``.  PyTorch supplies device memory (``tensor.data_ptr()``)
+and the stream (``torch.cuda.current_stream().cuda_stream``).  If the library
+is missing, every entry point raises: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED_DEVICE = 2
+MOE_ERR_CAPACITY = 3
+MOE_ERR_WORKSPACE = 4
+MOE_ERR_HIP = 5
+MOE_ERR_UNSUPPORTED = 6
+
+PREC_BF16 = 0
+PREC_MXFP8 = 1
+
+EXPORTED = [
+    "moe_status_string", "moe_validate_config", "moe_ring_rows", "moe_workspace_size",
+    "moe_device_supported", "moe_schedule", "moe_forward", "moe_backward",
+    "moe_check_device_error", "moe_profile_enable", "moe_profile_collect", "moe_profile_query",
+    "moe_profile_names", "moe_profile_reset",
+]
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class moe_config(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
+                ("macrobatch", ctypes.c_int32), ("minibatch", ctypes.c_int32),
+                ("capacity_rows", ctypes.c_int64), ("precision", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+class moe_sched(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("topk_idx", "topk_w", "counts", "offsets", "mini_counts", "row_of_slot",
+                 "slot_of_row")]
+
+
+class moe_weights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")]
+
+
+class moe_saved(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("g", "u", "sg", "su")]
+
+
+class moe_grads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("d_w_gate", "d_w_up", "d_w_down", "d_s_gate", "d_s_up", "d_s_down")]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: run `python -m "
+                               "mixture_experts_layer_dispatch_amd.build` first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, cfgp = ctypes.c_void_p, ctypes.POINTER(moe_config)
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_status_string.argtypes = [ctypes.c_int]
+        L.moe_validate_config.argtypes = [cfgp]
+        L.moe_ring_rows.argtypes = [cfgp, ctypes.POINTER(ctypes.c_int64)]
+        L.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_device_supported.argtypes = []
+        L.moe_schedule.argtypes = [cfgp, vp, ctypes.POINTER(moe_sched), vp, ctypes.c_size_t, vp]
+        L.moe_forward.argtypes = [cfgp, ctypes.POINTER(moe_sched), vp, ctypes.POINTER(moe_weights),
+                                  vp, ctypes.POINTER(moe_saved), vp, ctypes.c_size_t, vp]
+        L.moe_backward.argtypes = [cfgp, ctypes.POINTER(moe_sched), ctypes.POINTER(moe_saved), vp,
+                                   ctypes.POINTER(moe_weights), vp, vp, ctypes.POINTER(moe_grads),
+                                   vp, vp, vp, ctypes.c_size_t, vp]
+        L.moe_check_device_error.argtypes = [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_int32)]
+        L.moe_profile_enable.argtypes = [ctypes.c_int]
+        L.moe_profile_collect.argtypes = []
+        L.moe_profile_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
+                                        ctypes.POINTER(ctypes.c_double)]
+        L.moe_profile_names.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
+        L.moe_profile_reset.argtypes = []
+        for name in EXPORTED:
+            if name != "moe_status_string":
+                getattr(L, name).restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().moe_status_string(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != MOE_OK:
+        raise MoEError(status, where)
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+@dataclass
+class Config:
+    T: int
+    H: int
+    I: int
+    E: int
+    k: int
+    n_shared: int = 0
+    macrobatch: int = 0
+    minibatch: int = 0
+    capacity_rows: int = 0
+    precision: int = PREC_BF16
+
+    def c(self) -> moe_config:
+        return moe_config(self.T, self.H, self.I, self.E, self.k, self.n_shared, self.macrobatch,
+                          self.minibatch, self.capacity_rows, self.precision, 0)
+
+    @property
+    def M(self) -> int:
+        return self.macrobatch or self.T
+
+    @property
+    def mb(self) -> int:
+        return self.minibatch or self.M
+
+    @property
+    def n_macro(self) -> int:
+        return self.T // self.M
+
+    @property
+    def n_mini(self) -> int:
+        return self.M // self.mb
+
+    @property
+    def S(self) -> int:
+        return self.T * self.k
+
+
+def validate_config(cfg: Config) -> int:
+    return lib().moe_validate_config(ctypes.byref(cfg.c()))
+
+
+def ring_rows(cfg: Config) -> int:
+    v = ctypes.c_int64()
+    _check(lib().moe_ring_rows(ctypes.byref(cfg.c()), ctypes.byref(v)), "moe_ring_rows")
+    return v.value
+
+
+def workspace_size(cfg: Config) -> int:
+    v = ctypes.c_size_t()
+    _check(lib().moe_workspace_size(ctypes.byref(cfg.c()), ctypes.byref(v)), "moe_workspace_size")
+    return v.value
+
+
+def device_supported() -> bool:
+    return bool(lib().moe_device_supported())
+
+
+# ------------------------------------------------------------------ buffers
+def alloc_workspace(cfg: Config, device="cuda") -> torch.Tensor:
+    return torch.empty(workspace_size(cfg), dtype=torch.uint8, device=device)
+
+
+def alloc_schedule(cfg: Config, device="cuda") -> dict:
+    i32 = dict(dtype=torch.int32, device=device)
+    return {
+        "topk_idx": torch.empty(cfg.T, cfg.k, **i32),
+        "topk_w": torch.empty(cfg.T, cfg.k, dtype=torch.float32, device=device),
+        "counts": torch.empty(cfg.n_macro, cfg.E, **i32),
+        "offsets": torch.empty(cfg.n_macro, cfg.E + 1, **i32),
+        "mini_counts": torch.empty(cfg.n_macro, cfg.E, cfg.n_mini, **i32),
+        "row_of_slot": torch.empty(cfg.S, **i32),
+        "slot_of_row": torch.empty(cfg.S, **i32),
+    }
+
+
+def alloc_saved(cfg: Config, device="cuda") -> dict:
+    bf = dict(dtype=torch.bfloat16, device=device)
+    out = {"g": torch.empty(cfg.S, cfg.I, **bf), "u": torch.empty(cfg.S, cfg.I, **bf)}
+    if cfg.n_shared:
+        out["sg"] = torch.empty(cfg.T, cfg.I, **bf)
+        out["su"] = torch.empty(cfg.T, cfg.I, **bf)
+    return out
+
+
+def alloc_grads(cfg: Config, device="cuda") -> dict:
+    bf = dict(dtype=torch.bfloat16, device=device)
+    out = {"d_w_gate": torch.empty(cfg.E, cfg.I, cfg.H, **bf),
+           "d_w_up": torch.empty(cfg.E, cfg.I, cfg.H, **bf),
+           "d_w_down": torch.empty(cfg.E, cfg.H, cfg.I, **bf)}
+    if cfg.n_shared:
+        out["d_s_gate"] = torch.empty(cfg.I, cfg.H, **bf)
+        out["d_s_up"] = torch.empty(cfg.I, cfg.H, **bf)
+        out["d_s_down"] = torch.empty(cfg.H, cfg.I, **bf)
+    return out
+
+
+def _sched(s: dict) -> moe_sched:
+    return moe_sched(*[s[n].data_ptr() for n, _ in moe_sched._fields_])
+
+
+def _weights(w: dict) -> moe_weights:
+    return moe_weights(*[(w[n].data_ptr() if w.get(n) is not None else None)
+                         for n, _ in moe_weights._fields_])
+
+
+def _saved(s: dict) -> moe_saved:
+    return moe_saved(*[(s[n].data_ptr() if s.get(n) is not None else None)
+                       for n, _ in moe_saved._fields_])
+
+
+def _grads(g: dict) -> moe_grads:
+    return moe_grads(*[(g[n].data_ptr() if g.get(n) is not None else None)
+                       for n, _ in moe_grads._fields_])
+
+
+# ------------------------------------------------------------------ entry points
+def moe_schedule(cfg: Config, logits: torch.Tensor, sched: dict, ws: torch.Tensor, stream=None):
+    _check(lib().moe_schedule(ctypes.byref(cfg.c()), _p(logits), ctypes.byref(_sched(sched)),
+                              _p(ws), ws.numel(), _stream(stream)), "moe_schedule")
+
+
+def moe_forward(cfg: Config, sched: dict, x: torch.Tensor, weights: dict, y: torch.Tensor,
+                saved: dict, ws: torch.Tensor, stream=None):
+    _check(lib().moe_forward(ctypes.byref(cfg.c()), ctypes.byref(_sched(sched)), _p(x),
+                             ctypes.byref(_weights(weights)), _p(y), ctypes.byref(_saved(saved)),
+                             _p(ws), ws.numel(), _stream(stream)), "moe_forward")
+
+
+def moe_backward(cfg: Config, sched: dict, saved: dict, x: torch.Tensor, weights: dict,
+                 dy: torch.Tensor, dx: torch.Tensor, grads: dict, dw: torch.Tensor,
+                 d_logits, ws: torch.Tensor, stream=None):
+    _check(lib().moe_backward(ctypes.byref(cfg.c()), ctypes.byref(_sched(sched)),
+                              ctypes.byref(_saved(saved)), _p(x), ctypes.byref(_weights(weights)),
+                              _p(dy), _p(dx), ctypes.byref(_grads(grads)), _p(dw), _p(d_logits),
+                              _p(ws), ws.numel(), _stream(stream)), "moe_backward")
+
+
+def moe_check_device_error(ws: torch.Tensor, stream=None) -> int:
+    v = ctypes.c_int32()
+    _check(lib().moe_check_device_error(_p(ws), ws.numel(), _stream(stream), ctypes.byref(v)),
+           "moe_check_device_error")
+    return v.value
+
+
+# ------------------------------------------------------------------ kernel timing
+def profile_enable(on: bool = True):
+    _check(lib().moe_profile_enable(int(on)), "moe_profile_enable")
+
+
+def profile_collect():
+    _check(lib().moe_profile_collect(), "moe_profile_collect")
+
+
+def profile_reset():
+    _check(lib().moe_profile_reset(), "moe_profile_reset")
+
+
+def profile_stats() -> dict:
+    """{kernel name: (launches, total milliseconds)} of the collected events."""
+    buf = ctypes.create_string_buffer(1 << 14)
+    _check(lib().moe_profile_names(buf, len(buf)), "moe_profile_names")
+    out = {}
+    for name in buf.value.decode().split():
+        n, ms = ctypes.c_int64(), ctypes.c_double()
+        _check(lib().moe_profile_query(name.encode(), ctypes.byref(n), ctypes.byref(ms)),
+               "moe_profile_query")
+        out[name] = (n.value, ms.value)
+    return out

@@ -1,0 +1,411 @@
+// C ABI of the MoE layer: argument validation, workspace layout, and the
+// launch sequence of each call.  Host code only (plus two one-thread kernels
+// that read and clear the device error word).
+//
+// The order of work follows the pages: routing, then one schedule table
+// (arex-research.com "Cursor 放出 MoK", design section, first decision);
+// the forward walks macrobatches in order through a ring buffer filled per
+// minibatch, and the backward walks them in reverse (second decision);
+// alphalab.site "Mixture-of-Kittens" section 二: the router-weighted
+// reduction closes the forward.
+#include <atomic>
+#include <cstring>
+
+#include "../../include/moe.h"
+#include "common.h"
+#include "launch.h"
+
+using namespace moe;
+
+namespace {
+
+struct Geom {
+    int T, H, I, E, k, M, mb, n_macro, n_mini, Sm, Smb, S, P;
+    int64_t ring_rows;
+    int halves;
+    bool shared, mx;
+};
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Layout {
+    size_t err, hist, base, tile_off, ring, ring_half, sh, wacc, total;
+    // offsets inside one ring half (bytes)
+    size_t f_xd, f_h, f_o;            // forward
+    size_t b_dgu, b_hw, b_dx, b_part; // backward
+    // offsets inside the shared-expert region
+    size_t s_h, s_o, s_dgu, s_hw, s_dx;
+    size_t wacc_g, wacc_u, wacc_d, wacc_sg, wacc_su, wacc_sd;
+};
+
+moe_status make_geom(const moe_config* c, Geom& g) {
+    if (!c) return MOE_ERR_INVALID_ARG;
+    if (c->T < 1 || c->H < 128 || c->H % 128 || c->I < 128 || c->I % 128) return MOE_ERR_INVALID_ARG;
+    if (c->E < 1 || c->E > kMaxExperts || c->k < 1 || c->k > c->E || c->k > kMaxTopK)
+        return MOE_ERR_INVALID_ARG;
+    if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_INVALID_ARG;
+    if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
+    if (c->reserved != 0 || c->macrobatch < 0 || c->minibatch < 0 || c->capacity_rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (c->H > (1 << 16) || c->I > (1 << 16)) return MOE_ERR_INVALID_ARG;
+    const int64_t S = (int64_t)c->T * c->k;
+    if (S >= (1LL << 30)) return MOE_ERR_INVALID_ARG;
+    g.T = c->T; g.H = c->H; g.I = c->I; g.E = c->E; g.k = c->k;
+    g.M = c->macrobatch ? c->macrobatch : c->T;
+    if (g.M > g.T || g.T % g.M) return MOE_ERR_INVALID_ARG;
+    g.mb = c->minibatch ? c->minibatch : g.M;
+    if (g.mb > g.M || g.M % g.mb) return MOE_ERR_INVALID_ARG;
+    g.n_macro = g.T / g.M;
+    g.n_mini = g.M / g.mb;
+    g.Sm = g.M * g.k;
+    g.Smb = g.mb * g.k;
+    g.S = (int)S;
+    g.P = dgrad_col_tiles(g.I);
+    g.shared = c->n_shared == 1;
+    g.mx = c->precision == MOE_PREC_MXFP8;
+    if (c->capacity_rows) {
+        if (c->capacity_rows < g.Sm) return MOE_ERR_CAPACITY;
+        g.ring_rows = c->capacity_rows;
+    } else {
+        g.ring_rows = g.n_macro > 1 ? 2LL * g.Sm : g.Sm;
+    }
+    g.halves = (int)(g.ring_rows / g.Sm);
+    if (g.halves > g.n_macro) g.halves = g.n_macro;
+    return MOE_OK;
+}
+
+Layout make_layout(const Geom& g) {
+    Layout L{};
+    size_t at = 0;
+    auto take = [&](size_t bytes) {
+        size_t here = at;
+        at = align_up(at + bytes, 256);
+        return here;
+    };
+    L.err = take(256);
+    const size_t hist_ints = schedule_hist_ints(g.T, g.E, g.k, g.M, g.mb);
+    L.hist = take(hist_ints * 4);
+    L.base = take(hist_ints * 4);
+    L.tile_off = take((size_t)g.n_macro * (g.E + 1) * 4);
+    const size_t Sm = (size_t)g.Sm, H = g.H, I = g.I;
+    L.f_xd = 0;
+    L.f_h = align_up(L.f_xd + Sm * H * 2, 256);
+    L.f_o = align_up(L.f_h + Sm * I * 2, 256);
+    const size_t fwd_end = align_up(L.f_o + Sm * H * 2, 256);
+    L.b_dgu = 0;
+    L.b_hw = align_up(L.b_dgu + Sm * 2 * I * 2, 256);
+    L.b_dx = align_up(L.b_hw + Sm * I * 2, 256);
+    L.b_part = align_up(L.b_dx + Sm * H * 2, 256);
+    const size_t bwd_end = align_up(L.b_part + Sm * g.P * 4, 256);
+    L.ring_half = fwd_end > bwd_end ? fwd_end : bwd_end;
+    L.ring = take(L.ring_half * g.halves);
+    const size_t M = (size_t)g.M;
+    if (g.shared) {
+        L.s_h = 0;
+        L.s_o = align_up(M * I * 2, 256);
+        const size_t fe = align_up(L.s_o + M * H * 2, 256);
+        L.s_dgu = 0;
+        L.s_hw = align_up(M * 2 * I * 2, 256);
+        L.s_dx = align_up(L.s_hw + M * I * 2, 256);
+        const size_t be = align_up(L.s_dx + M * H * 2, 256);
+        L.sh = take(fe > be ? fe : be);
+    }
+    if (g.n_macro > 1) {
+        const size_t per = (size_t)g.E * I * H * 4;
+        L.wacc_g = 0;
+        L.wacc_u = per;
+        L.wacc_d = 2 * per;
+        size_t end = 3 * per;
+        if (g.shared) {
+            L.wacc_sg = end;
+            L.wacc_su = end + I * H * 4;
+            L.wacc_sd = end + 2 * I * H * 4;
+            end += 3 * I * H * 4;
+        }
+        L.wacc = take(end);
+    }
+    L.total = at;
+    return L;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+std::atomic<int> g_dev_ok[64];   // 0 unknown, 1 gfx950, 2 other
+
+bool device_ok() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+        (void)hipGetLastError();
+        return false;
+    }
+    if (dev < 64) {
+        const int v = g_dev_ok[dev].load(std::memory_order_relaxed);
+        if (v) return v == 1;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < 64) g_dev_ok[dev].store(ok ? 1 : 2, std::memory_order_relaxed);
+    return ok;
+}
+
+__global__ void k_clear_word(int32_t* p) { *p = 0; }
+
+moe_status common_checks(const moe_config* cfg, Geom& g, Layout& L, void* ws, size_t ws_bytes) {
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    L = make_layout(g);
+    if (!ws || !aligned(ws, 256) || ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+bool sched_ok(const moe_sched* s) {
+    return s && s->topk_idx && s->topk_w && s->counts && s->offsets && s->mini_counts &&
+           s->row_of_slot && s->slot_of_row && aligned(s->topk_idx, 4) && aligned(s->topk_w, 4) &&
+           aligned(s->counts, 4) && aligned(s->offsets, 4) && aligned(s->mini_counts, 4) &&
+           aligned(s->row_of_slot, 4) && aligned(s->slot_of_row, 4);
+}
+
+bool bf16_ok(const void* p) { return p && aligned(p, 16); }
+
+struct Ptrs {
+    char* ws;
+    const Layout* L;
+    int32_t* err() const { return (int32_t*)(ws + L->err); }
+    char* half(int m, int halves) const { return ws + L->ring + (size_t)(m % halves) * L->ring_half; }
+    char* sh() const { return ws + L->sh; }
+    float* wacc(size_t off) const { return (float*)(ws + L->wacc + off); }
+};
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+    switch (s) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED_DEVICE: return "unsupported device (gfx950 required)";
+        case MOE_ERR_CAPACITY: return "ring capacity below one macrobatch";
+        case MOE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+        case MOE_ERR_HIP: return "HIP error";
+        case MOE_ERR_UNSUPPORTED: return "not implemented in this build";
+    }
+    return "unknown status";
+}
+
+moe_status moe_validate_config(const moe_config* cfg) {
+    Geom g;
+    return make_geom(cfg, g);
+}
+
+moe_status moe_ring_rows(const moe_config* cfg, int64_t* rows) {
+    Geom g;
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    if (!rows) return MOE_ERR_INVALID_ARG;
+    *rows = g.ring_rows;
+    return MOE_OK;
+}
+
+moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
+    Geom g;
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    if (!bytes) return MOE_ERR_INVALID_ARG;
+    *bytes = make_layout(g).total;
+    return MOE_OK;
+}
+
+int moe_device_supported(void) { return device_ok() ? 1 : 0; }
+
+moe_status moe_schedule(const moe_config* cfg, const float* logits, const moe_sched* sched,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    Geom g;
+    Layout L;
+    moe_status s = common_checks(cfg, g, L, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    if (!logits || !aligned(logits, 4) || !sched_ok(sched)) return MOE_ERR_INVALID_ARG;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    hipStream_t st = (hipStream_t)stream;
+    char* ws = (char*)workspace;
+    int32_t* err = (int32_t*)(ws + L.err);
+    k_clear_word<<<1, 1, 0, st>>>(err);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    if (launch_topk_route(logits, g.T, g.E, g.k, sched->topk_idx, sched->topk_w, st)) return MOE_ERR_HIP;
+    if (launch_schedule(sched->topk_idx, g.T, g.E, g.k, g.M, g.mb, (int32_t*)(ws + L.hist),
+                        (int32_t*)(ws + L.base), sched->counts, sched->offsets, sched->mini_counts,
+                        sched->row_of_slot, sched->slot_of_row, err, st))
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void* x,
+                       const moe_weights* w, void* y, const moe_saved* saved, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+    Geom g;
+    Layout L;
+    moe_status s = common_checks(cfg, g, L, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    if (!sched_ok(sched) || !bf16_ok(x) || !bf16_ok(y) || !w || !saved) return MOE_ERR_INVALID_ARG;
+    if (!bf16_ok(w->w_gate) || !bf16_ok(w->w_up) || !bf16_ok(w->w_down)) return MOE_ERR_INVALID_ARG;
+    if (!bf16_ok(saved->g) || !bf16_ok(saved->u)) return MOE_ERR_INVALID_ARG;
+    if (g.shared && (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down) ||
+                     !bf16_ok(saved->sg) || !bf16_ok(saved->su)))
+        return MOE_ERR_INVALID_ARG;
+    if (g.mx) return MOE_ERR_UNSUPPORTED;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    hipStream_t st = (hipStream_t)stream;
+    Ptrs P{(char*)workspace, &L};
+    int32_t* err = P.err();
+    const uint16_t* xb = (const uint16_t*)x;
+    for (int m = 0; m < g.n_macro; ++m) {
+        char* half = P.half(m, g.halves);
+        uint16_t* xd = (uint16_t*)(half + L.f_xd);
+        uint16_t* hbuf = (uint16_t*)(half + L.f_h);
+        uint16_t* obuf = (uint16_t*)(half + L.f_o);
+        const int grow0 = m * g.Sm, t0 = m * g.M;
+        const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
+        int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
+        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
+        // dispatch, one minibatch at a time, into this macrobatch's ring half
+        for (int i = 0; i < g.n_mini; ++i) {
+            const int s0 = grow0 + i * g.Smb;
+            if (launch_dispatch(x, g.H, sched->row_of_slot, s0, s0 + g.Smb, g.k, grow0, g.Sm, xd, err, st))
+                return MOE_ERR_HIP;
+        }
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        GemmGateUpArgs a1{grp, xd, 0, 0, sched->slot_of_row, grow0, g.k, g.S,
+                          (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
+                          (uint16_t*)saved->g, (uint16_t*)saved->u, grow0, hbuf};
+        if (launch_gemm_gate_up(a1, st)) return MOE_ERR_HIP;
+        GemmDownArgs a2{grp, hbuf, (const uint16_t*)w->w_down, g.H, g.I, obuf};
+        if (launch_gemm_down(a2, st)) return MOE_ERR_HIP;
+        const uint16_t* sh_o = nullptr;
+        if (g.shared) {
+            uint16_t* sh_h = (uint16_t*)(P.sh() + L.s_h);
+            uint16_t* so = (uint16_t*)(P.sh() + L.s_o);
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GemmGateUpArgs s1{dense, xb, 0, t0, nullptr, 0, g.k, g.S,
+                              (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up, g.H, g.I,
+                              (uint16_t*)saved->sg, (uint16_t*)saved->su, t0, sh_h};
+            if (launch_gemm_gate_up(s1, st)) return MOE_ERR_HIP;
+            GemmDownArgs s2{dense, sh_h, (const uint16_t*)w->s_down, g.H, g.I, so};
+            if (launch_gemm_down(s2, st)) return MOE_ERR_HIP;
+            sh_o = so;
+        }
+        if (launch_combine(obuf, g.H, sched->row_of_slot, sched->topk_w, t0, t0 + g.M, g.k, grow0,
+                           g.Sm, sh_o, t0, y, err, st))
+            return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe_saved* saved,
+                        const void* x, const moe_weights* w, const void* dy, void* dx,
+                        const moe_grads* gr, float* dw, float* d_logits, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    Geom g;
+    Layout L;
+    moe_status s = common_checks(cfg, g, L, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    if (!sched_ok(sched) || !saved || !w || !gr || !bf16_ok(x) || !bf16_ok(dy) || !bf16_ok(dx))
+        return MOE_ERR_INVALID_ARG;
+    if (!bf16_ok(w->w_gate) || !bf16_ok(w->w_up) || !bf16_ok(w->w_down) || !bf16_ok(saved->g) ||
+        !bf16_ok(saved->u))
+        return MOE_ERR_INVALID_ARG;
+    if (!bf16_ok(gr->d_w_gate) || !bf16_ok(gr->d_w_up) || !bf16_ok(gr->d_w_down))
+        return MOE_ERR_INVALID_ARG;
+    if (!dw || !aligned(dw, 4) || (d_logits && !aligned(d_logits, 4))) return MOE_ERR_INVALID_ARG;
+    if (g.shared && (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down) ||
+                     !bf16_ok(saved->sg) || !bf16_ok(saved->su) || !bf16_ok(gr->d_s_gate) ||
+                     !bf16_ok(gr->d_s_up) || !bf16_ok(gr->d_s_down)))
+        return MOE_ERR_INVALID_ARG;
+    if (g.mx) return MOE_ERR_UNSUPPORTED;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    hipStream_t st = (hipStream_t)stream;
+    Ptrs P{(char*)workspace, &L};
+    int32_t* err = P.err();
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* dyb = (const uint16_t*)dy;
+    for (int m = g.n_macro - 1; m >= 0; --m) {
+        // weight-gradient accumulation across the reverse walk
+        int mode = 0;
+        if (g.n_macro > 1) mode = (m == g.n_macro - 1) ? 1 : (m == 0 ? 3 : 2);
+        char* half = P.half(m, g.halves);
+        uint16_t* dgu = (uint16_t*)(half + L.b_dgu);
+        uint16_t* hw = (uint16_t*)(half + L.b_hw);
+        uint16_t* dxd = (uint16_t*)(half + L.b_dx);
+        float* part = (float*)(half + L.b_part);
+        const int grow0 = m * g.Sm, t0 = m * g.M;
+        const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
+        int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
+        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        // reverse-combine (dy gathered on load) + down dgrad + SwiGLU backward + dw partials
+        GemmDownDgradArgs b1{grp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, sched->topk_w,
+                             (const uint16_t*)w->w_down, g.H, g.I, (const uint16_t*)saved->g,
+                             (const uint16_t*)saved->u, grow0, dgu, hw, part, g.P};
+        if (launch_gemm_down_dgrad(b1, st)) return MOE_ERR_HIP;
+        GemmGuDgradArgs b2{grp, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I, dxd};
+        if (launch_gemm_gu_dgrad(b2, st)) return MOE_ERR_HIP;
+        GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err};
+        WgradDownArgs b3{kgrp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, hw, g.H, g.I,
+                         {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode}};
+        if (launch_wgrad_down(b3, st)) return MOE_ERR_HIP;
+        WgradGateUpArgs b4{kgrp, dgu, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, g.H, g.I,
+                           {(uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), mode},
+                           {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode}};
+        if (launch_wgrad_gate_up(b4, st)) return MOE_ERR_HIP;
+        const uint16_t* sh_dx = nullptr;
+        if (g.shared) {
+            uint16_t* sdgu = (uint16_t*)(P.sh() + L.s_dgu);
+            uint16_t* shw = (uint16_t*)(P.sh() + L.s_hw);
+            uint16_t* sdx = (uint16_t*)(P.sh() + L.s_dx);
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GemmDownDgradArgs c1{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, nullptr,
+                                 (const uint16_t*)w->s_down, g.H, g.I, (const uint16_t*)saved->sg,
+                                 (const uint16_t*)saved->su, t0, sdgu, shw, nullptr, g.P};
+            if (launch_gemm_down_dgrad(c1, st)) return MOE_ERR_HIP;
+            GemmGuDgradArgs c2{dense, sdgu, (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up,
+                               g.H, g.I, sdx};
+            if (launch_gemm_gu_dgrad(c2, st)) return MOE_ERR_HIP;
+            WgradDownArgs c3{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, shw, g.H, g.I,
+                             {(uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), mode}};
+            if (launch_wgrad_down(c3, st)) return MOE_ERR_HIP;
+            WgradGateUpArgs c4{dense, sdgu, xb, 0, t0, nullptr, 0, g.k, g.S, g.H, g.I,
+                               {(uint16_t*)gr->d_s_gate, P.wacc(L.wacc_sg), mode},
+                               {(uint16_t*)gr->d_s_up, P.wacc(L.wacc_su), mode}};
+            if (launch_wgrad_gate_up(c4, st)) return MOE_ERR_HIP;
+            sh_dx = sdx;
+        }
+        // reverse-dispatch: dx_t = [shared] + sum_j dXd[row(t, j)]
+        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
+                             dx, err, st))
+            return MOE_ERR_HIP;
+        if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
+                               t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
+            return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+moe_status moe_check_device_error(void* workspace, size_t workspace_bytes, void* stream,
+                                  int32_t* flags) {
+    if (!workspace || !flags || workspace_bytes < 256 || !aligned(workspace, 256))
+        return MOE_ERR_INVALID_ARG;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    hipStream_t st = (hipStream_t)stream;
+    int32_t v = 0;
+    if (hipMemcpyAsync(&v, workspace, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return MOE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return MOE_ERR_HIP;
+    k_clear_word<<<1, 1, 0, st>>>((int32_t*)workspace);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    *flags = v;
+    return MOE_OK;
+}
+
+}  // extern "C"

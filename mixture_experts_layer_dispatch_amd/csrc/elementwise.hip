@@ -1,0 +1,242 @@
+// Bandwidth-bound steps of the layer: dispatch (gather into expert order),
+// the weighted combine, the reverse-dispatch reduction, the softmax backward,
+// and the per-expert tile prefix the grouped GEMMs are launched over.
+//
+// Dispatch / combine / reverse-dispatch: alphalab.site "Mixture-of-Kittens"
+// section 一 (tokens go to their experts and come back) and section 二 (the
+// router-weighted reduction; a fixed floating-point accumulation order makes
+// the layer bitwise reproducible); arex-research.com "Cursor 放出 MoK", design
+// section, first decision (forward dispatch/combine and backward
+// reverse-combine/reverse-dispatch all read one schedule table).
+//
+// Every kernel moves 16-byte chunks (8 bf16) per lane so that a wave reads or
+// writes 1 KiB contiguous per instruction; rows are H bf16 long.
+#include "common.h"
+#include "launch.h"
+#include "profile.h"
+
+namespace moe {
+
+// ============================================================== dispatch
+// Slot-major over one minibatch: slot s copies token s/k into ring row
+// row_of_slot[s] - ring_row0.  A token's k slots are adjacent, so its source
+// row is read from cache after the first copy.
+__global__ __launch_bounds__(256) void k_dispatch(const uint4* __restrict__ x, int H8,
+                                                  const int32_t* __restrict__ row_of_slot, int s0,
+                                                  int s1, int k, int ring_row0, int ring_rows,
+                                                  uint4* __restrict__ ring, int32_t* __restrict__ err) {
+    const int s = s0 + blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (s >= s1) return;
+    const int lane = lane_id();
+    const int r = row_of_slot[s] - ring_row0;
+    if ((unsigned)r >= (unsigned)ring_rows) {
+        if (lane == 0) raise_err(err, ERR_BAD_ROW);
+        return;
+    }
+    const uint4* src = x + (size_t)(s / k) * H8;
+    uint4* dst = ring + (size_t)r * H8;
+    for (int c = lane; c < H8; c += 64) dst[c] = src[c];
+}
+
+// ============================================================== combine
+// Lane j < k of the wave holds slot j's ring row and weight; the loops below
+// read them with uniform-lane shuffles, so the j order is fixed.
+__device__ __forceinline__ void load_slot_rows(const int32_t* __restrict__ row_of_slot,
+                                               const float* __restrict__ w, int t, int k,
+                                               int ring_row0, int ring_rows, int lane, int& row,
+                                               float& wt, int32_t* err) {
+    row = -1;
+    wt = 0.f;
+    if (lane < k) {
+        int r = row_of_slot[(size_t)t * k + lane] - ring_row0;
+        if ((unsigned)r < (unsigned)ring_rows) row = r;
+        else raise_err(err, ERR_BAD_ROW);
+        if (w) wt = w[(size_t)t * k + lane];
+    }
+}
+
+__device__ __forceinline__ void unpack8(const uint4& v, float* a) {
+    a[0] = lo_bf(v.x); a[1] = hi_bf(v.x); a[2] = lo_bf(v.y); a[3] = hi_bf(v.y);
+    a[4] = lo_bf(v.z); a[5] = hi_bf(v.z); a[6] = lo_bf(v.w); a[7] = hi_bf(v.w);
+}
+
+__device__ __forceinline__ uint4 pack8(const float* a) {
+    uint4 out;
+    out.x = pack_bf2(a[0], a[1]);
+    out.y = pack_bf2(a[2], a[3]);
+    out.z = pack_bf2(a[4], a[5]);
+    out.w = pack_bf2(a[6], a[7]);
+    return out;
+}
+
+// y_t = [shared_t] + sum_{j=0..k-1} w[t,j] * o[row(t,j)] in fp32, in this
+// order, one rounding to bf16 (w == nullptr: unit weights, the
+// reverse-dispatch sum of the backward).  One wave per token.
+__global__ __launch_bounds__(256) void k_combine(const uint4* __restrict__ o, int H8,
+                                                 const int32_t* __restrict__ row_of_slot,
+                                                 const float* __restrict__ w, int t0, int t1,
+                                                 int k, int ring_row0, int ring_rows,
+                                                 const uint4* __restrict__ shared, int shared_t0,
+                                                 uint4* __restrict__ y, int32_t* __restrict__ err) {
+    const int t = t0 + blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= t1) return;
+    const int lane = lane_id();
+    int myrow;
+    float myw;
+    load_slot_rows(row_of_slot, w, t, k, ring_row0, ring_rows, lane, myrow, myw, err);
+    for (int c0 = 0; c0 < H8; c0 += 64) {
+        const int c = c0 + lane;
+        const bool ok = c < H8;
+        float acc[8];
+        if (shared && ok) {
+            unpack8(shared[(size_t)(t - shared_t0) * H8 + c], acc);
+        } else {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) acc[q] = 0.f;
+        }
+        for (int j = 0; j < k; ++j) {
+            const int r = __shfl(myrow, j);
+            const float wj = w ? __shfl(myw, j) : 1.0f;
+            if (r < 0 || !ok) continue;
+            float v[8];
+            unpack8(o[(size_t)r * H8 + c], v);
+            if (w) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] += wj * v[q];
+            } else {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) acc[q] += v[q];
+            }
+        }
+        if (ok) y[(size_t)t * H8 + c] = pack8(acc);
+    }
+}
+
+// ============================================================== softmax backward
+// dw[t,j] = sum_p part[row(t,j)][p] (p ascending), then
+// d_logit[t, idx[t,j]] = w_j (dw_j - sum_i w_i dw_i), zero for other experts.
+// One wave per token.
+__global__ __launch_bounds__(256) void k_softmax_bwd(const float* __restrict__ part, int P,
+                                                     const int32_t* __restrict__ row_of_slot,
+                                                     const int32_t* __restrict__ idx,
+                                                     const float* __restrict__ w, int t0, int t1,
+                                                     int k, int E, int ring_row0, int ring_rows,
+                                                     float* __restrict__ dw,
+                                                     float* __restrict__ d_logits,
+                                                     int32_t* __restrict__ err) {
+    const int t = t0 + blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= t1) return;
+    const int lane = lane_id();
+    int myrow;
+    float wj;
+    load_slot_rows(row_of_slot, w, t, k, ring_row0, ring_rows, lane, myrow, wj, err);
+    float dwj = 0.f;
+    int ej = -1;
+    if (lane < k) {
+        if (myrow >= 0) {
+            const float* pr = part + (size_t)myrow * P;
+            for (int p = 0; p < P; ++p) dwj += pr[p];
+        }
+        ej = idx[(size_t)t * k + lane];
+        dw[(size_t)t * k + lane] = dwj;
+    }
+    float c = 0.f;
+    for (int j = 0; j < k; ++j) c += __shfl(wj, j) * __shfl(dwj, j);
+    const float dl = wj * (dwj - c);
+    if (d_logits) {
+        float* out = d_logits + (size_t)t * E;
+        for (int e0 = 0; e0 < E; e0 += 64) {
+            const int e = e0 + lane;
+            float v = 0.f;
+            for (int j = 0; j < k; ++j) {
+                const int ejj = __shfl(ej, j);
+                const float dlj = __shfl(dl, j);
+                if (ejj == e) v = dlj;
+            }
+            if (e < E) out[e] = v;
+        }
+    }
+}
+
+// ============================================================== tile prefix
+// tile_off[e] = sum_{e' < e} ceil(count(e') / TM) from one macrobatch's
+// offsets; tile_off[E] is the number of row tiles.  One block, E <= 1024.
+__global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict__ offsets, int E,
+                                                      int rows, int TM, int32_t* __restrict__ tile_off,
+                                                      int32_t* __restrict__ err) {
+    __shared__ int32_t wsum[16];
+    const int e = threadIdx.x;
+    int n = 0;
+    if (e < E) {
+        const int a = offsets[e], b = offsets[e + 1];
+        if (a < 0 || b < a || b > rows) {
+            raise_err(err, ERR_BAD_OFFSETS);
+        } else {
+            n = (b - a + TM - 1) / TM;
+        }
+    }
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    int incl = n;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int wpre = 0;
+    for (int q = 0; q < wv; ++q) wpre += wsum[q];
+    if (e < E) tile_off[e] = wpre + incl - n;
+    if (e == E - 1) tile_off[E] = wpre + incl;
+}
+
+// ============================================================== launchers
+int launch_dispatch(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
+                    int ring_row0, int ring_rows, void* ring, int32_t* err, hipStream_t st) {
+    ProfScope prof_(st, "dispatch");
+    if (s1 <= s0) return 0;
+    k_dispatch<<<(s1 - s0 + 3) / 4, 256, 0, st>>>((const uint4*)x, H / 8, row_of_slot, s0, s1, k,
+                                                  ring_row0, ring_rows, (uint4*)ring, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_combine(const void* o, int H, const int32_t* row_of_slot, const float* w, int t0, int t1,
+                   int k, int ring_row0, int ring_rows, const void* shared, int shared_t0, void* y,
+                   int32_t* err, hipStream_t st) {
+    ProfScope prof_(st, "combine");
+    if (t1 <= t0) return 0;
+    k_combine<<<(t1 - t0 + 3) / 4, 256, 0, st>>>((const uint4*)o, H / 8, row_of_slot, w, t0, t1, k,
+                                                 ring_row0, ring_rows, (const uint4*)shared,
+                                                 shared_t0, (uint4*)y, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_rd_reduce(const void* dxd, int H, const int32_t* row_of_slot, int t0, int t1, int k,
+                     int ring_row0, int ring_rows, const void* shared, int shared_t0, void* dx,
+                     int32_t* err, hipStream_t st) {
+    ProfScope prof_(st, "rd_reduce");
+    if (t1 <= t0) return 0;
+    k_combine<<<(t1 - t0 + 3) / 4, 256, 0, st>>>((const uint4*)dxd, H / 8, row_of_slot, nullptr, t0,
+                                                 t1, k, ring_row0, ring_rows, (const uint4*)shared,
+                                                 shared_t0, (uint4*)dx, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_softmax_bwd(const float* part, int P, const int32_t* row_of_slot, const int32_t* idx,
+                       const float* w, int t0, int t1, int k, int E, int ring_row0, int ring_rows,
+                       float* dw, float* d_logits, int32_t* err, hipStream_t st) {
+    ProfScope prof_(st, "softmax_bwd");
+    if (t1 <= t0) return 0;
+    k_softmax_bwd<<<(t1 - t0 + 3) / 4, 256, 0, st>>>(part, P, row_of_slot, idx, w, t0, t1, k, E,
+                                                     ring_row0, ring_rows, dw, d_logits, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
+                       int32_t* err, hipStream_t st) {
+    ProfScope prof_(st, "tile_prefix");
+    k_tile_prefix<<<1, 1024, 0, st>>>(offsets, E, rows, TM, tile_off, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+}  // namespace moe

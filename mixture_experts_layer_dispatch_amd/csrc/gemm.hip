@@ -1,0 +1,670 @@
+// Expert-grouped GEMMs of the SwiGLU FFN, forward and backward, on MFMA.
+//
+// alphalab.site "Mixture-of-Kittens", section 一: each expert runs a SwiGLU
+// FFN on the tokens routed to it (gate/up projection, SiLU(g) * u, down
+// projection), and the backward computes the expert gradients;
+// arex-research.com "Cursor 放出 MoK", design section: the GEMMs are grouped by
+// expert, and the router-weight gradient is fused into the SwiGLU backward
+// (closing paragraph).
+//
+// Two grouping shapes:
+//   M-grouped  C_e[rows of e, N] = A[rows of e, K] * B_e[N, K]^T   (forward,
+//              input gradients): the row count of each expert is dynamic; the
+//              grid covers an upper bound of row tiles and each block finds its
+//              (expert, row tile) by binary search over a device-side tile
+//              prefix, so no count ever reaches the host.
+//   K-grouped  C_e[M, N] = sum over rows r of e of A[r, M] (x) B[r, N]
+//              (weight gradients): M and N fixed, the reduction runs over the
+//              expert's rows in ascending order.
+//
+// Tiles: 256 threads = 4 waves in a 2 x 2 grid, each wave (TM/2) x (TN/2).
+// Both operands are staged through LDS in a [row][k] layout (row pitch
+// kTK + 8 bf16 = 144 B, so the 16 rows read by one MFMA fragment hit 16
+// different 16-byte bank groups), double-buffered with one barrier per K step.
+// Operands whose reduction index is the slow memory axis are transposed on
+// the way into LDS (two k rows are packed into one 32-bit word per row).
+// The MFMA is issued with the B tile as its first operand, so each lane's four
+// accumulators are four consecutive output columns (8-byte stores).
+// Each output element is a fixed-order fp32 sum: K steps ascend, and the
+// MFMA's internal order is fixed, so results are identical run to run and do
+// not depend on which other rows share the tile.
+#include "common.h"
+#include "launch.h"
+#include "profile.h"
+
+namespace moe {
+
+constexpr int kTK = 64;
+constexpr int kPitch = kTK + 8;
+
+// ================================================================ sources
+// Row-major operand whose tile rows are rows of memory (K contiguous).
+struct RowsDirect {
+    const uint16_t* base;
+    int64_t ld;
+    int row0, nvalid;
+    __device__ const uint16_t* row(int r) const {
+        return r < nvalid ? base + (int64_t)(row0 + r) * ld : nullptr;
+    }
+};
+
+// Tile row r = schedule row grow0 + r; memory row = token of its slot.
+struct RowsGather {
+    const uint16_t* base;
+    int64_t ld;
+    const int32_t* slot_of_row;
+    int grow0, nvalid, k, S;
+    int32_t* err;
+    __device__ const uint16_t* row(int r) const {
+        if (r >= nvalid) return nullptr;
+        const int s = slot_of_row[grow0 + r];
+        if ((unsigned)s >= (unsigned)S) {
+            raise_err(err, ERR_BAD_SLOT);
+            return nullptr;
+        }
+        return base + (int64_t)(s / k) * ld;
+    }
+};
+
+// Gate/up weight rows interleaved in quarters of 32 so that a wave owns
+// matching gate and up columns: tile row n -> quarter q = n / 32,
+// q even: W_gate row, q odd: W_up row, both at column i0 + 32*(q/2) + n%32.
+struct RowsGateUp {
+    const uint16_t* wg;
+    const uint16_t* wu;
+    int64_t ld;
+    int i0;
+    __device__ const uint16_t* row(int n) const {
+        const int q = n >> 5;
+        const int i = i0 + ((q >> 1) << 5) + (n & 31);
+        return ((q & 1) ? wu : wg) + (int64_t)i * ld;
+    }
+};
+
+// Operand whose reduction index k is the memory row: krow(k) points at the
+// tile's first column in memory row k.
+struct KRowsDirect {
+    const uint16_t* base;
+    int64_t ld;
+    int col0, kmax;
+    __device__ const uint16_t* krow(int kk) const {
+        return kk < kmax ? base + (int64_t)kk * ld + col0 : nullptr;
+    }
+};
+
+// k < I: W_gate row k; I <= k < 2I: W_up row k - I.
+struct KRowsGateUp {
+    const uint16_t* wg;
+    const uint16_t* wu;
+    int64_t ld;
+    int col0, I;
+    __device__ const uint16_t* krow(int kk) const {
+        if (kk < I) return wg + (int64_t)kk * ld + col0;
+        if (kk < 2 * I) return wu + (int64_t)(kk - I) * ld + col0;
+        return nullptr;
+    }
+};
+
+// k = the k-th row of a group: memory row row0 + k.
+struct KRowsGroup {
+    const uint16_t* base;
+    int64_t ld;
+    int row0, n, col0;
+    __device__ const uint16_t* krow(int kk) const {
+        return kk < n ? base + (int64_t)(row0 + kk) * ld + col0 : nullptr;
+    }
+};
+
+// k = the k-th row of a group in schedule rows; memory row = its token.
+struct KRowsGroupGather {
+    const uint16_t* base;
+    int64_t ld;
+    const int32_t* slot_of_row;
+    int grow0, n, col0, k, S;
+    int32_t* err;
+    __device__ const uint16_t* krow(int kk) const {
+        if (kk >= n) return nullptr;
+        const int s = slot_of_row[grow0 + kk];
+        if ((unsigned)s >= (unsigned)S) {
+            raise_err(err, ERR_BAD_SLOT);
+            return nullptr;
+        }
+        return base + (int64_t)(s / k) * ld + col0;
+    }
+};
+
+// ================================================================ loaders
+// K-contiguous tile of ROWS rows: 16-byte chunks, 8 lanes per 128-byte row
+// segment.
+template <int ROWS, class Src>
+struct LoadKC {
+    static constexpr int PER = ROWS * (kTK / 8) / 256;
+    const uint16_t* p[PER];
+    int off[PER];
+    uint4 v[PER];
+    __device__ explicit LoadKC(const Src& src) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int c = threadIdx.x + 256 * q;
+            const int r = c >> 3, kc = c & 7;
+            const uint16_t* b = src.row(r);
+            p[q] = b ? b + kc * 8 : nullptr;
+            off[q] = r * kPitch + kc * 8;
+        }
+    }
+    __device__ void load(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            v[q] = p[q] ? *(const uint4*)(p[q] + (int64_t)kt * kTK) : make_uint4(0, 0, 0, 0);
+    }
+    __device__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) *(uint4*)(s + off[q]) = v[q];
+    }
+};
+
+__device__ __forceinline__ uint32_t half_of(const uint4& v, int j) {
+    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
+    return (j & 1) ? (w >> 16) : (w & 0xffffu);
+}
+
+// Tile whose reduction index is the slow memory axis: a unit is (k pair,
+// 8-row chunk); the two 16-byte loads of a pair are interleaved into eight
+// 32-bit words, one per tile row.
+template <int ROWS, class Src>
+struct LoadKS {
+    static constexpr int CH = ROWS / 8;
+    static constexpr int PER = (kTK / 2) * CH / 256;
+    Src src;
+    int kp[PER], rc[PER];
+    uint4 lo[PER], hi[PER];
+    __device__ explicit LoadKS(const Src& s) : src(s) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int u = threadIdx.x + 256 * q;
+            rc[q] = u % CH;
+            kp[q] = u / CH;
+        }
+    }
+    __device__ void load(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int k0 = kt * kTK + 2 * kp[q];
+            const uint16_t* a = src.krow(k0);
+            const uint16_t* b = src.krow(k0 + 1);
+            lo[q] = a ? *(const uint4*)(a + rc[q] * 8) : make_uint4(0, 0, 0, 0);
+            hi[q] = b ? *(const uint4*)(b + rc[q] * 8) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            uint32_t* d = (uint32_t*)(s + rc[q] * 8 * kPitch + 2 * kp[q]);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) d[j * (kPitch / 2)] = half_of(lo[q], j) | (half_of(hi[q], j) << 16);
+        }
+    }
+};
+
+// ================================================================ main loop
+template <int MB, int NB>
+__device__ __forceinline__ void mma_tile(const uint16_t* sA, const uint16_t* sB, int wm0, int wn0,
+                                         f32x4 (&acc)[MB][NB]) {
+    const int lane = lane_id();
+    const int lr = lane & 15, lk = (lane >> 4) * 8;
+#pragma unroll
+    for (int ks = 0; ks < kTK; ks += 32) {
+        bf16x8 fb[MB], fa[NB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+            fb[mb] = *(const bf16x8*)(sA + (wm0 + mb * 16 + lr) * kPitch + ks + lk);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb)
+            fa[nb] = *(const bf16x8*)(sB + (wn0 + nb * 16 + lr) * kPitch + ks + lk);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], fb[mb], acc[mb][nb]);
+    }
+}
+
+template <int TM, int TN, class LA, class LB>
+__device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
+                                         f32x4 (&acc)[TM / 32][TN / 32]) {
+    constexpr int MB = TM / 32, NB = TN / 32;
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nk <= 0) return;
+    uint16_t* buf0 = smem;
+    uint16_t* buf1 = smem + (TM + TN) * kPitch;
+    la.load(0);
+    lb.load(0);
+    la.store(buf0);
+    lb.store(buf0 + TM * kPitch);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        uint16_t* cur = (kt & 1) ? buf1 : buf0;
+        uint16_t* nxt = (kt & 1) ? buf0 : buf1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            la.load(kt + 1);
+            lb.load(kt + 1);
+        }
+        mma_tile<MB, NB>(cur, cur + TM * kPitch, wm0, wn0, acc);
+        if (more) {
+            la.store(nxt);
+            lb.store(nxt + TM * kPitch);
+        }
+        __syncthreads();
+    }
+}
+
+// accumulator (mb, nb, r) -> tile coordinates
+template <int TM, int TN>
+struct AccPos {
+    int m_base, n_base;
+    __device__ AccPos() {
+        const int w = threadIdx.x >> 6, lane = lane_id();
+        m_base = (w & 1) * (TM / 2) + (lane & 15);
+        n_base = (w >> 1) * (TN / 2) + 4 * (lane >> 4);
+    }
+    __device__ int m(int mb) const { return m_base + mb * 16; }
+    __device__ int n(int nb) const { return n_base + nb * 16; }
+};
+
+__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
+    return make_uint2(pack_bf2(a, b), pack_bf2(c, d));
+}
+
+// ================================================================ tile maps
+// M-grouped: find (expert, row range, column tile) of block b.
+template <int TM>
+__device__ __forceinline__ bool map_mtile(const GroupRows& g, int nNt, int b, int& e, int& lo, int& hi,
+                                          int& nt) {
+    const int ntiles = g.tile_off ? g.tile_off[g.E] : (g.dense_rows + TM - 1) / TM;
+    const int total = ntiles * nNt;
+    if (b >= total) return false;
+    const int L = xcd_remap(b, total);
+    const int mt = L / nNt;
+    nt = L - mt * nNt;
+    if (!g.tile_off) {
+        e = 0;
+        lo = mt * TM;
+        hi = min(lo + TM, g.dense_rows);
+        return true;
+    }
+    int a = 0, z = g.E;
+    while (z - a > 1) {
+        const int mid = (a + z) >> 1;
+        if (g.tile_off[mid] <= mt) a = mid;
+        else z = mid;
+    }
+    e = a;
+    lo = g.offsets[e] + (mt - g.tile_off[e]) * TM;
+    hi = min(lo + TM, g.offsets[e + 1]);
+    return true;
+}
+
+// K-grouped: block b -> (expert, M tile, N tile) and the expert's rows.
+__device__ __forceinline__ bool map_ktile(const GroupRows& g, int nMt, int nNt, int b, int& e, int& mt,
+                                          int& nt, int& lo, int& n) {
+    const int per = nMt * nNt;
+    const int total = (g.offsets ? g.E : 1) * per;
+    if (b >= total) return false;
+    const int L = xcd_remap(b, total);
+    e = L / per;
+    const int rem = L - e * per;
+    mt = rem / nNt;
+    nt = rem - mt * nNt;
+    if (!g.offsets) {
+        lo = 0;
+        n = g.dense_rows;
+        return true;
+    }
+    const int a = g.offsets[e], z = g.offsets[e + 1];
+    if (a < 0 || z < a || z > g.rows) {
+        raise_err(g.err, ERR_BAD_OFFSETS);
+        lo = 0;
+        n = 0;
+    } else {
+        lo = a;
+        n = z - a;
+    }
+    return true;
+}
+
+// ================================================================ forward GEMM 1
+// g = X W_gate^T, u = X W_up^T, h = SiLU(g) * u; g, u saved (bf16), h to the
+// ring.  Tile: 64 rows x (64 gate + 64 up columns).
+constexpr int G1_TM = 64, G1_TN = 128;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G1_TM + G1_TN) * kPitch];
+    int e, lo, hi, nt;
+    if (!map_mtile<G1_TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
+    const int i0 = nt * 64;
+    f32x4 acc[2][4];
+    const int nk = a.H / kTK;
+    const uint16_t* wg = a.w_gate + (int64_t)e * a.I * a.H;
+    const uint16_t* wu = a.w_up + (int64_t)e * a.I * a.H;
+    RowsGateUp sb{wg, wu, a.H, i0};
+    LoadKC<G1_TN, RowsGateUp> lb(sb);
+    if (a.x_gather) {
+        RowsGather sa{a.x, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
+        LoadKC<G1_TM, RowsGather> la(sa);
+        mainloop<G1_TM, G1_TN>(la, lb, nk, smem, acc);
+    } else {
+        RowsDirect sa{a.x, a.H, a.xrow0 + lo, hi - lo};
+        LoadKC<G1_TM, RowsDirect> la(sa);
+        mainloop<G1_TM, G1_TN>(la, lb, nk, smem, acc);
+    }
+    AccPos<G1_TM, G1_TN> pos;
+    const int wn = threadIdx.x >> 7;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int rl = lo + pos.m(mb);
+        if (rl >= hi) continue;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int i = i0 + 32 * wn + nb * 16 + 4 * (lane_id() >> 4);
+            float gq[4], uq[4], hq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                gq[r] = bf2f(f2bf(acc[mb][nb][r]));
+                uq[r] = bf2f(f2bf(acc[mb][nb + 2][r]));
+                hq[r] = swiglu_h(gq[r], uq[r]);
+            }
+            const int64_t srow = (int64_t)(a.save_row0 + rl) * a.I + i;
+            *(uint2*)(a.g_out + srow) = pack4(gq[0], gq[1], gq[2], gq[3]);
+            *(uint2*)(a.u_out + srow) = pack4(uq[0], uq[1], uq[2], uq[3]);
+            *(uint2*)(a.h_out + (int64_t)rl * a.I + i) = pack4(hq[0], hq[1], hq[2], hq[3]);
+        }
+    }
+}
+
+// ================================================================ forward GEMM 2
+// o = h W_down^T.  Tile 64 rows x 128 columns of H.
+constexpr int G2_TM = 64, G2_TN = 128;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G2_TM + G2_TN) * kPitch];
+    int e, lo, hi, nt;
+    if (!map_mtile<G2_TM>(a.g, a.H / G2_TN, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * G2_TN;
+    f32x4 acc[2][4];
+    RowsDirect sa{a.h, a.I, lo, hi - lo};
+    LoadKC<G2_TM, RowsDirect> la(sa);
+    RowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, G2_TN};
+    LoadKC<G2_TN, RowsDirect> lb(sb);
+    mainloop<G2_TM, G2_TN>(la, lb, a.I / kTK, smem, acc);
+    AccPos<G2_TM, G2_TN> pos;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int rl = lo + pos.m(mb);
+        if (rl >= hi) continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int c = n0 + pos.n(nb);
+            const f32x4 v = acc[mb][nb];
+            *(uint2*)(a.o + (int64_t)rl * a.H + c) = pack4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+// ================================================================ backward: down dgrad
+// a = dY W_down (dY row = dy of the row's token, gathered on load), then the
+// SwiGLU backward and the router-weight gradient in the epilogue:
+//   h = SiLU(g) * u (recomputed from the saved bf16 g, u exactly as forward)
+//   dw partial = sum over this tile's columns of a * h
+//   dh = w * a;  du = dh * SiLU(g);  dg = dh * u * s * (1 + g (1 - s))
+//   hw = w * h   (the down-projection weight-gradient operand)
+// Tile 64 rows x 128 columns of I; reduction over H.
+constexpr int G3_TM = 64, G3_TN = 128;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G3_TM + G3_TN) * kPitch];
+    __shared__ float red[2][G3_TM];
+    int e, lo, hi, nt;
+    if (!map_mtile<G3_TM>(a.g, a.I / G3_TN, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * G3_TN;
+    f32x4 acc[2][4];
+    KRowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, a.H};
+    LoadKS<G3_TN, KRowsDirect> lb(sb);
+    if (a.dy_gather) {
+        RowsGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
+        LoadKC<G3_TM, RowsGather> la(sa);
+        mainloop<G3_TM, G3_TN>(la, lb, a.H / kTK, smem, acc);
+    } else {
+        RowsDirect sa{a.dy, a.H, a.dyrow0 + lo, hi - lo};
+        LoadKC<G3_TM, RowsDirect> la(sa);
+        mainloop<G3_TM, G3_TN>(la, lb, a.H / kTK, smem, acc);
+    }
+    AccPos<G3_TM, G3_TN> pos;
+    const int lane = lane_id();
+    const int wv = threadIdx.x >> 6, wm = wv & 1, wn = wv >> 1;
+    float dot[2] = {0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int rl = lo + pos.m(mb);
+        const bool ok = rl < hi;
+        float wr = 1.0f;
+        if (ok && a.topk_w) {
+            const int s = a.slot_of_row[a.grow0 + rl];
+            wr = (unsigned)s < (unsigned)a.S ? a.topk_w[s] : 0.f;
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            if (!ok) continue;
+            const int i = n0 + pos.n(nb);
+            const int64_t srow = (int64_t)(a.save_row0 + rl) * a.I + i;
+            const uint2 gb = *(const uint2*)(a.g_saved + srow);
+            const uint2 ub = *(const uint2*)(a.u_saved + srow);
+            const float gq[4] = {lo_bf(gb.x), hi_bf(gb.x), lo_bf(gb.y), hi_bf(gb.y)};
+            const float uq[4] = {lo_bf(ub.x), hi_bf(ub.x), lo_bf(ub.y), hi_bf(ub.y)};
+            float dg[4], du[4], hw[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float av = acc[mb][nb][r];
+                const float h = bf2f(f2bf(swiglu_h(gq[r], uq[r])));
+                dot[mb] += av * h;
+                const float dh = wr * av;
+                const float s = sigmoidf_(gq[r]);
+                du[r] = dh * (gq[r] * s);
+                dg[r] = dh * uq[r] * s * (1.0f + gq[r] * (1.0f - s));
+                hw[r] = wr * h;
+            }
+            const int64_t drow = (int64_t)rl * (2 * a.I);
+            *(uint2*)(a.dgu + drow + i) = pack4(dg[0], dg[1], dg[2], dg[3]);
+            *(uint2*)(a.dgu + drow + a.I + i) = pack4(du[0], du[1], du[2], du[3]);
+            *(uint2*)(a.hw + (int64_t)rl * a.I + i) = pack4(hw[0], hw[1], hw[2], hw[3]);
+        }
+    }
+    if (!a.dw_part) return;
+    // reduce the per-lane dots over the 4 lanes that share a row, then over
+    // the two column-halves of the tile (waves wn = 0, 1), in a fixed order
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        dot[mb] += __shfl_xor(dot[mb], 16);
+        dot[mb] += __shfl_xor(dot[mb], 32);
+    }
+    if (lane < 16) {
+        red[wn][wm * 32 + lane] = dot[0];
+        red[wn][wm * 32 + 16 + lane] = dot[1];
+    }
+    __syncthreads();
+    if (threadIdx.x < G3_TM) {
+        const int m = threadIdx.x;
+        const int rl = lo + m;
+        if (rl < hi) a.dw_part[(int64_t)rl * a.P + nt] = red[0][m] + red[1][m];
+    }
+}
+
+// ================================================================ backward: gate/up dgrad
+// dX = dg W_gate + du W_up: A = [dg | du] rows (K = 2I), B = [W_gate; W_up]
+// read with k as the memory row.  Tile 64 rows x 128 columns of H.
+constexpr int G4_TM = 64, G4_TN = 128;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G4_TM + G4_TN) * kPitch];
+    int e, lo, hi, nt;
+    if (!map_mtile<G4_TM>(a.g, a.H / G4_TN, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * G4_TN;
+    f32x4 acc[2][4];
+    RowsDirect sa{a.dgu, 2 * a.I, lo, hi - lo};
+    LoadKC<G4_TM, RowsDirect> la(sa);
+    KRowsGateUp sb{a.w_gate + (int64_t)e * a.I * a.H, a.w_up + (int64_t)e * a.I * a.H, a.H, n0, a.I};
+    LoadKS<G4_TN, KRowsGateUp> lb(sb);
+    mainloop<G4_TM, G4_TN>(la, lb, 2 * a.I / kTK, smem, acc);
+    AccPos<G4_TM, G4_TN> pos;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int rl = lo + pos.m(mb);
+        if (rl >= hi) continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int c = n0 + pos.n(nb);
+            const f32x4 v = acc[mb][nb];
+            *(uint2*)(a.dx + (int64_t)rl * a.H + c) = pack4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+// ================================================================ weight-gradient epilogue
+// mode: 0 write bf16; 1 write fp32 partial; 2 add to fp32 partial;
+//       3 add to fp32 partial and write bf16 (the last macrobatch of the walk)
+__device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, const f32x4& v) {
+    float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
+    if (o.mode >= 2) {
+        const float4 p = *(const float4*)(o.acc + idx);
+        x0 = p.x + x0; x1 = p.y + x1; x2 = p.z + x2; x3 = p.w + x3;
+    }
+    if (o.mode == 1 || o.mode == 2) *(float4*)(o.acc + idx) = make_float4(x0, x1, x2, x3);
+    else *(uint2*)(o.out + idx) = pack4(x0, x1, x2, x3);
+}
+
+// ================================================================ backward: down wgrad
+// dW_down[e][h, i] = sum over e's rows r (ascending) of dy[tok(r), h] * hw[r, i].
+constexpr int W_TM = 128, W_TN = 128;
+
+__global__ __launch_bounds__(256, 2) void k_wgrad_down(WgradDownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (W_TM + W_TN) * kPitch];
+    int e, mt, nt, lo, n;
+    if (!map_ktile(a.g, a.H / W_TM, a.I / W_TN, blockIdx.x, e, mt, nt, lo, n)) return;
+    const int m0 = mt * W_TM, n0 = nt * W_TN;
+    f32x4 acc[4][4];
+    const int nk = (n + kTK - 1) / kTK;
+    KRowsGroup sb{a.hw, a.I, lo, n, n0};
+    LoadKS<W_TN, KRowsGroup> lb(sb);
+    if (a.dy_gather) {
+        KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
+        LoadKS<W_TM, KRowsGroupGather> la(sa);
+        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+    } else {
+        KRowsGroup sa{a.dy, a.H, a.dyrow0 + lo, n, m0};
+        LoadKS<W_TM, KRowsGroup> la(sa);
+        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+    }
+    AccPos<W_TM, W_TN> pos;
+    const int64_t ebase = (int64_t)e * a.H * a.I;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            wgrad_store(a.out, ebase + (int64_t)(m0 + pos.m(mb)) * a.I + n0 + pos.n(nb), acc[mb][nb]);
+}
+
+// ================================================================ backward: gate/up wgrad
+// dW_gate[e][i, h] = sum_r dg[r, i] x[tok(r), h]; dW_up likewise with du.
+// M runs over the 2I columns of [dg | du].
+__global__ __launch_bounds__(256, 2) void k_wgrad_gate_up(WgradGateUpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (W_TM + W_TN) * kPitch];
+    int e, mt, nt, lo, n;
+    if (!map_ktile(a.g, 2 * a.I / W_TM, a.H / W_TN, blockIdx.x, e, mt, nt, lo, n)) return;
+    const int m0 = mt * W_TM, n0 = nt * W_TN;
+    f32x4 acc[4][4];
+    const int nk = (n + kTK - 1) / kTK;
+    KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};
+    LoadKS<W_TM, KRowsGroup> la(sa);
+    if (a.x_gather) {
+        KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, n0, a.k, a.S, a.g.err};
+        LoadKS<W_TN, KRowsGroupGather> lb(sb);
+        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+    } else {
+        KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, n0};
+        LoadKS<W_TN, KRowsGroup> lb(sb);
+        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+    }
+    AccPos<W_TM, W_TN> pos;
+    const bool up = m0 >= a.I;
+    const WgradOut& o = up ? a.out_up : a.out_gate;
+    const int mrow0 = up ? m0 - a.I : m0;
+    const int64_t ebase = (int64_t)e * a.I * a.H;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            wgrad_store(o, ebase + (int64_t)(mrow0 + pos.m(mb)) * a.H + n0 + pos.n(nb), acc[mb][nb]);
+}
+
+// ================================================================ launchers
+static inline int mgroup_grid(const GroupRows& g, int TM) {
+    if (!g.tile_off) return (g.dense_rows + TM - 1) / TM;
+    // sum_e ceil(n_e / TM) <= (rows + E (TM - 1)) / TM, and <= rows
+    const int64_t bound = ((int64_t)g.rows + (int64_t)g.E * (TM - 1)) / TM;
+    return (int)(bound < g.rows ? bound : g.rows);
+}
+
+int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "gemm_gate_up");
+    const int grid = mgroup_grid(a.g, G1_TM) * (a.I / 64);
+    if (grid <= 0) return 0;
+    k_gemm_gate_up<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "gemm_down");
+    const int grid = mgroup_grid(a.g, G2_TM) * (a.H / G2_TN);
+    if (grid <= 0) return 0;
+    k_gemm_down<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "gemm_down_dgrad");
+    const int grid = mgroup_grid(a.g, G3_TM) * (a.I / G3_TN);
+    if (grid <= 0) return 0;
+    k_gemm_down_dgrad<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "gemm_gu_dgrad");
+    const int grid = mgroup_grid(a.g, G4_TM) * (a.H / G4_TN);
+    if (grid <= 0) return 0;
+    k_gemm_gu_dgrad<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "wgrad_down");
+    const int grid = (a.g.offsets ? a.g.E : 1) * (a.H / W_TM) * (a.I / W_TN);
+    k_wgrad_down<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "wgrad_gate_up");
+    const int grid = (a.g.offsets ? a.g.E : 1) * (2 * a.I / W_TM) * (a.H / W_TN);
+    k_wgrad_gate_up<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int gemm_row_tile() { return G1_TM; }
+int dgrad_col_tiles(int I) { return I / G3_TN; }
+
+}  // namespace moe

@@ -1,0 +1,138 @@
+// Internal interface between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+constexpr int kBlockSlots = 512;   // slots per schedule block
+
+// Row groups of one macrobatch.  offsets == nullptr: a single dense group of
+// dense_rows rows (the shared expert).
+struct GroupRows {
+    const int32_t* offsets;   // [E+1] macrobatch-local row offsets
+    const int32_t* tile_off;  // [E+1] prefix of row tiles (M-grouped GEMMs)
+    int E;
+    int rows;                 // rows in the macrobatch (bounds check of offsets)
+    int dense_rows;
+    int32_t* err;
+};
+
+struct GemmGateUpArgs {
+    GroupRows g;
+    const uint16_t* x;        // routed: token rows gathered through slot_of_row; dense: rows xrow0+
+    int x_gather;
+    int xrow0;
+    const int32_t* slot_of_row;
+    int grow0;                // global row of the macrobatch's first row
+    int k, S;
+    const uint16_t* w_gate;   // [E, I, H]
+    const uint16_t* w_up;
+    int H, I;
+    uint16_t* g_out;          // saved g, row (save_row0 + local row)
+    uint16_t* u_out;
+    int save_row0;
+    uint16_t* h_out;          // ring h, local rows
+};
+
+struct GemmDownArgs {
+    GroupRows g;
+    const uint16_t* h;        // ring h [rows, I]
+    const uint16_t* w_down;   // [E, H, I]
+    int H, I;
+    uint16_t* o;              // ring o [rows, H]
+};
+
+struct GemmDownDgradArgs {
+    GroupRows g;
+    const uint16_t* dy;
+    int dy_gather;
+    int dyrow0;
+    const int32_t* slot_of_row;
+    int grow0, k, S;
+    const float* topk_w;      // nullptr: weight 1 (shared expert)
+    const uint16_t* w_down;
+    int H, I;
+    const uint16_t* g_saved;
+    const uint16_t* u_saved;
+    int save_row0;
+    uint16_t* dgu;            // ring [rows, 2I]: dg | du
+    uint16_t* hw;             // ring [rows, I]: w * h
+    float* dw_part;           // ring [rows, P] or nullptr
+    int P;
+};
+
+struct GemmGuDgradArgs {
+    GroupRows g;
+    const uint16_t* dgu;
+    const uint16_t* w_gate;
+    const uint16_t* w_up;
+    int H, I;
+    uint16_t* dx;             // ring [rows, H]
+};
+
+struct WgradOut {
+    uint16_t* out;            // bf16 result
+    float* acc;               // fp32 running sum across macrobatches
+    int mode;                 // 0 bf16; 1 write fp32; 2 add fp32; 3 add fp32 and write bf16
+};
+
+struct WgradDownArgs {
+    GroupRows g;
+    const uint16_t* dy;
+    int dy_gather, dyrow0;
+    const int32_t* slot_of_row;
+    int grow0, k, S;
+    const uint16_t* hw;
+    int H, I;
+    WgradOut out;
+};
+
+struct WgradGateUpArgs {
+    GroupRows g;
+    const uint16_t* dgu;
+    const uint16_t* x;
+    int x_gather, xrow0;
+    const int32_t* slot_of_row;
+    int grow0, k, S;
+    int H, I;
+    WgradOut out_gate, out_up;
+};
+
+// route_sched.hip
+int launch_topk_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
+                      hipStream_t st);
+int launch_schedule(const int32_t* idx, int T, int E, int k, int M, int mb, int32_t* hist,
+                    int32_t* base, int32_t* counts, int32_t* offsets, int32_t* mini_counts,
+                    int32_t* row_of_slot, int32_t* slot_of_row, int32_t* err, hipStream_t st);
+size_t schedule_hist_ints(int T, int E, int k, int M, int mb);
+
+// elementwise.hip
+int launch_dispatch(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
+                    int ring_row0, int ring_rows, void* ring, int32_t* err, hipStream_t st);
+int launch_combine(const void* o, int H, const int32_t* row_of_slot, const float* w, int t0, int t1,
+                   int k, int ring_row0, int ring_rows, const void* shared, int shared_t0, void* y,
+                   int32_t* err, hipStream_t st);
+int launch_rd_reduce(const void* dxd, int H, const int32_t* row_of_slot, int t0, int t1, int k,
+                     int ring_row0, int ring_rows, const void* shared, int shared_t0, void* dx,
+                     int32_t* err, hipStream_t st);
+int launch_softmax_bwd(const float* part, int P, const int32_t* row_of_slot, const int32_t* idx,
+                       const float* w, int t0, int t1, int k, int E, int ring_row0, int ring_rows,
+                       float* dw, float* d_logits, int32_t* err, hipStream_t st);
+int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
+                       int32_t* err, hipStream_t st);
+
+// gemm.hip
+int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st);
+int launch_gemm_down(const GemmDownArgs& a, hipStream_t st);
+int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st);
+int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st);
+int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st);
+int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st);
+int gemm_row_tile();
+int dgrad_col_tiles(int I);
+
+}  // namespace moe

@@ -1,0 +1,88 @@
+"""Shared helpers for the GPU parity tests: seeded inputs on both sides, one
+call sequence through the C ABI, and the comparisons against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth_inputs as si
+from mixture_experts_layer_dispatch_amd import binding as B
+
+BF16_TOL = 1e-2       # max |gpu - ref| <= BF16_TOL * max |ref|
+
+
+def cfg_of(shape: si.MoEShape) -> B.Config:
+    return B.Config(T=shape.T, H=shape.H, I=shape.I, E=shape.E, k=shape.k,
+                    n_shared=shape.n_shared, macrobatch=shape.macrobatch,
+                    minibatch=shape.minibatch)
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy()
+
+
+def assert_close(name, gpu, ref, tol=BF16_TOL):
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert gpu.shape == ref.shape, (name, gpu.shape, ref.shape)
+    scale = float(np.max(np.abs(ref))) if ref.size else 0.0
+    err = float(np.max(np.abs(gpu - ref))) if ref.size else 0.0
+    assert np.all(np.isfinite(gpu)), name
+    assert err <= tol * max(scale, 1e-30), f"{name}: max err {err:.3e} vs {tol} * {scale:.3e}"
+    return err / max(scale, 1e-30)
+
+
+class Case:
+    """Inputs of one shape on the GPU, and the CPU copies the oracle reads."""
+
+    def __init__(self, shape: si.MoEShape, logits_override=None, with_backward=True):
+        self.shape = shape
+        self.cfg = cfg_of(shape)
+        dev = "cuda"
+        self.logits = logits_override.to(dev) if logits_override is not None else si.logits(shape, dev)
+        self.x = si.tokens(shape, dev)
+        self.wg, self.wu, self.wd = si.all_expert_weights(shape, dev)
+        sh = si.shared_weights(shape, dev)
+        self.sw = sh
+        self.dy = si.grad_out(shape, dev) if with_backward else None
+        self.weights = {"w_gate": self.wg, "w_up": self.wu, "w_down": self.wd}
+        if sh is not None:
+            self.weights.update({"s_gate": sh[0], "s_up": sh[1], "s_down": sh[2]})
+        self.ws = B.alloc_workspace(self.cfg)
+        self.sched = B.alloc_schedule(self.cfg)
+        self.saved = B.alloc_saved(self.cfg)
+        self.y = torch.empty(shape.T, shape.H, dtype=torch.bfloat16, device=dev)
+
+    # ------------------------------------------------------------- GPU calls
+    def schedule(self):
+        B.moe_schedule(self.cfg, self.logits, self.sched, self.ws)
+
+    def forward(self):
+        B.moe_forward(self.cfg, self.sched, self.x, self.weights, self.y, self.saved, self.ws)
+
+    def backward(self):
+        c = self.cfg
+        self.dx = torch.empty_like(self.x)
+        self.grads = B.alloc_grads(c)
+        self.dw = torch.empty(c.T, c.k, dtype=torch.float32, device="cuda")
+        self.dlogits = torch.empty(c.T, c.E, dtype=torch.float32, device="cuda")
+        B.moe_backward(c, self.sched, self.saved, self.x, self.weights, self.dy, self.dx,
+                       self.grads, self.dw, self.dlogits, self.ws)
+
+    # ------------------------------------------------------------- oracle side
+    def oracle_schedule(self):
+        L = f32(self.logits)
+        idx, w = oracle.route(L, self.shape.k)
+        sch = oracle.schedule(idx, self.shape.E, self.shape.macrobatch, self.shape.minibatch)
+        return idx, w, sch
+
+    def expert_view(self, t: torch.Tensor):
+        """Lazy per-expert float32 numpy view of a device weight tensor."""
+        class _V:
+            def __getitem__(_, e):
+                return f32(t[int(e)])
+        return _V()
+
+    def shared_np(self):
+        return None if self.sw is None else tuple(f32(a) for a in self.sw)

@@ -1,0 +1,119 @@
+"""The C ABI on the host: the library loads, exports every entry point that
+include/moe.h declares, and validates arguments with exact status codes
+before touching any device (no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mixture_experts_layer_dispatch_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            names += re.findall(r"^MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared()
+    assert len(declared) >= 9
+    L = B.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert set(declared) == set(B.EXPORTED)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert B.status_string(s)
+    assert "gfx950" in B.status_string(B.MOE_ERR_UNSUPPORTED_DEVICE)
+
+
+def _cfg(**kw):
+    base = dict(T=256, H=256, I=128, E=8, k=2)
+    base.update(kw)
+    return B.Config(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    ({}, B.MOE_OK),
+    ({"T": 0}, B.MOE_ERR_INVALID_ARG),
+    ({"H": 200}, B.MOE_ERR_INVALID_ARG),          # H must be a multiple of 128
+    ({"I": 64}, B.MOE_ERR_INVALID_ARG),
+    ({"E": 0}, B.MOE_ERR_INVALID_ARG),
+    ({"E": 2048}, B.MOE_ERR_INVALID_ARG),
+    ({"k": 9}, B.MOE_ERR_INVALID_ARG),            # k > E
+    ({"E": 64, "k": 33}, B.MOE_ERR_INVALID_ARG),  # k > 32
+    ({"n_shared": 2}, B.MOE_ERR_INVALID_ARG),
+    ({"macrobatch": 100}, B.MOE_ERR_INVALID_ARG),  # does not divide T
+    ({"macrobatch": 128, "minibatch": 48}, B.MOE_ERR_INVALID_ARG),
+    ({"macrobatch": 128, "minibatch": 64}, B.MOE_OK),
+    ({"macrobatch": 128, "capacity_rows": 255}, B.MOE_ERR_CAPACITY),  # < 128 * 2 rows
+    ({"macrobatch": 128, "capacity_rows": 256}, B.MOE_OK),
+    ({"capacity_rows": -1}, B.MOE_ERR_INVALID_ARG),
+    ({"precision": 7}, B.MOE_ERR_INVALID_ARG),
+])
+def test_config_validation(kw, status):
+    assert B.validate_config(_cfg(**kw)) == status
+
+
+def test_ring_rows_and_workspace():
+    one = _cfg()
+    assert B.ring_rows(one) == 256 * 2
+    two = _cfg(macrobatch=64)
+    assert B.ring_rows(two) == 2 * 64 * 2
+    assert B.ring_rows(_cfg(macrobatch=64, capacity_rows=1000)) == 1000
+    ws1 = B.workspace_size(one)
+    assert ws1 > 256 * 2 * (2 * 256 + 128) * 2          # at least the forward ring
+    big = B.Config(T=2048, H=4096, I=1024, E=512, k=10)
+    assert B.workspace_size(big) > 20480 * (2 * 4096 + 1024) * 2
+    with pytest.raises(B.MoEError):
+        B.workspace_size(_cfg(T=0))
+
+
+def test_entry_points_reject_bad_arguments_before_any_device_work():
+    L = B.lib()
+    cfg = _cfg().c()
+    fake = ctypes.c_void_p(1 << 20)        # never dereferenced: validation fails first
+    sched = B.moe_sched()
+    # null schedule arrays
+    assert L.moe_schedule(ctypes.byref(cfg), fake, ctypes.byref(sched), fake, 1 << 40, None) in (
+        B.MOE_ERR_INVALID_ARG, B.MOE_ERR_WORKSPACE)
+    # workspace too small
+    s_ok = B.moe_sched(*([1 << 20] * 7))
+    assert L.moe_schedule(ctypes.byref(cfg), fake, ctypes.byref(s_ok), fake, 16, None) == B.MOE_ERR_WORKSPACE
+    # misaligned workspace
+    assert L.moe_schedule(ctypes.byref(cfg), fake, ctypes.byref(s_ok), ctypes.c_void_p((1 << 20) + 8),
+                          1 << 40, None) == B.MOE_ERR_WORKSPACE
+    # bad config
+    bad = _cfg(k=99).c()
+    assert L.moe_forward(ctypes.byref(bad), ctypes.byref(s_ok), fake, None, fake, None, fake,
+                         1 << 40, None) == B.MOE_ERR_INVALID_ARG
+    # misaligned activations
+    w = B.moe_weights(*([1 << 20] * 6))
+    sv = B.moe_saved(*([1 << 20] * 4))
+    assert L.moe_forward(ctypes.byref(cfg), ctypes.byref(s_ok), ctypes.c_void_p((1 << 20) + 2),
+                         ctypes.byref(w), fake, ctypes.byref(sv), fake, 1 << 40,
+                         None) == B.MOE_ERR_INVALID_ARG
+    g = B.moe_grads(*([1 << 20] * 6))
+    assert L.moe_backward(ctypes.byref(cfg), ctypes.byref(s_ok), ctypes.byref(sv), fake,
+                          ctypes.byref(w), fake, fake, ctypes.byref(g), None, None, fake, 1 << 40,
+                          None) == B.MOE_ERR_INVALID_ARG      # dw is required
+    assert L.moe_check_device_error(None, 0, None, None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "mixture_experts_layer_dispatch_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fn in files:
+            if fn.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fn)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fn
+                assert "synth_inputs" not in text, fn
