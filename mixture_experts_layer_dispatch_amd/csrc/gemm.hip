@@ -35,7 +35,6 @@
 namespace moe {
 
 constexpr int kTK = 64;
-constexpr int kPitch = kTK + 8;
 
 // ================================================================ sources
 // Row-major operand whose tile rows are rows of memory (K contiguous).
@@ -133,9 +132,27 @@ struct KRowsGroupGather {
     }
 };
 
+// ================================================================ LDS tiles
+// A tile holds ROWS rows (M or N indices) by kTK reduction indices.
+//   KC (K contiguous in memory): stored [row][k], pitch kTK + 8; a fragment
+//      row is read as 16 bytes (one row, 8 consecutive k).
+//   KS (K is the slow memory axis): stored as it lies in memory, [k][row],
+//      pitch ROWS + 16, and read with the LDS transpose load, which hands each
+//      lane four consecutive k of one row.
+// Pitches: the 16 rows of a KC fragment land on 16 different 16-byte bank
+// groups (144-byte rows); for KS the eight k rows read by one 32-lane pass of
+// transpose loads land on disjoint 32-byte bank ranges (pitch = 16 mod 32).
+template <int ROWS, bool KS>
+struct Tile {
+    static constexpr int P = KS ? ROWS + 16 : kTK + 8;
+    static constexpr int SIZE = KS ? kTK * P : ROWS * P;
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
 // ================================================================ loaders
-// K-contiguous tile of ROWS rows: 16-byte chunks, 8 lanes per 128-byte row
-// segment.
+// KC tile: 16-byte chunks, 8 lanes per 128-byte row segment.
 template <int ROWS, class Src>
 struct LoadKC {
     static constexpr int PER = ROWS * (kTK / 8) / 256;
@@ -149,7 +166,7 @@ struct LoadKC {
             const int r = c >> 3, kc = c & 7;
             const uint16_t* b = src.row(r);
             p[q] = b ? b + kc * 8 : nullptr;
-            off[q] = r * kPitch + kc * 8;
+            off[q] = r * Tile<ROWS, false>::P + kc * 8;
         }
     }
     __device__ void load(int kt) {
@@ -163,64 +180,95 @@ struct LoadKC {
     }
 };
 
-__device__ __forceinline__ uint32_t half_of(const uint4& v, int j) {
-    const uint32_t w = j < 2 ? v.x : j < 4 ? v.y : j < 6 ? v.z : v.w;
-    return (j & 1) ? (w >> 16) : (w & 0xffffu);
-}
-
-// Tile whose reduction index is the slow memory axis: a unit is (k pair,
-// 8-row chunk); the two 16-byte loads of a pair are interleaved into eight
-// 32-bit words, one per tile row.
+// KS tile: copied as it lies in memory, 16 lanes per 256-byte k-row segment.
+// src.krow(k) points at the tile's first column in memory row k (or null =
+// zeros); src.col0 may be moved between tiles.
 template <int ROWS, class Src>
 struct LoadKS {
-    static constexpr int CH = ROWS / 8;
-    static constexpr int PER = (kTK / 2) * CH / 256;
+    static constexpr int CPR = ROWS / 8;
+    static constexpr int PER = kTK * CPR / 256;
     Src src;
-    int kp[PER], rc[PER];
-    uint4 lo[PER], hi[PER];
+    int kr[PER], cc[PER];
+    uint4 v[PER];
     __device__ explicit LoadKS(const Src& s) : src(s) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int u = threadIdx.x + 256 * q;
-            rc[q] = u % CH;
-            kp[q] = u / CH;
+            const int c = threadIdx.x + 256 * q;
+            kr[q] = c / CPR;
+            cc[q] = c % CPR;
         }
     }
     __device__ void load(int kt) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int k0 = kt * kTK + 2 * kp[q];
-            const uint16_t* a = src.krow(k0);
-            const uint16_t* b = src.krow(k0 + 1);
-            lo[q] = a ? *(const uint4*)(a + rc[q] * 8) : make_uint4(0, 0, 0, 0);
-            hi[q] = b ? *(const uint4*)(b + rc[q] * 8) : make_uint4(0, 0, 0, 0);
+            const uint16_t* a = src.krow(kt * kTK + kr[q]);
+            v[q] = a ? *(const uint4*)(a + cc[q] * 8) : make_uint4(0, 0, 0, 0);
         }
     }
     __device__ void store(uint16_t* s) const {
 #pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            uint32_t* d = (uint32_t*)(s + rc[q] * 8 * kPitch + 2 * kp[q]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) d[j * (kPitch / 2)] = half_of(lo[q], j) | (half_of(hi[q], j) << 16);
-        }
+        for (int q = 0; q < PER; ++q) *(uint4*)(s + kr[q] * Tile<ROWS, true>::P + cc[q] * 8) = v[q];
     }
 };
 
-// ================================================================ main loop
-template <int MB, int NB>
-__device__ __forceinline__ void mma_tile(const uint16_t* sA, const uint16_t* sB, int wm0, int wn0,
-                                         f32x4 (&acc)[MB][NB]) {
+// ================================================================ fragments
+// Natural K order (both operands KC): lane l holds k = ks + 8*(l>>4) + 0..7.
+__device__ __forceinline__ bf16x8 frag_kc(const uint16_t* s, int P, int rbase, int ks) {
     const int lane = lane_id();
-    const int lr = lane & 15, lk = (lane >> 4) * 8;
+    return *(const bf16x8*)(s + (rbase + (lane & 15)) * P + ks + (lane >> 4) * 8);
+}
+
+// Permuted K order, used whenever an operand is KS: lane group g = l>>4 holds
+// k = ks + 4g + {0..3} and ks + 16 + 4g + {0..3}.  The MFMA sums over k, so
+// the permutation is harmless as long as both operands use it.
+__device__ __forceinline__ bf16x8 frag_kc_perm(const uint16_t* s, int P, int rbase, int ks) {
+    const int lane = lane_id();
+    const uint16_t* p = s + (rbase + (lane & 15)) * P + ks + 4 * (lane >> 4);
+    const uint2 a = *(const uint2*)p;
+    const uint2 b = *(const uint2*)(p + 16);
+    const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
+    return *(const bf16x8*)&v;
+}
+
+// Transpose load of a 16-lane group: lane i receives element (i % 4) of the
+// 8-byte chunk addressed by lane 4r + i/4, for r = 0..3.  Lane j therefore
+// addresses k row ks + 4g + j/4 at columns rbase + 4*(j%4), and every lane ends
+// up with four consecutive k of row rbase + (lane & 15).
+__device__ __forceinline__ bf16x8 frag_ks(const uint16_t* s, int P, int rbase, int ks) {
+    const int lane = lane_id();
+    const int g = lane >> 4, j = lane & 15;
+    const uint16_t* p = s + (ks + 4 * g + (j >> 2)) * P + rbase + 4 * (j & 3);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * P));
+    const uint4 v = make_uint4(__builtin_bit_cast(uint2, a).x, __builtin_bit_cast(uint2, a).y,
+                               __builtin_bit_cast(uint2, b).x, __builtin_bit_cast(uint2, b).y);
+    return *(const bf16x8*)&v;
+}
+
+template <bool KS, bool PERM>
+__device__ __forceinline__ bf16x8 frag(const uint16_t* s, int P, int rbase, int ks) {
+    if constexpr (KS) return frag_ks(s, P, rbase, ks);
+    else if constexpr (PERM) return frag_kc_perm(s, P, rbase, ks);
+    else return frag_kc(s, P, rbase, ks);
+}
+
+// ================================================================ main loop
+// sA: TM rows (output rows), sB: TN rows (output columns).  The MFMA takes the
+// column operand first, so each lane's four accumulators are four consecutive
+// output columns.
+template <int TM, int TN, bool AKS, bool BKS>
+__device__ __forceinline__ void mma_tile(const uint16_t* sA, const uint16_t* sB, int wm0, int wn0,
+                                         f32x4 (&acc)[TM / 32][TN / 32]) {
+    constexpr int MB = TM / 32, NB = TN / 32;
+    constexpr bool PERM = AKS || BKS;
+    constexpr int PA = Tile<TM, AKS>::P, PB = Tile<TN, BKS>::P;
 #pragma unroll
     for (int ks = 0; ks < kTK; ks += 32) {
         bf16x8 fb[MB], fa[NB];
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-            fb[mb] = *(const bf16x8*)(sA + (wm0 + mb * 16 + lr) * kPitch + ks + lk);
+        for (int mb = 0; mb < MB; ++mb) fb[mb] = frag<AKS, PERM>(sA, PA, wm0 + mb * 16, ks);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb)
-            fa[nb] = *(const bf16x8*)(sB + (wn0 + nb * 16 + lr) * kPitch + ks + lk);
+        for (int nb = 0; nb < NB; ++nb) fa[nb] = frag<BKS, PERM>(sB, PB, wn0 + nb * 16, ks);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -228,23 +276,36 @@ __device__ __forceinline__ void mma_tile(const uint16_t* sA, const uint16_t* sB,
     }
 }
 
-template <int TM, int TN, class LA, class LB>
+template <int TM, int TN>
+__device__ __forceinline__ void zero_acc(f32x4 (&acc)[TM / 32][TN / 32]) {
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < TN / 32; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+}
+
+template <int TM, int TN, bool AKS, bool BKS>
+struct Smem {
+    static constexpr int A = Tile<TM, AKS>::SIZE;
+    static constexpr int B = Tile<TN, BKS>::SIZE;
+    static constexpr int STAGE = A + B;
+};
+
+// Double-buffered K loop, one barrier per step.
+template <int TM, int TN, bool AKS, bool BKS, class LA, class LB>
 __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
                                          f32x4 (&acc)[TM / 32][TN / 32]) {
-    constexpr int MB = TM / 32, NB = TN / 32;
+    using SM = Smem<TM, TN, AKS, BKS>;
     const int w = threadIdx.x >> 6;
     const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
-#pragma unroll
-    for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    zero_acc<TM, TN>(acc);
     if (nk <= 0) return;
     uint16_t* buf0 = smem;
-    uint16_t* buf1 = smem + (TM + TN) * kPitch;
+    uint16_t* buf1 = smem + SM::STAGE;
     la.load(0);
     lb.load(0);
     la.store(buf0);
-    lb.store(buf0 + TM * kPitch);
+    lb.store(buf0 + SM::A);
     __syncthreads();
     for (int kt = 0; kt < nk; ++kt) {
         uint16_t* cur = (kt & 1) ? buf1 : buf0;
@@ -254,10 +315,10 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
             la.load(kt + 1);
             lb.load(kt + 1);
         }
-        mma_tile<MB, NB>(cur, cur + TM * kPitch, wm0, wn0, acc);
+        mma_tile<TM, TN, AKS, BKS>(cur, cur + SM::A, wm0, wn0, acc);
         if (more) {
             la.store(nxt);
-            lb.store(nxt + TM * kPitch);
+            lb.store(nxt + SM::A);
         }
         __syncthreads();
     }
@@ -343,7 +404,7 @@ __device__ __forceinline__ bool map_ktile(const GroupRows& g, int nMt, int nNt, 
 constexpr int G1_TM = 64, G1_TN = 128;
 
 __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G1_TM + G1_TN) * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G1_TM, G1_TN, false, false>::STAGE];
     int e, lo, hi, nt;
     if (!map_mtile<G1_TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
     const int i0 = nt * 64;
@@ -356,11 +417,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
     if (a.x_gather) {
         RowsGather sa{a.x, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
         LoadKC<G1_TM, RowsGather> la(sa);
-        mainloop<G1_TM, G1_TN>(la, lb, nk, smem, acc);
+        mainloop<G1_TM, G1_TN, false, false>(la, lb, nk, smem, acc);
     } else {
         RowsDirect sa{a.x, a.H, a.xrow0 + lo, hi - lo};
         LoadKC<G1_TM, RowsDirect> la(sa);
-        mainloop<G1_TM, G1_TN>(la, lb, nk, smem, acc);
+        mainloop<G1_TM, G1_TN, false, false>(la, lb, nk, smem, acc);
     }
     AccPos<G1_TM, G1_TN> pos;
     const int wn = threadIdx.x >> 7;
@@ -391,7 +452,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
 constexpr int G2_TM = 64, G2_TN = 128;
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G2_TM + G2_TN) * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G2_TM, G2_TN, false, false>::STAGE];
     int e, lo, hi, nt;
     if (!map_mtile<G2_TM>(a.g, a.H / G2_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * G2_TN;
@@ -400,7 +461,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
     LoadKC<G2_TM, RowsDirect> la(sa);
     RowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, G2_TN};
     LoadKC<G2_TN, RowsDirect> lb(sb);
-    mainloop<G2_TM, G2_TN>(la, lb, a.I / kTK, smem, acc);
+    mainloop<G2_TM, G2_TN, false, false>(la, lb, a.I / kTK, smem, acc);
     AccPos<G2_TM, G2_TN> pos;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -426,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
 constexpr int G3_TM = 64, G3_TN = 128;
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G3_TM + G3_TN) * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G3_TM, G3_TN, false, true>::STAGE];
     __shared__ float red[2][G3_TM];
     int e, lo, hi, nt;
     if (!map_mtile<G3_TM>(a.g, a.I / G3_TN, blockIdx.x, e, lo, hi, nt)) return;
@@ -437,11 +498,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a)
     if (a.dy_gather) {
         RowsGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
         LoadKC<G3_TM, RowsGather> la(sa);
-        mainloop<G3_TM, G3_TN>(la, lb, a.H / kTK, smem, acc);
+        mainloop<G3_TM, G3_TN, false, true>(la, lb, a.H / kTK, smem, acc);
     } else {
         RowsDirect sa{a.dy, a.H, a.dyrow0 + lo, hi - lo};
         LoadKC<G3_TM, RowsDirect> la(sa);
-        mainloop<G3_TM, G3_TN>(la, lb, a.H / kTK, smem, acc);
+        mainloop<G3_TM, G3_TN, false, true>(la, lb, a.H / kTK, smem, acc);
     }
     AccPos<G3_TM, G3_TN> pos;
     const int lane = lane_id();
@@ -509,7 +570,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a)
 constexpr int G4_TM = 64, G4_TN = 128;
 
 __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (G4_TM + G4_TN) * kPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G4_TM, G4_TN, false, true>::STAGE];
     int e, lo, hi, nt;
     if (!map_mtile<G4_TM>(a.g, a.H / G4_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * G4_TN;
@@ -518,7 +579,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
     LoadKC<G4_TM, RowsDirect> la(sa);
     KRowsGateUp sb{a.w_gate + (int64_t)e * a.I * a.H, a.w_up + (int64_t)e * a.I * a.H, a.H, n0, a.I};
     LoadKS<G4_TN, KRowsGateUp> lb(sb);
-    mainloop<G4_TM, G4_TN>(la, lb, 2 * a.I / kTK, smem, acc);
+    mainloop<G4_TM, G4_TN, false, true>(la, lb, 2 * a.I / kTK, smem, acc);
     AccPos<G4_TM, G4_TN> pos;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
@@ -533,7 +594,63 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
     }
 }
 
-// ================================================================ weight-gradient epilogue
+// ================================================================ weight gradients
+// K-grouped: C_e[M, N] = sum over e's rows (ascending) of A[r, M] (x) B[r, N];
+// both operands are KS tiles.  A block owns one expert's 128-row slab of C and
+// W_NPW consecutive 64-column tiles of it.  When the expert has at most kTK
+// rows (one K step, the common case for small token counts) the A tile stays
+// in LDS for all of them and the next B tile is fetched while the current one
+// is multiplied; otherwise each column tile runs the K loop.
+constexpr int W_TM = 128, W_TN = 64, W_NPW = 16;
+
+template <class SA, class SB, class Epi>
+__device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
+                                            int nt0, int ntn, uint16_t* smem, const Epi& epi) {
+    using SM = Smem<W_TM, W_TN, true, true>;
+    uint16_t* sA = smem;
+    uint16_t* sB = smem + SM::A;
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (W_TM / 2), wn0 = (w >> 1) * (W_TN / 2);
+    f32x4 acc[W_TM / 32][W_TN / 32];
+    if (nk <= 1) {
+        lb.src.col0 = nt0 * W_TN;
+        if (nk == 1) {
+            la.load(0);
+            lb.load(0);
+            la.store(sA);
+        }
+        for (int i = 0; i < ntn; ++i) {
+            zero_acc<W_TM, W_TN>(acc);
+            if (nk == 1) {
+                lb.store(sB);
+                __syncthreads();
+                if (i + 1 < ntn) {
+                    lb.src.col0 = (nt0 + i + 1) * W_TN;
+                    lb.load(0);
+                }
+                mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
+                __syncthreads();
+            }
+            epi(nt0 + i, acc);
+        }
+        return;
+    }
+    for (int i = 0; i < ntn; ++i) {
+        lb.src.col0 = (nt0 + i) * W_TN;
+        zero_acc<W_TM, W_TN>(acc);
+        for (int kt = 0; kt < nk; ++kt) {
+            la.load(kt);
+            lb.load(kt);
+            la.store(sA);
+            lb.store(sB);
+            __syncthreads();
+            mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
+            __syncthreads();
+        }
+        epi(nt0 + i, acc);
+    }
+}
+
 // mode: 0 write bf16; 1 write fp32 partial; 2 add to fp32 partial;
 //       3 add to fp32 partial and write bf16 (the last macrobatch of the walk)
 __device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, const f32x4& v) {
@@ -546,68 +663,66 @@ __device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, cons
     else *(uint2*)(o.out + idx) = pack4(x0, x1, x2, x3);
 }
 
-// ================================================================ backward: down wgrad
-// dW_down[e][h, i] = sum over e's rows r (ascending) of dy[tok(r), h] * hw[r, i].
-constexpr int W_TM = 128, W_TN = 128;
+struct WgradEpi {
+    WgradOut out;
+    int64_t ebase;   // first element of the expert's matrix
+    int64_t ld;      // row length of the output matrix
+    int m0;          // first output row of the slab
+    __device__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32]) const {
+        AccPos<W_TM, W_TN> pos;
+        const int n0 = nt * W_TN;
+#pragma unroll
+        for (int mb = 0; mb < W_TM / 32; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < W_TN / 32; ++nb)
+                wgrad_store(out, ebase + (int64_t)(m0 + pos.m(mb)) * ld + n0 + pos.n(nb), acc[mb][nb]);
+    }
+};
 
-__global__ __launch_bounds__(256, 2) void k_wgrad_down(WgradDownArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (W_TM + W_TN) * kPitch];
-    int e, mt, nt, lo, n;
-    if (!map_ktile(a.g, a.H / W_TM, a.I / W_TN, blockIdx.x, e, mt, nt, lo, n)) return;
-    const int m0 = mt * W_TM, n0 = nt * W_TN;
-    f32x4 acc[4][4];
+// dW_down[e][h, i] = sum over e's rows r of dy[tok(r), h] * hw[r, i].
+__global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[Smem<W_TM, W_TN, true, true>::STAGE];
+    const int ntiles = a.I / W_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    int e, mt, ng, lo, n;
+    if (!map_ktile(a.g, a.H / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
+    const int m0 = mt * W_TM;
     const int nk = (n + kTK - 1) / kTK;
-    KRowsGroup sb{a.hw, a.I, lo, n, n0};
+    KRowsGroup sb{a.hw, a.I, lo, n, 0};
     LoadKS<W_TN, KRowsGroup> lb(sb);
+    WgradEpi epi{a.out, (int64_t)e * a.H * a.I, a.I, m0};
     if (a.dy_gather) {
         KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
         LoadKS<W_TM, KRowsGroupGather> la(sa);
-        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
     } else {
         KRowsGroup sa{a.dy, a.H, a.dyrow0 + lo, n, m0};
         LoadKS<W_TM, KRowsGroup> la(sa);
-        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
     }
-    AccPos<W_TM, W_TN> pos;
-    const int64_t ebase = (int64_t)e * a.H * a.I;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            wgrad_store(a.out, ebase + (int64_t)(m0 + pos.m(mb)) * a.I + n0 + pos.n(nb), acc[mb][nb]);
 }
 
-// ================================================================ backward: gate/up wgrad
 // dW_gate[e][i, h] = sum_r dg[r, i] x[tok(r), h]; dW_up likewise with du.
 // M runs over the 2I columns of [dg | du].
-__global__ __launch_bounds__(256, 2) void k_wgrad_gate_up(WgradGateUpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * (W_TM + W_TN) * kPitch];
-    int e, mt, nt, lo, n;
-    if (!map_ktile(a.g, 2 * a.I / W_TM, a.H / W_TN, blockIdx.x, e, mt, nt, lo, n)) return;
-    const int m0 = mt * W_TM, n0 = nt * W_TN;
-    f32x4 acc[4][4];
+__global__ __launch_bounds__(256, 4) void k_wgrad_gate_up(WgradGateUpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[Smem<W_TM, W_TN, true, true>::STAGE];
+    const int ntiles = a.H / W_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    int e, mt, ng, lo, n;
+    if (!map_ktile(a.g, 2 * a.I / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
+    const int m0 = mt * W_TM;
     const int nk = (n + kTK - 1) / kTK;
+    const bool up = m0 >= a.I;
     KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};
     LoadKS<W_TM, KRowsGroup> la(sa);
+    WgradEpi epi{up ? a.out_up : a.out_gate, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0};
     if (a.x_gather) {
-        KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, n0, a.k, a.S, a.g.err};
+        KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, 0, a.k, a.S, a.g.err};
         LoadKS<W_TN, KRowsGroupGather> lb(sb);
-        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
     } else {
-        KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, n0};
+        KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, 0};
         LoadKS<W_TN, KRowsGroup> lb(sb);
-        mainloop<W_TM, W_TN>(la, lb, nk, smem, acc);
+        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
     }
-    AccPos<W_TM, W_TN> pos;
-    const bool up = m0 >= a.I;
-    const WgradOut& o = up ? a.out_up : a.out_gate;
-    const int mrow0 = up ? m0 - a.I : m0;
-    const int64_t ebase = (int64_t)e * a.I * a.H;
-#pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            wgrad_store(o, ebase + (int64_t)(mrow0 + pos.m(mb)) * a.H + n0 + pos.n(nb), acc[mb][nb]);
 }
 
 // ================================================================ launchers
@@ -652,14 +767,14 @@ int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
 
 int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_down");
-    const int grid = (a.g.offsets ? a.g.E : 1) * (a.H / W_TM) * (a.I / W_TN);
+    const int grid = (a.g.offsets ? a.g.E : 1) * (a.H / W_TM) * ((a.I / W_TN + W_NPW - 1) / W_NPW);
     k_wgrad_down<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_gate_up");
-    const int grid = (a.g.offsets ? a.g.E : 1) * (2 * a.I / W_TM) * (a.H / W_TN);
+    const int grid = (a.g.offsets ? a.g.E : 1) * (2 * a.I / W_TM) * ((a.H / W_TN + W_NPW - 1) / W_NPW);
     k_wgrad_gate_up<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
