@@ -42,7 +42,30 @@ def parse():
                     help="tokens in the CPU oracle's sample (forward + input gradients)")
     ap.add_argument("--cpu-experts", type=int, default=2,
                     help="experts in the CPU oracle's sample (weight gradients)")
+    ap.add_argument("--calibrate", action="store_true",
+                    help="only time plain HBM copy / fill / read kernels of known size and exit")
     return ap.parse_args()
+
+
+def calibrate(torch, nbytes=4 << 30, reps=10):
+    """Bandwidth of plain torch copy, fill and sum kernels on buffers of known size."""
+    a = torch.empty(nbytes // 2, dtype=torch.bfloat16, device="cuda").normal_()
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes),
+                            ("fill", lambda: b.fill_(1.0), nbytes),
+                            ("sum", lambda: a.sum(dtype=torch.float32), nbytes)):
+        fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / reps
+        out[name] = {"bytes": moved, "avg_ms": round(ms, 4), "GB/s": round(moved / ms / 1e6, 1)}
+    return out
 
 
 def kernel_bytes(shape, counts: np.ndarray) -> dict:
@@ -123,6 +146,9 @@ def main():
     if not B.device_supported():
         print("the library requires gfx950 (MI355X)", file=sys.stderr)
         sys.exit(1)
+    if args.calibrate:
+        print(json.dumps({"hbm_calibration": calibrate(torch)}), flush=True)
+        return
 
     shape = si.SHAPES[args.workload]
     T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k

@@ -209,6 +209,18 @@ struct LoadKS {
 #pragma unroll
         for (int q = 0; q < PER; ++q) *(uint4*)(s + kr[q] * Tile<ROWS, true>::P + cc[q] * 8) = v[q];
     }
+    // Row pointers of K step kt at column 0, kept for loads that only move
+    // the column window (src.col0 must be 0 when this is called).
+    const uint16_t* rp[PER];
+    __device__ void cache_rows(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) rp[q] = src.krow(kt * kTK + kr[q]);
+    }
+    __device__ void load_cached(int col) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            v[q] = rp[q] ? *(const uint4*)(rp[q] + col + cc[q] * 8) : make_uint4(0, 0, 0, 0);
+    }
 };
 
 // ================================================================ fragments
@@ -597,41 +609,46 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
 // ================================================================ weight gradients
 // K-grouped: C_e[M, N] = sum over e's rows (ascending) of A[r, M] (x) B[r, N];
 // both operands are KS tiles.  A block owns one expert's 128-row slab of C and
-// W_NPW consecutive 64-column tiles of it.  When the expert has at most kTK
+// up to W_NPW consecutive 64-column tiles of it (whole rows for N <= 4096, so
+// each block writes one contiguous region).  When the expert has at most kTK
 // rows (one K step, the common case for small token counts) the A tile stays
 // in LDS for all of them and the next B tile is fetched while the current one
 // is multiplied; otherwise each column tile runs the K loop.
-constexpr int W_TM = 128, W_TN = 64, W_NPW = 16;
+constexpr int W_TM = 128, W_TN = 64, W_NPW = 64;
+
+// LDS of a weight-gradient block: the resident A tile, then a region that
+// holds the B tile during the MFMAs and the bf16 output tile afterwards.
+constexpr int W_SP = W_TN + 8;                                    // staging pitch
+constexpr int W_REGION = (W_TM * W_SP > Tile<W_TN, true>::SIZE) ? W_TM * W_SP : Tile<W_TN, true>::SIZE;
+constexpr int W_SMEM = Tile<W_TM, true>::SIZE + W_REGION;
 
 template <class SA, class SB, class Epi>
 __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
                                             int nt0, int ntn, uint16_t* smem, const Epi& epi) {
-    using SM = Smem<W_TM, W_TN, true, true>;
     uint16_t* sA = smem;
-    uint16_t* sB = smem + SM::A;
+    uint16_t* sB = smem + Tile<W_TM, true>::SIZE;
     const int w = threadIdx.x >> 6;
     const int wm0 = (w & 1) * (W_TM / 2), wn0 = (w >> 1) * (W_TN / 2);
     f32x4 acc[W_TM / 32][W_TN / 32];
     if (nk <= 1) {
-        lb.src.col0 = nt0 * W_TN;
         if (nk == 1) {
             la.load(0);
-            lb.load(0);
+            lb.src.col0 = 0;
+            lb.cache_rows(0);
+            lb.load_cached(nt0 * W_TN);
             la.store(sA);
         }
         for (int i = 0; i < ntn; ++i) {
             zero_acc<W_TM, W_TN>(acc);
             if (nk == 1) {
+                if (i > 0) __syncthreads();          // the staged tile has been written out
                 lb.store(sB);
                 __syncthreads();
-                if (i + 1 < ntn) {
-                    lb.src.col0 = (nt0 + i + 1) * W_TN;
-                    lb.load(0);
-                }
+                if (i + 1 < ntn) lb.load_cached((nt0 + i + 1) * W_TN);
                 mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
                 __syncthreads();
             }
-            epi(nt0 + i, acc);
+            epi(nt0 + i, acc, sB);
         }
         return;
     }
@@ -647,7 +664,8 @@ __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, S
             mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
             __syncthreads();
         }
-        epi(nt0 + i, acc);
+        epi(nt0 + i, acc, sB);
+        __syncthreads();
     }
 }
 
@@ -668,20 +686,42 @@ struct WgradEpi {
     int64_t ebase;   // first element of the expert's matrix
     int64_t ld;      // row length of the output matrix
     int m0;          // first output row of the slab
-    __device__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32]) const {
+    // bf16 output (mode 0) goes through LDS so that every global store writes
+    // whole 128-byte row segments; the fp32 accumulation modes store directly.
+    __device__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32],
+                               uint16_t* stage) const {
         AccPos<W_TM, W_TN> pos;
         const int n0 = nt * W_TN;
+        if (out.mode != 0) {
+#pragma unroll
+            for (int mb = 0; mb < W_TM / 32; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < W_TN / 32; ++nb)
+                    wgrad_store(out, ebase + (int64_t)(m0 + pos.m(mb)) * ld + n0 + pos.n(nb), acc[mb][nb]);
+            return;
+        }
 #pragma unroll
         for (int mb = 0; mb < W_TM / 32; ++mb)
 #pragma unroll
-            for (int nb = 0; nb < W_TN / 32; ++nb)
-                wgrad_store(out, ebase + (int64_t)(m0 + pos.m(mb)) * ld + n0 + pos.n(nb), acc[mb][nb]);
+            for (int nb = 0; nb < W_TN / 32; ++nb) {
+                const f32x4 v = acc[mb][nb];
+                *(uint2*)(stage + pos.m(mb) * W_SP + pos.n(nb)) = pack4(v[0], v[1], v[2], v[3]);
+            }
+        __syncthreads();
+        constexpr int CPR = W_TN / 8;                  // 16-byte chunks per row
+#pragma unroll
+        for (int q = 0; q < W_TM * CPR / 256; ++q) {
+            const int c = threadIdx.x + 256 * q;
+            const int r = c / CPR, cc = c % CPR;
+            *(uint4*)(out.out + ebase + (int64_t)(m0 + r) * ld + n0 + cc * 8) =
+                *(const uint4*)(stage + r * W_SP + cc * 8);
+        }
     }
 };
 
 // dW_down[e][h, i] = sum over e's rows r of dy[tok(r), h] * hw[r, i].
 __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[Smem<W_TM, W_TN, true, true>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[W_SMEM];
     const int ntiles = a.I / W_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
     int e, mt, ng, lo, n;
     if (!map_ktile(a.g, a.H / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
@@ -703,8 +743,8 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
 
 // dW_gate[e][i, h] = sum_r dg[r, i] x[tok(r), h]; dW_up likewise with du.
 // M runs over the 2I columns of [dg | du].
-__global__ __launch_bounds__(256, 4) void k_wgrad_gate_up(WgradGateUpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[Smem<W_TM, W_TN, true, true>::STAGE];
+__global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[W_SMEM];
     const int ntiles = a.H / W_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
     int e, mt, ng, lo, n;
     if (!map_ktile(a.g, 2 * a.I / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
