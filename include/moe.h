@@ -102,7 +102,31 @@ typedef struct moe_sched {
     int32_t* slot_of_row;  /* [S]  inverse permutation                                */
 } moe_sched;
 
-/* bf16 weights.  The shared expert's pointers are read only if n_shared. */
+/* MXFP8 weights (written by moe_quantize_weights_mxfp8): E4M3 codes (one
+ * byte each) and E8M0 scales (one byte per 32 codes along the listed axis).
+ * The forward reads the first three pairs; the backward's input gradients
+ * read the transposed copies ([ALPHA] 三: weights are quantised outside the
+ * timed region, so both orientations are prepared ahead of time). */
+typedef struct moe_weights_mx {
+    const void* w_gate_q;  const void* w_gate_s;   /* [E, I, H], [E, I, H/32]  blocks along H */
+    const void* w_up_q;    const void* w_up_s;     /* [E, I, H], [E, I, H/32]                 */
+    const void* w_down_q;  const void* w_down_s;   /* [E, H, I], [E, H, I/32]  blocks along I */
+    const void* w_gate_tq; const void* w_gate_ts;  /* [E, H, I], [E, H, I/32]  W_gate^T, along I */
+    const void* w_up_tq;   const void* w_up_ts;    /* [E, H, I], [E, H, I/32]  W_up^T           */
+    const void* w_down_tq; const void* w_down_ts;  /* [E, I, H], [E, I, H/32]  W_down^T, along H */
+    /* the shared expert (if n_shared): the same twelve arrays without the E axis */
+    const void* s_gate_q;  const void* s_gate_s;
+    const void* s_up_q;    const void* s_up_s;
+    const void* s_down_q;  const void* s_down_s;
+    const void* s_gate_tq; const void* s_gate_ts;
+    const void* s_up_tq;   const void* s_up_ts;
+    const void* s_down_tq; const void* s_down_ts;
+} moe_weights_mx;
+
+/* Weights.  bf16 arrays are always given (the MXFP8 backward writes bf16
+ * gradients of them and the quantiser reads them); `mx` is required when
+ * cfg->precision is MOE_PREC_MXFP8 and ignored otherwise.  The shared
+ * expert's pointers are read only if n_shared. */
 typedef struct moe_weights {
     const void* w_gate;    /* [E, I, H] */
     const void* w_up;      /* [E, I, H] */
@@ -110,6 +134,7 @@ typedef struct moe_weights {
     const void* s_gate;    /* [I, H]    */
     const void* s_up;      /* [I, H]    */
     const void* s_down;    /* [H, I]    */
+    const moe_weights_mx* mx;
 } moe_weights;
 
 /* What the forward keeps for the backward (bf16, rows in schedule row order). */
@@ -186,6 +211,16 @@ MOE_API moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, c
                         const void* x, const moe_weights* w, const void* dy, void* dx,
                         const moe_grads* grads, float* dw, float* d_logits,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* MXFP8 weight quantisation ([AREX] closing paragraph: weights are quantised
+ * ahead of time; [ALPHA] 三: outside the timed region).  Reads w's bf16 arrays
+ * and writes every array of *out (caller-allocated, sizes as listed in
+ * moe_weights_mx), along the OCP MX v1.0 rule: per 32-element block, scale
+ * 2^(floor(log2 max|v|) - 8) clamped to [2^-127, 2^127], elements rounded to
+ * nearest-even E4M3 and saturated to +-448.  Enqueued on `stream`; needs no
+ * workspace. */
+MOE_API moe_status moe_quantize_weights_mxfp8(const moe_config* cfg, const moe_weights* w,
+                                              const moe_weights_mx* out, void* stream);
 
 /* Reads and clears the sticky device error word that kernels set when a
  * caller-built schedule holds an out-of-range expert, slot or row (those

@@ -5,11 +5,12 @@ weighted combine, and the backward) runs in hand-written HIP kernels behind the
 C ABI declared in ``include/moe.h``; this package is the thin Python binding.
 """
 from .binding import (Config, MoEError, PREC_BF16, PREC_MXFP8, alloc_grads, alloc_saved,
-                      alloc_schedule, alloc_workspace, device_supported, lib, moe_backward,
-                      moe_check_device_error, moe_forward, moe_schedule, ring_rows,
-                      status_string, validate_config, workspace_size)
+                      alloc_schedule, alloc_weights_mx, alloc_workspace, device_supported, lib,
+                      moe_backward, moe_check_device_error, moe_forward,
+                      moe_quantize_weights_mxfp8, moe_schedule, ring_rows, status_string,
+                      validate_config, workspace_size)
 
 __all__ = ["Config", "MoEError", "PREC_BF16", "PREC_MXFP8", "alloc_grads", "alloc_saved",
-           "alloc_schedule", "alloc_workspace", "device_supported", "lib", "moe_backward",
-           "moe_check_device_error", "moe_forward", "moe_schedule", "ring_rows", "status_string",
+           "alloc_schedule", "alloc_weights_mx", "alloc_workspace", "device_supported", "lib", "moe_backward",
+           "moe_check_device_error", "moe_forward", "moe_quantize_weights_mxfp8", "moe_schedule", "ring_rows", "status_string",
            "validate_config", "workspace_size"]

@@ -30,7 +30,7 @@ PREC_MXFP8 = 1
 EXPORTED = [
     "moe_status_string", "moe_validate_config", "moe_ring_rows", "moe_workspace_size",
     "moe_device_supported", "moe_schedule", "moe_forward", "moe_backward",
-    "moe_check_device_error", "moe_profile_enable", "moe_profile_collect", "moe_profile_query",
+    "moe_check_device_error", "moe_quantize_weights_mxfp8", "moe_profile_enable", "moe_profile_collect", "moe_profile_query",
     "moe_profile_names", "moe_profile_reset",
 ]
 
@@ -55,9 +55,20 @@ class moe_sched(ctypes.Structure):
                  "slot_of_row")]
 
 
+MX_FIELDS = ("w_gate_q", "w_gate_s", "w_up_q", "w_up_s", "w_down_q", "w_down_s",
+             "w_gate_tq", "w_gate_ts", "w_up_tq", "w_up_ts", "w_down_tq", "w_down_ts",
+             "s_gate_q", "s_gate_s", "s_up_q", "s_up_s", "s_down_q", "s_down_s",
+             "s_gate_tq", "s_gate_ts", "s_up_tq", "s_up_ts", "s_down_tq", "s_down_ts")
+
+
+class moe_weights_mx(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in MX_FIELDS]
+
+
 class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")]
+                ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")] + [
+                ("mx", ctypes.POINTER(moe_weights_mx))]
 
 
 class moe_saved(ctypes.Structure):
@@ -94,6 +105,8 @@ def lib() -> ctypes.CDLL:
                                    ctypes.POINTER(moe_weights), vp, vp, ctypes.POINTER(moe_grads),
                                    vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_check_device_error.argtypes = [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_int32)]
+        L.moe_quantize_weights_mxfp8.argtypes = [cfgp, ctypes.POINTER(moe_weights),
+                                                 ctypes.POINTER(moe_weights_mx), vp]
         L.moe_profile_enable.argtypes = [ctypes.c_int]
         L.moe_profile_collect.argtypes = []
         L.moe_profile_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
@@ -227,9 +240,18 @@ def _sched(s: dict) -> moe_sched:
     return moe_sched(*[s[n].data_ptr() for n, _ in moe_sched._fields_])
 
 
-def _weights(w: dict) -> moe_weights:
-    return moe_weights(*[(w[n].data_ptr() if w.get(n) is not None else None)
-                         for n, _ in moe_weights._fields_])
+def _weights_mx(q: dict) -> moe_weights_mx:
+    return moe_weights_mx(*[(q[n].data_ptr() if q.get(n) is not None else None) for n in MX_FIELDS])
+
+
+def _weights(w: dict):
+    """(moe_weights, keep-alive); w may hold an "mx" dict of quantised arrays."""
+    mx = _weights_mx(w["mx"]) if w.get("mx") is not None else None
+    st = moe_weights(*[(w[n].data_ptr() if w.get(n) is not None else None)
+                       for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")])
+    if mx is not None:
+        st.mx = ctypes.pointer(mx)
+    return st, mx
 
 
 def _saved(s: dict) -> moe_saved:
@@ -250,18 +272,52 @@ def moe_schedule(cfg: Config, logits: torch.Tensor, sched: dict, ws: torch.Tenso
 
 def moe_forward(cfg: Config, sched: dict, x: torch.Tensor, weights: dict, y: torch.Tensor,
                 saved: dict, ws: torch.Tensor, stream=None):
+    wst, _keep = _weights(weights)
     _check(lib().moe_forward(ctypes.byref(cfg.c()), ctypes.byref(_sched(sched)), _p(x),
-                             ctypes.byref(_weights(weights)), _p(y), ctypes.byref(_saved(saved)),
+                             ctypes.byref(wst), _p(y), ctypes.byref(_saved(saved)),
                              _p(ws), ws.numel(), _stream(stream)), "moe_forward")
 
 
 def moe_backward(cfg: Config, sched: dict, saved: dict, x: torch.Tensor, weights: dict,
                  dy: torch.Tensor, dx: torch.Tensor, grads: dict, dw: torch.Tensor,
                  d_logits, ws: torch.Tensor, stream=None):
+    wst, _keep = _weights(weights)
     _check(lib().moe_backward(ctypes.byref(cfg.c()), ctypes.byref(_sched(sched)),
-                              ctypes.byref(_saved(saved)), _p(x), ctypes.byref(_weights(weights)),
+                              ctypes.byref(_saved(saved)), _p(x), ctypes.byref(wst),
                               _p(dy), _p(dx), ctypes.byref(_grads(grads)), _p(dw), _p(d_logits),
                               _p(ws), ws.numel(), _stream(stream)), "moe_backward")
+
+
+def alloc_weights_mx(cfg: Config, device="cuda") -> dict:
+    """Buffers of every quantised weight array (codes and scales, uint8)."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    u8 = dict(dtype=torch.uint8, device=device)
+    q = {
+        "w_gate_q": torch.empty(E, I, H, **u8), "w_gate_s": torch.empty(E, I, H // 32, **u8),
+        "w_up_q": torch.empty(E, I, H, **u8), "w_up_s": torch.empty(E, I, H // 32, **u8),
+        "w_down_q": torch.empty(E, H, I, **u8), "w_down_s": torch.empty(E, H, I // 32, **u8),
+        "w_gate_tq": torch.empty(E, H, I, **u8), "w_gate_ts": torch.empty(E, H, I // 32, **u8),
+        "w_up_tq": torch.empty(E, H, I, **u8), "w_up_ts": torch.empty(E, H, I // 32, **u8),
+        "w_down_tq": torch.empty(E, I, H, **u8), "w_down_ts": torch.empty(E, I, H // 32, **u8),
+    }
+    if cfg.n_shared:
+        q.update({
+            "s_gate_q": torch.empty(I, H, **u8), "s_gate_s": torch.empty(I, H // 32, **u8),
+            "s_up_q": torch.empty(I, H, **u8), "s_up_s": torch.empty(I, H // 32, **u8),
+            "s_down_q": torch.empty(H, I, **u8), "s_down_s": torch.empty(H, I // 32, **u8),
+            "s_gate_tq": torch.empty(H, I, **u8), "s_gate_ts": torch.empty(H, I // 32, **u8),
+            "s_up_tq": torch.empty(H, I, **u8), "s_up_ts": torch.empty(H, I // 32, **u8),
+            "s_down_tq": torch.empty(I, H, **u8), "s_down_ts": torch.empty(I, H // 32, **u8),
+        })
+    return q
+
+
+def moe_quantize_weights_mxfp8(cfg: Config, weights: dict, out: dict, stream=None):
+    wst, _keep = _weights(weights)
+    mx = _weights_mx(out)
+    _check(lib().moe_quantize_weights_mxfp8(ctypes.byref(cfg.c()), ctypes.byref(wst),
+                                            ctypes.byref(mx), _stream(stream)),
+           "moe_quantize_weights_mxfp8")
 
 
 def moe_check_device_error(ws: torch.Tensor, stream=None) -> int:

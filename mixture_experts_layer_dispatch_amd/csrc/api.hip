@@ -32,9 +32,11 @@ struct Layout {
     size_t err, hist, base, tile_off, ring, ring_half, sh, wacc, total;
     // offsets inside one ring half (bytes)
     size_t f_xd, f_h, f_o;            // forward
+    size_t f_xs, f_hs;                // MXFP8 forward: scales after the codes (codes at f_xd, f_h)
     size_t b_dgu, b_hw, b_dx, b_part; // backward
     // offsets inside the shared-expert region
     size_t s_h, s_o, s_dgu, s_hw, s_dx;
+    size_t s_xq, s_xs, s_hq, s_hs;    // MXFP8 shared expert
     size_t wacc_g, wacc_u, wacc_d, wacc_sg, wacc_su, wacc_sd;
 };
 
@@ -92,6 +94,9 @@ Layout make_layout(const Geom& g) {
     L.f_h = align_up(L.f_xd + Sm * H * 2, 256);
     L.f_o = align_up(L.f_h + Sm * I * 2, 256);
     const size_t fwd_end = align_up(L.f_o + Sm * H * 2, 256);
+    // MXFP8 codes take one byte, so codes + scales fit in the bf16 slots
+    L.f_xs = align_up(L.f_xd + Sm * H, 256);
+    L.f_hs = align_up(L.f_h + Sm * I, 256);
     L.b_dgu = 0;
     L.b_hw = align_up(L.b_dgu + Sm * 2 * I * 2, 256);
     L.b_dx = align_up(L.b_hw + Sm * I * 2, 256);
@@ -103,7 +108,11 @@ Layout make_layout(const Geom& g) {
     if (g.shared) {
         L.s_h = 0;
         L.s_o = align_up(M * I * 2, 256);
-        const size_t fe = align_up(L.s_o + M * H * 2, 256);
+        L.s_xq = align_up(L.s_o + M * H * 2, 256);
+        L.s_xs = align_up(L.s_xq + M * H, 256);
+        L.s_hq = align_up(L.s_xs + M * H / 32, 256);
+        L.s_hs = align_up(L.s_hq + M * I, 256);
+        const size_t fe = align_up(L.s_hs + M * I / 32, 256);
         L.s_dgu = 0;
         L.s_hw = align_up(M * 2 * I * 2, 256);
         L.s_dx = align_up(L.s_hw + M * I * 2, 256);
@@ -179,6 +188,69 @@ struct Ptrs {
     char* sh() const { return ws + L->sh; }
     float* wacc(size_t off) const { return (float*)(ws + L->wacc + off); }
 };
+
+
+// MXFP8 forward: dispatch quantises each dispatched row along H, the gate/up
+// GEMM quantises h along I in its epilogue, the down GEMM writes bf16 o, and
+// the combine is the bf16 one.
+moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_sched* sched,
+                      const void* x, const moe_weights* w, void* y, const moe_saved* saved,
+                      hipStream_t st) {
+    const moe_weights_mx* wq = w->mx;
+    int32_t* err = P.err();
+    for (int m = 0; m < g.n_macro; ++m) {
+        char* half = P.half(m, g.halves);
+        uint8_t* xq = (uint8_t*)(half + L.f_xd);
+        uint8_t* xs = (uint8_t*)(half + L.f_xs);
+        uint8_t* hq = (uint8_t*)(half + L.f_h);
+        uint8_t* hs = (uint8_t*)(half + L.f_hs);
+        uint16_t* obuf = (uint16_t*)(half + L.f_o);
+        const int grow0 = m * g.Sm, t0 = m * g.M;
+        const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
+        int32_t* toff = (int32_t*)(P.ws + L.tile_off) + (size_t)m * (g.E + 1);
+        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
+        for (int i = 0; i < g.n_mini; ++i) {
+            const int s0 = grow0 + i * g.Smb;
+            if (launch_dispatch_mx(x, g.H, sched->row_of_slot, s0, s0 + g.Smb, g.k, grow0, g.Sm, xq, xs,
+                                   err, st))
+                return MOE_ERR_HIP;
+        }
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        GemmGateUpMXArgs a1{grp, xq, xs, 0,
+                            (const uint8_t*)wq->w_gate_q, (const uint8_t*)wq->w_gate_s,
+                            (const uint8_t*)wq->w_up_q, (const uint8_t*)wq->w_up_s, g.H, g.I,
+                            (uint16_t*)saved->g, (uint16_t*)saved->u, grow0, hq, hs};
+        if (launch_gemm_gate_up_mx(a1, st)) return MOE_ERR_HIP;
+        GemmDownMXArgs a2{grp, hq, hs, (const uint8_t*)wq->w_down_q, (const uint8_t*)wq->w_down_s,
+                          g.H, g.I, obuf};
+        if (launch_gemm_down_mx(a2, st)) return MOE_ERR_HIP;
+        const uint16_t* sh_o = nullptr;
+        if (g.shared) {
+            char* sh = P.sh();
+            uint8_t* sxq = (uint8_t*)(sh + L.s_xq);
+            uint8_t* sxs = (uint8_t*)(sh + L.s_xs);
+            uint8_t* shq = (uint8_t*)(sh + L.s_hq);
+            uint8_t* shs = (uint8_t*)(sh + L.s_hs);
+            uint16_t* so = (uint16_t*)(sh + L.s_o);
+            if (launch_mx_quant_rows((const uint16_t*)x + (size_t)t0 * g.H, g.M, g.H, sxq, sxs, st))
+                return MOE_ERR_HIP;
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GemmGateUpMXArgs s1{dense, sxq, sxs, 0,
+                                (const uint8_t*)wq->s_gate_q, (const uint8_t*)wq->s_gate_s,
+                                (const uint8_t*)wq->s_up_q, (const uint8_t*)wq->s_up_s, g.H, g.I,
+                                (uint16_t*)saved->sg, (uint16_t*)saved->su, t0, shq, shs};
+            if (launch_gemm_gate_up_mx(s1, st)) return MOE_ERR_HIP;
+            GemmDownMXArgs s2{dense, shq, shs, (const uint8_t*)wq->s_down_q,
+                              (const uint8_t*)wq->s_down_s, g.H, g.I, so};
+            if (launch_gemm_down_mx(s2, st)) return MOE_ERR_HIP;
+            sh_o = so;
+        }
+        if (launch_combine(obuf, g.H, sched->row_of_slot, sched->topk_w, t0, t0 + g.M, g.k, grow0,
+                           g.Sm, sh_o, t0, y, err, st))
+            return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
 
 }  // namespace
 
@@ -256,12 +328,24 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
     if (g.shared && (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down) ||
                      !bf16_ok(saved->sg) || !bf16_ok(saved->su)))
         return MOE_ERR_INVALID_ARG;
-    if (g.mx) return MOE_ERR_UNSUPPORTED;
+    const moe_weights_mx* wq = w->mx;
+    if (g.mx) {
+        if (!wq || !bf16_ok(wq->w_gate_q) || !wq->w_gate_s || !bf16_ok(wq->w_up_q) || !wq->w_up_s ||
+            !bf16_ok(wq->w_down_q) || !wq->w_down_s)
+            return MOE_ERR_INVALID_ARG;
+        if (!aligned(wq->w_gate_s, 4) || !aligned(wq->w_up_s, 4) || !aligned(wq->w_down_s, 4))
+            return MOE_ERR_INVALID_ARG;
+        if (g.shared && (!bf16_ok(wq->s_gate_q) || !bf16_ok(wq->s_up_q) || !bf16_ok(wq->s_down_q) ||
+                         !wq->s_gate_s || !wq->s_up_s || !wq->s_down_s || !aligned(wq->s_gate_s, 4) ||
+                         !aligned(wq->s_up_s, 4) || !aligned(wq->s_down_s, 4)))
+            return MOE_ERR_INVALID_ARG;
+    }
     if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
     hipStream_t st = (hipStream_t)stream;
     Ptrs P{(char*)workspace, &L};
     int32_t* err = P.err();
     const uint16_t* xb = (const uint16_t*)x;
+    if (g.mx) return forward_mx(g, L, P, sched, x, w, y, saved, st);
     for (int m = 0; m < g.n_macro; ++m) {
         char* half = P.half(m, g.halves);
         uint16_t* xd = (uint16_t*)(half + L.f_xd);
@@ -390,6 +474,55 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                                t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
             return MOE_ERR_HIP;
     }
+    return MOE_OK;
+}
+
+moe_status moe_quantize_weights_mxfp8(const moe_config* cfg, const moe_weights* w,
+                                      const moe_weights_mx* o, void* stream) {
+    Geom g;
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    if (!w || !o || !bf16_ok(w->w_gate) || !bf16_ok(w->w_up) || !bf16_ok(w->w_down))
+        return MOE_ERR_INVALID_ARG;
+    const void* need[] = {o->w_gate_q, o->w_gate_s, o->w_up_q, o->w_up_s, o->w_down_q, o->w_down_s,
+                          o->w_gate_tq, o->w_gate_ts, o->w_up_tq, o->w_up_ts, o->w_down_tq,
+                          o->w_down_ts};
+    for (const void* p : need)
+        if (!p || !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    if (g.shared) {
+        if (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down)) return MOE_ERR_INVALID_ARG;
+        const void* needs[] = {o->s_gate_q, o->s_gate_s, o->s_up_q, o->s_up_s, o->s_down_q,
+                               o->s_down_s, o->s_gate_tq, o->s_gate_ts, o->s_up_tq, o->s_up_ts,
+                               o->s_down_tq, o->s_down_ts};
+        for (const void* p : needs)
+            if (!p || !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    }
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    hipStream_t st = (hipStream_t)stream;
+    const int E = g.E, H = g.H, I = g.I;
+    auto one = [&](const void* wg, const void* wu, const void* wd, int n, const void* gq, const void* gs,
+                   const void* uq, const void* us, const void* dq, const void* ds, const void* gtq,
+                   const void* gts, const void* utq, const void* uts, const void* dtq,
+                   const void* dts) -> bool {
+        // forward: rows along their reduction axis
+        if (launch_mx_quant_rows(wg, (int64_t)n * I, H, (void*)gq, (void*)gs, st)) return false;
+        if (launch_mx_quant_rows(wu, (int64_t)n * I, H, (void*)uq, (void*)us, st)) return false;
+        if (launch_mx_quant_rows(wd, (int64_t)n * H, I, (void*)dq, (void*)ds, st)) return false;
+        // backward: transposed copies, blocks along the other axis
+        if (launch_mx_quant_cols(wg, n, I, H, (void*)gtq, (void*)gts, st)) return false;
+        if (launch_mx_quant_cols(wu, n, I, H, (void*)utq, (void*)uts, st)) return false;
+        if (launch_mx_quant_cols(wd, n, H, I, (void*)dtq, (void*)dts, st)) return false;
+        return true;
+    };
+    if (!one(w->w_gate, w->w_up, w->w_down, E, o->w_gate_q, o->w_gate_s, o->w_up_q, o->w_up_s,
+             o->w_down_q, o->w_down_s, o->w_gate_tq, o->w_gate_ts, o->w_up_tq, o->w_up_ts,
+             o->w_down_tq, o->w_down_ts))
+        return MOE_ERR_HIP;
+    if (g.shared &&
+        !one(w->s_gate, w->s_up, w->s_down, 1, o->s_gate_q, o->s_gate_s, o->s_up_q, o->s_up_s,
+             o->s_down_q, o->s_down_s, o->s_gate_tq, o->s_gate_ts, o->s_up_tq, o->s_up_ts,
+             o->s_down_tq, o->s_down_ts))
+        return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -28,387 +28,10 @@
 // Each output element is a fixed-order fp32 sum: K steps ascend, and the
 // MFMA's internal order is fixed, so results are identical run to run and do
 // not depend on which other rows share the tile.
-#include "common.h"
-#include "launch.h"
+#include "gemm_common.h"
 #include "profile.h"
 
 namespace moe {
-
-constexpr int kTK = 64;
-
-// ================================================================ sources
-// Row-major operand whose tile rows are rows of memory (K contiguous).
-struct RowsDirect {
-    const uint16_t* base;
-    int64_t ld;
-    int row0, nvalid;
-    __device__ const uint16_t* row(int r) const {
-        return r < nvalid ? base + (int64_t)(row0 + r) * ld : nullptr;
-    }
-};
-
-// Tile row r = schedule row grow0 + r; memory row = token of its slot.
-struct RowsGather {
-    const uint16_t* base;
-    int64_t ld;
-    const int32_t* slot_of_row;
-    int grow0, nvalid, k, S;
-    int32_t* err;
-    __device__ const uint16_t* row(int r) const {
-        if (r >= nvalid) return nullptr;
-        const int s = slot_of_row[grow0 + r];
-        if ((unsigned)s >= (unsigned)S) {
-            raise_err(err, ERR_BAD_SLOT);
-            return nullptr;
-        }
-        return base + (int64_t)(s / k) * ld;
-    }
-};
-
-// Gate/up weight rows interleaved in quarters of 32 so that a wave owns
-// matching gate and up columns: tile row n -> quarter q = n / 32,
-// q even: W_gate row, q odd: W_up row, both at column i0 + 32*(q/2) + n%32.
-struct RowsGateUp {
-    const uint16_t* wg;
-    const uint16_t* wu;
-    int64_t ld;
-    int i0;
-    __device__ const uint16_t* row(int n) const {
-        const int q = n >> 5;
-        const int i = i0 + ((q >> 1) << 5) + (n & 31);
-        return ((q & 1) ? wu : wg) + (int64_t)i * ld;
-    }
-};
-
-// Operand whose reduction index k is the memory row: krow(k) points at the
-// tile's first column in memory row k.
-struct KRowsDirect {
-    const uint16_t* base;
-    int64_t ld;
-    int col0, kmax;
-    __device__ const uint16_t* krow(int kk) const {
-        return kk < kmax ? base + (int64_t)kk * ld + col0 : nullptr;
-    }
-};
-
-// k < I: W_gate row k; I <= k < 2I: W_up row k - I.
-struct KRowsGateUp {
-    const uint16_t* wg;
-    const uint16_t* wu;
-    int64_t ld;
-    int col0, I;
-    __device__ const uint16_t* krow(int kk) const {
-        if (kk < I) return wg + (int64_t)kk * ld + col0;
-        if (kk < 2 * I) return wu + (int64_t)(kk - I) * ld + col0;
-        return nullptr;
-    }
-};
-
-// k = the k-th row of a group: memory row row0 + k.
-struct KRowsGroup {
-    const uint16_t* base;
-    int64_t ld;
-    int row0, n, col0;
-    __device__ const uint16_t* krow(int kk) const {
-        return kk < n ? base + (int64_t)(row0 + kk) * ld + col0 : nullptr;
-    }
-};
-
-// k = the k-th row of a group in schedule rows; memory row = its token.
-struct KRowsGroupGather {
-    const uint16_t* base;
-    int64_t ld;
-    const int32_t* slot_of_row;
-    int grow0, n, col0, k, S;
-    int32_t* err;
-    __device__ const uint16_t* krow(int kk) const {
-        if (kk >= n) return nullptr;
-        const int s = slot_of_row[grow0 + kk];
-        if ((unsigned)s >= (unsigned)S) {
-            raise_err(err, ERR_BAD_SLOT);
-            return nullptr;
-        }
-        return base + (int64_t)(s / k) * ld + col0;
-    }
-};
-
-// ================================================================ LDS tiles
-// A tile holds ROWS rows (M or N indices) by kTK reduction indices.
-//   KC (K contiguous in memory): stored [row][k], pitch kTK + 8; a fragment
-//      row is read as 16 bytes (one row, 8 consecutive k).
-//   KS (K is the slow memory axis): stored as it lies in memory, [k][row],
-//      pitch ROWS + 16, and read with the LDS transpose load, which hands each
-//      lane four consecutive k of one row.
-// Pitches: the 16 rows of a KC fragment land on 16 different 16-byte bank
-// groups (144-byte rows); for KS the eight k rows read by one 32-lane pass of
-// transpose loads land on disjoint 32-byte bank ranges (pitch = 16 mod 32).
-template <int ROWS, bool KS>
-struct Tile {
-    static constexpr int P = KS ? ROWS + 16 : kTK + 8;
-    static constexpr int SIZE = KS ? kTK * P : ROWS * P;
-};
-
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
-
-// ================================================================ loaders
-// KC tile: 16-byte chunks, 8 lanes per 128-byte row segment.
-template <int ROWS, class Src>
-struct LoadKC {
-    static constexpr int PER = ROWS * (kTK / 8) / 256;
-    const uint16_t* p[PER];
-    int off[PER];
-    uint4 v[PER];
-    __device__ explicit LoadKC(const Src& src) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int c = threadIdx.x + 256 * q;
-            const int r = c >> 3, kc = c & 7;
-            const uint16_t* b = src.row(r);
-            p[q] = b ? b + kc * 8 : nullptr;
-            off[q] = r * Tile<ROWS, false>::P + kc * 8;
-        }
-    }
-    __device__ void load(int kt) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-            v[q] = p[q] ? *(const uint4*)(p[q] + (int64_t)kt * kTK) : make_uint4(0, 0, 0, 0);
-    }
-    __device__ void store(uint16_t* s) const {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) *(uint4*)(s + off[q]) = v[q];
-    }
-};
-
-// KS tile: copied as it lies in memory, 16 lanes per 256-byte k-row segment.
-// src.krow(k) points at the tile's first column in memory row k (or null =
-// zeros); src.col0 may be moved between tiles.
-template <int ROWS, class Src>
-struct LoadKS {
-    static constexpr int CPR = ROWS / 8;
-    static constexpr int PER = kTK * CPR / 256;
-    Src src;
-    int kr[PER], cc[PER];
-    uint4 v[PER];
-    __device__ explicit LoadKS(const Src& s) : src(s) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const int c = threadIdx.x + 256 * q;
-            kr[q] = c / CPR;
-            cc[q] = c % CPR;
-        }
-    }
-    __device__ void load(int kt) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) {
-            const uint16_t* a = src.krow(kt * kTK + kr[q]);
-            v[q] = a ? *(const uint4*)(a + cc[q] * 8) : make_uint4(0, 0, 0, 0);
-        }
-    }
-    __device__ void store(uint16_t* s) const {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) *(uint4*)(s + kr[q] * Tile<ROWS, true>::P + cc[q] * 8) = v[q];
-    }
-    // Row pointers of K step kt at column 0, kept for loads that only move
-    // the column window (src.col0 must be 0 when this is called).
-    const uint16_t* rp[PER];
-    __device__ void cache_rows(int kt) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) rp[q] = src.krow(kt * kTK + kr[q]);
-    }
-    __device__ void load_cached(int col) {
-#pragma unroll
-        for (int q = 0; q < PER; ++q)
-            v[q] = rp[q] ? *(const uint4*)(rp[q] + col + cc[q] * 8) : make_uint4(0, 0, 0, 0);
-    }
-};
-
-// ================================================================ fragments
-// Natural K order (both operands KC): lane l holds k = ks + 8*(l>>4) + 0..7.
-__device__ __forceinline__ bf16x8 frag_kc(const uint16_t* s, int P, int rbase, int ks) {
-    const int lane = lane_id();
-    return *(const bf16x8*)(s + (rbase + (lane & 15)) * P + ks + (lane >> 4) * 8);
-}
-
-// Permuted K order, used whenever an operand is KS: lane group g = l>>4 holds
-// k = ks + 4g + {0..3} and ks + 16 + 4g + {0..3}.  The MFMA sums over k, so
-// the permutation is harmless as long as both operands use it.
-__device__ __forceinline__ bf16x8 frag_kc_perm(const uint16_t* s, int P, int rbase, int ks) {
-    const int lane = lane_id();
-    const uint16_t* p = s + (rbase + (lane & 15)) * P + ks + 4 * (lane >> 4);
-    const uint2 a = *(const uint2*)p;
-    const uint2 b = *(const uint2*)(p + 16);
-    const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
-    return *(const bf16x8*)&v;
-}
-
-// Transpose load of a 16-lane group: lane i receives element (i % 4) of the
-// 8-byte chunk addressed by lane 4r + i/4, for r = 0..3.  Lane j therefore
-// addresses k row ks + 4g + j/4 at columns rbase + 4*(j%4), and every lane ends
-// up with four consecutive k of row rbase + (lane & 15).
-__device__ __forceinline__ bf16x8 frag_ks(const uint16_t* s, int P, int rbase, int ks) {
-    const int lane = lane_id();
-    const int g = lane >> 4, j = lane & 15;
-    const uint16_t* p = s + (ks + 4 * g + (j >> 2)) * P + rbase + 4 * (j & 3);
-    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p);
-    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(p + 16 * P));
-    const uint4 v = make_uint4(__builtin_bit_cast(uint2, a).x, __builtin_bit_cast(uint2, a).y,
-                               __builtin_bit_cast(uint2, b).x, __builtin_bit_cast(uint2, b).y);
-    return *(const bf16x8*)&v;
-}
-
-template <bool KS, bool PERM>
-__device__ __forceinline__ bf16x8 frag(const uint16_t* s, int P, int rbase, int ks) {
-    if constexpr (KS) return frag_ks(s, P, rbase, ks);
-    else if constexpr (PERM) return frag_kc_perm(s, P, rbase, ks);
-    else return frag_kc(s, P, rbase, ks);
-}
-
-// ================================================================ main loop
-// sA: TM rows (output rows), sB: TN rows (output columns).  The MFMA takes the
-// column operand first, so each lane's four accumulators are four consecutive
-// output columns.
-template <int TM, int TN, bool AKS, bool BKS>
-__device__ __forceinline__ void mma_tile(const uint16_t* sA, const uint16_t* sB, int wm0, int wn0,
-                                         f32x4 (&acc)[TM / 32][TN / 32]) {
-    constexpr int MB = TM / 32, NB = TN / 32;
-    constexpr bool PERM = AKS || BKS;
-    constexpr int PA = Tile<TM, AKS>::P, PB = Tile<TN, BKS>::P;
-#pragma unroll
-    for (int ks = 0; ks < kTK; ks += 32) {
-        bf16x8 fb[MB], fa[NB];
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb) fb[mb] = frag<AKS, PERM>(sA, PA, wm0 + mb * 16, ks);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fa[nb] = frag<BKS, PERM>(sB, PB, wn0 + nb * 16, ks);
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], fb[mb], acc[mb][nb]);
-    }
-}
-
-template <int TM, int TN>
-__device__ __forceinline__ void zero_acc(f32x4 (&acc)[TM / 32][TN / 32]) {
-#pragma unroll
-    for (int mb = 0; mb < TM / 32; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < TN / 32; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-}
-
-template <int TM, int TN, bool AKS, bool BKS>
-struct Smem {
-    static constexpr int A = Tile<TM, AKS>::SIZE;
-    static constexpr int B = Tile<TN, BKS>::SIZE;
-    static constexpr int STAGE = A + B;
-};
-
-// Double-buffered K loop, one barrier per step.
-template <int TM, int TN, bool AKS, bool BKS, class LA, class LB>
-__device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
-                                         f32x4 (&acc)[TM / 32][TN / 32]) {
-    using SM = Smem<TM, TN, AKS, BKS>;
-    const int w = threadIdx.x >> 6;
-    const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
-    zero_acc<TM, TN>(acc);
-    if (nk <= 0) return;
-    uint16_t* buf0 = smem;
-    uint16_t* buf1 = smem + SM::STAGE;
-    la.load(0);
-    lb.load(0);
-    la.store(buf0);
-    lb.store(buf0 + SM::A);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        uint16_t* cur = (kt & 1) ? buf1 : buf0;
-        uint16_t* nxt = (kt & 1) ? buf0 : buf1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-            la.load(kt + 1);
-            lb.load(kt + 1);
-        }
-        mma_tile<TM, TN, AKS, BKS>(cur, cur + SM::A, wm0, wn0, acc);
-        if (more) {
-            la.store(nxt);
-            lb.store(nxt + SM::A);
-        }
-        __syncthreads();
-    }
-}
-
-// accumulator (mb, nb, r) -> tile coordinates
-template <int TM, int TN>
-struct AccPos {
-    int m_base, n_base;
-    __device__ AccPos() {
-        const int w = threadIdx.x >> 6, lane = lane_id();
-        m_base = (w & 1) * (TM / 2) + (lane & 15);
-        n_base = (w >> 1) * (TN / 2) + 4 * (lane >> 4);
-    }
-    __device__ int m(int mb) const { return m_base + mb * 16; }
-    __device__ int n(int nb) const { return n_base + nb * 16; }
-};
-
-__device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
-    return make_uint2(pack_bf2(a, b), pack_bf2(c, d));
-}
-
-// ================================================================ tile maps
-// M-grouped: find (expert, row range, column tile) of block b.
-template <int TM>
-__device__ __forceinline__ bool map_mtile(const GroupRows& g, int nNt, int b, int& e, int& lo, int& hi,
-                                          int& nt) {
-    const int ntiles = g.tile_off ? g.tile_off[g.E] : (g.dense_rows + TM - 1) / TM;
-    const int total = ntiles * nNt;
-    if (b >= total) return false;
-    const int L = xcd_remap(b, total);
-    const int mt = L / nNt;
-    nt = L - mt * nNt;
-    if (!g.tile_off) {
-        e = 0;
-        lo = mt * TM;
-        hi = min(lo + TM, g.dense_rows);
-        return true;
-    }
-    int a = 0, z = g.E;
-    while (z - a > 1) {
-        const int mid = (a + z) >> 1;
-        if (g.tile_off[mid] <= mt) a = mid;
-        else z = mid;
-    }
-    e = a;
-    lo = g.offsets[e] + (mt - g.tile_off[e]) * TM;
-    hi = min(lo + TM, g.offsets[e + 1]);
-    return true;
-}
-
-// K-grouped: block b -> (expert, M tile, N tile) and the expert's rows.
-__device__ __forceinline__ bool map_ktile(const GroupRows& g, int nMt, int nNt, int b, int& e, int& mt,
-                                          int& nt, int& lo, int& n) {
-    const int per = nMt * nNt;
-    const int total = (g.offsets ? g.E : 1) * per;
-    if (b >= total) return false;
-    const int L = xcd_remap(b, total);
-    e = L / per;
-    const int rem = L - e * per;
-    mt = rem / nNt;
-    nt = rem - mt * nNt;
-    if (!g.offsets) {
-        lo = 0;
-        n = g.dense_rows;
-        return true;
-    }
-    const int a = g.offsets[e], z = g.offsets[e + 1];
-    if (a < 0 || z < a || z > g.rows) {
-        raise_err(g.err, ERR_BAD_OFFSETS);
-        lo = 0;
-        n = 0;
-    } else {
-        lo = a;
-        n = z - a;
-    }
-    return true;
-}
 
 // ================================================================ forward GEMM 1
 // g = X W_gate^T, u = X W_up^T, h = SiLU(g) * u; g, u saved (bf16), h to the

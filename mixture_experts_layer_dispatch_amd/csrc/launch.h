@@ -102,6 +102,33 @@ struct WgradGateUpArgs {
     WgradOut out_gate, out_up;
 };
 
+struct GemmGateUpMXArgs {
+    GroupRows g;
+    const uint8_t* x_q;       // codes [rows, H] (rows xrow0 + local row)
+    const uint8_t* x_s;       // scales [rows, H/32]
+    int xrow0;
+    const uint8_t* wg_q;
+    const uint8_t* wg_s;
+    const uint8_t* wu_q;
+    const uint8_t* wu_s;
+    int H, I;
+    uint16_t* g_out;
+    uint16_t* u_out;
+    int save_row0;
+    uint8_t* h_q;             // ring codes [rows, I]
+    uint8_t* h_s;             // ring scales [rows, I/32]
+};
+
+struct GemmDownMXArgs {
+    GroupRows g;
+    const uint8_t* h_q;
+    const uint8_t* h_s;
+    const uint8_t* wd_q;      // [E, H, I]
+    const uint8_t* wd_s;      // [E, H, I/32]
+    int H, I;
+    uint16_t* o;
+};
+
 // route_sched.hip
 int launch_topk_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                       hipStream_t st);
@@ -124,6 +151,18 @@ int launch_softmax_bwd(const float* part, int P, const int32_t* row_of_slot, con
                        float* dw, float* d_logits, int32_t* err, hipStream_t st);
 int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
                        int32_t* err, hipStream_t st);
+
+// mx.hip
+int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st);
+int launch_mx_quant_cols(const void* w, int batch, int R, int C, void* codes, void* scales,
+                         hipStream_t st);
+int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
+                       int ring_row0, int ring_rows, void* codes, void* scales, int32_t* err,
+                       hipStream_t st);
+
+// gemm_mx.hip
+int launch_gemm_gate_up_mx(const GemmGateUpMXArgs& a, hipStream_t st);
+int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st);
 
 // gemm.hip
 int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st);

@@ -1,0 +1,61 @@
+// MXFP8 (E4M3 elements, E8M0 scale per 32 elements) arithmetic on the device.
+//
+// arex-research.com "Cursor 放出 MoK", design section, closing paragraph: the
+// layer runs in BF16 or MXFP8; weights are quantised ahead of time and the
+// activations inside dispatch, the expert GEMMs and SwiGLU.  The pages name the
+// format only; the rule is the OCP Microscaling (MX) v1.0 one:
+//   scale 2^s, s = floor(log2(max |v|)) - 8, clamped to [-127, 127] (all-zero
+//   block: s = -127); element = v / 2^s rounded to nearest-even on the E4M3 grid,
+//   saturated to +-448.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// s of a block whose largest magnitude is amax (>= 0, finite)
+__device__ __forceinline__ int mx_scale_exp(float amax) {
+    const uint32_t u = __float_as_uint(amax);
+    const int ef = (int)((u >> 23) & 0xffu);
+    if (ef == 0) return -127;          // zero or subnormal maximum: s < -127 before the clamp
+    const int s = ef - 127 - 8;        // floor(log2 amax) - 8 (ef <= 254 so s <= 119)
+    return s < -127 ? -127 : s;
+}
+
+// E4M3 code of v (already divided by the block scale), round to nearest even,
+// saturating; the sign bit is kept for zero results.
+__device__ __forceinline__ uint32_t e4m3_code(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 24) & 0x80u;
+    const float a = __uint_as_float(u & 0x7fffffffu);
+    if (a >= 448.0f) return sign | 0x7eu;
+    if (a < 0.015625f) {                       // below 2^-6: quantum 2^-9 (subnormals)
+        const uint32_t m = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8, 8 = 2^-6
+        return sign | m;
+    }
+    // normal: keep 3 mantissa bits, round half to even at bit 20
+    uint32_t b = __float_as_uint(a);
+    b += 0x7ffffu + ((b >> 20) & 1u);
+    const uint32_t e = (b >> 23) - 127u + 7u;  // biased E4M3 exponent, 1..15
+    const uint32_t m = (b >> 20) & 7u;
+    return sign | (e << 3) | m;
+}
+
+// Quantise 8 values that belong to one 32-element block whose scale exponent is s.
+__device__ __forceinline__ uint2 e4m3_pack8(const float* v, int s) {
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[q], -s)) << (8 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + q], -s)) << (8 * q);
+    return make_uint2(lo, hi);
+}
+
+__device__ __forceinline__ uint32_t e4m3_pack4(const float* v, int s) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) w |= e4m3_code(__builtin_amdgcn_ldexpf(v[q], -s)) << (8 * q);
+    return w;
+}
+
+}  // namespace moe

@@ -1,0 +1,131 @@
+"""GPU parity of the MXFP8 path against the oracle's MXFP8 mode.
+
+Quantised weights (codes and E8M0 scales, both orientations) must equal the
+oracle's quantiser bit for bit; the layer's outputs must be within
+3e-2 * max|ref| of the oracle run in MXFP8 mode (same quantisation rule, so
+the tolerance covers only fp32 summation order, bf16 storage of g/u/o and the
+rare quantisation code that flips because the GPU's h differs from the
+oracle's in the last fp32 bits).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth_inputs as si
+from gpu_cases import Case, assert_close, f32
+
+pytestmark = pytest.mark.gpu
+
+MX_TOL = 3e-2
+
+SHAPES = {
+    "tiny": si.SHAPES["tiny"],
+    "ragged": si.custom_shape("ragged_mx", T=100, H=256, I=256, E=7, k=3, seed=21),
+    "ring_shared": si.custom_shape("ring_shared_mx", T=512, H=256, I=128, E=16, k=4, seed=22,
+                                   n_shared=1, macrobatch=128, minibatch=64),
+}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+class MXCase(Case):
+    def __init__(self, shape, **kw):
+        super().__init__(shape, **kw)
+        from mixture_experts_layer_dispatch_amd import binding as B
+        self.cfg.precision = B.PREC_MXFP8
+        self.wq = B.alloc_weights_mx(self.cfg)
+        B.moe_quantize_weights_mxfp8(self.cfg, self.weights, self.wq)
+        self.weights = dict(self.weights, mx=self.wq)
+
+
+def _check_quantised(w_bf16, codes, scales, axis):
+    """codes/scales from the GPU vs the oracle's quantiser of w along `axis`."""
+    ref_c, ref_s = oracle.mx_quantize(f32(w_bf16).astype(np.float64), axis=axis)
+    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    if axis == 0:                       # the GPU stores the transposed copy
+        got_c, got_s = got_c.T, got_s.T
+    np.testing.assert_array_equal(got_s, ref_s)
+    np.testing.assert_array_equal(got_c, ref_c)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_weight_quantiser_bit_exact(name):
+    c = MXCase(SHAPES[name], with_backward=False)
+    torch.cuda.synchronize()
+    for e in range(c.shape.E):
+        _check_quantised(c.wg[e], c.wq["w_gate_q"][e], c.wq["w_gate_s"][e], 1)
+        _check_quantised(c.wu[e], c.wq["w_up_q"][e], c.wq["w_up_s"][e], 1)
+        _check_quantised(c.wd[e], c.wq["w_down_q"][e], c.wq["w_down_s"][e], 1)
+        _check_quantised(c.wg[e], c.wq["w_gate_tq"][e], c.wq["w_gate_ts"][e], 0)
+        _check_quantised(c.wu[e], c.wq["w_up_tq"][e], c.wq["w_up_ts"][e], 0)
+        _check_quantised(c.wd[e], c.wq["w_down_tq"][e], c.wq["w_down_ts"][e], 0)
+    if c.sw is not None:
+        _check_quantised(c.sw[0], c.wq["s_gate_q"], c.wq["s_gate_s"], 1)
+        _check_quantised(c.sw[2], c.wq["s_down_q"], c.wq["s_down_s"], 1)
+        _check_quantised(c.sw[1], c.wq["s_up_tq"], c.wq["s_up_ts"], 0)
+
+
+def test_quantiser_edge_values():
+    """Saturation, ties, subnormals, zero blocks and huge blocks, element by element."""
+    from mixture_experts_layer_dispatch_amd import binding as B
+    shape = si.custom_shape("edge", T=8, H=128, I=128, E=1, k=1, seed=0)
+    c = MXCase(shape, with_backward=False)
+    vals = torch.tensor([0.0, -0.0, 1.0, 1.0625, 1.1875, 448.0, 464.0, 500.0, 2.0 ** -9,
+                         2.0 ** -10, 3 * 2.0 ** -10, -1000.0, 2.0 ** 100, 2.0 ** -100, 7.0, 0.1],
+                        dtype=torch.float32)
+    w = torch.zeros(128, 128, dtype=torch.float32)
+    w[:, :16] = vals                       # block 0 of every row mixes everything
+    w[5] = 0.0                             # an all-zero row
+    w[6, 32:64] = 2.0 ** -130              # a block far below 2^-127 (bf16 keeps it)
+    w[7] *= -1
+    wb = w.to(torch.bfloat16).cuda()
+    weights = {"w_gate": wb[None].contiguous(), "w_up": wb[None].contiguous(),
+               "w_down": wb[None].contiguous()}
+    q = B.alloc_weights_mx(c.cfg)
+    B.moe_quantize_weights_mxfp8(c.cfg, weights, q)
+    torch.cuda.synchronize()
+    _check_quantised(wb, q["w_gate_q"][0], q["w_gate_s"][0], 1)
+    _check_quantised(wb, q["w_down_tq"][0], q["w_down_ts"][0], 0)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_forward_mx_small(name):
+    c = MXCase(SHAPES[name], with_backward=False)
+    c.schedule()
+    idx, w, sch = c.oracle_schedule()
+    c.forward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(c.ws) == 0
+    ref = oracle.forward(f32(c.x), c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd),
+                         idx, w, shared=c.shared_np(), mx=True)
+    assert_close("y (mxfp8)", f32(c.y), ref["y"], MX_TOL)
+    rows = sch["row_of_slot"].reshape(c.shape.T, c.shape.k)
+    assert_close("g (mxfp8)", f32(c.saved["g"])[rows], ref["g"], MX_TOL)
+    assert_close("u (mxfp8)", f32(c.saved["u"])[rows], ref["u"], MX_TOL)
+    # the quantisation is really applied: the bf16 oracle is measurably different
+    exact = oracle.forward(f32(c.x), c.expert_view(c.wg), c.expert_view(c.wu),
+                           c.expert_view(c.wd), idx, w, shared=c.shared_np())["y"]
+    assert np.max(np.abs(exact - ref["y"])) > 3 * np.max(np.abs(f32(c.y) - ref["y"]))
+
+
+def test_forward_mx_full_size_sampled():
+    c = MXCase(si.SHAPES["e512_t2048"], with_backward=False)
+    c.schedule()
+    c.forward()
+    torch.cuda.synchronize()
+    idx = c.sched["topk_idx"].cpu().numpy()
+    w = oracle.route(f32(c.logits), c.shape.k)[1]
+    rng = np.random.default_rng(1)
+    tokens = np.sort(rng.choice(c.shape.T, size=16, replace=False))
+    ref = oracle.forward(f32(c.x), c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd),
+                         idx, w, tokens=tokens, mx=True)
+    assert_close("y[sampled] (mxfp8)", f32(c.y)[tokens], ref["y"], MX_TOL)
+    for e in (0, 511):
+        _check_quantised(c.wg[e], c.wq["w_gate_q"][e], c.wq["w_gate_s"][e], 1)
+        _check_quantised(c.wd[e], c.wq["w_down_tq"][e], c.wq["w_down_ts"][e], 0)
