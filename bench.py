@@ -42,6 +42,8 @@ def parse():
                     help="tokens in the CPU oracle's sample (forward + input gradients)")
     ap.add_argument("--cpu-experts", type=int, default=2,
                     help="experts in the CPU oracle's sample (weight gradients)")
+    ap.add_argument("--no-mxfp8", action="store_true",
+                    help="skip the MXFP8 leg (reported beside the bf16 value)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only time plain HBM copy / fill / read kernels of known size and exit")
     return ap.parse_args()
@@ -165,62 +167,87 @@ def main():
     case.dy = si.grad_out(shape, "cuda")
     case.wg, case.wu, case.wd = si.all_expert_weights(shape, "cuda")
     weights = {"w_gate": case.wg, "w_up": case.wu, "w_down": case.wd}
-    ws = B.alloc_workspace(cfg)
     sched = B.alloc_schedule(cfg)
-    saved = B.alloc_saved(cfg)
-    grads = B.alloc_grads(cfg)
     y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     dx = torch.empty_like(y)
     dw = torch.empty(T, k, dtype=torch.float32, device="cuda")
     dlog = torch.empty(T, E, dtype=torch.float32, device="cuda")
     stream = torch.cuda.current_stream()
-
-    def step():
-        B.moe_schedule(cfg, case.logits, sched, ws, stream)
-        B.moe_forward(cfg, sched, case.x, weights, y, saved, ws, stream)
-        B.moe_backward(cfg, sched, saved, case.x, weights, case.dy, dx, grads, dw, dlog, ws, stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(stop) / args.steps
-    print(f"[bench] {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
-    assert B.moe_check_device_error(ws, stream) == 0
-
     S = T * k
     flops = 18.0 * H * I * S + (18.0 * H * I * T if shape.n_shared else 0.0)
-    value = flops / (ms * 1e-3) / 1e12
 
-    # per-kernel durations: HIP events around each launch, on the launch stream
-    B.profile_reset()
-    B.profile_enable(True)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    B.profile_collect()
-    B.profile_enable(False)
-    stats = B.profile_stats()
+    def run(precision):
+        """Time K steps of schedule + forward + backward, then a second pass with
+        per-kernel HIP events; returns (ms/step, kernel stats)."""
+        c = B.Config(T=T, H=H, I=I, E=E, k=k, n_shared=shape.n_shared,
+                     macrobatch=shape.macrobatch, minibatch=shape.minibatch, precision=precision)
+        ws = B.alloc_workspace(c)
+        saved = B.alloc_saved(c)
+        grads = B.alloc_grads(c)
+        wts = dict(weights)
+        if precision == B.PREC_MXFP8:
+            q = B.alloc_weights_mx(c)
+            B.moe_quantize_weights_mxfp8(c, weights, q, stream)   # outside timing
+            wts["mx"] = q
+
+        def step():
+            B.moe_schedule(c, case.logits, sched, ws, stream)
+            B.moe_forward(c, sched, case.x, wts, y, saved, ws, stream)
+            B.moe_backward(c, sched, saved, case.x, wts, case.dy, dx, grads, dw, dlog, ws, stream)
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        for _ in range(args.steps):
+            step()
+        stop.record(stream)
+        torch.cuda.synchronize()
+        ms = start.elapsed_time(stop) / args.steps
+        assert B.moe_check_device_error(ws, stream) == 0
+        B.profile_reset()
+        B.profile_enable(True)
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        B.profile_collect()
+        B.profile_enable(False)
+        stats = B.profile_stats()
+        del ws, saved, grads, wts
+        return ms, stats
+
+    ms, stats = run(B.PREC_BF16)
+    print(f"[bench] bf16: {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    value = flops / (ms * 1e-3) / 1e12
     counts = sched["counts"].cpu().numpy().sum(0)
     kb = kernel_bytes(shape, counts)
-    kernels = {}
-    for name, (n, tot) in stats.items():
-        avg = tot / max(n, 1)
-        entry = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4)}
-        if name in kb:
-            entry["GB/s"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
-        kernels[name] = entry
+
+    def kernel_table(st):
+        out = {}
+        for name, (n, tot) in st.items():
+            avg = tot / max(n, 1)
+            entry = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4)}
+            if name in kb:
+                entry["GB/s"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
+            out[name] = entry
+        return out
+
+    kernels = kernel_table(stats)
     dom = max(stats, key=lambda n: stats[n][1])
     dom_avg = stats[dom][1] / stats[dom][0]
     achieved = kb[dom] / (dom_avg * 1e-3) / 1e9
     roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": None, "avg_ms": round(dom_avg, 4), "bytes_per_launch": kb[dom]}
+
+    mx = None
+    if not args.no_mxfp8:
+        ms_mx, stats_mx = run(B.PREC_MXFP8)
+        print(f"[bench] mxfp8: {args.steps} steps, {ms_mx:.3f} ms/step", file=sys.stderr, flush=True)
+        mx = {"value": round(flops / (ms_mx * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+              "ms_per_step": round(ms_mx, 4), "dtype": "mxfp8 (e4m3 + e8m0 per 32)",
+              "kernels": kernel_table(stats_mx)}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -247,6 +274,7 @@ def main():
                    "T": T, "H": H, "I": I, "E": E, "k": k, "parallelism": "none (1 GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "mxfp8": mx,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)

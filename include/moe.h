@@ -137,7 +137,9 @@ typedef struct moe_weights {
     const moe_weights_mx* mx;
 } moe_weights;
 
-/* What the forward keeps for the backward (bf16, rows in schedule row order). */
+/* What the forward keeps for the backward, rows in schedule row order:
+ * bf16 in BF16 mode; fp32 in MXFP8 mode, so that the backward quantises h,
+ * dg and du from the same unrounded values the forward had. */
 typedef struct moe_saved {
     void* g;               /* [S, I]  gate pre-activations                            */
     void* u;               /* [S, I]  up projections                                  */

@@ -216,7 +216,9 @@ def alloc_schedule(cfg: Config, device="cuda") -> dict:
 
 
 def alloc_saved(cfg: Config, device="cuda") -> dict:
-    bf = dict(dtype=torch.bfloat16, device=device)
+    """g, u (and the shared expert's): bf16 in BF16 mode, fp32 in MXFP8 mode."""
+    dt = torch.float32 if cfg.precision == PREC_MXFP8 else torch.bfloat16
+    bf = dict(dtype=dt, device=device)
     out = {"g": torch.empty(cfg.S, cfg.I, **bf), "u": torch.empty(cfg.S, cfg.I, **bf)}
     if cfg.n_shared:
         out["sg"] = torch.empty(cfg.T, cfg.I, **bf)

@@ -37,6 +37,12 @@ struct Layout {
     // offsets inside the shared-expert region
     size_t s_h, s_o, s_dgu, s_hw, s_dx;
     size_t s_xq, s_xs, s_hq, s_hs;    // MXFP8 shared expert
+    // MXFP8 backward
+    size_t dyq, dys;                  // dy codes / scales [T, H]
+    size_t x_dgu32, x_h32, x_dguq, x_dgus, x_dx, x_part;    // inside a ring half
+    size_t tr, tr_wdy, tr_wdys, tr_h, tr_hs, tr_dgu, tr_dgus, tr_x, tr_xs, blk_off;
+    int64_t kcap;
+    size_t s_dgu32, s_h32, s_dguq, s_dgus, s_dxm;          // shared expert
     size_t wacc_g, wacc_u, wacc_d, wacc_sg, wacc_su, wacc_sd;
 };
 
@@ -103,7 +109,33 @@ Layout make_layout(const Geom& g) {
     L.b_part = align_up(L.b_dx + Sm * H * 2, 256);
     const size_t bwd_end = align_up(L.b_part + Sm * g.P * 4, 256);
     L.ring_half = fwd_end > bwd_end ? fwd_end : bwd_end;
+    if (g.mx) {
+        L.x_dgu32 = 0;
+        L.x_h32 = align_up(Sm * 2 * I * 4, 256);
+        L.x_dguq = align_up(L.x_h32 + Sm * I * 4, 256);
+        L.x_dgus = align_up(L.x_dguq + Sm * 2 * I, 256);
+        L.x_dx = align_up(L.x_dgus + Sm * 2 * I / 32, 256);
+        L.x_part = align_up(L.x_dx + Sm * H * 2, 256);
+        const size_t mx_end = align_up(L.x_part + Sm * g.P * 4, 256);
+        if (mx_end > L.ring_half) L.ring_half = mx_end;
+    }
     L.ring = take(L.ring_half * g.halves);
+    if (g.mx) {
+        L.dyq = take((size_t)g.T * H);
+        L.dys = take((size_t)g.T * H / 32);
+        // transposed, row-quantised operands of the weight gradients (one macrobatch)
+        L.kcap = (int64_t)align_up(Sm + 32 * (size_t)g.E, 128);
+        const size_t kc = (size_t)L.kcap;
+        L.tr_wdy = take(H * kc);
+        L.tr_wdys = take(H * kc / 32);
+        L.tr_h = take(I * kc);
+        L.tr_hs = take(I * kc / 32);
+        L.tr_dgu = take(2 * I * kc);
+        L.tr_dgus = take(2 * I * kc / 32);
+        L.tr_x = take(H * kc);
+        L.tr_xs = take(H * kc / 32);
+        L.blk_off = take((size_t)(g.E + 1) * 4);
+    }
     const size_t M = (size_t)g.M;
     if (g.shared) {
         L.s_h = 0;
@@ -116,7 +148,16 @@ Layout make_layout(const Geom& g) {
         L.s_dgu = 0;
         L.s_hw = align_up(M * 2 * I * 2, 256);
         L.s_dx = align_up(L.s_hw + M * I * 2, 256);
-        const size_t be = align_up(L.s_dx + M * H * 2, 256);
+        size_t be = align_up(L.s_dx + M * H * 2, 256);
+        if (g.mx) {
+            L.s_dgu32 = 0;
+            L.s_h32 = align_up(M * 2 * I * 4, 256);
+            L.s_dguq = align_up(L.s_h32 + M * I * 4, 256);
+            L.s_dgus = align_up(L.s_dguq + M * 2 * I, 256);
+            L.s_dxm = align_up(L.s_dgus + M * 2 * I / 32, 256);
+            const size_t me = align_up(L.s_dxm + M * H * 2, 256);
+            if (me > be) be = me;
+        }
         L.sh = take(fe > be ? fe : be);
     }
     if (g.n_macro > 1) {
@@ -219,7 +260,7 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
         GemmGateUpMXArgs a1{grp, xq, xs, 0,
                             (const uint8_t*)wq->w_gate_q, (const uint8_t*)wq->w_gate_s,
                             (const uint8_t*)wq->w_up_q, (const uint8_t*)wq->w_up_s, g.H, g.I,
-                            (uint16_t*)saved->g, (uint16_t*)saved->u, grow0, hq, hs};
+                            (float*)saved->g, (float*)saved->u, grow0, hq, hs};
         if (launch_gemm_gate_up_mx(a1, st)) return MOE_ERR_HIP;
         GemmDownMXArgs a2{grp, hq, hs, (const uint8_t*)wq->w_down_q, (const uint8_t*)wq->w_down_s,
                           g.H, g.I, obuf};
@@ -238,7 +279,7 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
             GemmGateUpMXArgs s1{dense, sxq, sxs, 0,
                                 (const uint8_t*)wq->s_gate_q, (const uint8_t*)wq->s_gate_s,
                                 (const uint8_t*)wq->s_up_q, (const uint8_t*)wq->s_up_s, g.H, g.I,
-                                (uint16_t*)saved->sg, (uint16_t*)saved->su, t0, shq, shs};
+                                (float*)saved->sg, (float*)saved->su, t0, shq, shs};
             if (launch_gemm_gate_up_mx(s1, st)) return MOE_ERR_HIP;
             GemmDownMXArgs s2{dense, shq, shs, (const uint8_t*)wq->s_down_q,
                               (const uint8_t*)wq->s_down_s, g.H, g.I, so};
@@ -247,6 +288,123 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
         }
         if (launch_combine(obuf, g.H, sched->row_of_slot, sched->topk_w, t0, t0 + g.M, g.k, grow0,
                            g.Sm, sh_o, t0, y, err, st))
+            return MOE_ERR_HIP;
+    }
+    return MOE_OK;
+}
+
+
+// MXFP8 backward.  Every GEMM runs on the scaled fp8 MFMA with its operands
+// quantised along that GEMM's reduction axis: dy along H; dg | du along I
+// (quantised in the down-dgrad epilogue from fp32); and for the weight
+// gradients, whose reduction runs over an expert's rows, w*dy, h, dg | du and
+// x in 32-row blocks of the expert's group, written transposed.
+moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_sched* sched,
+                       const moe_saved* saved, const void* x, const moe_weights* w, const void* dy,
+                       void* dx, const moe_grads* gr, float* dw, float* d_logits, hipStream_t st) {
+    const moe_weights_mx* wq = w->mx;
+    int32_t* err = P.err();
+    char* ws = P.ws;
+    const uint16_t* xb = (const uint16_t*)x;
+    const uint16_t* dyb = (const uint16_t*)dy;
+    uint8_t* dyq = (uint8_t*)(ws + L.dyq);
+    uint8_t* dys = (uint8_t*)(ws + L.dys);
+    if (launch_mx_quant_rows(dy, g.T, g.H, dyq, dys, st)) return MOE_ERR_HIP;
+    const int64_t kc = L.kcap;
+    uint8_t* twdy = (uint8_t*)(ws + L.tr_wdy);
+    uint8_t* twdys = (uint8_t*)(ws + L.tr_wdys);
+    uint8_t* th = (uint8_t*)(ws + L.tr_h);
+    uint8_t* ths = (uint8_t*)(ws + L.tr_hs);
+    uint8_t* tdgu = (uint8_t*)(ws + L.tr_dgu);
+    uint8_t* tdgus = (uint8_t*)(ws + L.tr_dgus);
+    uint8_t* tx = (uint8_t*)(ws + L.tr_x);
+    uint8_t* txs = (uint8_t*)(ws + L.tr_xs);
+    int32_t* blk = (int32_t*)(ws + L.blk_off);
+    auto wgrads = [&](const PadGroups& pg, int mode, uint16_t* dwd, float* accd, uint16_t* dwg,
+                      float* accg, uint16_t* dwu, float* accu) -> bool {
+        WgradMXArgs d{pg, twdy, twdys, th, ths, kc, g.H, g.I, g.H,
+                      {dwd, accd, mode}, {dwd, accd, mode}};
+        if (launch_wgrad_mx(d, st)) return false;
+        WgradMXArgs gu{pg, tdgu, tdgus, tx, txs, kc, 2 * g.I, g.H, g.I,
+                       {dwg, accg, mode}, {dwu, accu, mode}};
+        return launch_wgrad_mx(gu, st) == 0;
+    };
+    for (int m = g.n_macro - 1; m >= 0; --m) {
+        int mode = 0;
+        if (g.n_macro > 1) mode = (m == g.n_macro - 1) ? 1 : (m == 0 ? 3 : 2);
+        char* half = P.half(m, g.halves);
+        float* dgu32 = (float*)(half + L.x_dgu32);
+        float* h32 = (float*)(half + L.x_h32);
+        uint8_t* dguq = (uint8_t*)(half + L.x_dguq);
+        uint8_t* dgus = (uint8_t*)(half + L.x_dgus);
+        uint16_t* dxd = (uint16_t*)(half + L.x_dx);
+        float* part = (float*)(half + L.x_part);
+        const int grow0 = m * g.Sm, t0 = m * g.M;
+        const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
+        int32_t* toff = (int32_t*)(ws + L.tile_off) + (size_t)m * (g.E + 1);
+        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
+        if (launch_tile_prefix(off, g.E, g.Sm, 32, blk, err, st)) return MOE_ERR_HIP;
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        GemmDownDgradMXArgs b1{grp, dyq, dys, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
+                               sched->topk_w, (const uint8_t*)wq->w_down_tq,
+                               (const uint8_t*)wq->w_down_ts, g.H, g.I, (const float*)saved->g,
+                               (const float*)saved->u, grow0, dgu32, h32, dguq, dgus, part, g.P};
+        if (launch_gemm_down_dgrad_mx(b1, st)) return MOE_ERR_HIP;
+        GemmGuDgradMXArgs b2{grp, dguq, dgus, (const uint8_t*)wq->w_gate_tq,
+                             (const uint8_t*)wq->w_gate_ts, (const uint8_t*)wq->w_up_tq,
+                             (const uint8_t*)wq->w_up_ts, g.H, g.I, dxd};
+        if (launch_gemm_gu_dgrad_mx(b2, st)) return MOE_ERR_HIP;
+        PadGroups pg{off, blk, g.E, g.Sm, 0, err};
+        QtSrc qwdy{0, dyb, nullptr, g.H, sched->slot_of_row, sched->topk_w, grow0, 0, g.k, g.S};
+        QtSrc qh{1, nullptr, h32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
+        QtSrc qdgu{1, nullptr, dgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
+        QtSrc qx{2, xb, nullptr, g.H, sched->slot_of_row, nullptr, grow0, 0, g.k, g.S};
+        if (launch_mx_quant_group_t(pg, qwdy, g.H, kc, twdy, twdys, st) ||
+            launch_mx_quant_group_t(pg, qh, g.I, kc, th, ths, st) ||
+            launch_mx_quant_group_t(pg, qdgu, 2 * g.I, kc, tdgu, tdgus, st) ||
+            launch_mx_quant_group_t(pg, qx, g.H, kc, tx, txs, st))
+            return MOE_ERR_HIP;
+        if (!wgrads(pg, mode, (uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), (uint16_t*)gr->d_w_gate,
+                    P.wacc(L.wacc_g), (uint16_t*)gr->d_w_up, P.wacc(L.wacc_u)))
+            return MOE_ERR_HIP;
+        const uint16_t* sh_dx = nullptr;
+        if (g.shared) {
+            char* sh = P.sh();
+            float* sdgu32 = (float*)(sh + L.s_dgu32);
+            float* sh32 = (float*)(sh + L.s_h32);
+            uint8_t* sdguq = (uint8_t*)(sh + L.s_dguq);
+            uint8_t* sdgus = (uint8_t*)(sh + L.s_dgus);
+            uint16_t* sdx = (uint16_t*)(sh + L.s_dxm);
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GemmDownDgradMXArgs c1{dense, dyq, dys, 0, t0, nullptr, 0, g.k, g.S, nullptr,
+                                   (const uint8_t*)wq->s_down_tq, (const uint8_t*)wq->s_down_ts, g.H,
+                                   g.I, (const float*)saved->sg, (const float*)saved->su, t0, sdgu32,
+                                   sh32, sdguq, sdgus, nullptr, g.P};
+            if (launch_gemm_down_dgrad_mx(c1, st)) return MOE_ERR_HIP;
+            GemmGuDgradMXArgs c2{dense, sdguq, sdgus, (const uint8_t*)wq->s_gate_tq,
+                                 (const uint8_t*)wq->s_gate_ts, (const uint8_t*)wq->s_up_tq,
+                                 (const uint8_t*)wq->s_up_ts, g.H, g.I, sdx};
+            if (launch_gemm_gu_dgrad_mx(c2, st)) return MOE_ERR_HIP;
+            PadGroups pd{nullptr, nullptr, 1, g.M, g.M, err};
+            QtSrc sdy{3, dyb, nullptr, g.H, nullptr, nullptr, 0, t0, g.k, g.S};
+            QtSrc shh{1, nullptr, sh32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
+            QtSrc sdg{1, nullptr, sdgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
+            QtSrc sxx{3, xb, nullptr, g.H, nullptr, nullptr, 0, t0, g.k, g.S};
+            if (launch_mx_quant_group_t(pd, sdy, g.H, kc, twdy, twdys, st) ||
+                launch_mx_quant_group_t(pd, shh, g.I, kc, th, ths, st) ||
+                launch_mx_quant_group_t(pd, sdg, 2 * g.I, kc, tdgu, tdgus, st) ||
+                launch_mx_quant_group_t(pd, sxx, g.H, kc, tx, txs, st))
+                return MOE_ERR_HIP;
+            if (!wgrads(pd, mode, (uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), (uint16_t*)gr->d_s_gate,
+                        P.wacc(L.wacc_sg), (uint16_t*)gr->d_s_up, P.wacc(L.wacc_su)))
+                return MOE_ERR_HIP;
+            sh_dx = sdx;
+        }
+        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
+                             dx, err, st))
+            return MOE_ERR_HIP;
+        if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
+                               t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
             return MOE_ERR_HIP;
     }
     return MOE_OK;
@@ -408,10 +566,22 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                      !bf16_ok(saved->sg) || !bf16_ok(saved->su) || !bf16_ok(gr->d_s_gate) ||
                      !bf16_ok(gr->d_s_up) || !bf16_ok(gr->d_s_down)))
         return MOE_ERR_INVALID_ARG;
-    if (g.mx) return MOE_ERR_UNSUPPORTED;
+    if (g.mx) {
+        const moe_weights_mx* wq = w->mx;
+        if (!wq || !bf16_ok(wq->w_gate_tq) || !bf16_ok(wq->w_up_tq) || !bf16_ok(wq->w_down_tq) ||
+            !wq->w_gate_ts || !wq->w_up_ts || !wq->w_down_ts || !aligned(wq->w_gate_ts, 4) ||
+            !aligned(wq->w_up_ts, 4) || !aligned(wq->w_down_ts, 4))
+            return MOE_ERR_INVALID_ARG;
+        if (g.shared && (!bf16_ok(wq->s_gate_tq) || !bf16_ok(wq->s_up_tq) || !bf16_ok(wq->s_down_tq) ||
+                         !wq->s_gate_ts || !wq->s_up_ts || !wq->s_down_ts ||
+                         !aligned(wq->s_gate_ts, 4) || !aligned(wq->s_up_ts, 4) ||
+                         !aligned(wq->s_down_ts, 4)))
+            return MOE_ERR_INVALID_ARG;
+    }
     if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
     hipStream_t st = (hipStream_t)stream;
     Ptrs P{(char*)workspace, &L};
+    if (g.mx) return backward_mx(g, L, P, sched, saved, x, w, dy, dx, gr, dw, d_logits, st);
     int32_t* err = P.err();
     const uint16_t* xb = (const uint16_t*)x;
     const uint16_t* dyb = (const uint16_t*)dy;

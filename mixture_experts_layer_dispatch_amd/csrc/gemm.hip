@@ -237,14 +237,6 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
 // rows (one K step, the common case for small token counts) the A tile stays
 // in LDS for all of them and the next B tile is fetched while the current one
 // is multiplied; otherwise each column tile runs the K loop.
-constexpr int W_TM = 128, W_TN = 64, W_NPW = 64;
-
-// LDS of a weight-gradient block: the resident A tile, then a region that
-// holds the B tile during the MFMAs and the bf16 output tile afterwards.
-constexpr int W_SP = W_TN + 8;                                    // staging pitch
-constexpr int W_REGION = (W_TM * W_SP > Tile<W_TN, true>::SIZE) ? W_TM * W_SP : Tile<W_TN, true>::SIZE;
-constexpr int W_SMEM = Tile<W_TM, true>::SIZE + W_REGION;
-
 template <class SA, class SB, class Epi>
 __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
                                             int nt0, int ntn, uint16_t* smem, const Epi& epi) {
@@ -291,56 +283,6 @@ __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, S
         __syncthreads();
     }
 }
-
-// mode: 0 write bf16; 1 write fp32 partial; 2 add to fp32 partial;
-//       3 add to fp32 partial and write bf16 (the last macrobatch of the walk)
-__device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, const f32x4& v) {
-    float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
-    if (o.mode >= 2) {
-        const float4 p = *(const float4*)(o.acc + idx);
-        x0 = p.x + x0; x1 = p.y + x1; x2 = p.z + x2; x3 = p.w + x3;
-    }
-    if (o.mode == 1 || o.mode == 2) *(float4*)(o.acc + idx) = make_float4(x0, x1, x2, x3);
-    else *(uint2*)(o.out + idx) = pack4(x0, x1, x2, x3);
-}
-
-struct WgradEpi {
-    WgradOut out;
-    int64_t ebase;   // first element of the expert's matrix
-    int64_t ld;      // row length of the output matrix
-    int m0;          // first output row of the slab
-    // bf16 output (mode 0) goes through LDS so that every global store writes
-    // whole 128-byte row segments; the fp32 accumulation modes store directly.
-    __device__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32],
-                               uint16_t* stage) const {
-        AccPos<W_TM, W_TN> pos;
-        const int n0 = nt * W_TN;
-        if (out.mode != 0) {
-#pragma unroll
-            for (int mb = 0; mb < W_TM / 32; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < W_TN / 32; ++nb)
-                    wgrad_store(out, ebase + (int64_t)(m0 + pos.m(mb)) * ld + n0 + pos.n(nb), acc[mb][nb]);
-            return;
-        }
-#pragma unroll
-        for (int mb = 0; mb < W_TM / 32; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < W_TN / 32; ++nb) {
-                const f32x4 v = acc[mb][nb];
-                *(uint2*)(stage + pos.m(mb) * W_SP + pos.n(nb)) = pack4(v[0], v[1], v[2], v[3]);
-            }
-        __syncthreads();
-        constexpr int CPR = W_TN / 8;                  // 16-byte chunks per row
-#pragma unroll
-        for (int q = 0; q < W_TM * CPR / 256; ++q) {
-            const int c = threadIdx.x + 256 * q;
-            const int r = c / CPR, cc = c % CPR;
-            *(uint4*)(out.out + ebase + (int64_t)(m0 + r) * ld + n0 + cc * 8) =
-                *(const uint4*)(stage + r * W_SP + cc * 8);
-        }
-    }
-};
 
 // dW_down[e][h, i] = sum over e's rows r of dy[tok(r), h] * hw[r, i].
 __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {

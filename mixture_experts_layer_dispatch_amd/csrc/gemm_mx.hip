@@ -43,6 +43,19 @@ struct ScalesGateUp {          // same quarter interleave as RowsGateUp
     }
 };
 
+struct ScalesGather {         // row r = schedule row grow0 + r -> words of its token
+    const uint32_t* base;
+    int64_t ld;
+    const int32_t* slot_of_row;
+    int grow0, nvalid, k, S;
+    __device__ const uint32_t* row(int r) const {
+        if (r >= nvalid) return nullptr;
+        const int s = slot_of_row[grow0 + r];
+        if ((unsigned)s >= (unsigned)S) return nullptr;
+        return base + (int64_t)(s / k) * ld;
+    }
+};
+
 template <int ROWS, class Src>
 struct LoadScales {
     const uint32_t* p;
@@ -113,14 +126,65 @@ __device__ __forceinline__ void mma_tile_mx(const uint16_t* st, int wm0, int wn0
                 fa[nb], fb[mb], acc[mb][nb], 0, 0, 0, xa[nb], 0, xb[mb]);
 }
 
+// The same product evaluated on the bf16 MFMA: codes are decoded exactly to
+// bf16 (an E4M3 value times a power of two has at most 4 significant bits) at
+// fragment time.  The scaled fp8 MFMA accumulates a 128-product step less
+// precisely than fp32 (measured on gfx950: ~5e-5 relative on exactly
+// representable operands, vs ~7e-7 for the bf16 MFMA), which flips E4M3 codes
+// when its output is quantised again; the GEMMs whose outputs are re-quantised
+// (gate/up -> h, down dgrad -> dg, du) use this form.
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c, int sexp) {
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
+    const float x = __builtin_amdgcn_ldexpf(v, sexp);
+    return (__float_as_uint(x) >> 16) | ((c & 0x80u) << 8);
+}
+
+__device__ __forceinline__ bf16x8 frag_mx_bf16(const uint16_t* s, const uint32_t* sc, int rbase, int ks) {
+    const int lane = lane_id();
+    const int row = rbase + (lane & 15);
+    const uint8_t* p = (const uint8_t*)(s + row * (kTK + 8)) + 32 * ks + 8 * (lane >> 4);
+    const uint2 c = *(const uint2*)p;
+    const int sexp = (int)((sc[row] >> (8 * ks)) & 0xffu) - 127;
+    uint4 v;
+    v.x = e4m3_to_bf16_bits(c.x & 0xffu, sexp) | (e4m3_to_bf16_bits((c.x >> 8) & 0xffu, sexp) << 16);
+    v.y = e4m3_to_bf16_bits((c.x >> 16) & 0xffu, sexp) | (e4m3_to_bf16_bits(c.x >> 24, sexp) << 16);
+    v.z = e4m3_to_bf16_bits(c.y & 0xffu, sexp) | (e4m3_to_bf16_bits((c.y >> 8) & 0xffu, sexp) << 16);
+    v.w = e4m3_to_bf16_bits((c.y >> 16) & 0xffu, sexp) | (e4m3_to_bf16_bits(c.y >> 24, sexp) << 16);
+    return *(const bf16x8*)&v;
+}
+
+template <int TM, int TN>
+__device__ __forceinline__ void mma_tile_mx_precise(const uint16_t* st, int wm0, int wn0,
+                                                    f32x4 (&acc)[TM / 32][TN / 32]) {
+    using SM = SmemMX<TM, TN>;
+    constexpr int MB = TM / 32, NB = TN / 32;
+    const uint16_t* sA = st;
+    const uint16_t* sB = st + SM::A;
+    const uint32_t* cA = (const uint32_t*)(st + SM::A + SM::B);
+    const uint32_t* cB = cA + TM;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        bf16x8 fb[MB], fa[NB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) fb[mb] = frag_mx_bf16(sA, cA, wm0 + mb * 16, ks);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) fa[nb] = frag_mx_bf16(sB, cB, wn0 + nb * 16, ks);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < NB; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], fb[mb], acc[mb][nb]);
+    }
+}
+
 // Double-buffered K loop over 128-code steps.
-template <int TM, int TN, class LA, class LB, class SA, class SB>
+template <int TM, int TN, bool PRECISE = false, class LA, class LB, class SA, class SB>
 __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int nk, uint16_t* smem,
-                                            f32x4 (&acc)[TM / 32][TN / 32]) {
+                                            f32x4 (&acc)[TM / 32][TN / 32], bool keep = false) {
     using SM = SmemMX<TM, TN>;
     const int w = threadIdx.x >> 6;
     const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
-    zero_acc<TM, TN>(acc);
+    if (!keep) zero_acc<TM, TN>(acc);
     if (nk <= 0) return;
     auto put = [&](uint16_t* st) {
         la.store(st);
@@ -144,7 +208,8 @@ __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int 
         uint16_t* nxt = (kt & 1) ? buf0 : buf1;
         const bool more = kt + 1 < nk;
         if (more) get(kt + 1);
-        mma_tile_mx<TM, TN>(cur, wm0, wn0, acc);
+        if constexpr (PRECISE) mma_tile_mx_precise<TM, TN>(cur, wm0, wn0, acc);
+        else mma_tile_mx<TM, TN>(cur, wm0, wn0, acc);
         if (more) put(nxt);
         __syncthreads();
     }
@@ -175,7 +240,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
     LoadKC<M1_TN, RowsGateUp> lb(db);
     LoadScales<M1_TM, ScalesDirect> sa(dsa);
     LoadScales<M1_TN, ScalesGateUp> sb(ds);
-    mainloop_mx<M1_TM, M1_TN>(la, lb, sa, sb, H / 128, smem, acc);
+    mainloop_mx<M1_TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
     AccPos<M1_TM, M1_TN> pos;
     const int wn = threadIdx.x >> 7, lane = lane_id();
 #pragma unroll
@@ -185,21 +250,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
         float amax = 0.f;
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
-            float gq[4], uq[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                gq[r] = bf2f(f2bf(acc[mb][nb][r]));
-                uq[r] = bf2f(f2bf(acc[mb][nb + 2][r]));
-                // h is quantised from the fp32 accumulators; g and u are kept
-                // in bf16 for the backward
+                // h is quantised from the fp32 accumulators, which are also
+                // what the backward reads back (saved g, u are fp32 here)
                 hq[4 * nb + r] = swiglu_h(acc[mb][nb][r], acc[mb][nb + 2][r]);
                 amax = fmaxf(amax, fabsf(hq[4 * nb + r]));
             }
             if (rl < hi) {
                 const int i = i0 + 32 * wn + nb * 16 + 4 * (lane >> 4);
                 const int64_t srow = (int64_t)(a.save_row0 + rl) * I + i;
-                *(uint2*)(a.g_out + srow) = pack4(gq[0], gq[1], gq[2], gq[3]);
-                *(uint2*)(a.u_out + srow) = pack4(uq[0], uq[1], uq[2], uq[3]);
+                *(float4*)(a.g_out + srow) = make_float4(acc[mb][nb][0], acc[mb][nb][1],
+                                                         acc[mb][nb][2], acc[mb][nb][3]);
+                *(float4*)(a.u_out + srow) = make_float4(acc[mb][nb + 2][0], acc[mb][nb + 2][1],
+                                                         acc[mb][nb + 2][2], acc[mb][nb + 2][3]);
             }
         }
         amax = fmaxf(amax, __shfl_xor(amax, 16));
@@ -248,6 +312,302 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     }
 }
 
+
+// ================================================================ backward: down dgrad
+// a = Q(dY) Q(W_down) (reduction over H; dY codes gathered by token, W_down^T
+// pre-quantised along H), then in fp32: h = SiLU(g) * u from the saved fp32
+// g, u; the dw partial sum of a * h; dh = w a; dg, du.  Writes fp32 h and
+// dg | du for the row-wise quantisation of the weight gradients, and dg | du
+// quantised along I for the input gradient.  Tile 64 rows x 128 columns of I.
+constexpr int M3_TM = 64, M3_TN = 128;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<M3_TM, M3_TN>::STAGE];
+    __shared__ float red[2][M3_TM];
+    int e, lo, hi, nt;
+    if (!map_mtile<M3_TM>(a.g, a.I / M3_TN, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * M3_TN;
+    const int H = a.H, I = a.I;
+    f32x4 acc[2][4];
+    RowsDirect db{(const uint16_t*)(a.wdt_q + (int64_t)e * I * H), H / 2, n0, M3_TN};
+    ScalesDirect dsb{(const uint32_t*)(a.wdt_s + (int64_t)e * I * (H / 32)), H / 128, n0, M3_TN};
+    LoadKC<M3_TN, RowsDirect> lb(db);
+    LoadScales<M3_TN, ScalesDirect> sb(dsb);
+    if (a.dy_gather) {
+        RowsGather da{(const uint16_t*)a.dy_q, H / 2, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
+        ScalesGather dsa{(const uint32_t*)a.dy_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
+        LoadKC<M3_TM, RowsGather> la(da);
+        LoadScales<M3_TM, ScalesGather> sa(dsa);
+        mainloop_mx<M3_TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+    } else {
+        RowsDirect da{(const uint16_t*)a.dy_q, H / 2, a.dyrow0 + lo, hi - lo};
+        ScalesDirect dsa{(const uint32_t*)a.dy_s, H / 128, a.dyrow0 + lo, hi - lo};
+        LoadKC<M3_TM, RowsDirect> la(da);
+        LoadScales<M3_TM, ScalesDirect> sa(dsa);
+        mainloop_mx<M3_TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+    }
+    AccPos<M3_TM, M3_TN> pos;
+    const int lane = lane_id();
+    const int wv = threadIdx.x >> 6, wm = wv & 1, wn = wv >> 1;
+    float dot[2] = {0.f, 0.f};
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int rl = lo + pos.m(mb);
+        const bool ok = rl < hi;
+        float wr = 1.0f;
+        if (ok && a.topk_w) {
+            const int s = a.slot_of_row[a.grow0 + rl];
+            wr = (unsigned)s < (unsigned)a.S ? a.topk_w[s] : 0.f;
+        }
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {          // two 32-column blocks of the wave
+            float dgv[8], duv[8];
+            float mg = 0.f, mu = 0.f;
+#pragma unroll
+            for (int nbb = 0; nbb < 2; ++nbb) {
+                const int nb = 2 * blk + nbb;
+                const int i = n0 + pos.n(nb);
+                float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f), u4 = g4;
+                if (ok) {
+                    const int64_t srow = (int64_t)(a.save_row0 + rl) * I + i;
+                    g4 = *(const float4*)(a.g_saved + srow);
+                    u4 = *(const float4*)(a.u_saved + srow);
+                }
+                const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
+                const float uq[4] = {u4.x, u4.y, u4.z, u4.w};
+                float hv[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const float av = acc[mb][nb][r];
+                    hv[r] = swiglu_h(gq[r], uq[r]);
+                    dot[mb] += av * hv[r];
+                    const float dh = wr * av;
+                    const float sg = sigmoidf_(gq[r]);
+                    duv[4 * nbb + r] = dh * (gq[r] * sg);
+                    dgv[4 * nbb + r] = dh * uq[r] * sg * (1.0f + gq[r] * (1.0f - sg));
+                    mg = fmaxf(mg, fabsf(dgv[4 * nbb + r]));
+                    mu = fmaxf(mu, fabsf(duv[4 * nbb + r]));
+                }
+                if (ok) {
+                    *(float4*)(a.h32 + (int64_t)rl * I + i) = make_float4(hv[0], hv[1], hv[2], hv[3]);
+                    float* drow = a.dgu32 + (int64_t)rl * (2 * I);
+                    *(float4*)(drow + i) = make_float4(dgv[4 * nbb], dgv[4 * nbb + 1], dgv[4 * nbb + 2], dgv[4 * nbb + 3]);
+                    *(float4*)(drow + I + i) = make_float4(duv[4 * nbb], duv[4 * nbb + 1], duv[4 * nbb + 2], duv[4 * nbb + 3]);
+                }
+            }
+            mg = fmaxf(mg, __shfl_xor(mg, 16));
+            mg = fmaxf(mg, __shfl_xor(mg, 32));
+            mu = fmaxf(mu, __shfl_xor(mu, 16));
+            mu = fmaxf(mu, __shfl_xor(mu, 32));
+            const int sgx = mx_scale_exp(mg), sux = mx_scale_exp(mu);
+            if (ok) {
+                const int ib = n0 + wn * 64 + blk * 32;     // first column of the block
+                uint8_t* qrow = a.dgu_q + (int64_t)rl * (2 * I);
+                *(uint32_t*)(qrow + ib + 4 * (lane >> 4)) = e4m3_pack4(dgv, sgx);
+                *(uint32_t*)(qrow + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(dgv + 4, sgx);
+                *(uint32_t*)(qrow + I + ib + 4 * (lane >> 4)) = e4m3_pack4(duv, sux);
+                *(uint32_t*)(qrow + I + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(duv + 4, sux);
+                if ((lane >> 4) == 0) {
+                    uint8_t* srow = a.dgu_s + (int64_t)rl * (2 * I / 32);
+                    srow[ib / 32] = (uint8_t)(sgx + 127);
+                    srow[(I + ib) / 32] = (uint8_t)(sux + 127);
+                }
+            }
+        }
+    }
+    if (!a.dw_part) return;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        dot[mb] += __shfl_xor(dot[mb], 16);
+        dot[mb] += __shfl_xor(dot[mb], 32);
+    }
+    if (lane < 16) {
+        red[wn][wm * 32 + lane] = dot[0];
+        red[wn][wm * 32 + 16 + lane] = dot[1];
+    }
+    __syncthreads();
+    if (threadIdx.x < M3_TM) {
+        const int m = threadIdx.x;
+        const int rl = lo + m;
+        if (rl < hi) a.dw_part[(int64_t)rl * a.P + nt] = red[0][m] + red[1][m];
+    }
+}
+
+// ================================================================ backward: gate/up dgrad
+// dX = Q(dg) Q(W_gate) + Q(du) Q(W_up), reductions over I, against the
+// transposed pre-quantised weights; two K phases accumulate into one tile.
+constexpr int M4_TM = 64, M4_TN = 128;
+
+__global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<M4_TM, M4_TN>::STAGE];
+    int e, lo, hi, nt;
+    if (!map_mtile<M4_TM>(a.g, a.H / M4_TN, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * M4_TN;
+    const int H = a.H, I = a.I;
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int ph = 0; ph < 2; ++ph) {
+        const uint8_t* wq = ph ? a.wut_q : a.wgt_q;
+        const uint8_t* ws = ph ? a.wut_s : a.wgt_s;
+        RowsDirect da{(const uint16_t*)(a.dgu_q + ph * I), I, lo, hi - lo};
+        ScalesDirect dsa{(const uint32_t*)(a.dgu_s + ph * (I / 32)), I / 64, lo, hi - lo};
+        RowsDirect db{(const uint16_t*)(wq + (int64_t)e * H * I), I / 2, n0, M4_TN};
+        ScalesDirect dsb{(const uint32_t*)(ws + (int64_t)e * H * (I / 32)), I / 128, n0, M4_TN};
+        LoadKC<M4_TM, RowsDirect> la(da);
+        LoadKC<M4_TN, RowsDirect> lb(db);
+        LoadScales<M4_TM, ScalesDirect> sa(dsa);
+        LoadScales<M4_TN, ScalesDirect> sb(dsb);
+        mainloop_mx<M4_TM, M4_TN>(la, lb, sa, sb, I / 128, smem, acc, ph == 1);
+    }
+    AccPos<M4_TM, M4_TN> pos;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+        const int rl = lo + pos.m(mb);
+        if (rl >= hi) continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int c = n0 + pos.n(nb);
+            const f32x4 v = acc[mb][nb];
+            *(uint2*)(a.dx + (int64_t)rl * H + c) = pack4(v[0], v[1], v[2], v[3]);
+        }
+    }
+}
+
+// ================================================================ backward: weight gradients
+// C_e[m, n] = sum over the expert's padded rows of A^T[m, k] B^T[n, k], both
+// operands quantised along rows (32-row blocks) and stored transposed by the
+// group-transpose kernel.  A block owns a 128-row slab of one expert's output
+// and walks its 64-column tiles; the A tile stays in LDS when the expert's
+// padded rows fit one 128-code K step.
+constexpr int X_TM = W_TM, X_TN = W_TN;
+
+struct RowsPadK {              // row r of a transposed operand, from code kb0 on
+    const uint8_t* base;
+    int64_t ld;                // codes per row (kcap)
+    int row0;
+    int64_t kb0;
+    __device__ const uint16_t* row(int r) const {
+        return (const uint16_t*)(base + (int64_t)(row0 + r) * ld + kb0);
+    }
+};
+
+template <int ROWS>
+struct LoadKCPad {             // K-contiguous fp8 tile; chunks at or past kmax codes read as zero
+    static constexpr int PER = ROWS * 8 / 256;
+    const uint16_t* p[PER];
+    int off[PER], kc[PER];
+    int kmax;
+    uint4 v[PER];
+    __device__ LoadKCPad(const RowsPadK& src, int kmax_codes) : kmax(kmax_codes) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int c = threadIdx.x + 256 * q;
+            const int r = c >> 3;
+            kc[q] = c & 7;
+            p[q] = src.row(r) + kc[q] * 8;
+            off[q] = r * (kTK + 8) + kc[q] * 8;
+        }
+    }
+    __device__ void load(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            v[q] = (kt * 128 + kc[q] * 16 < kmax) ? *(const uint4*)(p[q] + (int64_t)kt * kTK)
+                                                  : make_uint4(0, 0, 0, 0);
+    }
+    __device__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) *(uint4*)(s + off[q]) = v[q];
+    }
+};
+
+template <int ROWS>
+struct LoadScalesPad {         // scale bytes of blocks at or past nblk read as zero
+    const uint8_t* p;
+    int nblk;
+    uint32_t v;
+    __device__ LoadScalesPad(const uint8_t* base, int64_t ld, int row0, int64_t b0, int nb)
+        : p(threadIdx.x < ROWS ? base + (int64_t)(row0 + threadIdx.x) * ld + b0 : nullptr), nblk(nb), v(0) {}
+    __device__ void load(int kt) {
+        v = 0;
+        if (!p) return;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (4 * kt + j < nblk) v |= (uint32_t)p[4 * kt + j] << (8 * j);
+    }
+    __device__ void store(uint32_t* s) const {
+        if (threadIdx.x < ROWS) s[threadIdx.x] = v;
+    }
+};
+
+constexpr int X_STAGE = SmemMX<X_TM, X_TN>::STAGE;
+constexpr int X_SMEM = X_STAGE + X_TM * W_SP;
+
+__global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[X_SMEM];
+    using SM = SmemMX<X_TM, X_TN>;
+    const int ntiles = a.N / X_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    const int nMt = a.M / X_TM;
+    const int per = nMt * nng;
+    const int total = (a.g.blk_off ? a.g.E : 1) * per;
+    const int b = blockIdx.x;
+    if (b >= total) return;
+    const int L = xcd_remap(b, total);
+    const int e = L / per;
+    const int mt = (L - e * per) / nng;
+    const int ng = L - e * per - mt * nng;
+    int64_t kb0 = 0;
+    int kcodes = 0;
+    if (a.g.blk_off) {
+        const int lo = a.g.off[e], hi = a.g.off[e + 1];
+        if (lo >= 0 && hi >= lo && hi <= a.g.rows) {
+            kb0 = 32LL * a.g.blk_off[e];
+            kcodes = 32 * (a.g.blk_off[e + 1] - a.g.blk_off[e]);
+        }
+    } else {
+        kcodes = 32 * ((a.g.dense_rows + 31) / 32);
+    }
+    const int nk = (kcodes + 127) / 128;
+    const int m0 = mt * X_TM;
+    const bool hi_part = m0 >= a.msplit;
+    WgradEpi epi{hi_part ? a.out_hi : a.out_lo, (int64_t)e * (int64_t)a.msplit * a.N, a.N,
+                 hi_part ? m0 - a.msplit : m0};
+    if (a.msplit == a.M) epi.ebase = (int64_t)e * a.M * a.N;
+    RowsPadK ra{a.at_q, a.kcap, m0, kb0};
+    LoadKCPad<X_TM> la(ra, kcodes);
+    LoadScalesPad<X_TM> sa(a.at_s, a.kcap / 32, m0, kb0 / 32, kcodes / 32);
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (X_TM / 2), wn0 = (w >> 1) * (X_TN / 2);
+    uint16_t* stage = smem + X_STAGE;
+    const int nt0 = ng * W_NPW, ntn = min(W_NPW, ntiles - nt0);
+    f32x4 acc[X_TM / 32][X_TN / 32];
+    for (int i = 0; i < ntn; ++i) {
+        const int n0 = (nt0 + i) * X_TN;
+        RowsPadK rb{a.bt_q, a.kcap, n0, kb0};
+        LoadKCPad<X_TN> lb(rb, kcodes);
+        LoadScalesPad<X_TN> sb(a.bt_s, a.kcap / 32, n0, kb0 / 32, kcodes / 32);
+        zero_acc<X_TM, X_TN>(acc);
+        for (int kt = 0; kt < nk; ++kt) {
+            const bool reload_a = !(nk == 1 && i > 0);
+            if (reload_a) {
+                la.load(kt);
+                sa.load(kt);
+            }
+            lb.load(kt);
+            sb.load(kt);
+            __syncthreads();                       // the previous step's MFMAs are done
+            if (reload_a) {
+                la.store(smem);
+                sa.store((uint32_t*)(smem + SM::A + SM::B));
+            }
+            lb.store(smem + SM::A);
+            sb.store((uint32_t*)(smem + SM::A + SM::B) + X_TM);
+            __syncthreads();
+            mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
+        }
+        epi(nt0 + i, acc, stage);
+    }
+}
+
 // ================================================================ launchers
 static inline int mgroup_grid_mx(const GroupRows& g, int TM) {
     if (!g.tile_off) return (g.dense_rows + TM - 1) / TM;
@@ -268,6 +628,31 @@ int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st) {
     const int grid = mgroup_grid_mx(a.g, M2_TM) * (a.H / M2_TN);
     if (grid <= 0) return 0;
     k_gemm_down_mx<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gemm_down_dgrad_mx(const GemmDownDgradMXArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "gemm_down_dgrad_mx");
+    const int grid = mgroup_grid_mx(a.g, M3_TM) * (a.I / M3_TN);
+    if (grid <= 0) return 0;
+    k_gemm_down_dgrad_mx<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_gemm_gu_dgrad_mx(const GemmGuDgradMXArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "gemm_gu_dgrad_mx");
+    const int grid = mgroup_grid_mx(a.g, M4_TM) * (a.H / M4_TN);
+    if (grid <= 0) return 0;
+    k_gemm_gu_dgrad_mx<<<grid, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "wgrad_mx");
+    const int ntiles = a.N / X_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    const int grid = (a.g.blk_off ? a.g.E : 1) * (a.M / X_TM) * nng;
+    if (grid <= 0) return 0;
+    k_wgrad_mx<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

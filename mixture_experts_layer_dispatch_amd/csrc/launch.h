@@ -112,8 +112,8 @@ struct GemmGateUpMXArgs {
     const uint8_t* wu_q;
     const uint8_t* wu_s;
     int H, I;
-    uint16_t* g_out;
-    uint16_t* u_out;
+    float* g_out;             // saved g, u in fp32
+    float* u_out;
     int save_row0;
     uint8_t* h_q;             // ring codes [rows, I]
     uint8_t* h_s;             // ring scales [rows, I/32]
@@ -127,6 +127,74 @@ struct GemmDownMXArgs {
     const uint8_t* wd_s;      // [E, H, I/32]
     int H, I;
     uint16_t* o;
+};
+
+// Expert groups padded to whole 32-row blocks (the MXFP8 weight gradients
+// quantise along rows).  blk_off == nullptr: one dense group of dense_rows.
+struct PadGroups {
+    const int32_t* off;       // [E+1] macrobatch-local row offsets
+    const int32_t* blk_off;   // [E+1] prefix of ceil(n_e / 32)
+    int E, rows, dense_rows;
+    int32_t* err;
+};
+
+// Source rows of a quantise-transpose: value(r, c) for local row r.
+struct QtSrc {
+    int kind;                 // 0: bf16 rows gathered by token, times the row's weight (w * dy)
+                              // 1: fp32 rows [rows, ld]; 2: bf16 rows gathered by token (x)
+                              // 3: bf16 rows row0 + r (dense; w = 1)
+    const uint16_t* b16;
+    const float* f32;
+    int64_t ld;
+    const int32_t* slot_of_row;
+    const float* topk_w;
+    int grow0, row0, k, S;
+};
+
+struct GemmDownDgradMXArgs {
+    GroupRows g;
+    const uint8_t* dy_q;      // [T, H] codes of dy (quantised along H)
+    const uint8_t* dy_s;
+    int dy_gather, dyrow0;
+    const int32_t* slot_of_row;
+    int grow0, k, S;
+    const float* topk_w;      // nullptr: weight 1
+    const uint8_t* wdt_q;     // [E, I, H] W_down^T codes
+    const uint8_t* wdt_s;
+    int H, I;
+    const float* g_saved;     // fp32
+    const float* u_saved;
+    int save_row0;
+    float* dgu32;             // ring [rows, 2I] fp32 dg | du
+    float* h32;               // ring [rows, I] fp32 h
+    uint8_t* dgu_q;           // ring [rows, 2I] codes along I
+    uint8_t* dgu_s;           // ring [rows, 2I/32]
+    float* dw_part;
+    int P;
+};
+
+struct GemmGuDgradMXArgs {
+    GroupRows g;
+    const uint8_t* dgu_q;
+    const uint8_t* dgu_s;
+    const uint8_t* wgt_q;     // [E, H, I] W_gate^T codes
+    const uint8_t* wgt_s;
+    const uint8_t* wut_q;
+    const uint8_t* wut_s;
+    int H, I;
+    uint16_t* dx;             // ring [rows, H] bf16
+};
+
+struct WgradMXArgs {
+    PadGroups g;
+    const uint8_t* at_q;      // [M, Kcap] codes, K = padded rows
+    const uint8_t* at_s;      // [M, Kcap/32]
+    const uint8_t* bt_q;      // [N, Kcap]
+    const uint8_t* bt_s;
+    int64_t kcap;
+    int M, N;
+    int msplit;               // rows m >= msplit go to out_hi (row m - msplit)
+    WgradOut out_lo, out_hi;
 };
 
 // route_sched.hip
@@ -160,7 +228,13 @@ int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0,
                        int ring_row0, int ring_rows, void* codes, void* scales, int32_t* err,
                        hipStream_t st);
 
+int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, int64_t kcap, void* codes,
+                            void* scales, hipStream_t st);
+
 // gemm_mx.hip
+int launch_gemm_down_dgrad_mx(const GemmDownDgradMXArgs& a, hipStream_t st);
+int launch_gemm_gu_dgrad_mx(const GemmGuDgradMXArgs& a, hipStream_t st);
+int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st);
 int launch_gemm_gate_up_mx(const GemmGateUpMXArgs& a, hipStream_t st);
 int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st);
 

@@ -115,6 +115,68 @@ __global__ __launch_bounds__(256) void k_dispatch_mx(const uint4* __restrict__ x
     }
 }
 
+// ------------------------------------------------------------------ group transpose
+// For the weight gradients, whose reduction runs over an expert's rows: rows of
+// each expert group, in 32-row blocks (the last one zero-padded), are quantised
+// along the row axis and written transposed: output row c holds, for padded
+// block b, the 32 codes of column c at [32b, 32b+32) and one scale at b.
+__device__ __forceinline__ bool map_pad_block(const PadGroups& g, int b, int& r0, int& nv) {
+    if (!g.blk_off) {
+        if (b * 32 >= g.dense_rows) return false;
+        r0 = b * 32;
+        nv = min(32, g.dense_rows - r0);
+        return true;
+    }
+    if (b >= g.blk_off[g.E]) return false;
+    int a = 0, z = g.E;
+    while (z - a > 1) {
+        const int mid = (a + z) >> 1;
+        if (g.blk_off[mid] <= b) a = mid;
+        else z = mid;
+    }
+    const int lo = g.off[a], hi = g.off[a + 1];
+    if (lo < 0 || hi < lo || hi > g.rows) return false;   // reported by the tile prefix
+    r0 = lo + (b - g.blk_off[a]) * 32;
+    nv = min(32, hi - r0);
+    return nv > 0;
+}
+
+__device__ __forceinline__ float qt_value(const QtSrc& s, int r, int c, int32_t* err) {
+    if (s.kind == 1) return s.f32[(int64_t)r * s.ld + c];
+    if (s.kind == 3) return bf2f(s.b16[(int64_t)(s.row0 + r) * s.ld + c]);
+    const int slot = s.slot_of_row[s.grow0 + r];
+    if ((unsigned)slot >= (unsigned)s.S) {
+        raise_err(err, ERR_BAD_SLOT);
+        return 0.f;
+    }
+    const float v = bf2f(s.b16[(int64_t)(slot / s.k) * s.ld + c]);
+    return s.kind == 0 ? v * s.topk_w[slot] : v;
+}
+
+__global__ __launch_bounds__(256) void k_mx_quant_group_t(PadGroups g, QtSrc src, int C, int64_t kcap,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int b = blockIdx.y;
+    int r0, nv;
+    if (c >= C || !map_pad_block(g, b, r0, nv)) return;
+    float v[32];
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        v[q] = q < nv ? qt_value(src, r0 + q, c, g.err) : 0.f;
+        amax = fmaxf(amax, fabsf(v[q]));
+    }
+    const int s = mx_scale_exp(amax);
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = e4m3_pack4(v + 4 * q, s);
+    uint4* dst = (uint4*)(codes + (int64_t)c * kcap + 32 * (int64_t)b);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+    scales[(int64_t)c * (kcap / 32) + b] = (uint8_t)(s + 127);
+}
+
 // ------------------------------------------------------------------ launchers
 int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st) {
     ProfScope prof_(st, "mx_quant_rows");
@@ -141,6 +203,22 @@ int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0,
     k_dispatch_mx<<<(s1 - s0 + 3) / 4, 256, 0, st>>>((const uint4*)x, H, row_of_slot, s0, s1, k,
                                                      ring_row0, ring_rows, (uint2*)codes,
                                                      (uint8_t*)scales, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, int64_t kcap, void* codes,
+                            void* scales, hipStream_t st) {
+    ProfScope prof_(st, "mx_quant_group_t");
+    int nblk;
+    if (!g.blk_off) {
+        nblk = (g.dense_rows + 31) / 32;
+    } else {
+        const int64_t bound = ((int64_t)g.rows + 31LL * g.E) / 32;
+        nblk = (int)(bound < g.rows ? bound : g.rows);
+    }
+    if (nblk <= 0) return 0;
+    dim3 grid((C + 255) / 256, nblk);
+    k_mx_quant_group_t<<<grid, 256, 0, st>>>(g, src, C, kcap, (uint8_t*)codes, (uint8_t*)scales);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -125,8 +125,10 @@ def backward(x, wg, wu, wd, idx, w, dy, shared=None, mx=False, sched=None,
     sched:   the schedule (oracle.schedule); needed in MXFP8 mode, where the
              weight gradients quantise rows in blocks of the expert's group of
              each macrobatch.
-    Returns a dict with dx [n, H]; dw [n, k] (= <dy, o>); dw_fused [n, k]
-    (= <W_down^T dy, h>, equal to dw in exact arithmetic); dl_sel [n, k] (the
+    Returns a dict with dx [n, H]; dw [n, k], the router-weight gradient
+    (<dy, o> in exact arithmetic; in MXFP8 mode the fused <Q(dy) Q(W_down), h>);
+    dw_direct [n, k] (= <dy, o>); dw_fused [n, k] (= <W_down^T dy, h>, with the
+    MXFP8 operands in MXFP8 mode); dl_sel [n, k] (the
     logit gradient at the selected experts; zero elsewhere); dWg, dWu, dWd
     (dicts by expert) and, when shared is given and tokens is None, the shared
     expert's dW_sg, dW_su, dW_sd.
@@ -172,11 +174,18 @@ def backward(x, wg, wu, wd, idx, w, dy, shared=None, mx=False, sched=None,
             out["dW_su"] = _wgrad(dus, X, mx)
     for j in range(k):
         dx = dx + dXd_slot[:, j]
+    # The router-weight gradient is computed inside the SwiGLU backward, from
+    # W_down^T dy ([AREX] closing paragraph).  In exact arithmetic that equals
+    # <dy, o>; in MXFP8 mode W_down^T dy is itself an MXFP8 GEMM, so the
+    # method's gradient is the fused form.
+    dw_direct = dw
+    if mx:
+        dw = dw_fused
     wsel = wf[tokens]
     centre = np.sum(wsel * dw, axis=1, keepdims=True)
     dl_sel = wsel * (dw - centre)
-    out.update({"dx": dx, "dw": dw, "dw_fused": dw_fused, "dl_sel": dl_sel,
-                "tokens": tokens, "fwd": fw})
+    out.update({"dx": dx, "dw": dw, "dw_direct": dw_direct, "dw_fused": dw_fused,
+                "dl_sel": dl_sel, "tokens": tokens, "fwd": fw})
 
     # ---- weight gradients of the requested experts ----------------------
     dWg, dWu, dWd = {}, {}, {}

@@ -3,9 +3,9 @@
 Quantised weights (codes and E8M0 scales, both orientations) must equal the
 oracle's quantiser bit for bit; the layer's outputs must be within
 3e-2 * max|ref| of the oracle run in MXFP8 mode (same quantisation rule, so
-the tolerance covers only fp32 summation order, bf16 storage of g/u/o and the
-rare quantisation code that flips because the GPU's h differs from the
-oracle's in the last fp32 bits).
+the tolerance covers only fp32 summation order, bf16 storage of o, dX and the
+outputs, and the rare quantisation code that flips because a GPU operand
+differs from the oracle's in the last fp32 bits).
 """
 import numpy as np
 import pytest
@@ -38,6 +38,8 @@ class MXCase(Case):
         super().__init__(shape, **kw)
         from mixture_experts_layer_dispatch_amd import binding as B
         self.cfg.precision = B.PREC_MXFP8
+        self.ws = B.alloc_workspace(self.cfg)          # MXFP8 needs more workspace
+        self.saved = B.alloc_saved(self.cfg)           # and fp32 g, u
         self.wq = B.alloc_weights_mx(self.cfg)
         B.moe_quantize_weights_mxfp8(self.cfg, self.weights, self.wq)
         self.weights = dict(self.weights, mx=self.wq)
@@ -129,3 +131,57 @@ def test_forward_mx_full_size_sampled():
     for e in (0, 511):
         _check_quantised(c.wg[e], c.wq["w_gate_q"][e], c.wq["w_gate_s"][e], 1)
         _check_quantised(c.wd[e], c.wq["w_down_tq"][e], c.wq["w_down_ts"][e], 0)
+
+
+@pytest.mark.parametrize("name", list(SHAPES))
+def test_backward_mx_small(name):
+    c = MXCase(SHAPES[name])
+    c.schedule()
+    idx, w, sch = c.oracle_schedule()
+    c.forward()
+    c.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(c.ws) == 0
+    E = c.shape.E
+    ref = oracle.backward(f32(c.x), c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd),
+                          idx, w, f32(c.dy), shared=c.shared_np(), mx=True, sched=sch,
+                          experts=list(range(E)))
+    assert_close("dx (mxfp8)", f32(c.dx), ref["dx"], MX_TOL)
+    assert_close("dw (mxfp8)", c.dw.cpu().numpy(), ref["dw"], MX_TOL)
+    dl = oracle.ffn.d_logits_dense(idx, ref["dl_sel"], E)
+    assert_close("d_logits (mxfp8)", c.dlogits.cpu().numpy(), dl, MX_TOL)
+    zg = np.zeros((c.shape.I, c.shape.H))
+    zd = np.zeros((c.shape.H, c.shape.I))
+    assert_close("dW_gate (mxfp8)", f32(c.grads["d_w_gate"]),
+                 np.stack([ref["dWg"].get(e, zg) for e in range(E)]), MX_TOL)
+    assert_close("dW_up (mxfp8)", f32(c.grads["d_w_up"]),
+                 np.stack([ref["dWu"].get(e, zg) for e in range(E)]), MX_TOL)
+    assert_close("dW_down (mxfp8)", f32(c.grads["d_w_down"]),
+                 np.stack([ref["dWd"].get(e, zd) for e in range(E)]), MX_TOL)
+    if c.sw is not None:
+        assert_close("dW_shared_gate (mxfp8)", f32(c.grads["d_s_gate"]), ref["dW_sg"], MX_TOL)
+        assert_close("dW_shared_up (mxfp8)", f32(c.grads["d_s_up"]), ref["dW_su"], MX_TOL)
+        assert_close("dW_shared_down (mxfp8)", f32(c.grads["d_s_down"]), ref["dW_sd"], MX_TOL)
+
+
+def test_backward_mx_full_size_sampled():
+    c = MXCase(si.SHAPES["e512_t2048"])
+    c.schedule()
+    c.forward()
+    c.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(c.ws) == 0
+    idx, w, sch = c.oracle_schedule()
+    rng = np.random.default_rng(2)
+    tokens = np.sort(rng.choice(c.shape.T, size=12, replace=False))
+    experts = [int(idx[0, 0]), 300]
+    rb = oracle.backward(f32(c.x), c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd),
+                         idx, w, f32(c.dy), mx=True, sched=sch, tokens=tokens, experts=experts)
+    assert_close("dx[sampled] (mxfp8)", f32(c.dx)[tokens], rb["dx"], MX_TOL)
+    assert_close("dw[sampled] (mxfp8)", c.dw.cpu().numpy()[tokens], rb["dw"], MX_TOL)
+    for e in experts:
+        assert_close(f"dW_gate[{e}] (mxfp8)", f32(c.grads["d_w_gate"][e]), rb["dWg"][e], MX_TOL)
+        assert_close(f"dW_up[{e}] (mxfp8)", f32(c.grads["d_w_up"][e]), rb["dWu"][e], MX_TOL)
+        assert_close(f"dW_down[{e}] (mxfp8)", f32(c.grads["d_w_down"][e]), rb["dWd"][e], MX_TOL)
