@@ -123,7 +123,8 @@ Layout make_layout(const Geom& g) {
     if (g.mx) {
         L.dyq = take((size_t)g.T * H);
         L.dys = take((size_t)g.T * H / 32);
-        // transposed, row-quantised operands of the weight gradients (one macrobatch)
+        // transposed, row-quantised operands of the weight gradients (one macrobatch,
+        // group-major); kcap bounds the macrobatch's rows padded group by group to 32
         L.kcap = (int64_t)align_up(Sm + 32 * (size_t)g.E, 128);
         const size_t kc = (size_t)L.kcap;
         L.tr_wdy = take(H * kc);
@@ -310,7 +311,6 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     uint8_t* dyq = (uint8_t*)(ws + L.dyq);
     uint8_t* dys = (uint8_t*)(ws + L.dys);
     if (launch_mx_quant_rows(dy, g.T, g.H, dyq, dys, st)) return MOE_ERR_HIP;
-    const int64_t kc = L.kcap;
     uint8_t* twdy = (uint8_t*)(ws + L.tr_wdy);
     uint8_t* twdys = (uint8_t*)(ws + L.tr_wdys);
     uint8_t* th = (uint8_t*)(ws + L.tr_h);
@@ -322,10 +322,10 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     int32_t* blk = (int32_t*)(ws + L.blk_off);
     auto wgrads = [&](const PadGroups& pg, int mode, uint16_t* dwd, float* accd, uint16_t* dwg,
                       float* accg, uint16_t* dwu, float* accu) -> bool {
-        WgradMXArgs d{pg, twdy, twdys, th, ths, kc, g.H, g.I, g.H,
+        WgradMXArgs d{pg, twdy, twdys, th, ths, g.H, g.I, g.H,
                       {dwd, accd, mode}, {dwd, accd, mode}};
         if (launch_wgrad_mx(d, st)) return false;
-        WgradMXArgs gu{pg, tdgu, tdgus, tx, txs, kc, 2 * g.I, g.H, g.I,
+        WgradMXArgs gu{pg, tdgu, tdgus, tx, txs, 2 * g.I, g.H, g.I,
                        {dwg, accg, mode}, {dwu, accu, mode}};
         return launch_wgrad_mx(gu, st) == 0;
     };
@@ -359,10 +359,10 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         QtSrc qh{1, nullptr, h32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
         QtSrc qdgu{1, nullptr, dgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
         QtSrc qx{2, xb, nullptr, g.H, sched->slot_of_row, nullptr, grow0, 0, g.k, g.S};
-        if (launch_mx_quant_group_t(pg, qwdy, g.H, kc, twdy, twdys, st) ||
-            launch_mx_quant_group_t(pg, qh, g.I, kc, th, ths, st) ||
-            launch_mx_quant_group_t(pg, qdgu, 2 * g.I, kc, tdgu, tdgus, st) ||
-            launch_mx_quant_group_t(pg, qx, g.H, kc, tx, txs, st))
+        if (launch_mx_quant_group_t(pg, qwdy, g.H, twdy, twdys, st) ||
+            launch_mx_quant_group_t(pg, qh, g.I, th, ths, st) ||
+            launch_mx_quant_group_t(pg, qdgu, 2 * g.I, tdgu, tdgus, st) ||
+            launch_mx_quant_group_t(pg, qx, g.H, tx, txs, st))
             return MOE_ERR_HIP;
         if (!wgrads(pg, mode, (uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), (uint16_t*)gr->d_w_gate,
                     P.wacc(L.wacc_g), (uint16_t*)gr->d_w_up, P.wacc(L.wacc_u)))
@@ -390,10 +390,10 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
             QtSrc shh{1, nullptr, sh32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
             QtSrc sdg{1, nullptr, sdgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
             QtSrc sxx{3, xb, nullptr, g.H, nullptr, nullptr, 0, t0, g.k, g.S};
-            if (launch_mx_quant_group_t(pd, sdy, g.H, kc, twdy, twdys, st) ||
-                launch_mx_quant_group_t(pd, shh, g.I, kc, th, ths, st) ||
-                launch_mx_quant_group_t(pd, sdg, 2 * g.I, kc, tdgu, tdgus, st) ||
-                launch_mx_quant_group_t(pd, sxx, g.H, kc, tx, txs, st))
+            if (launch_mx_quant_group_t(pd, sdy, g.H, twdy, twdys, st) ||
+                launch_mx_quant_group_t(pd, shh, g.I, th, ths, st) ||
+                launch_mx_quant_group_t(pd, sdg, 2 * g.I, tdgu, tdgus, st) ||
+                launch_mx_quant_group_t(pd, sxx, g.H, tx, txs, st))
                 return MOE_ERR_HIP;
             if (!wgrads(pd, mode, (uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), (uint16_t*)gr->d_s_gate,
                         P.wacc(L.wacc_sg), (uint16_t*)gr->d_s_up, P.wacc(L.wacc_su)))

@@ -126,31 +126,31 @@ __device__ __forceinline__ void mma_tile_mx(const uint16_t* st, int wm0, int wn0
                 fa[nb], fb[mb], acc[mb][nb], 0, 0, 0, xa[nb], 0, xb[mb]);
 }
 
-// The same product evaluated on the bf16 MFMA: codes are decoded exactly to
-// bf16 (an E4M3 value times a power of two has at most 4 significant bits) at
-// fragment time.  The scaled fp8 MFMA accumulates a 128-product step less
+// The same product evaluated on the bf16 MFMA: codes are decoded to bf16 at
+// fragment time (an E4M3 value times a power of two has at most 4 significant
+// bits, so the decode is exact).  The scaled fp8 MFMA accumulates a 128-product step less
 // precisely than fp32 (measured on gfx950: ~5e-5 relative on exactly
 // representable operands, vs ~7e-7 for the bf16 MFMA), which flips E4M3 codes
 // when its output is quantised again; the GEMMs whose outputs are re-quantised
 // (gate/up -> h, down dgrad -> dg, du) use this form.
-__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c, int sexp) {
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0.001953125f;
-    const float x = __builtin_amdgcn_ldexpf(v, sexp);
-    return (__float_as_uint(x) >> 16) | ((c & 0x80u) << 8);
-}
+// Decoding uses the hardware scaled conversion (two E4M3 codes times an fp32
+// scale to two bf16); checked on gfx950 against an exact decode of all 256
+// codes: exact for power-of-two scales, except that results below 2^-126 are
+// flushed to zero (blocks whose largest magnitude is under ~2^-109).
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bf16x8 frag_mx_bf16(const uint16_t* s, const uint32_t* sc, int rbase, int ks) {
     const int lane = lane_id();
     const int row = rbase + (lane & 15);
     const uint8_t* p = (const uint8_t*)(s + row * (kTK + 8)) + 32 * ks + 8 * (lane >> 4);
     const uint2 c = *(const uint2*)p;
-    const int sexp = (int)((sc[row] >> (8 * ks)) & 0xffu) - 127;
+    const uint32_t e8 = (sc[row] >> (8 * ks)) & 0xffu;
+    const float scale = __uint_as_float(e8 ? (e8 << 23) : 0x00400000u);   // 2^(e8 - 127)
     uint4 v;
-    v.x = e4m3_to_bf16_bits(c.x & 0xffu, sexp) | (e4m3_to_bf16_bits((c.x >> 8) & 0xffu, sexp) << 16);
-    v.y = e4m3_to_bf16_bits((c.x >> 16) & 0xffu, sexp) | (e4m3_to_bf16_bits(c.x >> 24, sexp) << 16);
-    v.z = e4m3_to_bf16_bits(c.y & 0xffu, sexp) | (e4m3_to_bf16_bits((c.y >> 8) & 0xffu, sexp) << 16);
-    v.w = e4m3_to_bf16_bits((c.y >> 16) & 0xffu, sexp) | (e4m3_to_bf16_bits(c.y >> 24, sexp) << 16);
+    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, scale, false));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, scale, true));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, scale, false));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, scale, true));
     return *(const bf16x8*)&v;
 }
 
@@ -475,15 +475,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a
 
 // ================================================================ backward: weight gradients
 // C_e[m, n] = sum over the expert's padded rows of A^T[m, k] B^T[n, k], both
-// operands quantised along rows (32-row blocks) and stored transposed by the
-// group-transpose kernel.  A block owns a 128-row slab of one expert's output
+// operands quantised along rows (32-row blocks) and stored transposed, one
+// contiguous [rows][padded K] block per expert, by the group-transpose kernel.  A block owns a 128-row slab of one expert's output
 // and walks its 64-column tiles; the A tile stays in LDS when the expert's
 // padded rows fit one 128-code K step.
 constexpr int X_TM = W_TM, X_TN = W_TN;
 
 struct RowsPadK {              // row r of a transposed operand, from code kb0 on
     const uint8_t* base;
-    int64_t ld;                // codes per row (kcap)
+    int64_t ld;                // codes per row
     int row0;
     int64_t kb0;
     __device__ const uint16_t* row(int r) const {
@@ -494,11 +494,12 @@ struct RowsPadK {              // row r of a transposed operand, from code kb0 o
 template <int ROWS>
 struct LoadKCPad {             // K-contiguous fp8 tile; chunks at or past kmax codes read as zero
     static constexpr int PER = ROWS * 8 / 256;
+    RowsPadK src;
     const uint16_t* p[PER];
     int off[PER], kc[PER];
     int kmax;
     uint4 v[PER];
-    __device__ LoadKCPad(const RowsPadK& src, int kmax_codes) : kmax(kmax_codes) {
+    __device__ LoadKCPad(const RowsPadK& s, int kmax_codes) : src(s), kmax(kmax_codes) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const int c = threadIdx.x + 256 * q;
@@ -507,6 +508,11 @@ struct LoadKCPad {             // K-contiguous fp8 tile; chunks at or past kmax 
             p[q] = src.row(r) + kc[q] * 8;
             off[q] = r * (kTK + 8) + kc[q] * 8;
         }
+    }
+    __device__ void retarget(int row0) {      // same K range, other rows
+        src.row0 = row0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) p[q] = src.row((threadIdx.x + 256 * q) >> 3) + kc[q] * 8;
     }
     __device__ void load(int kt) {
 #pragma unroll
@@ -522,11 +528,18 @@ struct LoadKCPad {             // K-contiguous fp8 tile; chunks at or past kmax 
 
 template <int ROWS>
 struct LoadScalesPad {         // scale bytes of blocks at or past nblk read as zero
+    const uint8_t* base;
+    int64_t ld, b0;
     const uint8_t* p;
     int nblk;
     uint32_t v;
-    __device__ LoadScalesPad(const uint8_t* base, int64_t ld, int row0, int64_t b0, int nb)
-        : p(threadIdx.x < ROWS ? base + (int64_t)(row0 + threadIdx.x) * ld + b0 : nullptr), nblk(nb), v(0) {}
+    __device__ LoadScalesPad(const uint8_t* bs, int64_t l, int row0, int64_t b, int nb)
+        : base(bs), ld(l), b0(b), p(nullptr), nblk(nb), v(0) {
+        retarget(row0);
+    }
+    __device__ void retarget(int row0) {
+        p = threadIdx.x < ROWS ? base + (int64_t)(row0 + threadIdx.x) * ld + b0 : nullptr;
+    }
     __device__ void load(int kt) {
         v = 0;
         if (!p) return;
@@ -555,12 +568,13 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     const int e = L / per;
     const int mt = (L - e * per) / nng;
     const int ng = L - e * per - mt * nng;
-    int64_t kb0 = 0;
+    // the group's operands are contiguous [rows][kcodes] blocks (group-major)
+    int64_t blk0 = 0;
     int kcodes = 0;
     if (a.g.blk_off) {
         const int lo = a.g.off[e], hi = a.g.off[e + 1];
         if (lo >= 0 && hi >= lo && hi <= a.g.rows) {
-            kb0 = 32LL * a.g.blk_off[e];
+            blk0 = a.g.blk_off[e];
             kcodes = 32 * (a.g.blk_off[e + 1] - a.g.blk_off[e]);
         }
     } else {
@@ -572,35 +586,67 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     WgradEpi epi{hi_part ? a.out_hi : a.out_lo, (int64_t)e * (int64_t)a.msplit * a.N, a.N,
                  hi_part ? m0 - a.msplit : m0};
     if (a.msplit == a.M) epi.ebase = (int64_t)e * a.M * a.N;
-    RowsPadK ra{a.at_q, a.kcap, m0, kb0};
+    const uint8_t* aq = a.at_q + 32 * blk0 * a.M;
+    const uint8_t* as_ = a.at_s + blk0 * a.M;
+    const uint8_t* bq = a.bt_q + 32 * blk0 * a.N;
+    const uint8_t* bs = a.bt_s + blk0 * a.N;
+    RowsPadK ra{aq, kcodes, m0, 0};
     LoadKCPad<X_TM> la(ra, kcodes);
-    LoadScalesPad<X_TM> sa(a.at_s, a.kcap / 32, m0, kb0 / 32, kcodes / 32);
+    LoadScalesPad<X_TM> sa(as_, kcodes / 32, m0, 0, kcodes / 32);
     const int w = threadIdx.x >> 6;
     const int wm0 = (w & 1) * (X_TM / 2), wn0 = (w >> 1) * (X_TN / 2);
     uint16_t* stage = smem + X_STAGE;
     const int nt0 = ng * W_NPW, ntn = min(W_NPW, ntiles - nt0);
+    uint32_t* cA = (uint32_t*)(smem + SM::A + SM::B);
+    uint32_t* cB = cA + X_TM;
     f32x4 acc[X_TM / 32][X_TN / 32];
+    RowsPadK rb{bq, kcodes, nt0 * X_TN, 0};
+    LoadKCPad<X_TN> lb(rb, kcodes);
+    LoadScalesPad<X_TN> sb(bs, kcodes / 32, nt0 * X_TN, 0, kcodes / 32);
+    if (nk <= 1) {
+        // one K step: A stays in LDS; the next column tile is fetched while the
+        // current one is multiplied and written out
+        if (nk == 1) {
+            la.load(0);
+            sa.load(0);
+            lb.load(0);
+            sb.load(0);
+            la.store(smem);
+            sa.store(cA);
+        }
+        for (int i = 0; i < ntn; ++i) {
+            zero_acc<X_TM, X_TN>(acc);
+            if (nk == 1) {
+                if (i > 0) __syncthreads();            // MFMAs and staged stores of tile i-1 done
+                lb.store(smem + SM::A);
+                sb.store(cB);
+                __syncthreads();
+                if (i + 1 < ntn) {
+                    lb.retarget((nt0 + i + 1) * X_TN);
+                    sb.retarget((nt0 + i + 1) * X_TN);
+                    lb.load(0);
+                    sb.load(0);
+                }
+                mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
+            }
+            epi(nt0 + i, acc, stage);
+        }
+        return;
+    }
     for (int i = 0; i < ntn; ++i) {
-        const int n0 = (nt0 + i) * X_TN;
-        RowsPadK rb{a.bt_q, a.kcap, n0, kb0};
-        LoadKCPad<X_TN> lb(rb, kcodes);
-        LoadScalesPad<X_TN> sb(a.bt_s, a.kcap / 32, n0, kb0 / 32, kcodes / 32);
+        lb.retarget((nt0 + i) * X_TN);
+        sb.retarget((nt0 + i) * X_TN);
         zero_acc<X_TM, X_TN>(acc);
         for (int kt = 0; kt < nk; ++kt) {
-            const bool reload_a = !(nk == 1 && i > 0);
-            if (reload_a) {
-                la.load(kt);
-                sa.load(kt);
-            }
+            la.load(kt);
+            sa.load(kt);
             lb.load(kt);
             sb.load(kt);
-            __syncthreads();                       // the previous step's MFMAs are done
-            if (reload_a) {
-                la.store(smem);
-                sa.store((uint32_t*)(smem + SM::A + SM::B));
-            }
+            __syncthreads();                           // the previous step's MFMAs are done
+            la.store(smem);
+            sa.store(cA);
             lb.store(smem + SM::A);
-            sb.store((uint32_t*)(smem + SM::A + SM::B) + X_TM);
+            sb.store(cB);
             __syncthreads();
             mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
         }
@@ -648,7 +694,7 @@ int launch_gemm_gu_dgrad_mx(const GemmGuDgradMXArgs& a, hipStream_t st) {
 }
 
 int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
-    ProfScope prof_(st, "wgrad_mx");
+    ProfScope prof_(st, a.msplit < a.M ? "wgrad_gate_up_mx" : "wgrad_down_mx");
     const int ntiles = a.N / X_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
     const int grid = (a.g.blk_off ? a.g.E : 1) * (a.M / X_TM) * nng;
     if (grid <= 0) return 0;

@@ -187,11 +187,10 @@ struct GemmGuDgradMXArgs {
 
 struct WgradMXArgs {
     PadGroups g;
-    const uint8_t* at_q;      // [M, Kcap] codes, K = padded rows
-    const uint8_t* at_s;      // [M, Kcap/32]
-    const uint8_t* bt_q;      // [N, Kcap]
+    const uint8_t* at_q;      // per group: [M, np_e] codes, K = the group's padded rows
+    const uint8_t* at_s;      // per group: [M, np_e / 32]
+    const uint8_t* bt_q;      // per group: [N, np_e]
     const uint8_t* bt_s;
-    int64_t kcap;
     int M, N;
     int msplit;               // rows m >= msplit go to out_hi (row m - msplit)
     WgradOut out_lo, out_hi;
@@ -228,8 +227,8 @@ int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0,
                        int ring_row0, int ring_rows, void* codes, void* scales, int32_t* err,
                        hipStream_t st);
 
-int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, int64_t kcap, void* codes,
-                            void* scales, hipStream_t st);
+int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, void* codes, void* scales,
+                            hipStream_t st);
 
 // gemm_mx.hip
 int launch_gemm_down_dgrad_mx(const GemmDownDgradMXArgs& a, hipStream_t st);

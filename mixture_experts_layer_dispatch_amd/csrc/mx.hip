@@ -118,13 +118,25 @@ __global__ __launch_bounds__(256) void k_dispatch_mx(const uint4* __restrict__ x
 // ------------------------------------------------------------------ group transpose
 // For the weight gradients, whose reduction runs over an expert's rows: rows of
 // each expert group, in 32-row blocks (the last one zero-padded), are quantised
-// along the row axis and written transposed: output row c holds, for padded
-// block b, the 32 codes of column c at [32b, 32b+32) and one scale at b.
-__device__ __forceinline__ bool map_pad_block(const PadGroups& g, int b, int& r0, int& nv) {
+// along the row axis and written transposed, group by group: group e (with
+// n_e rows padded to np_e = 32 * ceil(n_e / 32)) owns the contiguous block
+// starting at code 32 * blk_off[e] * C, laid out [C][np_e], and its scales
+// start at blk_off[e] * C, laid out [C][np_e / 32].
+struct PadBlock {
+    int r0, nv;                // first local row, valid rows of this 32-row block
+    int64_t gcode;             // first code of the group's block
+    int np;                    // padded rows of the group
+    int bl;                    // block index inside the group
+};
+
+__device__ __forceinline__ bool map_pad_block(const PadGroups& g, int C, int b, PadBlock& o) {
     if (!g.blk_off) {
         if (b * 32 >= g.dense_rows) return false;
-        r0 = b * 32;
-        nv = min(32, g.dense_rows - r0);
+        o.r0 = b * 32;
+        o.nv = min(32, g.dense_rows - o.r0);
+        o.gcode = 0;
+        o.np = 32 * ((g.dense_rows + 31) / 32);
+        o.bl = b;
         return true;
     }
     if (b >= g.blk_off[g.E]) return false;
@@ -136,9 +148,12 @@ __device__ __forceinline__ bool map_pad_block(const PadGroups& g, int b, int& r0
     }
     const int lo = g.off[a], hi = g.off[a + 1];
     if (lo < 0 || hi < lo || hi > g.rows) return false;   // reported by the tile prefix
-    r0 = lo + (b - g.blk_off[a]) * 32;
-    nv = min(32, hi - r0);
-    return nv > 0;
+    o.bl = b - g.blk_off[a];
+    o.r0 = lo + o.bl * 32;
+    o.nv = min(32, hi - o.r0);
+    o.gcode = 32LL * g.blk_off[a] * C;
+    o.np = 32 * (g.blk_off[a + 1] - g.blk_off[a]);
+    return o.nv > 0;
 }
 
 __device__ __forceinline__ float qt_value(const QtSrc& s, int r, int c, int32_t* err) {
@@ -153,28 +168,27 @@ __device__ __forceinline__ float qt_value(const QtSrc& s, int r, int c, int32_t*
     return s.kind == 0 ? v * s.topk_w[slot] : v;
 }
 
-__global__ __launch_bounds__(256) void k_mx_quant_group_t(PadGroups g, QtSrc src, int C, int64_t kcap,
+__global__ __launch_bounds__(256) void k_mx_quant_group_t(PadGroups g, QtSrc src, int C,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
     const int c = blockIdx.x * 256 + threadIdx.x;
-    const int b = blockIdx.y;
-    int r0, nv;
-    if (c >= C || !map_pad_block(g, b, r0, nv)) return;
+    PadBlock pb;
+    if (c >= C || !map_pad_block(g, C, blockIdx.y, pb)) return;
     float v[32];
     float amax = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-        v[q] = q < nv ? qt_value(src, r0 + q, c, g.err) : 0.f;
+        v[q] = q < pb.nv ? qt_value(src, pb.r0 + q, c, g.err) : 0.f;
         amax = fmaxf(amax, fabsf(v[q]));
     }
     const int s = mx_scale_exp(amax);
     uint32_t w[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) w[q] = e4m3_pack4(v + 4 * q, s);
-    uint4* dst = (uint4*)(codes + (int64_t)c * kcap + 32 * (int64_t)b);
+    uint4* dst = (uint4*)(codes + pb.gcode + (int64_t)c * pb.np + 32 * pb.bl);
     dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
     dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
-    scales[(int64_t)c * (kcap / 32) + b] = (uint8_t)(s + 127);
+    scales[pb.gcode / 32 + (int64_t)c * (pb.np / 32) + pb.bl] = (uint8_t)(s + 127);
 }
 
 // ------------------------------------------------------------------ launchers
@@ -206,9 +220,10 @@ int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0,
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, int64_t kcap, void* codes,
-                            void* scales, hipStream_t st) {
-    ProfScope prof_(st, "mx_quant_group_t");
+int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, void* codes, void* scales,
+                            hipStream_t st) {
+    static const char* names[4] = {"mx_qt_wdy", "mx_qt_f32", "mx_qt_x", "mx_qt_dense"};
+    ProfScope prof_(st, names[src.kind & 3]);
     int nblk;
     if (!g.blk_off) {
         nblk = (g.dense_rows + 31) / 32;
@@ -218,7 +233,7 @@ int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, int64_t
     }
     if (nblk <= 0) return 0;
     dim3 grid((C + 255) / 256, nblk);
-    k_mx_quant_group_t<<<grid, 256, 0, st>>>(g, src, C, kcap, (uint8_t*)codes, (uint8_t*)scales);
+    k_mx_quant_group_t<<<grid, 256, 0, st>>>(g, src, C, (uint8_t*)codes, (uint8_t*)scales);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
