@@ -124,17 +124,18 @@ Layout make_layout(const Geom& g) {
         L.dyq = take((size_t)g.T * H);
         L.dys = take((size_t)g.T * H / 32);
         // transposed, row-quantised operands of the weight gradients (one macrobatch,
-        // group-major); kcap bounds the macrobatch's rows padded group by group to 32
+        // group-major); kcap bounds the macrobatch's rows padded group by group to 32.
+        // Scale regions keep 16 spare bytes: their reader loads aligned words.
         L.kcap = (int64_t)align_up(Sm + 32 * (size_t)g.E, 128);
         const size_t kc = (size_t)L.kcap;
         L.tr_wdy = take(H * kc);
-        L.tr_wdys = take(H * kc / 32);
+        L.tr_wdys = take(H * kc / 32 + 16);
         L.tr_h = take(I * kc);
-        L.tr_hs = take(I * kc / 32);
+        L.tr_hs = take(I * kc / 32 + 16);
         L.tr_dgu = take(2 * I * kc);
-        L.tr_dgus = take(2 * I * kc / 32);
+        L.tr_dgus = take(2 * I * kc / 32 + 16);
         L.tr_x = take(H * kc);
-        L.tr_xs = take(H * kc / 32);
+        L.tr_xs = take(H * kc / 32 + 16);
         L.blk_off = take((size_t)(g.E + 1) * 4);
     }
     const size_t M = (size_t)g.M;

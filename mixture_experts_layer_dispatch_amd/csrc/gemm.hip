@@ -237,9 +237,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
 // rows (one K step, the common case for small token counts) the A tile stays
 // in LDS for all of them and the next B tile is fetched while the current one
 // is multiplied; otherwise each column tile runs the K loop.
-template <class SA, class SB, class Epi>
-__device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
-                                            int nt0, int ntn, uint16_t* smem, const Epi& epi) {
+template <bool BF16_ONLY, class SA, class SB>
+__device__ __forceinline__ void wgrad_tiles_(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
+                                             int nt0, int ntn, uint16_t* smem, const WgradEpi& epi) {
     uint16_t* sA = smem;
     uint16_t* sB = smem + Tile<W_TM, true>::SIZE;
     const int w = threadIdx.x >> 6;
@@ -263,7 +263,7 @@ __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, S
                 mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
                 __syncthreads();
             }
-            epi(nt0 + i, acc, sB);
+            epi.template store<BF16_ONLY>(nt0 + i, acc, sB);
         }
         return;
     }
@@ -279,9 +279,16 @@ __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, S
             mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
             __syncthreads();
         }
-        epi(nt0 + i, acc, sB);
+        epi.template store<BF16_ONLY>(nt0 + i, acc, sB);
         __syncthreads();
     }
+}
+
+template <class SA, class SB>
+__device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
+                                            int nt0, int ntn, uint16_t* smem, const WgradEpi& epi) {
+    if (epi.out.mode == 0) wgrad_tiles_<true>(la, lb, nk, nt0, ntn, smem, epi);
+    else wgrad_tiles_<false>(la, lb, nk, nt0, ntn, smem, epi);
 }
 
 // dW_down[e][h, i] = sum over e's rows r of dy[tok(r), h] * hw[r, i].

@@ -414,11 +414,13 @@ struct WgradEpi {
     int m0;          // first output row of the slab
     // bf16 output (mode 0) goes through LDS so that every global store writes
     // whole 128-byte row segments; the fp32 accumulation modes store directly.
-    __device__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32],
-                               uint16_t* stage) const {
+    // BF16_ONLY: the caller has checked mode == 0, so the stores are
+    // unconditional and the compiler can count them in its memory waits.
+    template <bool BF16_ONLY>
+    __device__ void store(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32], uint16_t* stage) const {
         AccPos<W_TM, W_TN> pos;
         const int n0 = nt * W_TN;
-        if (out.mode != 0) {
+        if (!BF16_ONLY && out.mode != 0) {
 #pragma unroll
             for (int mb = 0; mb < W_TM / 32; ++mb)
 #pragma unroll
@@ -442,6 +444,10 @@ struct WgradEpi {
             *(uint4*)(out.out + ebase + (int64_t)(m0 + r) * ld + n0 + cc * 8) =
                 *(const uint4*)(stage + r * W_SP + cc * 8);
         }
+    }
+    __device__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32],
+                               uint16_t* stage) const {
+        store<false>(nt, acc, stage);
     }
 };
 

@@ -532,32 +532,105 @@ struct LoadScalesPad {         // scale bytes of blocks at or past nblk read as 
     int64_t ld, b0;
     const uint8_t* p;
     int nblk;
-    uint32_t v;
+    uint32_t w0, w1, sh, mask;
     __device__ LoadScalesPad(const uint8_t* bs, int64_t l, int row0, int64_t b, int nb)
-        : base(bs), ld(l), b0(b), p(nullptr), nblk(nb), v(0) {
+        : base(bs), ld(l), b0(b), p(nullptr), nblk(nb), w0(0), w1(0), sh(0), mask(0) {
         retarget(row0);
     }
     __device__ void retarget(int row0) {
         p = threadIdx.x < ROWS ? base + (int64_t)(row0 + threadIdx.x) * ld + b0 : nullptr;
     }
+    // Four scale bytes from an arbitrary byte address: two aligned words, put
+    // together by a byte funnel shift when they are stored, so that neither
+    // byte loads nor an early wait hold up the loads issued with them (the
+    // words may reach up to 7 bytes past the row; the scale regions keep spare
+    // bytes for that).
     __device__ void load(int kt) {
-        v = 0;
-        if (!p) return;
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (4 * kt + j < nblk) v |= (uint32_t)p[4 * kt + j] << (8 * j);
+        const int rem = nblk - 4 * kt;
+        mask = 0;
+        if (!p || rem <= 0) return;
+        const uintptr_t a = (uintptr_t)(p + 4 * kt);
+        const uint32_t* w = (const uint32_t*)(a & ~(uintptr_t)3);
+        w0 = w[0];
+        w1 = w[1];
+        sh = (uint32_t)(a & 3);
+        mask = rem < 4 ? (1u << (8 * rem)) - 1u : ~0u;
     }
     __device__ void store(uint32_t* s) const {
-        if (threadIdx.x < ROWS) s[threadIdx.x] = v;
+        if (threadIdx.x < ROWS) s[threadIdx.x] = mask ? __builtin_amdgcn_alignbyte(w1, w0, sh) & mask : 0u;
     }
 };
 
 constexpr int X_STAGE = SmemMX<X_TM, X_TN>::STAGE;
 constexpr int X_SMEM = X_STAGE + X_TM * W_SP;
 
+// The column-tile walk of one weight-gradient block (A: 128 rows, B: the
+// current 64-row column tile).
+template <bool BF16_ONLY>
+__device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPad<X_TM>& sa,
+                                               LoadKCPad<X_TN>& lb, LoadScalesPad<X_TN>& sb,
+                                               int nk, int nt0, int ntn, uint16_t* smem,
+                                               const WgradEpi& epi) {
+    using SM = SmemMX<X_TM, X_TN>;
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (X_TM / 2), wn0 = (w >> 1) * (X_TN / 2);
+    uint16_t* stage = smem + X_STAGE;
+    uint32_t* cA = (uint32_t*)(smem + SM::A + SM::B);
+    uint32_t* cB = cA + X_TM;
+    f32x4 acc[X_TM / 32][X_TN / 32];
+    if (nk <= 1) {
+        // one K step: A stays in LDS; the next column tile is fetched while the
+        // current one is multiplied and written out
+        if (nk == 1) {
+            la.load(0);
+            sa.load(0);
+            lb.load(0);
+            sb.load(0);
+            la.store(smem);
+            sa.store(cA);
+        }
+        for (int i = 0; i < ntn; ++i) {
+            zero_acc<X_TM, X_TN>(acc);
+            if (nk == 1) {
+                if (i > 0) __syncthreads();            // MFMAs and staged stores of tile i-1 done
+                lb.store(smem + SM::A);
+                sb.store(cB);
+                __syncthreads();
+                if (i + 1 < ntn) {
+                    lb.retarget((nt0 + i + 1) * X_TN);
+                    sb.retarget((nt0 + i + 1) * X_TN);
+                    lb.load(0);
+                    sb.load(0);
+                }
+                mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
+            }
+            epi.template store<BF16_ONLY>(nt0 + i, acc, stage);
+        }
+        return;
+    }
+    for (int i = 0; i < ntn; ++i) {
+        lb.retarget((nt0 + i) * X_TN);
+        sb.retarget((nt0 + i) * X_TN);
+        zero_acc<X_TM, X_TN>(acc);
+        for (int kt = 0; kt < nk; ++kt) {
+            la.load(kt);
+            sa.load(kt);
+            lb.load(kt);
+            sb.load(kt);
+            __syncthreads();                           // the previous step's MFMAs are done
+            la.store(smem);
+            sa.store(cA);
+            lb.store(smem + SM::A);
+            sb.store(cB);
+            __syncthreads();
+            mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
+        }
+        epi.template store<BF16_ONLY>(nt0 + i, acc, stage);
+    }
+}
+
 __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[X_SMEM];
-    using SM = SmemMX<X_TM, X_TN>;
     const int ntiles = a.N / X_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
     const int nMt = a.M / X_TM;
     const int per = nMt * nng;
@@ -593,65 +666,12 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     RowsPadK ra{aq, kcodes, m0, 0};
     LoadKCPad<X_TM> la(ra, kcodes);
     LoadScalesPad<X_TM> sa(as_, kcodes / 32, m0, 0, kcodes / 32);
-    const int w = threadIdx.x >> 6;
-    const int wm0 = (w & 1) * (X_TM / 2), wn0 = (w >> 1) * (X_TN / 2);
-    uint16_t* stage = smem + X_STAGE;
     const int nt0 = ng * W_NPW, ntn = min(W_NPW, ntiles - nt0);
-    uint32_t* cA = (uint32_t*)(smem + SM::A + SM::B);
-    uint32_t* cB = cA + X_TM;
-    f32x4 acc[X_TM / 32][X_TN / 32];
     RowsPadK rb{bq, kcodes, nt0 * X_TN, 0};
     LoadKCPad<X_TN> lb(rb, kcodes);
     LoadScalesPad<X_TN> sb(bs, kcodes / 32, nt0 * X_TN, 0, kcodes / 32);
-    if (nk <= 1) {
-        // one K step: A stays in LDS; the next column tile is fetched while the
-        // current one is multiplied and written out
-        if (nk == 1) {
-            la.load(0);
-            sa.load(0);
-            lb.load(0);
-            sb.load(0);
-            la.store(smem);
-            sa.store(cA);
-        }
-        for (int i = 0; i < ntn; ++i) {
-            zero_acc<X_TM, X_TN>(acc);
-            if (nk == 1) {
-                if (i > 0) __syncthreads();            // MFMAs and staged stores of tile i-1 done
-                lb.store(smem + SM::A);
-                sb.store(cB);
-                __syncthreads();
-                if (i + 1 < ntn) {
-                    lb.retarget((nt0 + i + 1) * X_TN);
-                    sb.retarget((nt0 + i + 1) * X_TN);
-                    lb.load(0);
-                    sb.load(0);
-                }
-                mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
-            }
-            epi(nt0 + i, acc, stage);
-        }
-        return;
-    }
-    for (int i = 0; i < ntn; ++i) {
-        lb.retarget((nt0 + i) * X_TN);
-        sb.retarget((nt0 + i) * X_TN);
-        zero_acc<X_TM, X_TN>(acc);
-        for (int kt = 0; kt < nk; ++kt) {
-            la.load(kt);
-            sa.load(kt);
-            lb.load(kt);
-            sb.load(kt);
-            __syncthreads();                           // the previous step's MFMAs are done
-            la.store(smem);
-            sa.store(cA);
-            lb.store(smem + SM::A);
-            sb.store(cB);
-            __syncthreads();
-            mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
-        }
-        epi(nt0 + i, acc, stage);
-    }
+    if (epi.out.mode == 0) wgrad_mx_tiles<true>(la, sa, lb, sb, nk, nt0, ntn, smem, epi);
+    else wgrad_mx_tiles<false>(la, sa, lb, sb, nk, nt0, ntn, smem, epi);
 }
 
 // ================================================================ launchers
