@@ -11,6 +11,18 @@ constexpr int kWave = 64;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// ---------------------------------------------------------------- address spaces
+// Choosing between two global pointers with a per-lane select hides their
+// address space from the compiler, which then emits FLAT loads (counted
+// against the LDS wait counter too); the explicit global cast keeps them
+// global loads.
+template <class T>
+__device__ __forceinline__ const T* global_select(bool second, const T* a, const T* b) {
+    typedef const __attribute__((address_space(1))) T gT;
+    gT* p = second ? (gT*)b : (gT*)a;
+    return (const T*)p;
+}
+
 // ---------------------------------------------------------------- bf16 bits
 __device__ __forceinline__ float bf2f(uint32_t b16) { return __uint_as_float(b16 << 16); }
 

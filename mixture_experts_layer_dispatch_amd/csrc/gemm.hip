@@ -232,14 +232,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
 // ================================================================ weight gradients
 // K-grouped: C_e[M, N] = sum over e's rows (ascending) of A[r, M] (x) B[r, N];
 // both operands are KS tiles.  A block owns one expert's 128-row slab of C and
-// up to W_NPW consecutive 64-column tiles of it (whole rows for N <= 4096, so
+// its 64-column tiles g, g + ng, ... (dealt round robin over ng blocks, so
 // each block writes one contiguous region).  When the expert has at most kTK
 // rows (one K step, the common case for small token counts) the A tile stays
 // in LDS for all of them and the next B tile is fetched while the current one
 // is multiplied; otherwise each column tile runs the K loop.
 template <bool BF16_ONLY, class SA, class SB>
 __device__ __forceinline__ void wgrad_tiles_(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
-                                             int nt0, int ntn, uint16_t* smem, const WgradEpi& epi) {
+                                             int nt0, int ntn, int nstride, uint16_t* smem,
+                                             const WgradEpi& epi) {
     uint16_t* sA = smem;
     uint16_t* sB = smem + Tile<W_TM, true>::SIZE;
     const int w = threadIdx.x >> 6;
@@ -259,16 +260,16 @@ __device__ __forceinline__ void wgrad_tiles_(LoadKS<W_TM, SA>& la, LoadKS<W_TN, 
                 if (i > 0) __syncthreads();          // the staged tile has been written out
                 lb.store(sB);
                 __syncthreads();
-                if (i + 1 < ntn) lb.load_cached((nt0 + i + 1) * W_TN);
+                if (i + 1 < ntn) lb.load_cached((nt0 + (i + 1) * nstride) * W_TN);
                 mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
                 __syncthreads();
             }
-            epi.template store<BF16_ONLY>(nt0 + i, acc, sB);
+            epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, sB);
         }
         return;
     }
     for (int i = 0; i < ntn; ++i) {
-        lb.src.col0 = (nt0 + i) * W_TN;
+        lb.src.col0 = (nt0 + i * nstride) * W_TN;
         zero_acc<W_TM, W_TN>(acc);
         for (int kt = 0; kt < nk; ++kt) {
             la.load(kt);
@@ -279,22 +280,24 @@ __device__ __forceinline__ void wgrad_tiles_(LoadKS<W_TM, SA>& la, LoadKS<W_TN, 
             mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
             __syncthreads();
         }
-        epi.template store<BF16_ONLY>(nt0 + i, acc, sB);
+        epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, sB);
         __syncthreads();
     }
 }
 
 template <class SA, class SB>
 __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
-                                            int nt0, int ntn, uint16_t* smem, const WgradEpi& epi) {
-    if (epi.out.mode == 0) wgrad_tiles_<true>(la, lb, nk, nt0, ntn, smem, epi);
-    else wgrad_tiles_<false>(la, lb, nk, nt0, ntn, smem, epi);
+                                            int ntiles, int g, int ng, uint16_t* smem,
+                                            const WgradEpi& epi) {
+    const int ntn = wgrad_group_tiles(ntiles, ng, g);
+    if (epi.out.mode == 0) wgrad_tiles_<true>(la, lb, nk, g, ntn, ng, smem, epi);
+    else wgrad_tiles_<false>(la, lb, nk, g, ntn, ng, smem, epi);
 }
 
 // dW_down[e][h, i] = sum over e's rows r of dy[tok(r), h] * hw[r, i].
 __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[W_SMEM];
-    const int ntiles = a.I / W_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    const int ntiles = a.I / W_TN, nng = wgrad_groups(ntiles);
     int e, mt, ng, lo, n;
     if (!map_ktile(a.g, a.H / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
     const int m0 = mt * W_TM;
@@ -305,11 +308,11 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
     if (a.dy_gather) {
         KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
         LoadKS<W_TM, KRowsGroupGather> la(sa);
-        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
+        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
     } else {
         KRowsGroup sa{a.dy, a.H, a.dyrow0 + lo, n, m0};
         LoadKS<W_TM, KRowsGroup> la(sa);
-        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
+        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
     }
 }
 
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
 // M runs over the 2I columns of [dg | du].
 __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[W_SMEM];
-    const int ntiles = a.H / W_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    const int ntiles = a.H / W_TN, nng = wgrad_groups(ntiles);
     int e, mt, ng, lo, n;
     if (!map_ktile(a.g, 2 * a.I / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
     const int m0 = mt * W_TM;
@@ -329,11 +332,11 @@ __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
     if (a.x_gather) {
         KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, 0, a.k, a.S, a.g.err};
         LoadKS<W_TN, KRowsGroupGather> lb(sb);
-        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
+        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
     } else {
         KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, 0};
         LoadKS<W_TN, KRowsGroup> lb(sb);
-        wgrad_tiles(la, lb, nk, ng * W_NPW, min(W_NPW, ntiles - ng * W_NPW), smem, epi);
+        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
     }
 }
 
@@ -379,14 +382,14 @@ int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
 
 int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_down");
-    const int grid = (a.g.offsets ? a.g.E : 1) * (a.H / W_TM) * ((a.I / W_TN + W_NPW - 1) / W_NPW);
+    const int grid = (a.g.offsets ? a.g.E : 1) * (a.H / W_TM) * wgrad_groups(a.I / W_TN);
     k_wgrad_down<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_gate_up");
-    const int grid = (a.g.offsets ? a.g.E : 1) * (2 * a.I / W_TM) * ((a.H / W_TN + W_NPW - 1) / W_NPW);
+    const int grid = (a.g.offsets ? a.g.E : 1) * (2 * a.I / W_TM) * wgrad_groups(a.H / W_TN);
     k_wgrad_gate_up<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }

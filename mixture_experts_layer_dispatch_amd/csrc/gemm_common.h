@@ -50,19 +50,24 @@ struct RowsGateUp {
     __device__ const uint16_t* row(int n) const {
         const int q = n >> 5;
         const int i = i0 + ((q >> 1) << 5) + (n & 31);
-        return ((q & 1) ? wu : wg) + (int64_t)i * ld;
+        return global_select(q & 1, wg, wu) + (int64_t)i * ld;
     }
 };
 
 // Operand whose reduction index k is the memory row: krow(k) points at the
 // tile's first column in memory row k.
+// Every K-row source also splits krow into pre(k) (the loads it needs, issued
+// for a whole batch of rows first) and at(k, pre), so that gathered rows cost
+// one round trip per batch instead of one per row.
 struct KRowsDirect {
     const uint16_t* base;
     int64_t ld;
     int col0, kmax;
-    __device__ const uint16_t* krow(int kk) const {
+    __device__ int pre(int) const { return 0; }
+    __device__ const uint16_t* at(int kk, int) const {
         return kk < kmax ? base + (int64_t)kk * ld + col0 : nullptr;
     }
+    __device__ const uint16_t* krow(int kk) const { return at(kk, 0); }
 };
 
 // k < I: W_gate row k; I <= k < 2I: W_up row k - I.
@@ -71,11 +76,13 @@ struct KRowsGateUp {
     const uint16_t* wu;
     int64_t ld;
     int col0, I;
-    __device__ const uint16_t* krow(int kk) const {
+    __device__ int pre(int) const { return 0; }
+    __device__ const uint16_t* at(int kk, int) const {
         if (kk < I) return wg + (int64_t)kk * ld + col0;
         if (kk < 2 * I) return wu + (int64_t)(kk - I) * ld + col0;
         return nullptr;
     }
+    __device__ const uint16_t* krow(int kk) const { return at(kk, 0); }
 };
 
 // k = the k-th row of a group: memory row row0 + k.
@@ -83,9 +90,11 @@ struct KRowsGroup {
     const uint16_t* base;
     int64_t ld;
     int row0, n, col0;
-    __device__ const uint16_t* krow(int kk) const {
+    __device__ int pre(int) const { return 0; }
+    __device__ const uint16_t* at(int kk, int) const {
         return kk < n ? base + (int64_t)(row0 + kk) * ld + col0 : nullptr;
     }
+    __device__ const uint16_t* krow(int kk) const { return at(kk, 0); }
 };
 
 // k = the k-th row of a group in schedule rows; memory row = its token.
@@ -95,15 +104,16 @@ struct KRowsGroupGather {
     const int32_t* slot_of_row;
     int grow0, n, col0, k, S;
     int32_t* err;
-    __device__ const uint16_t* krow(int kk) const {
+    __device__ int pre(int kk) const { return kk < n ? slot_of_row[grow0 + kk] : 0; }
+    __device__ const uint16_t* at(int kk, int s) const {
         if (kk >= n) return nullptr;
-        const int s = slot_of_row[grow0 + kk];
         if ((unsigned)s >= (unsigned)S) {
             raise_err(err, ERR_BAD_SLOT);
             return nullptr;
         }
         return base + (int64_t)(s / k) * ld + col0;
     }
+    __device__ const uint16_t* krow(int kk) const { return at(kk, pre(kk)); }
 };
 
 // ================================================================ LDS tiles
@@ -173,9 +183,12 @@ struct LoadKS {
         }
     }
     __device__ void load(int kt) {
+        int pr[PER];
+#pragma unroll
+        for (int q = 0; q < PER; ++q) pr[q] = src.pre(kt * kTK + kr[q]);
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const uint16_t* a = src.krow(kt * kTK + kr[q]);
+            const uint16_t* a = src.at(kt * kTK + kr[q], pr[q]);
             v[q] = a ? *(const uint4*)(a + cc[q] * 8) : make_uint4(0, 0, 0, 0);
         }
     }
@@ -187,8 +200,11 @@ struct LoadKS {
     // the column window (src.col0 must be 0 when this is called).
     const uint16_t* rp[PER];
     __device__ void cache_rows(int kt) {
+        int pr[PER];
 #pragma unroll
-        for (int q = 0; q < PER; ++q) rp[q] = src.krow(kt * kTK + kr[q]);
+        for (int q = 0; q < PER; ++q) pr[q] = src.pre(kt * kTK + kr[q]);
+#pragma unroll
+        for (int q = 0; q < PER; ++q) rp[q] = src.at(kt * kTK + kr[q], pr[q]);
     }
     __device__ void load_cached(int col) {
 #pragma unroll
@@ -387,7 +403,21 @@ __device__ __forceinline__ bool map_ktile(const GroupRows& g, int nMt, int nNt, 
 // ================================================================ weight-gradient tiles
 // Shared by the bf16 and MXFP8 weight gradients: a block owns one expert's
 // 128-row slab of the output and walks its 64-column tiles.
-constexpr int W_TM = 128, W_TN = 64, W_NPW = 64;
+constexpr int W_TM = 128, W_TN = 64;
+// The column tiles of a slab are dealt to up to W_G blocks round robin
+// (block g: tiles g, g + ng, ...), so that ng neighbouring 128-byte pieces of
+// each row are written at about the same time (a plain store kernel of this
+// tile shape measured ~5.0 TB/s walking whole rows per block, ~5.7 TB/s dealt
+// over 8 blocks, but less over 2 or 4).  Slabs of fewer than W_G * W_MIN_TILES
+// tiles stay whole: there, loading the A slab once per block dominates.
+constexpr int W_G = 8, W_MIN_TILES = 8;
+__host__ __device__ __forceinline__ int wgrad_groups(int ntiles) {
+    return ntiles >= W_G * W_MIN_TILES ? W_G : 1;
+}
+// tiles of group g out of ng groups over ntiles
+__host__ __device__ __forceinline__ int wgrad_group_tiles(int ntiles, int ng, int g) {
+    return (ntiles - g + ng - 1) / ng;
+}
 
 // LDS of a weight-gradient block: the resident A tile, then a region that
 // holds the B tile during the MFMAs and the bf16 output tile afterwards.

@@ -39,7 +39,7 @@ struct ScalesGateUp {          // same quarter interleave as RowsGateUp
     __device__ const uint32_t* row(int n) const {
         const int q = n >> 5;
         const int i = i0 + ((q >> 1) << 5) + (n & 31);
-        return ((q & 1) ? wu : wg) + (int64_t)i * ld;
+        return global_select(q & 1, wg, wu) + (int64_t)i * ld;
     }
 };
 
@@ -549,11 +549,11 @@ struct LoadScalesPad {         // scale bytes of blocks at or past nblk read as 
         const int rem = nblk - 4 * kt;
         mask = 0;
         if (!p || rem <= 0) return;
-        const uintptr_t a = (uintptr_t)(p + 4 * kt);
-        const uint32_t* w = (const uint32_t*)(a & ~(uintptr_t)3);
+        const uint8_t* q = p + 4 * kt;
+        sh = (uint32_t)((uintptr_t)q & 3);
+        const uint32_t* w = (const uint32_t*)(q - sh);      // pointer arithmetic keeps it global
         w0 = w[0];
         w1 = w[1];
-        sh = (uint32_t)(a & 3);
         mask = rem < 4 ? (1u << (8 * rem)) - 1u : ~0u;
     }
     __device__ void store(uint32_t* s) const {
@@ -569,7 +569,7 @@ constexpr int X_SMEM = X_STAGE + X_TM * W_SP;
 template <bool BF16_ONLY>
 __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPad<X_TM>& sa,
                                                LoadKCPad<X_TN>& lb, LoadScalesPad<X_TN>& sb,
-                                               int nk, int nt0, int ntn, uint16_t* smem,
+                                               int nk, int nt0, int ntn, int nstride, uint16_t* smem,
                                                const WgradEpi& epi) {
     using SM = SmemMX<X_TM, X_TN>;
     const int w = threadIdx.x >> 6;
@@ -597,20 +597,20 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
                 sb.store(cB);
                 __syncthreads();
                 if (i + 1 < ntn) {
-                    lb.retarget((nt0 + i + 1) * X_TN);
-                    sb.retarget((nt0 + i + 1) * X_TN);
+                    lb.retarget((nt0 + (i + 1) * nstride) * X_TN);
+                    sb.retarget((nt0 + (i + 1) * nstride) * X_TN);
                     lb.load(0);
                     sb.load(0);
                 }
                 mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
             }
-            epi.template store<BF16_ONLY>(nt0 + i, acc, stage);
+            epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, stage);
         }
         return;
     }
     for (int i = 0; i < ntn; ++i) {
-        lb.retarget((nt0 + i) * X_TN);
-        sb.retarget((nt0 + i) * X_TN);
+        lb.retarget((nt0 + i * nstride) * X_TN);
+        sb.retarget((nt0 + i * nstride) * X_TN);
         zero_acc<X_TM, X_TN>(acc);
         for (int kt = 0; kt < nk; ++kt) {
             la.load(kt);
@@ -625,13 +625,13 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
             __syncthreads();
             mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
         }
-        epi.template store<BF16_ONLY>(nt0 + i, acc, stage);
+        epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, stage);
     }
 }
 
 __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[X_SMEM];
-    const int ntiles = a.N / X_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
     const int nMt = a.M / X_TM;
     const int per = nMt * nng;
     const int total = (a.g.blk_off ? a.g.E : 1) * per;
@@ -666,12 +666,12 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     RowsPadK ra{aq, kcodes, m0, 0};
     LoadKCPad<X_TM> la(ra, kcodes);
     LoadScalesPad<X_TM> sa(as_, kcodes / 32, m0, 0, kcodes / 32);
-    const int nt0 = ng * W_NPW, ntn = min(W_NPW, ntiles - nt0);
+    const int nt0 = ng, ntn = wgrad_group_tiles(ntiles, nng, ng);
     RowsPadK rb{bq, kcodes, nt0 * X_TN, 0};
     LoadKCPad<X_TN> lb(rb, kcodes);
     LoadScalesPad<X_TN> sb(bs, kcodes / 32, nt0 * X_TN, 0, kcodes / 32);
-    if (epi.out.mode == 0) wgrad_mx_tiles<true>(la, sa, lb, sb, nk, nt0, ntn, smem, epi);
-    else wgrad_mx_tiles<false>(la, sa, lb, sb, nk, nt0, ntn, smem, epi);
+    if (epi.out.mode == 0) wgrad_mx_tiles<true>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
+    else wgrad_mx_tiles<false>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
 }
 
 // ================================================================ launchers
@@ -715,7 +715,7 @@ int launch_gemm_gu_dgrad_mx(const GemmGuDgradMXArgs& a, hipStream_t st) {
 
 int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, a.msplit < a.M ? "wgrad_gate_up_mx" : "wgrad_down_mx");
-    const int ntiles = a.N / X_TN, nng = (ntiles + W_NPW - 1) / W_NPW;
+    const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
     const int grid = (a.g.blk_off ? a.g.E : 1) * (a.M / X_TM) * nng;
     if (grid <= 0) return 0;
     k_wgrad_mx<<<grid, 256, 0, st>>>(a);

@@ -24,6 +24,16 @@ SHAPES = {
     "ragged": si.custom_shape("ragged_mx", T=100, H=256, I=256, E=7, k=3, seed=21),
     "ring_shared": si.custom_shape("ring_shared_mx", T=512, H=256, I=128, E=16, k=4, seed=22,
                                    n_shared=1, macrobatch=128, minibatch=64),
+    # hot experts past one K step of the weight gradients (zipf), and experts
+    # with many rows each (the 128-row weight-gradient slabs)
+    "zipf_ring": si.custom_shape("zipf_ring_mx", T=1024, H=256, I=128, E=32, k=4, seed=23,
+                                 macrobatch=256, minibatch=128, zipf=True),
+    "dense_experts": si.custom_shape("dense_experts_mx", T=512, H=256, I=256, E=8, k=4, seed=24),
+    # column-stripe weight gradients (experts padded to at most 64 codes) next
+    # to the slab kernel, and their fp32 accumulation across macrobatches
+    "stripes": si.custom_shape("stripes_mx", T=256, H=512, I=512, E=16, k=4, seed=25),
+    "stripes_ring": si.custom_shape("stripes_ring_mx", T=512, H=512, I=1024, E=32, k=2, seed=26,
+                                    n_shared=1, macrobatch=256, minibatch=128),
 }
 
 

@@ -24,6 +24,12 @@ SMALL = {
                                    n_shared=1, macrobatch=128, minibatch=64),
     "zipf_ring": si.custom_shape("zipf_ring", T=1024, H=128, I=128, E=32, k=4, seed=15,
                                  macrobatch=256, minibatch=128, zipf=True),
+    # output widths that are multiples of 512: the column-stripe weight
+    # gradients take the experts with at most 64 rows, the slab kernels the
+    # rest; the ring variant accumulates them across two macrobatches in fp32
+    "stripes": si.custom_shape("stripes", T=256, H=512, I=512, E=16, k=4, seed=17),
+    "stripes_ring": si.custom_shape("stripes_ring", T=512, H=512, I=1024, E=32, k=2, seed=18,
+                                    n_shared=1, macrobatch=256, minibatch=128),
 }
 
 
