@@ -27,7 +27,7 @@ import time
 
 import numpy as np
 
-WORKLOADS = ("e512_t2048",)
+WORKLOADS = ("e512_t2048", "e512_t65536_zipf")
 HBM_PEAK_GBS = 8000.0
 
 
@@ -167,6 +167,9 @@ def main():
     case.dy = si.grad_out(shape, "cuda")
     case.wg, case.wu, case.wd = si.all_expert_weights(shape, "cuda")
     weights = {"w_gate": case.wg, "w_up": case.wu, "w_down": case.wd}
+    shared = si.shared_weights(shape, "cuda")
+    if shared is not None:
+        weights.update({"s_gate": shared[0], "s_up": shared[1], "s_down": shared[2]})
     sched = B.alloc_schedule(cfg)
     y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
     dx = torch.empty_like(y)

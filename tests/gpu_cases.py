@@ -86,3 +86,18 @@ class Case:
 
     def shared_np(self):
         return None if self.sw is None else tuple(f32(a) for a in self.sw)
+
+
+def ring_samples(case, sch, n_tokens=12, seed=5):
+    """Sampled tokens spread over the macrobatches (the first and last token of
+    each included) and two weight-gradient experts: the coldest routed expert
+    and a median one."""
+    rng = np.random.default_rng(seed)
+    T, M = case.shape.T, case.shape.macrobatch
+    edges = [m * M for m in range(T // M)] + [m * M - 1 for m in range(1, T // M + 1)]
+    tokens = np.unique(np.concatenate([rng.choice(T, size=n_tokens, replace=False), edges]))
+    counts = sch["counts"].sum(0)
+    routed = np.nonzero(counts)[0]
+    cold = int(routed[np.argmin(counts[routed])])
+    mid = int(routed[np.argsort(counts[routed])[len(routed) // 2]])
+    return tokens, sorted({cold, mid})

@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from gpu_cases import Case, assert_close, f32
+from gpu_cases import Case, assert_close, f32, ring_samples
 
 pytestmark = pytest.mark.gpu
 
@@ -189,6 +189,33 @@ def test_backward_mx_full_size_sampled():
     experts = [int(idx[0, 0]), 300]
     rb = oracle.backward(f32(c.x), c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd),
                          idx, w, f32(c.dy), mx=True, sched=sch, tokens=tokens, experts=experts)
+    assert_close("dx[sampled] (mxfp8)", f32(c.dx)[tokens], rb["dx"], MX_TOL)
+    assert_close("dw[sampled] (mxfp8)", c.dw.cpu().numpy()[tokens], rb["dw"], MX_TOL)
+    for e in experts:
+        assert_close(f"dW_gate[{e}] (mxfp8)", f32(c.grads["d_w_gate"][e]), rb["dWg"][e], MX_TOL)
+        assert_close(f"dW_up[{e}] (mxfp8)", f32(c.grads["d_w_up"][e]), rb["dWu"][e], MX_TOL)
+        assert_close(f"dW_down[{e}] (mxfp8)", f32(c.grads["d_w_down"][e]), rb["dWd"][e], MX_TOL)
+
+
+def test_forward_backward_mx_ring_full_size_sampled():
+    """MXFP8 on the 65 536-token Zipf workload: four macrobatches, the shared
+    expert, per-macrobatch 32-row blocks of the weight-gradient operands."""
+    c = MXCase(si.SHAPES["e512_t65536_zipf"])
+    c.schedule()
+    c.forward()
+    c.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(c.ws) == 0
+    idx, w, sch = c.oracle_schedule()
+    assert np.array_equal(c.sched["topk_idx"].cpu().numpy(), idx)
+    tokens, experts = ring_samples(c, sch)
+    x, dy = f32(c.x), f32(c.dy)
+    wgv, wuv, wdv = c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd)
+    ref = oracle.forward(x, wgv, wuv, wdv, idx, w, shared=c.shared_np(), tokens=tokens, mx=True)
+    assert_close("y[sampled] (mxfp8)", f32(c.y)[tokens], ref["y"], MX_TOL)
+    rb = oracle.backward(x, wgv, wuv, wdv, idx, w, dy, shared=c.shared_np(), mx=True, sched=sch,
+                         tokens=tokens, experts=experts)
     assert_close("dx[sampled] (mxfp8)", f32(c.dx)[tokens], rb["dx"], MX_TOL)
     assert_close("dw[sampled] (mxfp8)", c.dw.cpu().numpy()[tokens], rb["dw"], MX_TOL)
     for e in experts:

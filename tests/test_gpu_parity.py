@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from gpu_cases import Case, assert_close, f32
+from gpu_cases import Case, assert_close, f32, ring_samples
 
 pytestmark = pytest.mark.gpu
 
@@ -225,3 +225,32 @@ def test_forward_backward_full_size_sampled():
     counts = sch["counts"][0]
     n = case.grads["d_w_down"].float().flatten(1).abs().amax(1).cpu().numpy()
     assert np.all(np.isfinite(n)) and np.all((n == 0) == (counts == 0))
+
+
+def test_forward_backward_ring_full_size_sampled():
+    """The 65 536-token Zipf workload at full size: four macrobatches through
+    the ring (two halves, minibatch dispatch), a shared expert, and the weight
+    gradients summed over the reverse macrobatch walk in fp32."""
+    case = Case(si.SHAPES["e512_t65536_zipf"])
+    case.schedule()
+    idx, w, sch = _check_schedule(case)
+    case.forward()
+    case.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(case.ws) == 0
+    tokens, experts = ring_samples(case, sch)
+    x, dy = f32(case.x), f32(case.dy)
+    wgv, wuv, wdv = case.expert_view(case.wg), case.expert_view(case.wu), case.expert_view(case.wd)
+    ref = oracle.forward(x, wgv, wuv, wdv, idx, w, shared=case.shared_np(), tokens=tokens)
+    assert_close("y[sampled]", f32(case.y)[tokens], ref["y"])
+    rb = oracle.backward(x, wgv, wuv, wdv, idx, w, dy, shared=case.shared_np(), tokens=tokens,
+                         experts=experts)
+    assert_close("dx[sampled]", f32(case.dx)[tokens], rb["dx"])
+    assert_close("dw[sampled]", case.dw.cpu().numpy()[tokens], rb["dw"])
+    dl = oracle.ffn.d_logits_dense(idx, rb["dl_sel"], case.shape.E, tokens=tokens)
+    assert_close("d_logits[sampled]", case.dlogits.cpu().numpy()[tokens], dl)
+    for e in experts:
+        assert_close(f"dW_gate[{e}]", f32(case.grads["d_w_gate"][e]), rb["dWg"][e])
+        assert_close(f"dW_up[{e}]", f32(case.grads["d_w_up"][e]), rb["dWu"][e])
+        assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])
