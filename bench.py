@@ -30,6 +30,12 @@ import numpy as np
 WORKLOADS = ("e512_t2048", "e512_t65536_zipf")
 HBM_PEAK_GBS = 8000.0
 
+# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE on e512_t2048,
+# each scaled by what that counter reads for a copy kernel of known size
+# (FETCH_SIZE counts half of a copy's reads: x2; WRITE_SIZE counts them all);
+# filled in from profiles/, and dropped whenever the kernel changes.
+TRAFFIC = {}
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -71,13 +77,18 @@ def calibrate(torch, nbytes=4 << 30, reps=10):
 
 
 def kernel_bytes(shape, counts: np.ndarray) -> dict:
-    """Algorithmic HBM bytes per launch of each kernel (unique data it must move)."""
+    """Algorithmic HBM bytes per launch of each kernel (the unique data it must
+    move) for a workload that fits one macrobatch.  With several macrobatches
+    the per-launch figures differ per launch, and none are given."""
     T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    if shape.macrobatch and shape.macrobatch < T:
+        return {}
     S = T * k
     used = int(np.count_nonzero(counts))
     P = I // 128
     w_gu = used * 2 * I * H * 2
     w_d = used * H * I * 2
+    q = 1 + 1 / 32                      # an MXFP8 code and its share of a scale byte
     return {
         "topk_route": T * E * 4 + S * 8,
         "dispatch": T * H * 2 + S * H * 2,
@@ -90,6 +101,19 @@ def kernel_bytes(shape, counts: np.ndarray) -> dict:
         "wgrad_gate_up": E * 2 * I * H * 2 + T * H * 2 + S * 2 * I * 2,
         "rd_reduce": S * H * 2 + T * H * 2,
         "softmax_bwd": S * P * 4 + T * E * 4 + S * 12,
+        # MXFP8 leg
+        "dispatch_mx": T * H * 2 + S * H * q,
+        "gemm_gate_up_mx": int(w_gu / 2 * q + S * H * q + 2 * S * I * 4 + S * I * q),
+        "gemm_down_mx": int(w_d / 2 * q + S * I * q + S * H * 2),
+        "gemm_down_dgrad_mx": int(w_d / 2 * q + T * H * q + 4 * S * I * 4 + S * I * 4
+                                  + 2 * S * I * q + S * P * 4),
+        "gemm_gu_dgrad_mx": int(w_gu / 2 * q + 2 * S * I * q + S * H * 2),
+        "wgrad_down_mx": int(E * H * I * 2 + (H + I) * S * q),
+        "wgrad_gate_up_mx": int(E * 2 * I * H * 2 + (2 * I + H) * S * q),
+        "mx_quant_rows": int(T * H * 2 + T * H * q),
+        "mx_qt_wdy": int(T * H * 2 + S * H * q),
+        "mx_qt_x": int(T * H * 2 + S * H * q),
+        "mx_qt_f32": int((3 * S * I * 4 + 3 * S * I * q) / 2),   # mean of its two launches
     }
 
 
@@ -239,10 +263,13 @@ def main():
     kernels = kernel_table(stats)
     dom = max(stats, key=lambda n: stats[n][1])
     dom_avg = stats[dom][1] / stats[dom][0]
-    achieved = kb[dom] / (dom_avg * 1e-3) / 1e9
-    roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
-                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": None, "avg_ms": round(dom_avg, 4), "bytes_per_launch": kb[dom]}
+    roofline = None
+    if dom in kb:
+        achieved = kb[dom] / (dom_avg * 1e-3) / 1e9
+        roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": TRAFFIC.get(dom) if args.workload == "e512_t2048" else None,
+                    "avg_ms": round(dom_avg, 4), "bytes_per_launch": kb[dom]}
 
     mx = None
     if not args.no_mxfp8:

@@ -21,8 +21,9 @@
 // Both operands are staged through LDS in a [row][k] layout (row pitch
 // kTK + 8 bf16 = 144 B, so the 16 rows read by one MFMA fragment hit 16
 // different 16-byte bank groups), double-buffered with one barrier per K step.
-// Operands whose reduction index is the slow memory axis are transposed on
-// the way into LDS (two k rows are packed into one 32-bit word per row).
+// Operands whose reduction index is the slow memory axis are copied into LDS
+// as they lie ([k][row], KS tiles) and read with gfx950's LDS transpose load,
+// which hands each lane four consecutive k of one row.
 // The MFMA is issued with the B tile as its first operand, so each lane's four
 // accumulators are four consecutive output columns (8-byte stores).
 // Each output element is a fixed-order fp32 sum: K steps ascend, and the
