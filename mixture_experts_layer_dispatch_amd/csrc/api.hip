@@ -29,7 +29,7 @@ struct Geom {
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-    size_t err, hist, base, tile_off, ring, ring_half, sh, wacc, total;
+    size_t err, hist, base, tile_off, deep, ring, ring_half, sh, wacc, total;
     // offsets inside one ring half (bytes)
     size_t f_xd, f_h, f_o;            // forward
     size_t f_xs, f_hs;                // MXFP8 forward: scales after the codes (codes at f_xd, f_h)
@@ -95,6 +95,7 @@ Layout make_layout(const Geom& g) {
     L.hist = take(hist_ints * 4);
     L.base = take(hist_ints * 4);
     L.tile_off = take((size_t)g.n_macro * (g.E + 1) * 4);
+    L.deep = take((size_t)(g.E + 1) * 4);        // deep weight-gradient groups of one macrobatch
     const size_t Sm = (size_t)g.Sm, H = g.H, I = g.I;
     L.f_xd = 0;
     L.f_h = align_up(L.f_xd + Sm * H * 2, 256);
@@ -355,7 +356,9 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
                              (const uint8_t*)wq->w_gate_ts, (const uint8_t*)wq->w_up_tq,
                              (const uint8_t*)wq->w_up_ts, g.H, g.I, dxd};
         if (launch_gemm_gu_dgrad_mx(b2, st)) return MOE_ERR_HIP;
-        PadGroups pg{off, blk, g.E, g.Sm, 0, err};
+        int32_t* deep = (int32_t*)(ws + L.deep);
+        if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows_mx(), deep, st)) return MOE_ERR_HIP;
+        PadGroups pg{off, blk, g.E, g.Sm, 0, err, deep, wgrad_deep_rows_mx()};
         QtSrc qwdy{0, dyb, nullptr, g.H, sched->slot_of_row, sched->topk_w, grow0, 0, g.k, g.S};
         QtSrc qh{1, nullptr, h32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
         QtSrc qdgu{1, nullptr, dgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
@@ -386,7 +389,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
                                  (const uint8_t*)wq->s_gate_ts, (const uint8_t*)wq->s_up_tq,
                                  (const uint8_t*)wq->s_up_ts, g.H, g.I, sdx};
             if (launch_gemm_gu_dgrad_mx(c2, st)) return MOE_ERR_HIP;
-            PadGroups pd{nullptr, nullptr, 1, g.M, g.M, err};
+            PadGroups pd{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows_mx()};
             QtSrc sdy{3, dyb, nullptr, g.H, nullptr, nullptr, 0, t0, g.k, g.S};
             QtSrc shh{1, nullptr, sh32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
             QtSrc sdg{1, nullptr, sdgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
@@ -607,7 +610,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         if (launch_gemm_down_dgrad(b1, st)) return MOE_ERR_HIP;
         GemmGuDgradArgs b2{grp, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I, dxd};
         if (launch_gemm_gu_dgrad(b2, st)) return MOE_ERR_HIP;
-        GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err};
+        int32_t* deep = (int32_t*)((char*)workspace + L.deep);
+        if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows(), deep, st)) return MOE_ERR_HIP;
+        GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err, deep, wgrad_deep_rows()};
         WgradDownArgs b3{kgrp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, hw, g.H, g.I,
                          {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode}};
         if (launch_wgrad_down(b3, st)) return MOE_ERR_HIP;
@@ -620,7 +625,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
             uint16_t* sdgu = (uint16_t*)(P.sh() + L.s_dgu);
             uint16_t* shw = (uint16_t*)(P.sh() + L.s_hw);
             uint16_t* sdx = (uint16_t*)(P.sh() + L.s_dx);
-            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows()};
             GemmDownDgradArgs c1{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, nullptr,
                                  (const uint16_t*)w->s_down, g.H, g.I, (const uint16_t*)saved->sg,
                                  (const uint16_t*)saved->su, t0, sdgu, shw, nullptr, g.P};

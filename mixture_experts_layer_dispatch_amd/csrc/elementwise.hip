@@ -190,6 +190,33 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict_
     if (e == E - 1) tile_off[E] = wpre + incl;
 }
 
+// Experts whose group has more than thr rows, in ascending order:
+// list[0] = their count, list[1..] = their ids.  Bad offsets count as empty
+// (the tile prefix reports them).
+__global__ __launch_bounds__(1024) void k_deep_list(const int32_t* __restrict__ offsets, int E,
+                                                    int rows, int thr, int32_t* __restrict__ list) {
+    __shared__ int32_t wsum[16];
+    const int e = threadIdx.x;
+    int f = 0;
+    if (e < E) {
+        const int a = offsets[e], b = offsets[e + 1];
+        f = (a >= 0 && b >= a && b <= rows && b - a > thr) ? 1 : 0;
+    }
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    const unsigned long long m = __ballot(f);
+    const int incl = __popcll(m & ((2ull << lane) - 1ull));
+    if (lane == 63) wsum[wv] = incl;
+    __syncthreads();
+    int wpre = 0;
+    for (int q = 0; q < wv; ++q) wpre += wsum[q];
+    if (f) list[1 + wpre + incl - 1] = e;
+    if (threadIdx.x == 1023) {
+        int tot = 0;
+        for (int q = 0; q < 16; ++q) tot += wsum[q];
+        list[0] = tot;
+    }
+}
+
 // ============================================================== launchers
 int launch_dispatch(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
                     int ring_row0, int ring_rows, void* ring, int32_t* err, hipStream_t st) {
@@ -236,6 +263,13 @@ int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t*
                        int32_t* err, hipStream_t st) {
     ProfScope prof_(st, "tile_prefix");
     k_tile_prefix<<<1, 1024, 0, st>>>(offsets, E, rows, TM, tile_off, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_deep_list(const int32_t* offsets, int E, int rows, int thr, int32_t* list, hipStream_t st) {
+    ProfScope prof_(st, "deep_list");
+    if (E > 1024) return -1;
+    k_deep_list<<<1, 1024, 0, st>>>(offsets, E, rows, thr, list);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

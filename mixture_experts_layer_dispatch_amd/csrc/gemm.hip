@@ -301,6 +301,7 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
     const int ntiles = a.I / W_TN, nng = wgrad_groups(ntiles);
     int e, mt, ng, lo, n;
     if (!map_ktile(a.g, a.H / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
+    if (a.g.deep_thr > 0 && n > a.g.deep_thr) return;          // the deep kernel's group
     const int m0 = mt * W_TM;
     const int nk = (n + kTK - 1) / kTK;
     KRowsGroup sb{a.hw, a.I, lo, n, 0};
@@ -324,6 +325,7 @@ __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
     const int ntiles = a.H / W_TN, nng = wgrad_groups(ntiles);
     int e, mt, ng, lo, n;
     if (!map_ktile(a.g, 2 * a.I / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
+    if (a.g.deep_thr > 0 && n > a.g.deep_thr) return;          // the deep kernel's group
     const int m0 = mt * W_TM;
     const int nk = (n + kTK - 1) / kTK;
     const bool up = m0 >= a.I;
@@ -338,6 +340,95 @@ __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
         KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, 0};
         LoadKS<W_TN, KRowsGroup> lb(sb);
         wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
+    }
+}
+
+// ---------------------------------------------------------------- deep groups
+// Groups with more than kTK rows (hot experts, the dense shared expert of a
+// large macrobatch) are GEMMs with a real K: 128 x 128 output tiles, the
+// double-buffered K loop, run by a persistent grid over the items (deep group,
+// tile) so that a hot expert's tiles spread over the whole chip.
+constexpr int D_TM = 128, D_TN = 128, D_GRID = 512;
+
+__device__ __forceinline__ int deep_count(const GroupRows& g) {
+    if (g.deep_thr <= 0) return 0;
+    if (g.offsets) return g.deep[0];
+    return g.dense_rows > g.deep_thr ? 1 : 0;
+}
+
+// group d of the deep list -> (expert, first row, rows)
+__device__ __forceinline__ void deep_group(const GroupRows& g, int d, int& e, int& lo, int& n) {
+    if (!g.offsets) {
+        e = 0;
+        lo = 0;
+        n = g.dense_rows;
+        return;
+    }
+    e = g.deep[1 + d];
+    lo = g.offsets[e];
+    n = g.offsets[e + 1] - lo;          // validated when the list was built
+}
+
+__device__ __forceinline__ void deep_store(const WgradOut& out, int64_t ebase, int64_t ld, int r0, int n0,
+                                           const f32x4 (&acc)[D_TM / 32][D_TN / 32]) {
+    AccPos<D_TM, D_TN> pos;
+#pragma unroll
+    for (int mb = 0; mb < D_TM / 32; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < D_TN / 32; ++nb)
+            wgrad_store(out, ebase + (int64_t)(r0 + pos.m(mb)) * ld + n0 + pos.n(nb), acc[mb][nb]);
+}
+
+__global__ __launch_bounds__(256, 2) void k_wgrad_down_deep(WgradDownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<D_TM, D_TN, true, true>::STAGE];
+    const int nNt = a.I / D_TN, per = (a.H / D_TM) * nNt;
+    const int total = deep_count(a.g) * per;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int d = item / per, tile = item - d * per;
+        int e, lo, n;
+        deep_group(a.g, d, e, lo, n);
+        const int m0 = (tile / nNt) * D_TM, n0 = (tile % nNt) * D_TN;
+        const int nk = (n + kTK - 1) / kTK;
+        KRowsGroup sb{a.hw, a.I, lo, n, n0};
+        LoadKS<D_TN, KRowsGroup> lb(sb);
+        f32x4 acc[D_TM / 32][D_TN / 32];
+        if (a.dy_gather) {
+            KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
+            LoadKS<D_TM, KRowsGroupGather> la(sa);
+            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+        } else {
+            KRowsGroup sa{a.dy, a.H, a.dyrow0 + lo, n, m0};
+            LoadKS<D_TM, KRowsGroup> la(sa);
+            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+        }
+        deep_store(a.out, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void k_wgrad_gate_up_deep(WgradGateUpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<D_TM, D_TN, true, true>::STAGE];
+    const int nNt = a.H / D_TN, per = (2 * a.I / D_TM) * nNt;
+    const int total = deep_count(a.g) * per;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int d = item / per, tile = item - d * per;
+        int e, lo, n;
+        deep_group(a.g, d, e, lo, n);
+        const int m0 = (tile / nNt) * D_TM, n0 = (tile % nNt) * D_TN;
+        const int nk = (n + kTK - 1) / kTK;
+        const bool up = m0 >= a.I;
+        KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};
+        LoadKS<D_TM, KRowsGroup> la(sa);
+        f32x4 acc[D_TM / 32][D_TN / 32];
+        if (a.x_gather) {
+            KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, n0, a.k, a.S, a.g.err};
+            LoadKS<D_TN, KRowsGroupGather> lb(sb);
+            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+        } else {
+            KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, n0};
+            LoadKS<D_TN, KRowsGroup> lb(sb);
+            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+        }
+        deep_store(up ? a.out_up : a.out_gate, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
     }
 }
 
@@ -383,6 +474,10 @@ int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
 
 int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_down");
+    if (a.g.deep_thr > 0) {
+        k_wgrad_down_deep<<<D_GRID, 256, 0, st>>>(a);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     const int grid = (a.g.offsets ? a.g.E : 1) * (a.H / W_TM) * wgrad_groups(a.I / W_TN);
     k_wgrad_down<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
@@ -390,12 +485,17 @@ int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
 
 int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_gate_up");
+    if (a.g.deep_thr > 0) {
+        k_wgrad_gate_up_deep<<<D_GRID, 256, 0, st>>>(a);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     const int grid = (a.g.offsets ? a.g.E : 1) * (2 * a.I / W_TM) * wgrad_groups(a.H / W_TN);
     k_wgrad_gate_up<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int gemm_row_tile() { return G1_TM; }
+int wgrad_deep_rows() { return kTK; }
 int dgrad_col_tiles(int I) { return I / G3_TN; }
 
 }  // namespace moe

@@ -653,6 +653,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     } else {
         kcodes = 32 * ((a.g.dense_rows + 31) / 32);
     }
+    if (a.g.deep_thr > 0 && kcodes > a.g.deep_thr) return;     // the deep kernel's group
     const int nk = (kcodes + 127) / 128;
     const int m0 = mt * X_TM;
     const bool hi_part = m0 >= a.msplit;
@@ -672,6 +673,53 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     LoadScalesPad<X_TN> sb(bs, kcodes / 32, nt0 * X_TN, 0, kcodes / 32);
     if (epi.out.mode == 0) wgrad_mx_tiles<true>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
     else wgrad_mx_tiles<false>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
+}
+
+// ---------------------------------------------------------------- deep groups
+// Groups past one 128-code K step: 128 x 128 output tiles with the double-
+// buffered scaled-MFMA K loop, a persistent grid over (deep group, tile).
+constexpr int XD_T = 128, XD_GRID = 512;
+
+__global__ __launch_bounds__(256, 2) void k_wgrad_mx_deep(WgradMXArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<XD_T, XD_T>::STAGE];
+    const PadGroups& g = a.g;
+    const int cnt = g.deep_thr <= 0 ? 0
+                  : g.blk_off ? g.deep[0] : (32 * ((g.dense_rows + 31) / 32) > g.deep_thr ? 1 : 0);
+    const int nNt = a.N / XD_T, per = (a.M / XD_T) * nNt;
+    const int total = cnt * per;
+    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+        const int d = item / per, tile = item - d * per;
+        const int e = g.blk_off ? g.deep[1 + d] : 0;
+        int64_t blk0 = 0;
+        int kcodes = 32 * ((g.dense_rows + 31) / 32);
+        if (g.blk_off) {                                   // offsets validated by the list
+            blk0 = g.blk_off[e];
+            kcodes = 32 * (g.blk_off[e + 1] - g.blk_off[e]);
+        }
+        const int m0 = (tile / nNt) * XD_T, n0 = (tile % nNt) * XD_T;
+        const uint8_t* aq = a.at_q + 32 * blk0 * a.M;
+        const uint8_t* as_ = a.at_s + blk0 * a.M;
+        const uint8_t* bq = a.bt_q + 32 * blk0 * a.N;
+        const uint8_t* bs = a.bt_s + blk0 * a.N;
+        RowsPadK ra{aq, kcodes, m0, 0};
+        LoadKCPad<XD_T> la(ra, kcodes);
+        LoadScalesPad<XD_T> sa(as_, kcodes / 32, m0, 0, kcodes / 32);
+        RowsPadK rb{bq, kcodes, n0, 0};
+        LoadKCPad<XD_T> lb(rb, kcodes);
+        LoadScalesPad<XD_T> sb(bs, kcodes / 32, n0, 0, kcodes / 32);
+        f32x4 acc[XD_T / 32][XD_T / 32];
+        mainloop_mx<XD_T, XD_T, false>(la, lb, sa, sb, (kcodes + 127) / 128, smem, acc);
+        const bool hi_part = m0 >= a.msplit;
+        const WgradOut& out = hi_part ? a.out_hi : a.out_lo;
+        const int64_t ebase = (int64_t)e * (a.msplit == a.M ? a.M : a.msplit) * a.N;
+        const int r0 = hi_part ? m0 - a.msplit : m0;
+        AccPos<XD_T, XD_T> pos;
+#pragma unroll
+        for (int mb = 0; mb < XD_T / 32; ++mb)
+#pragma unroll
+            for (int nb = 0; nb < XD_T / 32; ++nb)
+                wgrad_store(out, ebase + (int64_t)(r0 + pos.m(mb)) * a.N + n0 + pos.n(nb), acc[mb][nb]);
+    }
 }
 
 // ================================================================ launchers
@@ -715,11 +763,17 @@ int launch_gemm_gu_dgrad_mx(const GemmGuDgradMXArgs& a, hipStream_t st) {
 
 int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, a.msplit < a.M ? "wgrad_gate_up_mx" : "wgrad_down_mx");
+    if (a.g.deep_thr > 0) {
+        k_wgrad_mx_deep<<<XD_GRID, 256, 0, st>>>(a);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
     const int grid = (a.g.blk_off ? a.g.E : 1) * (a.M / X_TM) * nng;
     if (grid <= 0) return 0;
     k_wgrad_mx<<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
+
+int wgrad_deep_rows_mx() { return 128; }
 
 }  // namespace moe

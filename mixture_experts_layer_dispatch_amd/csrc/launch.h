@@ -19,6 +19,11 @@ struct GroupRows {
     int rows;                 // rows in the macrobatch (bounds check of offsets)
     int dense_rows;
     int32_t* err;
+    // weight gradients: groups of more than deep_thr rows (deep_thr > 0) are
+    // left to the deep kernels; deep = [count, expert ids...] of those groups
+    // (routed groups; a dense group is deep when dense_rows > deep_thr)
+    const int32_t* deep;
+    int deep_thr;
 };
 
 struct GemmGateUpArgs {
@@ -136,6 +141,8 @@ struct PadGroups {
     const int32_t* blk_off;   // [E+1] prefix of ceil(n_e / 32)
     int E, rows, dense_rows;
     int32_t* err;
+    const int32_t* deep;      // as in GroupRows
+    int deep_thr;
 };
 
 // Source rows of a quantise-transpose: value(r, c) for local row r.
@@ -218,6 +225,7 @@ int launch_softmax_bwd(const float* part, int P, const int32_t* row_of_slot, con
                        float* dw, float* d_logits, int32_t* err, hipStream_t st);
 int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
                        int32_t* err, hipStream_t st);
+int launch_deep_list(const int32_t* offsets, int E, int rows, int thr, int32_t* list, hipStream_t st);
 
 // mx.hip
 int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st);
@@ -246,5 +254,7 @@ int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st);
 int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st);
 int gemm_row_tile();
 int dgrad_col_tiles(int I);
+int wgrad_deep_rows();        // bf16 weight gradients: groups above this go to the deep kernels
+int wgrad_deep_rows_mx();     // MXFP8 weight gradients: the same, in rows
 
 }  // namespace moe
