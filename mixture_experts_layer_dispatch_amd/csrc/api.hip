@@ -322,13 +322,17 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     uint8_t* tx = (uint8_t*)(ws + L.tr_x);
     uint8_t* txs = (uint8_t*)(ws + L.tr_xs);
     int32_t* blk = (int32_t*)(ws + L.blk_off);
-    auto wgrads = [&](const PadGroups& pg, int mode, uint16_t* dwd, float* accd, uint16_t* dwg,
-                      float* accg, uint16_t* dwu, float* accu) -> bool {
+    // counts: the schedule's [n_macro, E] counts for routed groups over several
+    // macrobatches (per-expert modes), nullptr otherwise
+    auto wgrads = [&](const PadGroups& pg, int mode, const int32_t* counts, int m, uint16_t* dwd,
+                      float* accd, uint16_t* dwg, float* accg, uint16_t* dwu, float* accu) -> bool {
         WgradMXArgs d{pg, twdy, twdys, th, ths, g.H, g.I, g.H,
-                      {dwd, accd, mode}, {dwd, accd, mode}};
+                      {dwd, accd, mode, counts, m, g.n_macro, g.E},
+                      {dwd, accd, mode, counts, m, g.n_macro, g.E}};
         if (launch_wgrad_mx(d, st)) return false;
         WgradMXArgs gu{pg, tdgu, tdgus, tx, txs, 2 * g.I, g.H, g.I,
-                       {dwg, accg, mode}, {dwu, accu, mode}};
+                       {dwg, accg, mode, counts, m, g.n_macro, g.E},
+                       {dwu, accu, mode, counts, m, g.n_macro, g.E}};
         return launch_wgrad_mx(gu, st) == 0;
     };
     for (int m = g.n_macro - 1; m >= 0; --m) {
@@ -368,8 +372,9 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
             launch_mx_quant_group_t(pg, qdgu, 2 * g.I, tdgu, tdgus, st) ||
             launch_mx_quant_group_t(pg, qx, g.H, tx, txs, st))
             return MOE_ERR_HIP;
-        if (!wgrads(pg, mode, (uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), (uint16_t*)gr->d_w_gate,
-                    P.wacc(L.wacc_g), (uint16_t*)gr->d_w_up, P.wacc(L.wacc_u)))
+        const int32_t* cnts = g.n_macro > 1 ? sched->counts : nullptr;
+        if (!wgrads(pg, mode, cnts, m, (uint16_t*)gr->d_w_down, P.wacc(L.wacc_d),
+                    (uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), (uint16_t*)gr->d_w_up, P.wacc(L.wacc_u)))
             return MOE_ERR_HIP;
         const uint16_t* sh_dx = nullptr;
         if (g.shared) {
@@ -399,8 +404,9 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
                 launch_mx_quant_group_t(pd, sdg, 2 * g.I, tdgu, tdgus, st) ||
                 launch_mx_quant_group_t(pd, sxx, g.H, tx, txs, st))
                 return MOE_ERR_HIP;
-            if (!wgrads(pd, mode, (uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), (uint16_t*)gr->d_s_gate,
-                        P.wacc(L.wacc_sg), (uint16_t*)gr->d_s_up, P.wacc(L.wacc_su)))
+            if (!wgrads(pd, mode, nullptr, m, (uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd),
+                        (uint16_t*)gr->d_s_gate, P.wacc(L.wacc_sg), (uint16_t*)gr->d_s_up,
+                        P.wacc(L.wacc_su)))
                 return MOE_ERR_HIP;
             sh_dx = sdx;
         }
@@ -613,12 +619,13 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         int32_t* deep = (int32_t*)((char*)workspace + L.deep);
         if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows(), deep, st)) return MOE_ERR_HIP;
         GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err, deep, wgrad_deep_rows()};
+        const int32_t* cnts = g.n_macro > 1 ? sched->counts : nullptr;   // per-expert modes
         WgradDownArgs b3{kgrp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, hw, g.H, g.I,
-                         {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode}};
+                         {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode, cnts, m, g.n_macro, g.E}};
         if (launch_wgrad_down(b3, st)) return MOE_ERR_HIP;
         WgradGateUpArgs b4{kgrp, dgu, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, g.H, g.I,
-                           {(uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), mode},
-                           {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode}};
+                           {(uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), mode, cnts, m, g.n_macro, g.E},
+                           {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode, cnts, m, g.n_macro, g.E}};
         if (launch_wgrad_gate_up(b4, st)) return MOE_ERR_HIP;
         const uint16_t* sh_dx = nullptr;
         if (g.shared) {

@@ -306,7 +306,10 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
     const int nk = (n + kTK - 1) / kTK;
     KRowsGroup sb{a.hw, a.I, lo, n, 0};
     LoadKS<W_TN, KRowsGroup> lb(sb);
-    WgradEpi epi{a.out, (int64_t)e * a.H * a.I, a.I, m0};
+    WgradOut o = a.out;
+    o.mode = wgrad_mode(a.out, e, n);
+    if (o.mode < 0) return;                                    // nothing to add for this expert
+    WgradEpi epi{o, (int64_t)e * a.H * a.I, a.I, m0};
     if (a.dy_gather) {
         KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
         LoadKS<W_TM, KRowsGroupGather> la(sa);
@@ -331,7 +334,10 @@ __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
     const bool up = m0 >= a.I;
     KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};
     LoadKS<W_TM, KRowsGroup> la(sa);
-    WgradEpi epi{up ? a.out_up : a.out_gate, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0};
+    WgradOut o = up ? a.out_up : a.out_gate;
+    o.mode = wgrad_mode(o, e, n);
+    if (o.mode < 0) return;                                    // nothing to add for this expert
+    WgradEpi epi{o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0};
     if (a.x_gather) {
         KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, 0, a.k, a.S, a.g.err};
         LoadKS<W_TN, KRowsGroupGather> lb(sb);
@@ -401,7 +407,9 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_down_deep(WgradDownArgs a) {
             LoadKS<D_TM, KRowsGroup> la(sa);
             mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
         }
-        deep_store(a.out, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
+        WgradOut o = a.out;
+        o.mode = wgrad_mode(a.out, e, n);
+        deep_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
     }
 }
 
@@ -428,7 +436,9 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_gate_up_deep(WgradGateUpArgs a
             LoadKS<D_TN, KRowsGroup> lb(sb);
             mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
         }
-        deep_store(up ? a.out_up : a.out_gate, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
+        WgradOut o = up ? a.out_up : a.out_gate;
+        o.mode = wgrad_mode(o, e, n);
+        deep_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
     }
 }
 

@@ -643,12 +643,13 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     const int ng = L - e * per - mt * nng;
     // the group's operands are contiguous [rows][kcodes] blocks (group-major)
     int64_t blk0 = 0;
-    int kcodes = 0;
+    int kcodes = 0, rows = 0;
     if (a.g.blk_off) {
         const int lo = a.g.off[e], hi = a.g.off[e + 1];
         if (lo >= 0 && hi >= lo && hi <= a.g.rows) {
             blk0 = a.g.blk_off[e];
             kcodes = 32 * (a.g.blk_off[e + 1] - a.g.blk_off[e]);
+            rows = hi - lo;
         }
     } else {
         kcodes = 32 * ((a.g.dense_rows + 31) / 32);
@@ -657,8 +658,10 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
     const int nk = (kcodes + 127) / 128;
     const int m0 = mt * X_TM;
     const bool hi_part = m0 >= a.msplit;
-    WgradEpi epi{hi_part ? a.out_hi : a.out_lo, (int64_t)e * (int64_t)a.msplit * a.N, a.N,
-                 hi_part ? m0 - a.msplit : m0};
+    WgradOut o = hi_part ? a.out_hi : a.out_lo;
+    o.mode = wgrad_mode(o, e, rows);
+    if (o.mode < 0) return;                                    // nothing to add for this expert
+    WgradEpi epi{o, (int64_t)e * (int64_t)a.msplit * a.N, a.N, hi_part ? m0 - a.msplit : m0};
     if (a.msplit == a.M) epi.ebase = (int64_t)e * a.M * a.N;
     const uint8_t* aq = a.at_q + 32 * blk0 * a.M;
     const uint8_t* as_ = a.at_s + blk0 * a.M;
@@ -710,7 +713,8 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx_deep(WgradMXArgs a) {
         f32x4 acc[XD_T / 32][XD_T / 32];
         mainloop_mx<XD_T, XD_T, false>(la, lb, sa, sb, (kcodes + 127) / 128, smem, acc);
         const bool hi_part = m0 >= a.msplit;
-        const WgradOut& out = hi_part ? a.out_hi : a.out_lo;
+        WgradOut out = hi_part ? a.out_hi : a.out_lo;
+        out.mode = wgrad_mode(out, e, g.blk_off ? g.off[e + 1] - g.off[e] : g.dense_rows);
         const int64_t ebase = (int64_t)e * (a.msplit == a.M ? a.M : a.msplit) * a.N;
         const int r0 = hi_part ? m0 - a.msplit : m0;
         AccPos<XD_T, XD_T> pos;

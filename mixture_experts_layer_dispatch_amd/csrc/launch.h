@@ -83,7 +83,26 @@ struct WgradOut {
     uint16_t* out;            // bf16 result
     float* acc;               // fp32 running sum across macrobatches
     int mode;                 // 0 bf16; 1 write fp32; 2 add fp32; 3 add fp32 and write bf16
+    // routed groups over several macrobatches: the mode is chosen per expert
+    // from the schedule's counts [n_macro, E] (see wgrad_mode); nullptr: mode
+    const int32_t* counts;
+    int m, n_macro, E;
 };
+
+// Weight-gradient mode of expert e with n rows in macrobatch m, the backward
+// walking m = n_macro - 1 .. 0: the fp32 sum is only used by experts with
+// rows in several macrobatches; an expert's bf16 result is written once, by
+// the last macrobatch of the walk that has its rows (or as zeros at m = 0
+// when it has none).  -1: nothing to do.
+__host__ __device__ inline int wgrad_mode(const WgradOut& o, int e, int n) {
+    if (!o.counts) return o.mode;
+    bool earlier = false, later = false;          // rows in macrobatches walked before / after m
+    for (int q = o.m + 1; q < o.n_macro; ++q) earlier |= o.counts[(int64_t)q * o.E + e] > 0;
+    for (int q = 0; q < o.m; ++q) later |= o.counts[(int64_t)q * o.E + e] > 0;
+    if (n == 0) return (o.m == 0 && !earlier) ? 0 : -1;
+    if (!earlier) return later ? 1 : 0;
+    return later ? 2 : 3;
+}
 
 struct WgradDownArgs {
     GroupRows g;

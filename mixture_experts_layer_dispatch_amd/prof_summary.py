@@ -1,0 +1,95 @@
+"""Summarise a rocprofv3 kernel trace (``--kernel-trace --output-format csv``)
+of ``bench.py`` into a per-kernel table.
+
+    python -m mixture_experts_layer_dispatch_amd.prof_summary TRACE.csv [--counters FETCH.csv WRITE.csv
+        --calib CFETCH.csv CWRITE.csv]
+
+Kernels of this library are grouped by name and grid size (one kernel can
+serve two shapes, e.g. both MXFP8 weight gradients); everything else (torch's
+input generation) is summed in one line.  With counter files, each group also
+gets its HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
+each scaled by what that counter reads for torch's copy kernel of known size
+in the calibration files (``bench.py --calibrate`` copies 4 GiB).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import re
+
+COPY_BYTES = 4 << 30          # bench.py --calibrate: 4 GiB read and 4 GiB written
+
+
+def _short(name: str):
+    m = re.match(r".*moe::(k_\w+)", name)
+    return m.group(1) if m else None
+
+
+def trace_table(path):
+    groups = collections.defaultdict(list)
+    other_ns, other_calls = 0, 0
+    for r in csv.DictReader(open(path)):
+        n = _short(r["Kernel_Name"])
+        dur = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+        if n is None:
+            other_ns += dur
+            other_calls += 1
+            continue
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        groups[(n, grid)].append(dur)
+    return groups, other_ns, other_calls
+
+
+def counter_table(path, counter):
+    vals = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        n = _short(r["Kernel_Name"])
+        key = (n, int(r["Grid_Size"])) if n else r["Kernel_Name"]
+        vals[key].append(float(r["Counter_Value"]))
+    return {k: sum(v) / len(v) for k, v in vals.items()}
+
+
+def copy_factor(path, counter):
+    vals = [float(r["Counter_Value"]) for r in csv.DictReader(open(path))
+            if r["Counter_Name"] == counter and "copyBuffer" in r["Kernel_Name"]]
+    kib = sorted(vals)[len(vals) // 2]                      # median launch
+    return COPY_BYTES / (kib * 1024.0)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("trace")
+    ap.add_argument("--counters", nargs=2, metavar=("FETCH", "WRITE"))
+    ap.add_argument("--calib", nargs=2, metavar=("CFETCH", "CWRITE"))
+    args = ap.parse_args()
+    groups, other_ns, other_calls = trace_table(args.trace)
+    fetch = write = None
+    if args.counters and args.calib:
+        ff = copy_factor(args.calib[0], "FETCH_SIZE")
+        fw = copy_factor(args.calib[1], "WRITE_SIZE")
+        fetch = {k: v * 1024 * ff for k, v in counter_table(args.counters[0], "FETCH_SIZE").items()}
+        write = {k: v * 1024 * fw for k, v in counter_table(args.counters[1], "WRITE_SIZE").items()}
+        print(f"copy calibration: FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{fw:.3f}")
+    head = f"{'kernel':24s} {'grid':>9s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>10s}"
+    if fetch is not None:
+        head += f" {'read_MB':>10s} {'write_MB':>10s} {'GB/s':>8s}"
+    print(head)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    for (n, grid), d in rows:
+        avg = sum(d) / len(d)
+        line = (f"{n:24s} {grid:9d} {len(d):6d} {avg / 1e3:10.1f} {min(d) / 1e3:10.1f} "
+                f"{max(d) / 1e3:10.1f} {sum(d) / 1e6:10.3f}")
+        if fetch is not None:
+            rd, wr = fetch.get((n, grid)), write.get((n, grid))
+            if rd is not None and wr is not None:
+                line += f" {rd / 1e6:10.1f} {wr / 1e6:10.1f} {(rd + wr) / avg:8.1f}"
+        print(line)
+    print(f"{'(torch input generation)':24s} {'':>9s} {other_calls:6d} {'':>10s} {'':>10s} {'':>10s} "
+          f"{other_ns / 1e6:10.3f}")
+
+
+if __name__ == "__main__":
+    main()
