@@ -156,30 +156,50 @@ __device__ __forceinline__ bool map_pad_block(const PadGroups& g, int C, int b, 
     return o.nv > 0;
 }
 
-__device__ __forceinline__ float qt_value(const QtSrc& s, int r, int c, int32_t* err) {
-    if (s.kind == 1) return s.f32[(int64_t)r * s.ld + c];
-    if (s.kind == 3) return bf2f(s.b16[(int64_t)(s.row0 + r) * s.ld + c]);
-    const int slot = s.slot_of_row[s.grow0 + r];
-    if ((unsigned)slot >= (unsigned)s.S) {
-        raise_err(err, ERR_BAD_SLOT);
-        return 0.f;
-    }
-    const float v = bf2f(s.b16[(int64_t)(slot / s.k) * s.ld + c]);
-    return s.kind == 0 ? v * s.topk_w[slot] : v;
-}
-
+// The block's 32 source rows are resolved once (threads 0..31 look up their
+// slots and weights) and shared through LDS, so that each thread's 32 loads
+// are independent and in flight together.
 __global__ __launch_bounds__(256) void k_mx_quant_group_t(PadGroups g, QtSrc src, int C,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
-    const int c = blockIdx.x * 256 + threadIdx.x;
+    __shared__ int64_t roff[32];      // element offset of row q in the source; -1: a zero row
+    __shared__ float rwt[32];         // the row's factor (the slot's weight for w * dy, else 1)
     PadBlock pb;
-    if (c >= C || !map_pad_block(g, C, blockIdx.y, pb)) return;
+    if (!map_pad_block(g, C, blockIdx.y, pb)) return;         // the same for the whole block
+    if (threadIdx.x < 32) {
+        const int q = threadIdx.x, r = pb.r0 + q;
+        int64_t off = -1;
+        float wt = 1.f;
+        if (q < pb.nv) {
+            if (src.kind == 1) {
+                off = (int64_t)r * src.ld;
+            } else if (src.kind == 3) {
+                off = (int64_t)(src.row0 + r) * src.ld;
+            } else {
+                const int slot = src.slot_of_row[src.grow0 + r];
+                if ((unsigned)slot >= (unsigned)src.S) {
+                    raise_err(g.err, ERR_BAD_SLOT);
+                } else {
+                    off = (int64_t)(slot / src.k) * src.ld;
+                    if (src.kind == 0) wt = src.topk_w[slot];
+                }
+            }
+        }
+        roff[q] = off;
+        rwt[q] = wt;
+    }
+    __syncthreads();
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= C) return;
     float v[32];
     float amax = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-        v[q] = q < pb.nv ? qt_value(src, pb.r0 + q, c, g.err) : 0.f;
-        amax = fmaxf(amax, fabsf(v[q]));
+        const int64_t o = roff[q];
+        float x = 0.f;
+        if (o >= 0) x = src.kind == 1 ? src.f32[o + c] : bf2f(src.b16[o + c]) * rwt[q];
+        v[q] = x;
+        amax = fmaxf(amax, fabsf(x));
     }
     const int s = mx_scale_exp(amax);
     uint32_t w[8];
