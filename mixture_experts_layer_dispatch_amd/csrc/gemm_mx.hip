@@ -98,14 +98,10 @@ __device__ __forceinline__ int scale_mx(const uint32_t* sc, int rbase) {
 }
 
 template <int TM, int TN>
-__device__ __forceinline__ void mma_tile_mx(const uint16_t* st, int wm0, int wn0,
-                                            f32x4 (&acc)[TM / 32][TN / 32]) {
-    using SM = SmemMX<TM, TN>;
+__device__ __forceinline__ void mma_tile_mx_at(const uint16_t* sA, const uint16_t* sB, const uint32_t* cA,
+                                               const uint32_t* cB, int wm0, int wn0,
+                                               f32x4 (&acc)[TM / 32][TN / 32]) {
     constexpr int MB = TM / 32, NB = TN / 32;
-    const uint16_t* sA = st;
-    const uint16_t* sB = st + SM::A;
-    const uint32_t* cA = (const uint32_t*)(st + SM::A + SM::B);
-    const uint32_t* cB = cA + TM;
     v8i32 fb[MB], fa[NB];
     int xb[MB], xa[NB];
 #pragma unroll
@@ -124,6 +120,15 @@ __device__ __forceinline__ void mma_tile_mx(const uint16_t* st, int wm0, int wn0
         for (int nb = 0; nb < NB; ++nb)
             acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
                 fa[nb], fb[mb], acc[mb][nb], 0, 0, 0, xa[nb], 0, xb[mb]);
+}
+
+// operands in the SmemMX stage layout
+template <int TM, int TN>
+__device__ __forceinline__ void mma_tile_mx(const uint16_t* st, int wm0, int wn0,
+                                            f32x4 (&acc)[TM / 32][TN / 32]) {
+    using SM = SmemMX<TM, TN>;
+    const uint32_t* cA = (const uint32_t*)(st + SM::A + SM::B);
+    mma_tile_mx_at<TM, TN>(st, st + SM::A, cA, cA + TM, wm0, wn0, acc);
 }
 
 // The same product evaluated on the bf16 MFMA: codes are decoded to bf16 at
@@ -494,35 +499,28 @@ struct RowsPadK {              // row r of a transposed operand, from code kb0 o
 template <int ROWS>
 struct LoadKCPad {             // K-contiguous fp8 tile; chunks at or past kmax codes read as zero
     static constexpr int PER = ROWS * 8 / 256;
+    // thread t, item q: row (t + 256 q) / 8, 16-code chunk t % 8 (the same for
+    // every q); addresses are formed at each load to keep few registers live
     RowsPadK src;
-    const uint16_t* p[PER];
-    int off[PER], kc[PER];
     int kmax;
     uint4 v[PER];
-    __device__ LoadKCPad(const RowsPadK& s, int kmax_codes) : src(s), kmax(kmax_codes) {
+    __device__ LoadKCPad(const RowsPadK& s, int kmax_codes) : src(s), kmax(kmax_codes) {}
+    __device__ void retarget(int row0) { src.row0 = row0; }   // same K range, other rows
+    __device__ void load(int kt) {
+        const int kc = threadIdx.x & 7;
+        const bool in = kt * 128 + kc * 16 < kmax;
+        const uint8_t* b = src.base + src.kb0 + kt * 128 + kc * 16;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int c = threadIdx.x + 256 * q;
-            const int r = c >> 3;
-            kc[q] = c & 7;
-            p[q] = src.row(r) + kc[q] * 8;
-            off[q] = r * (kTK + 8) + kc[q] * 8;
+            const int r = (threadIdx.x >> 3) + 32 * q;
+            v[q] = in ? *(const uint4*)(b + (int64_t)(src.row0 + r) * src.ld) : make_uint4(0, 0, 0, 0);
         }
     }
-    __device__ void retarget(int row0) {      // same K range, other rows
-        src.row0 = row0;
-#pragma unroll
-        for (int q = 0; q < PER; ++q) p[q] = src.row((threadIdx.x + 256 * q) >> 3) + kc[q] * 8;
-    }
-    __device__ void load(int kt) {
+    __device__ void store(uint16_t* s) const {
+        const int kc = threadIdx.x & 7;
 #pragma unroll
         for (int q = 0; q < PER; ++q)
-            v[q] = (kt * 128 + kc[q] * 16 < kmax) ? *(const uint4*)(p[q] + (int64_t)kt * kTK)
-                                                  : make_uint4(0, 0, 0, 0);
-    }
-    __device__ void store(uint16_t* s) const {
-#pragma unroll
-        for (int q = 0; q < PER; ++q) *(uint4*)(s + off[q]) = v[q];
+            *(uint4*)(s + ((threadIdx.x >> 3) + 32 * q) * (kTK + 8) + kc * 8) = v[q];
     }
 };
 
@@ -561,8 +559,13 @@ struct LoadScalesPad {         // scale bytes of blocks at or past nblk read as 
     }
 };
 
-constexpr int X_STAGE = SmemMX<X_TM, X_TN>::STAGE;
-constexpr int X_SMEM = X_STAGE + X_TM * W_SP;
+// LDS: the resident A tile and both scale vectors, then one region that holds
+// the current B tile and, after its MFMAs, the staged bf16 output tile.
+constexpr int X_P = kTK + 8;                              // uint16 per code row (144 bytes)
+constexpr int X_CA = X_TM * X_P;                          // A scales: X_TM words
+constexpr int X_CB = X_CA + 2 * X_TM;                     // B scales: X_TN words
+constexpr int X_REG = X_CB + 2 * X_TN;
+constexpr int X_SMEM = X_REG + (X_TM * W_SP > X_TN * X_P ? X_TM * W_SP : X_TN * X_P);
 
 // The column-tile walk of one weight-gradient block (A: 128 rows, B: the
 // current 64-row column tile).
@@ -571,12 +574,11 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
                                                LoadKCPad<X_TN>& lb, LoadScalesPad<X_TN>& sb,
                                                int nk, int nt0, int ntn, int nstride, uint16_t* smem,
                                                const WgradEpi& epi) {
-    using SM = SmemMX<X_TM, X_TN>;
     const int w = threadIdx.x >> 6;
     const int wm0 = (w & 1) * (X_TM / 2), wn0 = (w >> 1) * (X_TN / 2);
-    uint16_t* stage = smem + X_STAGE;
-    uint32_t* cA = (uint32_t*)(smem + SM::A + SM::B);
-    uint32_t* cB = cA + X_TM;
+    uint16_t* region = smem + X_REG;                      // B tile, then the staged output
+    uint32_t* cA = (uint32_t*)(smem + X_CA);
+    uint32_t* cB = (uint32_t*)(smem + X_CB);
     f32x4 acc[X_TM / 32][X_TN / 32];
     if (nk <= 1) {
         // one K step: A stays in LDS; the next column tile is fetched while the
@@ -592,8 +594,8 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
         for (int i = 0; i < ntn; ++i) {
             zero_acc<X_TM, X_TN>(acc);
             if (nk == 1) {
-                if (i > 0) __syncthreads();            // MFMAs and staged stores of tile i-1 done
-                lb.store(smem + SM::A);
+                if (i > 0) __syncthreads();            // the staged tile i-1 has been written out
+                lb.store(region);
                 sb.store(cB);
                 __syncthreads();
                 if (i + 1 < ntn) {
@@ -602,9 +604,10 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
                     lb.load(0);
                     sb.load(0);
                 }
-                mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
+                mma_tile_mx_at<X_TM, X_TN>(smem, region, cA, cB, wm0, wn0, acc);
+                __syncthreads();                       // the MFMAs are done with the B tile
             }
-            epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, stage);
+            epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, region);
         }
         return;
     }
@@ -617,19 +620,20 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
             sa.load(kt);
             lb.load(kt);
             sb.load(kt);
-            __syncthreads();                           // the previous step's MFMAs are done
+            __syncthreads();        // the previous step's MFMAs (or staged stores) are done
             la.store(smem);
             sa.store(cA);
-            lb.store(smem + SM::A);
+            lb.store(region);
             sb.store(cB);
             __syncthreads();
-            mma_tile_mx<X_TM, X_TN>(smem, wm0, wn0, acc);
+            mma_tile_mx_at<X_TM, X_TN>(smem, region, cA, cB, wm0, wn0, acc);
         }
-        epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, stage);
+        __syncthreads();                               // the MFMAs are done with the B tile
+        epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, region);
     }
 }
 
-__global__ __launch_bounds__(256, 2) void k_wgrad_mx(WgradMXArgs a) {
+__global__ __launch_bounds__(256, 4) void k_wgrad_mx(WgradMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[X_SMEM];
     const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
     const int nMt = a.M / X_TM;
