@@ -18,9 +18,10 @@
 //              expert's rows in ascending order.
 //
 // Tiles: 256 threads = 4 waves in a 2 x 2 grid, each wave (TM/2) x (TN/2).
-// Both operands are staged through LDS in a [row][k] layout (row pitch
-// kTK + 8 bf16 = 144 B, so the 16 rows read by one MFMA fragment hit 16
-// different 16-byte bank groups), double-buffered with one barrier per K step.
+// Both operands are staged through LDS in a [row][k] layout (unpadded
+// 128-byte rows with XOR-swizzled 16-byte chunks, so the 16 rows read by one
+// MFMA fragment hit 16 different 16-byte bank groups), double-buffered with
+// one barrier per K step.
 // Operands whose reduction index is the slow memory axis are copied into LDS
 // as they lie ([k][row], KS tiles) and read with gfx950's LDS transpose load,
 // which hands each lane four consecutive k of one row.
@@ -40,7 +41,7 @@ namespace moe {
 constexpr int G1_TM = 64, G1_TN = 128;
 
 __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G1_TM, G1_TN, false, false>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[lds_two_blocks(2 * Smem<G1_TM, G1_TN, false, false>::STAGE)];
     int e, lo, hi, nt;
     if (!map_mtile<G1_TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
     const int i0 = nt * 64;
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
 constexpr int G3_TM = 64, G3_TN = 128;
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G3_TM, G3_TN, false, true>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[lds_two_blocks(2 * Smem<G3_TM, G3_TN, false, true>::STAGE)];
     __shared__ float red[2][G3_TM];
     int e, lo, hi, nt;
     if (!map_mtile<G3_TM>(a.g, a.I / G3_TN, blockIdx.x, e, lo, hi, nt)) return;

@@ -118,19 +118,32 @@ struct KRowsGroupGather {
 
 // ================================================================ LDS tiles
 // A tile holds ROWS rows (M or N indices) by kTK reduction indices.
-//   KC (K contiguous in memory): stored [row][k], pitch kTK + 8; a fragment
-//      row is read as 16 bytes (one row, 8 consecutive k).
+//   KC (K contiguous in memory): stored [row][k] in unpadded 128-byte rows
+//      (kTK bf16, or 128 fp8 codes); the 16-byte chunk c of row r sits at
+//      chunk c ^ ((r >> 1) & 7).  A fragment reads the same chunk of 16 rows:
+//      consecutive rows alternate halves of the 64 banks and the swizzle
+//      spreads the eight row pairs over the eight chunks, so the 16 reads hit
+//      16 different 16-byte bank groups.
 //   KS (K is the slow memory axis): stored as it lies in memory, [k][row],
 //      pitch ROWS + 16, and read with the LDS transpose load, which hands each
-//      lane four consecutive k of one row.
-// Pitches: the 16 rows of a KC fragment land on 16 different 16-byte bank
-// groups (144-byte rows); for KS the eight k rows read by one 32-lane pass of
-// transpose loads land on disjoint 32-byte bank ranges (pitch = 16 mod 32).
+//      lane four consecutive k of one row; the eight k rows read by one
+//      32-lane pass land on disjoint 32-byte bank ranges (pitch = 16 mod 32).
 template <int ROWS, bool KS>
 struct Tile {
-    static constexpr int P = KS ? ROWS + 16 : kTK + 8;
+    static constexpr int P = KS ? ROWS + 16 : kTK;
     static constexpr int SIZE = KS ? kTK * P : ROWS * P;
 };
+
+// LDS (in uint16) that a kernel reserves so that at most two of its blocks
+// share a CU: for the weight-streaming GEMMs whose two-block occupancy measured
+// faster than three (more concurrent weight streams cost HBM efficiency).
+constexpr int kTwoBlocksLds = 160 * 1024 / 3 / 2 + 64;
+constexpr int lds_two_blocks(int n) { return n > kTwoBlocksLds ? n : kTwoBlocksLds; }
+
+// uint16 offset in a KC tile of byte `byte` (even) of row r
+__device__ __forceinline__ int kc_off(int r, int byte) {
+    return r * kTK + (((((byte >> 4) ^ ((r >> 1) & 7)) << 4) | (byte & 15)) >> 1);
+}
 
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
@@ -150,7 +163,7 @@ struct LoadKC {
             const int r = c >> 3, kc = c & 7;
             const uint16_t* b = src.row(r);
             p[q] = b ? b + kc * 8 : nullptr;
-            off[q] = r * Tile<ROWS, false>::P + kc * 8;
+            off[q] = kc_off(r, kc * 16);
         }
     }
     __device__ void load(int kt) {
@@ -215,19 +228,19 @@ struct LoadKS {
 
 // ================================================================ fragments
 // Natural K order (both operands KC): lane l holds k = ks + 8*(l>>4) + 0..7.
-__device__ __forceinline__ bf16x8 frag_kc(const uint16_t* s, int P, int rbase, int ks) {
+__device__ __forceinline__ bf16x8 frag_kc(const uint16_t* s, int, int rbase, int ks) {
     const int lane = lane_id();
-    return *(const bf16x8*)(s + (rbase + (lane & 15)) * P + ks + (lane >> 4) * 8);
+    return *(const bf16x8*)(s + kc_off(rbase + (lane & 15), 2 * (ks + (lane >> 4) * 8)));
 }
 
 // Permuted K order, used whenever an operand is KS: lane group g = l>>4 holds
 // k = ks + 4g + {0..3} and ks + 16 + 4g + {0..3}.  The MFMA sums over k, so
 // the permutation is harmless as long as both operands use it.
-__device__ __forceinline__ bf16x8 frag_kc_perm(const uint16_t* s, int P, int rbase, int ks) {
+__device__ __forceinline__ bf16x8 frag_kc_perm(const uint16_t* s, int, int rbase, int ks) {
     const int lane = lane_id();
-    const uint16_t* p = s + (rbase + (lane & 15)) * P + ks + 4 * (lane >> 4);
-    const uint2 a = *(const uint2*)p;
-    const uint2 b = *(const uint2*)(p + 16);
+    const int row = rbase + (lane & 15);
+    const uint2 a = *(const uint2*)(s + kc_off(row, 2 * (ks + 4 * (lane >> 4))));
+    const uint2 b = *(const uint2*)(s + kc_off(row, 2 * (ks + 16 + 4 * (lane >> 4))));
     const uint4 v = make_uint4(a.x, a.y, b.x, b.y);
     return *(const bf16x8*)&v;
 }

@@ -11,8 +11,8 @@
 // lane l (group g = l >> 4) supplies row (l & 15) with the 16 codes at
 // K = 16g .. 16g+15 and the 16 at K = 64+16g .. 64+16g+15, and supplies the
 // scale of row (l & 15), 32-block g.  Data tiles sit in LDS as [row][128 B]
-// with a 144-byte pitch (16 rows read together hit 16 different bank groups),
-// scales as one 32-bit word (4 blocks) per row.
+// with XOR-swizzled 16-byte chunks (kc_off: 16 rows read together hit 16
+// different bank groups), scales as one 32-bit word (4 blocks) per row.
 #include "gemm_common.h"
 #include "mx.h"
 #include "profile.h"
@@ -73,7 +73,7 @@ struct LoadScales {
 // ================================================================ tiles
 template <int TM, int TN>
 struct SmemMX {
-    static constexpr int P = kTK + 8;                 // in uint16: 144 bytes
+    static constexpr int P = kTK;                     // in uint16: 128-byte swizzled rows (kc_off)
     static constexpr int A = TM * P;                  // uint16 units
     static constexpr int B = TN * P;
     static constexpr int SA = 2 * TM;                 // TM words
@@ -83,9 +83,9 @@ struct SmemMX {
 
 __device__ __forceinline__ v8i32 frag_mx(const uint16_t* s, int rbase) {
     const int lane = lane_id();
-    const uint8_t* p = (const uint8_t*)(s + (rbase + (lane & 15)) * (kTK + 8)) + 16 * (lane >> 4);
-    const uint4 a = *(const uint4*)p;
-    const uint4 b = *(const uint4*)(p + 64);
+    const int row = rbase + (lane & 15);
+    const uint4 a = *(const uint4*)(s + kc_off(row, 16 * (lane >> 4)));
+    const uint4 b = *(const uint4*)(s + kc_off(row, 64 + 16 * (lane >> 4)));
     v8i32 v;
     v[0] = (int)a.x; v[1] = (int)a.y; v[2] = (int)a.z; v[3] = (int)a.w;
     v[4] = (int)b.x; v[5] = (int)b.y; v[6] = (int)b.z; v[7] = (int)b.w;
@@ -147,8 +147,7 @@ typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ bf16x8 frag_mx_bf16(const uint16_t* s, const uint32_t* sc, int rbase, int ks) {
     const int lane = lane_id();
     const int row = rbase + (lane & 15);
-    const uint8_t* p = (const uint8_t*)(s + row * (kTK + 8)) + 32 * ks + 8 * (lane >> 4);
-    const uint2 c = *(const uint2*)p;
+    const uint2 c = *(const uint2*)(s + kc_off(row, 32 * ks + 8 * (lane >> 4)));
     const uint32_t e8 = (sc[row] >> (8 * ks)) & 0xffu;
     const float scale = __uint_as_float(e8 ? (e8 << 23) : 0x00400000u);   // 2^(e8 - 127)
     uint4 v;
@@ -520,7 +519,7 @@ struct LoadKCPad {             // K-contiguous fp8 tile; chunks at or past kmax 
         const int kc = threadIdx.x & 7;
 #pragma unroll
         for (int q = 0; q < PER; ++q)
-            *(uint4*)(s + ((threadIdx.x >> 3) + 32 * q) * (kTK + 8) + kc * 8) = v[q];
+            *(uint4*)(s + kc_off((threadIdx.x >> 3) + 32 * q, kc * 16)) = v[q];
     }
 };
 
@@ -561,7 +560,7 @@ struct LoadScalesPad {         // scale bytes of blocks at or past nblk read as 
 
 // LDS: the resident A tile and both scale vectors, then one region that holds
 // the current B tile and, after its MFMAs, the staged bf16 output tile.
-constexpr int X_P = kTK + 8;                              // uint16 per code row (144 bytes)
+constexpr int X_P = kTK;                                  // uint16 per code row (128 bytes, kc_off)
 constexpr int X_CA = X_TM * X_P;                          // A scales: X_TM words
 constexpr int X_CB = X_CA + 2 * X_TM;                     // B scales: X_TN words
 constexpr int X_REG = X_CB + 2 * X_TN;
