@@ -147,11 +147,30 @@ SHAPES = {
     "e512_t65536_zipf": MoEShape("e512_t65536_zipf", T=65536, H=4096, I=1024, E=512, k=10,
                                  seed=4, n_shared=1, macrobatch=16384, minibatch=4096,
                                  zipf=True),
+    # one GPU's expert-parallel share of the 512-expert layer (64 ranks x 2048
+    # tokens x top-10 / 512): 8 local experts, exactly 2560 rows each; every row
+    # is routed top-1 to its expert by one-hot logits from a seeded balanced
+    # assignment (weight 1), so dispatch, GEMMs and combine see that share
+    "e8_ep_share": MoEShape("e8_ep_share", T=20480, H=4096, I=1024, E=8, k=1, seed=2,
+                            extra={"balanced": True}),
 }
 
 
+def balanced_assignment(shape: MoEShape, device="cpu") -> torch.Tensor:
+    """int64 [T]: row t's expert, exactly T/E rows each (rank in a seeded permutation // (T/E))."""
+    per = shape.T // shape.E
+    rank = torch.empty(shape.T, dtype=torch.int64, device=device)
+    rank[permutation(shape.T, shape.seed, S_PERM, device)] = torch.arange(shape.T, device=device)
+    return rank // per
+
+
 def logits(shape: MoEShape, device="cpu") -> torch.Tensor:
-    """fp32 [T, E] router logits: N(0,1), plus the Zipf bias per expert if shape.zipf."""
+    """fp32 [T, E] router logits: N(0,1), plus the Zipf bias per expert if shape.zipf;
+    one-hot (1 at the assigned expert, 0 elsewhere) for a balanced shape."""
+    if shape.extra.get("balanced"):
+        L = torch.zeros((shape.T, shape.E), dtype=torch.float32, device=device)
+        L[torch.arange(shape.T, device=device), balanced_assignment(shape, device)] = 1.0
+        return L
     L = normal((shape.T, shape.E), shape.seed, S_LOGITS, 1.0, torch.float32, device)
     if shape.zipf:
         L = L + zipf_bias(shape.E).to(device)

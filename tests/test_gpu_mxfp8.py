@@ -222,3 +222,30 @@ def test_forward_backward_mx_ring_full_size_sampled():
         assert_close(f"dW_gate[{e}] (mxfp8)", f32(c.grads["d_w_gate"][e]), rb["dWg"][e], MX_TOL)
         assert_close(f"dW_up[{e}] (mxfp8)", f32(c.grads["d_w_up"][e]), rb["dWu"][e], MX_TOL)
         assert_close(f"dW_down[{e}] (mxfp8)", f32(c.grads["d_w_down"][e]), rb["dWd"][e], MX_TOL)
+
+
+def test_forward_backward_mx_ep_share_full_size_sampled():
+    """MXFP8 on one GPU's expert-parallel share (8 experts x 2560 rows, top-1)."""
+    c = MXCase(si.SHAPES["e8_ep_share"])
+    c.schedule()
+    c.forward()
+    c.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(c.ws) == 0
+    idx, w, sch = c.oracle_schedule()
+    assert np.array_equal(c.sched["topk_idx"].cpu().numpy(), idx)
+    rng = np.random.default_rng(8)
+    tokens = np.sort(rng.choice(c.shape.T, size=24, replace=False))
+    x, dy = f32(c.x), f32(c.dy)
+    wgv, wuv, wdv = c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd)
+    ref = oracle.forward(x, wgv, wuv, wdv, idx, w, tokens=tokens, mx=True)
+    assert_close("y[sampled] (mxfp8)", f32(c.y)[tokens], ref["y"], MX_TOL)
+    rb = oracle.backward(x, wgv, wuv, wdv, idx, w, dy, mx=True, sched=sch, tokens=tokens,
+                         experts=[0, 7])
+    assert_close("dx[sampled] (mxfp8)", f32(c.dx)[tokens], rb["dx"], MX_TOL)
+    assert_close("dw[sampled] (mxfp8)", c.dw.cpu().numpy()[tokens], rb["dw"], MX_TOL)
+    for e in (0, 7):
+        assert_close(f"dW_gate[{e}] (mxfp8)", f32(c.grads["d_w_gate"][e]), rb["dWg"][e], MX_TOL)
+        assert_close(f"dW_up[{e}] (mxfp8)", f32(c.grads["d_w_up"][e]), rb["dWu"][e], MX_TOL)
+        assert_close(f"dW_down[{e}] (mxfp8)", f32(c.grads["d_w_down"][e]), rb["dWd"][e], MX_TOL)

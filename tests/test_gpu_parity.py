@@ -88,7 +88,7 @@ def test_schedule_with_ties_and_signed_zeros():
     _check_schedule(case)
 
 
-@pytest.mark.parametrize("name", ["e512_t2048", "e512_t65536_zipf"])
+@pytest.mark.parametrize("name", ["e512_t2048", "e512_t65536_zipf", "e8_ep_share"])
 def test_schedule_full_size(name):
     from gpu_cases import cfg_of
     from mixture_experts_layer_dispatch_amd import binding as B
@@ -251,6 +251,31 @@ def test_forward_backward_ring_full_size_sampled():
     dl = oracle.ffn.d_logits_dense(idx, rb["dl_sel"], case.shape.E, tokens=tokens)
     assert_close("d_logits[sampled]", case.dlogits.cpu().numpy()[tokens], dl)
     for e in experts:
+        assert_close(f"dW_gate[{e}]", f32(case.grads["d_w_gate"][e]), rb["dWg"][e])
+        assert_close(f"dW_up[{e}]", f32(case.grads["d_w_up"][e]), rb["dWu"][e])
+        assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])
+
+
+def test_forward_backward_ep_share_full_size_sampled():
+    """One GPU's expert-parallel share: 8 experts with 2560 rows each, top-1."""
+    case = Case(si.SHAPES["e8_ep_share"])
+    case.schedule()
+    idx, w, sch = _check_schedule(case)
+    case.forward()
+    case.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(case.ws) == 0
+    rng = np.random.default_rng(7)
+    tokens = np.sort(rng.choice(case.shape.T, size=24, replace=False))
+    x, dy = f32(case.x), f32(case.dy)
+    wgv, wuv, wdv = case.expert_view(case.wg), case.expert_view(case.wu), case.expert_view(case.wd)
+    ref = oracle.forward(x, wgv, wuv, wdv, idx, w, tokens=tokens)
+    assert_close("y[sampled]", f32(case.y)[tokens], ref["y"])
+    rb = oracle.backward(x, wgv, wuv, wdv, idx, w, dy, tokens=tokens, experts=[0, 7])
+    assert_close("dx[sampled]", f32(case.dx)[tokens], rb["dx"])
+    assert_close("dw[sampled]", case.dw.cpu().numpy()[tokens], rb["dw"])
+    for e in (0, 7):
         assert_close(f"dW_gate[{e}]", f32(case.grads["d_w_gate"][e]), rb["dWg"][e])
         assert_close(f"dW_up[{e}]", f32(case.grads["d_w_up"][e]), rb["dWu"][e])
         assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])

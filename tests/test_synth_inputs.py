@@ -45,3 +45,16 @@ def test_zipf_bias_and_permutation():
     assert abs(p[0] / p[1] - 2 ** 1.1) < 1e-4
     perm = si.permutation(1000, 2, si.S_PERM)
     assert sorted(perm.tolist()) == list(range(1000))
+
+
+def test_balanced_ep_share_logits():
+    """One GPU's expert-parallel share: every expert gets exactly T/E rows, each
+    row routed top-1 to its assigned expert with weight 1."""
+    import oracle
+    sh = si.SHAPES["e8_ep_share"]
+    L = si.logits(sh, "cpu").numpy()
+    assert set(np.unique(L)) == {0.0, 1.0} and np.all(L.sum(1) == 1.0)
+    idx, w = oracle.route(L.astype(np.float64), sh.k)
+    assert np.array_equal(idx[:, 0], si.balanced_assignment(sh).numpy())
+    assert np.array_equal(np.bincount(idx[:, 0], minlength=sh.E), np.full(sh.E, sh.T // sh.E))
+    assert np.all(w == 1.0)
