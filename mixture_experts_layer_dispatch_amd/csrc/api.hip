@@ -252,7 +252,7 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)(P.ws + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
+        if (launch_tile_prefix(off, g.E, g.Sm, 64, toff, err, st)) return MOE_ERR_HIP;
         for (int i = 0; i < g.n_mini; ++i) {
             const int s0 = grow0 + i * g.Smb;
             if (launch_dispatch_mx(x, g.H, sched->row_of_slot, s0, s0 + g.Smb, g.k, grow0, g.Sm, xq, xs,
@@ -348,7 +348,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)(ws + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
+        if (launch_tile_prefix(off, g.E, g.Sm, 64, toff, err, st)) return MOE_ERR_HIP;
         if (launch_tile_prefix(off, g.E, g.Sm, 32, blk, err, st)) return MOE_ERR_HIP;
         GroupRows grp{off, toff, g.E, g.Sm, 0, err};
         GemmDownDgradMXArgs b1{grp, dyq, dys, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
@@ -514,6 +514,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
     int32_t* err = P.err();
     const uint16_t* xb = (const uint16_t*)x;
     if (g.mx) return forward_mx(g, L, P, sched, x, w, y, saved, st);
+    const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
     for (int m = 0; m < g.n_macro; ++m) {
         char* half = P.half(m, g.halves);
         uint16_t* xd = (uint16_t*)(half + L.f_xd);
@@ -522,14 +523,14 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
+        if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
         // dispatch, one minibatch at a time, into this macrobatch's ring half
         for (int i = 0; i < g.n_mini; ++i) {
             const int s0 = grow0 + i * g.Smb;
             if (launch_dispatch(x, g.H, sched->row_of_slot, s0, s0 + g.Smb, g.k, grow0, g.Sm, xd, err, st))
                 return MOE_ERR_HIP;
         }
-        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
         GemmGateUpArgs a1{grp, xd, 0, 0, sched->slot_of_row, grow0, g.k, g.S,
                           (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
                           (uint16_t*)saved->g, (uint16_t*)saved->u, grow0, hbuf};
@@ -540,7 +541,7 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
         if (g.shared) {
             uint16_t* sh_h = (uint16_t*)(P.sh() + L.s_h);
             uint16_t* so = (uint16_t*)(P.sh() + L.s_o);
-            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
             GemmGateUpArgs s1{dense, xb, 0, t0, nullptr, 0, g.k, g.S,
                               (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up, g.H, g.I,
                               (uint16_t*)saved->sg, (uint16_t*)saved->su, t0, sh_h};
@@ -595,6 +596,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
     int32_t* err = P.err();
     const uint16_t* xb = (const uint16_t*)x;
     const uint16_t* dyb = (const uint16_t*)dy;
+    const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
     for (int m = g.n_macro - 1; m >= 0; --m) {
         // weight-gradient accumulation across the reverse walk
         int mode = 0;
@@ -607,8 +609,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, gemm_row_tile(), toff, err, st)) return MOE_ERR_HIP;
-        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
         // reverse-combine (dy gathered on load) + down dgrad + SwiGLU backward + dw partials
         GemmDownDgradArgs b1{grp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, sched->topk_w,
                              (const uint16_t*)w->w_down, g.H, g.I, (const uint16_t*)saved->g,
@@ -632,7 +634,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
             uint16_t* sdgu = (uint16_t*)(P.sh() + L.s_dgu);
             uint16_t* shw = (uint16_t*)(P.sh() + L.s_hw);
             uint16_t* sdx = (uint16_t*)(P.sh() + L.s_dx);
-            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows()};
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows(), gemm_row_tile(g.M, 1)};
             GemmDownDgradArgs c1{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, nullptr,
                                  (const uint16_t*)w->s_down, g.H, g.I, (const uint16_t*)saved->sg,
                                  (const uint16_t*)saved->su, t0, sdgu, shw, nullptr, g.P};

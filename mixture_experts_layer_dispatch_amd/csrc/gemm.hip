@@ -37,15 +37,21 @@ namespace moe {
 
 // ================================================================ forward GEMM 1
 // g = X W_gate^T, u = X W_up^T, h = SiLU(g) * u; g, u saved (bf16), h to the
-// ring.  Tile: 64 rows x (64 gate + 64 up columns).
-constexpr int G1_TM = 64, G1_TN = 128;
+// ring.  Tile: TM rows x (64 gate + 64 up columns).
+//
+// Row tiles (TM): 64 when groups are small (each weight byte is then read by
+// one or two tiles and the GEMM streams weights), 128 when the groups are
+// large enough for the GEMM to be MFMA work: a wave then computes 64 x 64
+// instead of 32 x 64 and reads a third less LDS per MFMA.
+constexpr int G1_TN = 128;
 
+template <int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[lds_two_blocks(2 * Smem<G1_TM, G1_TN, false, false>::STAGE)];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[lds_two_blocks(2 * Smem<TM, G1_TN, false, false>::STAGE)];
     int e, lo, hi, nt;
-    if (!map_mtile<G1_TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
     const int i0 = nt * 64;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
     const int nk = a.H / kTK;
     const uint16_t* wg = a.w_gate + (int64_t)e * a.I * a.H;
     const uint16_t* wu = a.w_up + (int64_t)e * a.I * a.H;
@@ -53,17 +59,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
     LoadKC<G1_TN, RowsGateUp> lb(sb);
     if (a.x_gather) {
         RowsGather sa{a.x, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
-        LoadKC<G1_TM, RowsGather> la(sa);
-        mainloop<G1_TM, G1_TN, false, false>(la, lb, nk, smem, acc);
+        LoadKC<TM, RowsGather> la(sa);
+        mainloop<TM, G1_TN, false, false>(la, lb, nk, smem, acc);
     } else {
         RowsDirect sa{a.x, a.H, a.xrow0 + lo, hi - lo};
-        LoadKC<G1_TM, RowsDirect> la(sa);
-        mainloop<G1_TM, G1_TN, false, false>(la, lb, nk, smem, acc);
+        LoadKC<TM, RowsDirect> la(sa);
+        mainloop<TM, G1_TN, false, false>(la, lb, nk, smem, acc);
     }
-    AccPos<G1_TM, G1_TN> pos;
+    AccPos<TM, G1_TN> pos;
     const int wn = threadIdx.x >> 7;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         if (rl >= hi) continue;
 #pragma unroll
@@ -85,23 +91,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
 }
 
 // ================================================================ forward GEMM 2
-// o = h W_down^T.  Tile 64 rows x 128 columns of H.
-constexpr int G2_TM = 64, G2_TN = 128;
+// o = h W_down^T.  Tile TM rows x 128 columns of H.
+constexpr int G2_TN = 128;
 
+template <int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G2_TM, G2_TN, false, false>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<TM, G2_TN, false, false>::STAGE];
     int e, lo, hi, nt;
-    if (!map_mtile<G2_TM>(a.g, a.H / G2_TN, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.H / G2_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * G2_TN;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
     RowsDirect sa{a.h, a.I, lo, hi - lo};
-    LoadKC<G2_TM, RowsDirect> la(sa);
+    LoadKC<TM, RowsDirect> la(sa);
     RowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, G2_TN};
     LoadKC<G2_TN, RowsDirect> lb(sb);
-    mainloop<G2_TM, G2_TN, false, false>(la, lb, a.I / kTK, smem, acc);
-    AccPos<G2_TM, G2_TN> pos;
+    mainloop<TM, G2_TN, false, false>(la, lb, a.I / kTK, smem, acc);
+    AccPos<TM, G2_TN> pos;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         if (rl >= hi) continue;
 #pragma unroll
@@ -120,33 +127,36 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
 //   dw partial = sum over this tile's columns of a * h
 //   dh = w * a;  du = dh * SiLU(g);  dg = dh * u * s * (1 + g (1 - s))
 //   hw = w * h   (the down-projection weight-gradient operand)
-// Tile 64 rows x 128 columns of I; reduction over H.
-constexpr int G3_TM = 64, G3_TN = 128;
+// Tile TM rows x 128 columns of I; reduction over H.
+constexpr int G3_TN = 128;
 
+template <int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[lds_two_blocks(2 * Smem<G3_TM, G3_TN, false, true>::STAGE)];
-    __shared__ float red[2][G3_TM];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[lds_two_blocks(2 * Smem<TM, G3_TN, false, true>::STAGE)];
+    __shared__ float red[2][TM];
     int e, lo, hi, nt;
-    if (!map_mtile<G3_TM>(a.g, a.I / G3_TN, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.I / G3_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * G3_TN;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
     KRowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, a.H};
     LoadKS<G3_TN, KRowsDirect> lb(sb);
     if (a.dy_gather) {
         RowsGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
-        LoadKC<G3_TM, RowsGather> la(sa);
-        mainloop<G3_TM, G3_TN, false, true>(la, lb, a.H / kTK, smem, acc);
+        LoadKC<TM, RowsGather> la(sa);
+        mainloop<TM, G3_TN, false, true>(la, lb, a.H / kTK, smem, acc);
     } else {
         RowsDirect sa{a.dy, a.H, a.dyrow0 + lo, hi - lo};
-        LoadKC<G3_TM, RowsDirect> la(sa);
-        mainloop<G3_TM, G3_TN, false, true>(la, lb, a.H / kTK, smem, acc);
+        LoadKC<TM, RowsDirect> la(sa);
+        mainloop<TM, G3_TN, false, true>(la, lb, a.H / kTK, smem, acc);
     }
-    AccPos<G3_TM, G3_TN> pos;
+    AccPos<TM, G3_TN> pos;
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6, wm = wv & 1, wn = wv >> 1;
-    float dot[2] = {0.f, 0.f};
+    float dot[TM / 32];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) dot[mb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         const bool ok = rl < hi;
         float wr = 1.0f;
@@ -185,16 +195,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a)
     // reduce the per-lane dots over the 4 lanes that share a row, then over
     // the two column-halves of the tile (waves wn = 0, 1), in a fixed order
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         dot[mb] += __shfl_xor(dot[mb], 16);
         dot[mb] += __shfl_xor(dot[mb], 32);
     }
     if (lane < 16) {
-        red[wn][wm * 32 + lane] = dot[0];
-        red[wn][wm * 32 + 16 + lane] = dot[1];
+#pragma unroll
+        for (int mb = 0; mb < TM / 32; ++mb) red[wn][wm * (TM / 2) + 16 * mb + lane] = dot[mb];
     }
     __syncthreads();
-    if (threadIdx.x < G3_TM) {
+    if (threadIdx.x < TM) {
         const int m = threadIdx.x;
         const int rl = lo + m;
         if (rl < hi) a.dw_part[(int64_t)rl * a.P + nt] = red[0][m] + red[1][m];
@@ -203,23 +213,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a)
 
 // ================================================================ backward: gate/up dgrad
 // dX = dg W_gate + du W_up: A = [dg | du] rows (K = 2I), B = [W_gate; W_up]
-// read with k as the memory row.  Tile 64 rows x 128 columns of H.
-constexpr int G4_TM = 64, G4_TN = 128;
+// read with k as the memory row.  Tile TM rows x 128 columns of H.
+constexpr int G4_TN = 128;
 
+template <int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<G4_TM, G4_TN, false, true>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<TM, G4_TN, false, true>::STAGE];
     int e, lo, hi, nt;
-    if (!map_mtile<G4_TM>(a.g, a.H / G4_TN, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.H / G4_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * G4_TN;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
     RowsDirect sa{a.dgu, 2 * a.I, lo, hi - lo};
-    LoadKC<G4_TM, RowsDirect> la(sa);
+    LoadKC<TM, RowsDirect> la(sa);
     KRowsGateUp sb{a.w_gate + (int64_t)e * a.I * a.H, a.w_up + (int64_t)e * a.I * a.H, a.H, n0, a.I};
     LoadKS<G4_TN, KRowsGateUp> lb(sb);
-    mainloop<G4_TM, G4_TN, false, true>(la, lb, 2 * a.I / kTK, smem, acc);
-    AccPos<G4_TM, G4_TN> pos;
+    mainloop<TM, G4_TN, false, true>(la, lb, 2 * a.I / kTK, smem, acc);
+    AccPos<TM, G4_TN> pos;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         if (rl >= hi) continue;
 #pragma unroll
@@ -451,36 +462,37 @@ static inline int mgroup_grid(const GroupRows& g, int TM) {
     return (int)(bound < g.rows ? bound : g.rows);
 }
 
+// row tile of a group description (the tile prefix was built with it)
+static inline int row_tile(const GroupRows& g) { return g.tm == 128 ? 128 : 64; }
+
+#define MOE_LAUNCH_TM(KERNEL, NCOLTILES)                                           \
+    do {                                                                           \
+        const int tm_ = row_tile(a.g);                                             \
+        const int grid_ = mgroup_grid(a.g, tm_) * (NCOLTILES);                     \
+        if (grid_ <= 0) return 0;                                                  \
+        if (tm_ == 128) KERNEL<128><<<grid_, 256, 0, st>>>(a);                     \
+        else KERNEL<64><<<grid_, 256, 0, st>>>(a);                                 \
+        return hipGetLastError() == hipSuccess ? 0 : -1;                           \
+    } while (0)
+
 int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gate_up");
-    const int grid = mgroup_grid(a.g, G1_TM) * (a.I / 64);
-    if (grid <= 0) return 0;
-    k_gemm_gate_up<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM(k_gemm_gate_up, a.I / 64);
 }
 
 int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down");
-    const int grid = mgroup_grid(a.g, G2_TM) * (a.H / G2_TN);
-    if (grid <= 0) return 0;
-    k_gemm_down<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM(k_gemm_down, a.H / G2_TN);
 }
 
 int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down_dgrad");
-    const int grid = mgroup_grid(a.g, G3_TM) * (a.I / G3_TN);
-    if (grid <= 0) return 0;
-    k_gemm_down_dgrad<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM(k_gemm_down_dgrad, a.I / G3_TN);
 }
 
 int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gu_dgrad");
-    const int grid = mgroup_grid(a.g, G4_TM) * (a.H / G4_TN);
-    if (grid <= 0) return 0;
-    k_gemm_gu_dgrad<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM(k_gemm_gu_dgrad, a.H / G4_TN);
 }
 
 int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
@@ -505,7 +517,9 @@ int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
-int gemm_row_tile() { return G1_TM; }
+// 128-row tiles once the mean group holds at least 192 rows (there the GEMMs
+// are MFMA work rather than weight streaming)
+int gemm_row_tile(int rows, int E) { return (int64_t)rows >= 192LL * E ? 128 : 64; }
 int wgrad_deep_rows() { return kTK; }
 int dgrad_col_tiles(int I) { return I / G3_TN; }
 

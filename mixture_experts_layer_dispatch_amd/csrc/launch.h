@@ -24,6 +24,7 @@ struct GroupRows {
     // (routed groups; a dense group is deep when dense_rows > deep_thr)
     const int32_t* deep;
     int deep_thr;
+    int tm;                   // M-grouped GEMMs: row tile of tile_off (64 or 128; 0 = 64)
 };
 
 struct GemmGateUpArgs {
@@ -271,7 +272,7 @@ int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st);
 int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st);
 int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st);
 int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st);
-int gemm_row_tile();
+int gemm_row_tile(int rows, int E);   // M-grouped row tile for a macrobatch of rows over E groups
 int dgrad_col_tiles(int I);
 int wgrad_deep_rows();        // bf16 weight gradients: groups above this go to the deep kernels
 int wgrad_deep_rows_mx();     // MXFP8 weight gradients: the same, in rows

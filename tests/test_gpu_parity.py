@@ -30,6 +30,8 @@ SMALL = {
     "stripes": si.custom_shape("stripes", T=256, H=512, I=512, E=16, k=4, seed=17),
     "stripes_ring": si.custom_shape("stripes_ring", T=512, H=512, I=1024, E=32, k=2, seed=18,
                                     n_shared=1, macrobatch=256, minibatch=128),
+    # groups of ~256 rows: the 128-row tiles of the row-grouped GEMMs
+    "dense_experts": si.custom_shape("dense_experts", T=512, H=256, I=256, E=8, k=4, seed=19),
 }
 
 
