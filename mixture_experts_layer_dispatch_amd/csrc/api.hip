@@ -242,6 +242,7 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
                       hipStream_t st) {
     const moe_weights_mx* wq = w->mx;
     int32_t* err = P.err();
+    const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
     for (int m = 0; m < g.n_macro; ++m) {
         char* half = P.half(m, g.halves);
         uint8_t* xq = (uint8_t*)(half + L.f_xd);
@@ -252,14 +253,14 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)(P.ws + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, 64, toff, err, st)) return MOE_ERR_HIP;
+        if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
         for (int i = 0; i < g.n_mini; ++i) {
             const int s0 = grow0 + i * g.Smb;
             if (launch_dispatch_mx(x, g.H, sched->row_of_slot, s0, s0 + g.Smb, g.k, grow0, g.Sm, xq, xs,
                                    err, st))
                 return MOE_ERR_HIP;
         }
-        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
         GemmGateUpMXArgs a1{grp, xq, xs, 0,
                             (const uint8_t*)wq->w_gate_q, (const uint8_t*)wq->w_gate_s,
                             (const uint8_t*)wq->w_up_q, (const uint8_t*)wq->w_up_s, g.H, g.I,
@@ -278,7 +279,7 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
             uint16_t* so = (uint16_t*)(sh + L.s_o);
             if (launch_mx_quant_rows((const uint16_t*)x + (size_t)t0 * g.H, g.M, g.H, sxq, sxs, st))
                 return MOE_ERR_HIP;
-            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
             GemmGateUpMXArgs s1{dense, sxq, sxs, 0,
                                 (const uint8_t*)wq->s_gate_q, (const uint8_t*)wq->s_gate_s,
                                 (const uint8_t*)wq->s_up_q, (const uint8_t*)wq->s_up_s, g.H, g.I,
@@ -335,6 +336,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
                        {dwu, accu, mode, counts, m, g.n_macro, g.E}};
         return launch_wgrad_mx(gu, st) == 0;
     };
+    const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
     for (int m = g.n_macro - 1; m >= 0; --m) {
         int mode = 0;
         if (g.n_macro > 1) mode = (m == g.n_macro - 1) ? 1 : (m == 0 ? 3 : 2);
@@ -348,9 +350,9 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)(ws + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, 64, toff, err, st)) return MOE_ERR_HIP;
+        if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
         if (launch_tile_prefix(off, g.E, g.Sm, 32, blk, err, st)) return MOE_ERR_HIP;
-        GroupRows grp{off, toff, g.E, g.Sm, 0, err};
+        GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
         GemmDownDgradMXArgs b1{grp, dyq, dys, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
                                sched->topk_w, (const uint8_t*)wq->w_down_tq,
                                (const uint8_t*)wq->w_down_ts, g.H, g.I, (const float*)saved->g,
@@ -384,7 +386,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
             uint8_t* sdguq = (uint8_t*)(sh + L.s_dguq);
             uint8_t* sdgus = (uint8_t*)(sh + L.s_dgus);
             uint16_t* sdx = (uint16_t*)(sh + L.s_dxm);
-            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err};
+            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
             GemmDownDgradMXArgs c1{dense, dyq, dys, 0, t0, nullptr, 0, g.k, g.S, nullptr,
                                    (const uint8_t*)wq->s_down_tq, (const uint8_t*)wq->s_down_ts, g.H,
                                    g.I, (const float*)saved->sg, (const float*)saved->su, t0, sdgu32,

@@ -223,15 +223,17 @@ __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int 
 // Like the bf16 kernel; in addition h = SiLU(g) * u, from the fp32
 // accumulators, is quantised along I: each wave holds exactly one 32-wide
 // block of h per row (lanes l, l^16, l^32, l^48 share it).
-constexpr int M1_TM = 64, M1_TN = 128;
+constexpr int M1_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
+
+template <int TM>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<M1_TM, M1_TN>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M1_TN>::STAGE];
     int e, lo, hi, nt;
-    if (!map_mtile<M1_TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
     const int i0 = nt * 64;
     const int H = a.H, I = a.I;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
     const uint16_t* wg = (const uint16_t*)(a.wg_q + (int64_t)e * I * H);
     const uint16_t* wu = (const uint16_t*)(a.wu_q + (int64_t)e * I * H);
     const uint32_t* wgs = (const uint32_t*)(a.wg_s + (int64_t)e * I * (H / 32));
@@ -240,15 +242,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
     ScalesGateUp ds{wgs, wus, H / 128, i0};
     RowsDirect da{(const uint16_t*)a.x_q, H / 2, a.xrow0 + lo, hi - lo};
     ScalesDirect dsa{(const uint32_t*)a.x_s, H / 128, a.xrow0 + lo, hi - lo};
-    LoadKC<M1_TM, RowsDirect> la(da);
+    LoadKC<TM, RowsDirect> la(da);
     LoadKC<M1_TN, RowsGateUp> lb(db);
-    LoadScales<M1_TM, ScalesDirect> sa(dsa);
+    LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScales<M1_TN, ScalesGateUp> sb(ds);
-    mainloop_mx<M1_TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
-    AccPos<M1_TM, M1_TN> pos;
+    mainloop_mx<TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+    AccPos<TM, M1_TN> pos;
     const int wn = threadIdx.x >> 7, lane = lane_id();
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         float hq[8];
         float amax = 0.f;
@@ -284,27 +286,29 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
 }
 
 // ================================================================ down projection
-constexpr int M2_TM = 64, M2_TN = 128;
+constexpr int M2_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
+
+template <int TM>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<M2_TM, M2_TN>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M2_TN>::STAGE];
     int e, lo, hi, nt;
-    if (!map_mtile<M2_TM>(a.g, a.H / M2_TN, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.H / M2_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * M2_TN;
     const int H = a.H, I = a.I;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
     RowsDirect da{(const uint16_t*)a.h_q, I / 2, lo, hi - lo};
     ScalesDirect dsa{(const uint32_t*)a.h_s, I / 128, lo, hi - lo};
     RowsDirect db{(const uint16_t*)(a.wd_q + (int64_t)e * H * I), I / 2, n0, M2_TN};
     ScalesDirect dsb{(const uint32_t*)(a.wd_s + (int64_t)e * H * (I / 32)), I / 128, n0, M2_TN};
-    LoadKC<M2_TM, RowsDirect> la(da);
+    LoadKC<TM, RowsDirect> la(da);
     LoadKC<M2_TN, RowsDirect> lb(db);
-    LoadScales<M2_TM, ScalesDirect> sa(dsa);
+    LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScales<M2_TN, ScalesDirect> sb(dsb);
-    mainloop_mx<M2_TM, M2_TN>(la, lb, sa, sb, I / 128, smem, acc);
-    AccPos<M2_TM, M2_TN> pos;
+    mainloop_mx<TM, M2_TN>(la, lb, sa, sb, I / 128, smem, acc);
+    AccPos<TM, M2_TN> pos;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         if (rl >= hi) continue;
 #pragma unroll
@@ -323,16 +327,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
 // g, u; the dw partial sum of a * h; dh = w a; dg, du.  Writes fp32 h and
 // dg | du for the row-wise quantisation of the weight gradients, and dg | du
 // quantised along I for the input gradient.  Tile 64 rows x 128 columns of I.
-constexpr int M3_TM = 64, M3_TN = 128;
+constexpr int M3_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
+
+template <int TM>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<M3_TM, M3_TN>::STAGE];
-    __shared__ float red[2][M3_TM];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M3_TN>::STAGE];
+    __shared__ float red[2][TM];
     int e, lo, hi, nt;
-    if (!map_mtile<M3_TM>(a.g, a.I / M3_TN, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.I / M3_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * M3_TN;
     const int H = a.H, I = a.I;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
     RowsDirect db{(const uint16_t*)(a.wdt_q + (int64_t)e * I * H), H / 2, n0, M3_TN};
     ScalesDirect dsb{(const uint32_t*)(a.wdt_s + (int64_t)e * I * (H / 32)), H / 128, n0, M3_TN};
     LoadKC<M3_TN, RowsDirect> lb(db);
@@ -340,22 +346,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
     if (a.dy_gather) {
         RowsGather da{(const uint16_t*)a.dy_q, H / 2, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
         ScalesGather dsa{(const uint32_t*)a.dy_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
-        LoadKC<M3_TM, RowsGather> la(da);
-        LoadScales<M3_TM, ScalesGather> sa(dsa);
-        mainloop_mx<M3_TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+        LoadKC<TM, RowsGather> la(da);
+        LoadScales<TM, ScalesGather> sa(dsa);
+        mainloop_mx<TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
     } else {
         RowsDirect da{(const uint16_t*)a.dy_q, H / 2, a.dyrow0 + lo, hi - lo};
         ScalesDirect dsa{(const uint32_t*)a.dy_s, H / 128, a.dyrow0 + lo, hi - lo};
-        LoadKC<M3_TM, RowsDirect> la(da);
-        LoadScales<M3_TM, ScalesDirect> sa(dsa);
-        mainloop_mx<M3_TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+        LoadKC<TM, RowsDirect> la(da);
+        LoadScales<TM, ScalesDirect> sa(dsa);
+        mainloop_mx<TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
     }
-    AccPos<M3_TM, M3_TN> pos;
+    AccPos<TM, M3_TN> pos;
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6, wm = wv & 1, wn = wv >> 1;
-    float dot[2] = {0.f, 0.f};
+    float dot[TM / 32];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) dot[mb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         const bool ok = rl < hi;
         float wr = 1.0f;
@@ -421,16 +429,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
     }
     if (!a.dw_part) return;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         dot[mb] += __shfl_xor(dot[mb], 16);
         dot[mb] += __shfl_xor(dot[mb], 32);
     }
     if (lane < 16) {
-        red[wn][wm * 32 + lane] = dot[0];
-        red[wn][wm * 32 + 16 + lane] = dot[1];
+#pragma unroll
+        for (int mb = 0; mb < TM / 32; ++mb) red[wn][wm * (TM / 2) + 16 * mb + lane] = dot[mb];
     }
     __syncthreads();
-    if (threadIdx.x < M3_TM) {
+    if (threadIdx.x < TM) {
         const int m = threadIdx.x;
         const int rl = lo + m;
         if (rl < hi) a.dw_part[(int64_t)rl * a.P + nt] = red[0][m] + red[1][m];
@@ -440,15 +448,17 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
 // ================================================================ backward: gate/up dgrad
 // dX = Q(dg) Q(W_gate) + Q(du) Q(W_up), reductions over I, against the
 // transposed pre-quantised weights; two K phases accumulate into one tile.
-constexpr int M4_TM = 64, M4_TN = 128;
+constexpr int M4_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
+
+template <int TM>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<M4_TM, M4_TN>::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M4_TN>::STAGE];
     int e, lo, hi, nt;
-    if (!map_mtile<M4_TM>(a.g, a.H / M4_TN, blockIdx.x, e, lo, hi, nt)) return;
+    if (!map_mtile<TM>(a.g, a.H / M4_TN, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * M4_TN;
     const int H = a.H, I = a.I;
-    f32x4 acc[2][4];
+    f32x4 acc[TM / 32][4];
 #pragma unroll
     for (int ph = 0; ph < 2; ++ph) {
         const uint8_t* wq = ph ? a.wut_q : a.wgt_q;
@@ -457,15 +467,15 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a
         ScalesDirect dsa{(const uint32_t*)(a.dgu_s + ph * (I / 32)), I / 64, lo, hi - lo};
         RowsDirect db{(const uint16_t*)(wq + (int64_t)e * H * I), I / 2, n0, M4_TN};
         ScalesDirect dsb{(const uint32_t*)(ws + (int64_t)e * H * (I / 32)), I / 128, n0, M4_TN};
-        LoadKC<M4_TM, RowsDirect> la(da);
+        LoadKC<TM, RowsDirect> la(da);
         LoadKC<M4_TN, RowsDirect> lb(db);
-        LoadScales<M4_TM, ScalesDirect> sa(dsa);
+        LoadScales<TM, ScalesDirect> sa(dsa);
         LoadScales<M4_TN, ScalesDirect> sb(dsb);
-        mainloop_mx<M4_TM, M4_TN>(la, lb, sa, sb, I / 128, smem, acc, ph == 1);
+        mainloop_mx<TM, M4_TN>(la, lb, sa, sb, I / 128, smem, acc, ph == 1);
     }
-    AccPos<M4_TM, M4_TN> pos;
+    AccPos<TM, M4_TN> pos;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
         if (rl >= hi) continue;
 #pragma unroll
@@ -736,36 +746,34 @@ static inline int mgroup_grid_mx(const GroupRows& g, int TM) {
     return (int)(bound < g.rows ? bound : g.rows);
 }
 
+#define MOE_LAUNCH_TM_MX(KERNEL, NCOLTILES)                                        \
+    do {                                                                           \
+        const int tm_ = a.g.tm == 128 ? 128 : 64;                                  \
+        const int grid_ = mgroup_grid_mx(a.g, tm_) * (NCOLTILES);                  \
+        if (grid_ <= 0) return 0;                                                  \
+        if (tm_ == 128) KERNEL<128><<<grid_, 256, 0, st>>>(a);                     \
+        else KERNEL<64><<<grid_, 256, 0, st>>>(a);                                 \
+        return hipGetLastError() == hipSuccess ? 0 : -1;                           \
+    } while (0)
+
 int launch_gemm_gate_up_mx(const GemmGateUpMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gate_up_mx");
-    const int grid = mgroup_grid_mx(a.g, M1_TM) * (a.I / 64);
-    if (grid <= 0) return 0;
-    k_gemm_gate_up_mx<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM_MX(k_gemm_gate_up_mx, a.I / 64);
 }
 
 int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down_mx");
-    const int grid = mgroup_grid_mx(a.g, M2_TM) * (a.H / M2_TN);
-    if (grid <= 0) return 0;
-    k_gemm_down_mx<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM_MX(k_gemm_down_mx, a.H / M2_TN);
 }
 
 int launch_gemm_down_dgrad_mx(const GemmDownDgradMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down_dgrad_mx");
-    const int grid = mgroup_grid_mx(a.g, M3_TM) * (a.I / M3_TN);
-    if (grid <= 0) return 0;
-    k_gemm_down_dgrad_mx<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM_MX(k_gemm_down_dgrad_mx, a.I / M3_TN);
 }
 
 int launch_gemm_gu_dgrad_mx(const GemmGuDgradMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gu_dgrad_mx");
-    const int grid = mgroup_grid_mx(a.g, M4_TM) * (a.H / M4_TN);
-    if (grid <= 0) return 0;
-    k_gemm_gu_dgrad_mx<<<grid, 256, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
+    MOE_LAUNCH_TM_MX(k_gemm_gu_dgrad_mx, a.H / M4_TN);
 }
 
 int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
