@@ -413,11 +413,11 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_down_deep(WgradDownArgs a) {
         if (a.dy_gather) {
             KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
             LoadKS<D_TM, KRowsGroupGather> la(sa);
-            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+            mainloop_ks_pipe<D_TM, D_TN>(la, lb, nk, smem, acc);
         } else {
             KRowsGroup sa{a.dy, a.H, a.dyrow0 + lo, n, m0};
             LoadKS<D_TM, KRowsGroup> la(sa);
-            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+            mainloop_ks_pipe<D_TM, D_TN>(la, lb, nk, smem, acc);
         }
         WgradOut o = a.out;
         o.mode = wgrad_mode(a.out, e, n);
@@ -442,11 +442,11 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_gate_up_deep(WgradGateUpArgs a
         if (a.x_gather) {
             KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, n0, a.k, a.S, a.g.err};
             LoadKS<D_TN, KRowsGroupGather> lb(sb);
-            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+            mainloop_ks_pipe<D_TM, D_TN>(la, lb, nk, smem, acc);
         } else {
             KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, n0};
             LoadKS<D_TN, KRowsGroup> lb(sb);
-            mainloop<D_TM, D_TN, true, true>(la, lb, nk, smem, acc);
+            mainloop_ks_pipe<D_TM, D_TN>(la, lb, nk, smem, acc);
         }
         WgradOut o = up ? a.out_up : a.out_gate;
         o.mode = wgrad_mode(o, e, n);

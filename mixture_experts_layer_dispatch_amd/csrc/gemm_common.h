@@ -209,6 +209,23 @@ struct LoadKS {
 #pragma unroll
         for (int q = 0; q < PER; ++q) *(uint4*)(s + kr[q] * Tile<ROWS, true>::P + cc[q] * 8) = v[q];
     }
+    // Pipelined form for long K loops: load_pipe(kt) uses the row indices the
+    // previous call (or prime) fetched and fetches those of step kt + 1, so a
+    // gathered source's index load is off the critical path.
+    int pn[PER];
+    __device__ void prime(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) pn[q] = src.pre(kt * kTK + kr[q]);
+    }
+    __device__ void load_pipe(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const uint16_t* a = src.at(kt * kTK + kr[q], pn[q]);
+            v[q] = a ? *(const uint4*)(a + cc[q] * 8) : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int q = 0; q < PER; ++q) pn[q] = src.pre((kt + 1) * kTK + kr[q]);
+    }
     // Row pointers of K step kt at column 0, kept for loads that only move
     // the column window (src.col0 must be 0 when this is called).
     const uint16_t* rp[PER];
@@ -331,6 +348,42 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
             lb.load(kt + 1);
         }
         mma_tile<TM, TN, AKS, BKS>(cur, cur + SM::A, wm0, wn0, acc);
+        if (more) {
+            la.store(nxt);
+            lb.store(nxt + SM::A);
+        }
+        __syncthreads();
+    }
+}
+
+// The same K loop for KS operands whose rows may be gathered: index loads run
+// one K step ahead of the data loads they feed.
+template <int TM, int TN, class LA, class LB>
+__device__ __forceinline__ void mainloop_ks_pipe(LA& la, LB& lb, int nk, uint16_t* smem,
+                                                 f32x4 (&acc)[TM / 32][TN / 32]) {
+    using SM = Smem<TM, TN, true, true>;
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
+    zero_acc<TM, TN>(acc);
+    if (nk <= 0) return;
+    uint16_t* buf0 = smem;
+    uint16_t* buf1 = smem + SM::STAGE;
+    la.prime(0);
+    lb.prime(0);
+    la.load_pipe(0);
+    lb.load_pipe(0);
+    la.store(buf0);
+    lb.store(buf0 + SM::A);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        uint16_t* cur = (kt & 1) ? buf1 : buf0;
+        uint16_t* nxt = (kt & 1) ? buf0 : buf1;
+        const bool more = kt + 1 < nk;
+        if (more) {
+            la.load_pipe(kt + 1);
+            lb.load_pipe(kt + 1);
+        }
+        mma_tile<TM, TN, true, true>(cur, cur + SM::A, wm0, wn0, acc);
         if (more) {
             la.store(nxt);
             lb.store(nxt + SM::A);
