@@ -106,14 +106,19 @@ typedef struct moe_sched {
  * byte each) and E8M0 scales (one byte per 32 codes along the listed axis).
  * The forward reads the first three pairs; the backward's input gradients
  * read the transposed copies ([ALPHA] 三: weights are quantised outside the
- * timed region, so both orientations are prepared ahead of time). */
+ * timed region, so both orientations are prepared ahead of time).
+ * Codes are row-major [rows, K].  Scales are K-step-major per matrix: for a
+ * matrix of R rows and K columns they form [K/128, R, 4] bytes, the scale of
+ * row r, block b (codes 32b..32b+31 of that row) at byte
+ * ((b / 4) * R + r) * 4 + b % 4, so the scales of one 128-code step of
+ * consecutive rows are contiguous.  Sizes below are in bytes per matrix. */
 typedef struct moe_weights_mx {
-    const void* w_gate_q;  const void* w_gate_s;   /* [E, I, H], [E, I, H/32]  blocks along H */
-    const void* w_up_q;    const void* w_up_s;     /* [E, I, H], [E, I, H/32]                 */
-    const void* w_down_q;  const void* w_down_s;   /* [E, H, I], [E, H, I/32]  blocks along I */
-    const void* w_gate_tq; const void* w_gate_ts;  /* [E, H, I], [E, H, I/32]  W_gate^T, along I */
-    const void* w_up_tq;   const void* w_up_ts;    /* [E, H, I], [E, H, I/32]  W_up^T           */
-    const void* w_down_tq; const void* w_down_ts;  /* [E, I, H], [E, I, H/32]  W_down^T, along H */
+    const void* w_gate_q;  const void* w_gate_s;   /* [E, I, H], [E, H/128, I, 4]  blocks along H */
+    const void* w_up_q;    const void* w_up_s;     /* [E, I, H], [E, H/128, I, 4]                 */
+    const void* w_down_q;  const void* w_down_s;   /* [E, H, I], [E, I/128, H, 4]  blocks along I */
+    const void* w_gate_tq; const void* w_gate_ts;  /* [E, H, I], [E, I/128, H, 4]  W_gate^T, along I */
+    const void* w_up_tq;   const void* w_up_ts;    /* [E, H, I], [E, I/128, H, 4]  W_up^T           */
+    const void* w_down_tq; const void* w_down_ts;  /* [E, I, H], [E, H/128, I, 4]  W_down^T, along H */
     /* the shared expert (if n_shared): the same twelve arrays without the E axis */
     const void* s_gate_q;  const void* s_gate_s;
     const void* s_up_q;    const void* s_up_s;

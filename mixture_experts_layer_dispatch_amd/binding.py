@@ -291,26 +291,19 @@ def moe_backward(cfg: Config, sched: dict, saved: dict, x: torch.Tensor, weights
 
 
 def alloc_weights_mx(cfg: Config, device="cuda") -> dict:
-    """Buffers of every quantised weight array (codes and scales, uint8)."""
+    """Buffers of every quantised weight array (uint8): codes [.., rows, K],
+    scales K-step-major [.., K/128, rows, 4]."""
     E, H, I = cfg.E, cfg.H, cfg.I
     u8 = dict(dtype=torch.uint8, device=device)
-    q = {
-        "w_gate_q": torch.empty(E, I, H, **u8), "w_gate_s": torch.empty(E, I, H // 32, **u8),
-        "w_up_q": torch.empty(E, I, H, **u8), "w_up_s": torch.empty(E, I, H // 32, **u8),
-        "w_down_q": torch.empty(E, H, I, **u8), "w_down_s": torch.empty(E, H, I // 32, **u8),
-        "w_gate_tq": torch.empty(E, H, I, **u8), "w_gate_ts": torch.empty(E, H, I // 32, **u8),
-        "w_up_tq": torch.empty(E, H, I, **u8), "w_up_ts": torch.empty(E, H, I // 32, **u8),
-        "w_down_tq": torch.empty(E, I, H, **u8), "w_down_ts": torch.empty(E, I, H // 32, **u8),
-    }
-    if cfg.n_shared:
-        q.update({
-            "s_gate_q": torch.empty(I, H, **u8), "s_gate_s": torch.empty(I, H // 32, **u8),
-            "s_up_q": torch.empty(I, H, **u8), "s_up_s": torch.empty(I, H // 32, **u8),
-            "s_down_q": torch.empty(H, I, **u8), "s_down_s": torch.empty(H, I // 32, **u8),
-            "s_gate_tq": torch.empty(H, I, **u8), "s_gate_ts": torch.empty(H, I // 32, **u8),
-            "s_up_tq": torch.empty(H, I, **u8), "s_up_ts": torch.empty(H, I // 32, **u8),
-            "s_down_tq": torch.empty(I, H, **u8), "s_down_ts": torch.empty(I, H // 32, **u8),
-        })
+    mats = (("gate_", I, H), ("up_", I, H), ("down_", H, I),          # "w_gate_q", "w_gate_s", ...
+            ("gate_t", H, I), ("up_t", H, I), ("down_t", I, H))      # "w_gate_tq", "w_gate_ts", ...
+    q = {}
+    for prefix, lead in (("w_", (E,)), ("s_", ())):
+        if prefix == "s_" and not cfg.n_shared:
+            continue
+        for name, rows, K in mats:
+            q[prefix + name + "q"] = torch.empty(*lead, rows, K, **u8)
+            q[prefix + name + "s"] = torch.empty(*lead, K // 128, rows, 4, **u8)
     return q
 
 

@@ -692,9 +692,10 @@ moe_status moe_quantize_weights_mxfp8(const moe_config* cfg, const moe_weights* 
                    const void* gts, const void* utq, const void* uts, const void* dtq,
                    const void* dts) -> bool {
         // forward: rows along their reduction axis
-        if (launch_mx_quant_rows(wg, (int64_t)n * I, H, (void*)gq, (void*)gs, st)) return false;
-        if (launch_mx_quant_rows(wu, (int64_t)n * I, H, (void*)uq, (void*)us, st)) return false;
-        if (launch_mx_quant_rows(wd, (int64_t)n * H, I, (void*)dq, (void*)ds, st)) return false;
+        // (scales K-step-major per matrix, so a GEMM's K step of scales is contiguous)
+        if (launch_mx_quant_rows(wg, (int64_t)n * I, H, (void*)gq, (void*)gs, st, I)) return false;
+        if (launch_mx_quant_rows(wu, (int64_t)n * I, H, (void*)uq, (void*)us, st, I)) return false;
+        if (launch_mx_quant_rows(wd, (int64_t)n * H, I, (void*)dq, (void*)ds, st, H)) return false;
         // backward: transposed copies, blocks along the other axis
         if (launch_mx_quant_cols(wg, n, I, H, (void*)gtq, (void*)gts, st)) return false;
         if (launch_mx_quant_cols(wu, n, I, H, (void*)utq, (void*)uts, st)) return false;

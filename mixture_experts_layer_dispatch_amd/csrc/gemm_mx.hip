@@ -22,25 +22,37 @@ namespace moe {
 typedef int v8i32 __attribute__((ext_vector_type(8)));
 
 // ================================================================ scale sources
-struct ScalesDirect {          // row r -> words of row row0 + r
+// row(r) points at the scale word of row r for K step 0; kstride() is the
+// distance in words between K steps.
+struct ScalesDirect {          // activations, [rows, K / 128] words
     const uint32_t* base;
     int64_t ld;                // words per row (K / 128)
     int row0, nvalid;
     __device__ const uint32_t* row(int r) const {
         return r < nvalid ? base + (int64_t)(row0 + r) * ld : nullptr;
     }
+    __device__ int kstride() const { return 1; }
 };
 
-struct ScalesGateUp {          // same quarter interleave as RowsGateUp
+struct ScalesKMajor {          // weights, K-step-major: word (j, r) at j * nrows + r
+    const uint32_t* base;
+    int nrows;                 // rows of the matrix
+    int row0, nvalid;
+    __device__ const uint32_t* row(int r) const { return r < nvalid ? base + row0 + r : nullptr; }
+    __device__ int kstride() const { return nrows; }
+};
+
+struct ScalesGateUp {          // same quarter interleave as RowsGateUp, K-step-major
     const uint32_t* wg;
     const uint32_t* wu;
-    int64_t ld;
+    int nrows;                 // I
     int i0;
     __device__ const uint32_t* row(int n) const {
         const int q = n >> 5;
         const int i = i0 + ((q >> 1) << 5) + (n & 31);
-        return global_select(q & 1, wg, wu) + (int64_t)i * ld;
+        return global_select(q & 1, wg, wu) + i;
     }
+    __device__ int kstride() const { return nrows; }
 };
 
 struct ScalesGather {         // row r = schedule row grow0 + r -> words of its token
@@ -54,17 +66,20 @@ struct ScalesGather {         // row r = schedule row grow0 + r -> words of its 
         if ((unsigned)s >= (unsigned)S) return nullptr;
         return base + (int64_t)(s / k) * ld;
     }
+    __device__ int kstride() const { return 1; }
 };
 
 template <int ROWS, class Src>
 struct LoadScales {
     const uint32_t* p;
     uint32_t v;
+    int kst;
     __device__ explicit LoadScales(const Src& s) {
         p = threadIdx.x < ROWS ? s.row(threadIdx.x) : nullptr;
         v = 0;
+        kst = s.kstride();
     }
-    __device__ void load(int kt) { v = p ? p[kt] : 0u; }
+    __device__ void load(int kt) { v = p ? p[(int64_t)kt * kst] : 0u; }
     __device__ void store(uint32_t* s) const {
         if (threadIdx.x < ROWS) s[threadIdx.x] = v;
     }
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
     const uint32_t* wgs = (const uint32_t*)(a.wg_s + (int64_t)e * I * (H / 32));
     const uint32_t* wus = (const uint32_t*)(a.wu_s + (int64_t)e * I * (H / 32));
     RowsGateUp db{wg, wu, H / 2, i0};
-    ScalesGateUp ds{wgs, wus, H / 128, i0};
+    ScalesGateUp ds{wgs, wus, I, i0};
     RowsDirect da{(const uint16_t*)a.x_q, H / 2, a.xrow0 + lo, hi - lo};
     ScalesDirect dsa{(const uint32_t*)a.x_s, H / 128, a.xrow0 + lo, hi - lo};
     LoadKC<TM, RowsDirect> la(da);
@@ -300,11 +315,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     RowsDirect da{(const uint16_t*)a.h_q, I / 2, lo, hi - lo};
     ScalesDirect dsa{(const uint32_t*)a.h_s, I / 128, lo, hi - lo};
     RowsDirect db{(const uint16_t*)(a.wd_q + (int64_t)e * H * I), I / 2, n0, M2_TN};
-    ScalesDirect dsb{(const uint32_t*)(a.wd_s + (int64_t)e * H * (I / 32)), I / 128, n0, M2_TN};
+    ScalesKMajor dsb{(const uint32_t*)(a.wd_s + (int64_t)e * H * (I / 32)), H, n0, M2_TN};
     LoadKC<TM, RowsDirect> la(da);
     LoadKC<M2_TN, RowsDirect> lb(db);
     LoadScales<TM, ScalesDirect> sa(dsa);
-    LoadScales<M2_TN, ScalesDirect> sb(dsb);
+    LoadScales<M2_TN, ScalesKMajor> sb(dsb);
     mainloop_mx<TM, M2_TN>(la, lb, sa, sb, I / 128, smem, acc);
     AccPos<TM, M2_TN> pos;
 #pragma unroll
@@ -340,9 +355,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
     const int H = a.H, I = a.I;
     f32x4 acc[TM / 32][4];
     RowsDirect db{(const uint16_t*)(a.wdt_q + (int64_t)e * I * H), H / 2, n0, M3_TN};
-    ScalesDirect dsb{(const uint32_t*)(a.wdt_s + (int64_t)e * I * (H / 32)), H / 128, n0, M3_TN};
+    ScalesKMajor dsb{(const uint32_t*)(a.wdt_s + (int64_t)e * I * (H / 32)), I, n0, M3_TN};
     LoadKC<M3_TN, RowsDirect> lb(db);
-    LoadScales<M3_TN, ScalesDirect> sb(dsb);
+    LoadScales<M3_TN, ScalesKMajor> sb(dsb);
     if (a.dy_gather) {
         RowsGather da{(const uint16_t*)a.dy_q, H / 2, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
         ScalesGather dsa{(const uint32_t*)a.dy_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
@@ -466,11 +481,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a
         RowsDirect da{(const uint16_t*)(a.dgu_q + ph * I), I, lo, hi - lo};
         ScalesDirect dsa{(const uint32_t*)(a.dgu_s + ph * (I / 32)), I / 64, lo, hi - lo};
         RowsDirect db{(const uint16_t*)(wq + (int64_t)e * H * I), I / 2, n0, M4_TN};
-        ScalesDirect dsb{(const uint32_t*)(ws + (int64_t)e * H * (I / 32)), I / 128, n0, M4_TN};
+        ScalesKMajor dsb{(const uint32_t*)(ws + (int64_t)e * H * (I / 32)), H, n0, M4_TN};
         LoadKC<TM, RowsDirect> la(da);
         LoadKC<M4_TN, RowsDirect> lb(db);
         LoadScales<TM, ScalesDirect> sa(dsa);
-        LoadScales<M4_TN, ScalesDirect> sb(dsb);
+        LoadScales<M4_TN, ScalesKMajor> sb(dsb);
         mainloop_mx<TM, M4_TN>(la, lb, sa, sb, I / 128, smem, acc, ph == 1);
     }
     AccPos<TM, M4_TN> pos;

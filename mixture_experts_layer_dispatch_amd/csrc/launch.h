@@ -248,7 +248,8 @@ int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t*
 int launch_deep_list(const int32_t* offsets, int E, int rows, int thr, int32_t* list, hipStream_t st);
 
 // mx.hip
-int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st);
+int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st,
+                         int kmaj_rows = 0);
 int launch_mx_quant_cols(const void* w, int batch, int R, int C, void* codes, void* scales,
                          hipStream_t st);
 int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,

@@ -10,11 +10,14 @@
 namespace moe {
 
 // ------------------------------------------------------------------ rows
-// X [R, K] bf16 -> codes [R, K] e4m3, scales [R, K/32] e8m0, blocks along K.
+// X [R, K] bf16 -> codes [R, K] e4m3, scales e8m0, blocks along K.
+// Scales are [R, K/32] (kmaj_rows == 0), or K-step-major per matrix of
+// kmaj_rows rows: the four scales of row r's K step j (codes 128j..128j+127)
+// form word j * kmaj_rows + r, so one K step of consecutive rows is contiguous.
 // A thread owns 8 consecutive elements; four neighbouring threads share a
 // block and agree on its maximum through two lane exchanges.
-__global__ __launch_bounds__(256) void k_mx_quant_rows(const uint4* __restrict__ x, int64_t n8,
-                                                       uint2* __restrict__ codes,
+__global__ __launch_bounds__(256) void k_mx_quant_rows(const uint4* __restrict__ x, int64_t n8, int K,
+                                                       int kmaj_rows, uint2* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     const bool ok = i < n8;
@@ -35,14 +38,26 @@ __global__ __launch_bounds__(256) void k_mx_quant_rows(const uint4* __restrict__
     const int s = mx_scale_exp(amax);
     if (ok) {
         codes[i] = e4m3_pack8(v, s);
-        if ((i & 3) == 0) scales[i >> 2] = (uint8_t)(s + 127);
+        if ((i & 3) == 0) {
+            int64_t at = i >> 2;
+            if (kmaj_rows > 0) {
+                const int nb = K / 32;
+                const int64_t row = at / nb;
+                const int b = (int)(at - row * nb);
+                const int64_t mat = row / kmaj_rows, r = row - mat * kmaj_rows;
+                at = mat * kmaj_rows * nb + ((int64_t)(b >> 2) * kmaj_rows + r) * 4 + (b & 3);
+            }
+            scales[at] = (uint8_t)(s + 127);
+        }
     }
 }
 
 // ------------------------------------------------------------------ columns
-// W [R, C] bf16 (per matrix of a batch) -> codes [C, R], scales [C, R/32]:
-// blocks of 32 consecutive rows of one column, written transposed so that the
-// block is contiguous.  A thread owns one column of a 32-row band.
+// W [R, C] bf16 (per matrix of a batch) -> codes [C, R]: blocks of 32
+// consecutive rows of one column, written transposed so that the block is
+// contiguous; scales K-step-major over the C rows of the transposed matrix
+// (the scale of row c, block b at byte ((b / 4) * C + c) * 4 + b % 4).
+// A thread owns one column of a 32-row band.
 __global__ __launch_bounds__(256) void k_mx_quant_cols(const uint16_t* __restrict__ w, int R, int C,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
@@ -65,7 +80,8 @@ __global__ __launch_bounds__(256) void k_mx_quant_cols(const uint16_t* __restric
     uint4* dst = (uint4*)(codes + mat * R * (int64_t)C + (int64_t)c * R + r0);
     dst[0] = make_uint4(wds[0], wds[1], wds[2], wds[3]);
     dst[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
-    scales[mat * (int64_t)C * (R / 32) + (int64_t)c * (R / 32) + blockIdx.y] = (uint8_t)(s + 127);
+    const int b = blockIdx.y;
+    scales[mat * (int64_t)C * (R / 32) + ((int64_t)(b >> 2) * C + c) * 4 + (b & 3)] = (uint8_t)(s + 127);
 }
 
 // ------------------------------------------------------------------ dispatch
@@ -212,12 +228,13 @@ __global__ __launch_bounds__(256) void k_mx_quant_group_t(PadGroups g, QtSrc src
 }
 
 // ------------------------------------------------------------------ launchers
-int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st) {
+int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st,
+                         int kmaj_rows) {
     ProfScope prof_(st, "mx_quant_rows");
     const int64_t n8 = rows * (int64_t)K / 8;
     if (n8 <= 0) return 0;
-    k_mx_quant_rows<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint4*)x, n8, (uint2*)codes,
-                                                                 (uint8_t*)scales);
+    k_mx_quant_rows<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint4*)x, n8, K, kmaj_rows,
+                                                                 (uint2*)codes, (uint8_t*)scales);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -117,3 +117,18 @@ def test_product_package_does_not_import_the_oracle():
                 text = open(os.path.join(dirpath, fn)).read()
                 assert "import oracle" not in text and "from oracle" not in text, fn
                 assert "synth_inputs" not in text, fn
+
+
+def test_mx_weight_buffers_match_the_header_layout():
+    """alloc_weights_mx gives every field of moe_weights_mx, codes [.., rows, K]
+    and K-step-major scales [.., K/128, rows, 4], as include/moe.h lays them out."""
+    cfg = B.Config(T=8, H=256, I=384, E=3, k=1, n_shared=1)
+    q = B.alloc_weights_mx(cfg, "cpu")
+    assert sorted(q) == sorted(B.MX_FIELDS)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    dims = {"gate_": (I, H), "up_": (I, H), "down_": (H, I),
+            "gate_t": (H, I), "up_t": (H, I), "down_t": (I, H)}
+    for name, (rows, K) in dims.items():
+        for pre, lead in (("w_", (E,)), ("s_", ())):
+            assert tuple(q[pre + name + "q"].shape) == (*lead, rows, K)
+            assert tuple(q[pre + name + "s"].shape) == (*lead, K // 128, rows, 4)

@@ -56,9 +56,13 @@ class MXCase(Case):
 
 
 def _check_quantised(w_bf16, codes, scales, axis):
-    """codes/scales from the GPU vs the oracle's quantiser of w along `axis`."""
+    """codes/scales from the GPU vs the oracle's quantiser of w along `axis`.
+    The GPU's scales are K-step-major, [K/128, rows, 4]: scale (row r, block b)
+    sits at [b // 4, r, b % 4]."""
     ref_c, ref_s = oracle.mx_quantize(f32(w_bf16).astype(np.float64), axis=axis)
-    got_c, got_s = codes.cpu().numpy(), scales.cpu().numpy()
+    got_c, ks = codes.cpu().numpy(), scales.cpu().numpy()
+    assert ks.ndim == 3 and ks.shape[1:] == (got_c.shape[0], 4) and ks.shape[0] * 128 == got_c.shape[1]
+    got_s = ks.transpose(1, 0, 2).reshape(got_c.shape[0], got_c.shape[1] // 32)
     if axis == 0:                       # the GPU stores the transposed copy
         got_c, got_s = got_c.T, got_s.T
     np.testing.assert_array_equal(got_s, ref_s)
