@@ -362,6 +362,35 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
                              (const uint8_t*)wq->w_gate_ts, (const uint8_t*)wq->w_up_tq,
                              (const uint8_t*)wq->w_up_ts, g.H, g.I, dxd};
         if (launch_gemm_gu_dgrad_mx(b2, st)) return MOE_ERR_HIP;
+        // the shared expert's input gradient, then reverse-dispatch and the
+        // softmax backward while dXd is still in cache; the weight gradients
+        // (the large writes) come last
+        const uint16_t* sh_dx = nullptr;
+        char* sh = g.shared ? P.sh() : nullptr;
+        GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
+        if (g.shared) {
+            float* sdgu32 = (float*)(sh + L.s_dgu32);
+            float* sh32 = (float*)(sh + L.s_h32);
+            uint8_t* sdguq = (uint8_t*)(sh + L.s_dguq);
+            uint8_t* sdgus = (uint8_t*)(sh + L.s_dgus);
+            uint16_t* sdx = (uint16_t*)(sh + L.s_dxm);
+            GemmDownDgradMXArgs c1{dense, dyq, dys, 0, t0, nullptr, 0, g.k, g.S, nullptr,
+                                   (const uint8_t*)wq->s_down_tq, (const uint8_t*)wq->s_down_ts, g.H,
+                                   g.I, (const float*)saved->sg, (const float*)saved->su, t0, sdgu32,
+                                   sh32, sdguq, sdgus, nullptr, g.P};
+            if (launch_gemm_down_dgrad_mx(c1, st)) return MOE_ERR_HIP;
+            GemmGuDgradMXArgs c2{dense, sdguq, sdgus, (const uint8_t*)wq->s_gate_tq,
+                                 (const uint8_t*)wq->s_gate_ts, (const uint8_t*)wq->s_up_tq,
+                                 (const uint8_t*)wq->s_up_ts, g.H, g.I, sdx};
+            if (launch_gemm_gu_dgrad_mx(c2, st)) return MOE_ERR_HIP;
+            sh_dx = sdx;
+        }
+        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
+                             dx, err, st))
+            return MOE_ERR_HIP;
+        if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
+                               t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
+            return MOE_ERR_HIP;
         int32_t* deep = (int32_t*)(ws + L.deep);
         if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows_mx(), deep, st)) return MOE_ERR_HIP;
         PadGroups pg{off, blk, g.E, g.Sm, 0, err, deep, wgrad_deep_rows_mx()};
@@ -378,24 +407,9 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         if (!wgrads(pg, mode, cnts, m, (uint16_t*)gr->d_w_down, P.wacc(L.wacc_d),
                     (uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), (uint16_t*)gr->d_w_up, P.wacc(L.wacc_u)))
             return MOE_ERR_HIP;
-        const uint16_t* sh_dx = nullptr;
         if (g.shared) {
-            char* sh = P.sh();
             float* sdgu32 = (float*)(sh + L.s_dgu32);
             float* sh32 = (float*)(sh + L.s_h32);
-            uint8_t* sdguq = (uint8_t*)(sh + L.s_dguq);
-            uint8_t* sdgus = (uint8_t*)(sh + L.s_dgus);
-            uint16_t* sdx = (uint16_t*)(sh + L.s_dxm);
-            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
-            GemmDownDgradMXArgs c1{dense, dyq, dys, 0, t0, nullptr, 0, g.k, g.S, nullptr,
-                                   (const uint8_t*)wq->s_down_tq, (const uint8_t*)wq->s_down_ts, g.H,
-                                   g.I, (const float*)saved->sg, (const float*)saved->su, t0, sdgu32,
-                                   sh32, sdguq, sdgus, nullptr, g.P};
-            if (launch_gemm_down_dgrad_mx(c1, st)) return MOE_ERR_HIP;
-            GemmGuDgradMXArgs c2{dense, sdguq, sdgus, (const uint8_t*)wq->s_gate_tq,
-                                 (const uint8_t*)wq->s_gate_ts, (const uint8_t*)wq->s_up_tq,
-                                 (const uint8_t*)wq->s_up_ts, g.H, g.I, sdx};
-            if (launch_gemm_gu_dgrad_mx(c2, st)) return MOE_ERR_HIP;
             PadGroups pd{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows_mx()};
             QtSrc sdy{3, dyb, nullptr, g.H, nullptr, nullptr, 0, t0, g.k, g.S};
             QtSrc shh{1, nullptr, sh32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
@@ -410,14 +424,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
                         (uint16_t*)gr->d_s_gate, P.wacc(L.wacc_sg), (uint16_t*)gr->d_s_up,
                         P.wacc(L.wacc_su)))
                 return MOE_ERR_HIP;
-            sh_dx = sdx;
         }
-        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
-                             dx, err, st))
-            return MOE_ERR_HIP;
-        if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
-                               t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
-            return MOE_ERR_HIP;
     }
     return MOE_OK;
 }
@@ -620,6 +627,31 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         if (launch_gemm_down_dgrad(b1, st)) return MOE_ERR_HIP;
         GemmGuDgradArgs b2{grp, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I, dxd};
         if (launch_gemm_gu_dgrad(b2, st)) return MOE_ERR_HIP;
+        // the shared expert's input gradient, then reverse-dispatch and the
+        // softmax backward while dXd is still in cache; the weight gradients
+        // (the large writes) come last
+        const uint16_t* sh_dx = nullptr;
+        GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows(), gemm_row_tile(g.M, 1)};
+        uint16_t* sdgu = g.shared ? (uint16_t*)(P.sh() + L.s_dgu) : nullptr;
+        uint16_t* shw = g.shared ? (uint16_t*)(P.sh() + L.s_hw) : nullptr;
+        if (g.shared) {
+            uint16_t* sdx = (uint16_t*)(P.sh() + L.s_dx);
+            GemmDownDgradArgs c1{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, nullptr,
+                                 (const uint16_t*)w->s_down, g.H, g.I, (const uint16_t*)saved->sg,
+                                 (const uint16_t*)saved->su, t0, sdgu, shw, nullptr, g.P};
+            if (launch_gemm_down_dgrad(c1, st)) return MOE_ERR_HIP;
+            GemmGuDgradArgs c2{dense, sdgu, (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up,
+                               g.H, g.I, sdx};
+            if (launch_gemm_gu_dgrad(c2, st)) return MOE_ERR_HIP;
+            sh_dx = sdx;
+        }
+        // reverse-dispatch: dx_t = [shared] + sum_j dXd[row(t, j)]
+        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
+                             dx, err, st))
+            return MOE_ERR_HIP;
+        if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
+                               t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
+            return MOE_ERR_HIP;
         int32_t* deep = (int32_t*)((char*)workspace + L.deep);
         if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows(), deep, st)) return MOE_ERR_HIP;
         GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err, deep, wgrad_deep_rows()};
@@ -631,19 +663,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                            {(uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), mode, cnts, m, g.n_macro, g.E},
                            {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode, cnts, m, g.n_macro, g.E}};
         if (launch_wgrad_gate_up(b4, st)) return MOE_ERR_HIP;
-        const uint16_t* sh_dx = nullptr;
         if (g.shared) {
-            uint16_t* sdgu = (uint16_t*)(P.sh() + L.s_dgu);
-            uint16_t* shw = (uint16_t*)(P.sh() + L.s_hw);
-            uint16_t* sdx = (uint16_t*)(P.sh() + L.s_dx);
-            GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows(), gemm_row_tile(g.M, 1)};
-            GemmDownDgradArgs c1{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, nullptr,
-                                 (const uint16_t*)w->s_down, g.H, g.I, (const uint16_t*)saved->sg,
-                                 (const uint16_t*)saved->su, t0, sdgu, shw, nullptr, g.P};
-            if (launch_gemm_down_dgrad(c1, st)) return MOE_ERR_HIP;
-            GemmGuDgradArgs c2{dense, sdgu, (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up,
-                               g.H, g.I, sdx};
-            if (launch_gemm_gu_dgrad(c2, st)) return MOE_ERR_HIP;
             WgradDownArgs c3{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, shw, g.H, g.I,
                              {(uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), mode}};
             if (launch_wgrad_down(c3, st)) return MOE_ERR_HIP;
@@ -651,15 +671,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                                {(uint16_t*)gr->d_s_gate, P.wacc(L.wacc_sg), mode},
                                {(uint16_t*)gr->d_s_up, P.wacc(L.wacc_su), mode}};
             if (launch_wgrad_gate_up(c4, st)) return MOE_ERR_HIP;
-            sh_dx = sdx;
         }
-        // reverse-dispatch: dx_t = [shared] + sum_j dXd[row(t, j)]
-        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
-                             dx, err, st))
-            return MOE_ERR_HIP;
-        if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
-                               t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
-            return MOE_ERR_HIP;
     }
     return MOE_OK;
 }

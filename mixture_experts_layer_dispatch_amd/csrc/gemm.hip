@@ -250,7 +250,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
 // rows (one K step, the common case for small token counts) the A tile stays
 // in LDS for all of them and the next B tile is fetched while the current one
 // is multiplied; otherwise each column tile runs the K loop.
-template <bool BF16_ONLY, class SA, class SB>
+template <bool BF16_ONLY, bool STREAM, class SA, class SB>
 __device__ __forceinline__ void wgrad_tiles_(LoadKS<W_TM, SA>& la, LoadKS<W_TN, SB>& lb, int nk,
                                              int nt0, int ntn, int nstride, uint16_t* smem,
                                              const WgradEpi& epi) {
@@ -277,7 +277,7 @@ __device__ __forceinline__ void wgrad_tiles_(LoadKS<W_TM, SA>& la, LoadKS<W_TN, 
                 mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
                 __syncthreads();
             }
-            epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, sB);
+            epi.template store<BF16_ONLY, STREAM>(nt0 + i * nstride, acc, sB);
         }
         return;
     }
@@ -293,7 +293,7 @@ __device__ __forceinline__ void wgrad_tiles_(LoadKS<W_TM, SA>& la, LoadKS<W_TN, 
             mma_tile<W_TM, W_TN, true, true>(sA, sB, wm0, wn0, acc);
             __syncthreads();
         }
-        epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, sB);
+        epi.template store<BF16_ONLY, STREAM>(nt0 + i * nstride, acc, sB);
         __syncthreads();
     }
 }
@@ -303,8 +303,9 @@ __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, S
                                             int ntiles, int g, int ng, uint16_t* smem,
                                             const WgradEpi& epi) {
     const int ntn = wgrad_group_tiles(ntiles, ng, g);
-    if (epi.out.mode == 0) wgrad_tiles_<true>(la, lb, nk, g, ntn, ng, smem, epi);
-    else wgrad_tiles_<false>(la, lb, nk, g, ntn, ng, smem, epi);
+    if (epi.out.mode != 0) wgrad_tiles_<false, false>(la, lb, nk, g, ntn, ng, smem, epi);
+    else if (ng > 1) wgrad_tiles_<true, true>(la, lb, nk, g, ntn, ng, smem, epi);
+    else wgrad_tiles_<true, false>(la, lb, nk, g, ntn, ng, smem, epi);
 }
 
 // dW_down[e][h, i] = sum over e's rows r of dy[tok(r), h] * hw[r, i].

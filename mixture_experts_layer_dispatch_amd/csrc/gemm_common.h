@@ -503,6 +503,8 @@ __device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, cons
     else *(uint2*)(o.out + idx) = pack4(x0, x1, x2, x3);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
 struct WgradEpi {
     WgradOut out;
     int64_t ebase;   // first element of the expert's matrix
@@ -512,8 +514,13 @@ struct WgradEpi {
     // whole 128-byte row segments; the fp32 accumulation modes store directly.
     // BF16_ONLY: the caller has checked mode == 0, so the stores are
     // unconditional and the compiler can count them in its memory waits.
-    template <bool BF16_ONLY>
-    __device__ void store(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32], uint16_t* stage) const {
+    // STREAM: streaming (non-temporal) bf16 stores, for slabs whose column
+    // tiles are dealt over several blocks: measured faster there (the gradient
+    // is not read again by this layer), slower for a slab one block writes
+    // alone.
+    template <bool BF16_ONLY, bool STREAM = false>
+    __device__ __forceinline__ void store(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32],
+                                          uint16_t* stage) const {
         AccPos<W_TM, W_TN> pos;
         const int n0 = nt * W_TN;
         if (!BF16_ONLY && out.mode != 0) {
@@ -533,6 +540,16 @@ struct WgradEpi {
             }
         __syncthreads();
         constexpr int CPR = W_TN / 8;                  // 16-byte chunks per row
+        if constexpr (STREAM) {
+#pragma unroll
+            for (int q = 0; q < W_TM * CPR / 256; ++q) {
+                const int c = threadIdx.x + 256 * q;
+                const int r = c / CPR, cc = c % CPR;
+                __builtin_nontemporal_store(*(const u32x4*)(stage + r * W_SP + cc * 8),
+                                            (u32x4*)(out.out + ebase + (int64_t)(m0 + r) * ld + n0 + cc * 8));
+            }
+            return;
+        }
 #pragma unroll
         for (int q = 0; q < W_TM * CPR / 256; ++q) {
             const int c = threadIdx.x + 256 * q;
@@ -541,8 +558,8 @@ struct WgradEpi {
                 *(const uint4*)(stage + r * W_SP + cc * 8);
         }
     }
-    __device__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32],
-                               uint16_t* stage) const {
+    __device__ __forceinline__ void operator()(int nt, const f32x4 (&acc)[W_TM / 32][W_TN / 32],
+                                               uint16_t* stage) const {
         store<false>(nt, acc, stage);
     }
 };

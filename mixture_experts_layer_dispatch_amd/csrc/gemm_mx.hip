@@ -593,7 +593,7 @@ constexpr int X_SMEM = X_REG + (X_TM * W_SP > X_TN * X_P ? X_TM * W_SP : X_TN * 
 
 // The column-tile walk of one weight-gradient block (A: 128 rows, B: the
 // current 64-row column tile).
-template <bool BF16_ONLY>
+template <bool BF16_ONLY, bool STREAM>
 __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPad<X_TM>& sa,
                                                LoadKCPad<X_TN>& lb, LoadScalesPad<X_TN>& sb,
                                                int nk, int nt0, int ntn, int nstride, uint16_t* smem,
@@ -631,7 +631,7 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
                 mma_tile_mx_at<X_TM, X_TN>(smem, region, cA, cB, wm0, wn0, acc);
                 __syncthreads();                       // the MFMAs are done with the B tile
             }
-            epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, region);
+            epi.template store<BF16_ONLY, STREAM>(nt0 + i * nstride, acc, region);
         }
         return;
     }
@@ -653,10 +653,14 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
             mma_tile_mx_at<X_TM, X_TN>(smem, region, cA, cB, wm0, wn0, acc);
         }
         __syncthreads();                               // the MFMAs are done with the B tile
-        epi.template store<BF16_ONLY>(nt0 + i * nstride, acc, region);
+        epi.template store<BF16_ONLY, STREAM>(nt0 + i * nstride, acc, region);
     }
 }
 
+// STREAM: the slabs' column tiles are dealt over several blocks (streaming
+// bf16 stores); a template parameter of the kernel, so that each kernel holds
+// two instantiations of the tile walk.
+template <bool STREAM>
 __global__ __launch_bounds__(256, 4) void k_wgrad_mx(WgradMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[X_SMEM];
     const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
@@ -702,8 +706,8 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_mx(WgradMXArgs a) {
     RowsPadK rb{bq, kcodes, nt0 * X_TN, 0};
     LoadKCPad<X_TN> lb(rb, kcodes);
     LoadScalesPad<X_TN> sb(bs, kcodes / 32, nt0 * X_TN, 0, kcodes / 32);
-    if (epi.out.mode == 0) wgrad_mx_tiles<true>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
-    else wgrad_mx_tiles<false>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
+    if (epi.out.mode == 0) wgrad_mx_tiles<true, STREAM>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
+    else wgrad_mx_tiles<false, false>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
 }
 
 // ---------------------------------------------------------------- deep groups
@@ -800,7 +804,8 @@ int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
     const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
     const int grid = (a.g.blk_off ? a.g.E : 1) * (a.M / X_TM) * nng;
     if (grid <= 0) return 0;
-    k_wgrad_mx<<<grid, 256, 0, st>>>(a);
+    if (nng > 1) k_wgrad_mx<true><<<grid, 256, 0, st>>>(a);
+    else k_wgrad_mx<false><<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
