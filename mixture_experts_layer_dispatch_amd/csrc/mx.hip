@@ -3,6 +3,8 @@
 // quantised outside the timed region), and the dispatch gather with the
 // activation quantisation fused in (arex-research.com "Cursor 放出 MoK",
 // design section, closing paragraph).
+#include <type_traits>
+
 #include "launch.h"
 #include "mx.h"
 #include "profile.h"
@@ -172,14 +174,22 @@ __device__ __forceinline__ bool map_pad_block(const PadGroups& g, int C, int b, 
     return o.nv > 0;
 }
 
-// The block's 32 source rows are resolved once (threads 0..31 look up their
-// slots and weights) and shared through LDS, so that each thread's 32 loads
-// are independent and in flight together.
+// A block quantises one 32-row block of a group over 256 columns.  Its 32
+// source rows are resolved once (threads 0..31 look up their slots and
+// weights); the 32 x 256 tile is then read row-wise in 16-byte pieces into
+// LDS, and each thread takes one column of it: 32 values, one scale, 32 codes.
+constexpr int QT_COLS = 256;
+
+template <bool F32>            // fp32 source rows (src.kind == 1), else bf16
 __global__ __launch_bounds__(256) void k_mx_quant_group_t(PadGroups g, QtSrc src, int C,
                                                           uint8_t* __restrict__ codes,
                                                           uint8_t* __restrict__ scales) {
+    using T = typename std::conditional<F32, float, uint16_t>::type;
+    constexpr int EPC = 16 / sizeof(T);               // elements per 16-byte piece
+    constexpr int PPR = QT_COLS / EPC;                // pieces per row
     __shared__ int64_t roff[32];      // element offset of row q in the source; -1: a zero row
     __shared__ float rwt[32];         // the row's factor (the slot's weight for w * dy, else 1)
+    __shared__ __attribute__((aligned(16))) T tile[32 * QT_COLS];
     PadBlock pb;
     if (!map_pad_block(g, C, blockIdx.y, pb)) return;         // the same for the whole block
     if (threadIdx.x < 32) {
@@ -205,15 +215,32 @@ __global__ __launch_bounds__(256) void k_mx_quant_group_t(PadGroups g, QtSrc src
         rwt[q] = wt;
     }
     __syncthreads();
-    const int c = blockIdx.x * 256 + threadIdx.x;
+    const int c0 = blockIdx.x * QT_COLS;
+    const T* base;
+    if constexpr (F32) base = src.f32;
+    else base = src.b16;
+    uint4 piece[32 * PPR / 256];
+#pragma unroll
+    for (int i = 0; i < 32 * PPR / 256; ++i) {
+        const int idx = threadIdx.x + 256 * i, q = idx / PPR, col = c0 + (idx % PPR) * EPC;
+        const int64_t o = roff[q];
+        piece[i] = (o >= 0 && col < C) ? *(const uint4*)(base + o + col) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 32 * PPR / 256; ++i) {
+        const int idx = threadIdx.x + 256 * i;
+        *(uint4*)(tile + (idx / PPR) * QT_COLS + (idx % PPR) * EPC) = piece[i];
+    }
+    __syncthreads();
+    const int c = c0 + threadIdx.x;
     if (c >= C) return;
     float v[32];
     float amax = 0.f;
 #pragma unroll
     for (int q = 0; q < 32; ++q) {
-        const int64_t o = roff[q];
-        float x = 0.f;
-        if (o >= 0) x = src.kind == 1 ? src.f32[o + c] : bf2f(src.b16[o + c]) * rwt[q];
+        float x;
+        if constexpr (F32) x = tile[q * QT_COLS + threadIdx.x];
+        else x = bf2f(tile[q * QT_COLS + threadIdx.x]) * rwt[q];
         v[q] = x;
         amax = fmaxf(amax, fabsf(x));
     }
@@ -269,8 +296,9 @@ int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, void* c
         nblk = (int)(bound < g.rows ? bound : g.rows);
     }
     if (nblk <= 0) return 0;
-    dim3 grid((C + 255) / 256, nblk);
-    k_mx_quant_group_t<<<grid, 256, 0, st>>>(g, src, C, (uint8_t*)codes, (uint8_t*)scales);
+    dim3 grid((C + QT_COLS - 1) / QT_COLS, nblk);
+    if (src.kind == 1) k_mx_quant_group_t<true><<<grid, 256, 0, st>>>(g, src, C, (uint8_t*)codes, (uint8_t*)scales);
+    else k_mx_quant_group_t<false><<<grid, 256, 0, st>>>(g, src, C, (uint8_t*)codes, (uint8_t*)scales);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
