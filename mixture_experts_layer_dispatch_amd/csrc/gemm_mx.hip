@@ -85,6 +85,62 @@ struct LoadScales {
     }
 };
 
+// Rows of two matrices joined along K: K steps [0, nk1) come from the first,
+// the rest from the second (the same rows of each).
+template <int ROWS>
+struct LoadKCCat {
+    static constexpr int PER = ROWS * (kTK / 8) / 256;
+    const uint16_t* p0[PER];
+    const uint16_t* p1[PER];
+    int off[PER];
+    int nk1;
+    uint4 v[PER];
+    __device__ LoadKCCat(const RowsDirect& s0, const RowsDirect& s1, int n1) : nk1(n1) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int c = threadIdx.x + 256 * q;
+            const int r = c >> 3, kc = c & 7;
+            const uint16_t* b0 = s0.row(r);
+            const uint16_t* b1 = s1.row(r);
+            p0[q] = b0 ? b0 + kc * 8 : nullptr;
+            p1[q] = b1 ? b1 + kc * 8 : nullptr;
+            off[q] = kc_off(r, kc * 16);
+        }
+    }
+    __device__ void load(int kt) {
+        const bool second = kt >= nk1;
+        const int64_t k = (int64_t)(second ? kt - nk1 : kt) * kTK;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const uint16_t* pb = global_select(second, p0[q], p1[q]);
+            v[q] = pb ? *(const uint4*)(pb + k) : make_uint4(0, 0, 0, 0);
+        }
+    }
+    __device__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) *(uint4*)(s + off[q]) = v[q];
+    }
+};
+
+template <int ROWS>
+struct LoadScalesCat {         // K-step-major scales of two matrices joined along K
+    const uint32_t* p0;
+    const uint32_t* p1;
+    int kst, nk1;
+    uint32_t v;
+    __device__ LoadScalesCat(const ScalesKMajor& s0, const ScalesKMajor& s1, int n1)
+        : p0(threadIdx.x < ROWS ? s0.row(threadIdx.x) : nullptr),
+          p1(threadIdx.x < ROWS ? s1.row(threadIdx.x) : nullptr), kst(s0.kstride()), nk1(n1), v(0) {}
+    __device__ void load(int kt) {
+        const bool second = kt >= nk1;
+        const uint32_t* pb = global_select(second, p0, p1);
+        v = pb ? pb[(int64_t)(second ? kt - nk1 : kt) * kst] : 0u;
+    }
+    __device__ void store(uint32_t* s) const {
+        if (threadIdx.x < ROWS) s[threadIdx.x] = v;
+    }
+};
+
 // ================================================================ tiles
 template <int TM, int TN>
 struct SmemMX {
@@ -462,7 +518,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
 
 // ================================================================ backward: gate/up dgrad
 // dX = Q(dg) Q(W_gate) + Q(du) Q(W_up), reductions over I, against the
-// transposed pre-quantised weights; two K phases accumulate into one tile.
+// transposed pre-quantised weights, in one K loop: the W_gate^T steps, then
+// the W_up^T steps.
 constexpr int M4_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
 
 template <int TM>
@@ -474,20 +531,19 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a
     const int n0 = nt * M4_TN;
     const int H = a.H, I = a.I;
     f32x4 acc[TM / 32][4];
-#pragma unroll
-    for (int ph = 0; ph < 2; ++ph) {
-        const uint8_t* wq = ph ? a.wut_q : a.wgt_q;
-        const uint8_t* ws = ph ? a.wut_s : a.wgt_s;
-        RowsDirect da{(const uint16_t*)(a.dgu_q + ph * I), I, lo, hi - lo};
-        ScalesDirect dsa{(const uint32_t*)(a.dgu_s + ph * (I / 32)), I / 64, lo, hi - lo};
-        RowsDirect db{(const uint16_t*)(wq + (int64_t)e * H * I), I / 2, n0, M4_TN};
-        ScalesKMajor dsb{(const uint32_t*)(ws + (int64_t)e * H * (I / 32)), H, n0, M4_TN};
-        LoadKC<TM, RowsDirect> la(da);
-        LoadKC<M4_TN, RowsDirect> lb(db);
-        LoadScales<TM, ScalesDirect> sa(dsa);
-        LoadScales<M4_TN, ScalesKMajor> sb(dsb);
-        mainloop_mx<TM, M4_TN>(la, lb, sa, sb, I / 128, smem, acc, ph == 1);
-    }
+    // one K loop over [dg | du] (2I codes per row) against W_gate^T then W_up^T
+    RowsDirect da{(const uint16_t*)a.dgu_q, I, lo, hi - lo};
+    ScalesDirect dsa{(const uint32_t*)a.dgu_s, I / 64, lo, hi - lo};
+    const int64_t wo = (int64_t)e * H * I;
+    RowsDirect dbg{(const uint16_t*)(a.wgt_q + wo), I / 2, n0, M4_TN};
+    RowsDirect dbu{(const uint16_t*)(a.wut_q + wo), I / 2, n0, M4_TN};
+    ScalesKMajor dsg{(const uint32_t*)(a.wgt_s + wo / 32), H, n0, M4_TN};
+    ScalesKMajor dsu{(const uint32_t*)(a.wut_s + wo / 32), H, n0, M4_TN};
+    LoadKC<TM, RowsDirect> la(da);
+    LoadKCCat<M4_TN> lb(dbg, dbu, I / 128);
+    LoadScales<TM, ScalesDirect> sa(dsa);
+    LoadScalesCat<M4_TN> sb(dsg, dsu, I / 128);
+    mainloop_mx<TM, M4_TN>(la, lb, sa, sb, 2 * I / 128, smem, acc);
     AccPos<TM, M4_TN> pos;
 #pragma unroll
     for (int mb = 0; mb < TM / 32; ++mb) {
