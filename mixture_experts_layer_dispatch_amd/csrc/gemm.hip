@@ -91,33 +91,39 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
 }
 
 // ================================================================ forward GEMM 2
-// o = h W_down^T.  Tile TM rows x 128 columns of H.
+// o = h W_down^T.  Tile TM rows x 128 columns of H; with 128-row tiles a
+// block takes two neighbouring column tiles in one K loop (K = I is short).
 constexpr int G2_TN = 128;
 
 template <int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<TM, G2_TN, false, false>::STAGE];
-    int e, lo, hi, nt;
-    if (!map_mtile<TM>(a.g, a.H / G2_TN, blockIdx.x, e, lo, hi, nt)) return;
-    const int n0 = nt * G2_TN;
+    constexpr int NT = down_tiles_per_block<TM>();
+    const int ncol = a.H / G2_TN;
+    int e, lo, hi, np;
+    if (!map_mtile<TM>(a.g, (ncol + NT - 1) / NT, blockIdx.x, e, lo, hi, np)) return;
+    const int n0 = NT * np * G2_TN;
+    const int ntl = min(NT, ncol - NT * np);
     f32x4 acc[TM / 32][4];
     RowsDirect sa{a.h, a.I, lo, hi - lo};
     LoadKC<TM, RowsDirect> la(sa);
     RowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, G2_TN};
     LoadKC<G2_TN, RowsDirect> lb(sb);
-    mainloop<TM, G2_TN, false, false>(la, lb, a.I / kTK, smem, acc);
     AccPos<TM, G2_TN> pos;
+    auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
-    for (int mb = 0; mb < TM / 32; ++mb) {
-        const int rl = lo + pos.m(mb);
-        if (rl >= hi) continue;
+        for (int mb = 0; mb < TM / 32; ++mb) {
+            const int rl = lo + pos.m(mb);
+            if (rl >= hi) continue;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int c = n0 + pos.n(nb);
-            const f32x4 v = acc[mb][nb];
-            *(uint2*)(a.o + (int64_t)rl * a.H + c) = pack4(v[0], v[1], v[2], v[3]);
+            for (int nb = 0; nb < 4; ++nb) {
+                const int col = n0 + t * G2_TN + pos.n(nb);
+                const f32x4 v = c[mb][nb];
+                *(uint2*)(a.o + (int64_t)rl * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
+            }
         }
-    }
+    };
+    mainloop_kc_tiles<TM, G2_TN>(la, lb, a.I / kTK, ntl, (int64_t)G2_TN * a.I, smem, acc, epi);
 }
 
 // ================================================================ backward: down dgrad
@@ -476,6 +482,17 @@ static inline int row_tile(const GroupRows& g) { return g.tm == 128 ? 128 : 64; 
         return hipGetLastError() == hipSuccess ? 0 : -1;                           \
     } while (0)
 
+// the same with the column-tile count depending on the row tile
+#define MOE_LAUNCH_TM2(KERNEL, NCOL64, NCOL128)                                    \
+    do {                                                                           \
+        const int tm_ = row_tile(a.g);                                             \
+        const int grid_ = mgroup_grid(a.g, tm_) * (tm_ == 128 ? (NCOL128) : (NCOL64)); \
+        if (grid_ <= 0) return 0;                                                  \
+        if (tm_ == 128) KERNEL<128><<<grid_, 256, 0, st>>>(a);                     \
+        else KERNEL<64><<<grid_, 256, 0, st>>>(a);                                 \
+        return hipGetLastError() == hipSuccess ? 0 : -1;                           \
+    } while (0)
+
 int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gate_up");
     MOE_LAUNCH_TM(k_gemm_gate_up, a.I / 64);
@@ -483,7 +500,9 @@ int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
 
 int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down");
-    MOE_LAUNCH_TM(k_gemm_down, a.H / G2_TN);
+    const int ncol = a.H / G2_TN;
+    MOE_LAUNCH_TM2(k_gemm_down, (ncol + down_tiles_per_block<64>() - 1) / down_tiles_per_block<64>(),
+                   (ncol + down_tiles_per_block<128>() - 1) / down_tiles_per_block<128>());
 }
 
 int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st) {

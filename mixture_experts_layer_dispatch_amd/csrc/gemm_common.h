@@ -166,10 +166,12 @@ struct LoadKC {
             off[q] = kc_off(r, kc * 16);
         }
     }
-    __device__ void load(int kt) {
+    __device__ void load(int kt) { load_off(kt, 0); }
+    // K step kt of the rows `extra` elements further (a later column tile)
+    __device__ void load_off(int kt, int64_t extra) {
 #pragma unroll
         for (int q = 0; q < PER; ++q)
-            v[q] = p[q] ? *(const uint4*)(p[q] + (int64_t)kt * kTK) : make_uint4(0, 0, 0, 0);
+            v[q] = p[q] ? *(const uint4*)(p[q] + extra + (int64_t)kt * kTK) : make_uint4(0, 0, 0, 0);
     }
     __device__ void store(uint16_t* s) const {
 #pragma unroll
@@ -354,6 +356,58 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
         }
         __syncthreads();
     }
+}
+
+// Column tiles per block of the down projection: two with 128-row tiles (large
+// groups, where the GEMM is MFMA work and a short K loop's pipeline fill
+// shows), one with 64-row tiles (small groups stream weights: more blocks in
+// flight measured faster).
+template <int TM>
+constexpr int down_tiles_per_block() { return TM == 128 ? 2 : 1; }
+
+// One or two column tiles of one row tile (KC operands) in a single K loop:
+// steps [0, nk) for tile 0 and [nk, 2 nk) for tile 1, whose B rows lie
+// bstride elements further.  The loads of tile 1's first step are in flight
+// while tile 0's epilogue, epi(0, acc), stores its outputs, so a short K loop
+// does not pay the pipeline fill once per tile.
+template <int TM, int TN, class LA, class LB, class EPI>
+__device__ __forceinline__ void mainloop_kc_tiles(LA& la, LB& lb, int nk, int ntl, int64_t bstride,
+                                                  uint16_t* smem, f32x4 (&acc)[TM / 32][TN / 32],
+                                                  const EPI& epi) {
+    using SM = Smem<TM, TN, false, false>;
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
+    zero_acc<TM, TN>(acc);
+    if (nk <= 0) return;
+    uint16_t* buf0 = smem;
+    uint16_t* buf1 = smem + SM::STAGE;
+    la.load(0);
+    lb.load_off(0, 0);
+    la.store(buf0);
+    lb.store(buf0 + SM::A);
+    __syncthreads();
+    const int steps = nk * ntl;
+    for (int s = 0; s < steps; ++s) {
+        uint16_t* cur = (s & 1) ? buf1 : buf0;
+        uint16_t* nxt = (s & 1) ? buf0 : buf1;
+        const bool more = s + 1 < steps;
+        if (more) {
+            const int t1 = s + 1 >= nk ? 1 : 0;
+            la.load(s + 1 - t1 * nk);
+            lb.load_off(s + 1 - t1 * nk, t1 ? bstride : 0);
+        }
+        mma_tile<TM, TN, false, false>(cur, cur + SM::A, wm0, wn0, acc);
+        if (more) {
+            la.store(nxt);
+            lb.store(nxt + SM::A);
+        }
+        if (s == nk - 1 && more) {
+            epi(0, acc);
+            zero_acc<TM, TN>(acc);
+        }
+        __syncthreads();
+    }
+    epi(ntl - 1, acc);
 }
 
 // The same K loop for KS operands whose rows may be gathered: index loads run

@@ -79,7 +79,8 @@ struct LoadScales {
         v = 0;
         kst = s.kstride();
     }
-    __device__ void load(int kt) { v = p ? p[(int64_t)kt * kst] : 0u; }
+    __device__ void load(int kt) { load_off(kt, 0); }
+    __device__ void load_off(int kt, int64_t extra) { v = p ? p[extra + (int64_t)kt * kst] : 0u; }
     __device__ void store(uint32_t* s) const {
         if (threadIdx.x < ROWS) s[threadIdx.x] = v;
     }
@@ -290,6 +291,53 @@ __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int 
     }
 }
 
+// One or two column tiles of one row tile in a single K loop (as
+// mainloop_kc_tiles): tile 1's B codes lie bstride uint16 further, its B
+// scales bstride_s words further.
+template <int TM, int TN, class LA, class LB, class SA, class SB, class EPI>
+__device__ __forceinline__ void mainloop_mx_tiles(LA& la, LB& lb, SA& sa, SB& sb, int nk, int ntl,
+                                                  int64_t bstride, int64_t bstride_s, uint16_t* smem,
+                                                  f32x4 (&acc)[TM / 32][TN / 32], const EPI& epi) {
+    using SM = SmemMX<TM, TN>;
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
+    zero_acc<TM, TN>(acc);
+    if (nk <= 0) return;
+    auto put = [&](uint16_t* st) {
+        la.store(st);
+        lb.store(st + SM::A);
+        sa.store((uint32_t*)(st + SM::A + SM::B));
+        sb.store((uint32_t*)(st + SM::A + SM::B) + TM);
+    };
+    auto get = [&](int s) {
+        const int t = s >= nk ? 1 : 0, kt = s - t * nk;
+        la.load(kt);
+        lb.load_off(kt, t ? bstride : 0);
+        sa.load(kt);
+        sb.load_off(kt, t ? bstride_s : 0);
+    };
+    uint16_t* buf0 = smem;
+    uint16_t* buf1 = smem + SM::STAGE;
+    get(0);
+    put(buf0);
+    __syncthreads();
+    const int steps = nk * ntl;
+    for (int s = 0; s < steps; ++s) {
+        uint16_t* cur = (s & 1) ? buf1 : buf0;
+        uint16_t* nxt = (s & 1) ? buf0 : buf1;
+        const bool more = s + 1 < steps;
+        if (more) get(s + 1);
+        mma_tile_mx<TM, TN>(cur, wm0, wn0, acc);
+        if (more) put(nxt);
+        if (s == nk - 1 && more) {
+            epi(0, acc);
+            zero_acc<TM, TN>(acc);
+        }
+        __syncthreads();
+    }
+    epi(ntl - 1, acc);
+}
+
 // ================================================================ gate/up + SwiGLU
 // Like the bf16 kernel; in addition h = SiLU(g) * u, from the fp32
 // accumulators, is quantised along I: each wave holds exactly one 32-wide
@@ -357,15 +405,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
 }
 
 // ================================================================ down projection
+// With 128-row tiles, two neighbouring column tiles per block in one K loop
+// (K = I is short).
 constexpr int M2_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
 
 template <int TM>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M2_TN>::STAGE];
-    int e, lo, hi, nt;
-    if (!map_mtile<TM>(a.g, a.H / M2_TN, blockIdx.x, e, lo, hi, nt)) return;
-    const int n0 = nt * M2_TN;
+    constexpr int NT = down_tiles_per_block<TM>();
+    const int ncol = a.H / M2_TN;
+    int e, lo, hi, np;
+    if (!map_mtile<TM>(a.g, (ncol + NT - 1) / NT, blockIdx.x, e, lo, hi, np)) return;
+    const int n0 = NT * np * M2_TN;
+    const int ntl = min(NT, ncol - NT * np);
     const int H = a.H, I = a.I;
     f32x4 acc[TM / 32][4];
     RowsDirect da{(const uint16_t*)a.h_q, I / 2, lo, hi - lo};
@@ -376,19 +429,22 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     LoadKC<M2_TN, RowsDirect> lb(db);
     LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScales<M2_TN, ScalesKMajor> sb(dsb);
-    mainloop_mx<TM, M2_TN>(la, lb, sa, sb, I / 128, smem, acc);
     AccPos<TM, M2_TN> pos;
+    auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
-    for (int mb = 0; mb < TM / 32; ++mb) {
-        const int rl = lo + pos.m(mb);
-        if (rl >= hi) continue;
+        for (int mb = 0; mb < TM / 32; ++mb) {
+            const int rl = lo + pos.m(mb);
+            if (rl >= hi) continue;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int c = n0 + pos.n(nb);
-            const f32x4 v = acc[mb][nb];
-            *(uint2*)(a.o + (int64_t)rl * H + c) = pack4(v[0], v[1], v[2], v[3]);
+            for (int nb = 0; nb < 4; ++nb) {
+                const int col = n0 + t * M2_TN + pos.n(nb);
+                const f32x4 v = c[mb][nb];
+                *(uint2*)(a.o + (int64_t)rl * H + col) = pack4(v[0], v[1], v[2], v[3]);
+            }
         }
-    }
+    };
+    mainloop_mx_tiles<TM, M2_TN>(la, lb, sa, sb, I / 128, ntl, (int64_t)M2_TN * (I / 2), M2_TN, smem,
+                                 acc, epi);
 }
 
 
@@ -838,7 +894,14 @@ int launch_gemm_gate_up_mx(const GemmGateUpMXArgs& a, hipStream_t st) {
 
 int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down_mx");
-    MOE_LAUNCH_TM_MX(k_gemm_down_mx, a.H / M2_TN);
+    const int ncol = a.H / M2_TN;
+    const int tm_ = a.g.tm == 128 ? 128 : 64;
+    const int nt_ = tm_ == 128 ? down_tiles_per_block<128>() : down_tiles_per_block<64>();
+    const int grid_ = mgroup_grid_mx(a.g, tm_) * ((ncol + nt_ - 1) / nt_);
+    if (grid_ <= 0) return 0;
+    if (tm_ == 128) k_gemm_down_mx<128><<<grid_, 256, 0, st>>>(a);
+    else k_gemm_down_mx<64><<<grid_, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_gemm_down_dgrad_mx(const GemmDownDgradMXArgs& a, hipStream_t st) {
