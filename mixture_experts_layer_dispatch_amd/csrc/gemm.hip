@@ -98,7 +98,7 @@ constexpr int G2_TN = 128;
 template <int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<TM, G2_TN, false, false>::STAGE];
-    constexpr int NT = down_tiles_per_block<TM>();
+    constexpr int NT = short_k_tiles_per_block<TM>();
     const int ncol = a.H / G2_TN;
     int e, lo, hi, np;
     if (!map_mtile<TM>(a.g, (ncol + NT - 1) / NT, blockIdx.x, e, lo, hi, np)) return;
@@ -123,7 +123,12 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
             }
         }
     };
-    mainloop_kc_tiles<TM, G2_TN>(la, lb, a.I / kTK, ntl, (int64_t)G2_TN * a.I, smem, acc, epi);
+    if constexpr (NT == 1) {
+        mainloop<TM, G2_TN, false, false>(la, lb, a.I / kTK, smem, acc);
+        epi(0, acc);
+    } else {
+        mainloop_tiles<TM, G2_TN, false, false>(la, lb, a.I / kTK, ntl, (int64_t)G2_TN * a.I, smem, acc, epi);
+    }
 }
 
 // ================================================================ backward: down dgrad
@@ -219,32 +224,43 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a)
 
 // ================================================================ backward: gate/up dgrad
 // dX = dg W_gate + du W_up: A = [dg | du] rows (K = 2I), B = [W_gate; W_up]
-// read with k as the memory row.  Tile TM rows x 128 columns of H.
+// read with k as the memory row.  Tile TM rows x 128 columns of H; with
+// 128-row tiles a block takes two neighbouring column tiles in one K loop.
 constexpr int G4_TN = 128;
 
 template <int TM>
 __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<TM, G4_TN, false, true>::STAGE];
-    int e, lo, hi, nt;
-    if (!map_mtile<TM>(a.g, a.H / G4_TN, blockIdx.x, e, lo, hi, nt)) return;
-    const int n0 = nt * G4_TN;
+    constexpr int NT = short_k_tiles_per_block<TM>();
+    const int ncol = a.H / G4_TN;
+    int e, lo, hi, np;
+    if (!map_mtile<TM>(a.g, (ncol + NT - 1) / NT, blockIdx.x, e, lo, hi, np)) return;
+    const int n0 = NT * np * G4_TN;
+    const int ntl = min(NT, ncol - NT * np);
     f32x4 acc[TM / 32][4];
     RowsDirect sa{a.dgu, 2 * a.I, lo, hi - lo};
     LoadKC<TM, RowsDirect> la(sa);
     KRowsGateUp sb{a.w_gate + (int64_t)e * a.I * a.H, a.w_up + (int64_t)e * a.I * a.H, a.H, n0, a.I};
     LoadKS<G4_TN, KRowsGateUp> lb(sb);
-    mainloop<TM, G4_TN, false, true>(la, lb, 2 * a.I / kTK, smem, acc);
     AccPos<TM, G4_TN> pos;
+    auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
-    for (int mb = 0; mb < TM / 32; ++mb) {
-        const int rl = lo + pos.m(mb);
-        if (rl >= hi) continue;
+        for (int mb = 0; mb < TM / 32; ++mb) {
+            const int rl = lo + pos.m(mb);
+            if (rl >= hi) continue;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int c = n0 + pos.n(nb);
-            const f32x4 v = acc[mb][nb];
-            *(uint2*)(a.dx + (int64_t)rl * a.H + c) = pack4(v[0], v[1], v[2], v[3]);
+            for (int nb = 0; nb < 4; ++nb) {
+                const int col = n0 + t * G4_TN + pos.n(nb);
+                const f32x4 v = c[mb][nb];
+                *(uint2*)(a.dx + (int64_t)rl * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
+            }
         }
+    };
+    if constexpr (NT == 1) {
+        mainloop<TM, G4_TN, false, true>(la, lb, 2 * a.I / kTK, smem, acc);
+        epi(0, acc);
+    } else {
+        mainloop_tiles<TM, G4_TN, false, true>(la, lb, 2 * a.I / kTK, ntl, G4_TN, smem, acc, epi);
     }
 }
 
@@ -501,8 +517,8 @@ int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
 int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down");
     const int ncol = a.H / G2_TN;
-    MOE_LAUNCH_TM2(k_gemm_down, (ncol + down_tiles_per_block<64>() - 1) / down_tiles_per_block<64>(),
-                   (ncol + down_tiles_per_block<128>() - 1) / down_tiles_per_block<128>());
+    MOE_LAUNCH_TM2(k_gemm_down, (ncol + short_k_tiles_per_block<64>() - 1) / short_k_tiles_per_block<64>(),
+                   (ncol + short_k_tiles_per_block<128>() - 1) / short_k_tiles_per_block<128>());
 }
 
 int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st) {
@@ -512,7 +528,9 @@ int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st) {
 
 int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gu_dgrad");
-    MOE_LAUNCH_TM(k_gemm_gu_dgrad, a.H / G4_TN);
+    const int ncol = a.H / G4_TN;
+    MOE_LAUNCH_TM2(k_gemm_gu_dgrad, (ncol + short_k_tiles_per_block<64>() - 1) / short_k_tiles_per_block<64>(),
+                   (ncol + short_k_tiles_per_block<128>() - 1) / short_k_tiles_per_block<128>());
 }
 
 int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {

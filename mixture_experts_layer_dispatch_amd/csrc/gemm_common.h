@@ -197,14 +197,16 @@ struct LoadKS {
             cc[q] = c % CPR;
         }
     }
-    __device__ void load(int kt) {
+    __device__ void load(int kt) { load_off(kt, 0); }
+    // K step kt of the columns `extra` elements further (a later column tile)
+    __device__ void load_off(int kt, int64_t extra) {
         int pr[PER];
 #pragma unroll
         for (int q = 0; q < PER; ++q) pr[q] = src.pre(kt * kTK + kr[q]);
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const uint16_t* a = src.at(kt * kTK + kr[q], pr[q]);
-            v[q] = a ? *(const uint4*)(a + cc[q] * 8) : make_uint4(0, 0, 0, 0);
+            v[q] = a ? *(const uint4*)(a + extra + cc[q] * 8) : make_uint4(0, 0, 0, 0);
         }
     }
     __device__ void store(uint16_t* s) const {
@@ -358,23 +360,24 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
     }
 }
 
-// Column tiles per block of the down projection: two with 128-row tiles (large
-// groups, where the GEMM is MFMA work and a short K loop's pipeline fill
-// shows), one with 64-row tiles (small groups stream weights: more blocks in
-// flight measured faster).
+// Column tiles per block of the GEMMs with a short K loop (down projection,
+// gate/up input gradient): two with 128-row tiles (large groups, where the
+// GEMM is MFMA work and the pipeline fill of a short K loop shows), one with
+// 64-row tiles (small groups stream weights: more blocks in flight measured
+// faster).
 template <int TM>
-constexpr int down_tiles_per_block() { return TM == 128 ? 2 : 1; }
+constexpr int short_k_tiles_per_block() { return TM == 128 ? 2 : 1; }
 
-// One or two column tiles of one row tile (KC operands) in a single K loop:
-// steps [0, nk) for tile 0 and [nk, 2 nk) for tile 1, whose B rows lie
-// bstride elements further.  The loads of tile 1's first step are in flight
+// One or two column tiles of one row tile in a single K loop: steps [0, nk)
+// for tile 0 and [nk, 2 nk) for tile 1, whose B operand lies bstride elements
+// further.  The loads of tile 1's first step are in flight
 // while tile 0's epilogue, epi(0, acc), stores its outputs, so a short K loop
 // does not pay the pipeline fill once per tile.
-template <int TM, int TN, class LA, class LB, class EPI>
-__device__ __forceinline__ void mainloop_kc_tiles(LA& la, LB& lb, int nk, int ntl, int64_t bstride,
-                                                  uint16_t* smem, f32x4 (&acc)[TM / 32][TN / 32],
-                                                  const EPI& epi) {
-    using SM = Smem<TM, TN, false, false>;
+template <int TM, int TN, bool AKS, bool BKS, class LA, class LB, class EPI>
+__device__ __forceinline__ void mainloop_tiles(LA& la, LB& lb, int nk, int ntl, int64_t bstride,
+                                               uint16_t* smem, f32x4 (&acc)[TM / 32][TN / 32],
+                                               const EPI& epi) {
+    using SM = Smem<TM, TN, AKS, BKS>;
     const int w = threadIdx.x >> 6;
     const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TN / 2);
     zero_acc<TM, TN>(acc);
@@ -396,7 +399,7 @@ __device__ __forceinline__ void mainloop_kc_tiles(LA& la, LB& lb, int nk, int nt
             la.load(s + 1 - t1 * nk);
             lb.load_off(s + 1 - t1 * nk, t1 ? bstride : 0);
         }
-        mma_tile<TM, TN, false, false>(cur, cur + SM::A, wm0, wn0, acc);
+        mma_tile<TM, TN, AKS, BKS>(cur, cur + SM::A, wm0, wn0, acc);
         if (more) {
             la.store(nxt);
             lb.store(nxt + SM::A);

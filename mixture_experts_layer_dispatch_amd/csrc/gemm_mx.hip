@@ -108,9 +108,11 @@ struct LoadKCCat {
             off[q] = kc_off(r, kc * 16);
         }
     }
-    __device__ void load(int kt) {
+    __device__ void load(int kt) { load_off(kt, 0); }
+    // K step kt of the rows `extra` elements further (a later column tile)
+    __device__ void load_off(int kt, int64_t extra) {
         const bool second = kt >= nk1;
-        const int64_t k = (int64_t)(second ? kt - nk1 : kt) * kTK;
+        const int64_t k = extra + (int64_t)(second ? kt - nk1 : kt) * kTK;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
             const uint16_t* pb = global_select(second, p0[q], p1[q]);
@@ -132,10 +134,11 @@ struct LoadScalesCat {         // K-step-major scales of two matrices joined alo
     __device__ LoadScalesCat(const ScalesKMajor& s0, const ScalesKMajor& s1, int n1)
         : p0(threadIdx.x < ROWS ? s0.row(threadIdx.x) : nullptr),
           p1(threadIdx.x < ROWS ? s1.row(threadIdx.x) : nullptr), kst(s0.kstride()), nk1(n1), v(0) {}
-    __device__ void load(int kt) {
+    __device__ void load(int kt) { load_off(kt, 0); }
+    __device__ void load_off(int kt, int64_t extra) {
         const bool second = kt >= nk1;
         const uint32_t* pb = global_select(second, p0, p1);
-        v = pb ? pb[(int64_t)(second ? kt - nk1 : kt) * kst] : 0u;
+        v = pb ? pb[extra + (int64_t)(second ? kt - nk1 : kt) * kst] : 0u;
     }
     __device__ void store(uint32_t* s) const {
         if (threadIdx.x < ROWS) s[threadIdx.x] = v;
@@ -413,7 +416,7 @@ template <int TM>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M2_TN>::STAGE];
-    constexpr int NT = down_tiles_per_block<TM>();
+    constexpr int NT = short_k_tiles_per_block<TM>();
     const int ncol = a.H / M2_TN;
     int e, lo, hi, np;
     if (!map_mtile<TM>(a.g, (ncol + NT - 1) / NT, blockIdx.x, e, lo, hi, np)) return;
@@ -443,8 +446,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
             }
         }
     };
-    mainloop_mx_tiles<TM, M2_TN>(la, lb, sa, sb, I / 128, ntl, (int64_t)M2_TN * (I / 2), M2_TN, smem,
-                                 acc, epi);
+    if constexpr (NT == 1) {
+        mainloop_mx<TM, M2_TN>(la, lb, sa, sb, I / 128, smem, acc);
+        epi(0, acc);
+    } else {
+        mainloop_mx_tiles<TM, M2_TN>(la, lb, sa, sb, I / 128, ntl, (int64_t)M2_TN * (I / 2), M2_TN, smem,
+                                     acc, epi);
+    }
 }
 
 
@@ -575,16 +583,20 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
 // ================================================================ backward: gate/up dgrad
 // dX = Q(dg) Q(W_gate) + Q(du) Q(W_up), reductions over I, against the
 // transposed pre-quantised weights, in one K loop: the W_gate^T steps, then
-// the W_up^T steps.
+// the W_up^T steps; with 128-row tiles a block takes two neighbouring column
+// tiles in that loop.
 constexpr int M4_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
 
 template <int TM>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M4_TN>::STAGE];
-    int e, lo, hi, nt;
-    if (!map_mtile<TM>(a.g, a.H / M4_TN, blockIdx.x, e, lo, hi, nt)) return;
-    const int n0 = nt * M4_TN;
+    constexpr int NT = short_k_tiles_per_block<TM>();
+    const int ncol = a.H / M4_TN;
+    int e, lo, hi, np;
+    if (!map_mtile<TM>(a.g, (ncol + NT - 1) / NT, blockIdx.x, e, lo, hi, np)) return;
+    const int n0 = NT * np * M4_TN;
+    const int ntl = min(NT, ncol - NT * np);
     const int H = a.H, I = a.I;
     f32x4 acc[TM / 32][4];
     // one K loop over [dg | du] (2I codes per row) against W_gate^T then W_up^T
@@ -599,18 +611,26 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a
     LoadKCCat<M4_TN> lb(dbg, dbu, I / 128);
     LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScalesCat<M4_TN> sb(dsg, dsu, I / 128);
-    mainloop_mx<TM, M4_TN>(la, lb, sa, sb, 2 * I / 128, smem, acc);
     AccPos<TM, M4_TN> pos;
+    auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
-    for (int mb = 0; mb < TM / 32; ++mb) {
-        const int rl = lo + pos.m(mb);
-        if (rl >= hi) continue;
+        for (int mb = 0; mb < TM / 32; ++mb) {
+            const int rl = lo + pos.m(mb);
+            if (rl >= hi) continue;
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int c = n0 + pos.n(nb);
-            const f32x4 v = acc[mb][nb];
-            *(uint2*)(a.dx + (int64_t)rl * H + c) = pack4(v[0], v[1], v[2], v[3]);
+            for (int nb = 0; nb < 4; ++nb) {
+                const int col = n0 + t * M4_TN + pos.n(nb);
+                const f32x4 v = c[mb][nb];
+                *(uint2*)(a.dx + (int64_t)rl * H + col) = pack4(v[0], v[1], v[2], v[3]);
+            }
         }
+    };
+    if constexpr (NT == 1) {
+        mainloop_mx<TM, M4_TN>(la, lb, sa, sb, 2 * I / 128, smem, acc);
+        epi(0, acc);
+    } else {
+        mainloop_mx_tiles<TM, M4_TN>(la, lb, sa, sb, 2 * I / 128, ntl, (int64_t)M4_TN * (I / 2), M4_TN, smem,
+                                     acc, epi);
     }
 }
 
@@ -896,7 +916,7 @@ int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down_mx");
     const int ncol = a.H / M2_TN;
     const int tm_ = a.g.tm == 128 ? 128 : 64;
-    const int nt_ = tm_ == 128 ? down_tiles_per_block<128>() : down_tiles_per_block<64>();
+    const int nt_ = tm_ == 128 ? short_k_tiles_per_block<128>() : short_k_tiles_per_block<64>();
     const int grid_ = mgroup_grid_mx(a.g, tm_) * ((ncol + nt_ - 1) / nt_);
     if (grid_ <= 0) return 0;
     if (tm_ == 128) k_gemm_down_mx<128><<<grid_, 256, 0, st>>>(a);
@@ -911,7 +931,14 @@ int launch_gemm_down_dgrad_mx(const GemmDownDgradMXArgs& a, hipStream_t st) {
 
 int launch_gemm_gu_dgrad_mx(const GemmGuDgradMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gu_dgrad_mx");
-    MOE_LAUNCH_TM_MX(k_gemm_gu_dgrad_mx, a.H / M4_TN);
+    const int ncol = a.H / M4_TN;
+    const int tm_ = a.g.tm == 128 ? 128 : 64;
+    const int nt_ = tm_ == 128 ? short_k_tiles_per_block<128>() : short_k_tiles_per_block<64>();
+    const int grid_ = mgroup_grid_mx(a.g, tm_) * ((ncol + nt_ - 1) / nt_);
+    if (grid_ <= 0) return 0;
+    if (tm_ == 128) k_gemm_gu_dgrad_mx<128><<<grid_, 256, 0, st>>>(a);
+    else k_gemm_gu_dgrad_mx<64><<<grid_, 256, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
