@@ -531,11 +531,13 @@ constexpr int W_TM = 128, W_TN = 64;
 // (block g: tiles g, g + ng, ...), so that ng neighbouring 128-byte pieces of
 // each row are written at about the same time (a plain store kernel of this
 // tile shape measured ~5.0 TB/s walking whole rows per block, ~5.7 TB/s dealt
-// over 8 blocks, but less over 2 or 4).  Slabs of fewer than W_G * W_MIN_TILES
-// tiles stay whole: there, loading the A slab once per block dominates.
+// over 8 blocks).  Slabs of 16 to 63 tiles are dealt over 2 blocks (the down
+// projection's 16: 0.87 -> 0.83 ms with streaming stores; over 4 blocks,
+// loading the A slab once per block dominates: 1.01 ms); smaller slabs stay
+// whole.
 constexpr int W_G = 8, W_MIN_TILES = 8;
 __host__ __device__ __forceinline__ int wgrad_groups(int ntiles) {
-    return ntiles >= W_G * W_MIN_TILES ? W_G : 1;
+    return ntiles >= W_G * W_MIN_TILES ? W_G : (ntiles >= 16 ? 2 : 1);
 }
 // tiles of group g out of ng groups over ntiles
 __host__ __device__ __forceinline__ int wgrad_group_tiles(int ntiles, int ng, int g) {
