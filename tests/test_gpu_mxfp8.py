@@ -29,11 +29,17 @@ SHAPES = {
     "zipf_ring": si.custom_shape("zipf_ring_mx", T=1024, H=256, I=128, E=32, k=4, seed=23,
                                  macrobatch=256, minibatch=128, zipf=True),
     "dense_experts": si.custom_shape("dense_experts_mx", T=512, H=256, I=256, E=8, k=4, seed=24),
-    # column-stripe weight gradients (experts padded to at most 64 codes) next
-    # to the slab kernel, and their fp32 accumulation across macrobatches
+    # wider outputs: weight-gradient slabs of 8 and 16 column tiles (the
+    # latter dealt over two blocks), and their fp32 accumulation across
+    # macrobatches
     "stripes": si.custom_shape("stripes_mx", T=256, H=512, I=512, E=16, k=4, seed=25),
     "stripes_ring": si.custom_shape("stripes_ring_mx", T=512, H=512, I=1024, E=32, k=2, seed=26,
                                     n_shared=1, macrobatch=256, minibatch=128),
+    # 128-row tiles with an odd number of 128-column tiles (the two-tile K
+    # loops end on a single tile), for the routed experts and a dense shared
+    # expert; their weight gradients take the deep kernels
+    "odd_tiles": si.custom_shape("odd_tiles_mx", T=512, H=1152, I=384, E=4, k=2, seed=27,
+                                 n_shared=1),
 }
 
 

@@ -24,14 +24,18 @@ SMALL = {
                                    n_shared=1, macrobatch=128, minibatch=64),
     "zipf_ring": si.custom_shape("zipf_ring", T=1024, H=128, I=128, E=32, k=4, seed=15,
                                  macrobatch=256, minibatch=128, zipf=True),
-    # output widths that are multiples of 512: the column-stripe weight
-    # gradients take the experts with at most 64 rows, the slab kernels the
-    # rest; the ring variant accumulates them across two macrobatches in fp32
+    # wider outputs: weight-gradient slabs of 8 and 16 column tiles (the
+    # latter dealt over two blocks); the ring variant accumulates them across
+    # two macrobatches in fp32
     "stripes": si.custom_shape("stripes", T=256, H=512, I=512, E=16, k=4, seed=17),
     "stripes_ring": si.custom_shape("stripes_ring", T=512, H=512, I=1024, E=32, k=2, seed=18,
                                     n_shared=1, macrobatch=256, minibatch=128),
     # groups of ~256 rows: the 128-row tiles of the row-grouped GEMMs
     "dense_experts": si.custom_shape("dense_experts", T=512, H=256, I=256, E=8, k=4, seed=19),
+    # 128-row tiles with an odd number of 128-column tiles (the last block of
+    # the two-tile K loops holds one tile), for the routed experts and a dense
+    # shared expert; their weight gradients take the deep kernels
+    "odd_tiles": si.custom_shape("odd_tiles", T=512, H=1152, I=384, E=4, k=2, seed=20, n_shared=1),
 }
 
 
