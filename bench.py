@@ -35,12 +35,12 @@ HBM_PEAK_GBS = 8000.0
 # (FETCH_SIZE counts half of a copy's reads: x2; WRITE_SIZE counts them all);
 # filled in from profiles/, and dropped whenever the kernel changes.
 TRAFFIC = {                      # profiles/kernels_e512_t2048.txt
-    "gemm_gate_up": 8886.5e6,
-    "gemm_gu_dgrad": 8882.8e6,
-    "wgrad_gate_up": 8826.2e6,
-    "gemm_down": 4505.9e6,
-    "gemm_down_dgrad": 4687.5e6,
-    "wgrad_down": 4505.3e6,
+    "gemm_gate_up": 8884.1e6,
+    "gemm_gu_dgrad": 8875.8e6,
+    "wgrad_gate_up": 8825.7e6,
+    "gemm_down": 4505.1e6,
+    "gemm_down_dgrad": 4678.5e6,
+    "wgrad_down": 4485.9e6,
 }
 
 

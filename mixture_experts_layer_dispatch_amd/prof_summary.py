@@ -2,14 +2,19 @@
 of ``bench.py`` into a per-kernel table.
 
     python -m mixture_experts_layer_dispatch_amd.prof_summary TRACE.csv [--counters FETCH.csv WRITE.csv
-        --calib CFETCH.csv CWRITE.csv]
+        --calib CFETCH.csv CWRITE.csv] [--mfma MFMA.csv]
 
 Kernels of this library are grouped by name and grid size (one kernel can
 serve two shapes, e.g. both MXFP8 weight gradients); everything else (torch's
 input generation) is summed in one line.  With counter files, each group also
 gets its HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch),
 each scaled by what that counter reads for torch's copy kernel of known size
-in the calibration files (``bench.py --calibrate`` copies 4 GiB).
+in the calibration files (``bench.py --calibrate`` copies 4 GiB).  With an
+MFMA counter file (``--pmc MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16
+SQ_INSTS_VALU_MFMA_MOPS_F8``), each group gets the percentage of cycles the
+MFMA units were busy (rocprofv3's MfmaUtil: busy cycles summed over SIMDs over
+active GPU cycles times the SIMD count) and the matrix TFLOP/s the counters
+saw (MOPS x 512 flops, padded rows included) over the traced average duration.
 """
 from __future__ import annotations
 
@@ -64,6 +69,7 @@ def main():
     ap.add_argument("trace")
     ap.add_argument("--counters", nargs=2, metavar=("FETCH", "WRITE"))
     ap.add_argument("--calib", nargs=2, metavar=("CFETCH", "CWRITE"))
+    ap.add_argument("--mfma", metavar="MFMA")
     args = ap.parse_args()
     groups, other_ns, other_calls = trace_table(args.trace)
     fetch = write = None
@@ -73,9 +79,17 @@ def main():
         fetch = {k: v * 1024 * ff for k, v in counter_table(args.counters[0], "FETCH_SIZE").items()}
         write = {k: v * 1024 * fw for k, v in counter_table(args.counters[1], "WRITE_SIZE").items()}
         print(f"copy calibration: FETCH_SIZE x{ff:.3f}, WRITE_SIZE x{fw:.3f}")
+    util = mops = None
+    if args.mfma:
+        util = counter_table(args.mfma, "MfmaUtil")
+        bf = counter_table(args.mfma, "SQ_INSTS_VALU_MFMA_MOPS_BF16")
+        f8 = counter_table(args.mfma, "SQ_INSTS_VALU_MFMA_MOPS_F8")
+        mops = {k: bf.get(k, 0.0) + f8.get(k, 0.0) for k in set(bf) | set(f8)}
     head = f"{'kernel':24s} {'grid':>9s} {'calls':>6s} {'avg_us':>10s} {'min_us':>10s} {'max_us':>10s} {'total_ms':>10s}"
     if fetch is not None:
         head += f" {'read_MB':>10s} {'write_MB':>10s} {'GB/s':>8s}"
+    if util is not None:
+        head += f" {'mfma_busy%':>10s} {'mfma_TF/s':>10s}"
     print(head)
     rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
     for (n, grid), d in rows:
@@ -86,6 +100,10 @@ def main():
             rd, wr = fetch.get((n, grid)), write.get((n, grid))
             if rd is not None and wr is not None:
                 line += f" {rd / 1e6:10.1f} {wr / 1e6:10.1f} {(rd + wr) / avg:8.1f}"
+            elif util is not None:
+                line += f" {'':>10s} {'':>10s} {'':>8s}"
+        if util is not None and (n, grid) in util:
+            line += f" {util[(n, grid)]:10.1f} {mops.get((n, grid), 0.0) * 512 / avg / 1e3:10.1f}"
         print(line)
     print(f"{'(torch input generation)':24s} {'':>9s} {other_calls:6d} {'':>10s} {'':>10s} {'':>10s} "
           f"{other_ns / 1e6:10.3f}")
