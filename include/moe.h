@@ -76,7 +76,7 @@ typedef enum moe_precision {
 /* Layer shape and the tunables of [AREX] (third decision) / [ALPHA] 四, minus
  * the communication ones (there is no cross-GPU traffic on one GPU). */
 typedef struct moe_config {
-    int32_t T;             /* tokens                                                  */
+    int32_t T;             /* tokens, >= 1 (an empty batch is rejected: no call needed) */
     int32_t H;             /* hidden size, multiple of 128                            */
     int32_t I;             /* expert intermediate size, multiple of 128               */
     int32_t E;             /* routed experts, 1..1024                                 */
