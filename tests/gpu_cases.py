@@ -88,6 +88,24 @@ class Case:
         return None if self.sw is None else tuple(f32(a) for a in self.sw)
 
 
+def assert_rerun_bitwise(case):
+    """Run schedule, forward and backward again on the same inputs and require
+    every output to be bit-identical to the first run's (y, dx, dw, d_logits
+    and all weight gradients): the fixed accumulation order makes reruns
+    reproducible bit for bit."""
+    first = {"y": case.y.clone(), "dx": case.dx.clone(), "dw": case.dw.clone(),
+             "d_logits": case.dlogits.clone()}
+    first.update({k: v.clone() for k, v in case.grads.items()})
+    case.schedule()
+    case.forward()
+    case.backward()
+    again = {"y": case.y, "dx": case.dx, "dw": case.dw, "d_logits": case.dlogits}
+    again.update(case.grads)
+    for k, v in first.items():
+        assert torch.equal(again[k], v), f"{k} differs between two runs"
+    del first
+
+
 def ring_samples(case, sch, n_tokens=12, seed=5):
     """Sampled tokens spread over the macrobatches (the first and last token of
     each included) and two weight-gradient experts: the coldest routed expert

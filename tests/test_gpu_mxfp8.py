@@ -13,7 +13,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from gpu_cases import Case, assert_close, f32, ring_samples
+from gpu_cases import Case, assert_close, assert_rerun_bitwise, f32, ring_samples
 
 pytestmark = pytest.mark.gpu
 
@@ -205,6 +205,7 @@ def test_backward_mx_full_size_sampled():
         assert_close(f"dW_gate[{e}] (mxfp8)", f32(c.grads["d_w_gate"][e]), rb["dWg"][e], MX_TOL)
         assert_close(f"dW_up[{e}] (mxfp8)", f32(c.grads["d_w_up"][e]), rb["dWu"][e], MX_TOL)
         assert_close(f"dW_down[{e}] (mxfp8)", f32(c.grads["d_w_down"][e]), rb["dWd"][e], MX_TOL)
+    assert_rerun_bitwise(c)
 
 
 def test_forward_backward_mx_ring_full_size_sampled():
@@ -232,6 +233,7 @@ def test_forward_backward_mx_ring_full_size_sampled():
         assert_close(f"dW_gate[{e}] (mxfp8)", f32(c.grads["d_w_gate"][e]), rb["dWg"][e], MX_TOL)
         assert_close(f"dW_up[{e}] (mxfp8)", f32(c.grads["d_w_up"][e]), rb["dWu"][e], MX_TOL)
         assert_close(f"dW_down[{e}] (mxfp8)", f32(c.grads["d_w_down"][e]), rb["dWd"][e], MX_TOL)
+    assert_rerun_bitwise(c)
 
 
 def test_forward_backward_mx_ep_share_full_size_sampled():

@@ -11,7 +11,7 @@ import torch
 
 import oracle
 import synth_inputs as si
-from gpu_cases import Case, assert_close, f32, ring_samples
+from gpu_cases import Case, assert_close, assert_rerun_bitwise, f32, ring_samples
 
 pytestmark = pytest.mark.gpu
 
@@ -231,6 +231,7 @@ def test_forward_backward_full_size_sampled():
     counts = sch["counts"][0]
     n = case.grads["d_w_down"].float().flatten(1).abs().amax(1).cpu().numpy()
     assert np.all(np.isfinite(n)) and np.all((n == 0) == (counts == 0))
+    assert_rerun_bitwise(case)
 
 
 def test_forward_backward_ring_full_size_sampled():
@@ -260,6 +261,7 @@ def test_forward_backward_ring_full_size_sampled():
         assert_close(f"dW_gate[{e}]", f32(case.grads["d_w_gate"][e]), rb["dWg"][e])
         assert_close(f"dW_up[{e}]", f32(case.grads["d_w_up"][e]), rb["dWu"][e])
         assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])
+    assert_rerun_bitwise(case)
 
 
 def test_forward_backward_ep_share_full_size_sampled():
