@@ -37,36 +37,50 @@ namespace moe {
 
 // ================================================================ forward GEMM 1
 // g = X W_gate^T, u = X W_up^T, h = SiLU(g) * u; g, u saved (bf16), h to the
-// ring.  Tile: TM rows x (64 gate + 64 up columns).
+// ring.  Tile: TM rows x (TN/2 gate + TN/2 up columns).
 //
 // Row tiles (TM): 64 when groups are small (each weight byte is then read by
-// one or two tiles and the GEMM streams weights), 128 when the groups are
-// large enough for the GEMM to be MFMA work: a wave then computes 64 x 64
-// instead of 32 x 64 and reads a third less LDS per MFMA.
-constexpr int G1_TN = 128;
+// one or two tiles and the GEMM streams weights; four-wave blocks, 64 + 64
+// columns), 128 when the groups are large enough for the GEMM to be MFMA work
+// (eight-wave blocks, 128 + 128 columns, one block per CU, loads two K steps
+// ahead).  Each wave computes (TM/2) x 64: 32 gate and the matching 32 up
+// columns.
+template <int TM> struct GateUpShape;
+template <> struct GateUpShape<64> { static constexpr int TN = 128, NTHR = 256; };
+template <> struct GateUpShape<128> { static constexpr int TN = 256, NTHR = 512; };
 
 template <int TM>
-__global__ __launch_bounds__(256, 2) void k_gemm_gate_up(GemmGateUpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[lds_two_blocks(2 * Smem<TM, G1_TN, false, false>::STAGE)];
+constexpr int gate_up_lds() {
+    return TM == 64 ? lds_two_blocks(2 * Smem<64, 128, false, false>::STAGE) : 2 * SmemW8<128, 256>::STAGE;
+}
+
+template <int TM>
+__global__ __launch_bounds__(GateUpShape<TM>::NTHR, TM == 64 ? 2 : 1) void k_gemm_gate_up(GemmGateUpArgs a) {
+    constexpr int TN = GateUpShape<TM>::TN, NTHR = GateUpShape<TM>::NTHR;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[gate_up_lds<TM>()];
     int e, lo, hi, nt;
-    if (!map_mtile<TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
-    const int i0 = nt * 64;
+    if (!map_mtile<TM>(a.g, a.I / (TN / 2), blockIdx.x, e, lo, hi, nt)) return;
+    const int i0 = nt * (TN / 2);
     f32x4 acc[TM / 32][4];
     const int nk = a.H / kTK;
     const uint16_t* wg = a.w_gate + (int64_t)e * a.I * a.H;
     const uint16_t* wu = a.w_up + (int64_t)e * a.I * a.H;
     RowsGateUp sb{wg, wu, a.H, i0};
-    LoadKC<G1_TN, RowsGateUp> lb(sb);
+    LoadKC<TN, RowsGateUp, NTHR> lb(sb);
+    auto run = [&](auto& la) {
+        if constexpr (TM == 64) mainloop<TM, TN, false, false>(la, lb, nk, smem, acc);
+        else mainloop_w8<TM, TN>(la, lb, nk, smem, acc);
+    };
     if (a.x_gather) {
         RowsGather sa{a.x, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
-        LoadKC<TM, RowsGather> la(sa);
-        mainloop<TM, G1_TN, false, false>(la, lb, nk, smem, acc);
+        LoadKC<TM, RowsGather, NTHR> la(sa);
+        run(la);
     } else {
         RowsDirect sa{a.x, a.H, a.xrow0 + lo, hi - lo};
-        LoadKC<TM, RowsDirect> la(sa);
-        mainloop<TM, G1_TN, false, false>(la, lb, nk, smem, acc);
+        LoadKC<TM, RowsDirect, NTHR> la(sa);
+        run(la);
     }
-    AccPos<TM, G1_TN> pos;
+    AccPos<TM, 128> pos;          // wave tile (TM/2) x 64 at column 64 * (wave >> 1)
     const int wn = threadIdx.x >> 7;
 #pragma unroll
     for (int mb = 0; mb < TM / 32; ++mb) {
@@ -511,7 +525,12 @@ static inline int row_tile(const GroupRows& g) { return g.tm == 128 ? 128 : 64; 
 
 int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gate_up");
-    MOE_LAUNCH_TM(k_gemm_gate_up, a.I / 64);
+    const int tm_ = row_tile(a.g);
+    const int grid_ = mgroup_grid(a.g, tm_) * (a.I / (tm_ == 128 ? 128 : 64));
+    if (grid_ <= 0) return 0;
+    if (tm_ == 128) k_gemm_gate_up<128><<<grid_, GateUpShape<128>::NTHR, 0, st>>>(a);
+    else k_gemm_gate_up<64><<<grid_, GateUpShape<64>::NTHR, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {

@@ -19,6 +19,7 @@ struct RowsDirect {
     __device__ const uint16_t* row(int r) const {
         return r < nvalid ? base + (int64_t)(row0 + r) * ld : nullptr;
     }
+    __device__ const uint16_t* safe() const { return base; }
 };
 
 // Tile row r = schedule row grow0 + r; memory row = token of its slot.
@@ -37,6 +38,7 @@ struct RowsGather {
         }
         return base + (int64_t)(s / k) * ld;
     }
+    __device__ const uint16_t* safe() const { return base; }
 };
 
 // Gate/up weight rows interleaved in quarters of 32 so that a wave owns
@@ -52,6 +54,7 @@ struct RowsGateUp {
         const int i = i0 + ((q >> 1) << 5) + (n & 31);
         return global_select(q & 1, wg, wu) + (int64_t)i * ld;
     }
+    __device__ const uint16_t* safe() const { return wg; }
 };
 
 // Operand whose reduction index k is the memory row: krow(k) points at the
@@ -148,24 +151,40 @@ __device__ __forceinline__ int kc_off(int r, int byte) {
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
 
+// Branch-free 16-byte load: a null p reads the always-valid address `safe`
+// instead and yields zeros.  Loads guarded by a per-lane branch sit in
+// divergent blocks, where the compiler's memory-wait counting falls back to
+// waiting for every outstanding load; these never do.  (The zeroing is a
+// mask, not a select: a select on a loaded value is turned back into a branch
+// around the load.)
+__device__ __forceinline__ uint4 ld16_or_zero(const uint16_t* p, const uint16_t* safe) {
+    const bool ok = p != nullptr;
+    const uint4 x = *(const uint4*)global_select(!ok, p, safe);
+    const uint32_t m = 0u - (uint32_t)ok;
+    return make_uint4(x.x & m, x.y & m, x.z & m, x.w & m);
+}
+
 // ================================================================ loaders
-// KC tile: 16-byte chunks, 8 lanes per 128-byte row segment.
-template <int ROWS, class Src>
+// KC tile: 16-byte chunks, 8 lanes per 128-byte row segment; NTHR threads
+// share the loads.
+template <int ROWS, class Src, int NTHR = 256>
 struct LoadKC {
-    static constexpr int PER = ROWS * (kTK / 8) / 256;
+    static constexpr int PER = ROWS * (kTK / 8) / NTHR;
     const uint16_t* p[PER];
     int off[PER];
     uint4 v[PER];
     __device__ explicit LoadKC(const Src& src) {
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
-            const int c = threadIdx.x + 256 * q;
+            const int c = threadIdx.x + NTHR * q;
             const int r = c >> 3, kc = c & 7;
             const uint16_t* b = src.row(r);
             p[q] = b ? b + kc * 8 : nullptr;
             off[q] = kc_off(r, kc * 16);
         }
+        safe = src.safe();
     }
+    const uint16_t* safe;
     __device__ void load(int kt) { load_off(kt, 0); }
     // K step kt of the rows `extra` elements further (a later column tile)
     __device__ void load_off(int kt, int64_t extra) {
@@ -176,6 +195,21 @@ struct LoadKC {
     __device__ void store(uint16_t* s) const {
 #pragma unroll
         for (int q = 0; q < PER; ++q) *(uint4*)(s + off[q]) = v[q];
+    }
+    // Two register stages (R = 0: v, 1: v2) with branch-free loads, for K
+    // loops that keep two steps of loads in flight and rely on precise waits.
+    uint4 v2[PER];
+    template <int R>
+    __device__ void load_r(int kt) {
+        uint4(&d)[PER] = R ? v2 : v;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) d[q] = ld16_or_zero(p[q] ? p[q] + (int64_t)kt * kTK : nullptr, safe);
+    }
+    template <int R>
+    __device__ void store_r(uint16_t* s) const {
+        const uint4(&d)[PER] = R ? v2 : v;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) *(uint4*)(s + off[q]) = d[q];
     }
 };
 
@@ -358,6 +392,75 @@ __device__ __forceinline__ void mainloop(LA& la, LB& lb, int nk, uint16_t* smem,
         }
         __syncthreads();
     }
+}
+
+// Eight-wave blocks (512 threads) for GEMMs that are MFMA work: the block
+// tile is TM x TNB with both operands KC, the waves form a 2 x 4 grid and
+// each computes a (TM/2) x (TNB/4) tile (one wave's share of
+// mma_tile<TM, TNB/2>).  A CU holds one such block, so the loads are issued
+// two K steps ahead (two register stages, two LDS buffers): with one step in
+// flight every barrier waited for the next step's loads.  The loop body issues
+// its loads unconditionally (the last steps run in a tail), so each wait
+// covers only the older stage.
+template <int TM, int TNB>
+struct SmemW8 {
+    static constexpr int A = Tile<TM, false>::SIZE;
+    static constexpr int B = Tile<TNB, false>::SIZE;
+    static constexpr int STAGE = A + B;
+};
+
+template <int TM, int TNB, class LA, class LB>
+__device__ __forceinline__ void mainloop_w8(LA& la, LB& lb, int nk, uint16_t* smem,
+                                            f32x4 (&acc)[TM / 32][TNB / 64]) {
+    using SM = SmemW8<TM, TNB>;
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * (TM / 2), wn0 = (w >> 1) * (TNB / 4);
+    zero_acc<TM, TNB / 2>(acc);
+    if (nk <= 0) return;
+    uint16_t* buf0 = smem;
+    uint16_t* buf1 = smem + SM::STAGE;
+    auto mma = [&](const uint16_t* b) { mma_tile<TM, TNB / 2, false, false>(b, b + SM::A, wm0, wn0, acc); };
+    la.template load_r<0>(0);
+    lb.template load_r<0>(0);
+    if (nk > 1) {
+        la.template load_r<1>(1);
+        lb.template load_r<1>(1);
+    }
+    la.template store_r<0>(buf0);
+    lb.template store_r<0>(buf0 + SM::A);
+    __syncthreads();
+    int kt = 0;
+    // steps kt, kt + 1: buf0 holds kt, stage 1 holds kt + 1, stage 0 is free
+    for (; kt + 3 < nk; kt += 2) {
+        la.template load_r<0>(kt + 2);
+        lb.template load_r<0>(kt + 2);
+        mma(buf0);
+        la.template store_r<1>(buf1);
+        lb.template store_r<1>(buf1 + SM::A);
+        __syncthreads();
+        la.template load_r<1>(kt + 3);
+        lb.template load_r<1>(kt + 3);
+        mma(buf1);
+        la.template store_r<0>(buf0);
+        lb.template store_r<0>(buf0 + SM::A);
+        __syncthreads();
+    }
+    const int rest = nk - kt;              // the last one to three steps
+    if (rest == 3) {
+        la.template load_r<0>(kt + 2);
+        lb.template load_r<0>(kt + 2);
+    }
+    mma(buf0);
+    if (rest == 1) return;
+    la.template store_r<1>(buf1);
+    lb.template store_r<1>(buf1 + SM::A);
+    __syncthreads();
+    mma(buf1);
+    if (rest == 2) return;
+    la.template store_r<0>(buf0);        // buf0 is free since the last barrier
+    lb.template store_r<0>(buf0 + SM::A);
+    __syncthreads();
+    mma(buf0);
 }
 
 // Column tiles per block of the GEMMs with a short K loop (down projection,
