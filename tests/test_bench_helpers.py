@@ -1,0 +1,57 @@
+"""Host-side checks of bench.py's accounting: the per-GEMM flop split adds up
+to the step convention (6 H I per routed row forward, 12 H I backward, the
+shared expert's rows included), and the per-kernel algorithmic bytes of the
+2048-token layer match their closed forms."""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+import synth_inputs as si  # noqa: E402
+
+
+@pytest.mark.parametrize("name", ["e512_t2048", "e8_ep_share", "e512_t65536_zipf"])
+def test_gemm_flops_add_up_to_the_step(name):
+    s = si.SHAPES[name]
+    kf = bench.kernel_flops(s)
+    rows = s.T * s.k + (s.T if s.n_shared else 0)
+    bf16 = sum(v for k, v in kf.items() if not k.endswith("_mx"))
+    mx = sum(v for k, v in kf.items() if k.endswith("_mx"))
+    assert bf16 == mx == 18.0 * s.H * s.I * rows
+    assert kf["gemm_gate_up"] == 2 * kf["gemm_down"]          # 2I outputs vs H outputs, same K x N product
+
+
+def test_algorithmic_bytes_of_the_2048_token_layer():
+    s = si.SHAPES["e512_t2048"]
+    T, H, I, E, k = s.T, s.H, s.I, s.E, s.k
+    S = T * k
+    counts = np.full(E, S // E)                # every expert touched
+    kb = bench.kernel_bytes(s, counts)
+    # each touched expert's gate and up weights once, the gathered rows once, g, u, h written
+    assert kb["gemm_gate_up"] == E * 2 * I * H * 2 + S * H * 2 + 3 * S * I * 2
+    # the weight gradients: every expert's gradient written once (bf16)
+    assert kb["wgrad_gate_up"] >= E * 2 * I * H * 2
+    assert kb["wgrad_down"] >= E * H * I * 2
+    # MXFP8 weights: a code and 1/32 of a scale byte per element
+    assert kb["gemm_down_mx"] == int(E * H * I * (1 + 1 / 32) + S * I * (1 + 1 / 32) + S * H * 2)
+    # per-launch figures are not given for several macrobatches
+    assert bench.kernel_bytes(si.SHAPES["e512_t65536_zipf"], counts) == {}
+
+
+def test_roofline_ridge_separates_the_workloads():
+    """The 2048-token layer's GEMMs sit far below the bf16 ridge point (so their
+    roofline is HBM); the expert-parallel share's far above it (MFMA)."""
+    ridge = bench.MFMA_PEAK_TFLOPS["bf16"] * 1e12 / (bench.HBM_PEAK_GBS * 1e9)
+    s = si.SHAPES["e512_t2048"]
+    kb = bench.kernel_bytes(s, np.full(s.E, s.T * s.k // s.E))
+    kf = bench.kernel_flops(s)
+    assert kf["gemm_gate_up"] / kb["gemm_gate_up"] < ridge / 5
+    s = si.SHAPES["e8_ep_share"]
+    kb = bench.kernel_bytes(s, np.full(s.E, s.T * s.k // s.E))
+    kf = bench.kernel_flops(s)
+    assert kf["wgrad_gate_up"] / kb["wgrad_gate_up"] > ridge
