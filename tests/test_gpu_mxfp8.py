@@ -40,6 +40,9 @@ SHAPES = {
     # expert; their weight gradients take the deep kernels
     "odd_tiles": si.custom_shape("odd_tiles_mx", T=512, H=1152, I=384, E=4, k=2, seed=27,
                                  n_shared=1),
+    # k = E (every token to every expert) and the largest k (32)
+    "all_experts": si.custom_shape("all_experts_mx", T=96, H=128, I=128, E=4, k=4, seed=30),
+    "max_k": si.custom_shape("max_k_mx", T=64, H=128, I=128, E=64, k=32, seed=31),
 }
 
 

@@ -36,6 +36,11 @@ SMALL = {
     # the two-tile K loops holds one tile), for the routed experts and a dense
     # shared expert; their weight gradients take the deep kernels
     "odd_tiles": si.custom_shape("odd_tiles", T=512, H=1152, I=384, E=4, k=2, seed=20, n_shared=1),
+    # k = E: every token goes to every expert (the dense softmax mixture)
+    "all_experts": si.custom_shape("all_experts", T=96, H=128, I=128, E=4, k=4, seed=28),
+    # the largest k the library takes (32): 32 slots per token in the combine
+    # and the reverse-dispatch, 32 selection rounds in the routing
+    "max_k": si.custom_shape("max_k", T=64, H=128, I=128, E=64, k=32, seed=29),
 }
 
 
