@@ -43,6 +43,7 @@ SHAPES = {
     # k = E (every token to every expert) and the largest k (32)
     "all_experts": si.custom_shape("all_experts_mx", T=96, H=128, I=128, E=4, k=4, seed=30),
     "max_k": si.custom_shape("max_k_mx", T=64, H=128, I=128, E=64, k=32, seed=31),
+    "max_e": si.custom_shape("max_e_mx", T=256, H=128, I=128, E=1024, k=8, seed=33),
 }
 
 

@@ -41,6 +41,9 @@ SMALL = {
     # the largest k the library takes (32): 32 slots per token in the combine
     # and the reverse-dispatch, 32 selection rounds in the routing
     "max_k": si.custom_shape("max_k", T=64, H=128, I=128, E=64, k=32, seed=29),
+    # the largest E (1024): ten ballot rounds over the expert-id bits, most
+    # experts empty
+    "max_e": si.custom_shape("max_e", T=256, H=128, I=128, E=1024, k=8, seed=32),
 }
 
 
