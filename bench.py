@@ -57,9 +57,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="e512_t2048", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=8,
+    ap.add_argument("--cpu-tokens", type=int, default=48,
                     help="tokens in the CPU oracle's sample (forward + input gradients)")
-    ap.add_argument("--cpu-experts", type=int, default=2,
+    ap.add_argument("--cpu-experts", type=int, default=12,
                     help="experts in the CPU oracle's sample (weight gradients)")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8 leg (reported beside the bf16 value)")
