@@ -41,12 +41,12 @@ PAGES_CONTEXT = ("MoK 531.1 and HybridEP + Megatron 224.4 TFLOP/s per GPU: MXFP8
 # (FETCH_SIZE counts half of a copy's reads: x2; WRITE_SIZE counts them all);
 # filled in from profiles/, and dropped whenever the kernel changes.
 TRAFFIC = {                      # profiles/kernels_e512_t2048.txt
-    "gemm_gate_up": 8884.1e6,
-    "gemm_gu_dgrad": 8875.8e6,
+    "gemm_gate_up": 8888.0e6,
+    "gemm_gu_dgrad": 8882.0e6,
     "wgrad_gate_up": 8825.7e6,
-    "gemm_down": 4505.1e6,
-    "gemm_down_dgrad": 4678.5e6,
-    "wgrad_down": 4485.9e6,
+    "gemm_down": 4505.6e6,
+    "gemm_down_dgrad": 4690.2e6,
+    "wgrad_down": 4486.0e6,
 }
 
 
