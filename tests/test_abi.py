@@ -132,3 +132,15 @@ def test_mx_weight_buffers_match_the_header_layout():
         for pre, lead in (("w_", (E,)), ("s_", ())):
             assert tuple(q[pre + name + "q"].shape) == (*lead, rows, K)
             assert tuple(q[pre + name + "s"].shape) == (*lead, K // 128, rows, 4)
+
+
+def test_binding_raises_when_the_library_is_missing(monkeypatch, tmp_path):
+    """No fallback: without the built library every entry point raises."""
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libmoe_mi355x.so"))
+    monkeypatch.setattr(B, "_lib", None)
+    with pytest.raises(RuntimeError, match="missing"):
+        B.lib()
+    with pytest.raises(RuntimeError, match="missing"):
+        B.workspace_size(_cfg())
+    with pytest.raises(RuntimeError, match="missing"):
+        B.validate_config(_cfg())
