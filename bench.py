@@ -36,18 +36,28 @@ PAGES_CONTEXT = ("MoK 531.1 and HybridEP + Megatron 224.4 TFLOP/s per GPU: MXFP8
                  "512-expert H=4096 I=1024 top-10 layer on 64 GB300 GPUs (expert parallelism 64, "
                  "cross-GPU dispatch/combine included); other hardware and setup, so vs_baseline is null")
 
-# HBM bytes per launch from rocprofv3 FETCH_SIZE + WRITE_SIZE on e512_t2048,
-# each scaled by what that counter reads for a copy kernel of known size
-# (FETCH_SIZE counts half of a copy's reads: x2; WRITE_SIZE counts them all);
-# filled in from profiles/, and dropped whenever the kernel changes.
-TRAFFIC = {                      # profiles/kernels_e512_t2048.txt
-    "gemm_gate_up": 8888.0e6,
-    "gemm_gu_dgrad": 8882.0e6,
-    "wgrad_gate_up": 8825.7e6,
-    "gemm_down": 4505.6e6,
-    "gemm_down_dgrad": 4690.2e6,
-    "wgrad_down": 4486.0e6,
-}
+ROOT = os.path.dirname(os.path.abspath(__file__))
+
+
+def counter_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` from rocprofv3 FETCH_SIZE + WRITE_SIZE
+    runs (each scaled by what that counter reads for a copy kernel of known
+    size), as recorded in profiles/traffic_<workload>.json, with the state of
+    the record: "measured" when the file's source hash matches the HIP sources
+    of this build, else "stale" (the kernels changed since: bytes None) or
+    "absent"."""
+    from mixture_experts_layer_dispatch_amd.prof_summary import sources_sha256
+
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None, "absent"
+    rec = json.load(open(path))
+    if rec.get("sources_sha256") != sources_sha256():
+        return None, "stale"
+    k = rec.get("kernels", {}).get("k_" + kernel)
+    if k is None:
+        return None, "absent"
+    return k["read_bytes"] + k["write_bytes"], "measured"
 
 
 def parse():
@@ -57,12 +67,14 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="e512_t2048", choices=WORKLOADS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=48,
+    ap.add_argument("--cpu-tokens", type=int, default=24,
                     help="tokens in the CPU oracle's sample (forward + input gradients)")
-    ap.add_argument("--cpu-experts", type=int, default=12,
+    ap.add_argument("--cpu-experts", type=int, default=6,
                     help="experts in the CPU oracle's sample (weight gradients)")
     ap.add_argument("--no-mxfp8", action="store_true",
                     help="skip the MXFP8 leg (reported beside the bf16 value)")
+    ap.add_argument("--no-ep-share", action="store_true",
+                    help="skip the expert-parallel-share leg (reported beside the headline)")
     ap.add_argument("--calibrate", action="store_true",
                     help="only time plain HBM copy / fill / read kernels of known size and exit")
     return ap.parse_args()
@@ -141,16 +153,22 @@ def kernel_flops(shape) -> dict:
     return out
 
 
-def cpu_baseline(case, idx, w, n_tokens: int, n_experts: int):
-    """Time the oracle on a bounded sample of the same workload."""
+def cpu_baseline(case, n_tokens: int, n_experts: int):
+    """Time the oracle on a bounded sample of the same workload: routing and the
+    schedule of the whole batch (its own, from the logits on the host), then the
+    forward and input-gradient backward of n_tokens tokens and the weight
+    gradients of n_experts experts.  One untimed warm-up run, then the median
+    of three timed runs."""
     import oracle
     from threadpoolctl import threadpool_info
 
     shape = case.shape
     H, I, k = shape.H, shape.I, shape.k
+    logits = case.logits.cpu().numpy()
+    idx, w = oracle.route(logits, k)
+    counts = np.bincount(idx.reshape(-1), minlength=shape.E)
     rng = np.random.default_rng(0)
     tokens = np.sort(rng.choice(shape.T, size=n_tokens, replace=False))
-    counts = np.bincount(idx.reshape(-1), minlength=shape.E)
     experts = [int(e) for e in rng.choice(np.nonzero(counts)[0], size=n_experts, replace=False)]
     need = sorted(set(idx[tokens].reshape(-1).tolist()) | set(experts))
     # host copies of the weights the sample touches (fetched before timing)
@@ -159,10 +177,18 @@ def cpu_baseline(case, idx, w, n_tokens: int, n_experts: int):
     wd = {e: case.wd[e].float().cpu().numpy() for e in need}
     x = case.x.float().cpu().numpy()
     dy = case.dy.float().cpu().numpy()
-    t0 = time.perf_counter()
-    oracle.forward(x, wg, wu, wd, idx, w, tokens=tokens)
-    oracle.backward(x, wg, wu, wd, idx, w, dy, tokens=tokens, experts=experts)
-    dt = time.perf_counter() - t0
+
+    def once():
+        t0 = time.perf_counter()
+        idx_, w_ = oracle.route(logits, k)
+        oracle.schedule(idx_, shape.E)
+        oracle.forward(x, wg, wu, wd, idx_, w_, tokens=tokens)
+        oracle.backward(x, wg, wu, wd, idx_, w_, dy, tokens=tokens, experts=experts)
+        return time.perf_counter() - t0
+
+    once()
+    runs = sorted(once() for _ in range(3))
+    dt = runs[1]
     rows = int(sum(counts[e] for e in experts))
     flops = 12.0 * H * I * k * n_tokens + 6.0 * H * I * rows
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
@@ -171,10 +197,119 @@ def cpu_baseline(case, idx, w, n_tokens: int, n_experts: int):
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"float64 NumPy oracle: forward + input-gradient backward of {n_tokens} tokens "
-                   f"({n_tokens * k} slots) and the weight gradients of {n_experts} experts "
-                   f"({rows} rows) of the {shape.name} workload; {dt:.1f} s"),
+        "sample": (f"float64 NumPy oracle: routing + schedule of all {shape.T} tokens, forward + "
+                   f"input-gradient backward of {n_tokens} tokens ({n_tokens * k} slots) and the "
+                   f"weight gradients of {n_experts} experts ({rows} rows) of the {shape.name} "
+                   f"workload; median of 3 timed runs after 1 warm-up: {dt:.2f} s "
+                   f"(runs {', '.join(f'{r:.2f}' for r in runs)} s); flops counted on the sample only"),
     }
+
+
+class Inputs:
+    """Seeded inputs of one workload, resident on the GPU."""
+
+    def __init__(self, si, shape):
+        self.shape = shape
+        self.logits = si.logits(shape, "cuda")
+        self.x = si.tokens(shape, "cuda")
+        self.dy = si.grad_out(shape, "cuda")
+        self.wg, self.wu, self.wd = si.all_expert_weights(shape, "cuda")
+        self.weights = {"w_gate": self.wg, "w_up": self.wu, "w_down": self.wd}
+        shared = si.shared_weights(shape, "cuda")
+        if shared is not None:
+            self.weights.update({"s_gate": shared[0], "s_up": shared[1], "s_down": shared[2]})
+
+
+def step_flops(shape) -> float:
+    """Convention flops of one step: 18 H I per routed slot (+ per token for a
+    shared expert); the forward is a third of it."""
+    f = 18.0 * shape.H * shape.I * shape.T * shape.k
+    return f + (18.0 * shape.H * shape.I * shape.T if shape.n_shared else 0.0)
+
+
+def measure(torch, B, inp, precision, steps, warmup, stream):
+    """Time `steps` steps of schedule + forward + backward (after `warmup`),
+    then `steps` forward-only passes, then a pass with per-kernel HIP events.
+    Returns (ms per step, ms per forward, kernel stats, per-expert counts)."""
+    shape = inp.shape
+    T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
+    c = B.Config(T=T, H=H, I=I, E=E, k=k, n_shared=shape.n_shared,
+                 macrobatch=shape.macrobatch, minibatch=shape.minibatch, precision=precision)
+    ws = B.alloc_workspace(c)
+    sched = B.alloc_schedule(c)
+    saved = B.alloc_saved(c)
+    grads = B.alloc_grads(c)
+    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+    dx = torch.empty_like(y)
+    dw = torch.empty(T, k, dtype=torch.float32, device="cuda")
+    dlog = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    wts = dict(inp.weights)
+    if precision == B.PREC_MXFP8:
+        q = B.alloc_weights_mx(c)
+        B.moe_quantize_weights_mxfp8(c, inp.weights, q, stream)   # outside timing
+        wts["mx"] = q
+
+    def step():
+        B.moe_schedule(c, inp.logits, sched, ws, stream)
+        B.moe_forward(c, sched, inp.x, wts, y, saved, ws, stream)
+        B.moe_backward(c, sched, saved, inp.x, wts, inp.dy, dx, grads, dw, dlog, ws, stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    # forward alone (the schedule of the last step stays in place), the form in
+    # which the pages quote their MXFP8 numbers
+    start.record(stream)
+    for _ in range(steps):
+        B.moe_forward(c, sched, inp.x, wts, y, saved, ws, stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms_fwd = start.elapsed_time(stop) / steps
+    assert B.moe_check_device_error(ws, stream) == 0
+    B.profile_reset()
+    B.profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    B.profile_collect()
+    B.profile_enable(False)
+    stats = B.profile_stats()
+    counts = sched["counts"].cpu().numpy().sum(0)
+    del ws, saved, grads, wts
+    return ms, ms_fwd, stats, counts
+
+
+def kernel_table(stats, steps, kb):
+    out = {}
+    for name, (n, tot) in stats.items():
+        avg = tot / max(n, 1)
+        entry = {"launches_per_step": n / steps, "avg_ms": round(avg, 4)}
+        if name in kb:
+            entry["GB/s"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
+        out[name] = entry
+    return out
+
+
+def mfma_dominant(stats, steps, shape, prec):
+    """The GEMM with the largest time per step, as a fraction of the dense
+    matrix peak of its precision: its convention flops per step (its share of
+    the step's flops) over its measured time per step."""
+    kf = kernel_flops(shape)
+    gem = {n: v for n, v in stats.items() if n in kf}
+    if not gem:
+        return None
+    dom = max(gem, key=lambda n: gem[n][1])
+    t = gem[dom][1] / steps
+    tf = kf[dom] / (t * 1e-3) / 1e12
+    return {"kernel": dom, "ms_per_step": round(t, 4), "TFLOP/s": round(tf, 1),
+            "mfma_frac": round(tf / MFMA_PEAK_TFLOPS[prec], 4)}
 
 
 def main():
@@ -186,7 +321,7 @@ def main():
 
     import torch
 
-    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    sys.path.insert(0, ROOT)
     import synth_inputs as si
     from mixture_experts_layer_dispatch_amd import binding as B
 
@@ -202,96 +337,15 @@ def main():
 
     shape = si.SHAPES[args.workload]
     T, H, I, E, k = shape.T, shape.H, shape.I, shape.E, shape.k
-    cfg = B.Config(T=T, H=H, I=I, E=E, k=k, n_shared=shape.n_shared,
-                   macrobatch=shape.macrobatch, minibatch=shape.minibatch)
-
-    class Case:
-        pass
-
-    case = Case()
-    case.shape = shape
-    case.logits = si.logits(shape, "cuda")
-    case.x = si.tokens(shape, "cuda")
-    case.dy = si.grad_out(shape, "cuda")
-    case.wg, case.wu, case.wd = si.all_expert_weights(shape, "cuda")
-    weights = {"w_gate": case.wg, "w_up": case.wu, "w_down": case.wd}
-    shared = si.shared_weights(shape, "cuda")
-    if shared is not None:
-        weights.update({"s_gate": shared[0], "s_up": shared[1], "s_down": shared[2]})
-    sched = B.alloc_schedule(cfg)
-    y = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
-    dx = torch.empty_like(y)
-    dw = torch.empty(T, k, dtype=torch.float32, device="cuda")
-    dlog = torch.empty(T, E, dtype=torch.float32, device="cuda")
+    inp = Inputs(si, shape)
     stream = torch.cuda.current_stream()
-    S = T * k
-    flops = 18.0 * H * I * S + (18.0 * H * I * T if shape.n_shared else 0.0)
+    flops = step_flops(shape)
     flops_fwd = flops / 3.0
 
-    def run(precision):
-        """Time K steps of schedule + forward + backward, then a second pass with
-        per-kernel HIP events; returns (ms/step, kernel stats)."""
-        c = B.Config(T=T, H=H, I=I, E=E, k=k, n_shared=shape.n_shared,
-                     macrobatch=shape.macrobatch, minibatch=shape.minibatch, precision=precision)
-        ws = B.alloc_workspace(c)
-        saved = B.alloc_saved(c)
-        grads = B.alloc_grads(c)
-        wts = dict(weights)
-        if precision == B.PREC_MXFP8:
-            q = B.alloc_weights_mx(c)
-            B.moe_quantize_weights_mxfp8(c, weights, q, stream)   # outside timing
-            wts["mx"] = q
-
-        def step():
-            B.moe_schedule(c, case.logits, sched, ws, stream)
-            B.moe_forward(c, sched, case.x, wts, y, saved, ws, stream)
-            B.moe_backward(c, sched, saved, case.x, wts, case.dy, dx, grads, dw, dlog, ws, stream)
-
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        start.record(stream)
-        for _ in range(args.steps):
-            step()
-        stop.record(stream)
-        torch.cuda.synchronize()
-        ms = start.elapsed_time(stop) / args.steps
-        # forward alone (the schedule of the last step stays in place), the
-        # form in which the pages quote their MXFP8 numbers
-        start.record(stream)
-        for _ in range(args.steps):
-            B.moe_forward(c, sched, case.x, wts, y, saved, ws, stream)
-        stop.record(stream)
-        torch.cuda.synchronize()
-        ms_fwd = start.elapsed_time(stop) / args.steps
-        assert B.moe_check_device_error(ws, stream) == 0
-        B.profile_reset()
-        B.profile_enable(True)
-        for _ in range(args.steps):
-            step()
-        torch.cuda.synchronize()
-        B.profile_collect()
-        B.profile_enable(False)
-        stats = B.profile_stats()
-        del ws, saved, grads, wts
-        return ms, ms_fwd, stats
-
-    ms, ms_fwd, stats = run(B.PREC_BF16)
+    ms, ms_fwd, stats, counts = measure(torch, B, inp, B.PREC_BF16, args.steps, args.warmup, stream)
     print(f"[bench] bf16: {args.steps} steps, {ms:.3f} ms/step", file=sys.stderr, flush=True)
     value = flops / (ms * 1e-3) / 1e12
-    counts = sched["counts"].cpu().numpy().sum(0)
     kb = kernel_bytes(shape, counts)
-
-    def kernel_table(st):
-        out = {}
-        for name, (n, tot) in st.items():
-            avg = tot / max(n, 1)
-            entry = {"launches_per_step": n / args.steps, "avg_ms": round(avg, 4)}
-            if name in kb:
-                entry["GB/s"] = round(kb[name] / (avg * 1e-3) / 1e9, 1)
-            out[name] = entry
-        return out
 
     def step_roofline(st, ms_step):
         """The whole step against HBM: the algorithmic bytes of every launch
@@ -304,7 +358,7 @@ def main():
                 "frac": round(floor / ms_step, 4),
                 "TFLOP/s_ceiling": round(flops / (floor * 1e-3) / 1e12, 1)}
 
-    kernels = kernel_table(stats)
+    kernels = kernel_table(stats, args.steps, kb)
     dom = max(stats, key=lambda n: stats[n][1])
     dom_avg = stats[dom][1] / stats[dom][0]
     kf = kernel_flops(shape)
@@ -313,9 +367,10 @@ def main():
     per_step = stats[dom][0] / args.steps                  # launches of the kernel per step
     if dom in kb and (dom not in kf or kf[dom] / (kb[dom] * per_step) < ridge):
         achieved = kb[dom] / (dom_avg * 1e-3) / 1e9
+        traffic, tstate = counter_traffic(args.workload, dom)
         roofline = {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                    "traffic": TRAFFIC.get(dom) if args.workload == "e512_t2048" else None,
+                    "traffic": traffic, "traffic_source": tstate,
                     "avg_ms": round(dom_avg, 4), "bytes_per_launch": kb[dom]}
     elif dom in kf:
         # a GEMM whose groups are large (or a stream of macrobatches, where
@@ -330,7 +385,8 @@ def main():
 
     mx = None
     if not args.no_mxfp8:
-        ms_mx, ms_fwd_mx, stats_mx = run(B.PREC_MXFP8)
+        ms_mx, ms_fwd_mx, stats_mx, _ = measure(torch, B, inp, B.PREC_MXFP8, args.steps,
+                                                args.warmup, stream)
         print(f"[bench] mxfp8: {args.steps} steps, {ms_mx:.3f} ms/step", file=sys.stderr, flush=True)
         v_mx = flops / (ms_mx * 1e-3) / 1e12
         mx = {"value": round(v_mx, 2), "unit": "TFLOP/s",
@@ -339,14 +395,35 @@ def main():
               "step_roofline": step_roofline(stats_mx, ms_mx),
               "forward": {"ms": round(ms_fwd_mx, 4),
                           "TFLOP/s": round(flops_fwd / (ms_fwd_mx * 1e-3) / 1e12, 2)},
-              "kernels": kernel_table(stats_mx)}
+              "kernels": kernel_table(stats_mx, args.steps, kb)}
+
+    ep = None
+    if not args.no_ep_share and args.workload != "e8_ep_share":
+        # one GPU's expert-parallel share (8 experts x 2560 rows): the MFMA-bound
+        # shape of the same layer, measured beside the headline
+        es = si.SHAPES["e8_ep_share"]
+        einp = Inputs(si, es)
+        ef = step_flops(es)
+        ep = {"workload": f"{es.name}: T={es.T} rows H={es.H} I={es.I} E={es.E} top-{es.k}, "
+                          "schedule+forward+backward", "steps": 10, "warmup": 3}
+        for prec, pname in ((B.PREC_BF16, "bf16"), (B.PREC_MXFP8, "mxfp8")):
+            if prec == B.PREC_MXFP8 and args.no_mxfp8:
+                continue
+            e_ms, e_fwd, e_st, _ = measure(torch, B, einp, prec, 10, 3, stream)
+            tf = ef / (e_ms * 1e-3) / 1e12
+            ep[pname] = {"TFLOP/s": round(tf, 1), "ms_per_step": round(e_ms, 4),
+                         "mfma_peak_frac": round(tf / MFMA_PEAK_TFLOPS[pname], 4),
+                         "forward": {"ms": round(e_fwd, 4),
+                                     "TFLOP/s": round(ef / 3 / (e_fwd * 1e-3) / 1e12, 1)},
+                         "dominant": mfma_dominant(e_st, 10, es, pname),
+                         "kernels": kernel_table(e_st, 10, {})}
+            print(f"[bench] ep_share {pname}: {e_ms:.3f} ms/step", file=sys.stderr, flush=True)
+        del einp
 
     cpu = None
     if not args.no_cpu_baseline:
-        idx = sched["topk_idx"].cpu().numpy()
-        wts = sched["topk_w"].cpu().numpy().astype(np.float64)
         import oracle  # noqa: F401  (test infrastructure: the CPU baseline only)
-        cpu = cpu_baseline(case, idx, wts, args.cpu_tokens, args.cpu_experts)
+        cpu = cpu_baseline(inp, args.cpu_tokens, args.cpu_experts)
 
     out = {
         "metric": "MoE layer TFLOP/s fwd+bwd (bf16, MXFP8) at 512E H4096 I1024 top-10",
@@ -371,6 +448,7 @@ def main():
         "pages_context": PAGES_CONTEXT,
         "cpu_baseline": cpu,
         "mxfp8": mx,
+        "ep_share": ep,
         "kernels": kernels,
     }
     print(json.dumps(out), flush=True)

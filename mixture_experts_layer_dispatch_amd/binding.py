@@ -266,14 +266,122 @@ def _grads(g: dict) -> moe_grads:
                        for n, _ in moe_grads._fields_])
 
 
+# ------------------------------------------------------------------ argument checks
+# The C side can only check pointers for null and alignment; a buffer of the
+# wrong size would be written out of bounds on the device.  Every tensor is
+# therefore checked against the Config here, before anything reaches the
+# library: shape, dtype and contiguity of all of them first, then that each
+# lives on a GPU.  The _spec_* helpers list (name, tensor, shape, dtype).
+def _validate(specs):
+    for name, t, shape, dtype in specs:
+        if t is None:
+            raise ValueError(f"{name}: missing")
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+    for name, t, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: must be on the GPU, found on {t.device}")
+
+
+def _spec_ws(cfg: Config, ws):
+    n = ws.numel() if isinstance(ws, torch.Tensor) else -1
+    need = workspace_size(cfg)
+    if isinstance(ws, torch.Tensor) and ws.dtype == torch.uint8 and n < need:
+        raise ValueError(f"workspace: {n} bytes, the config needs {need}")
+    return [("workspace", ws, (n,), torch.uint8)]
+
+
+def _spec_sched(cfg: Config, s: dict):
+    i32, f32_ = torch.int32, torch.float32
+    want = {"topk_idx": ((cfg.T, cfg.k), i32), "topk_w": ((cfg.T, cfg.k), f32_),
+            "counts": ((cfg.n_macro, cfg.E), i32), "offsets": ((cfg.n_macro, cfg.E + 1), i32),
+            "mini_counts": ((cfg.n_macro, cfg.E, cfg.n_mini), i32),
+            "row_of_slot": ((cfg.S,), i32), "slot_of_row": ((cfg.S,), i32)}
+    return [(f"sched[{n!r}]", s.get(n), shape, dt) for n, (shape, dt) in want.items()]
+
+
+def _spec_weights(cfg: Config, w: dict):
+    E, H, I, bf = cfg.E, cfg.H, cfg.I, torch.bfloat16
+    out = [("w_gate", w.get("w_gate"), (E, I, H), bf), ("w_up", w.get("w_up"), (E, I, H), bf),
+           ("w_down", w.get("w_down"), (E, H, I), bf)]
+    if cfg.n_shared:
+        out += [("s_gate", w.get("s_gate"), (I, H), bf), ("s_up", w.get("s_up"), (I, H), bf),
+                ("s_down", w.get("s_down"), (H, I), bf)]
+    return out
+
+
+def _mx_shapes(cfg: Config):
+    """{field: shape} of every quantised weight array (uint8)."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    mats = (("gate_", I, H), ("up_", I, H), ("down_", H, I),
+            ("gate_t", H, I), ("up_t", H, I), ("down_t", I, H))
+    out = {}
+    for prefix, lead in (("w_", (E,)), ("s_", ())):
+        if prefix == "s_" and not cfg.n_shared:
+            continue
+        for name, rows, K in mats:
+            out[prefix + name + "q"] = (*lead, rows, K)
+            out[prefix + name + "s"] = (*lead, K // 128, rows, 4)
+    return out
+
+
+def _spec_weights_mx(cfg: Config, q, forward: bool = True, transposed: bool = True):
+    """The quantised arrays a call reads: the forward orientation, the
+    transposed one (backward), or both (the quantiser writes both)."""
+    if q is None:
+        raise ValueError("weights['mx']: the MXFP8 path needs the quantised weights")
+    out = []
+    for n, shape in _mx_shapes(cfg).items():
+        is_t = n.endswith(("_tq", "_ts"))
+        if (is_t and transposed) or (not is_t and forward):
+            out.append((f"mx[{n!r}]", q.get(n), shape, torch.uint8))
+    return out
+
+
+def _spec_saved(cfg: Config, s: dict):
+    dt = torch.float32 if cfg.precision == PREC_MXFP8 else torch.bfloat16
+    out = [("saved['g']", s.get("g"), (cfg.S, cfg.I), dt),
+           ("saved['u']", s.get("u"), (cfg.S, cfg.I), dt)]
+    if cfg.n_shared:
+        out += [("saved['sg']", s.get("sg"), (cfg.T, cfg.I), dt),
+                ("saved['su']", s.get("su"), (cfg.T, cfg.I), dt)]
+    return out
+
+
+def _spec_grads(cfg: Config, g: dict):
+    E, H, I, bf = cfg.E, cfg.H, cfg.I, torch.bfloat16
+    out = [("grads['d_w_gate']", g.get("d_w_gate"), (E, I, H), bf),
+           ("grads['d_w_up']", g.get("d_w_up"), (E, I, H), bf),
+           ("grads['d_w_down']", g.get("d_w_down"), (E, H, I), bf)]
+    if cfg.n_shared:
+        out += [("grads['d_s_gate']", g.get("d_s_gate"), (I, H), bf),
+                ("grads['d_s_up']", g.get("d_s_up"), (I, H), bf),
+                ("grads['d_s_down']", g.get("d_s_down"), (H, I), bf)]
+    return out
+
+
 # ------------------------------------------------------------------ entry points
 def moe_schedule(cfg: Config, logits: torch.Tensor, sched: dict, ws: torch.Tensor, stream=None):
+    _validate([("logits", logits, (cfg.T, cfg.E), torch.float32)] + _spec_sched(cfg, sched)
+              + _spec_ws(cfg, ws))
     _check(lib().moe_schedule(ctypes.byref(cfg.c()), _p(logits), ctypes.byref(_sched(sched)),
                               _p(ws), ws.numel(), _stream(stream)), "moe_schedule")
 
 
 def moe_forward(cfg: Config, sched: dict, x: torch.Tensor, weights: dict, y: torch.Tensor,
                 saved: dict, ws: torch.Tensor, stream=None):
+    bf = torch.bfloat16
+    specs = _spec_sched(cfg, sched) + [("x", x, (cfg.T, cfg.H), bf), ("y", y, (cfg.T, cfg.H), bf)]
+    specs += _spec_weights(cfg, weights)
+    if cfg.precision == PREC_MXFP8:
+        specs += _spec_weights_mx(cfg, weights.get("mx"), forward=True, transposed=False)
+    _validate(specs + _spec_saved(cfg, saved) + _spec_ws(cfg, ws))
     wst, _keep = _weights(weights)
     _check(lib().moe_forward(ctypes.byref(cfg.c()), ctypes.byref(_sched(sched)), _p(x),
                              ctypes.byref(wst), _p(y), ctypes.byref(_saved(saved)),
@@ -283,6 +391,17 @@ def moe_forward(cfg: Config, sched: dict, x: torch.Tensor, weights: dict, y: tor
 def moe_backward(cfg: Config, sched: dict, saved: dict, x: torch.Tensor, weights: dict,
                  dy: torch.Tensor, dx: torch.Tensor, grads: dict, dw: torch.Tensor,
                  d_logits, ws: torch.Tensor, stream=None):
+    bf = torch.bfloat16
+    specs = _spec_sched(cfg, sched) + _spec_saved(cfg, saved)
+    specs += [("x", x, (cfg.T, cfg.H), bf), ("dy", dy, (cfg.T, cfg.H), bf),
+              ("dx", dx, (cfg.T, cfg.H), bf)]
+    specs += _spec_weights(cfg, weights)
+    if cfg.precision == PREC_MXFP8:
+        specs += _spec_weights_mx(cfg, weights.get("mx"), forward=False, transposed=True)
+    specs += _spec_grads(cfg, grads) + [("dw", dw, (cfg.T, cfg.k), torch.float32)]
+    if d_logits is not None:
+        specs.append(("d_logits", d_logits, (cfg.T, cfg.E), torch.float32))
+    _validate(specs + _spec_ws(cfg, ws))
     wst, _keep = _weights(weights)
     _check(lib().moe_backward(ctypes.byref(cfg.c()), ctypes.byref(_sched(sched)),
                               ctypes.byref(_saved(saved)), _p(x), ctypes.byref(wst),
@@ -293,21 +412,12 @@ def moe_backward(cfg: Config, sched: dict, saved: dict, x: torch.Tensor, weights
 def alloc_weights_mx(cfg: Config, device="cuda") -> dict:
     """Buffers of every quantised weight array (uint8): codes [.., rows, K],
     scales K-step-major [.., K/128, rows, 4]."""
-    E, H, I = cfg.E, cfg.H, cfg.I
     u8 = dict(dtype=torch.uint8, device=device)
-    mats = (("gate_", I, H), ("up_", I, H), ("down_", H, I),          # "w_gate_q", "w_gate_s", ...
-            ("gate_t", H, I), ("up_t", H, I), ("down_t", I, H))      # "w_gate_tq", "w_gate_ts", ...
-    q = {}
-    for prefix, lead in (("w_", (E,)), ("s_", ())):
-        if prefix == "s_" and not cfg.n_shared:
-            continue
-        for name, rows, K in mats:
-            q[prefix + name + "q"] = torch.empty(*lead, rows, K, **u8)
-            q[prefix + name + "s"] = torch.empty(*lead, K // 128, rows, 4, **u8)
-    return q
+    return {n: torch.empty(*shape, **u8) for n, shape in _mx_shapes(cfg).items()}
 
 
 def moe_quantize_weights_mxfp8(cfg: Config, weights: dict, out: dict, stream=None):
+    _validate(_spec_weights(cfg, weights) + _spec_weights_mx(cfg, out))
     wst, _keep = _weights(weights)
     mx = _weights_mx(out)
     _check(lib().moe_quantize_weights_mxfp8(ctypes.byref(cfg.c()), ctypes.byref(wst),
@@ -316,6 +426,7 @@ def moe_quantize_weights_mxfp8(cfg: Config, weights: dict, out: dict, stream=Non
 
 
 def moe_check_device_error(ws: torch.Tensor, stream=None) -> int:
+    _validate([("workspace", ws, (ws.numel() if isinstance(ws, torch.Tensor) else -1,), torch.uint8)])
     v = ctypes.c_int32()
     _check(lib().moe_check_device_error(_p(ws), ws.numel(), _stream(stream), ctypes.byref(v)),
            "moe_check_device_error")

@@ -15,15 +15,35 @@ SQ_INSTS_VALU_MFMA_MOPS_F8``), each group gets the percentage of cycles the
 MFMA units were busy (rocprofv3's MfmaUtil: busy cycles summed over SIMDs over
 active GPU cycles times the SIMD count) and the matrix TFLOP/s the counters
 saw (MOPS x 512 flops, padded rows included) over the traced average duration.
+
+``--traffic-json OUT`` also writes the counter bytes per launch of every
+kernel that ran with a single grid size, keyed by kernel name, together with
+``sources_sha256()`` of the HIP sources they were measured on; ``bench.py``
+reports a kernel's counter traffic only while that hash still matches.
 """
 from __future__ import annotations
 
 import argparse
 import collections
 import csv
+import hashlib
+import json
+import os
 import re
 
 COPY_BYTES = 4 << 30          # bench.py --calibrate: 4 GiB read and 4 GiB written
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def sources_sha256() -> str:
+    """Hash of every HIP source and header the library is built from."""
+    h = hashlib.sha256()
+    for fn in sorted(os.listdir(CSRC)):
+        if fn.endswith((".hip", ".h")):
+            h.update(fn.encode())
+            with open(os.path.join(CSRC, fn), "rb") as f:
+                h.update(f.read())
+    return h.hexdigest()
 
 
 def _short(name: str):
@@ -70,6 +90,9 @@ def main():
     ap.add_argument("--counters", nargs=2, metavar=("FETCH", "WRITE"))
     ap.add_argument("--calib", nargs=2, metavar=("CFETCH", "CWRITE"))
     ap.add_argument("--mfma", metavar="MFMA")
+    ap.add_argument("--traffic-json", metavar="OUT")
+    ap.add_argument("--workload", default="", help="workload name recorded in the traffic file")
+    ap.add_argument("--command", default="", help="command line recorded in the traffic file")
     args = ap.parse_args()
     groups, other_ns, other_calls = trace_table(args.trace)
     fetch = write = None
@@ -107,6 +130,17 @@ def main():
         print(line)
     print(f"{'(torch input generation)':24s} {'':>9s} {other_calls:6d} {'':>10s} {'':>10s} {'':>10s} "
           f"{other_ns / 1e6:10.3f}")
+    if args.traffic_json and fetch is not None:
+        grids = collections.Counter(n for (n, _) in groups)
+        kern = {}
+        for (n, grid), d in groups.items():
+            rd, wr = fetch.get((n, grid)), write.get((n, grid))
+            if grids[n] == 1 and rd is not None and wr is not None:
+                kern[n] = {"grid": grid, "read_bytes": round(rd), "write_bytes": round(wr),
+                           "avg_us": round(sum(d) / len(d) / 1e3, 1)}
+        with open(args.traffic_json, "w") as f:
+            json.dump({"workload": args.workload, "sources_sha256": sources_sha256(),
+                       "command": args.command, "kernels": kern}, f, indent=1, sort_keys=True)
 
 
 if __name__ == "__main__":

@@ -63,12 +63,31 @@ class Case:
 
     def backward(self):
         c = self.cfg
-        self.dx = torch.empty_like(self.x)
-        self.grads = B.alloc_grads(c)
-        self.dw = torch.empty(c.T, c.k, dtype=torch.float32, device="cuda")
-        self.dlogits = torch.empty(c.T, c.E, dtype=torch.float32, device="cuda")
+        if getattr(self, "dx", None) is None:          # outputs allocated once, reused by reruns
+            self.dx = torch.empty_like(self.x)
+            self.grads = B.alloc_grads(c)
+            self.dw = torch.empty(c.T, c.k, dtype=torch.float32, device="cuda")
+            self.dlogits = torch.empty(c.T, c.E, dtype=torch.float32, device="cuda")
         B.moe_backward(c, self.sched, self.saved, self.x, self.weights, self.dy, self.dx,
                        self.grads, self.dw, self.dlogits, self.ws)
+
+    def poison_outputs(self):
+        """Fill every buffer the layer writes (schedule, saved activations,
+        outputs, gradients, workspace) with NaN / -1 patterns, so that a rerun
+        that skipped a write cannot pass by leaving the previous run's values
+        in place."""
+        for t in self.sched.values():
+            t.fill_(-1)
+        for t in self.saved.values():
+            t.fill_(float("nan"))
+        self.y.fill_(float("nan"))
+        self.ws.fill_(0xFF)
+        if getattr(self, "dx", None) is not None:
+            self.dx.fill_(float("nan"))
+            self.dw.fill_(float("nan"))
+            self.dlogits.fill_(float("nan"))
+            for t in self.grads.values():
+                t.fill_(float("nan"))
 
     # ------------------------------------------------------------- oracle side
     def oracle_schedule(self):
@@ -96,6 +115,7 @@ def assert_rerun_bitwise(case):
     first = {"y": case.y.clone(), "dx": case.dx.clone(), "dw": case.dw.clone(),
              "d_logits": case.dlogits.clone()}
     first.update({k: v.clone() for k, v in case.grads.items()})
+    case.poison_outputs()
     case.schedule()
     case.forward()
     case.backward()

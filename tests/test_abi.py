@@ -144,3 +144,74 @@ def test_binding_raises_when_the_library_is_missing(monkeypatch, tmp_path):
         B.workspace_size(_cfg())
     with pytest.raises(RuntimeError, match="missing"):
         B.validate_config(_cfg())
+
+
+def _cpu_buffers(cfg):
+    """Correctly shaped buffers of every argument, on the CPU (the binding's
+    checks run before any device work, so nothing here reaches the library)."""
+    import torch
+
+    bf = torch.bfloat16
+    ws = torch.empty(B.workspace_size(cfg), dtype=torch.uint8)
+    sched = B.alloc_schedule(cfg, "cpu")
+    x = torch.zeros(cfg.T, cfg.H, dtype=bf)
+    w = {"w_gate": torch.zeros(cfg.E, cfg.I, cfg.H, dtype=bf),
+         "w_up": torch.zeros(cfg.E, cfg.I, cfg.H, dtype=bf),
+         "w_down": torch.zeros(cfg.E, cfg.H, cfg.I, dtype=bf)}
+    return dict(ws=ws, sched=sched, x=x, y=x.clone(), w=w, saved=B.alloc_saved(cfg, "cpu"),
+                grads=B.alloc_grads(cfg, "cpu"), dw=torch.zeros(cfg.T, cfg.k),
+                dl=torch.zeros(cfg.T, cfg.E), logits=torch.zeros(cfg.T, cfg.E))
+
+
+def test_binding_checks_every_tensor_before_the_call():
+    """Wrong shape, dtype or layout of any tensor raises ValueError on the host,
+    before anything is enqueued (the C side can only see pointers)."""
+    import torch
+
+    cfg = _cfg()
+    b = _cpu_buffers(cfg)
+    # everything right but on the CPU: the device check is the one that fires
+    with pytest.raises(ValueError, match="GPU"):
+        B.moe_schedule(cfg, b["logits"], b["sched"], b["ws"])
+    with pytest.raises(ValueError, match="shape"):
+        B.moe_schedule(cfg, torch.zeros(cfg.T, cfg.E + 1), b["sched"], b["ws"])
+    with pytest.raises(ValueError, match="dtype"):
+        B.moe_schedule(cfg, b["logits"].double(), b["sched"], b["ws"])
+    bad = dict(b["sched"], row_of_slot=torch.zeros(cfg.S - 1, dtype=torch.int32))
+    with pytest.raises(ValueError, match="row_of_slot"):
+        B.moe_schedule(cfg, b["logits"], bad, b["ws"])
+    with pytest.raises(ValueError, match="workspace"):
+        B.moe_schedule(cfg, b["logits"], b["sched"], b["ws"][:16])
+    # forward: a non-contiguous x, a y of the wrong shape, weights of another E
+    with pytest.raises(ValueError, match="contiguous"):
+        B.moe_forward(cfg, b["sched"], torch.zeros(cfg.H, cfg.T, dtype=torch.bfloat16).t(),
+                      b["w"], b["y"], b["saved"], b["ws"])
+    with pytest.raises(ValueError, match="y: shape"):
+        B.moe_forward(cfg, b["sched"], b["x"], b["w"], b["y"][:-1], b["saved"], b["ws"])
+    w_bad = dict(b["w"], w_down=torch.zeros(cfg.E + 1, cfg.H, cfg.I, dtype=torch.bfloat16))
+    with pytest.raises(ValueError, match="w_down"):
+        B.moe_forward(cfg, b["sched"], b["x"], w_bad, b["y"], b["saved"], b["ws"])
+    # bf16 saved activations handed to an MXFP8 config (which saves fp32)
+    mx = B.Config(**{**cfg.__dict__, "precision": B.PREC_MXFP8})
+    bmx = _cpu_buffers(mx)
+    bmx["w"]["mx"] = B.alloc_weights_mx(mx, "cpu")
+    with pytest.raises(ValueError, match="saved\\['g'\\]: dtype"):
+        B.moe_forward(mx, bmx["sched"], bmx["x"], bmx["w"], bmx["y"], b["saved"], bmx["ws"])
+    with pytest.raises(ValueError, match="mx"):
+        B.moe_forward(mx, bmx["sched"], bmx["x"], b["w"], bmx["y"], bmx["saved"], bmx["ws"])
+    # backward: dw of [T, k+1], d_logits of [T, k], a gradient of the wrong dtype
+    args = (cfg, b["sched"], b["saved"], b["x"], b["w"], b["x"], b["y"], b["grads"])
+    with pytest.raises(ValueError, match="dw"):
+        B.moe_backward(*args, torch.zeros(cfg.T, cfg.k + 1), b["dl"], b["ws"])
+    with pytest.raises(ValueError, match="d_logits"):
+        B.moe_backward(*args, b["dw"], torch.zeros(cfg.T, cfg.k), b["ws"])
+    g_bad = dict(b["grads"], d_w_up=b["grads"]["d_w_up"].float())
+    with pytest.raises(ValueError, match="d_w_up"):
+        B.moe_backward(*args[:-1], g_bad, b["dw"], b["dl"], b["ws"])
+    with pytest.raises(ValueError, match="GPU"):
+        B.moe_backward(*args, b["dw"], None, b["ws"])
+    # the quantiser: an output array of the wrong shape
+    q = B.alloc_weights_mx(mx, "cpu")
+    q["w_up_ts"] = q["w_up_ts"][:-1]
+    with pytest.raises(ValueError, match="w_up_ts"):
+        B.moe_quantize_weights_mxfp8(mx, b["w"], q)

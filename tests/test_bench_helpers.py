@@ -55,3 +55,24 @@ def test_roofline_ridge_separates_the_workloads():
     kb = bench.kernel_bytes(s, np.full(s.E, s.T * s.k // s.E))
     kf = bench.kernel_flops(s)
     assert kf["wgrad_gate_up"] / kb["wgrad_gate_up"] > ridge
+
+
+def test_counter_traffic_is_reported_only_for_the_sources_it_was_measured_on(tmp_path, monkeypatch):
+    """The roofline entry's counter bytes come from a profiles/ record that
+    carries the hash of the HIP sources it was taken on; a record of other
+    sources is stale and gives no bytes."""
+    import json
+
+    from mixture_experts_layer_dispatch_amd.prof_summary import sources_sha256
+
+    (tmp_path / "profiles").mkdir()
+    rec = {"sources_sha256": sources_sha256(), "kernels": {
+        "k_gemm_gate_up": {"grid": 1, "read_bytes": 100, "write_bytes": 20, "avg_us": 1.0}}}
+    (tmp_path / "profiles" / "traffic_w.json").write_text(json.dumps(rec))
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    assert bench.counter_traffic("w", "gemm_gate_up") == (120, "measured")
+    assert bench.counter_traffic("w", "gemm_down") == (None, "absent")
+    assert bench.counter_traffic("other", "gemm_gate_up") == (None, "absent")
+    rec["sources_sha256"] = "0" * 64
+    (tmp_path / "profiles" / "traffic_w.json").write_text(json.dumps(rec))
+    assert bench.counter_traffic("w", "gemm_gate_up") == (None, "stale")

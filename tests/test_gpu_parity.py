@@ -186,6 +186,7 @@ def test_bitwise_determinism_and_grouping_independence():
     g1 = {k: v.clone() for k, v in case.grads.items()}
     dw1 = case.dw.clone()
     for _ in range(2):
+        case.poison_outputs()
         case.schedule()
         case.forward()
         case.backward()
