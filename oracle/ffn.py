@@ -22,14 +22,23 @@ Backward, with dy_t the upstream gradient:
   d_logit[t, idx[t, j]] = w_j (dw_j - sum_i w_i dw_i); zero for unselected experts.
 
 MXFP8 mode quantises each GEMM operand along that GEMM's reduction axis
-(oracle.mx) before float64 arithmetic:
+(oracle.mx) before float64 arithmetic.  Every product of the layer goes
+through mm(A, B, mx) = Q(A along its last axis) @ Q(B along its first axis),
+so the axis of each operand is the contraction axis by construction:
   forward:   x along H, W_gate / W_up rows along H; h along I, W_down rows along I.
   backward:  dy along H and W_down along H (for W_down^T dy); dg, du along I and
              W_gate, W_up along I (for the input gradient); for the weight
              gradients, whose reduction runs over an expert's rows, the row
              operands in blocks of 32 consecutive rows of the expert's group
              (ascending slot order, one group per macrobatch, last block
-             zero-padded).
+             zero-padded); the shared expert's group in a macrobatch is that
+             macrobatch's tokens.
+Pins of the MXFP8 mode (tests/test_oracle_mx.py): mm's two axes (operands
+exact along the contraction axis only); each forward operand's axis (x, h,
+W_gate / W_up, W_down: the MXFP8 layer equals the exact layer on operands
+exact along the intended axis and lossy along the other); the backward's
+dy, dg / du and W_down^T axes (dx and dw); the 32-row blocks per macrobatch
+group (a two-macrobatch stream whose blocks would straddle the boundary).
 """
 from __future__ import annotations
 
@@ -42,8 +51,14 @@ def _f64(a):
     return np.asarray(a, dtype=np.float64)
 
 
-def _q(a, axis, mx):
-    return mx_roundtrip(a, axis) if mx else a
+def mm(A, B, mx=False):
+    """A [.., K] @ B [K, ..]; in MXFP8 mode both operands are first quantised
+    along K, the contraction axis (A along its last axis, B along its first)."""
+    A, B = _f64(A), _f64(B)
+    if mx:
+        A = mx_roundtrip(A, -1)
+        B = mx_roundtrip(B, 0)
+    return A @ B
 
 
 def sigmoid(g):
@@ -66,11 +81,10 @@ def swiglu_grad(g, u, dh):
 def expert_forward(X, wg, wu, wd, mx=False):
     """One expert's FFN on rows X [n, H]: returns g, u, h [n, I] and o [n, H]."""
     X, wg, wu, wd = _f64(X), _f64(wg), _f64(wu), _f64(wd)
-    Xq = _q(X, 1, mx)
-    g = Xq @ _q(wg, 1, mx).T
-    u = Xq @ _q(wu, 1, mx).T
+    g = mm(X, wg.T, mx)
+    u = mm(X, wu.T, mx)
     h = swiglu(g, u)
-    o = _q(h, 1, mx) @ _q(wd, 1, mx).T
+    o = mm(h, wd.T, mx)
     return g, u, h, o
 
 
@@ -106,12 +120,19 @@ def forward(x, wg, wu, wd, idx, w, shared=None, tokens=None, mx=False):
     return {"y": y, "g": g, "u": u, "h": h, "o": o, "tokens": tokens}
 
 
-def _wgrad(A, B, mx):
-    """sum over rows r of A[r] (outer) B[r]: A [n, P], B [n, Q] -> [P, Q]."""
-    if mx:
-        A = mx_roundtrip(A, 0)
-        B = mx_roundtrip(B, 0)
-    return A.T @ B
+def _wgrad(A, B, mx, groups=None):
+    """sum over rows r of A[r] (outer) B[r]: A [n, P], B [n, Q] -> [P, Q];
+    the reduction runs over the rows.  groups: row-index arrays (one per
+    macrobatch) summed separately, so that MXFP8 blocks of 32 rows never span
+    two macrobatches; the partial sums are added in the given order."""
+    A, B = _f64(A), _f64(B)
+    if groups is None:
+        groups = [np.arange(A.shape[0])]
+    acc = np.zeros((A.shape[1], B.shape[1]))
+    for rows in groups:
+        if len(rows):
+            acc = acc + mm(A[rows].T, B[rows], mx)
+    return acc
 
 
 def backward(x, wg, wu, wd, idx, w, dy, shared=None, mx=False, sched=None,
@@ -155,23 +176,32 @@ def backward(x, wg, wu, wd, idx, w, dy, shared=None, mx=False, sched=None,
     for e in np.unique(sel):
         ti, jj = np.nonzero(sel == e)
         wge, wue, wde = _f64(wg[e]), _f64(wu[e]), _f64(wd[e])
-        a = _q(DY[ti], 1, mx) @ _q(wde, 0, mx)          # W_down^T dy, per row
+        a = mm(DY[ti], wde, mx)                         # W_down^T dy, per row
         dw_fused[ti, jj] = np.sum(a * fw["h"][ti, jj], axis=1)
         dh = wf[tokens[ti], jj][:, None] * a
         dg, du = swiglu_grad(fw["g"][ti, jj], fw["u"][ti, jj], dh)
-        dXd_slot[ti, jj] = _q(dg, 1, mx) @ _q(wge, 0, mx) + _q(du, 1, mx) @ _q(wue, 0, mx)
+        dXd_slot[ti, jj] = mm(dg, wge, mx) + mm(du, wue, mx)
     # reverse-dispatch: shared term first, then slots j = 0..k-1
     dx = np.zeros((n, H))
     if shared is not None:
         sg, su, sd = (_f64(a) for a in shared)
         g, u, h, _ = expert_forward(X, sg, su, sd, mx)
-        a = _q(DY, 1, mx) @ _q(sd, 0, mx)
+        a = mm(DY, sd, mx)
         dgs, dus = swiglu_grad(g, u, a)
-        dx = dx + _q(dgs, 1, mx) @ _q(sg, 0, mx) + _q(dus, 1, mx) @ _q(su, 0, mx)
+        dx = dx + mm(dgs, sg, mx) + mm(dus, su, mx)
         if all_tokens:
-            out["dW_sd"] = _wgrad(DY, h, mx)
-            out["dW_sg"] = _wgrad(dgs, X, mx)
-            out["dW_su"] = _wgrad(dus, X, mx)
+            # the shared expert's group in macrobatch m is that macrobatch's
+            # tokens; the partial sums are added in the backward's order
+            # (macrobatches in reverse)
+            groups = None
+            if mx:
+                if sched is None:
+                    raise ValueError("MXFP8 weight gradients need the schedule")
+                M = sched["macro_rows"] // k
+                groups = [np.arange(m * M, (m + 1) * M) for m in range(sched["n_macro"])][::-1]
+            out["dW_sd"] = _wgrad(DY, h, mx, groups)
+            out["dW_sg"] = _wgrad(dgs, X, mx, groups)
+            out["dW_su"] = _wgrad(dus, X, mx, groups)
     for j in range(k):
         dx = dx + dXd_slot[:, j]
     # The router-weight gradient is computed inside the SwiGLU backward, from
@@ -197,7 +227,7 @@ def backward(x, wg, wu, wd, idx, w, dy, shared=None, mx=False, sched=None,
             if sched is None:
                 raise ValueError("MXFP8 weight gradients need the schedule")
             Sm = sched["macro_rows"]
-            groups = [slots[(slots // Sm) == m] for m in range(sched["n_macro"])]
+            groups = [slots[(slots // Sm) == m] for m in range(sched["n_macro"])][::-1]
         wge, wue, wde = _f64(wg[e]), _f64(wu[e]), _f64(wd[e])
         accg = np.zeros(wge.shape); accu = np.zeros(wue.shape); accd = np.zeros(wde.shape)
         for sl in groups:
@@ -207,7 +237,7 @@ def backward(x, wg, wu, wd, idx, w, dy, shared=None, mx=False, sched=None,
             Xe = _f64(np.asarray(x)[t])
             DYe = _f64(np.asarray(dy)[t])
             ge, ue, he, _ = expert_forward(Xe, wge, wue, wde, mx)
-            a = _q(DYe, 1, mx) @ _q(wde, 0, mx)
+            a = mm(DYe, wde, mx)
             ws = wf[t, j][:, None]
             dge, due = swiglu_grad(ge, ue, ws * a)
             accd = accd + _wgrad(ws * DYe, he, mx)

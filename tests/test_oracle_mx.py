@@ -2,6 +2,7 @@
 with torch's float8 conversions on in-range values, round-trip exactness,
 the error bound, the quantisation axis, and an MXFP8 layer on exactly
 representable operands reducing to the exact layer."""
+import math
 import os
 
 import numpy as np
@@ -167,3 +168,187 @@ def test_mx_layer_is_close_but_not_equal_on_gaussian_operands():
     # and the output compounds five of them
     rel_rms = np.sqrt(np.mean((fm - fe) ** 2) / np.mean(fe ** 2))
     assert 0.02 < rel_rms < 0.12
+
+
+# ------------------------------------------------------------------ quantisation axes
+# Each MXFP8 operand is quantised along its GEMM's reduction axis (oracle.ffn.mm).
+# The pins below use operands that E4M3 blocks represent exactly along the
+# intended axis and lossily along the other (values 2^20 apart inside a block
+# of the wrong axis), so the MXFP8 layer equals the exact layer only if every
+# operand is quantised along the intended axis.  Each pin is run once more
+# with a planted mistake (an mm quantising an operand along the wrong axis)
+# to show that it would catch it.
+S20 = 2.0 ** 20
+
+
+def _mm_wrong_a(A, B, mx=False):
+    """planted mistake: the left operand quantised along its first axis"""
+    A, B = np.asarray(A, np.float64), np.asarray(B, np.float64)
+    if mx:
+        A, B = oracle.mx_roundtrip(A, 0), oracle.mx_roundtrip(B, 0)
+    return A @ B
+
+
+def _mm_wrong_b(A, B, mx=False):
+    """planted mistake: the right operand quantised along its last axis"""
+    A, B = np.asarray(A, np.float64), np.asarray(B, np.float64)
+    if mx:
+        A, B = oracle.mx_roundtrip(A, -1), oracle.mx_roundtrip(B, -1)
+    return A @ B
+
+
+def test_mm_quantises_both_operands_along_the_contraction_axis():
+    rng = np.random.default_rng(8)
+    grid = np.array([1.0, 1.25, 1.5, 1.75, -1.0, -1.5, 0.0])
+    A = rng.choice(grid, size=(8, 64)) * np.where(np.arange(8) % 2, S20, 1.0)[:, None]
+    B = rng.choice(grid, size=(64, 6)) * np.where(np.arange(6) % 2, S20, 1.0)[None, :]
+    np.testing.assert_array_equal(oracle.ffn.mm(A, B, mx=True), A @ B)     # exact along K
+    Ak = rng.choice(grid, size=(8, 64)) * np.where(np.arange(64) % 2, S20, 1.0)[None, :]
+    Bk = rng.choice(grid, size=(64, 6)) * np.where(np.arange(64) % 2, S20, 1.0)[:, None]
+    assert not np.array_equal(oracle.ffn.mm(Ak, B, mx=True), Ak @ B)      # lossy along K
+    assert not np.array_equal(oracle.ffn.mm(A, Bk, mx=True), A @ Bk)
+    # ragged K (40 = 32 + 8): brute force, block by block, element by element
+    A = rng.standard_normal((3, 40))
+    B = rng.standard_normal((40, 2))
+
+    def q_block(vals):
+        amax = max(abs(v) for v in vals)
+        s = -127 if amax == 0 else max(-127, min(127, math.frexp(amax)[1] - 1 - 8))
+        return [float(mx.e4m3_round(v / 2.0 ** s)) * 2.0 ** s for v in vals]
+
+    Aq = np.array([sum((q_block(list(A[r, b:b + 32])) for b in (0, 32)), []) for r in range(3)])
+    Bq = np.array([sum((q_block(list(B[b:b + 32, c])) for b in (0, 32)), []) for c in range(2)]).T
+    got = oracle.ffn.mm(A, B, mx=True)
+    for r in range(3):
+        for c in range(2):
+            want = sum(Aq[r, q] * Bq[q, c] for q in range(40))
+            assert abs(got[r, c] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+def _axis_case(kind, seed=5):
+    """The exactly representable layer of _mx_exact_layer with one operand
+    made exact along its intended axis only."""
+    x, wg, wu, wd, L, dy = _mx_exact_layer(seed)
+    H = x.shape[1]
+    rng = np.random.default_rng(9)
+    alt = lambda n: np.where(np.arange(n) % 2, S20, 1.0)
+    if kind == "x_rows":           # token rows 2^20 apart: x along H, and h along I
+        x = x * alt(x.shape[0])[:, None]
+    elif kind == "wgu_rows":       # W_gate rows 2^20 apart (W_up rows the inverse): along H
+        f = alt(wg.shape[1])[None, :, None]
+        wg, wu = wg * f, wu / f
+    elif kind == "wd_rows":        # W_down rows 2^20 apart: the forward's W_down along I
+        wd = wd * alt(wd.shape[1])[None, :, None]
+    elif kind == "dy_rows":        # dy rows 2^20 apart: dy along H, then dg, du along I
+        dy = dy * alt(dy.shape[0])[:, None]
+    elif kind == "wd_cols":        # W_down columns 2^20 apart: the dgrad's W_down along H
+        wd = wd * alt(wd.shape[2])[None, None, :]
+    elif kind == "wgu_tail":       # tiny W_gate / W_up entries beside 40..64 in one H block,
+        x[:, 1:32] = 0             # where x is zero: the input gradient's weights along I
+        wg[:, :, 1:32] = rng.choice([-1.0, 0.0, 1.0], size=wg[:, :, 1:32].shape) / S20
+        wu[:, :, 1:32] = rng.choice([-1.0, 0.0, 1.0], size=wu[:, :, 1:32].shape) / S20
+    elif kind == "dy_cols":        # dy columns 2^20 apart: w * dy along the rows (dW_down)
+        dy = dy * alt(H)[None, :]
+    elif kind == "x_cols_tail":    # x columns 2^20 apart where the weights are zero: x along rows
+        wg[:, :, H // 2:] = 0
+        wu[:, :, H // 2:] = 0
+        x[:, H // 2:] = rng.choice([-1.0, 0.0, 1.0], size=x[:, H // 2:].shape) * alt(H // 2)
+    elif kind == "wu_rows":        # W_up rows 2^20 apart: dg and h along the rows
+        wu = wu * alt(wu.shape[1])[None, :, None]
+    return x, wg, wu, wd, L, dy
+
+
+def _axis_outputs(kind):
+    x, wg, wu, wd, L, dy = _axis_case(kind)
+    idx, w = oracle.route(L, 1)
+    sched = oracle.schedule(idx, 2)
+    out = {}
+    for mode in (False, True):
+        f = oracle.forward(x, wg, wu, wd, idx, w, mx=mode)
+        b = oracle.backward(x, wg, wu, wd, idx, w, dy, mx=mode, sched=sched)
+        out[mode] = {"y": f["y"], "dx": b["dx"], "dw": b["dw"],
+                     "dWg": np.stack([b["dWg"][e] for e in sorted(b["dWg"])]),
+                     "dWu": np.stack([b["dWu"][e] for e in sorted(b["dWu"])]),
+                     "dWd": np.stack([b["dWd"][e] for e in sorted(b["dWd"])])}
+    return out
+
+
+# kind: (outputs that the MXFP8 layer must give exactly, the planted mistake
+# that breaks them, and which of them it breaks)
+AXIS_PINS = {
+    "x_rows": (("y", "dx", "dw"), _mm_wrong_a, ("y",)),
+    "wgu_rows": (("y",), _mm_wrong_b, ("y",)),
+    "wd_rows": (("y",), _mm_wrong_b, ("y",)),
+    "dy_rows": (("dx", "dw"), _mm_wrong_a, ("dx", "dw")),
+    "wd_cols": (("dw",), _mm_wrong_b, ("dw",)),
+    "wgu_tail": (("y", "dx"), _mm_wrong_b, ("dx",)),
+    "dy_cols": (("dWd",), _mm_wrong_a, ("dWd",)),
+    "x_cols_tail": (("y", "dx", "dWg", "dWu"), _mm_wrong_b, ("dWg", "dWu")),
+    "wu_rows": (("dw", "dWg", "dWu", "dWd"), _mm_wrong_a, ("dWg",)),
+}
+
+
+@pytest.mark.parametrize("kind", list(AXIS_PINS))
+def test_mx_layer_quantises_each_operand_along_its_reduction_axis(kind, monkeypatch):
+    exact_outputs, planted, broken = AXIS_PINS[kind]
+    out = _axis_outputs(kind)
+    for name in exact_outputs:
+        np.testing.assert_array_equal(out[True][name], out[False][name], err_msg=f"{kind}: {name}")
+    monkeypatch.setattr(oracle.ffn, "mm", planted)
+    bad = _axis_outputs(kind)
+    for name in broken:
+        assert not np.array_equal(bad[True][name], bad[False][name]), f"{kind}: {name} misses the mistake"
+
+
+def _straddle_case(seed=7, T=96, M=48, H=64, I=32):
+    """One routed expert (k = 1) and a shared expert over two macrobatches of
+    48 tokens.  Tokens 32..47 are 2^20 times larger than the rest, so the
+    weight-gradient operands (rows of x, dg, du, h) are exact in 32-row blocks
+    of each macrobatch's group ([0, 32), [32, 48) | [48, 80), [80, 96)) and
+    lossy in blocks that cross the boundary ([32, 64))."""
+    rng = np.random.default_rng(seed)
+
+    def weights():
+        wg = np.zeros((I, H))
+        wg[:, 0] = rng.choice([40.0, 48.0, 56.0, 64.0], size=I)
+        wu = np.zeros((I, H))
+        wd = np.zeros((H, I))
+        for i in range(I):
+            wu[i, rng.choice(np.arange(1, H), size=2, replace=False)] = rng.choice([-1.0, 1.0], size=2)
+            wd[rng.choice(np.arange(H), size=2, replace=False), i] = rng.choice([-1.0, 1.0], size=2)
+        return wg, wu, wd
+
+    x = rng.integers(-1, 2, (T, H)).astype(np.float64)
+    x[:, 0] = 1.0
+    scale = np.ones(T)
+    scale[32:48] = S20
+    x = x * scale[:, None]
+    wg, wu, wd = weights()
+    shared = weights()
+    dy = rng.integers(-1, 2, (T, H)).astype(np.float64)
+    L = np.zeros((T, 1), np.float32)
+    return x, wg[None], wu[None], wd[None], shared, L, dy, M
+
+
+def test_mx_weight_gradients_block_rows_per_macrobatch_group():
+    x, wg, wu, wd, sh, L, dy, M = _straddle_case()
+    idx, w = oracle.route(L, 1)
+    ex = oracle.backward(x, wg, wu, wd, idx, w, dy, shared=sh)
+    fe = oracle.forward(x, wg, wu, wd, idx, w, shared=sh)["y"]
+    fm = oracle.forward(x, wg, wu, wd, idx, w, shared=sh, mx=True)["y"]
+    np.testing.assert_array_equal(fm, fe)
+    two = oracle.schedule(idx, 1, macrobatch=M)
+    bm = oracle.backward(x, wg, wu, wd, idx, w, dy, shared=sh, mx=True, sched=two)
+    for n in ("dx", "dw"):
+        np.testing.assert_array_equal(bm[n], ex[n], err_msg=n)
+    for n in ("dWg", "dWu", "dWd"):
+        np.testing.assert_array_equal(bm[n][0], ex[n][0], err_msg=n)
+    for n in ("dW_sg", "dW_su", "dW_sd"):
+        np.testing.assert_array_equal(bm[n], ex[n], err_msg=n)
+    # planted mistake: the same stream blocked as if it were one macrobatch
+    one = oracle.schedule(idx, 1)
+    bw = oracle.backward(x, wg, wu, wd, idx, w, dy, shared=sh, mx=True, sched=one)
+    for n in ("dWg", "dWu", "dWd"):
+        assert not np.array_equal(bw[n][0], ex[n][0]), n
+    for n in ("dW_sg", "dW_su", "dW_sd"):
+        assert not np.array_equal(bw[n], ex[n]), n
