@@ -116,26 +116,26 @@ def kernel_bytes(shape, counts: np.ndarray) -> dict:
     q = 1 + 1 / 32                      # an MXFP8 code and its share of a scale byte
     return {
         "topk_route": T * E * 4 + S * 8,
-        "dispatch": T * H * 2 + S * H * 2,
-        "gemm_gate_up": w_gu + S * H * 2 + 3 * S * I * 2,
-        "gemm_down": w_d + S * I * 2 + S * H * 2,
-        "combine": S * H * 2 + T * H * 2 + S * 8,
+        # the dispatch is fused into the gate/up GEMM's loads: x is read once
+        # (a token's k rows are re-read from cache), g, u, h written
+        "gemm_gate_up": w_gu + T * H * 2 + 3 * S * I * 2,
+        "gemm_down": w_d + S * I * 2 + S * H * 2 + S * 8,
+        "combine": S * H * 2 + T * H * 2 + S * 4,
         "gemm_down_dgrad": w_d + T * H * 2 + 2 * S * I * 2 + 3 * S * I * 2 + S * P * 4,
         "gemm_gu_dgrad": w_gu + S * 2 * I * 2 + S * H * 2,
         "wgrad_down": E * H * I * 2 + T * H * 2 + S * I * 2,
         "wgrad_gate_up": E * 2 * I * H * 2 + T * H * 2 + S * 2 * I * 2,
         "rd_reduce": S * H * 2 + T * H * 2,
         "softmax_bwd": S * P * 4 + T * E * 4 + S * 12,
-        # MXFP8 leg
-        "dispatch_mx": T * H * 2 + S * H * q,
-        "gemm_gate_up_mx": int(w_gu / 2 * q + S * H * q + 2 * S * I * 4 + S * I * q),
-        "gemm_down_mx": int(w_d / 2 * q + S * I * q + S * H * 2),
+        # MXFP8 leg (x quantised once per token by mx_quant_rows, gathered on load)
+        "gemm_gate_up_mx": int(w_gu / 2 * q + T * H * q + 2 * S * I * 4 + S * I * q),
+        "gemm_down_mx": int(w_d / 2 * q + S * I * q + S * H * 2 + S * 8),
         "gemm_down_dgrad_mx": int(w_d / 2 * q + T * H * q + 4 * S * I * 4 + S * I * 4
                                   + 2 * S * I * q + S * P * 4),
         "gemm_gu_dgrad_mx": int(w_gu / 2 * q + 2 * S * I * q + S * H * 2),
         "wgrad_down_mx": int(E * H * I * 2 + (H + I) * S * q),
         "wgrad_gate_up_mx": int(E * 2 * I * H * 2 + (2 * I + H) * S * q),
-        "mx_quant_rows": int(T * H * 2 + T * H * q),
+        "mx_quant_rows": int(T * H * 2 + T * H * q),       # x (forward) and dy (backward)
         "mx_qt_wdy": int(T * H * 2 + S * H * q),
         "mx_qt_x": int(T * H * 2 + S * H * q),
         "mx_qt_f32": int((3 * S * I * 4 + 3 * S * I * q) / 2),   # mean of its two launches

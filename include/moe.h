@@ -86,8 +86,22 @@ typedef struct moe_config {
     int32_t minibatch;     /* tokens per minibatch (fill granularity); 0 = macrobatch */
     int64_t capacity_rows; /* ring-buffer rows; 0 = the minimum (see moe_ring_rows)   */
     int32_t precision;     /* moe_precision                                           */
-    int32_t reserved;      /* must be 0                                               */
+    int32_t flags;         /* MOE_FLAG_* bits; 0 = none                               */
 } moe_config;
+
+/* moe_config.flags.
+ * MOE_FLAG_RECOMPUTE: nothing but the schedule is saved for the backward
+ *   (moe_saved is neither read nor written and may be NULL).  The backward
+ *   walks macrobatches in reverse ([AREX] second decision: the reverse walk
+ *   keeps the recomputation of forward activations small): the last
+ *   macrobatch's gate and up projections are still in the workspace, where
+ *   the forward left them, and every earlier macrobatch's are recomputed from
+ *   x before its SwiGLU backward.  So moe_backward must be given the
+ *   workspace of the moe_forward of the same batch, unchanged in between.
+ *   Costs one gate/up GEMM per macrobatch but the last; saves the 4*S*I bytes
+ *   (bf16) or 8*S*I bytes (MXFP8) of moe_saved, S = T*k (plus T*I*4 or T*I*8
+ *   for a shared expert), for 4*M*k*I (or 8*M*k*I) bytes of workspace. */
+#define MOE_FLAG_RECOMPUTE 1
 
 /* The schedule table ([AREX] first decision): written by moe_schedule, read by
  * moe_forward and moe_backward.  n_macro = T / macrobatch,
@@ -179,6 +193,19 @@ MOE_API moe_status moe_ring_rows(const moe_config* cfg, int64_t* rows);
  * moe_backward need (one workspace serves all three; it holds the ring
  * buffer and per-call scratch, nothing that must survive between calls). */
 MOE_API moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
+
+/* Host-only diagnostics: byte offset and size, inside the workspace of `cfg`,
+ * of a named array the MXFP8 path keeps there (tests read them to compare
+ * the activation quantisation bit for bit):
+ *   "x_codes"  [T, H] E4M3 codes of x along H, written by moe_forward (the
+ *              dispatch gathers routed rows from them, [ALPHA] 一: MXFP8
+ *              activation quantisation inside the forward);
+ *   "x_scales" [T, H/32] their E8M0 scales, row-major;
+ *   "dy_codes", "dy_scales": the same of dy, written by moe_backward (the
+ *              reverse-combine gathers them).
+ * MOE_ERR_INVALID_ARG for other names or a BF16 config. */
+MOE_API moe_status moe_workspace_region(const moe_config* cfg, const char* name, size_t* offset,
+                                        size_t* bytes);
 
 /* Host-only: 1 if the current HIP device is gfx950, else 0 (also 0 when no
  * device is visible).  The library refuses other devices, as the reference

@@ -31,8 +31,10 @@ EXPORTED = [
     "moe_status_string", "moe_validate_config", "moe_ring_rows", "moe_workspace_size",
     "moe_device_supported", "moe_schedule", "moe_forward", "moe_backward",
     "moe_check_device_error", "moe_quantize_weights_mxfp8", "moe_profile_enable", "moe_profile_collect", "moe_profile_query",
-    "moe_profile_names", "moe_profile_reset",
+    "moe_profile_names", "moe_profile_reset", "moe_workspace_region",
 ]
+
+FLAG_RECOMPUTE = 1
 
 
 class MoEError(RuntimeError):
@@ -46,7 +48,7 @@ class moe_config(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("macrobatch", ctypes.c_int32), ("minibatch", ctypes.c_int32),
                 ("capacity_rows", ctypes.c_int64), ("precision", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32)]
 
 
 class moe_sched(ctypes.Structure):
@@ -113,6 +115,8 @@ def lib() -> ctypes.CDLL:
                                         ctypes.POINTER(ctypes.c_double)]
         L.moe_profile_names.argtypes = [ctypes.c_char_p, ctypes.c_size_t]
         L.moe_profile_reset.argtypes = []
+        L.moe_workspace_region.argtypes = [cfgp, ctypes.c_char_p, ctypes.POINTER(ctypes.c_size_t),
+                                           ctypes.POINTER(ctypes.c_size_t)]
         for name in EXPORTED:
             if name != "moe_status_string":
                 getattr(L, name).restype = ctypes.c_int
@@ -151,10 +155,12 @@ class Config:
     minibatch: int = 0
     capacity_rows: int = 0
     precision: int = PREC_BF16
+    recompute: bool = False
 
     def c(self) -> moe_config:
         return moe_config(self.T, self.H, self.I, self.E, self.k, self.n_shared, self.macrobatch,
-                          self.minibatch, self.capacity_rows, self.precision, 0)
+                          self.minibatch, self.capacity_rows, self.precision,
+                          FLAG_RECOMPUTE if self.recompute else 0)
 
     @property
     def M(self) -> int:
@@ -215,8 +221,20 @@ def alloc_schedule(cfg: Config, device="cuda") -> dict:
     }
 
 
+def workspace_region(cfg: Config, name: str) -> tuple:
+    """(byte offset, bytes) of a named array inside the workspace (MXFP8:
+    "x_codes", "x_scales", "dy_codes", "dy_scales")."""
+    off, n = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().moe_workspace_region(ctypes.byref(cfg.c()), name.encode(), ctypes.byref(off),
+                                      ctypes.byref(n)), "moe_workspace_region")
+    return off.value, n.value
+
+
 def alloc_saved(cfg: Config, device="cuda") -> dict:
-    """g, u (and the shared expert's): bf16 in BF16 mode, fp32 in MXFP8 mode."""
+    """g, u (and the shared expert's): bf16 in BF16 mode, fp32 in MXFP8 mode;
+    nothing in recompute mode."""
+    if cfg.recompute:
+        return {}
     dt = torch.float32 if cfg.precision == PREC_MXFP8 else torch.bfloat16
     bf = dict(dtype=dt, device=device)
     out = {"g": torch.empty(cfg.S, cfg.I, **bf), "u": torch.empty(cfg.S, cfg.I, **bf)}
@@ -256,7 +274,8 @@ def _weights(w: dict):
     return st, mx
 
 
-def _saved(s: dict) -> moe_saved:
+def _saved(s) -> moe_saved:
+    s = s or {}
     return moe_saved(*[(s[n].data_ptr() if s.get(n) is not None else None)
                        for n, _ in moe_saved._fields_])
 
@@ -345,6 +364,10 @@ def _spec_weights_mx(cfg: Config, q, forward: bool = True, transposed: bool = Tr
 
 
 def _spec_saved(cfg: Config, s: dict):
+    if cfg.recompute:
+        return []                  # nothing is saved: the backward recomputes g, u
+    if s is None:
+        raise ValueError("saved: missing (only recompute mode saves nothing)")
     dt = torch.float32 if cfg.precision == PREC_MXFP8 else torch.bfloat16
     out = [("saved['g']", s.get("g"), (cfg.S, cfg.I), dt),
            ("saved['u']", s.get("u"), (cfg.S, cfg.I), dt)]

@@ -23,7 +23,7 @@ struct Geom {
     int T, H, I, E, k, M, mb, n_macro, n_mini, Sm, Smb, S, P;
     int64_t ring_rows;
     int halves;
-    bool shared, mx;
+    bool shared, mx, recompute;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -31,12 +31,13 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 struct Layout {
     size_t err, hist, base, tile_off, deep, ring, ring_half, sh, wacc, total;
     // offsets inside one ring half (bytes)
-    size_t f_xd, f_h, f_o;            // forward
-    size_t f_xs, f_hs;                // MXFP8 forward: scales after the codes (codes at f_xd, f_h)
+    size_t f_h, f_o;                  // forward
+    size_t f_hs;                      // MXFP8 forward: h scales after the codes (codes at f_h)
     size_t b_dgu, b_hw, b_dx, b_part; // backward
     // offsets inside the shared-expert region
     size_t s_h, s_o, s_dgu, s_hw, s_dx;
-    size_t s_xq, s_xs, s_hq, s_hs;    // MXFP8 shared expert
+    size_t s_hq, s_hs;                // MXFP8 shared expert
+    size_t xq, xs;                    // MXFP8 forward: x codes / scales [T, H] (quantised once)
     // MXFP8 backward
     size_t dyq, dys;                  // dy codes / scales [T, H]
     size_t x_dgu32, x_h32, x_dguq, x_dgus, x_dx, x_part;    // inside a ring half
@@ -44,6 +45,7 @@ struct Layout {
     int64_t kcap;
     size_t s_dgu32, s_h32, s_dguq, s_dgus, s_dxm;          // shared expert
     size_t wacc_g, wacc_u, wacc_d, wacc_sg, wacc_su, wacc_sd;
+    size_t rc_g, rc_u, rc_sg, rc_su;  // recompute mode: one macrobatch's g, u (and the shared expert's)
 };
 
 moe_status make_geom(const moe_config* c, Geom& g) {
@@ -53,7 +55,8 @@ moe_status make_geom(const moe_config* c, Geom& g) {
         return MOE_ERR_INVALID_ARG;
     if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_INVALID_ARG;
     if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
-    if (c->reserved != 0 || c->macrobatch < 0 || c->minibatch < 0 || c->capacity_rows < 0)
+    if ((c->flags & ~MOE_FLAG_RECOMPUTE) != 0 || c->macrobatch < 0 || c->minibatch < 0 ||
+        c->capacity_rows < 0)
         return MOE_ERR_INVALID_ARG;
     if (c->H > (1 << 16) || c->I > (1 << 16)) return MOE_ERR_INVALID_ARG;
     const int64_t S = (int64_t)c->T * c->k;
@@ -71,6 +74,7 @@ moe_status make_geom(const moe_config* c, Geom& g) {
     g.P = dgrad_col_tiles(g.I);
     g.shared = c->n_shared == 1;
     g.mx = c->precision == MOE_PREC_MXFP8;
+    g.recompute = (c->flags & MOE_FLAG_RECOMPUTE) != 0;
     if (c->capacity_rows) {
         if (c->capacity_rows < g.Sm) return MOE_ERR_CAPACITY;
         g.ring_rows = c->capacity_rows;
@@ -97,12 +101,12 @@ Layout make_layout(const Geom& g) {
     L.tile_off = take((size_t)g.n_macro * (g.E + 1) * 4);
     L.deep = take((size_t)(g.E + 1) * 4);        // deep weight-gradient groups of one macrobatch
     const size_t Sm = (size_t)g.Sm, H = g.H, I = g.I;
-    L.f_xd = 0;
-    L.f_h = align_up(L.f_xd + Sm * H * 2, 256);
+    // the forward's ring rows: h and the weighted o of the macrobatch (the
+    // dispatched x rows are gathered by the gate/up GEMM's loads, never stored)
+    L.f_h = 0;
     L.f_o = align_up(L.f_h + Sm * I * 2, 256);
     const size_t fwd_end = align_up(L.f_o + Sm * H * 2, 256);
-    // MXFP8 codes take one byte, so codes + scales fit in the bf16 slots
-    L.f_xs = align_up(L.f_xd + Sm * H, 256);
+    // MXFP8 codes take one byte, so codes + scales fit in the bf16 slot
     L.f_hs = align_up(L.f_h + Sm * I, 256);
     L.b_dgu = 0;
     L.b_hw = align_up(L.b_dgu + Sm * 2 * I * 2, 256);
@@ -122,6 +126,8 @@ Layout make_layout(const Geom& g) {
     }
     L.ring = take(L.ring_half * g.halves);
     if (g.mx) {
+        L.xq = take((size_t)g.T * H);
+        L.xs = take((size_t)g.T * H / 32);
         L.dyq = take((size_t)g.T * H);
         L.dys = take((size_t)g.T * H / 32);
         // transposed, row-quantised operands of the weight gradients (one macrobatch,
@@ -143,9 +149,7 @@ Layout make_layout(const Geom& g) {
     if (g.shared) {
         L.s_h = 0;
         L.s_o = align_up(M * I * 2, 256);
-        L.s_xq = align_up(L.s_o + M * H * 2, 256);
-        L.s_xs = align_up(L.s_xq + M * H, 256);
-        L.s_hq = align_up(L.s_xs + M * H / 32, 256);
+        L.s_hq = align_up(L.s_o + M * H * 2, 256);
         L.s_hs = align_up(L.s_hq + M * I, 256);
         const size_t fe = align_up(L.s_hs + M * I / 32, 256);
         L.s_dgu = 0;
@@ -162,6 +166,15 @@ Layout make_layout(const Geom& g) {
             if (me > be) be = me;
         }
         L.sh = take(fe > be ? fe : be);
+    }
+    if (g.recompute) {
+        const size_t es = g.mx ? 4 : 2;                 // fp32 in MXFP8 mode, as the saved ones
+        L.rc_g = take(Sm * I * es);
+        L.rc_u = take(Sm * I * es);
+        if (g.shared) {
+            L.rc_sg = take(M * I * es);
+            L.rc_su = take(M * I * es);
+        }
     }
     if (g.n_macro > 1) {
         const size_t per = (size_t)g.E * I * H * 4;
@@ -224,6 +237,13 @@ bool sched_ok(const moe_sched* s) {
 
 bool bf16_ok(const void* p) { return p && aligned(p, 16); }
 
+// the saved activations: not used in recompute mode (saved may then be null)
+bool saved_ok(const Geom& g, const moe_saved* s) {
+    if (g.recompute) return true;
+    if (!s || !bf16_ok(s->g) || !bf16_ok(s->u)) return false;
+    return !g.shared || (bf16_ok(s->sg) && bf16_ok(s->su));
+}
+
 struct Ptrs {
     char* ws;
     const Layout* L;
@@ -233,20 +253,45 @@ struct Ptrs {
     float* wacc(size_t off) const { return (float*)(ws + L->wacc + off); }
 };
 
+// Where macrobatch m's gate and up projections are kept for the backward:
+// the caller's saved arrays (rows of the whole batch), or in recompute mode
+// the workspace's one-macrobatch buffers (local rows), which the forward
+// fills for the last macrobatch only and the backward refills for the others.
+struct GU {
+    void* g;
+    void* u;
+    int row0;
+};
 
-// MXFP8 forward: dispatch quantises each dispatched row along H, the gate/up
-// GEMM quantises h along I in its epilogue, the down GEMM writes bf16 o, and
-// the combine is the bf16 one.
+GU gu_routed(const Geom& g, const Layout& L, const Ptrs& P, const moe_saved* saved, int m, bool fwd) {
+    if (!g.recompute) return {saved->g, saved->u, m * g.Sm};
+    if (fwd && m != g.n_macro - 1) return {nullptr, nullptr, 0};
+    return {P.ws + L.rc_g, P.ws + L.rc_u, 0};
+}
+
+GU gu_shared(const Geom& g, const Layout& L, const Ptrs& P, const moe_saved* saved, int m, bool fwd) {
+    if (!g.recompute) return {saved->sg, saved->su, m * g.M};
+    if (fwd && m != g.n_macro - 1) return {nullptr, nullptr, 0};
+    return {P.ws + L.rc_sg, P.ws + L.rc_su, 0};
+}
+
+
+// MXFP8 forward: x is quantised along H once per token; the gate/up GEMM
+// gathers each routed row's codes by token on load (dispatch fused into the
+// operand loads) and quantises h along I in its epilogue; the down GEMM
+// writes each row scaled by its router weight; the combine sums a token's
+// rows in a fixed order.
 moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_sched* sched,
                       const void* x, const moe_weights* w, void* y, const moe_saved* saved,
                       hipStream_t st) {
     const moe_weights_mx* wq = w->mx;
     int32_t* err = P.err();
     const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
+    uint8_t* xq = (uint8_t*)(P.ws + L.xq);
+    uint8_t* xs = (uint8_t*)(P.ws + L.xs);
+    if (launch_mx_quant_rows(x, g.T, g.H, xq, xs, st)) return MOE_ERR_HIP;
     for (int m = 0; m < g.n_macro; ++m) {
         char* half = P.half(m, g.halves);
-        uint8_t* xq = (uint8_t*)(half + L.f_xd);
-        uint8_t* xs = (uint8_t*)(half + L.f_xs);
         uint8_t* hq = (uint8_t*)(half + L.f_h);
         uint8_t* hs = (uint8_t*)(half + L.f_hs);
         uint16_t* obuf = (uint16_t*)(half + L.f_o);
@@ -254,44 +299,36 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)(P.ws + L.tile_off) + (size_t)m * (g.E + 1);
         if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
-        for (int i = 0; i < g.n_mini; ++i) {
-            const int s0 = grow0 + i * g.Smb;
-            if (launch_dispatch_mx(x, g.H, sched->row_of_slot, s0, s0 + g.Smb, g.k, grow0, g.Sm, xq, xs,
-                                   err, st))
-                return MOE_ERR_HIP;
-        }
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
-        GemmGateUpMXArgs a1{grp, xq, xs, 0,
+        const GU keep = gu_routed(g, L, P, saved, m, true);
+        GemmGateUpMXArgs a1{grp, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
                             (const uint8_t*)wq->w_gate_q, (const uint8_t*)wq->w_gate_s,
                             (const uint8_t*)wq->w_up_q, (const uint8_t*)wq->w_up_s, g.H, g.I,
-                            (float*)saved->g, (float*)saved->u, grow0, hq, hs};
+                            (float*)keep.g, (float*)keep.u, keep.row0, hq, hs};
         if (launch_gemm_gate_up_mx(a1, st)) return MOE_ERR_HIP;
         GemmDownMXArgs a2{grp, hq, hs, (const uint8_t*)wq->w_down_q, (const uint8_t*)wq->w_down_s,
-                          g.H, g.I, obuf};
+                          g.H, g.I, obuf, {sched->topk_w, sched->slot_of_row, grow0, g.S}};
         if (launch_gemm_down_mx(a2, st)) return MOE_ERR_HIP;
         const uint16_t* sh_o = nullptr;
         if (g.shared) {
             char* sh = P.sh();
-            uint8_t* sxq = (uint8_t*)(sh + L.s_xq);
-            uint8_t* sxs = (uint8_t*)(sh + L.s_xs);
             uint8_t* shq = (uint8_t*)(sh + L.s_hq);
             uint8_t* shs = (uint8_t*)(sh + L.s_hs);
             uint16_t* so = (uint16_t*)(sh + L.s_o);
-            if (launch_mx_quant_rows((const uint16_t*)x + (size_t)t0 * g.H, g.M, g.H, sxq, sxs, st))
-                return MOE_ERR_HIP;
             GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
-            GemmGateUpMXArgs s1{dense, sxq, sxs, 0,
+            const GU skeep = gu_shared(g, L, P, saved, m, true);
+            GemmGateUpMXArgs s1{dense, xq, xs, t0, 0, nullptr, 0, g.k, g.S,
                                 (const uint8_t*)wq->s_gate_q, (const uint8_t*)wq->s_gate_s,
                                 (const uint8_t*)wq->s_up_q, (const uint8_t*)wq->s_up_s, g.H, g.I,
-                                (float*)saved->sg, (float*)saved->su, t0, shq, shs};
+                                (float*)skeep.g, (float*)skeep.u, skeep.row0, shq, shs};
             if (launch_gemm_gate_up_mx(s1, st)) return MOE_ERR_HIP;
             GemmDownMXArgs s2{dense, shq, shs, (const uint8_t*)wq->s_down_q,
-                              (const uint8_t*)wq->s_down_s, g.H, g.I, so};
+                              (const uint8_t*)wq->s_down_s, g.H, g.I, so, {nullptr, nullptr, 0, 0}};
             if (launch_gemm_down_mx(s2, st)) return MOE_ERR_HIP;
             sh_o = so;
         }
-        if (launch_combine(obuf, g.H, sched->row_of_slot, sched->topk_w, t0, t0 + g.M, g.k, grow0,
-                           g.Sm, sh_o, t0, y, err, st))
+        if (launch_combine(obuf, g.H, sched->row_of_slot, nullptr, t0, t0 + g.M, g.k, grow0, g.Sm,
+                           sh_o, t0, y, err, st))
             return MOE_ERR_HIP;
     }
     return MOE_OK;
@@ -314,6 +351,10 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     uint8_t* dyq = (uint8_t*)(ws + L.dyq);
     uint8_t* dys = (uint8_t*)(ws + L.dys);
     if (launch_mx_quant_rows(dy, g.T, g.H, dyq, dys, st)) return MOE_ERR_HIP;
+    uint8_t* xq = (uint8_t*)(ws + L.xq);
+    uint8_t* xs = (uint8_t*)(ws + L.xs);
+    if (g.recompute && g.n_macro > 1 && launch_mx_quant_rows(x, g.T, g.H, xq, xs, st))
+        return MOE_ERR_HIP;                     // the codes the recomputation gathers
     uint8_t* twdy = (uint8_t*)(ws + L.tr_wdy);
     uint8_t* twdys = (uint8_t*)(ws + L.tr_wdys);
     uint8_t* th = (uint8_t*)(ws + L.tr_h);
@@ -353,10 +394,20 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
         if (launch_tile_prefix(off, g.E, g.Sm, 32, blk, err, st)) return MOE_ERR_HIP;
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
+        const GU gu = gu_routed(g, L, P, saved, m, false);
+        if (g.recompute && m != g.n_macro - 1) {
+            // recompute this macrobatch's g, u (h codes go to scratch that the
+            // dgrad below overwrites)
+            GemmGateUpMXArgs r1{grp, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
+                                (const uint8_t*)wq->w_gate_q, (const uint8_t*)wq->w_gate_s,
+                                (const uint8_t*)wq->w_up_q, (const uint8_t*)wq->w_up_s, g.H, g.I,
+                                (float*)gu.g, (float*)gu.u, 0, dguq, dgus};
+            if (launch_gemm_gate_up_mx(r1, st)) return MOE_ERR_HIP;
+        }
         GemmDownDgradMXArgs b1{grp, dyq, dys, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
                                sched->topk_w, (const uint8_t*)wq->w_down_tq,
-                               (const uint8_t*)wq->w_down_ts, g.H, g.I, (const float*)saved->g,
-                               (const float*)saved->u, grow0, dgu32, h32, dguq, dgus, part, g.P};
+                               (const uint8_t*)wq->w_down_ts, g.H, g.I, (const float*)gu.g,
+                               (const float*)gu.u, gu.row0, dgu32, h32, dguq, dgus, part, g.P};
         if (launch_gemm_down_dgrad_mx(b1, st)) return MOE_ERR_HIP;
         GemmGuDgradMXArgs b2{grp, dguq, dgus, (const uint8_t*)wq->w_gate_tq,
                              (const uint8_t*)wq->w_gate_ts, (const uint8_t*)wq->w_up_tq,
@@ -374,9 +425,17 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
             uint8_t* sdguq = (uint8_t*)(sh + L.s_dguq);
             uint8_t* sdgus = (uint8_t*)(sh + L.s_dgus);
             uint16_t* sdx = (uint16_t*)(sh + L.s_dxm);
+            const GU sgu = gu_shared(g, L, P, saved, m, false);
+            if (g.recompute && m != g.n_macro - 1) {
+                GemmGateUpMXArgs r2{dense, xq, xs, t0, 0, nullptr, 0, g.k, g.S,
+                                    (const uint8_t*)wq->s_gate_q, (const uint8_t*)wq->s_gate_s,
+                                    (const uint8_t*)wq->s_up_q, (const uint8_t*)wq->s_up_s, g.H, g.I,
+                                    (float*)sgu.g, (float*)sgu.u, 0, sdguq, sdgus};
+                if (launch_gemm_gate_up_mx(r2, st)) return MOE_ERR_HIP;
+            }
             GemmDownDgradMXArgs c1{dense, dyq, dys, 0, t0, nullptr, 0, g.k, g.S, nullptr,
                                    (const uint8_t*)wq->s_down_tq, (const uint8_t*)wq->s_down_ts, g.H,
-                                   g.I, (const float*)saved->sg, (const float*)saved->su, t0, sdgu32,
+                                   g.I, (const float*)sgu.g, (const float*)sgu.u, sgu.row0, sdgu32,
                                    sh32, sdguq, sdgus, nullptr, g.P};
             if (launch_gemm_down_dgrad_mx(c1, st)) return MOE_ERR_HIP;
             GemmGuDgradMXArgs c2{dense, sdguq, sdgus, (const uint8_t*)wq->s_gate_tq,
@@ -471,6 +530,28 @@ moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes) {
 
 int moe_device_supported(void) { return device_ok() ? 1 : 0; }
 
+moe_status moe_workspace_region(const moe_config* cfg, const char* name, size_t* offset,
+                                size_t* bytes) {
+    Geom g;
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    if (!name || !offset || !bytes || !g.mx) return MOE_ERR_INVALID_ARG;
+    const Layout L = make_layout(g);
+    const size_t th = (size_t)g.T * g.H;
+    struct { const char* n; size_t off, len; } regions[] = {
+        {"x_codes", L.xq, th}, {"x_scales", L.xs, th / 32},
+        {"dy_codes", L.dyq, th}, {"dy_scales", L.dys, th / 32},
+    };
+    for (const auto& r : regions) {
+        if (std::strcmp(r.n, name) == 0) {
+            *offset = r.off;
+            *bytes = r.len;
+            return MOE_OK;
+        }
+    }
+    return MOE_ERR_INVALID_ARG;
+}
+
 moe_status moe_schedule(const moe_config* cfg, const float* logits, const moe_sched* sched,
                         void* workspace, size_t workspace_bytes, void* stream) {
     Geom g;
@@ -499,11 +580,10 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
     Layout L;
     moe_status s = common_checks(cfg, g, L, workspace, workspace_bytes);
     if (s != MOE_OK) return s;
-    if (!sched_ok(sched) || !bf16_ok(x) || !bf16_ok(y) || !w || !saved) return MOE_ERR_INVALID_ARG;
+    if (!sched_ok(sched) || !bf16_ok(x) || !bf16_ok(y) || !w) return MOE_ERR_INVALID_ARG;
     if (!bf16_ok(w->w_gate) || !bf16_ok(w->w_up) || !bf16_ok(w->w_down)) return MOE_ERR_INVALID_ARG;
-    if (!bf16_ok(saved->g) || !bf16_ok(saved->u)) return MOE_ERR_INVALID_ARG;
-    if (g.shared && (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down) ||
-                     !bf16_ok(saved->sg) || !bf16_ok(saved->su)))
+    if (!saved_ok(g, saved)) return MOE_ERR_INVALID_ARG;
+    if (g.shared && (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down)))
         return MOE_ERR_INVALID_ARG;
     const moe_weights_mx* wq = w->mx;
     if (g.mx) {
@@ -526,41 +606,41 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
     const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
     for (int m = 0; m < g.n_macro; ++m) {
         char* half = P.half(m, g.halves);
-        uint16_t* xd = (uint16_t*)(half + L.f_xd);
         uint16_t* hbuf = (uint16_t*)(half + L.f_h);
         uint16_t* obuf = (uint16_t*)(half + L.f_o);
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
         if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
-        // dispatch, one minibatch at a time, into this macrobatch's ring half
-        for (int i = 0; i < g.n_mini; ++i) {
-            const int s0 = grow0 + i * g.Smb;
-            if (launch_dispatch(x, g.H, sched->row_of_slot, s0, s0 + g.Smb, g.k, grow0, g.Sm, xd, err, st))
-                return MOE_ERR_HIP;
-        }
+        // dispatch fused into the gate/up GEMM: its operand loads gather each
+        // routed row from the row of its token
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
-        GemmGateUpArgs a1{grp, xd, 0, 0, sched->slot_of_row, grow0, g.k, g.S,
+        const GU keep = gu_routed(g, L, P, saved, m, true);
+        GemmGateUpArgs a1{grp, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
                           (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
-                          (uint16_t*)saved->g, (uint16_t*)saved->u, grow0, hbuf};
+                          (uint16_t*)keep.g, (uint16_t*)keep.u, keep.row0, hbuf};
         if (launch_gemm_gate_up(a1, st)) return MOE_ERR_HIP;
-        GemmDownArgs a2{grp, hbuf, (const uint16_t*)w->w_down, g.H, g.I, obuf};
+        GemmDownArgs a2{grp, hbuf, (const uint16_t*)w->w_down, g.H, g.I, obuf,
+                        {sched->topk_w, sched->slot_of_row, grow0, g.S}};
         if (launch_gemm_down(a2, st)) return MOE_ERR_HIP;
         const uint16_t* sh_o = nullptr;
         if (g.shared) {
             uint16_t* sh_h = (uint16_t*)(P.sh() + L.s_h);
             uint16_t* so = (uint16_t*)(P.sh() + L.s_o);
             GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
+            const GU skeep = gu_shared(g, L, P, saved, m, true);
             GemmGateUpArgs s1{dense, xb, 0, t0, nullptr, 0, g.k, g.S,
                               (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up, g.H, g.I,
-                              (uint16_t*)saved->sg, (uint16_t*)saved->su, t0, sh_h};
+                              (uint16_t*)skeep.g, (uint16_t*)skeep.u, skeep.row0, sh_h};
             if (launch_gemm_gate_up(s1, st)) return MOE_ERR_HIP;
-            GemmDownArgs s2{dense, sh_h, (const uint16_t*)w->s_down, g.H, g.I, so};
+            GemmDownArgs s2{dense, sh_h, (const uint16_t*)w->s_down, g.H, g.I, so, {nullptr, nullptr, 0, 0}};
             if (launch_gemm_down(s2, st)) return MOE_ERR_HIP;
             sh_o = so;
         }
-        if (launch_combine(obuf, g.H, sched->row_of_slot, sched->topk_w, t0, t0 + g.M, g.k, grow0,
-                           g.Sm, sh_o, t0, y, err, st))
+        // the router-weighted reduction: y_t = [shared] + sum_j (w o)_(t,j), in
+        // that fixed order (the rows already carry their weights)
+        if (launch_combine(obuf, g.H, sched->row_of_slot, nullptr, t0, t0 + g.M, g.k, grow0, g.Sm,
+                           sh_o, t0, y, err, st))
             return MOE_ERR_HIP;
     }
     return MOE_OK;
@@ -574,17 +654,15 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
     Layout L;
     moe_status s = common_checks(cfg, g, L, workspace, workspace_bytes);
     if (s != MOE_OK) return s;
-    if (!sched_ok(sched) || !saved || !w || !gr || !bf16_ok(x) || !bf16_ok(dy) || !bf16_ok(dx))
+    if (!sched_ok(sched) || !saved_ok(g, saved) || !w || !gr || !bf16_ok(x) || !bf16_ok(dy) ||
+        !bf16_ok(dx))
         return MOE_ERR_INVALID_ARG;
-    if (!bf16_ok(w->w_gate) || !bf16_ok(w->w_up) || !bf16_ok(w->w_down) || !bf16_ok(saved->g) ||
-        !bf16_ok(saved->u))
-        return MOE_ERR_INVALID_ARG;
+    if (!bf16_ok(w->w_gate) || !bf16_ok(w->w_up) || !bf16_ok(w->w_down)) return MOE_ERR_INVALID_ARG;
     if (!bf16_ok(gr->d_w_gate) || !bf16_ok(gr->d_w_up) || !bf16_ok(gr->d_w_down))
         return MOE_ERR_INVALID_ARG;
     if (!dw || !aligned(dw, 4) || (d_logits && !aligned(d_logits, 4))) return MOE_ERR_INVALID_ARG;
     if (g.shared && (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down) ||
-                     !bf16_ok(saved->sg) || !bf16_ok(saved->su) || !bf16_ok(gr->d_s_gate) ||
-                     !bf16_ok(gr->d_s_up) || !bf16_ok(gr->d_s_down)))
+                     !bf16_ok(gr->d_s_gate) || !bf16_ok(gr->d_s_up) || !bf16_ok(gr->d_s_down)))
         return MOE_ERR_INVALID_ARG;
     if (g.mx) {
         const moe_weights_mx* wq = w->mx;
@@ -620,10 +698,19 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
         if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
+        const GU gu = gu_routed(g, L, P, saved, m, false);
+        if (g.recompute && m != g.n_macro - 1) {
+            // recompute this macrobatch's g, u (h goes to the hw rows, which
+            // the dgrad below overwrites)
+            GemmGateUpArgs r1{grp, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
+                              (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
+                              (uint16_t*)gu.g, (uint16_t*)gu.u, 0, hw};
+            if (launch_gemm_gate_up(r1, st)) return MOE_ERR_HIP;
+        }
         // reverse-combine (dy gathered on load) + down dgrad + SwiGLU backward + dw partials
         GemmDownDgradArgs b1{grp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, sched->topk_w,
-                             (const uint16_t*)w->w_down, g.H, g.I, (const uint16_t*)saved->g,
-                             (const uint16_t*)saved->u, grow0, dgu, hw, part, g.P};
+                             (const uint16_t*)w->w_down, g.H, g.I, (const uint16_t*)gu.g,
+                             (const uint16_t*)gu.u, gu.row0, dgu, hw, part, g.P};
         if (launch_gemm_down_dgrad(b1, st)) return MOE_ERR_HIP;
         GemmGuDgradArgs b2{grp, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I, dxd};
         if (launch_gemm_gu_dgrad(b2, st)) return MOE_ERR_HIP;
@@ -636,9 +723,16 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         uint16_t* shw = g.shared ? (uint16_t*)(P.sh() + L.s_hw) : nullptr;
         if (g.shared) {
             uint16_t* sdx = (uint16_t*)(P.sh() + L.s_dx);
+            const GU sgu = gu_shared(g, L, P, saved, m, false);
+            if (g.recompute && m != g.n_macro - 1) {
+                GemmGateUpArgs r2{dense, xb, 0, t0, nullptr, 0, g.k, g.S,
+                                  (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up, g.H, g.I,
+                                  (uint16_t*)sgu.g, (uint16_t*)sgu.u, 0, shw};
+                if (launch_gemm_gate_up(r2, st)) return MOE_ERR_HIP;
+            }
             GemmDownDgradArgs c1{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, nullptr,
-                                 (const uint16_t*)w->s_down, g.H, g.I, (const uint16_t*)saved->sg,
-                                 (const uint16_t*)saved->su, t0, sdgu, shw, nullptr, g.P};
+                                 (const uint16_t*)w->s_down, g.H, g.I, (const uint16_t*)sgu.g,
+                                 (const uint16_t*)sgu.u, sgu.row0, sdgu, shw, nullptr, g.P};
             if (launch_gemm_down_dgrad(c1, st)) return MOE_ERR_HIP;
             GemmGuDgradArgs c2{dense, sdgu, (const uint16_t*)w->s_gate, (const uint16_t*)w->s_up,
                                g.H, g.I, sdx};

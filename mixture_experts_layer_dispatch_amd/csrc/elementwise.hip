@@ -1,8 +1,9 @@
-// Bandwidth-bound steps of the layer: dispatch (gather into expert order),
-// the weighted combine, the reverse-dispatch reduction, the softmax backward,
-// and the per-expert tile prefix the grouped GEMMs are launched over.
+// Bandwidth-bound steps of the layer: the combine (the final sum of a token's
+// weighted expert rows), the reverse-dispatch reduction, the softmax backward,
+// and the per-expert tile prefix the grouped GEMMs are launched over.  The
+// dispatch itself is fused into the gate/up GEMM's operand loads.
 //
-// Dispatch / combine / reverse-dispatch: alphalab.site "Mixture-of-Kittens"
+// Combine / reverse-dispatch: alphalab.site "Mixture-of-Kittens"
 // section 一 (tokens go to their experts and come back) and section 二 (the
 // router-weighted reduction; a fixed floating-point accumulation order makes
 // the layer bitwise reproducible); arex-research.com "Cursor 放出 MoK", design
@@ -16,27 +17,6 @@
 #include "profile.h"
 
 namespace moe {
-
-// ============================================================== dispatch
-// Slot-major over one minibatch: slot s copies token s/k into ring row
-// row_of_slot[s] - ring_row0.  A token's k slots are adjacent, so its source
-// row is read from cache after the first copy.
-__global__ __launch_bounds__(256) void k_dispatch(const uint4* __restrict__ x, int H8,
-                                                  const int32_t* __restrict__ row_of_slot, int s0,
-                                                  int s1, int k, int ring_row0, int ring_rows,
-                                                  uint4* __restrict__ ring, int32_t* __restrict__ err) {
-    const int s = s0 + blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (s >= s1) return;
-    const int lane = lane_id();
-    const int r = row_of_slot[s] - ring_row0;
-    if ((unsigned)r >= (unsigned)ring_rows) {
-        if (lane == 0) raise_err(err, ERR_BAD_ROW);
-        return;
-    }
-    const uint4* src = x + (size_t)(s / k) * H8;
-    uint4* dst = ring + (size_t)r * H8;
-    for (int c = lane; c < H8; c += 64) dst[c] = src[c];
-}
 
 // ============================================================== combine
 // Lane j < k of the wave holds slot j's ring row and weight; the loops below
@@ -272,15 +252,6 @@ __global__ __launch_bounds__(1024) void k_deep_list(const int32_t* __restrict__ 
 }
 
 // ============================================================== launchers
-int launch_dispatch(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
-                    int ring_row0, int ring_rows, void* ring, int32_t* err, hipStream_t st) {
-    ProfScope prof_(st, "dispatch");
-    if (s1 <= s0) return 0;
-    k_dispatch<<<(s1 - s0 + 3) / 4, 256, 0, st>>>((const uint4*)x, H / 8, row_of_slot, s0, s1, k,
-                                                  ring_row0, ring_rows, (uint4*)ring, err);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
 int launch_combine(const void* o, int H, const int32_t* row_of_slot, const float* w, int t0, int t1,
                    int k, int ring_row0, int ring_rows, const void* shared, int shared_t0, void* y,
                    int32_t* err, hipStream_t st) {

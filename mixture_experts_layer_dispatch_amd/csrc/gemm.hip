@@ -96,17 +96,24 @@ __global__ __launch_bounds__(GateUpShape<TM>::NTHR, TM == 64 ? 2 : 1) void k_gem
                 uq[r] = bf2f(f2bf(acc[mb][nb + 2][r]));
                 hq[r] = swiglu_h(gq[r], uq[r]);
             }
-            const int64_t srow = (int64_t)(a.save_row0 + rl) * a.I + i;
-            *(uint2*)(a.g_out + srow) = pack4(gq[0], gq[1], gq[2], gq[3]);
-            *(uint2*)(a.u_out + srow) = pack4(uq[0], uq[1], uq[2], uq[3]);
+            if (a.g_out) {                  // null: g, u are not kept (recomputed later)
+                const int64_t srow = (int64_t)(a.save_row0 + rl) * a.I + i;
+                *(uint2*)(a.g_out + srow) = pack4(gq[0], gq[1], gq[2], gq[3]);
+                *(uint2*)(a.u_out + srow) = pack4(uq[0], uq[1], uq[2], uq[3]);
+            }
             *(uint2*)(a.h_out + (int64_t)rl * a.I + i) = pack4(hq[0], hq[1], hq[2], hq[3]);
         }
     }
 }
 
 // ================================================================ forward GEMM 2
-// o = h W_down^T.  Tile TM rows x 128 columns of H; with 128-row tiles a
-// block takes two neighbouring column tiles in one K loop (K = I is short).
+// o = w * (h W_down^T), each row scaled by its slot's router weight in fp32
+// before the one rounding to bf16.  alphalab.site "Mixture-of-Kittens" keeps
+// the final router-weighted reduction as a step of its own after the combine
+// (section 二); applying the weight here leaves that step a plain fixed-order
+// sum of a token's rows.  Tile TM rows x 128 columns of H;
+// with 128-row tiles a block takes two neighbouring column tiles in one K
+// loop (K = I is short).
 constexpr int G2_TN = 128;
 
 template <int TM>
@@ -124,6 +131,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
     RowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, G2_TN};
     LoadKC<G2_TN, RowsDirect> lb(sb);
     AccPos<TM, G2_TN> pos;
+    float wr[TM / 32];
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) wr[mb] = lo + pos.m(mb) < hi ? a.rw.at(lo + pos.m(mb)) : 0.f;
     auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
         for (int mb = 0; mb < TM / 32; ++mb) {
@@ -133,7 +143,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
             for (int nb = 0; nb < 4; ++nb) {
                 const int col = n0 + t * G2_TN + pos.n(nb);
                 const f32x4 v = c[mb][nb];
-                *(uint2*)(a.o + (int64_t)rl * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
+                *(uint2*)(a.o + (int64_t)rl * a.H + col) =
+                    pack4(wr[mb] * v[0], wr[mb] * v[1], wr[mb] * v[2], wr[mb] * v[3]);
             }
         }
     };

@@ -362,13 +362,24 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
     const uint32_t* wus = (const uint32_t*)(a.wu_s + (int64_t)e * I * (H / 32));
     RowsGateUp db{wg, wu, H / 2, i0};
     ScalesGateUp ds{wgs, wus, I, i0};
-    RowsDirect da{(const uint16_t*)a.x_q, H / 2, a.xrow0 + lo, hi - lo};
-    ScalesDirect dsa{(const uint32_t*)a.x_s, H / 128, a.xrow0 + lo, hi - lo};
-    LoadKC<TM, RowsDirect> la(da);
     LoadKC<M1_TN, RowsGateUp> lb(db);
-    LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScales<M1_TN, ScalesGateUp> sb(ds);
-    mainloop_mx<TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+    if (a.x_gather) {
+        // dispatch fused into the operand loads: a routed row's codes are its
+        // token's row of the once-quantised x
+        RowsGather da{(const uint16_t*)a.x_q, H / 2, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S,
+                      a.g.err};
+        ScalesGather dsa{(const uint32_t*)a.x_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
+        LoadKC<TM, RowsGather> la(da);
+        LoadScales<TM, ScalesGather> sa(dsa);
+        mainloop_mx<TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+    } else {
+        RowsDirect da{(const uint16_t*)a.x_q, H / 2, a.xrow0 + lo, hi - lo};
+        ScalesDirect dsa{(const uint32_t*)a.x_s, H / 128, a.xrow0 + lo, hi - lo};
+        LoadKC<TM, RowsDirect> la(da);
+        LoadScales<TM, ScalesDirect> sa(dsa);
+        mainloop_mx<TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+    }
     AccPos<TM, M1_TN> pos;
     const int wn = threadIdx.x >> 7, lane = lane_id();
 #pragma unroll
@@ -385,7 +396,7 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
                 hq[4 * nb + r] = swiglu_h(acc[mb][nb][r], acc[mb][nb + 2][r]);
                 amax = fmaxf(amax, fabsf(hq[4 * nb + r]));
             }
-            if (rl < hi) {
+            if (rl < hi && a.g_out) {       // null: g, u are not kept (recomputed later)
                 const int i = i0 + 32 * wn + nb * 16 + 4 * (lane >> 4);
                 const int64_t srow = (int64_t)(a.save_row0 + rl) * I + i;
                 *(float4*)(a.g_out + srow) = make_float4(acc[mb][nb][0], acc[mb][nb][1],
@@ -433,6 +444,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScales<M2_TN, ScalesKMajor> sb(dsb);
     AccPos<TM, M2_TN> pos;
+    float wr[TM / 32];          // router weight of each row (the combine is a plain sum)
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) wr[mb] = lo + pos.m(mb) < hi ? a.rw.at(lo + pos.m(mb)) : 0.f;
     auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
         for (int mb = 0; mb < TM / 32; ++mb) {
@@ -442,7 +456,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
             for (int nb = 0; nb < 4; ++nb) {
                 const int col = n0 + t * M2_TN + pos.n(nb);
                 const f32x4 v = c[mb][nb];
-                *(uint2*)(a.o + (int64_t)rl * H + col) = pack4(v[0], v[1], v[2], v[3]);
+                *(uint2*)(a.o + (int64_t)rl * H + col) =
+                    pack4(wr[mb] * v[0], wr[mb] * v[1], wr[mb] * v[2], wr[mb] * v[3]);
             }
         }
     };

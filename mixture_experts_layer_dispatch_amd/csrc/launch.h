@@ -38,10 +38,25 @@ struct GemmGateUpArgs {
     const uint16_t* w_gate;   // [E, I, H]
     const uint16_t* w_up;
     int H, I;
-    uint16_t* g_out;          // saved g, row (save_row0 + local row)
+    uint16_t* g_out;          // saved g, row (save_row0 + local row); nullptr: not kept
     uint16_t* u_out;
     int save_row0;
     uint16_t* h_out;          // ring h, local rows
+};
+
+// Router weight of each output row, for GEMMs whose epilogue scales their rows
+// (the down projection writes w * o so that the combine is a plain sum):
+// row r of a macrobatch has weight w[slot_of_row[grow0 + r]]; w == nullptr:
+// weight 1 (the shared expert).
+struct RowWeights {
+    const float* w;
+    const int32_t* slot_of_row;
+    int grow0, S;
+    __device__ float at(int r) const {
+        if (!w) return 1.0f;
+        const int s = slot_of_row[grow0 + r];
+        return (unsigned)s < (unsigned)S ? w[s] : 0.0f;
+    }
 };
 
 struct GemmDownArgs {
@@ -49,7 +64,8 @@ struct GemmDownArgs {
     const uint16_t* h;        // ring h [rows, I]
     const uint16_t* w_down;   // [E, H, I]
     int H, I;
-    uint16_t* o;              // ring o [rows, H]
+    uint16_t* o;              // ring o [rows, H]: w * (h W_down^T) per row
+    RowWeights rw;
 };
 
 struct GemmDownDgradArgs {
@@ -129,15 +145,18 @@ struct WgradGateUpArgs {
 
 struct GemmGateUpMXArgs {
     GroupRows g;
-    const uint8_t* x_q;       // codes [rows, H] (rows xrow0 + local row)
-    const uint8_t* x_s;       // scales [rows, H/32]
+    const uint8_t* x_q;       // codes [tokens, H]: routed rows gathered by token through
+    const uint8_t* x_s;       // slot_of_row (x_gather), dense rows xrow0 + local row; scales [tokens, H/32]
     int xrow0;
+    int x_gather;
+    const int32_t* slot_of_row;
+    int grow0, k, S;
     const uint8_t* wg_q;
     const uint8_t* wg_s;
     const uint8_t* wu_q;
     const uint8_t* wu_s;
     int H, I;
-    float* g_out;             // saved g, u in fp32
+    float* g_out;             // saved g, u in fp32; nullptr: not kept
     float* u_out;
     int save_row0;
     uint8_t* h_q;             // ring codes [rows, I]
@@ -151,7 +170,8 @@ struct GemmDownMXArgs {
     const uint8_t* wd_q;      // [E, H, I]
     const uint8_t* wd_s;      // [E, H, I/32]
     int H, I;
-    uint16_t* o;
+    uint16_t* o;              // w * (Q(h) Q(W_down)^T) per row
+    RowWeights rw;
 };
 
 // Expert groups padded to whole 32-row blocks (the MXFP8 weight gradients
@@ -232,8 +252,6 @@ int launch_schedule(const int32_t* idx, int T, int E, int k, int M, int mb, int3
 size_t schedule_hist_ints(int T, int E, int k, int M, int mb);
 
 // elementwise.hip
-int launch_dispatch(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
-                    int ring_row0, int ring_rows, void* ring, int32_t* err, hipStream_t st);
 int launch_combine(const void* o, int H, const int32_t* row_of_slot, const float* w, int t0, int t1,
                    int k, int ring_row0, int ring_rows, const void* shared, int shared_t0, void* y,
                    int32_t* err, hipStream_t st);
@@ -252,9 +270,6 @@ int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* 
                          int kmaj_rows = 0);
 int launch_mx_quant_cols(const void* w, int batch, int R, int C, void* codes, void* scales,
                          hipStream_t st);
-int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
-                       int ring_row0, int ring_rows, void* codes, void* scales, int32_t* err,
-                       hipStream_t st);
 
 int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, void* codes, void* scales,
                             hipStream_t st);

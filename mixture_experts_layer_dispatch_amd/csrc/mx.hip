@@ -1,8 +1,10 @@
 // MXFP8 quantisation kernels: weights along either axis (ahead of time, as the
 // pages describe: alphalab.site "Mixture-of-Kittens" section 三, weights are
-// quantised outside the timed region), and the dispatch gather with the
-// activation quantisation fused in (arex-research.com "Cursor 放出 MoK",
-// design section, closing paragraph).
+// quantised outside the timed region), and the activations: x and dy along H
+// once per token (the dispatch and the reverse-combine gather these codes on
+// load), and the row-block transposes of the weight-gradient operands
+// (arex-research.com "Cursor 放出 MoK", design section, closing paragraph:
+// activation quantisation is fused into dispatch, the GEMMs and SwiGLU).
 #include <type_traits>
 
 #include "launch.h"
@@ -84,53 +86,6 @@ __global__ __launch_bounds__(256) void k_mx_quant_cols(const uint16_t* __restric
     dst[1] = make_uint4(wds[4], wds[5], wds[6], wds[7]);
     const int b = blockIdx.y;
     scales[mat * (int64_t)C * (R / 32) + ((int64_t)(b >> 2) * C + c) * 4 + (b & 3)] = (uint8_t)(s + 127);
-}
-
-// ------------------------------------------------------------------ dispatch
-// Slot-major over one minibatch: slot s quantises token s/k along H into ring
-// row row_of_slot[s] - ring_row0.  One wave per slot, 8 elements per lane,
-// four lanes per block.
-__global__ __launch_bounds__(256) void k_dispatch_mx(const uint4* __restrict__ x, int H,
-                                                     const int32_t* __restrict__ row_of_slot, int s0,
-                                                     int s1, int k, int ring_row0, int ring_rows,
-                                                     uint2* __restrict__ codes,
-                                                     uint8_t* __restrict__ scales,
-                                                     int32_t* __restrict__ err) {
-    const int s = s0 + blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (s >= s1) return;
-    const int lane = lane_id();
-    const int r = row_of_slot[s] - ring_row0;
-    if ((unsigned)r >= (unsigned)ring_rows) {
-        if (lane == 0) raise_err(err, ERR_BAD_ROW);
-        return;
-    }
-    const int H8 = H / 8;
-    const uint4* src = x + (int64_t)(s / k) * H8;
-    uint2* dst = codes + (int64_t)r * H8;
-    uint8_t* sdst = scales + (int64_t)r * (H / 32);
-    for (int c0 = 0; c0 < H8; c0 += 64) {         // H8 is a multiple of 16: whole blocks per pass
-        const int c = c0 + lane;
-        const bool ok = c < H8;
-        float v[8];
-        if (ok) {
-            const uint4 w = src[c];
-            v[0] = lo_bf(w.x); v[1] = hi_bf(w.x); v[2] = lo_bf(w.y); v[3] = hi_bf(w.y);
-            v[4] = lo_bf(w.z); v[5] = hi_bf(w.z); v[6] = lo_bf(w.w); v[7] = hi_bf(w.w);
-        } else {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = 0.f;
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
-        amax = fmaxf(amax, __shfl_xor(amax, 1));
-        amax = fmaxf(amax, __shfl_xor(amax, 2));
-        const int se = mx_scale_exp(amax);
-        if (ok) {
-            dst[c] = e4m3_pack8(v, se);
-            if ((c & 3) == 0) sdst[c >> 2] = (uint8_t)(se + 127);
-        }
-    }
 }
 
 // ------------------------------------------------------------------ group transpose
@@ -270,17 +225,6 @@ int launch_mx_quant_cols(const void* w, int batch, int R, int C, void* codes, vo
     ProfScope prof_(st, "mx_quant_cols");
     dim3 grid((C + 255) / 256, R / 32, batch);
     k_mx_quant_cols<<<grid, 256, 0, st>>>((const uint16_t*)w, R, C, (uint8_t*)codes, (uint8_t*)scales);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
-int launch_dispatch_mx(const void* x, int H, const int32_t* row_of_slot, int s0, int s1, int k,
-                       int ring_row0, int ring_rows, void* codes, void* scales, int32_t* err,
-                       hipStream_t st) {
-    ProfScope prof_(st, "dispatch_mx");
-    if (s1 <= s0) return 0;
-    k_dispatch_mx<<<(s1 - s0 + 3) / 4, 256, 0, st>>>((const uint4*)x, H, row_of_slot, s0, s1, k,
-                                                     ring_row0, ring_rows, (uint2*)codes,
-                                                     (uint8_t*)scales, err);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

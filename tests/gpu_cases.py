@@ -12,10 +12,10 @@ from mixture_experts_layer_dispatch_amd import binding as B
 BF16_TOL = 1e-2       # max |gpu - ref| <= BF16_TOL * max |ref|
 
 
-def cfg_of(shape: si.MoEShape) -> B.Config:
+def cfg_of(shape: si.MoEShape, precision=B.PREC_BF16, recompute=False) -> B.Config:
     return B.Config(T=shape.T, H=shape.H, I=shape.I, E=shape.E, k=shape.k,
                     n_shared=shape.n_shared, macrobatch=shape.macrobatch,
-                    minibatch=shape.minibatch)
+                    minibatch=shape.minibatch, precision=precision, recompute=recompute)
 
 
 def f32(t: torch.Tensor) -> np.ndarray:
@@ -36,9 +36,10 @@ def assert_close(name, gpu, ref, tol=BF16_TOL):
 class Case:
     """Inputs of one shape on the GPU, and the CPU copies the oracle reads."""
 
-    def __init__(self, shape: si.MoEShape, logits_override=None, with_backward=True):
+    def __init__(self, shape: si.MoEShape, logits_override=None, with_backward=True,
+                 precision=B.PREC_BF16, recompute=False):
         self.shape = shape
-        self.cfg = cfg_of(shape)
+        self.cfg = cfg_of(shape, precision, recompute)
         dev = "cuda"
         self.logits = logits_override.to(dev) if logits_override is not None else si.logits(shape, dev)
         self.x = si.tokens(shape, dev)
@@ -53,6 +54,10 @@ class Case:
         self.sched = B.alloc_schedule(self.cfg)
         self.saved = B.alloc_saved(self.cfg)
         self.y = torch.empty(shape.T, shape.H, dtype=torch.bfloat16, device=dev)
+        if precision == B.PREC_MXFP8:
+            self.wq = B.alloc_weights_mx(self.cfg)
+            B.moe_quantize_weights_mxfp8(self.cfg, self.weights, self.wq)
+            self.weights = dict(self.weights, mx=self.wq)
 
     # ------------------------------------------------------------- GPU calls
     def schedule(self):

@@ -59,6 +59,7 @@ def _cfg(**kw):
     ({"macrobatch": 128, "capacity_rows": 256}, B.MOE_OK),
     ({"capacity_rows": -1}, B.MOE_ERR_INVALID_ARG),
     ({"precision": 7}, B.MOE_ERR_INVALID_ARG),
+    ({"recompute": True}, B.MOE_OK),
 ])
 def test_config_validation(kw, status):
     assert B.validate_config(_cfg(**kw)) == status
@@ -71,9 +72,9 @@ def test_ring_rows_and_workspace():
     assert B.ring_rows(two) == 2 * 64 * 2
     assert B.ring_rows(_cfg(macrobatch=64, capacity_rows=1000)) == 1000
     ws1 = B.workspace_size(one)
-    assert ws1 > 256 * 2 * (2 * 256 + 128) * 2          # at least the forward ring
+    assert ws1 > 256 * 2 * (3 * 128 + 256) * 2          # at least the backward ring (dg|du, hw, dX)
     big = B.Config(T=2048, H=4096, I=1024, E=512, k=10)
-    assert B.workspace_size(big) > 20480 * (2 * 4096 + 1024) * 2
+    assert B.workspace_size(big) > 20480 * (3 * 1024 + 4096) * 2
     with pytest.raises(B.MoEError):
         B.workspace_size(_cfg(T=0))
 
@@ -215,3 +216,34 @@ def test_binding_checks_every_tensor_before_the_call():
     q["w_up_ts"] = q["w_up_ts"][:-1]
     with pytest.raises(ValueError, match="w_up_ts"):
         B.moe_quantize_weights_mxfp8(mx, b["w"], q)
+
+
+def test_config_flags_and_recompute_workspace():
+    """Unknown flag bits are rejected; recompute mode adds one macrobatch's g, u
+    (bf16, or fp32 in MXFP8 mode) to the workspace and saves nothing."""
+    bad = _cfg().c()
+    bad.flags = 2
+    assert B.lib().moe_validate_config(ctypes.byref(bad)) == B.MOE_ERR_INVALID_ARG
+    for prec, es in ((B.PREC_BF16, 2), (B.PREC_MXFP8, 4)):
+        base = _cfg(macrobatch=64, n_shared=1, precision=prec)
+        rc = _cfg(macrobatch=64, n_shared=1, precision=prec, recompute=True)
+        extra = B.workspace_size(rc) - B.workspace_size(base)
+        assert extra >= 2 * 64 * 2 * 128 * es + 2 * 64 * 128 * es     # routed + shared g, u
+        assert B.alloc_saved(rc, "cpu") == {}
+
+
+def test_workspace_regions_of_the_mx_activation_codes():
+    mx = _cfg(precision=B.PREC_MXFP8)
+    total = B.workspace_size(mx)
+    seen = []
+    for name, n in (("x_codes", 256 * 256), ("x_scales", 256 * 256 // 32),
+                    ("dy_codes", 256 * 256), ("dy_scales", 256 * 256 // 32)):
+        off, nb = B.workspace_region(mx, name)
+        assert nb == n and off % 256 == 0 and off + nb <= total
+        seen.append((off, off + nb))
+    seen.sort()
+    assert all(a[1] <= b[0] for a, b in zip(seen, seen[1:]))        # disjoint
+    with pytest.raises(B.MoEError):
+        B.workspace_region(_cfg(), "x_codes")                        # bf16: no codes
+    with pytest.raises(B.MoEError):
+        B.workspace_region(mx, "nothing")

@@ -32,13 +32,14 @@ def test_algorithmic_bytes_of_the_2048_token_layer():
     S = T * k
     counts = np.full(E, S // E)                # every expert touched
     kb = bench.kernel_bytes(s, counts)
-    # each touched expert's gate and up weights once, the gathered rows once, g, u, h written
-    assert kb["gemm_gate_up"] == E * 2 * I * H * 2 + S * H * 2 + 3 * S * I * 2
+    # each touched expert's gate and up weights once, x once (the dispatch is
+    # fused into the loads), g, u, h written
+    assert kb["gemm_gate_up"] == E * 2 * I * H * 2 + T * H * 2 + 3 * S * I * 2
     # the weight gradients: every expert's gradient written once (bf16)
     assert kb["wgrad_gate_up"] >= E * 2 * I * H * 2
     assert kb["wgrad_down"] >= E * H * I * 2
     # MXFP8 weights: a code and 1/32 of a scale byte per element
-    assert kb["gemm_down_mx"] == int(E * H * I * (1 + 1 / 32) + S * I * (1 + 1 / 32) + S * H * 2)
+    assert kb["gemm_down_mx"] == int(E * H * I * (1 + 1 / 32) + S * I * (1 + 1 / 32) + S * H * 2 + S * 8)
     # per-launch figures are not given for several macrobatches
     assert bench.kernel_bytes(si.SHAPES["e512_t65536_zipf"], counts) == {}
 

@@ -55,14 +55,8 @@ def _gpu():
 
 class MXCase(Case):
     def __init__(self, shape, **kw):
-        super().__init__(shape, **kw)
         from mixture_experts_layer_dispatch_amd import binding as B
-        self.cfg.precision = B.PREC_MXFP8
-        self.ws = B.alloc_workspace(self.cfg)          # MXFP8 needs more workspace
-        self.saved = B.alloc_saved(self.cfg)           # and fp32 g, u
-        self.wq = B.alloc_weights_mx(self.cfg)
-        B.moe_quantize_weights_mxfp8(self.cfg, self.weights, self.wq)
-        self.weights = dict(self.weights, mx=self.wq)
+        super().__init__(shape, precision=B.PREC_MXFP8, **kw)
 
 
 def _check_quantised(w_bf16, codes, scales, axis):
@@ -145,8 +139,7 @@ def test_forward_mx_full_size_sampled():
     c.schedule()
     c.forward()
     torch.cuda.synchronize()
-    idx = c.sched["topk_idx"].cpu().numpy()
-    w = oracle.route(f32(c.logits), c.shape.k)[1]
+    idx, w = oracle.route(f32(c.logits), c.shape.k)       # the oracle's own routing
     rng = np.random.default_rng(1)
     tokens = np.sort(rng.choice(c.shape.T, size=16, replace=False))
     ref = oracle.forward(f32(c.x), c.expert_view(c.wg), c.expert_view(c.wu), c.expert_view(c.wd),
@@ -265,3 +258,47 @@ def test_forward_backward_mx_ep_share_full_size_sampled():
         assert_close(f"dW_gate[{e}] (mxfp8)", f32(c.grads["d_w_gate"][e]), rb["dWg"][e], MX_TOL)
         assert_close(f"dW_up[{e}] (mxfp8)", f32(c.grads["d_w_up"][e]), rb["dWu"][e], MX_TOL)
         assert_close(f"dW_down[{e}] (mxfp8)", f32(c.grads["d_w_down"][e]), rb["dWd"][e], MX_TOL)
+
+
+def _region(c, name, shape):
+    from mixture_experts_layer_dispatch_amd import binding as B
+    off, n = B.workspace_region(c.cfg, name)
+    return c.ws[off:off + n].view(*shape).cpu().numpy()
+
+
+def _check_activation_codes(c, which):
+    """The E4M3 codes and E8M0 scales the path made of x (forward) or dy
+    (backward), bit for bit against the oracle's quantiser of the same bf16
+    rows along H."""
+    src = c.x if which == "x" else c.dy
+    T, H = c.shape.T, c.shape.H
+    codes = _region(c, f"{which}_codes", (T, H))
+    scales = _region(c, f"{which}_scales", (T, H // 32))
+    ref_c, ref_s = oracle.mx_quantize(f32(src).astype(np.float64), axis=1)
+    np.testing.assert_array_equal(scales, ref_s)
+    np.testing.assert_array_equal(codes, ref_c)
+
+
+@pytest.mark.parametrize("name", ["tiny", "ring_shared", "zipf_ring", "max_k"])
+def test_activation_codes_bit_exact(name):
+    """The dispatch gathers each routed row's codes from x quantised once per
+    token, and the reverse-combine those of dy: both quantisations compared
+    bit for bit with the oracle's (identical bf16 inputs on both sides)."""
+    c = MXCase(SHAPES[name])
+    c.schedule()
+    c.forward()
+    torch.cuda.synchronize()
+    _check_activation_codes(c, "x")
+    c.backward()
+    torch.cuda.synchronize()
+    _check_activation_codes(c, "dy")
+
+
+def test_activation_codes_bit_exact_full_size():
+    c = MXCase(si.SHAPES["e512_t2048"])
+    c.schedule()
+    c.forward()
+    c.backward()
+    torch.cuda.synchronize()
+    _check_activation_codes(c, "x")
+    _check_activation_codes(c, "dy")
