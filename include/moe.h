@@ -220,6 +220,26 @@ MOE_API int moe_device_supported(void);
 MOE_API moe_status moe_schedule(const moe_config* cfg, const float* logits, const moe_sched* sched,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* moe_schedule without a workspace, for callers that cannot allocate device
+ * memory (code under stream capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments and results as moe_schedule minus the
+ * workspace: its scratch (error word, per-block histograms and bases) lives in
+ * a fixed 16 MiB device array inside the library, one per GPU, held until the
+ * process ends.  Allocates nothing and makes no allocating call.
+ *   Limit: 256 + 2 * align256(4 * E * nb) <= 16 MiB, nb = the schedule's
+ *   512-slot blocks (ceil(minibatch * k / 512) per minibatch, summed over
+ *   all minibatches); the 65,536-token, 512-expert, top-10 stream needs
+ *   5.0 MiB.  Larger configs return MOE_ERR_WORKSPACE before anything is
+ *   enqueued.
+ *   Every call on a GPU shares that GPU's array: calls that overlap on one
+ *   GPU (on different streams, or from different threads) race; serialise
+ *   them.  The array keeps the last call's contents; what must start at zero
+ *   is cleared by the call itself.  Its device error word is not reported
+ *   (moe_check_device_error reads a workspace); routing of finite logits
+ *   cannot produce an out-of-range entry. */
+MOE_API moe_status moe_schedule_noalloc(const moe_config* cfg, const float* logits,
+                                        const moe_sched* sched, void* stream);
+
 /* Forward ([ALPHA] 一: dispatch, expert SwiGLU FFN, combine; 二: the
  * router-weighted reduction in a fixed order).
  *   x [T, H] bf16; y [T, H] bf16 (written);

@@ -31,7 +31,7 @@ EXPORTED = [
     "moe_status_string", "moe_validate_config", "moe_ring_rows", "moe_workspace_size",
     "moe_device_supported", "moe_schedule", "moe_forward", "moe_backward",
     "moe_check_device_error", "moe_quantize_weights_mxfp8", "moe_profile_enable", "moe_profile_collect", "moe_profile_query",
-    "moe_profile_names", "moe_profile_reset", "moe_workspace_region",
+    "moe_profile_names", "moe_profile_reset", "moe_workspace_region", "moe_schedule_noalloc",
 ]
 
 FLAG_RECOMPUTE = 1
@@ -101,6 +101,7 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_size.argtypes = [cfgp, ctypes.POINTER(ctypes.c_size_t)]
         L.moe_device_supported.argtypes = []
         L.moe_schedule.argtypes = [cfgp, vp, ctypes.POINTER(moe_sched), vp, ctypes.c_size_t, vp]
+        L.moe_schedule_noalloc.argtypes = [cfgp, vp, ctypes.POINTER(moe_sched), vp]
         L.moe_forward.argtypes = [cfgp, ctypes.POINTER(moe_sched), vp, ctypes.POINTER(moe_weights),
                                   vp, ctypes.POINTER(moe_saved), vp, ctypes.c_size_t, vp]
         L.moe_backward.argtypes = [cfgp, ctypes.POINTER(moe_sched), ctypes.POINTER(moe_saved), vp,
@@ -395,6 +396,14 @@ def moe_schedule(cfg: Config, logits: torch.Tensor, sched: dict, ws: torch.Tenso
               + _spec_ws(cfg, ws))
     _check(lib().moe_schedule(ctypes.byref(cfg.c()), _p(logits), ctypes.byref(_sched(sched)),
                               _p(ws), ws.numel(), _stream(stream)), "moe_schedule")
+
+
+def moe_schedule_noalloc(cfg: Config, logits: torch.Tensor, sched: dict, stream=None):
+    """moe_schedule without a workspace: the library's fixed scratch array is
+    used instead (overlapping calls on one GPU race)."""
+    _validate([("logits", logits, (cfg.T, cfg.E), torch.float32)] + _spec_sched(cfg, sched))
+    _check(lib().moe_schedule_noalloc(ctypes.byref(cfg.c()), _p(logits), ctypes.byref(_sched(sched)),
+                                      _stream(stream)), "moe_schedule_noalloc")
 
 
 def moe_forward(cfg: Config, sched: dict, x: torch.Tensor, weights: dict, y: torch.Tensor,

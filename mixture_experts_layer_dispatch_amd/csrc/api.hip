@@ -10,6 +10,7 @@
 // reduction closes the forward.
 #include <atomic>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "common.h"
@@ -488,6 +489,42 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     return MOE_OK;
 }
 
+// ---------------------------------------------------------------- no-allocation schedule
+// moe_schedule_noalloc keeps the schedule's scratch (the error word, the
+// per-block histograms and bases) in this fixed device array instead of a
+// caller workspace.  Host code never passes the array's name to a kernel (in
+// host code it is only a stand-in); the device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+constexpr size_t kNoAllocScratch = 16u << 20;
+__device__ __align__(256) unsigned char scratch[kNoAllocScratch];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+void* scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+// bytes of scratch the schedule of `g` needs: error word, histograms, bases
+size_t schedule_scratch_bytes(const Geom& g) {
+    const size_t hist = schedule_hist_ints(g.T, g.E, g.k, g.M, g.mb) * 4;
+    return 256 + 2 * align_up(hist, 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -569,6 +606,33 @@ moe_status moe_schedule(const moe_config* cfg, const float* logits, const moe_sc
     if (launch_schedule(sched->topk_idx, g.T, g.E, g.k, g.M, g.mb, (int32_t*)(ws + L.hist),
                         (int32_t*)(ws + L.base), sched->counts, sched->offsets, sched->mini_counts,
                         sched->row_of_slot, sched->slot_of_row, err, st))
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_schedule_noalloc(const moe_config* cfg, const float* logits, const moe_sched* sched,
+                                void* stream) {
+    Geom g;
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    if (!logits || !aligned(logits, 4) || !sched_ok(sched)) return MOE_ERR_INVALID_ARG;
+    if (schedule_scratch_bytes(g) > kNoAllocScratch) return MOE_ERR_WORKSPACE;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    char* base = (char*)scratch_ptr();
+    if (!base) return MOE_ERR_HIP;
+    hipStream_t st = (hipStream_t)stream;
+    const size_t hist = align_up(schedule_hist_ints(g.T, g.E, g.k, g.M, g.mb) * 4, 256);
+    int32_t* err = (int32_t*)base;
+    int32_t* hh = (int32_t*)(base + 256);
+    int32_t* bb = (int32_t*)(base + 256 + hist);
+    // the histograms and bases are written in full before they are read; the
+    // error word is cleared by a kernel (no memset node if the call is captured)
+    k_clear_word<<<1, 1, 0, st>>>(err);
+    if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    if (launch_topk_route(logits, g.T, g.E, g.k, sched->topk_idx, sched->topk_w, st)) return MOE_ERR_HIP;
+    if (launch_schedule(sched->topk_idx, g.T, g.E, g.k, g.M, g.mb, hh, bb, sched->counts,
+                        sched->offsets, sched->mini_counts, sched->row_of_slot, sched->slot_of_row,
+                        err, st))
         return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -247,3 +247,15 @@ def test_workspace_regions_of_the_mx_activation_codes():
         B.workspace_region(_cfg(), "x_codes")                        # bf16: no codes
     with pytest.raises(B.MoEError):
         B.workspace_region(mx, "nothing")
+
+
+def test_noalloc_schedule_rejects_configs_beyond_its_scratch():
+    """moe_schedule_noalloc checks its fixed scratch on the host: a schedule
+    needing more than 16 MiB of histograms is refused before any device work."""
+    L = B.lib()
+    fake = ctypes.c_void_p(1 << 20)                # never dereferenced
+    s_ok = B.moe_sched(*([1 << 20] * 7))
+    huge = B.Config(T=262144, H=128, I=128, E=1024, k=10).c()     # 5120 blocks x 1024 experts
+    assert L.moe_schedule_noalloc(ctypes.byref(huge), fake, ctypes.byref(s_ok), None) == B.MOE_ERR_WORKSPACE
+    assert L.moe_schedule_noalloc(ctypes.byref(_cfg().c()), fake, ctypes.byref(B.moe_sched()),
+                                  None) == B.MOE_ERR_INVALID_ARG
