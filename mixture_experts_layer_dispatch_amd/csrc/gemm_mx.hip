@@ -206,6 +206,41 @@ __device__ __forceinline__ void mma_tile_mx(const uint16_t* st, int wm0, int wn0
     mma_tile_mx_at<TM, TN>(st, st + SM::A, cA, cA + TM, wm0, wn0, acc);
 }
 
+// The scaled fp8 MFMA started from zero for each 128-code K step, its result
+// added to the fp32 accumulator in ascending K order: the MFMA's own
+// accumulation then covers one step's 128 products only.
+template <int TM, int TN>
+__device__ __forceinline__ void mma_tile_mx_stepwise(const uint16_t* st, int wm0, int wn0,
+                                                     f32x4 (&acc)[TM / 32][TN / 32]) {
+    using SM = SmemMX<TM, TN>;
+    constexpr int MB = TM / 32, NB = TN / 32;
+    const uint16_t* sA = st;
+    const uint16_t* sB = st + SM::A;
+    const uint32_t* cA = (const uint32_t*)(st + SM::A + SM::B);
+    const uint32_t* cB = cA + TM;
+    v8i32 fb[MB], fa[NB];
+    int xb[MB], xa[NB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        fb[mb] = frag_mx(sA, wm0 + mb * 16);
+        xb[mb] = scale_mx(cA, wm0 + mb * 16);
+    }
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+        fa[nb] = frag_mx(sB, wn0 + nb * 16);
+        xa[nb] = scale_mx(cB, wn0 + nb * 16);
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) {
+            const f32x4 t = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                fa[nb], fb[mb], f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0, xa[nb], 0, xb[mb]);
+            acc[mb][nb] = f32x4{acc[mb][nb][0] + t[0], acc[mb][nb][1] + t[1], acc[mb][nb][2] + t[2],
+                                acc[mb][nb][3] + t[3]};
+        }
+}
+
 // The same product evaluated on the bf16 MFMA: codes are decoded to bf16 at
 // fragment time (an E4M3 value times a power of two has at most 4 significant
 // bits, so the decode is exact).  The scaled fp8 MFMA accumulates a 128-product step less
@@ -256,8 +291,13 @@ __device__ __forceinline__ void mma_tile_mx_precise(const uint16_t* st, int wm0,
     }
 }
 
-// Double-buffered K loop over 128-code steps.
-template <int TM, int TN, bool PRECISE = false, class LA, class LB, class SA, class SB>
+// Double-buffered K loop over 128-code steps.  MODE: how a K step's products
+// are formed and summed: MX_ACC, the scaled MFMA accumulating across steps;
+// MX_STEPWISE, the scaled MFMA from zero per step, added in fp32; MX_BF16,
+// codes decoded exactly to bf16 on the bf16 MFMA (for GEMMs whose outputs
+// are quantised again; see the kernels for which each uses).
+constexpr int MX_ACC = 0, MX_STEPWISE = 1, MX_BF16 = 2;
+template <int TM, int TN, int MODE = MX_ACC, class LA, class LB, class SA, class SB>
 __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int nk, uint16_t* smem,
                                             f32x4 (&acc)[TM / 32][TN / 32], bool keep = false) {
     using SM = SmemMX<TM, TN>;
@@ -287,7 +327,8 @@ __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int 
         uint16_t* nxt = (kt & 1) ? buf0 : buf1;
         const bool more = kt + 1 < nk;
         if (more) get(kt + 1);
-        if constexpr (PRECISE) mma_tile_mx_precise<TM, TN>(cur, wm0, wn0, acc);
+        if constexpr (MODE == MX_BF16) mma_tile_mx_precise<TM, TN>(cur, wm0, wn0, acc);
+        else if constexpr (MODE == MX_STEPWISE) mma_tile_mx_stepwise<TM, TN>(cur, wm0, wn0, acc);
         else mma_tile_mx<TM, TN>(cur, wm0, wn0, acc);
         if (more) put(nxt);
         __syncthreads();
@@ -372,13 +413,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
         ScalesGather dsa{(const uint32_t*)a.x_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
         LoadKC<TM, RowsGather> la(da);
         LoadScales<TM, ScalesGather> sa(dsa);
-        mainloop_mx<TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+        mainloop_mx<TM, M1_TN, MX_BF16>(la, lb, sa, sb, H / 128, smem, acc);
     } else {
         RowsDirect da{(const uint16_t*)a.x_q, H / 2, a.xrow0 + lo, hi - lo};
         ScalesDirect dsa{(const uint32_t*)a.x_s, H / 128, a.xrow0 + lo, hi - lo};
         LoadKC<TM, RowsDirect> la(da);
         LoadScales<TM, ScalesDirect> sa(dsa);
-        mainloop_mx<TM, M1_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+        mainloop_mx<TM, M1_TN, MX_BF16>(la, lb, sa, sb, H / 128, smem, acc);
     }
     AccPos<TM, M1_TN> pos;
     const int wn = threadIdx.x >> 7, lane = lane_id();
@@ -498,13 +539,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
         ScalesGather dsa{(const uint32_t*)a.dy_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
         LoadKC<TM, RowsGather> la(da);
         LoadScales<TM, ScalesGather> sa(dsa);
-        mainloop_mx<TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+        mainloop_mx<TM, M3_TN, MX_BF16>(la, lb, sa, sb, H / 128, smem, acc);
     } else {
         RowsDirect da{(const uint16_t*)a.dy_q, H / 2, a.dyrow0 + lo, hi - lo};
         ScalesDirect dsa{(const uint32_t*)a.dy_s, H / 128, a.dyrow0 + lo, hi - lo};
         LoadKC<TM, RowsDirect> la(da);
         LoadScales<TM, ScalesDirect> sa(dsa);
-        mainloop_mx<TM, M3_TN, true>(la, lb, sa, sb, H / 128, smem, acc);
+        mainloop_mx<TM, M3_TN, MX_BF16>(la, lb, sa, sb, H / 128, smem, acc);
     }
     AccPos<TM, M3_TN> pos;
     const int lane = lane_id();
@@ -890,7 +931,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx_deep(WgradMXArgs a) {
         LoadKCPad<XD_T> lb(rb, kcodes);
         LoadScalesPad<XD_T> sb(bs, kcodes / 32, n0, 0, kcodes / 32);
         f32x4 acc[XD_T / 32][XD_T / 32];
-        mainloop_mx<XD_T, XD_T, false>(la, lb, sa, sb, (kcodes + 127) / 128, smem, acc);
+        mainloop_mx<XD_T, XD_T, MX_ACC>(la, lb, sa, sb, (kcodes + 127) / 128, smem, acc);
         const bool hi_part = m0 >= a.msplit;
         WgradOut out = hi_part ? a.out_hi : a.out_lo;
         out.mode = wgrad_mode(out, e, g.blk_off ? g.off[e + 1] - g.off[e] : g.dense_rows);
