@@ -29,9 +29,11 @@ No function is "parity unpinned".
 from .routing import route
 from .schedule import schedule
 from .ffn import forward, backward, swiglu, swiglu_grad
+from .router import router_logits, router_backward
 from .mx import (mx_quantize, mx_dequantize, mx_roundtrip, e4m3_round, e4m3_encode,
                  e4m3_decode, E4M3_MAX, MX_BLOCK)
 
 __all__ = ["route", "schedule", "forward", "backward", "swiglu", "swiglu_grad",
+           "router_logits", "router_backward",
            "mx_quantize", "mx_dequantize", "mx_roundtrip", "e4m3_round", "e4m3_encode",
            "e4m3_decode", "E4M3_MAX", "MX_BLOCK"]
