@@ -240,6 +240,29 @@ MOE_API moe_status moe_schedule(const moe_config* cfg, const float* logits, cons
 MOE_API moe_status moe_schedule_noalloc(const moe_config* cfg, const float* logits,
                                         const moe_sched* sched, void* stream);
 
+/* The router projection upstream of the layer ([ALPHA] 二: it sits outside
+ * the layer, which starts from the logits; provided so that the logit
+ * gradient reaches the router weights and the tokens).
+ *   x [T, H] bf16, w_router [E, H] bf16 (row e = expert e), logits [T, E]
+ *   fp32 written: logits = x w_router^T, fp32 accumulation.  Needs no
+ *   workspace. */
+MOE_API moe_status moe_router_forward(const moe_config* cfg, const void* x, const void* w_router,
+                                      float* logits, void* stream);
+
+/* Backward of the router projection, after moe_backward produced d_logits:
+ *   d_logits [T, E] fp32 (read; rounded once to bf16 as the GEMM operand);
+ *   dx [T, H] bf16 read and written: dx += d_logits w_router (the stored dx
+ *   and the fp32 product summed in fp32, rounded once), so that dx becomes
+ *   the full input gradient of router + layer;
+ *   dw_router [E, H] bf16 written: d_logits^T x, summed over the tokens in
+ *   ascending order.
+ * Uses the layer's workspace (a bf16 copy of d_logits); in recompute mode
+ * it leaves the part that carries g, u from moe_forward to moe_backward
+ * alone. */
+MOE_API moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,
+                                       const float* d_logits, void* dx, void* dw_router,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
 /* Forward ([ALPHA] 一: dispatch, expert SwiGLU FFN, combine; 二: the
  * router-weighted reduction in a fixed order).
  *   x [T, H] bf16; y [T, H] bf16 (written);

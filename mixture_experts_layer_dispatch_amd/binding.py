@@ -32,6 +32,7 @@ EXPORTED = [
     "moe_device_supported", "moe_schedule", "moe_forward", "moe_backward",
     "moe_check_device_error", "moe_quantize_weights_mxfp8", "moe_profile_enable", "moe_profile_collect", "moe_profile_query",
     "moe_profile_names", "moe_profile_reset", "moe_workspace_region", "moe_schedule_noalloc",
+    "moe_router_forward", "moe_router_backward",
 ]
 
 FLAG_RECOMPUTE = 1
@@ -102,6 +103,8 @@ def lib() -> ctypes.CDLL:
         L.moe_device_supported.argtypes = []
         L.moe_schedule.argtypes = [cfgp, vp, ctypes.POINTER(moe_sched), vp, ctypes.c_size_t, vp]
         L.moe_schedule_noalloc.argtypes = [cfgp, vp, ctypes.POINTER(moe_sched), vp]
+        L.moe_router_forward.argtypes = [cfgp, vp, vp, vp, vp]
+        L.moe_router_backward.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.moe_forward.argtypes = [cfgp, ctypes.POINTER(moe_sched), vp, ctypes.POINTER(moe_weights),
                                   vp, ctypes.POINTER(moe_saved), vp, ctypes.c_size_t, vp]
         L.moe_backward.argtypes = [cfgp, ctypes.POINTER(moe_sched), ctypes.POINTER(moe_saved), vp,
@@ -404,6 +407,28 @@ def moe_schedule_noalloc(cfg: Config, logits: torch.Tensor, sched: dict, stream=
     _validate([("logits", logits, (cfg.T, cfg.E), torch.float32)] + _spec_sched(cfg, sched))
     _check(lib().moe_schedule_noalloc(ctypes.byref(cfg.c()), _p(logits), ctypes.byref(_sched(sched)),
                                       _stream(stream)), "moe_schedule_noalloc")
+
+
+def moe_router_forward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, logits: torch.Tensor,
+                       stream=None):
+    """logits [T, E] fp32 = x [T, H] @ w_router [E, H]^T."""
+    _validate([("x", x, (cfg.T, cfg.H), torch.bfloat16),
+               ("w_router", w_router, (cfg.E, cfg.H), torch.bfloat16),
+               ("logits", logits, (cfg.T, cfg.E), torch.float32)])
+    _check(lib().moe_router_forward(ctypes.byref(cfg.c()), _p(x), _p(w_router), _p(logits),
+                                    _stream(stream)), "moe_router_forward")
+
+
+def moe_router_backward(cfg: Config, x: torch.Tensor, w_router: torch.Tensor, d_logits: torch.Tensor,
+                        dx: torch.Tensor, dw_router: torch.Tensor, ws: torch.Tensor, stream=None):
+    """dx += d_logits @ w_router (in place); dw_router = d_logits^T @ x."""
+    bf = torch.bfloat16
+    _validate([("x", x, (cfg.T, cfg.H), bf), ("w_router", w_router, (cfg.E, cfg.H), bf),
+               ("d_logits", d_logits, (cfg.T, cfg.E), torch.float32), ("dx", dx, (cfg.T, cfg.H), bf),
+               ("dw_router", dw_router, (cfg.E, cfg.H), bf)] + _spec_ws(cfg, ws))
+    _check(lib().moe_router_backward(ctypes.byref(cfg.c()), _p(x), _p(w_router), _p(d_logits), _p(dx),
+                                     _p(dw_router), _p(ws), ws.numel(), _stream(stream)),
+           "moe_router_backward")
 
 
 def moe_forward(cfg: Config, sched: dict, x: torch.Tensor, weights: dict, y: torch.Tensor,

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmoe_mi355x.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["route_sched.hip", "elementwise.hip", "gemm.hip", "gemm_mx.hip", "mx.hip", "api.hip", "profile.hip"]
+SOURCES = ["route_sched.hip", "elementwise.hip", "gemm.hip", "gemm_mx.hip", "mx.hip", "router.hip", "api.hip",
+           "profile.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -47,6 +47,7 @@ struct Layout {
     size_t s_dgu32, s_h32, s_dguq, s_dgus, s_dxm;          // shared expert
     size_t wacc_g, wacc_u, wacc_d, wacc_sg, wacc_su, wacc_sd;
     size_t rc_g, rc_u, rc_sg, rc_su;  // recompute mode: one macrobatch's g, u (and the shared expert's)
+    size_t dl16;                      // router backward: bf16 d_logits [T, Ep]
 };
 
 moe_status make_geom(const moe_config* c, Geom& g) {
@@ -168,6 +169,7 @@ Layout make_layout(const Geom& g) {
         }
         L.sh = take(fe > be ? fe : be);
     }
+    L.dl16 = take((size_t)g.T * router_padded_experts(g.E) * 2);
     if (g.recompute) {
         const size_t es = g.mx ? 4 : 2;                 // fp32 in MXFP8 mode, as the saved ones
         L.rc_g = take(Sm * I * es);
@@ -633,6 +635,34 @@ moe_status moe_schedule_noalloc(const moe_config* cfg, const float* logits, cons
     if (launch_schedule(sched->topk_idx, g.T, g.E, g.k, g.M, g.mb, hh, bb, sched->counts,
                         sched->offsets, sched->mini_counts, sched->row_of_slot, sched->slot_of_row,
                         err, st))
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_router_forward(const moe_config* cfg, const void* x, const void* w_router, float* logits,
+                              void* stream) {
+    Geom g;
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    if (!bf16_ok(x) || !bf16_ok(w_router) || !logits || !aligned(logits, 4)) return MOE_ERR_INVALID_ARG;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    if (launch_router_logits(x, w_router, logits, g.T, g.H, g.E, (hipStream_t)stream)) return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_router_backward(const moe_config* cfg, const void* x, const void* w_router,
+                               const float* d_logits, void* dx, void* dw_router, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    Geom g;
+    Layout L;
+    moe_status s = common_checks(cfg, g, L, workspace, workspace_bytes);
+    if (s != MOE_OK) return s;
+    if (!bf16_ok(x) || !bf16_ok(w_router) || !bf16_ok(dx) || !bf16_ok(dw_router) || !d_logits ||
+        !aligned(d_logits, 4))
+        return MOE_ERR_INVALID_ARG;
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    if (launch_router_backward(x, w_router, d_logits, dx, dw_router, (char*)workspace + L.dl16, g.T, g.H,
+                               g.E, (hipStream_t)stream))
         return MOE_ERR_HIP;
     return MOE_OK;
 }

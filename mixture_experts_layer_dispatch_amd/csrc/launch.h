@@ -281,6 +281,12 @@ int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st);
 int launch_gemm_gate_up_mx(const GemmGateUpMXArgs& a, hipStream_t st);
 int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st);
 
+// router.hip
+int router_padded_experts(int E);
+int launch_router_logits(const void* x, const void* wr, float* logits, int T, int H, int E, hipStream_t st);
+int launch_router_backward(const void* x, const void* wr, const float* d_logits, void* dx, void* dwr,
+                           void* dl16, int T, int H, int E, hipStream_t st);
+
 // gemm.hip
 int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st);
 int launch_gemm_down(const GemmDownArgs& a, hipStream_t st);

@@ -35,7 +35,7 @@ TABLE_BITS = 20
 _M32 = 0xFFFFFFFF
 
 # stream ids
-S_LOGITS, S_X, S_WGATE, S_WUP, S_WDOWN, S_SGATE, S_SUP, S_SDOWN, S_DY, S_PERM = range(1, 11)
+S_LOGITS, S_X, S_WGATE, S_WUP, S_WDOWN, S_SGATE, S_SUP, S_SDOWN, S_DY, S_PERM, S_ROUTER = range(1, 12)
 
 _TABLES: dict = {}
 
@@ -221,6 +221,11 @@ def shared_weights(shape: MoEShape, device="cpu"):
     wu = normal((I, H), shape.seed, S_SUP, 1.0 / math.sqrt(H), torch.bfloat16, device)
     wd = normal((H, I), shape.seed, S_SDOWN, 1.0 / math.sqrt(I), torch.bfloat16, device)
     return wg, wu, wd
+
+
+def router_weights(shape: MoEShape, device="cpu") -> torch.Tensor:
+    """bf16 [E, H] router projection (row e = expert e), std 1/sqrt(H)."""
+    return normal((shape.E, shape.H), shape.seed, S_ROUTER, 1.0 / math.sqrt(shape.H), torch.bfloat16, device)
 
 
 def custom_shape(name, T, H, I, E, k, seed, **kw) -> MoEShape:
