@@ -31,9 +31,11 @@ from .schedule import schedule
 from .ffn import forward, backward, swiglu, swiglu_grad
 from .router import router_logits, router_backward
 from .mx import (mx_quantize, mx_dequantize, mx_roundtrip, e4m3_round, e4m3_encode,
-                 e4m3_decode, E4M3_MAX, MX_BLOCK)
+                 e4m3_decode, E4M3_MAX, MX_BLOCK, mxfp4_quantize, mxfp4_dequantize,
+                 mxfp4_roundtrip, e2m1_round, e2m1_encode, e2m1_decode)
 
 __all__ = ["route", "schedule", "forward", "backward", "swiglu", "swiglu_grad",
            "router_logits", "router_backward",
            "mx_quantize", "mx_dequantize", "mx_roundtrip", "e4m3_round", "e4m3_encode",
-           "e4m3_decode", "E4M3_MAX", "MX_BLOCK"]
+           "e4m3_decode", "E4M3_MAX", "MX_BLOCK", "mxfp4_quantize", "mxfp4_dequantize",
+           "mxfp4_roundtrip", "e2m1_round", "e2m1_encode", "e2m1_decode"]

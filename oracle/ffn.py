@@ -21,6 +21,10 @@ Backward, with dy_t the upstream gradient:
   dW_up[e] = sum du x_t^T
   d_logit[t, idx[t, j]] = w_j (dw_j - sum_i w_i dw_i); zero for unselected experts.
 
+MXFP4-weight mode (mx="w4", forward only): the weights of every forward GEMM
+in MXFP4 (E2M1 elements, E8M0 scales per 32 along K), the activations (x, h)
+in MXFP8, both along K.
+
 MXFP8 mode quantises each GEMM operand along that GEMM's reduction axis
 (oracle.mx) before float64 arithmetic.  Every product of the layer goes
 through mm(A, B, mx) = Q(A along its last axis) @ Q(B along its first axis),
@@ -44,7 +48,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .mx import mx_roundtrip
+from .mx import mx_roundtrip, mxfp4_roundtrip
 
 
 def _f64(a):
@@ -53,8 +57,12 @@ def _f64(a):
 
 def mm(A, B, mx=False):
     """A [.., K] @ B [K, ..]; in MXFP8 mode both operands are first quantised
-    along K, the contraction axis (A along its last axis, B along its first)."""
+    along K, the contraction axis (A along its last axis, B along its first).
+    mx == "w4" (the MXFP4-weight forward): A, the activations, in MXFP8 and B,
+    the weights, in MXFP4, both along K."""
     A, B = _f64(A), _f64(B)
+    if mx == "w4":
+        return mx_roundtrip(A, -1) @ mxfp4_roundtrip(B, 0)
     if mx:
         A = mx_roundtrip(A, -1)
         B = mx_roundtrip(B, 0)
@@ -154,6 +162,8 @@ def backward(x, wg, wu, wd, idx, w, dy, shared=None, mx=False, sched=None,
     (dicts by expert) and, when shared is given and tokens is None, the shared
     expert's dW_sg, dW_su, dW_sd.
     """
+    if mx == "w4":
+        raise ValueError("the MXFP4-weight variant is forward-only")
     idx = np.asarray(idx)
     T, k = idx.shape
     all_tokens = tokens is None

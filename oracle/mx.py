@@ -109,3 +109,67 @@ def mx_roundtrip(v, axis: int = -1):
     """Quantise then dequantise v along `axis` (float64 result)."""
     c, s = mx_quantize(v, axis)
     return mx_dequantize(c, s, axis)
+
+
+# ------------------------------------------------------------------ MXFP4
+# The same block structure with E2M1 elements (OCP MX v1.0, MXFP4): 1 sign
+# bit, 2 exponent bits (bias 1), 1 mantissa bit; magnitudes 0, 0.5, 1, 1.5,
+# 2, 3, 4, 6; scale 2**(floor(log2(amax)) - 2), 2 being the exponent of the
+# largest value (6 = 1.5 * 2**2); round to nearest even, saturate to +-6.
+E2M1_MAX = 6.0
+E2M1_EMAX = 2
+E2M1_GRID = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+
+
+def e2m1_round(v):
+    """Round float64 values to the nearest-even E2M1 value, saturating at 6."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    _, q = np.frexp(a)                      # a = f * 2**q, f in [0.5, 1)
+    e = np.maximum(q - 1, 0)                # below 1 the quantum is that of [1, 2)
+    quantum = np.ldexp(1.0, e - 1)          # one mantissa bit
+    r = np.round(a / quantum) * quantum     # np.round rounds halves to even
+    r = np.minimum(r, E2M1_MAX)
+    return np.copysign(r, v)
+
+
+def e2m1_encode(r):
+    """Code (uint8, 0..15) of E2M1 values r (which must lie on the grid)."""
+    r = np.asarray(r, dtype=np.float64)
+    a = np.abs(r)
+    idx = np.searchsorted(E2M1_GRID, a)
+    if not np.all((idx < 8) & (E2M1_GRID[np.minimum(idx, 7)] == a)):
+        raise ValueError("value not on the E2M1 grid")
+    return (np.signbit(r).astype(np.uint8) << 3) | idx.astype(np.uint8)
+
+
+def e2m1_decode(code):
+    c = np.asarray(code, dtype=np.int64)
+    return np.where(c & 8, -1.0, 1.0) * E2M1_GRID[c & 7]
+
+
+def mxfp4_quantize(v, axis: int = -1):
+    """MXFP4 along `axis` in blocks of 32: (codes uint8 0..15, same shape as v;
+    E8M0 scales uint8 with the axis length replaced by the number of blocks)."""
+    v = np.moveaxis(np.asarray(v, dtype=np.float64), axis, -1)
+    b, n = _blocks_last(v)
+    amax = np.max(np.abs(b), axis=-1)
+    _, q = np.frexp(amax)
+    s = np.where(amax > 0, (q - 1) - E2M1_EMAX, -127)
+    s = np.clip(s, -127, 127)
+    X = np.ldexp(1.0, s)[..., None]
+    codes = e2m1_encode(e2m1_round(b / X)).reshape(b.shape[:-2] + (-1,))[..., :n]
+    return np.moveaxis(codes, -1, axis), np.moveaxis((s + 127).astype(np.uint8), -1, axis)
+
+
+def mxfp4_dequantize(codes, scales, axis: int = -1):
+    c = np.moveaxis(np.asarray(codes), axis, -1)
+    sc = np.moveaxis(np.asarray(scales), axis, -1).astype(np.int64)
+    n = c.shape[-1]
+    Xe = np.repeat(np.ldexp(1.0, sc - 127), MX_BLOCK, axis=-1)[..., :n]
+    return np.moveaxis(e2m1_decode(c) * Xe, -1, axis)
+
+
+def mxfp4_roundtrip(v, axis: int = -1):
+    c, s = mxfp4_quantize(v, axis)
+    return mxfp4_dequantize(c, s, axis)

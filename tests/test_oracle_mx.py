@@ -352,3 +352,116 @@ def test_mx_weight_gradients_block_rows_per_macrobatch_group():
         assert not np.array_equal(bw[n][0], ex[n][0]), n
     for n in ("dW_sg", "dW_su", "dW_sd"):
         assert not np.array_equal(bw[n], ex[n]), n
+
+
+# ------------------------------------------------------------------ MXFP4 (the weight variant)
+def _golden_rows(name):
+    rows = []
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#")[0].strip()
+        if line:
+            rows.append(line.split())
+    return rows
+
+
+def test_e2m1_codes_match_the_hand_derived_table():
+    rows = _golden_rows("e2m1_codes.txt")
+    v = np.array([float(r[0]) for r in rows])
+    r = mx.e2m1_round(v)
+    np.testing.assert_array_equal(r, [float(x[2]) for x in rows])
+    np.testing.assert_array_equal(mx.e2m1_encode(r), [int(x[1], 16) for x in rows])
+    np.testing.assert_array_equal(mx.e2m1_decode(mx.e2m1_encode(r)), r)
+
+
+def test_mxfp4_scales_match_the_hand_derived_table():
+    for row in _golden_rows("mx4_scales.txt"):
+        amax, want = float(row[0]), int(row[1])
+        block = np.zeros(32)
+        block[5] = amax
+        block[9] = -amax / 3
+        _, s = mx.mxfp4_quantize(block)
+        assert int(s[0]) == want, (amax, int(s[0]), want)
+
+
+def test_mxfp4_roundtrip_and_error_bound():
+    rng = np.random.default_rng(12)
+    # blocks of grid values times a power of two are exact
+    v = rng.choice(np.concatenate([mx.E2M1_GRID, -mx.E2M1_GRID]), size=(16, 64))
+    v[:, ::32] = 6.0                       # every block holds its maximum
+    v = v * np.exp2(rng.integers(-20, 20, size=(16, 1)))
+    np.testing.assert_array_equal(mx.mxfp4_roundtrip(v, axis=1), v)
+    # Gaussian blocks: every element within half a quantum of its block
+    g = rng.standard_normal((64, 96))
+    q = mx.mxfp4_roundtrip(g, axis=1)
+    c, s = mx.mxfp4_quantize(g, axis=1)
+    X = np.repeat(np.exp2(s.astype(np.float64) - 127), 32, axis=1)
+    a = np.abs(g) / X
+    quantum = np.where(a < 2, 0.5, np.where(a < 4, 1.0, 2.0)) * X
+    inside = a <= 6.0
+    assert np.all((np.abs(q - g) <= quantum / 2)[inside])
+    # the scale rule leaves a block's largest magnitudes in [4, 8) quanta; those
+    # above 6 saturate to 6
+    np.testing.assert_array_equal(np.abs(q)[~inside], 6.0 * X[~inside])
+    # the quantiser is along the given axis only
+    np.testing.assert_array_equal(mx.mxfp4_roundtrip(g.T, axis=0), q.T)
+
+
+def _w4_exact_layer(seed, T=32, H=64, I=32, E=2):
+    """Operands exact in MXFP4 (weights) and MXFP8 (activations) along K:
+    W_gate's one nonzero per row from {48, 64, 96, 128} (g >= 48, so
+    sigma(g) == 1 in float64), the other entries and x in {-1, 0, 1}."""
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-1, 2, (T, H)).astype(np.float64)
+    x[:, 0] = 1.0
+    wg = np.zeros((E, I, H))
+    wg[:, :, 0] = rng.choice([48.0, 64.0, 96.0, 128.0], size=(E, I))
+    wu = np.zeros((E, I, H))
+    wd = np.zeros((E, H, I))
+    for e in range(E):
+        for i in range(I):
+            wu[e, i, rng.choice(np.arange(1, H), size=2, replace=False)] = rng.choice([-1.0, 1.0], size=2)
+            wd[e, rng.choice(np.arange(H), size=2, replace=False), i] = rng.choice([-1.0, 1.0], size=2)
+    L = rng.standard_normal((T, E)).astype(np.float32)
+    return x, wg, wu, wd, L
+
+
+def test_w4_layer_equals_the_exact_layer_on_representable_operands(monkeypatch):
+    x, wg, wu, wd, L = _w4_exact_layer(7)
+    idx, w = oracle.route(L, 1)
+    ex = oracle.forward(x, wg, wu, wd, idx, w)["y"]
+    np.testing.assert_array_equal(oracle.forward(x, wg, wu, wd, idx, w, mx="w4")["y"], ex)
+    # weight rows 2^20 apart: exact along K (H) only; a weight quantised along
+    # the wrong axis breaks it
+    f = np.where(np.arange(wg.shape[1]) % 2, 2.0 ** 20, 1.0)[None, :, None]
+    wg2, wu2 = wg * f, wu / f
+    np.testing.assert_array_equal(oracle.forward(x, wg2, wu2, wd, idx, w, mx="w4")["y"], ex)
+
+    def wrong_axis(A, B, mx=False):
+        return oracle.mx_roundtrip(np.asarray(A, np.float64), -1) @ oracle.mxfp4_roundtrip(
+            np.asarray(B, np.float64), -1)
+
+    monkeypatch.setattr(oracle.ffn, "mm", wrong_axis)
+    assert not np.array_equal(oracle.forward(x, wg2, wu2, wd, idx, w, mx="w4")["y"], ex)
+
+
+def test_w4_layer_rounds_the_weights_to_e2m1_not_e4m3(monkeypatch):
+    """W_up entries of 1.25 are exact in E4M3 but not in E2M1: a block holding
+    +-1.25 as its largest values gets scale 2^-2, 1.25 / 0.25 = 5 rounds to 4
+    (ties to even), so the MXFP4 layer equals the exact layer with 1.0."""
+    x, wg, wu, wd, L = _w4_exact_layer(8)
+    idx, w = oracle.route(L, 1)
+    wu5 = wu * 1.25
+    got = oracle.forward(x, wg, wu5, wd, idx, w, mx="w4")["y"]
+    np.testing.assert_array_equal(got, oracle.forward(x, wg, wu, wd, idx, w)["y"])
+    assert not np.array_equal(got, oracle.forward(x, wg, wu5, wd, idx, w)["y"])
+    # planted mistake: the weights in MXFP8 instead
+    monkeypatch.setattr(oracle.ffn, "mm", lambda A, B, mx=False: oracle.mx_roundtrip(
+        np.asarray(A, np.float64), -1) @ oracle.mx_roundtrip(np.asarray(B, np.float64), 0))
+    assert not np.array_equal(oracle.forward(x, wg, wu5, wd, idx, w, mx="w4")["y"], got)
+
+
+def test_w4_backward_is_refused():
+    x, wg, wu, wd, L = _w4_exact_layer(9)
+    idx, w = oracle.route(L, 1)
+    with pytest.raises(ValueError):
+        oracle.backward(x, wg, wu, wd, idx, w, x, mx="w4")
