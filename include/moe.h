@@ -70,7 +70,10 @@ typedef enum moe_status {
 
 typedef enum moe_precision {
     MOE_PREC_BF16 = 0,   /* bf16 operands, fp32 accumulation                             */
-    MOE_PREC_MXFP8 = 1   /* E4M3 operands with E8M0 scales per 32 elements along K       */
+    MOE_PREC_MXFP8 = 1,  /* E4M3 operands with E8M0 scales per 32 elements along K       */
+    MOE_PREC_MXFP4 = 2   /* forward only: weights E2M1 with E8M0 scales per 32 along K,  */
+                         /* activations (x, h) MXFP8; moe_backward returns               */
+                         /* MOE_ERR_UNSUPPORTED                                          */
 } moe_precision;
 
 /* Layer shape and the tunables of [AREX] (third decision) / [ALPHA] 四, minus
@@ -142,6 +145,19 @@ typedef struct moe_weights_mx {
     const void* s_down_tq; const void* s_down_ts;
 } moe_weights_mx;
 
+/* MXFP4 forward weights (written by moe_quantize_weights_mxfp4): E2M1 codes,
+ * two per byte (element 2q in the low nibble of byte q), row-major
+ * [rows, K/2] bytes, and E8M0 scales per 32 codes along K in the K-step-major
+ * layout of moe_weights_mx ([K/128, rows, 4] bytes per matrix). */
+typedef struct moe_weights_mx4 {
+    const void* w_gate_q;  const void* w_gate_s;   /* [E, I, H/2], [E, H/128, I, 4] */
+    const void* w_up_q;    const void* w_up_s;     /* [E, I, H/2], [E, H/128, I, 4] */
+    const void* w_down_q;  const void* w_down_s;   /* [E, H, I/2], [E, I/128, H, 4] */
+    const void* s_gate_q;  const void* s_gate_s;   /* the shared expert (if n_shared)  */
+    const void* s_up_q;    const void* s_up_s;
+    const void* s_down_q;  const void* s_down_s;
+} moe_weights_mx4;
+
 /* Weights.  bf16 arrays are always given (the MXFP8 backward writes bf16
  * gradients of them and the quantiser reads them); `mx` is required when
  * cfg->precision is MOE_PREC_MXFP8 and ignored otherwise.  The shared
@@ -154,6 +170,7 @@ typedef struct moe_weights {
     const void* s_up;      /* [I, H]    */
     const void* s_down;    /* [H, I]    */
     const moe_weights_mx* mx;
+    const moe_weights_mx4* mx4;  /* required when cfg->precision is MOE_PREC_MXFP4 */
 } moe_weights;
 
 /* What the forward keeps for the backward, rows in schedule row order:
@@ -298,6 +315,17 @@ MOE_API moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, c
  * workspace. */
 MOE_API moe_status moe_quantize_weights_mxfp8(const moe_config* cfg, const moe_weights* w,
                                               const moe_weights_mx* out, void* stream);
+
+/* MXFP4 weight quantisation for the MXFP4-weight forward ([AREX], section
+ * "一个代码编辑器，怎么会去写 GPU 内核？", names the authors' earlier MXFP8 and
+ * NVFP4 training kernels; MXFP4 is the OCP block format of the same E2M1
+ * element, with E8M0 scales per 32): reads w's bf16 arrays and
+ * writes every array of *out (caller-allocated, layouts as in
+ * moe_weights_mx4), per 32-element block along K: scale 2^(floor(log2
+ * max|v|) - 2) clamped to [2^-127, 2^127], elements rounded to nearest-even
+ * E2M1 and saturated to +-6.  Enqueued on `stream`; needs no workspace. */
+MOE_API moe_status moe_quantize_weights_mxfp4(const moe_config* cfg, const moe_weights* w,
+                                              const moe_weights_mx4* out, void* stream);
 
 /* Reads and clears the sticky device error word that kernels set when a
  * caller-built schedule holds an out-of-range expert, slot or row (those

@@ -26,13 +26,14 @@ MOE_ERR_UNSUPPORTED = 6
 
 PREC_BF16 = 0
 PREC_MXFP8 = 1
+PREC_MXFP4 = 2          # forward only: MXFP4 weights, MXFP8 activations
 
 EXPORTED = [
     "moe_status_string", "moe_validate_config", "moe_ring_rows", "moe_workspace_size",
     "moe_device_supported", "moe_schedule", "moe_forward", "moe_backward",
     "moe_check_device_error", "moe_quantize_weights_mxfp8", "moe_profile_enable", "moe_profile_collect", "moe_profile_query",
     "moe_profile_names", "moe_profile_reset", "moe_workspace_region", "moe_schedule_noalloc",
-    "moe_router_forward", "moe_router_backward",
+    "moe_router_forward", "moe_router_backward", "moe_quantize_weights_mxfp4",
 ]
 
 FLAG_RECOMPUTE = 1
@@ -68,10 +69,18 @@ class moe_weights_mx(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in MX_FIELDS]
 
 
+MX4_FIELDS = ("w_gate_q", "w_gate_s", "w_up_q", "w_up_s", "w_down_q", "w_down_s",
+              "s_gate_q", "s_gate_s", "s_up_q", "s_up_s", "s_down_q", "s_down_s")
+
+
+class moe_weights_mx4(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in MX4_FIELDS]
+
+
 class moe_weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
                 ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")] + [
-                ("mx", ctypes.POINTER(moe_weights_mx))]
+                ("mx", ctypes.POINTER(moe_weights_mx)), ("mx4", ctypes.POINTER(moe_weights_mx4))]
 
 
 class moe_saved(ctypes.Structure):
@@ -113,6 +122,8 @@ def lib() -> ctypes.CDLL:
         L.moe_check_device_error.argtypes = [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_int32)]
         L.moe_quantize_weights_mxfp8.argtypes = [cfgp, ctypes.POINTER(moe_weights),
                                                  ctypes.POINTER(moe_weights_mx), vp]
+        L.moe_quantize_weights_mxfp4.argtypes = [cfgp, ctypes.POINTER(moe_weights),
+                                                 ctypes.POINTER(moe_weights_mx4), vp]
         L.moe_profile_enable.argtypes = [ctypes.c_int]
         L.moe_profile_collect.argtypes = []
         L.moe_profile_query.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_int64),
@@ -235,11 +246,11 @@ def workspace_region(cfg: Config, name: str) -> tuple:
 
 
 def alloc_saved(cfg: Config, device="cuda") -> dict:
-    """g, u (and the shared expert's): bf16 in BF16 mode, fp32 in MXFP8 mode;
+    """g, u (and the shared expert's): bf16 in BF16 mode, fp32 in the MX modes;
     nothing in recompute mode."""
     if cfg.recompute:
         return {}
-    dt = torch.float32 if cfg.precision == PREC_MXFP8 else torch.bfloat16
+    dt = torch.float32 if cfg.precision in (PREC_MXFP8, PREC_MXFP4) else torch.bfloat16
     bf = dict(dtype=dt, device=device)
     out = {"g": torch.empty(cfg.S, cfg.I, **bf), "u": torch.empty(cfg.S, cfg.I, **bf)}
     if cfg.n_shared:
@@ -268,14 +279,22 @@ def _weights_mx(q: dict) -> moe_weights_mx:
     return moe_weights_mx(*[(q[n].data_ptr() if q.get(n) is not None else None) for n in MX_FIELDS])
 
 
+def _weights_mx4(q: dict) -> moe_weights_mx4:
+    return moe_weights_mx4(*[(q[n].data_ptr() if q.get(n) is not None else None) for n in MX4_FIELDS])
+
+
 def _weights(w: dict):
-    """(moe_weights, keep-alive); w may hold an "mx" dict of quantised arrays."""
+    """(moe_weights, keep-alive); w may hold an "mx" dict (MXFP8) and an "mx4"
+    dict (MXFP4) of quantised arrays."""
     mx = _weights_mx(w["mx"]) if w.get("mx") is not None else None
+    mx4 = _weights_mx4(w["mx4"]) if w.get("mx4") is not None else None
     st = moe_weights(*[(w[n].data_ptr() if w.get(n) is not None else None)
                        for n in ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")])
     if mx is not None:
         st.mx = ctypes.pointer(mx)
-    return st, mx
+    if mx4 is not None:
+        st.mx4 = ctypes.pointer(mx4)
+    return st, (mx, mx4)
 
 
 def _saved(s) -> moe_saved:
@@ -367,12 +386,46 @@ def _spec_weights_mx(cfg: Config, q, forward: bool = True, transposed: bool = Tr
     return out
 
 
+def _mx4_shapes(cfg: Config):
+    """{field: shape} of every MXFP4 weight array (uint8): codes two per byte."""
+    E, H, I = cfg.E, cfg.H, cfg.I
+    out = {}
+    for prefix, lead in (("w_", (E,)), ("s_", ())):
+        if prefix == "s_" and not cfg.n_shared:
+            continue
+        for name, rows, K in (("gate_", I, H), ("up_", I, H), ("down_", H, I)):
+            out[prefix + name + "q"] = (*lead, rows, K // 2)
+            out[prefix + name + "s"] = (*lead, K // 128, rows, 4)
+    return out
+
+
+def _spec_weights_mx4(cfg: Config, q):
+    if q is None:
+        raise ValueError("weights['mx4']: the MXFP4 path needs the quantised weights")
+    return [(f"mx4[{n!r}]", q.get(n), shape, torch.uint8) for n, shape in _mx4_shapes(cfg).items()]
+
+
+def alloc_weights_mx4(cfg: Config, device="cuda") -> dict:
+    """Buffers of every MXFP4 weight array (uint8): E2M1 codes two per byte
+    [.., rows, K/2], scales K-step-major [.., K/128, rows, 4]."""
+    return {n: torch.empty(*shape, dtype=torch.uint8, device=device) for n, shape in _mx4_shapes(cfg).items()}
+
+
+def moe_quantize_weights_mxfp4(cfg: Config, weights: dict, out: dict, stream=None):
+    _validate(_spec_weights(cfg, weights) + _spec_weights_mx4(cfg, out))
+    wst, _keep = _weights(weights)
+    mx4 = _weights_mx4(out)
+    _check(lib().moe_quantize_weights_mxfp4(ctypes.byref(cfg.c()), ctypes.byref(wst),
+                                            ctypes.byref(mx4), _stream(stream)),
+           "moe_quantize_weights_mxfp4")
+
+
 def _spec_saved(cfg: Config, s: dict):
     if cfg.recompute:
         return []                  # nothing is saved: the backward recomputes g, u
     if s is None:
         raise ValueError("saved: missing (only recompute mode saves nothing)")
-    dt = torch.float32 if cfg.precision == PREC_MXFP8 else torch.bfloat16
+    dt = torch.float32 if cfg.precision in (PREC_MXFP8, PREC_MXFP4) else torch.bfloat16
     out = [("saved['g']", s.get("g"), (cfg.S, cfg.I), dt),
            ("saved['u']", s.get("u"), (cfg.S, cfg.I), dt)]
     if cfg.n_shared:
@@ -438,6 +491,8 @@ def moe_forward(cfg: Config, sched: dict, x: torch.Tensor, weights: dict, y: tor
     specs += _spec_weights(cfg, weights)
     if cfg.precision == PREC_MXFP8:
         specs += _spec_weights_mx(cfg, weights.get("mx"), forward=True, transposed=False)
+    if cfg.precision == PREC_MXFP4:
+        specs += _spec_weights_mx4(cfg, weights.get("mx4"))
     _validate(specs + _spec_saved(cfg, saved) + _spec_ws(cfg, ws))
     wst, _keep = _weights(weights)
     _check(lib().moe_forward(ctypes.byref(cfg.c()), ctypes.byref(_sched(sched)), _p(x),

@@ -24,7 +24,7 @@ struct Geom {
     int T, H, I, E, k, M, mb, n_macro, n_mini, Sm, Smb, S, P;
     int64_t ring_rows;
     int halves;
-    bool shared, mx, recompute;
+    bool shared, mx, w4, recompute;
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -56,7 +56,8 @@ moe_status make_geom(const moe_config* c, Geom& g) {
     if (c->E < 1 || c->E > kMaxExperts || c->k < 1 || c->k > c->E || c->k > kMaxTopK)
         return MOE_ERR_INVALID_ARG;
     if (c->n_shared != 0 && c->n_shared != 1) return MOE_ERR_INVALID_ARG;
-    if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8) return MOE_ERR_INVALID_ARG;
+    if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8 && c->precision != MOE_PREC_MXFP4)
+        return MOE_ERR_INVALID_ARG;
     if ((c->flags & ~MOE_FLAG_RECOMPUTE) != 0 || c->macrobatch < 0 || c->minibatch < 0 ||
         c->capacity_rows < 0)
         return MOE_ERR_INVALID_ARG;
@@ -75,7 +76,8 @@ moe_status make_geom(const moe_config* c, Geom& g) {
     g.S = (int)S;
     g.P = dgrad_col_tiles(g.I);
     g.shared = c->n_shared == 1;
-    g.mx = c->precision == MOE_PREC_MXFP8;
+    g.mx = c->precision != MOE_PREC_BF16;           // MXFP8 activations in both MX modes
+    g.w4 = c->precision == MOE_PREC_MXFP4;
     g.recompute = (c->flags & MOE_FLAG_RECOMPUTE) != 0;
     if (c->capacity_rows) {
         if (c->capacity_rows < g.Sm) return MOE_ERR_CAPACITY;
@@ -287,7 +289,21 @@ GU gu_shared(const Geom& g, const Layout& L, const Ptrs& P, const moe_saved* sav
 moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_sched* sched,
                       const void* x, const moe_weights* w, void* y, const moe_saved* saved,
                       hipStream_t st) {
-    const moe_weights_mx* wq = w->mx;
+    // forward weights: MXFP8 codes, or E2M1 codes (two per byte) in MXFP4 mode;
+    // the scales have the same layout in both
+    struct FwdW {
+        const void *gq, *gs, *uq, *us, *dq, *ds, *sgq, *sgs, *suq, *sus, *sdq, *sds;
+    } fw;
+    if (g.w4) {
+        const moe_weights_mx4* q = w->mx4;
+        fw = {q->w_gate_q, q->w_gate_s, q->w_up_q, q->w_up_s, q->w_down_q, q->w_down_s,
+              q->s_gate_q, q->s_gate_s, q->s_up_q, q->s_up_s, q->s_down_q, q->s_down_s};
+    } else {
+        const moe_weights_mx* q = w->mx;
+        fw = {q->w_gate_q, q->w_gate_s, q->w_up_q, q->w_up_s, q->w_down_q, q->w_down_s,
+              q->s_gate_q, q->s_gate_s, q->s_up_q, q->s_up_s, q->s_down_q, q->s_down_s};
+    }
+    const int w4 = g.w4 ? 1 : 0;
     int32_t* err = P.err();
     const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
     uint8_t* xq = (uint8_t*)(P.ws + L.xq);
@@ -304,13 +320,13 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
         if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
         const GU keep = gu_routed(g, L, P, saved, m, true);
-        GemmGateUpMXArgs a1{grp, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
-                            (const uint8_t*)wq->w_gate_q, (const uint8_t*)wq->w_gate_s,
-                            (const uint8_t*)wq->w_up_q, (const uint8_t*)wq->w_up_s, g.H, g.I,
-                            (float*)keep.g, (float*)keep.u, keep.row0, hq, hs};
+        GemmGateUpMXArgs a1{grp, w4, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
+                            (const uint8_t*)fw.gq, (const uint8_t*)fw.gs, (const uint8_t*)fw.uq,
+                            (const uint8_t*)fw.us, g.H, g.I, (float*)keep.g, (float*)keep.u, keep.row0,
+                            hq, hs};
         if (launch_gemm_gate_up_mx(a1, st)) return MOE_ERR_HIP;
-        GemmDownMXArgs a2{grp, hq, hs, (const uint8_t*)wq->w_down_q, (const uint8_t*)wq->w_down_s,
-                          g.H, g.I, obuf, {sched->topk_w, sched->slot_of_row, grow0, g.S}};
+        GemmDownMXArgs a2{grp, w4, hq, hs, (const uint8_t*)fw.dq, (const uint8_t*)fw.ds, g.H, g.I, obuf,
+                          {sched->topk_w, sched->slot_of_row, grow0, g.S}};
         if (launch_gemm_down_mx(a2, st)) return MOE_ERR_HIP;
         const uint16_t* sh_o = nullptr;
         if (g.shared) {
@@ -320,13 +336,13 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
             uint16_t* so = (uint16_t*)(sh + L.s_o);
             GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
             const GU skeep = gu_shared(g, L, P, saved, m, true);
-            GemmGateUpMXArgs s1{dense, xq, xs, t0, 0, nullptr, 0, g.k, g.S,
-                                (const uint8_t*)wq->s_gate_q, (const uint8_t*)wq->s_gate_s,
-                                (const uint8_t*)wq->s_up_q, (const uint8_t*)wq->s_up_s, g.H, g.I,
-                                (float*)skeep.g, (float*)skeep.u, skeep.row0, shq, shs};
+            GemmGateUpMXArgs s1{dense, w4, xq, xs, t0, 0, nullptr, 0, g.k, g.S,
+                                (const uint8_t*)fw.sgq, (const uint8_t*)fw.sgs, (const uint8_t*)fw.suq,
+                                (const uint8_t*)fw.sus, g.H, g.I, (float*)skeep.g, (float*)skeep.u,
+                                skeep.row0, shq, shs};
             if (launch_gemm_gate_up_mx(s1, st)) return MOE_ERR_HIP;
-            GemmDownMXArgs s2{dense, shq, shs, (const uint8_t*)wq->s_down_q,
-                              (const uint8_t*)wq->s_down_s, g.H, g.I, so, {nullptr, nullptr, 0, 0}};
+            GemmDownMXArgs s2{dense, w4, shq, shs, (const uint8_t*)fw.sdq, (const uint8_t*)fw.sds, g.H, g.I,
+                              so, {nullptr, nullptr, 0, 0}};
             if (launch_gemm_down_mx(s2, st)) return MOE_ERR_HIP;
             sh_o = so;
         }
@@ -401,7 +417,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         if (g.recompute && m != g.n_macro - 1) {
             // recompute this macrobatch's g, u (h codes go to scratch that the
             // dgrad below overwrites)
-            GemmGateUpMXArgs r1{grp, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
+            GemmGateUpMXArgs r1{grp, 0, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
                                 (const uint8_t*)wq->w_gate_q, (const uint8_t*)wq->w_gate_s,
                                 (const uint8_t*)wq->w_up_q, (const uint8_t*)wq->w_up_s, g.H, g.I,
                                 (float*)gu.g, (float*)gu.u, 0, dguq, dgus};
@@ -430,7 +446,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
             uint16_t* sdx = (uint16_t*)(sh + L.s_dxm);
             const GU sgu = gu_shared(g, L, P, saved, m, false);
             if (g.recompute && m != g.n_macro - 1) {
-                GemmGateUpMXArgs r2{dense, xq, xs, t0, 0, nullptr, 0, g.k, g.S,
+                GemmGateUpMXArgs r2{dense, 0, xq, xs, t0, 0, nullptr, 0, g.k, g.S,
                                     (const uint8_t*)wq->s_gate_q, (const uint8_t*)wq->s_gate_s,
                                     (const uint8_t*)wq->s_up_q, (const uint8_t*)wq->s_up_s, g.H, g.I,
                                     (float*)sgu.g, (float*)sgu.u, 0, sdguq, sdgus};
@@ -680,7 +696,18 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
     if (g.shared && (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down)))
         return MOE_ERR_INVALID_ARG;
     const moe_weights_mx* wq = w->mx;
-    if (g.mx) {
+    if (g.w4) {
+        const moe_weights_mx4* q = w->mx4;
+        if (!q) return MOE_ERR_INVALID_ARG;
+        const void* need[] = {q->w_gate_q, q->w_up_q, q->w_down_q, q->w_gate_s, q->w_up_s, q->w_down_s};
+        for (const void* p : need)
+            if (!p || !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+        if (g.shared) {
+            const void* needs[] = {q->s_gate_q, q->s_up_q, q->s_down_q, q->s_gate_s, q->s_up_s, q->s_down_s};
+            for (const void* p : needs)
+                if (!p || !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+        }
+    } else if (g.mx) {
         if (!wq || !bf16_ok(wq->w_gate_q) || !wq->w_gate_s || !bf16_ok(wq->w_up_q) || !wq->w_up_s ||
             !bf16_ok(wq->w_down_q) || !wq->w_down_s)
             return MOE_ERR_INVALID_ARG;
@@ -748,6 +775,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
     Layout L;
     moe_status s = common_checks(cfg, g, L, workspace, workspace_bytes);
     if (s != MOE_OK) return s;
+    if (g.w4) return MOE_ERR_UNSUPPORTED;       // the MXFP4-weight variant is forward-only
     if (!sched_ok(sched) || !saved_ok(g, saved) || !w || !gr || !bf16_ok(x) || !bf16_ok(dy) ||
         !bf16_ok(dx))
         return MOE_ERR_INVALID_ARG;
@@ -910,6 +938,40 @@ moe_status moe_quantize_weights_mxfp8(const moe_config* cfg, const moe_weights* 
         !one(w->s_gate, w->s_up, w->s_down, 1, o->s_gate_q, o->s_gate_s, o->s_up_q, o->s_up_s,
              o->s_down_q, o->s_down_s, o->s_gate_tq, o->s_gate_ts, o->s_up_tq, o->s_up_ts,
              o->s_down_tq, o->s_down_ts))
+        return MOE_ERR_HIP;
+    return MOE_OK;
+}
+
+moe_status moe_quantize_weights_mxfp4(const moe_config* cfg, const moe_weights* w,
+                                      const moe_weights_mx4* o, void* stream) {
+    Geom g;
+    moe_status s = make_geom(cfg, g);
+    if (s != MOE_OK) return s;
+    if (!w || !o || !bf16_ok(w->w_gate) || !bf16_ok(w->w_up) || !bf16_ok(w->w_down))
+        return MOE_ERR_INVALID_ARG;
+    const void* need[] = {o->w_gate_q, o->w_gate_s, o->w_up_q, o->w_up_s, o->w_down_q, o->w_down_s};
+    for (const void* p : need)
+        if (!p || !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    if (g.shared) {
+        if (!bf16_ok(w->s_gate) || !bf16_ok(w->s_up) || !bf16_ok(w->s_down)) return MOE_ERR_INVALID_ARG;
+        const void* needs[] = {o->s_gate_q, o->s_gate_s, o->s_up_q, o->s_up_s, o->s_down_q, o->s_down_s};
+        for (const void* p : needs)
+            if (!p || !aligned(p, 16)) return MOE_ERR_INVALID_ARG;
+    }
+    if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
+    hipStream_t st = (hipStream_t)stream;
+    const int E = g.E, H = g.H, I = g.I;
+    auto one = [&](const void* wg, const void* wu, const void* wd, int n, const void* gq, const void* gs,
+                   const void* uq, const void* us, const void* dq, const void* ds) -> bool {
+        return launch_mx4_quant_rows(wg, (int64_t)n * I, H, I, (void*)gq, (void*)gs, st) == 0 &&
+               launch_mx4_quant_rows(wu, (int64_t)n * I, H, I, (void*)uq, (void*)us, st) == 0 &&
+               launch_mx4_quant_rows(wd, (int64_t)n * H, I, H, (void*)dq, (void*)ds, st) == 0;
+    };
+    if (!one(w->w_gate, w->w_up, w->w_down, E, o->w_gate_q, o->w_gate_s, o->w_up_q, o->w_up_s,
+             o->w_down_q, o->w_down_s))
+        return MOE_ERR_HIP;
+    if (g.shared && !one(w->s_gate, w->s_up, w->s_down, 1, o->s_gate_q, o->s_gate_s, o->s_up_q,
+                         o->s_up_s, o->s_down_q, o->s_down_s))
         return MOE_ERR_HIP;
     return MOE_OK;
 }

@@ -13,6 +13,8 @@
 // scale of row (l & 15), 32-block g.  Data tiles sit in LDS as [row][128 B]
 // with XOR-swizzled 16-byte chunks (kc_off: 16 rows read together hit 16
 // different bank groups), scales as one 32-bit word (4 blocks) per row.
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "mx.h"
 #include "profile.h"
@@ -268,7 +270,57 @@ __device__ __forceinline__ bf16x8 frag_mx_bf16(const uint16_t* s, const uint32_t
     return *(const bf16x8*)&v;
 }
 
-template <int TM, int TN>
+// MXFP4 (E2M1) operand tiles: 128 codes of a K step are 64 bytes per row,
+// stored in the first half of the row's 128-byte LDS slot (four 16-byte
+// chunks, swizzled like every KC tile).  Lane group g of a 32-code sub-step
+// ks reads the 4 bytes (8 codes) at byte 16 ks + 4 g of its row and decodes
+// them exactly with the hardware scaled conversion (checked on gfx950 against
+// an exact decode of all 256 byte values: element 2q in the low nibble of
+// byte q).
+template <int ROWS, class Src, int NTHR = 256>
+struct LoadKC4 {
+    static constexpr int PER = (ROWS * 4 + NTHR - 1) / NTHR;
+    const uint16_t* p[PER];
+    int off[PER];
+    uint4 v[PER];
+    __device__ explicit LoadKC4(const Src& src) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int c = threadIdx.x + NTHR * q;
+            const int r = c >> 2, kc = c & 3;
+            const uint16_t* b = (c < ROWS * 4) ? src.row(r) : nullptr;
+            p[q] = b ? b + kc * 8 : nullptr;
+            off[q] = kc_off(r, kc * 16);
+        }
+    }
+    __device__ void load(int kt) { load_off(kt, 0); }
+    __device__ void load_off(int kt, int64_t extra) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            v[q] = p[q] ? *(const uint4*)(p[q] + extra + (int64_t)kt * 32) : make_uint4(0, 0, 0, 0);
+    }
+    __device__ void store(uint16_t* s) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q)
+            if (threadIdx.x + NTHR * q < ROWS * 4) *(uint4*)(s + off[q]) = v[q];
+    }
+};
+
+__device__ __forceinline__ bf16x8 frag_mx4_bf16(const uint16_t* s, const uint32_t* sc, int rbase, int ks) {
+    const int lane = lane_id();
+    const int row = rbase + (lane & 15);
+    const uint32_t c = *(const uint32_t*)(s + kc_off(row, 16 * ks + 4 * (lane >> 4)));
+    const uint32_t e8 = (sc[row] >> (8 * ks)) & 0xffu;
+    const float scale = __uint_as_float(e8 ? (e8 << 23) : 0x00400000u);   // 2^(e8 - 127)
+    uint4 v;
+    v.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 0));
+    v.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 1));
+    v.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 2));
+    v.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, scale, 3));
+    return *(const bf16x8*)&v;
+}
+
+template <int TM, int TN, bool B4 = false>
 __device__ __forceinline__ void mma_tile_mx_precise(const uint16_t* st, int wm0, int wn0,
                                                     f32x4 (&acc)[TM / 32][TN / 32]) {
     using SM = SmemMX<TM, TN>;
@@ -283,7 +335,10 @@ __device__ __forceinline__ void mma_tile_mx_precise(const uint16_t* st, int wm0,
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) fb[mb] = frag_mx_bf16(sA, cA, wm0 + mb * 16, ks);
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) fa[nb] = frag_mx_bf16(sB, cB, wn0 + nb * 16, ks);
+        for (int nb = 0; nb < NB; ++nb) {
+            if constexpr (B4) fa[nb] = frag_mx4_bf16(sB, cB, wn0 + nb * 16, ks);
+            else fa[nb] = frag_mx_bf16(sB, cB, wn0 + nb * 16, ks);
+        }
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -297,6 +352,7 @@ __device__ __forceinline__ void mma_tile_mx_precise(const uint16_t* st, int wm0,
 // codes decoded exactly to bf16 on the bf16 MFMA (for GEMMs whose outputs
 // are quantised again; see the kernels for which each uses).
 constexpr int MX_ACC = 0, MX_STEPWISE = 1, MX_BF16 = 2;
+constexpr int MX_BF16_B4 = 3;   // as MX_BF16, the B operand in MXFP4 (E2M1 codes)
 template <int TM, int TN, int MODE = MX_ACC, class LA, class LB, class SA, class SB>
 __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int nk, uint16_t* smem,
                                             f32x4 (&acc)[TM / 32][TN / 32], bool keep = false) {
@@ -328,6 +384,7 @@ __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int 
         const bool more = kt + 1 < nk;
         if (more) get(kt + 1);
         if constexpr (MODE == MX_BF16) mma_tile_mx_precise<TM, TN>(cur, wm0, wn0, acc);
+        else if constexpr (MODE == MX_BF16_B4) mma_tile_mx_precise<TM, TN, true>(cur, wm0, wn0, acc);
         else if constexpr (MODE == MX_STEPWISE) mma_tile_mx_stepwise<TM, TN>(cur, wm0, wn0, acc);
         else mma_tile_mx<TM, TN>(cur, wm0, wn0, acc);
         if (more) put(nxt);
@@ -388,7 +445,7 @@ __device__ __forceinline__ void mainloop_mx_tiles(LA& la, LB& lb, SA& sa, SB& sb
 // block of h per row (lanes l, l^16, l^32, l^48 share it).
 constexpr int M1_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
 
-template <int TM>
+template <int TM, bool W4>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M1_TN>::STAGE];
@@ -396,14 +453,16 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
     if (!map_mtile<TM>(a.g, a.I / 64, blockIdx.x, e, lo, hi, nt)) return;
     const int i0 = nt * 64;
     const int H = a.H, I = a.I;
+    constexpr int WB = W4 ? 2 : 1;              // weight codes per byte
+    constexpr int MODE = W4 ? MX_BF16_B4 : MX_BF16;
     f32x4 acc[TM / 32][4];
-    const uint16_t* wg = (const uint16_t*)(a.wg_q + (int64_t)e * I * H);
-    const uint16_t* wu = (const uint16_t*)(a.wu_q + (int64_t)e * I * H);
+    const uint16_t* wg = (const uint16_t*)(a.wg_q + (int64_t)e * I * H / WB);
+    const uint16_t* wu = (const uint16_t*)(a.wu_q + (int64_t)e * I * H / WB);
     const uint32_t* wgs = (const uint32_t*)(a.wg_s + (int64_t)e * I * (H / 32));
     const uint32_t* wus = (const uint32_t*)(a.wu_s + (int64_t)e * I * (H / 32));
-    RowsGateUp db{wg, wu, H / 2, i0};
+    RowsGateUp db{wg, wu, H / 2 / WB, i0};
     ScalesGateUp ds{wgs, wus, I, i0};
-    LoadKC<M1_TN, RowsGateUp> lb(db);
+    typename std::conditional<W4, LoadKC4<M1_TN, RowsGateUp>, LoadKC<M1_TN, RowsGateUp>>::type lb(db);
     LoadScales<M1_TN, ScalesGateUp> sb(ds);
     if (a.x_gather) {
         // dispatch fused into the operand loads: a routed row's codes are its
@@ -413,13 +472,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
         ScalesGather dsa{(const uint32_t*)a.x_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
         LoadKC<TM, RowsGather> la(da);
         LoadScales<TM, ScalesGather> sa(dsa);
-        mainloop_mx<TM, M1_TN, MX_BF16>(la, lb, sa, sb, H / 128, smem, acc);
+        mainloop_mx<TM, M1_TN, MODE>(la, lb, sa, sb, H / 128, smem, acc);
     } else {
         RowsDirect da{(const uint16_t*)a.x_q, H / 2, a.xrow0 + lo, hi - lo};
         ScalesDirect dsa{(const uint32_t*)a.x_s, H / 128, a.xrow0 + lo, hi - lo};
         LoadKC<TM, RowsDirect> la(da);
         LoadScales<TM, ScalesDirect> sa(dsa);
-        mainloop_mx<TM, M1_TN, MX_BF16>(la, lb, sa, sb, H / 128, smem, acc);
+        mainloop_mx<TM, M1_TN, MODE>(la, lb, sa, sb, H / 128, smem, acc);
     }
     AccPos<TM, M1_TN> pos;
     const int wn = threadIdx.x >> 7, lane = lane_id();
@@ -464,11 +523,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
 // (K = I is short).
 constexpr int M2_TN = 128;     // row tile TM: 64 or 128 (the bf16 GEMMs give the reasons)
 
-template <int TM>
+template <int TM, bool W4>
 
 __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * SmemMX<TM, M2_TN>::STAGE];
-    constexpr int NT = short_k_tiles_per_block<TM>();
+    constexpr int NT = W4 ? 1 : short_k_tiles_per_block<TM>();
     const int ncol = a.H / M2_TN;
     int e, lo, hi, np;
     if (!map_mtile<TM>(a.g, (ncol + NT - 1) / NT, blockIdx.x, e, lo, hi, np)) return;
@@ -478,10 +537,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     f32x4 acc[TM / 32][4];
     RowsDirect da{(const uint16_t*)a.h_q, I / 2, lo, hi - lo};
     ScalesDirect dsa{(const uint32_t*)a.h_s, I / 128, lo, hi - lo};
-    RowsDirect db{(const uint16_t*)(a.wd_q + (int64_t)e * H * I), I / 2, n0, M2_TN};
+    constexpr int WB = W4 ? 2 : 1;              // weight codes per byte
+    RowsDirect db{(const uint16_t*)(a.wd_q + (int64_t)e * H * I / WB), I / 2 / WB, n0, M2_TN};
     ScalesKMajor dsb{(const uint32_t*)(a.wd_s + (int64_t)e * H * (I / 32)), H, n0, M2_TN};
     LoadKC<TM, RowsDirect> la(da);
-    LoadKC<M2_TN, RowsDirect> lb(db);
+    typename std::conditional<W4, LoadKC4<M2_TN, RowsDirect>, LoadKC<M2_TN, RowsDirect>>::type lb(db);
     LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScales<M2_TN, ScalesKMajor> sb(dsb);
     AccPos<TM, M2_TN> pos;
@@ -502,7 +562,11 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
             }
         }
     };
-    if constexpr (NT == 1) {
+    if constexpr (W4) {
+        // E2M1 weights decoded exactly to bf16 (see frag_mx4_bf16)
+        mainloop_mx<TM, M2_TN, MX_BF16_B4>(la, lb, sa, sb, I / 128, smem, acc);
+        epi(0, acc);
+    } else if constexpr (NT == 1) {
         mainloop_mx<TM, M2_TN>(la, lb, sa, sb, I / 128, smem, acc);
         epi(0, acc);
     } else {
@@ -964,19 +1028,34 @@ static inline int mgroup_grid_mx(const GroupRows& g, int TM) {
     } while (0)
 
 int launch_gemm_gate_up_mx(const GemmGateUpMXArgs& a, hipStream_t st) {
-    ProfScope prof_(st, "gemm_gate_up_mx");
-    MOE_LAUNCH_TM_MX(k_gemm_gate_up_mx, a.I / 64);
+    ProfScope prof_(st, a.w4 ? "gemm_gate_up_mx4" : "gemm_gate_up_mx");
+    const int tm_ = a.g.tm == 128 ? 128 : 64;
+    const int grid_ = mgroup_grid_mx(a.g, tm_) * (a.I / 64);
+    if (grid_ <= 0) return 0;
+    if (a.w4) {
+        if (tm_ == 128) k_gemm_gate_up_mx<128, true><<<grid_, 256, 0, st>>>(a);
+        else k_gemm_gate_up_mx<64, true><<<grid_, 256, 0, st>>>(a);
+    } else {
+        if (tm_ == 128) k_gemm_gate_up_mx<128, false><<<grid_, 256, 0, st>>>(a);
+        else k_gemm_gate_up_mx<64, false><<<grid_, 256, 0, st>>>(a);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
 int launch_gemm_down_mx(const GemmDownMXArgs& a, hipStream_t st) {
-    ProfScope prof_(st, "gemm_down_mx");
+    ProfScope prof_(st, a.w4 ? "gemm_down_mx4" : "gemm_down_mx");
     const int ncol = a.H / M2_TN;
     const int tm_ = a.g.tm == 128 ? 128 : 64;
-    const int nt_ = tm_ == 128 ? short_k_tiles_per_block<128>() : short_k_tiles_per_block<64>();
+    const int nt_ = a.w4 ? 1 : (tm_ == 128 ? short_k_tiles_per_block<128>() : short_k_tiles_per_block<64>());
     const int grid_ = mgroup_grid_mx(a.g, tm_) * ((ncol + nt_ - 1) / nt_);
     if (grid_ <= 0) return 0;
-    if (tm_ == 128) k_gemm_down_mx<128><<<grid_, 256, 0, st>>>(a);
-    else k_gemm_down_mx<64><<<grid_, 256, 0, st>>>(a);
+    if (a.w4) {
+        if (tm_ == 128) k_gemm_down_mx<128, true><<<grid_, 256, 0, st>>>(a);
+        else k_gemm_down_mx<64, true><<<grid_, 256, 0, st>>>(a);
+    } else {
+        if (tm_ == 128) k_gemm_down_mx<128, false><<<grid_, 256, 0, st>>>(a);
+        else k_gemm_down_mx<64, false><<<grid_, 256, 0, st>>>(a);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

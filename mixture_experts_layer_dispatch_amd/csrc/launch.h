@@ -145,6 +145,7 @@ struct WgradGateUpArgs {
 
 struct GemmGateUpMXArgs {
     GroupRows g;
+    int w4;                   // weights in MXFP4: wg_q / wu_q hold E2M1 codes [E, I, H/2]
     const uint8_t* x_q;       // codes [tokens, H]: routed rows gathered by token through
     const uint8_t* x_s;       // slot_of_row (x_gather), dense rows xrow0 + local row; scales [tokens, H/32]
     int xrow0;
@@ -165,6 +166,7 @@ struct GemmGateUpMXArgs {
 
 struct GemmDownMXArgs {
     GroupRows g;
+    int w4;                   // weights in MXFP4: wd_q holds E2M1 codes [E, H, I/2]
     const uint8_t* h_q;
     const uint8_t* h_s;
     const uint8_t* wd_q;      // [E, H, I]
@@ -270,6 +272,8 @@ int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* 
                          int kmaj_rows = 0);
 int launch_mx_quant_cols(const void* w, int batch, int R, int C, void* codes, void* scales,
                          hipStream_t st);
+int launch_mx4_quant_rows(const void* w, int64_t rows, int K, int kmaj_rows, void* codes, void* scales,
+                          hipStream_t st);
 
 int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, void* codes, void* scales,
                             hipStream_t st);

@@ -58,4 +58,43 @@ __device__ __forceinline__ uint32_t e4m3_pack4(const float* v, int s) {
     return w;
 }
 
+// ------------------------------------------------------------------ MXFP4
+// E2M1 elements (the MXFP4 element type of OCP MX v1.0): magnitudes 0, 0.5, 1,
+// 1.5, 2, 3, 4, 6; the block scale is 2^(floor(log2 amax) - 2), 2 being the
+// exponent of the largest value (6 = 1.5 * 2^2); round to nearest even,
+// saturate to +-6; the sign bit is kept for zero results.
+__device__ __forceinline__ int mx4_scale_exp(float amax) {
+    const uint32_t u = __float_as_uint(amax);
+    const int ef = (int)((u >> 23) & 0xffu);
+    if (ef == 0) return -127;
+    const int s = ef - 127 - 2;
+    return s < -127 ? -127 : s;
+}
+
+// E2M1 code (0..15) of v, already divided by the block scale
+__device__ __forceinline__ uint32_t e2m1_code(float v) {
+    const uint32_t u = __float_as_uint(v);
+    const uint32_t sign = (u >> 28) & 0x8u;
+    const float a = __uint_as_float(u & 0x7fffffffu);
+    // quantum: 0.5 below 2, 1 in [2, 4), 2 from 4; count of quanta rounded half to even
+    float r;
+    if (a < 2.0f) r = __builtin_rintf(a * 2.0f) * 0.5f;
+    else if (a < 4.0f) r = __builtin_rintf(a);
+    else r = __builtin_rintf(a * 0.5f) * 2.0f;
+    uint32_t m;                        // index on the grid 0, .5, 1, 1.5, 2, 3, 4, 6
+    if (r < 2.0f) m = (uint32_t)(r * 2.0f);          // 0..3 (r = 2 handled below)
+    else if (r < 4.0f) m = 2u + (uint32_t)r;        // 2 -> 4, 3 -> 5
+    else m = r < 6.0f ? 6u : 7u;                     // 4 -> 6, >= 6 saturates
+    return sign | m;
+}
+
+// eight values of one 32-element block (scale exponent s) -> 8 codes, element
+// 2q in the low nibble of byte q
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* v, int s) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w |= e2m1_code(__builtin_amdgcn_ldexpf(v[q], -s)) << (4 * q);
+    return w;
+}
+
 }  // namespace moe

@@ -88,6 +88,44 @@ __global__ __launch_bounds__(256) void k_mx_quant_cols(const uint16_t* __restric
     scales[mat * (int64_t)C * (R / 32) + ((int64_t)(b >> 2) * C + c) * 4 + (b & 3)] = (uint8_t)(s + 127);
 }
 
+// ------------------------------------------------------------------ MXFP4 rows
+// W [R, K] bf16 -> E2M1 codes [R, K/2] (two per byte, the even element in the
+// low nibble) and E8M0 scales, blocks of 32 along K, K-step-major per matrix
+// of kmaj_rows rows as the MXFP8 weights ([K/128, rows, 4]).  A thread owns 8
+// consecutive elements; four neighbouring threads share a block.
+__global__ __launch_bounds__(256) void k_mx4_quant_rows(const uint4* __restrict__ x, int64_t n8, int K,
+                                                        int kmaj_rows, uint32_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool ok = i < n8;
+    float v[8];
+    if (ok) {
+        const uint4 w = x[i];
+        v[0] = lo_bf(w.x); v[1] = hi_bf(w.x); v[2] = lo_bf(w.y); v[3] = hi_bf(w.y);
+        v[4] = lo_bf(w.z); v[5] = hi_bf(w.z); v[6] = lo_bf(w.w); v[7] = hi_bf(w.w);
+    } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) v[q] = 0.f;
+    }
+    float amax = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    amax = fmaxf(amax, __shfl_xor(amax, 1));
+    amax = fmaxf(amax, __shfl_xor(amax, 2));
+    const int s = mx4_scale_exp(amax);
+    if (ok) {
+        codes[i] = e2m1_pack8(v, s);
+        if ((i & 3) == 0) {
+            const int nb = K / 32;
+            const int64_t blk = i >> 2;
+            const int64_t row = blk / nb;
+            const int b = (int)(blk - row * nb);
+            const int64_t mat = row / kmaj_rows, r = row - mat * kmaj_rows;
+            scales[mat * kmaj_rows * nb + ((int64_t)(b >> 2) * kmaj_rows + r) * 4 + (b & 3)] = (uint8_t)(s + 127);
+        }
+    }
+}
+
 // ------------------------------------------------------------------ group transpose
 // For the weight gradients, whose reduction runs over an expert's rows: rows of
 // each expert group, in 32-row blocks (the last one zero-padded), are quantised
@@ -217,6 +255,16 @@ int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* 
     if (n8 <= 0) return 0;
     k_mx_quant_rows<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint4*)x, n8, K, kmaj_rows,
                                                                  (uint2*)codes, (uint8_t*)scales);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
+int launch_mx4_quant_rows(const void* w, int64_t rows, int K, int kmaj_rows, void* codes, void* scales,
+                          hipStream_t st) {
+    ProfScope prof_(st, "mx4_quant_rows");
+    const int64_t n8 = rows * (int64_t)K / 8;
+    if (n8 <= 0) return 0;
+    k_mx4_quant_rows<<<(unsigned)((n8 + 255) / 256), 256, 0, st>>>((const uint4*)w, n8, K, kmaj_rows,
+                                                                  (uint32_t*)codes, (uint8_t*)scales);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

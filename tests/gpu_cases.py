@@ -58,6 +58,10 @@ class Case:
             self.wq = B.alloc_weights_mx(self.cfg)
             B.moe_quantize_weights_mxfp8(self.cfg, self.weights, self.wq)
             self.weights = dict(self.weights, mx=self.wq)
+        if precision == B.PREC_MXFP4:
+            self.wq4 = B.alloc_weights_mx4(self.cfg)
+            B.moe_quantize_weights_mxfp4(self.cfg, self.weights, self.wq4)
+            self.weights = dict(self.weights, mx4=self.wq4)
 
     # ------------------------------------------------------------- GPU calls
     def schedule(self):

@@ -259,3 +259,18 @@ def test_noalloc_schedule_rejects_configs_beyond_its_scratch():
     assert L.moe_schedule_noalloc(ctypes.byref(huge), fake, ctypes.byref(s_ok), None) == B.MOE_ERR_WORKSPACE
     assert L.moe_schedule_noalloc(ctypes.byref(_cfg().c()), fake, ctypes.byref(B.moe_sched()),
                                   None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_mx4_weight_buffers_match_the_header_layout():
+    """alloc_weights_mx4 gives every field of moe_weights_mx4: E2M1 codes two per
+    byte [.., rows, K/2] and K-step-major scales [.., K/128, rows, 4]."""
+    cfg = B.Config(T=8, H=256, I=384, E=3, k=1, n_shared=1, precision=B.PREC_MXFP4)
+    q = B.alloc_weights_mx4(cfg, "cpu")
+    assert sorted(q) == sorted(B.MX4_FIELDS)
+    E, H, I = cfg.E, cfg.H, cfg.I
+    for name, (rows, K) in {"gate_": (I, H), "up_": (I, H), "down_": (H, I)}.items():
+        for pre, lead in (("w_", (E,)), ("s_", ())):
+            assert tuple(q[pre + name + "q"].shape) == (*lead, rows, K // 2)
+            assert tuple(q[pre + name + "s"].shape) == (*lead, K // 128, rows, 4)
+    assert B.validate_config(cfg) == B.MOE_OK
+    assert B.validate_config(B.Config(T=8, H=256, I=384, E=3, k=1, precision=3)) == B.MOE_ERR_INVALID_ARG
