@@ -397,6 +397,67 @@ def main():
                           "TFLOP/s": round(flops_fwd / (ms_fwd_mx * 1e-3) / 1e12, 2)},
               "kernels": kernel_table(stats_mx, args.steps, kb)}
 
+    w4 = None
+    if not args.no_mxfp8:
+        # the MXFP4-weight forward (E2M1 weights, MXFP8 activations; forward
+        # only): the weight stream of the forward halves against MXFP8
+        c4 = B.Config(T=T, H=H, I=I, E=E, k=k, n_shared=shape.n_shared, macrobatch=shape.macrobatch,
+                      minibatch=shape.minibatch, precision=B.PREC_MXFP4)
+        ws4 = B.alloc_workspace(c4)
+        sch4 = B.alloc_schedule(c4)
+        sv4 = B.alloc_saved(c4)
+        q4 = B.alloc_weights_mx4(c4)
+        B.moe_quantize_weights_mxfp4(c4, inp.weights, q4, stream)      # outside timing
+        wts4 = dict(inp.weights, mx4=q4)
+        y4 = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+        B.moe_schedule(c4, inp.logits, sch4, ws4, stream)
+        for _ in range(args.warmup):
+            B.moe_forward(c4, sch4, inp.x, wts4, y4, sv4, ws4, stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            B.moe_forward(c4, sch4, inp.x, wts4, y4, sv4, ws4, stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms4 = e0.elapsed_time(e1) / args.steps
+        w4 = {"ms": round(ms4, 4), "TFLOP/s": round(flops_fwd / (ms4 * 1e-3) / 1e12, 2),
+              "dtype": "weights mxfp4 (e2m1 + e8m0 per 32), activations mxfp8; forward only"}
+        print(f"[bench] mxfp4-weight forward: {ms4:.3f} ms", file=sys.stderr, flush=True)
+        del ws4, sv4, q4, wts4, y4
+
+    router = None
+    if shape.E <= 1024:
+        # the router projection upstream of the layer (outside the metric, as on
+        # the pages): logits = x W_r^T, and its backward
+        wr = si.router_weights(shape, "cuda")
+        lg = torch.empty(T, E, dtype=torch.float32, device="cuda")
+        dxr = torch.zeros(T, H, dtype=torch.bfloat16, device="cuda")
+        dwr = torch.empty(E, H, dtype=torch.bfloat16, device="cuda")
+        cr = B.Config(T=T, H=H, I=I, E=E, k=k, n_shared=shape.n_shared, macrobatch=shape.macrobatch,
+                      minibatch=shape.minibatch)
+        wsr = B.alloc_workspace(cr)
+
+        def rstep():
+            B.moe_router_forward(cr, inp.x, wr, lg, stream)
+            B.moe_router_backward(cr, inp.x, wr, lg, dxr, dwr, wsr, stream)
+
+        for _ in range(args.warmup):
+            rstep()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            rstep()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        msr = e0.elapsed_time(e1) / args.steps
+        rfl = 3 * 2.0 * T * H * E
+        router = {"ms_fwd_bwd": round(msr, 4), "TFLOP/s": round(rfl / (msr * 1e-3) / 1e12, 1),
+                  "note": "router projection x W_r^T and its backward (d_logits W_r into dx, dW_r); "
+                          "outside the layer metric"}
+        del wr, lg, dxr, dwr, wsr
+
     ep = None
     if not args.no_ep_share and args.workload != "e8_ep_share":
         # one GPU's expert-parallel share (8 experts x 2560 rows): the MFMA-bound
@@ -448,6 +509,8 @@ def main():
         "pages_context": PAGES_CONTEXT,
         "cpu_baseline": cpu,
         "mxfp8": mx,
+        "mxfp4_weight_forward": w4,
+        "router": router,
         "ep_share": ep,
         "kernels": kernels,
     }
