@@ -465,3 +465,30 @@ def test_w4_backward_is_refused():
     idx, w = oracle.route(L, 1)
     with pytest.raises(ValueError):
         oracle.backward(x, wg, wu, wd, idx, w, x, mx="w4")
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e2m1"])
+@pytest.mark.parametrize("axis", [0, 1])
+def test_roundtrip_equals_dequantised_codes(fmt, axis):
+    """mx_roundtrip / mxfp4_roundtrip return grid value x block scale without
+    forming the bit patterns; they must equal decoding the quantiser's codes,
+    bit for bit, on Gaussian data, all-zero blocks, saturating blocks (one
+    large element beside small ones), values far below a block's scale
+    (E4M3 subnormals, flushes to zero), signed zeros and a ragged tail."""
+    rng = np.random.default_rng(41)
+    v = rng.standard_normal((70, 97)) * np.exp(rng.uniform(-30, 30, (70, 1)))
+    v[3, :] = 0.0
+    v[5, :] = -0.0
+    v[7, 10] = 1e6
+    v[9, :32] = np.ldexp(1.0, -140) * rng.standard_normal(32)
+    v[11, 40] = 1e-30
+    v[:, 64] *= 1e-12
+    v = v if axis == 1 else v.T.copy()
+    if fmt == "e4m3":
+        want = mx.mx_dequantize(*mx.mx_quantize(v, axis=axis), axis=axis)
+        got = mx.mx_roundtrip(v, axis=axis)
+    else:
+        want = mx.mxfp4_dequantize(*mx.mxfp4_quantize(v, axis=axis), axis=axis)
+        got = mx.mxfp4_roundtrip(v, axis=axis)
+    assert got.shape == v.shape
+    np.testing.assert_array_equal(got.view(np.uint64), want.view(np.uint64))
