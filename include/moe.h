@@ -208,7 +208,9 @@ MOE_API moe_status moe_ring_rows(const moe_config* cfg, int64_t* rows);
 
 /* Host-only: bytes of device workspace that moe_schedule, moe_forward and
  * moe_backward need (one workspace serves all three; it holds the ring
- * buffer and per-call scratch, nothing that must survive between calls). */
+ * buffer and per-call scratch, nothing that must survive between calls
+ * except, under MOE_FLAG_RECOMPUTE, the forward's last macrobatch of gate
+ * and up projections that the backward reads). */
 MOE_API moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
 
 /* Host-only diagnostics: byte offset and size, inside the workspace of `cfg`,
@@ -219,7 +221,15 @@ MOE_API moe_status moe_workspace_size(const moe_config* cfg, size_t* bytes);
  *              activation quantisation inside the forward);
  *   "x_scales" [T, H/32] their E8M0 scales, row-major;
  *   "dy_codes", "dy_scales": the same of dy, written by moe_backward (the
- *              reverse-combine gathers them).
+ *              reverse-combine gathers them);
+ *   "wgrad_x_codes", "wgrad_x_scales": the dW_gate / dW_up operand x of the
+ *              last macrobatch moe_backward processed, quantised along the
+ *              rows of each expert's group in 32-row blocks (the last one
+ *              zero-padded to np_e = 32 * ceil(n_e / 32) rows) and stored
+ *              group after group, transposed: group e's codes are [H, np_e]
+ *              from byte 32 * B_e * H, its scales [H, np_e / 32] from byte
+ *              B_e * H, where B_e = "wgrad_block_offsets"[e];
+ *   "wgrad_block_offsets" int32 [E + 1]: B_e = sum over e' < e of np_e' / 32.
  * MOE_ERR_INVALID_ARG for other names or a BF16 config. */
 MOE_API moe_status moe_workspace_region(const moe_config* cfg, const char* name, size_t* offset,
                                         size_t* bytes);

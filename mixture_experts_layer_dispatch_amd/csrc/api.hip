@@ -593,9 +593,16 @@ moe_status moe_workspace_region(const moe_config* cfg, const char* name, size_t*
     if (!name || !offset || !bytes || !g.mx) return MOE_ERR_INVALID_ARG;
     const Layout L = make_layout(g);
     const size_t th = (size_t)g.T * g.H;
+    const size_t tk = (size_t)g.H * (size_t)L.kcap;
     struct { const char* n; size_t off, len; } regions[] = {
         {"x_codes", L.xq, th}, {"x_scales", L.xs, th / 32},
         {"dy_codes", L.dyq, th}, {"dy_scales", L.dys, th / 32},
+        // the dW_gate / dW_up operand x of the last macrobatch the backward
+        // processed, quantised in 32-row blocks of each expert's group and
+        // stored group-major and transposed, with the prefix of the groups'
+        // 32-row block counts that places them
+        {"wgrad_x_codes", L.tr_x, tk}, {"wgrad_x_scales", L.tr_xs, tk / 32},
+        {"wgrad_block_offsets", L.blk_off, (size_t)(g.E + 1) * 4},
     };
     for (const auto& r : regions) {
         if (std::strcmp(r.n, name) == 0) {

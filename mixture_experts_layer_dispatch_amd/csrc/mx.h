@@ -41,21 +41,26 @@ __device__ __forceinline__ uint32_t e4m3_code(float v) {
     return sign | (e << 3) | m;
 }
 
-// Quantise 8 values that belong to one 32-element block whose scale exponent is s.
-__device__ __forceinline__ uint2 e4m3_pack8(const float* v, int s) {
-    uint32_t lo = 0, hi = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lo |= e4m3_code(__builtin_amdgcn_ldexpf(v[q], -s)) << (8 * q);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) hi |= e4m3_code(__builtin_amdgcn_ldexpf(v[4 + q], -s)) << (8 * q);
-    return make_uint2(lo, hi);
+// Four values of one 32-element block whose scale exponent is s -> four codes,
+// value q in byte q.  The packed conversion instruction rounds to nearest
+// even and keeps the sign of zero results, like e4m3_code; with the
+// magnitude clamped to 448 first (its saturation) it returned e4m3_code's
+// byte for every float32 below 512 in magnitude, both signs, subnormals
+// included (a scaled block element is below 2^9), checked on gfx950.  It is
+// one instruction per two values where e4m3_code takes a dozen with a branch.
+__device__ __forceinline__ float e4m3_clamp(float v, int s) {
+    const float x = __builtin_amdgcn_ldexpf(v, -s);
+    return __builtin_copysignf(__builtin_fminf(__builtin_fabsf(x), 448.0f), x);
 }
 
 __device__ __forceinline__ uint32_t e4m3_pack4(const float* v, int s) {
-    uint32_t w = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) w |= e4m3_code(__builtin_amdgcn_ldexpf(v[q], -s)) << (8 * q);
-    return w;
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(v[0], s), e4m3_clamp(v[1], s), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_clamp(v[2], s), e4m3_clamp(v[3], s), lo, true);
+}
+
+// Quantise 8 values that belong to one 32-element block whose scale exponent is s.
+__device__ __forceinline__ uint2 e4m3_pack8(const float* v, int s) {
+    return make_uint2(e4m3_pack4(v, s), e4m3_pack4(v + 4, s));
 }
 
 // ------------------------------------------------------------------ MXFP4

@@ -241,6 +241,12 @@ def test_workspace_regions_of_the_mx_activation_codes():
         off, nb = B.workspace_region(mx, name)
         assert nb == n and off % 256 == 0 and off + nb <= total
         seen.append((off, off + nb))
+    kcap = -(-(256 * 2 + 32 * 8) // 128) * 128          # the macrobatch's rows padded group by group
+    for name, n in (("wgrad_x_codes", 256 * kcap), ("wgrad_x_scales", 256 * kcap // 32),
+                    ("wgrad_block_offsets", (8 + 1) * 4)):
+        off, nb = B.workspace_region(mx, name)
+        assert nb >= n and off % 256 == 0 and off + nb <= total
+        seen.append((off, off + nb))
     seen.sort()
     assert all(a[1] <= b[0] for a, b in zip(seen, seen[1:]))        # disjoint
     with pytest.raises(B.MoEError):

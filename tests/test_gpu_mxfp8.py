@@ -279,6 +279,56 @@ def _check_activation_codes(c, which):
     np.testing.assert_array_equal(codes, ref_c)
 
 
+def _check_wgrad_x_codes(c, experts=None):
+    """The weight-gradient operand x (dW_gate, dW_up reduce over an expert's
+    rows): each expert group's x rows, zero-padded to a multiple of 32 rows,
+    quantised along the rows in 32-row blocks, stored transposed group after
+    group; compared bit for bit with the oracle's quantiser of the same bf16
+    rows (one macrobatch, no shared expert)."""
+    idx, w, sch = c.oracle_schedule()
+    assert sch["n_macro"] == 1 and c.shape.n_shared == 0
+    E, H, k = c.shape.E, c.shape.H, c.shape.k
+    counts, offsets = sch["counts"][0], sch["offsets"][0]
+    nblk = -(-counts // 32)
+    boff = np.concatenate([[0], np.cumsum(nblk)])
+    np.testing.assert_array_equal(_region(c, "wgrad_block_offsets", (-1,)).view(np.int32), boff)
+    codes = _region(c, "wgrad_x_codes", (-1,))
+    scales = _region(c, "wgrad_x_scales", (-1,))
+    x = f32(c.x).astype(np.float64)
+    for e in (range(E) if experts is None else experts):
+        n, npad = int(counts[e]), 32 * int(nblk[e])
+        if n == 0:
+            continue
+        tok = sch["slot_of_row"][offsets[e]:offsets[e + 1]] // k
+        xe = np.zeros((npad, H))
+        xe[:n] = x[tok]
+        rc, rs = oracle.mx_quantize(xe, axis=0)
+        c0, s0 = 32 * int(boff[e]) * H, int(boff[e]) * H
+        np.testing.assert_array_equal(codes[c0:c0 + H * npad].reshape(H, npad), rc.T, err_msg=f"expert {e}")
+        np.testing.assert_array_equal(scales[s0:s0 + H * npad // 32].reshape(H, npad // 32), rs.T,
+                                      err_msg=f"expert {e}")
+
+
+@pytest.mark.parametrize("name", ["tiny", "ragged", "dense_experts", "stripes", "all_experts", "max_k",
+                                  "max_e"])
+def test_wgrad_operand_codes_bit_exact(name):
+    c = MXCase(SHAPES[name])
+    c.schedule()
+    c.forward()
+    c.backward()
+    torch.cuda.synchronize()
+    _check_wgrad_x_codes(c)
+
+
+def test_wgrad_operand_codes_bit_exact_full_size():
+    c = MXCase(si.SHAPES["e512_t2048"])
+    c.schedule()
+    c.forward()
+    c.backward()
+    torch.cuda.synchronize()
+    _check_wgrad_x_codes(c, experts=[0, 1, 77, 300, 511])
+
+
 @pytest.mark.parametrize("name", ["tiny", "ring_shared", "zipf_ring", "max_k"])
 def test_activation_codes_bit_exact(name):
     """The dispatch gathers each routed row's codes from x quantised once per
