@@ -90,6 +90,10 @@ typedef struct moe_config {
     int64_t capacity_rows; /* ring-buffer rows; 0 = the minimum (see moe_ring_rows)   */
     int32_t precision;     /* moe_precision                                           */
     int32_t flags;         /* MOE_FLAG_* bits; 0 = none                               */
+    int32_t acc_experts;   /* several macrobatches: routed experts whose weight       */
+                           /* gradients may take rows from more than one macrobatch  */
+                           /* (the workspace keeps fp32 running sums for that many); */
+                           /* 0 = E.  Exceeding it sets MOE_DEVERR_ACC_CAPACITY.     */
 } moe_config;
 
 /* moe_config.flags.
@@ -339,8 +343,16 @@ MOE_API moe_status moe_quantize_weights_mxfp4(const moe_config* cfg, const moe_w
 
 /* Reads and clears the sticky device error word that kernels set when a
  * caller-built schedule holds an out-of-range expert, slot or row (those
- * entries are skipped, never dereferenced).  Synchronises `stream`; meant for
- * tests.  *flags = 0 when nothing was found. */
+ * entries are skipped, never dereferenced), or when more routed experts take
+ * rows from several macrobatches than moe_config.acc_experts allows (the
+ * weight gradients of the experts past it are left unwritten).  Synchronises
+ * `stream`; meant for tests.  *flags = 0 when nothing was found, else an OR
+ * of the bits below. */
+#define MOE_DEVERR_BAD_EXPERT 1
+#define MOE_DEVERR_BAD_SLOT 2
+#define MOE_DEVERR_BAD_ROW 4
+#define MOE_DEVERR_BAD_OFFSETS 8
+#define MOE_DEVERR_ACC_CAPACITY 16
 MOE_API moe_status moe_check_device_error(void* workspace, size_t workspace_bytes, void* stream,
                                   int32_t* flags);
 

@@ -50,7 +50,7 @@ class moe_config(ctypes.Structure):
                 ("E", ctypes.c_int32), ("k", ctypes.c_int32), ("n_shared", ctypes.c_int32),
                 ("macrobatch", ctypes.c_int32), ("minibatch", ctypes.c_int32),
                 ("capacity_rows", ctypes.c_int64), ("precision", ctypes.c_int32),
-                ("flags", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("acc_experts", ctypes.c_int32)]
 
 
 class moe_sched(ctypes.Structure):
@@ -171,11 +171,12 @@ class Config:
     capacity_rows: int = 0
     precision: int = PREC_BF16
     recompute: bool = False
+    acc_experts: int = 0
 
     def c(self) -> moe_config:
         return moe_config(self.T, self.H, self.I, self.E, self.k, self.n_shared, self.macrobatch,
                           self.minibatch, self.capacity_rows, self.precision,
-                          FLAG_RECOMPUTE if self.recompute else 0)
+                          FLAG_RECOMPUTE if self.recompute else 0, self.acc_experts)
 
     @property
     def M(self) -> int:
@@ -535,6 +536,10 @@ def moe_quantize_weights_mxfp8(cfg: Config, weights: dict, out: dict, stream=Non
     _check(lib().moe_quantize_weights_mxfp8(ctypes.byref(cfg.c()), ctypes.byref(wst),
                                             ctypes.byref(mx), _stream(stream)),
            "moe_quantize_weights_mxfp8")
+
+
+# device error bits (moe_check_device_error)
+DEVERR_BAD_EXPERT, DEVERR_BAD_SLOT, DEVERR_BAD_ROW, DEVERR_BAD_OFFSETS, DEVERR_ACC_CAPACITY = 1, 2, 4, 8, 16
 
 
 def moe_check_device_error(ws: torch.Tensor, stream=None) -> int:

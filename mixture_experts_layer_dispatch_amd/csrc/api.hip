@@ -25,6 +25,7 @@ struct Geom {
     int64_t ring_rows;
     int halves;
     bool shared, mx, w4, recompute;
+    int acc_cap;              // experts with fp32 running sums across macrobatches
 };
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -46,6 +47,7 @@ struct Layout {
     int64_t kcap;
     size_t s_dgu32, s_h32, s_dguq, s_dgus, s_dxm;          // shared expert
     size_t wacc_g, wacc_u, wacc_d, wacc_sg, wacc_su, wacc_sd;
+    size_t acc_slot;                  // int32 [E]: each routed expert's accumulator slot
     size_t rc_g, rc_u, rc_sg, rc_su;  // recompute mode: one macrobatch's g, u (and the shared expert's)
     size_t dl16;                      // router backward: bf16 d_logits [T, Ep]
 };
@@ -59,7 +61,7 @@ moe_status make_geom(const moe_config* c, Geom& g) {
     if (c->precision != MOE_PREC_BF16 && c->precision != MOE_PREC_MXFP8 && c->precision != MOE_PREC_MXFP4)
         return MOE_ERR_INVALID_ARG;
     if ((c->flags & ~MOE_FLAG_RECOMPUTE) != 0 || c->macrobatch < 0 || c->minibatch < 0 ||
-        c->capacity_rows < 0)
+        c->capacity_rows < 0 || c->acc_experts < 0)
         return MOE_ERR_INVALID_ARG;
     if (c->H > (1 << 16) || c->I > (1 << 16)) return MOE_ERR_INVALID_ARG;
     const int64_t S = (int64_t)c->T * c->k;
@@ -79,6 +81,7 @@ moe_status make_geom(const moe_config* c, Geom& g) {
     g.mx = c->precision != MOE_PREC_BF16;           // MXFP8 activations in both MX modes
     g.w4 = c->precision == MOE_PREC_MXFP4;
     g.recompute = (c->flags & MOE_FLAG_RECOMPUTE) != 0;
+    g.acc_cap = c->acc_experts > 0 && c->acc_experts < c->E ? c->acc_experts : c->E;
     if (c->capacity_rows) {
         if (c->capacity_rows < g.Sm) return MOE_ERR_CAPACITY;
         g.ring_rows = c->capacity_rows;
@@ -182,18 +185,22 @@ Layout make_layout(const Geom& g) {
         }
     }
     if (g.n_macro > 1) {
-        const size_t per = (size_t)g.E * I * H * 4;
+        // the low halves of fp32 running sums whose high halves live in the
+        // gradient outputs (see wgrad_store): 2 bytes per weight, for the
+        // acc_cap experts that may take rows from several macrobatches
+        const size_t per = (size_t)g.acc_cap * I * H * 2;
         L.wacc_g = 0;
         L.wacc_u = per;
         L.wacc_d = 2 * per;
         size_t end = 3 * per;
         if (g.shared) {
             L.wacc_sg = end;
-            L.wacc_su = end + I * H * 4;
-            L.wacc_sd = end + 2 * I * H * 4;
-            end += 3 * I * H * 4;
+            L.wacc_su = end + I * H * 2;
+            L.wacc_sd = end + 2 * I * H * 2;
+            end += 3 * I * H * 2;
         }
         L.wacc = take(end);
+        L.acc_slot = take((size_t)g.E * 4);
     }
     L.total = at;
     return L;
@@ -255,7 +262,8 @@ struct Ptrs {
     int32_t* err() const { return (int32_t*)(ws + L->err); }
     char* half(int m, int halves) const { return ws + L->ring + (size_t)(m % halves) * L->ring_half; }
     char* sh() const { return ws + L->sh; }
-    float* wacc(size_t off) const { return (float*)(ws + L->wacc + off); }
+    uint16_t* wacc(size_t off) const { return (uint16_t*)(ws + L->wacc + off); }
+    int32_t* acc_slot() const { return (int32_t*)(ws + L->acc_slot); }
 };
 
 // Where macrobatch m's gate and up projections are kept for the backward:
@@ -386,14 +394,15 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     // counts: the schedule's [n_macro, E] counts for routed groups over several
     // macrobatches (per-expert modes), nullptr otherwise
     auto wgrads = [&](const PadGroups& pg, int mode, const int32_t* counts, int m, uint16_t* dwd,
-                      float* accd, uint16_t* dwg, float* accg, uint16_t* dwu, float* accu) -> bool {
+                      uint16_t* accd, uint16_t* dwg, uint16_t* accg, uint16_t* dwu, uint16_t* accu) -> bool {
+        const int32_t* sl = counts ? P.acc_slot() : nullptr;
         WgradMXArgs d{pg, twdy, twdys, th, ths, g.H, g.I, g.H,
-                      {dwd, accd, mode, counts, m, g.n_macro, g.E},
-                      {dwd, accd, mode, counts, m, g.n_macro, g.E}};
+                      {dwd, accd, mode, counts, m, g.n_macro, g.E, sl},
+                      {dwd, accd, mode, counts, m, g.n_macro, g.E, sl}};
         if (launch_wgrad_mx(d, st)) return false;
         WgradMXArgs gu{pg, tdgu, tdgus, tx, txs, 2 * g.I, g.H, g.I,
-                       {dwg, accg, mode, counts, m, g.n_macro, g.E},
-                       {dwu, accu, mode, counts, m, g.n_macro, g.E}};
+                       {dwg, accg, mode, counts, m, g.n_macro, g.E, sl},
+                       {dwu, accu, mode, counts, m, g.n_macro, g.E, sl}};
         return launch_wgrad_mx(gu, st) == 0;
     };
     const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
@@ -808,6 +817,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
     if (!device_ok()) return MOE_ERR_UNSUPPORTED_DEVICE;
     hipStream_t st = (hipStream_t)stream;
     Ptrs P{(char*)workspace, &L};
+    // the accumulator slots of the experts whose gradients span macrobatches
+    if (g.n_macro > 1 &&
+        launch_acc_slots(sched->counts, g.n_macro, g.E, g.acc_cap, P.acc_slot(), P.err(), st))
+        return MOE_ERR_HIP;
     if (g.mx) return backward_mx(g, L, P, sched, saved, x, w, dy, dx, gr, dw, d_logits, st);
     int32_t* err = P.err();
     const uint16_t* xb = (const uint16_t*)x;
@@ -879,12 +892,13 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows(), deep, st)) return MOE_ERR_HIP;
         GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err, deep, wgrad_deep_rows()};
         const int32_t* cnts = g.n_macro > 1 ? sched->counts : nullptr;   // per-expert modes
+        const int32_t* sl = g.n_macro > 1 ? P.acc_slot() : nullptr;
         WgradDownArgs b3{kgrp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, hw, g.H, g.I,
-                         {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode, cnts, m, g.n_macro, g.E}};
+                         {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode, cnts, m, g.n_macro, g.E, sl}};
         if (launch_wgrad_down(b3, st)) return MOE_ERR_HIP;
         WgradGateUpArgs b4{kgrp, dgu, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, g.H, g.I,
-                           {(uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), mode, cnts, m, g.n_macro, g.E},
-                           {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode, cnts, m, g.n_macro, g.E}};
+                           {(uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), mode, cnts, m, g.n_macro, g.E, sl},
+                           {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode, cnts, m, g.n_macro, g.E, sl}};
         if (launch_wgrad_gate_up(b4, st)) return MOE_ERR_HIP;
         if (g.shared) {
             WgradDownArgs c3{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, shw, g.H, g.I,

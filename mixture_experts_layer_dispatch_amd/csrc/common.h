@@ -85,6 +85,7 @@ enum : int32_t {
     ERR_BAD_SLOT = 2,
     ERR_BAD_ROW = 4,
     ERR_BAD_OFFSETS = 8,
+    ERR_ACC_CAPACITY = 16,    // more experts span macrobatches than the workspace keeps sums for
 };
 
 __device__ __forceinline__ void raise_err(int32_t* err, int32_t bit) {

@@ -367,8 +367,7 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
     KRowsGroup sb{a.hw, a.I, lo, n, 0};
     LoadKS<W_TN, KRowsGroup> lb(sb);
     WgradOut o = a.out;
-    o.mode = wgrad_mode(a.out, e, n);
-    if (o.mode < 0) return;                                    // nothing to add for this expert
+    if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) < 0) return;   // nothing to add for this expert
     WgradEpi epi{o, (int64_t)e * a.H * a.I, a.I, m0};
     if (a.dy_gather) {
         KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
@@ -395,8 +394,7 @@ __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
     KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};
     LoadKS<W_TM, KRowsGroup> la(sa);
     WgradOut o = up ? a.out_up : a.out_gate;
-    o.mode = wgrad_mode(o, e, n);
-    if (o.mode < 0) return;                                    // nothing to add for this expert
+    if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) < 0) return;   // nothing to add for this expert
     WgradEpi epi{o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0};
     if (a.x_gather) {
         KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, 0, a.k, a.S, a.g.err};
@@ -468,8 +466,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_down_deep(WgradDownArgs a) {
             mainloop_ks_pipe<D_TM, D_TN>(la, lb, nk, smem, acc);
         }
         WgradOut o = a.out;
-        o.mode = wgrad_mode(a.out, e, n);
-        deep_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
+        if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) >= 0) deep_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
     }
 }
 
@@ -497,8 +494,8 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_gate_up_deep(WgradGateUpArgs a
             mainloop_ks_pipe<D_TM, D_TN>(la, lb, nk, smem, acc);
         }
         WgradOut o = up ? a.out_up : a.out_gate;
-        o.mode = wgrad_mode(o, e, n);
-        deep_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
+        if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) >= 0)
+            deep_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
     }
 }
 

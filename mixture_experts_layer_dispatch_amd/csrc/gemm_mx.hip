@@ -943,10 +943,9 @@ __global__ __launch_bounds__(256, 4) void k_wgrad_mx(WgradMXArgs a) {
     const int m0 = mt * X_TM;
     const bool hi_part = m0 >= a.msplit;
     WgradOut o = hi_part ? a.out_hi : a.out_lo;
-    o.mode = wgrad_mode(o, e, rows);
-    if (o.mode < 0) return;                                    // nothing to add for this expert
-    WgradEpi epi{o, (int64_t)e * (int64_t)a.msplit * a.N, a.N, hi_part ? m0 - a.msplit : m0};
-    if (a.msplit == a.M) epi.ebase = (int64_t)e * a.M * a.N;
+    const int64_t mat = (int64_t)(a.msplit == a.M ? a.M : a.msplit) * a.N;   // elements per expert
+    if (wgrad_bind(o, e, rows, mat) < 0) return;               // nothing to add for this expert
+    WgradEpi epi{o, (int64_t)e * mat, a.N, hi_part ? m0 - a.msplit : m0};
     const uint8_t* aq = a.at_q + 32 * blk0 * a.M;
     const uint8_t* as_ = a.at_s + blk0 * a.M;
     const uint8_t* bq = a.bt_q + 32 * blk0 * a.N;
@@ -998,8 +997,9 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx_deep(WgradMXArgs a) {
         mainloop_mx<XD_T, XD_T, MX_ACC>(la, lb, sa, sb, (kcodes + 127) / 128, smem, acc);
         const bool hi_part = m0 >= a.msplit;
         WgradOut out = hi_part ? a.out_hi : a.out_lo;
-        out.mode = wgrad_mode(out, e, g.blk_off ? g.off[e + 1] - g.off[e] : g.dense_rows);
-        const int64_t ebase = (int64_t)e * (a.msplit == a.M ? a.M : a.msplit) * a.N;
+        const int64_t mat = (int64_t)(a.msplit == a.M ? a.M : a.msplit) * a.N;
+        if (wgrad_bind(out, e, g.blk_off ? g.off[e + 1] - g.off[e] : g.dense_rows, mat) < 0) continue;
+        const int64_t ebase = (int64_t)e * mat;
         const int r0 = hi_part ? m0 - a.msplit : m0;
         AccPos<XD_T, XD_T> pos;
 #pragma unroll

@@ -97,13 +97,17 @@ struct GemmGuDgradArgs {
 };
 
 struct WgradOut {
-    uint16_t* out;            // bf16 result
-    float* acc;               // fp32 running sum across macrobatches
+    uint16_t* out;            // bf16 result; while a sum runs, the high halves of its fp32 bits
+    uint16_t* acc_lo;         // the low halves of the fp32 running sums' bits (across macrobatches)
     int mode;                 // 0 bf16; 1 write fp32; 2 add fp32; 3 add fp32 and write bf16
     // routed groups over several macrobatches: the mode is chosen per expert
     // from the schedule's counts [n_macro, E] (see wgrad_mode); nullptr: mode
     const int32_t* counts;
     int m, n_macro, E;
+    // routed groups over several macrobatches: each expert's accumulator slot
+    // (k_acc_slots; -1: none); nullptr: acc_lo holds one matrix per expert
+    // index (or the one dense matrix)
+    const int32_t* slot;
 };
 
 // Weight-gradient mode of expert e with n rows in macrobatch m, the backward
@@ -119,6 +123,21 @@ __host__ __device__ inline int wgrad_mode(const WgradOut& o, int e, int n) {
     if (n == 0) return (o.m == 0 && !earlier) ? 0 : -1;
     if (!earlier) return later ? 1 : 0;
     return later ? 2 : 3;
+}
+
+// The mode of expert e's gradient, with o.acc_lo moved to the expert's
+// accumulator slot (slot[e] matrices of mat elements from the start instead
+// of e), so that acc_lo + the element's index in the output addresses its
+// running sum.  An expert that needs a slot and has none (more spanning
+// experts than the workspace holds, reported by k_acc_slots) gets -1.
+__device__ inline int wgrad_bind(WgradOut& o, int e, int n, int64_t mat) {
+    o.mode = wgrad_mode(o, e, n);
+    if (o.mode >= 1 && o.slot) {
+        const int sl = o.slot[e];
+        if (sl < 0) o.mode = -1;
+        else o.acc_lo += ((int64_t)sl - e) * mat;
+    }
+    return o.mode;
 }
 
 struct WgradDownArgs {
@@ -246,6 +265,8 @@ struct WgradMXArgs {
 };
 
 // route_sched.hip
+int launch_acc_slots(const int32_t* counts, int n_macro, int E, int cap, int32_t* slot, int32_t* err,
+                     hipStream_t st);
 int launch_topk_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                       hipStream_t st);
 int launch_schedule(const int32_t* idx, int T, int E, int k, int M, int mb, int32_t* hist,

@@ -207,7 +207,47 @@ __global__ __launch_bounds__(64) void k_sched_scatter(const int32_t* __restrict_
     }
 }
 
+// Accumulator slots for a stream of several macrobatches: the routed experts
+// with rows in at least two macrobatches (the only ones whose weight
+// gradients keep a running sum across the reverse walk) get slots 0, 1, ...
+// in expert order, the others -1; past `cap` slots the expert gets -1 and
+// ERR_ACC_CAPACITY is raised.  One block of kMaxExperts threads, one expert
+// each, and a block-wide scan.
+__global__ __launch_bounds__(kMaxExperts) void k_acc_slots(const int32_t* __restrict__ counts, int n_macro,
+                                                         int E, int cap, int32_t* __restrict__ slot,
+                                                         int32_t* err) {
+    __shared__ int32_t sc[kMaxExperts];
+    const int e = threadIdx.x;
+    int spans = 0;
+    if (e < E)
+        for (int m = 0; m < n_macro; ++m) spans += counts[(int64_t)m * E + e] > 0;
+    const int need = spans >= 2 ? 1 : 0;
+    sc[e] = need;
+    __syncthreads();
+    for (int d = 1; d < kMaxExperts; d <<= 1) {          // inclusive scan
+        const int v = e >= d ? sc[e - d] : 0;
+        __syncthreads();
+        sc[e] += v;
+        __syncthreads();
+    }
+    if (e < E) {
+        int sl = need ? sc[e] - 1 : -1;
+        if (sl >= cap) {
+            raise_err(err, ERR_ACC_CAPACITY);
+            sl = -1;
+        }
+        slot[e] = sl;
+    }
+}
+
 // ============================================================== host launchers
+int launch_acc_slots(const int32_t* counts, int n_macro, int E, int cap, int32_t* slot, int32_t* err,
+                     hipStream_t st) {
+    ProfScope prof_(st, "acc_slots");
+    k_acc_slots<<<1, kMaxExperts, 0, st>>>(counts, n_macro, E, cap, slot, err);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_topk_route(const float* logits, int T, int E, int k, int32_t* idx, float* w,
                       hipStream_t st) {
     ProfScope prof_(st, "topk_route");

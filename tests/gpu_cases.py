@@ -12,10 +12,11 @@ from mixture_experts_layer_dispatch_amd import binding as B
 BF16_TOL = 1e-2       # max |gpu - ref| <= BF16_TOL * max |ref|
 
 
-def cfg_of(shape: si.MoEShape, precision=B.PREC_BF16, recompute=False) -> B.Config:
+def cfg_of(shape: si.MoEShape, precision=B.PREC_BF16, recompute=False, acc_experts=0) -> B.Config:
     return B.Config(T=shape.T, H=shape.H, I=shape.I, E=shape.E, k=shape.k,
                     n_shared=shape.n_shared, macrobatch=shape.macrobatch,
-                    minibatch=shape.minibatch, precision=precision, recompute=recompute)
+                    minibatch=shape.minibatch, precision=precision, recompute=recompute,
+                    acc_experts=acc_experts)
 
 
 def f32(t: torch.Tensor) -> np.ndarray:
@@ -37,9 +38,9 @@ class Case:
     """Inputs of one shape on the GPU, and the CPU copies the oracle reads."""
 
     def __init__(self, shape: si.MoEShape, logits_override=None, with_backward=True,
-                 precision=B.PREC_BF16, recompute=False):
+                 precision=B.PREC_BF16, recompute=False, acc_experts=0):
         self.shape = shape
-        self.cfg = cfg_of(shape, precision, recompute)
+        self.cfg = cfg_of(shape, precision, recompute, acc_experts)
         dev = "cuda"
         self.logits = logits_override.to(dev) if logits_override is not None else si.logits(shape, dev)
         self.x = si.tokens(shape, dev)

@@ -60,6 +60,9 @@ def _cfg(**kw):
     ({"capacity_rows": -1}, B.MOE_ERR_INVALID_ARG),
     ({"precision": 7}, B.MOE_ERR_INVALID_ARG),
     ({"recompute": True}, B.MOE_OK),
+    ({"macrobatch": 64, "acc_experts": 3}, B.MOE_OK),
+    ({"macrobatch": 64, "acc_experts": 100}, B.MOE_OK),        # more than E: E
+    ({"acc_experts": -1}, B.MOE_ERR_INVALID_ARG),
 ])
 def test_config_validation(kw, status):
     assert B.validate_config(_cfg(**kw)) == status
@@ -280,3 +283,17 @@ def test_mx4_weight_buffers_match_the_header_layout():
             assert tuple(q[pre + name + "s"].shape) == (*lead, K // 128, rows, 4)
     assert B.validate_config(cfg) == B.MOE_OK
     assert B.validate_config(B.Config(T=8, H=256, I=384, E=3, k=1, precision=3)) == B.MOE_ERR_INVALID_ARG
+
+
+def test_accumulators_are_sized_by_acc_experts():
+    """Several macrobatches keep fp32 running sums of the weight gradients:
+    2 bytes per weight in the workspace (the other half of each sum lives in
+    the gradient output), for acc_experts experts (0 or more than E: E); one
+    macrobatch keeps none."""
+    E, H, I = 8, 256, 128
+    full = B.workspace_size(_cfg(macrobatch=64))
+    assert B.workspace_size(_cfg(macrobatch=64, acc_experts=E)) == full
+    assert B.workspace_size(_cfg(macrobatch=64, acc_experts=100)) == full
+    three = B.workspace_size(_cfg(macrobatch=64, acc_experts=3))
+    assert full - three == (E - 3) * 3 * H * I * 2
+    assert B.workspace_size(_cfg(acc_experts=3)) == B.workspace_size(_cfg())
