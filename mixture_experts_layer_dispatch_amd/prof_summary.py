@@ -47,8 +47,16 @@ def sources_sha256() -> str:
 
 
 def _short(name: str):
-    m = re.match(r".*moe::(k_\w+)", name)
-    return m.group(1) if m else None
+    """The kernel's name without namespace and template arguments; the MXFP4
+    instantiations of the MX GEMMs (second template argument true) are told
+    apart as k_gemm_*_mx4, the names their launches time under."""
+    m = re.match(r".*moe::(k_\w+)(<[^>]*>)?", name)
+    if not m:
+        return None
+    n, targs = m.group(1), m.group(2) or ""
+    if n in ("k_gemm_gate_up_mx", "k_gemm_down_mx") and targs.replace(" ", "").endswith(",true>"):
+        n += "4"
+    return n
 
 
 def trace_table(path):
