@@ -185,19 +185,18 @@ Layout make_layout(const Geom& g) {
         }
     }
     if (g.n_macro > 1) {
-        // the low halves of fp32 running sums whose high halves live in the
-        // gradient outputs (see wgrad_store): 2 bytes per weight, for the
-        // acc_cap experts that may take rows from several macrobatches
-        const size_t per = (size_t)g.acc_cap * I * H * 2;
+        // fp32 running sums for the acc_cap experts that may take rows from
+        // several macrobatches (slots assigned on the device, k_acc_slots)
+        const size_t per = (size_t)g.acc_cap * I * H * 4;
         L.wacc_g = 0;
         L.wacc_u = per;
         L.wacc_d = 2 * per;
         size_t end = 3 * per;
         if (g.shared) {
             L.wacc_sg = end;
-            L.wacc_su = end + I * H * 2;
-            L.wacc_sd = end + 2 * I * H * 2;
-            end += 3 * I * H * 2;
+            L.wacc_su = end + I * H * 4;
+            L.wacc_sd = end + 2 * I * H * 4;
+            end += 3 * I * H * 4;
         }
         L.wacc = take(end);
         L.acc_slot = take((size_t)g.E * 4);
@@ -262,7 +261,7 @@ struct Ptrs {
     int32_t* err() const { return (int32_t*)(ws + L->err); }
     char* half(int m, int halves) const { return ws + L->ring + (size_t)(m % halves) * L->ring_half; }
     char* sh() const { return ws + L->sh; }
-    uint16_t* wacc(size_t off) const { return (uint16_t*)(ws + L->wacc + off); }
+    float* wacc(size_t off) const { return (float*)(ws + L->wacc + off); }
     int32_t* acc_slot() const { return (int32_t*)(ws + L->acc_slot); }
 };
 
@@ -394,7 +393,7 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     // counts: the schedule's [n_macro, E] counts for routed groups over several
     // macrobatches (per-expert modes), nullptr otherwise
     auto wgrads = [&](const PadGroups& pg, int mode, const int32_t* counts, int m, uint16_t* dwd,
-                      uint16_t* accd, uint16_t* dwg, uint16_t* accg, uint16_t* dwu, uint16_t* accu) -> bool {
+                      float* accd, uint16_t* dwg, float* accg, uint16_t* dwu, float* accu) -> bool {
         const int32_t* sl = counts ? P.acc_slot() : nullptr;
         WgradMXArgs d{pg, twdy, twdys, th, ths, g.H, g.I, g.H,
                       {dwd, accd, mode, counts, m, g.n_macro, g.E, sl},

@@ -97,15 +97,15 @@ struct GemmGuDgradArgs {
 };
 
 struct WgradOut {
-    uint16_t* out;            // bf16 result; while a sum runs, the high halves of its fp32 bits
-    uint16_t* acc_lo;         // the low halves of the fp32 running sums' bits (across macrobatches)
+    uint16_t* out;            // bf16 result
+    float* acc;               // fp32 running sums across macrobatches (the expert's slot)
     int mode;                 // 0 bf16; 1 write fp32; 2 add fp32; 3 add fp32 and write bf16
     // routed groups over several macrobatches: the mode is chosen per expert
     // from the schedule's counts [n_macro, E] (see wgrad_mode); nullptr: mode
     const int32_t* counts;
     int m, n_macro, E;
     // routed groups over several macrobatches: each expert's accumulator slot
-    // (k_acc_slots; -1: none); nullptr: acc_lo holds one matrix per expert
+    // (k_acc_slots; -1: none); nullptr: acc holds one matrix per expert
     // index (or the one dense matrix)
     const int32_t* slot;
 };
@@ -125,9 +125,9 @@ __host__ __device__ inline int wgrad_mode(const WgradOut& o, int e, int n) {
     return later ? 2 : 3;
 }
 
-// The mode of expert e's gradient, with o.acc_lo moved to the expert's
+// The mode of expert e's gradient, with o.acc moved to the expert's
 // accumulator slot (slot[e] matrices of mat elements from the start instead
-// of e), so that acc_lo + the element's index in the output addresses its
+// of e), so that acc + the element's index in the output addresses its
 // running sum.  An expert that needs a slot and has none (more spanning
 // experts than the workspace holds, reported by k_acc_slots) gets -1.
 __device__ inline int wgrad_bind(WgradOut& o, int e, int n, int64_t mat) {
@@ -135,7 +135,7 @@ __device__ inline int wgrad_bind(WgradOut& o, int e, int n, int64_t mat) {
     if (o.mode >= 1 && o.slot) {
         const int sl = o.slot[e];
         if (sl < 0) o.mode = -1;
-        else o.acc_lo += ((int64_t)sl - e) * mat;
+        else o.acc += ((int64_t)sl - e) * mat;
     }
     return o.mode;
 }

@@ -328,8 +328,16 @@ int launch_mx_quant_group_t(const PadGroups& g, const QtSrc& src, int C, void* c
     const int64_t rows = g.blk_off ? g.rows : g.dense_rows;
     const int64_t chunks = (g.blk_off && rows <= 128LL * g.E) ? (rows < g.E ? rows : g.E) : (rows + 127) / 128;
     const int64_t total = chunks * ((C + cb - 1) / cb);
+    // Source rows that do not stay in cache (gathered token rows past 64 MB,
+    // fp32 rows past 256 MB) come from HBM, where a chunk's column segments
+    // must be read side by side: one step per block (the 65 536-token
+    // stream's x and w*dy operands, 134 MB per macrobatch: 2.33 ms per layer
+    // step with eight steps per block, 1.71 with one).
+    const int64_t src_rows = src.kind == 1 ? rows : (src.kind == 3 ? g.dense_rows : rows / src.k);
+    const int64_t src_bytes = src_rows * src.ld * (src.kind == 1 ? 4 : 2);
+    const bool from_hbm = src_bytes > (src.kind == 1 ? (256LL << 20) : (64LL << 20));
     int steps = 1;
-    while (steps < 8 && total / (2 * steps) >= 4096) steps *= 2;
+    while (!from_hbm && steps < 8 && total / (2 * steps) >= 4096) steps *= 2;
     dim3 grid((C + steps * cb - 1) / (steps * cb), nblk);
     if (src.kind == 1)
         k_mx_quant_group_t<true><<<grid, 256, 0, st>>>(g, src, C, steps, (uint8_t*)codes, (uint8_t*)scales);

@@ -286,14 +286,13 @@ def test_mx4_weight_buffers_match_the_header_layout():
 
 
 def test_accumulators_are_sized_by_acc_experts():
-    """Several macrobatches keep fp32 running sums of the weight gradients:
-    2 bytes per weight in the workspace (the other half of each sum lives in
-    the gradient output), for acc_experts experts (0 or more than E: E); one
+    """Several macrobatches keep fp32 running sums of the weight gradients
+    (4 bytes per weight) for acc_experts experts (0 or more than E: E); one
     macrobatch keeps none."""
     E, H, I = 8, 256, 128
     full = B.workspace_size(_cfg(macrobatch=64))
     assert B.workspace_size(_cfg(macrobatch=64, acc_experts=E)) == full
     assert B.workspace_size(_cfg(macrobatch=64, acc_experts=100)) == full
     three = B.workspace_size(_cfg(macrobatch=64, acc_experts=3))
-    assert full - three == (E - 3) * 3 * H * I * 2
+    assert full - three == (E - 3) * 3 * H * I * 4
     assert B.workspace_size(_cfg(acc_experts=3)) == B.workspace_size(_cfg())
