@@ -265,6 +265,17 @@ struct Ptrs {
     int32_t* acc_slot() const { return (int32_t*)(ws + L->acc_slot); }
 };
 
+// Top-1 routing without a shared expert: a token's layer output (and input
+// gradient) is its one routed row, so the down GEMM (and the gate/up input
+// gradient) write it straight to the token's row of y (dx) and the combine
+// (reverse-dispatch) pass is skipped.  The single fp32 term rounds once
+// either way, so the bits are those of the combine.
+bool top1_direct(const Geom& g) { return g.k == 1 && !g.shared; }
+
+RowDest token_rows(const Geom& g, const moe_sched* s, int grow0) {
+    return top1_direct(g) ? RowDest{s->slot_of_row, grow0, g.k, g.S} : RowDest{nullptr, 0, 1, 0};
+}
+
 // Where macrobatch m's gate and up projections are kept for the backward:
 // the caller's saved arrays (rows of the whole batch), or in recompute mode
 // the workspace's one-macrobatch buffers (local rows), which the forward
@@ -332,8 +343,9 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
                             (const uint8_t*)fw.us, g.H, g.I, (float*)keep.g, (float*)keep.u, keep.row0,
                             hq, hs};
         if (launch_gemm_gate_up_mx(a1, st)) return MOE_ERR_HIP;
-        GemmDownMXArgs a2{grp, w4, hq, hs, (const uint8_t*)fw.dq, (const uint8_t*)fw.ds, g.H, g.I, obuf,
-                          {sched->topk_w, sched->slot_of_row, grow0, g.S}};
+        GemmDownMXArgs a2{grp, w4, hq, hs, (const uint8_t*)fw.dq, (const uint8_t*)fw.ds, g.H, g.I,
+                          top1_direct(g) ? (uint16_t*)y : obuf, {sched->topk_w, sched->slot_of_row, grow0, g.S},
+                          token_rows(g, sched, grow0)};
         if (launch_gemm_down_mx(a2, st)) return MOE_ERR_HIP;
         const uint16_t* sh_o = nullptr;
         if (g.shared) {
@@ -353,8 +365,8 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
             if (launch_gemm_down_mx(s2, st)) return MOE_ERR_HIP;
             sh_o = so;
         }
-        if (launch_combine(obuf, g.H, sched->row_of_slot, nullptr, t0, t0 + g.M, g.k, grow0, g.Sm,
-                           sh_o, t0, y, err, st))
+        if (!top1_direct(g) && launch_combine(obuf, g.H, sched->row_of_slot, nullptr, t0, t0 + g.M, g.k, grow0,
+                                              g.Sm, sh_o, t0, y, err, st))
             return MOE_ERR_HIP;
     }
     return MOE_OK;
@@ -438,7 +450,8 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         if (launch_gemm_down_dgrad_mx(b1, st)) return MOE_ERR_HIP;
         GemmGuDgradMXArgs b2{grp, dguq, dgus, (const uint8_t*)wq->w_gate_tq,
                              (const uint8_t*)wq->w_gate_ts, (const uint8_t*)wq->w_up_tq,
-                             (const uint8_t*)wq->w_up_ts, g.H, g.I, dxd};
+                             (const uint8_t*)wq->w_up_ts, g.H, g.I, top1_direct(g) ? (uint16_t*)dx : dxd,
+                             token_rows(g, sched, grow0)};
         if (launch_gemm_gu_dgrad_mx(b2, st)) return MOE_ERR_HIP;
         // the shared expert's input gradient, then reverse-dispatch and the
         // softmax backward while dXd is still in cache; the weight gradients
@@ -471,8 +484,8 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
             if (launch_gemm_gu_dgrad_mx(c2, st)) return MOE_ERR_HIP;
             sh_dx = sdx;
         }
-        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
-                             dx, err, st))
+        if (!top1_direct(g) && launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm,
+                                                sh_dx, t0, dx, err, st))
             return MOE_ERR_HIP;
         if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
                                t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
@@ -756,8 +769,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
                           (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
                           (uint16_t*)keep.g, (uint16_t*)keep.u, keep.row0, hbuf};
         if (launch_gemm_gate_up(a1, st)) return MOE_ERR_HIP;
-        GemmDownArgs a2{grp, hbuf, (const uint16_t*)w->w_down, g.H, g.I, obuf,
-                        {sched->topk_w, sched->slot_of_row, grow0, g.S}};
+        GemmDownArgs a2{grp, hbuf, (const uint16_t*)w->w_down, g.H, g.I, top1_direct(g) ? (uint16_t*)y : obuf,
+                        {sched->topk_w, sched->slot_of_row, grow0, g.S}, token_rows(g, sched, grow0)};
         if (launch_gemm_down(a2, st)) return MOE_ERR_HIP;
         const uint16_t* sh_o = nullptr;
         if (g.shared) {
@@ -775,8 +788,8 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
         }
         // the router-weighted reduction: y_t = [shared] + sum_j (w o)_(t,j), in
         // that fixed order (the rows already carry their weights)
-        if (launch_combine(obuf, g.H, sched->row_of_slot, nullptr, t0, t0 + g.M, g.k, grow0, g.Sm,
-                           sh_o, t0, y, err, st))
+        if (!top1_direct(g) && launch_combine(obuf, g.H, sched->row_of_slot, nullptr, t0, t0 + g.M, g.k, grow0,
+                                              g.Sm, sh_o, t0, y, err, st))
             return MOE_ERR_HIP;
     }
     return MOE_OK;
@@ -853,7 +866,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                              (const uint16_t*)w->w_down, g.H, g.I, (const uint16_t*)gu.g,
                              (const uint16_t*)gu.u, gu.row0, dgu, hw, part, g.P};
         if (launch_gemm_down_dgrad(b1, st)) return MOE_ERR_HIP;
-        GemmGuDgradArgs b2{grp, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I, dxd};
+        GemmGuDgradArgs b2{grp, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
+                           top1_direct(g) ? (uint16_t*)dx : dxd, token_rows(g, sched, grow0)};
         if (launch_gemm_gu_dgrad(b2, st)) return MOE_ERR_HIP;
         // the shared expert's input gradient, then reverse-dispatch and the
         // softmax backward while dXd is still in cache; the weight gradients
@@ -881,8 +895,8 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
             sh_dx = sdx;
         }
         // reverse-dispatch: dx_t = [shared] + sum_j dXd[row(t, j)]
-        if (launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm, sh_dx, t0,
-                             dx, err, st))
+        if (!top1_direct(g) && launch_rd_reduce(dxd, g.H, sched->row_of_slot, t0, t0 + g.M, g.k, grow0, g.Sm,
+                                                sh_dx, t0, dx, err, st))
             return MOE_ERR_HIP;
         if (launch_softmax_bwd(part, g.P, sched->row_of_slot, sched->topk_idx, sched->topk_w, t0,
                                t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))

@@ -134,16 +134,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
     float wr[TM / 32];
 #pragma unroll
     for (int mb = 0; mb < TM / 32; ++mb) wr[mb] = lo + pos.m(mb) < hi ? a.rw.at(lo + pos.m(mb)) : 0.f;
+    int64_t orow[TM / 32];
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) orow[mb] = lo + pos.m(mb) < hi ? a.dest.row(lo + pos.m(mb), a.g.err) : -1;
     auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
         for (int mb = 0; mb < TM / 32; ++mb) {
-            const int rl = lo + pos.m(mb);
-            if (rl >= hi) continue;
+            if (orow[mb] < 0) continue;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 const int col = n0 + t * G2_TN + pos.n(nb);
                 const f32x4 v = c[mb][nb];
-                *(uint2*)(a.o + (int64_t)rl * a.H + col) =
+                *(uint2*)(a.o + orow[mb] * a.H + col) =
                     pack4(wr[mb] * v[0], wr[mb] * v[1], wr[mb] * v[2], wr[mb] * v[3]);
             }
         }
@@ -268,16 +270,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
     KRowsGateUp sb{a.w_gate + (int64_t)e * a.I * a.H, a.w_up + (int64_t)e * a.I * a.H, a.H, n0, a.I};
     LoadKS<G4_TN, KRowsGateUp> lb(sb);
     AccPos<TM, G4_TN> pos;
+    int64_t orow[TM / 32];
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) orow[mb] = lo + pos.m(mb) < hi ? a.dest.row(lo + pos.m(mb), a.g.err) : -1;
     auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
         for (int mb = 0; mb < TM / 32; ++mb) {
-            const int rl = lo + pos.m(mb);
-            if (rl >= hi) continue;
+            if (orow[mb] < 0) continue;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 const int col = n0 + t * G4_TN + pos.n(nb);
                 const f32x4 v = c[mb][nb];
-                *(uint2*)(a.dx + (int64_t)rl * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
+                *(uint2*)(a.dx + orow[mb] * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
             }
         }
     };

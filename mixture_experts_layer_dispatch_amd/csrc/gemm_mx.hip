@@ -548,16 +548,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_mx(GemmDownMXArgs a) {
     float wr[TM / 32];          // router weight of each row (the combine is a plain sum)
 #pragma unroll
     for (int mb = 0; mb < TM / 32; ++mb) wr[mb] = lo + pos.m(mb) < hi ? a.rw.at(lo + pos.m(mb)) : 0.f;
+    int64_t orow[TM / 32];
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) orow[mb] = lo + pos.m(mb) < hi ? a.dest.row(lo + pos.m(mb), a.g.err) : -1;
     auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
         for (int mb = 0; mb < TM / 32; ++mb) {
-            const int rl = lo + pos.m(mb);
-            if (rl >= hi) continue;
+            if (orow[mb] < 0) continue;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 const int col = n0 + t * M2_TN + pos.n(nb);
                 const f32x4 v = c[mb][nb];
-                *(uint2*)(a.o + (int64_t)rl * H + col) =
+                *(uint2*)(a.o + orow[mb] * H + col) =
                     pack4(wr[mb] * v[0], wr[mb] * v[1], wr[mb] * v[2], wr[mb] * v[3]);
             }
         }
@@ -732,16 +734,18 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad_mx(GemmGuDgradMXArgs a
     LoadScales<TM, ScalesDirect> sa(dsa);
     LoadScalesCat<M4_TN> sb(dsg, dsu, I / 128);
     AccPos<TM, M4_TN> pos;
+    int64_t orow[TM / 32];
+#pragma unroll
+    for (int mb = 0; mb < TM / 32; ++mb) orow[mb] = lo + pos.m(mb) < hi ? a.dest.row(lo + pos.m(mb), a.g.err) : -1;
     auto epi = [&](int t, const f32x4 (&c)[TM / 32][4]) {
 #pragma unroll
         for (int mb = 0; mb < TM / 32; ++mb) {
-            const int rl = lo + pos.m(mb);
-            if (rl >= hi) continue;
+            if (orow[mb] < 0) continue;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 const int col = n0 + t * M4_TN + pos.n(nb);
                 const f32x4 v = c[mb][nb];
-                *(uint2*)(a.dx + (int64_t)rl * H + col) = pack4(v[0], v[1], v[2], v[3]);
+                *(uint2*)(a.dx + orow[mb] * H + col) = pack4(v[0], v[1], v[2], v[3]);
             }
         }
     };

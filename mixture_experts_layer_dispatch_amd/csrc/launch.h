@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "common.h"
+
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
@@ -59,6 +61,25 @@ struct RowWeights {
     }
 };
 
+// Where an output row of a routed GEMM goes: its ring row (slot_of_row null),
+// or, with one expert per token and no shared expert (top-1 routing), its
+// token's row of the caller's output, which then needs no combine or
+// reverse-dispatch pass: the row is the token's whole sum.  -1: a bad slot
+// (raised, nothing written).
+struct RowDest {
+    const int32_t* slot_of_row;
+    int grow0, k, S;
+    __device__ int64_t row(int rl, int32_t* err) const {
+        if (!slot_of_row) return rl;
+        const int s = slot_of_row[grow0 + rl];
+        if ((unsigned)s >= (unsigned)S) {
+            raise_err(err, ERR_BAD_SLOT);
+            return -1;
+        }
+        return s / k;
+    }
+};
+
 struct GemmDownArgs {
     GroupRows g;
     const uint16_t* h;        // ring h [rows, I]
@@ -66,6 +87,7 @@ struct GemmDownArgs {
     int H, I;
     uint16_t* o;              // ring o [rows, H]: w * (h W_down^T) per row
     RowWeights rw;
+    RowDest dest;             // null slot_of_row: row rl of o; else the token's row
 };
 
 struct GemmDownDgradArgs {
@@ -94,6 +116,7 @@ struct GemmGuDgradArgs {
     const uint16_t* w_up;
     int H, I;
     uint16_t* dx;             // ring [rows, H]
+    RowDest dest;             // as in GemmDownArgs
 };
 
 struct WgradOut {
@@ -193,6 +216,7 @@ struct GemmDownMXArgs {
     int H, I;
     uint16_t* o;              // w * (Q(h) Q(W_down)^T) per row
     RowWeights rw;
+    RowDest dest;             // as in GemmDownArgs
 };
 
 // Expert groups padded to whole 32-row blocks (the MXFP8 weight gradients
@@ -251,6 +275,7 @@ struct GemmGuDgradMXArgs {
     const uint8_t* wut_s;
     int H, I;
     uint16_t* dx;             // ring [rows, H] bf16
+    RowDest dest;             // as in GemmDownArgs
 };
 
 struct WgradMXArgs {

@@ -44,6 +44,8 @@ SHAPES = {
     "all_experts": si.custom_shape("all_experts_mx", T=96, H=128, I=128, E=4, k=4, seed=30),
     "max_k": si.custom_shape("max_k_mx", T=64, H=128, I=128, E=64, k=32, seed=31),
     "max_e": si.custom_shape("max_e_mx", T=256, H=128, I=128, E=1024, k=8, seed=33),
+    "top1_ring": si.custom_shape("top1_ring_mx", T=512, H=256, I=256, E=8, k=1, seed=35,
+                                 macrobatch=128, minibatch=64),
 }
 
 

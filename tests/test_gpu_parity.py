@@ -44,6 +44,11 @@ SMALL = {
     # the largest E (1024): ten ballot rounds over the expert-id bits, most
     # experts empty
     "max_e": si.custom_shape("max_e", T=256, H=128, I=128, E=1024, k=8, seed=32),
+    # top-1 routing without a shared expert over several macrobatches: the
+    # down projection and the gate/up input gradient write y and dx rows
+    # directly (no combine or reverse-dispatch pass)
+    "top1_ring": si.custom_shape("top1_ring", T=512, H=256, I=256, E=8, k=1, seed=34,
+                                 macrobatch=128, minibatch=64),
 }
 
 
