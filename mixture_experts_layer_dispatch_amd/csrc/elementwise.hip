@@ -194,21 +194,11 @@ __global__ __launch_bounds__(256) void k_softmax_bwd(const float* __restrict__ p
 
 // ============================================================== tile prefix
 // tile_off[e] = sum_{e' < e} ceil(count(e') / TM) from one macrobatch's
-// offsets; tile_off[E] is the number of row tiles.  One block, E <= 1024.
-__global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict__ offsets, int E,
-                                                      int rows, int TM, int32_t* __restrict__ tile_off,
-                                                      int32_t* __restrict__ err) {
-    __shared__ int32_t wsum[16];
-    const int e = threadIdx.x;
-    int n = 0;
-    if (e < E) {
-        const int a = offsets[e], b = offsets[e + 1];
-        if (a < 0 || b < a || b > rows) {
-            raise_err(err, ERR_BAD_OFFSETS);
-        } else {
-            n = (b - a + TM - 1) / TM;
-        }
-    }
+// offsets; tile_off[E] is the number of row tiles.  With split outputs, also
+// the same prefix over the groups below big_rows rows only (small, TM-row
+// tiles) and over the others only (big, big_tm-row tiles), for GEMMs that
+// take the large groups in a tile form of their own.  One block, E <= 1024.
+__device__ __forceinline__ int block_excl_scan(int n, int32_t* wsum, int& total) {
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     int incl = n;
 #pragma unroll
@@ -220,8 +210,39 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict_
     __syncthreads();
     int wpre = 0;
     for (int q = 0; q < wv; ++q) wpre += wsum[q];
-    if (e < E) tile_off[e] = wpre + incl - n;
-    if (e == E - 1) tile_off[E] = wpre + incl;
+    total = 0;
+    for (int q = 0; q < (int)(blockDim.x >> 6); ++q) total += wsum[q];
+    __syncthreads();                       // wsum is reused by the next scan
+    return wpre + incl - n;
+}
+
+__global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict__ offsets, int E,
+                                                      int rows, int TM, int32_t* __restrict__ tile_off,
+                                                      int big_rows, int big_tm, int32_t* __restrict__ small,
+                                                      int32_t* __restrict__ big, int32_t* __restrict__ err) {
+    __shared__ int32_t wsum[16];
+    const int e = threadIdx.x;
+    int cnt = 0;
+    if (e < E) {
+        const int a = offsets[e], b = offsets[e + 1];
+        if (a < 0 || b < a || b > rows) raise_err(err, ERR_BAD_OFFSETS);
+        else cnt = b - a;
+    }
+    int total;
+    const int n = (cnt + TM - 1) / TM;
+    const int pre = block_excl_scan(n, wsum, total);
+    if (e < E) tile_off[e] = pre;
+    if (e == 0) tile_off[E] = total;
+    if (!big) return;
+    const bool is_big = cnt >= big_rows;
+    const int ns = is_big ? 0 : n;
+    const int ps = block_excl_scan(ns, wsum, total);
+    if (e < E) small[e] = ps;
+    if (e == 0) small[E] = total;
+    const int nb = is_big ? (cnt + big_tm - 1) / big_tm : 0;
+    const int pb = block_excl_scan(nb, wsum, total);
+    if (e < E) big[e] = pb;
+    if (e == 0) big[E] = total;
 }
 
 // Experts whose group has more than thr rows, in ascending order:
@@ -280,8 +301,15 @@ int launch_softmax_bwd(const float* part, int P, const int32_t* row_of_slot, con
 
 int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
                        int32_t* err, hipStream_t st) {
+    return launch_tile_prefix_split(offsets, E, rows, TM, tile_off, 0, 0, nullptr, nullptr, err, st);
+}
+
+int launch_tile_prefix_split(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
+                             int big_rows, int big_tm, int32_t* small, int32_t* big, int32_t* err,
+                             hipStream_t st) {
     ProfScope prof_(st, "tile_prefix");
-    k_tile_prefix<<<1, 1024, 0, st>>>(offsets, E, rows, TM, tile_off, err);
+    if (E > 1024 || (big && (!small || big_rows <= 0 || big_tm <= 0))) return -1;
+    k_tile_prefix<<<1, 1024, 0, st>>>(offsets, E, rows, TM, tile_off, big_rows, big_tm, small, big, err);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

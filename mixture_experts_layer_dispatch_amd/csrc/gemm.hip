@@ -158,6 +158,39 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
     }
 }
 
+// The groups of at least kBigRows rows in 256 x 256 tiles (mainloop_big):
+// the same rows, scaled by their router weights, and the same bits (K steps
+// ascend and each MFMA sums in a fixed order, whatever the tile shape).
+__global__ __launch_bounds__(kBigThreads, 1) void k_gemm_down_big(GemmDownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[SmemBig::TOTAL];
+    int e, lo, hi, nt;
+    if (!map_mtile_big(a.g, a.H / kBig, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * kBig;
+    f32x4 acc[8][4];
+    {
+        const RowsDirect sa{a.h, a.I, lo, hi - lo};
+        const RowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, kBig};
+        const DirectKC la(sa), lb(sb);
+        mainloop_big(la, lb, a.I / kTK, smem, acc);
+    }
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int rl = lo + wm0 + mb * 16 + (lane & 15);
+        if (rl >= hi) continue;
+        const int64_t orow = a.dest.row(rl, a.g.err);
+        if (orow < 0) continue;
+        const float wr = a.rw.at(rl);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int col = n0 + wn0 + nb * 16 + 4 * (lane >> 4);
+            const f32x4 v = acc[mb][nb];
+            *(uint2*)(a.o + orow * a.H + col) = pack4(wr * v[0], wr * v[1], wr * v[2], wr * v[3]);
+        }
+    }
+}
+
 // ================================================================ backward: down dgrad
 // a = dY W_down (dY row = dy of the row's token, gathered on load), then the
 // SwiGLU backward and the router-weight gradient in the epilogue:
@@ -545,8 +578,31 @@ int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+// 256 x 256 tiles: the routed groups of tile_big, or a dense group of at
+// least kBigRows rows (then alone)
+static inline bool dense_big(const GroupRows& g, int ncols) {
+    return !g.tile_off && g.tm == 128 && g.dense_rows >= kBigRows && ncols % kBig == 0;
+}
+
+static inline int big_grid(const GroupRows& g) {
+    if (!g.tile_off) return (g.dense_rows + kBig - 1) / kBig;
+    // groups of n >= kBigRows rows take ceil(n / kBig) <= n / 128 tiles
+    const int64_t a = (int64_t)g.rows / 128, b = ((int64_t)g.rows + (int64_t)g.E * (kBig - 1)) / kBig;
+    return (int)(a < b ? a : b);
+}
+
 int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down");
+    const bool dbig = dense_big(a.g, a.H);
+    if (a.g.tile_big || dbig) {
+        if (a.H % kBig != 0 || a.I % kTK != 0) return -1;
+        const int grid = big_grid(a.g) * (a.H / kBig);
+        if (grid > 0) {
+            k_gemm_down_big<<<grid, kBigThreads, 0, st>>>(a);
+            if (hipGetLastError() != hipSuccess) return -1;
+        }
+        if (dbig) return 0;
+    }
     const int ncol = a.H / G2_TN;
     MOE_LAUNCH_TM2(k_gemm_down, (ncol + short_k_tiles_per_block<64>() - 1) / short_k_tiles_per_block<64>(),
                    (ncol + short_k_tiles_per_block<128>() - 1) / short_k_tiles_per_block<128>());

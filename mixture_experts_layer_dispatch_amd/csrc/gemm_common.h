@@ -552,6 +552,109 @@ __device__ __forceinline__ void mainloop_ks_pipe(LA& la, LB& lb, int nk, uint16_
     }
 }
 
+// ================================================================ 256 x 256 tiles
+// Groups of hundreds of rows or more (each weight tile then feeds hundreds of
+// output rows, and the GEMM is MFMA work): 512-thread blocks of 256 x 256
+// output, eight waves in a 2 (rows) x 4 (columns) grid, each 128 x 64.  Per
+// 64-deep K step a block reads 64 KB of operands for 8.4 MFLOP (128 flop per
+// byte from L2, twice the 128 x 128 tile's), and each wave reads 24 KB of
+// fragments from LDS for 64 MFMAs.  Operands go from global memory straight
+// into LDS (gfx950's global_load_lds, 16 bytes per lane, no register
+// staging) in the swizzled KC layout, two stages of 64 KB; the copies of the
+// next step are issued one per column block inside the MFMA loop, so they
+// fly while the current step computes.
+constexpr int kBigThreads = 512;       // kBig, kBigRows: launch.h
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+
+// KC tile of kBig rows by kTK: the 16-byte chunk g = q * 512 + wave * 64 + lane
+// of the tile (row g / 8, slot g % 8) is loaded by lane `lane` of wave `wave`
+// in its q-th copy; slot s of row r holds chunk s ^ ((r >> 1) & 7) of the row,
+// the layout kc_off describes.  Rows the source does not have read its safe
+// row instead (their results are never stored).
+struct DirectKC {
+    static constexpr int PER = kBig * (kTK / 8) / kBigThreads;
+    const uint16_t* p[PER];
+    template <class Src>
+    __device__ explicit DirectKC(const Src& src) {
+        const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int g = q * kBigThreads + w * 64 + lane;
+            const int r = g >> 3, c = (g & 7) ^ ((r >> 1) & 7);
+            const uint16_t* b = src.row(r);
+            p[q] = (b ? b : src.safe()) + c * 8;
+        }
+    }
+    __device__ __forceinline__ void issue1(int q, int kt, uint16_t* tile) const {
+        const int w = threadIdx.x >> 6;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(p[q] + (int64_t)kt * kTK),
+                                         (lds_void_t*)(tile + (q * kBigThreads + w * 64) * 8), 16, 0, 0);
+    }
+    __device__ __forceinline__ void issue(int kt, uint16_t* tile) const {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) issue1(q, kt, tile);
+    }
+};
+
+struct SmemBig {
+    static constexpr int A = Tile<kBig, false>::SIZE;     // uint16 per operand tile
+    static constexpr int STAGE = 2 * A;
+    static constexpr int TOTAL = 2 * STAGE;               // 128 KB
+};
+
+// wait for every copy this thread issued (vmcnt 0; the expcnt and lgkmcnt
+// fields left at their maxima would not wait, but lgkmcnt 0 is harmless here)
+__device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x0070); }
+
+// acc[mb][nb]: output rows wm0 + 16 mb + (lane & 15), columns wn0 + 16 nb +
+// 4 (lane >> 4) + r, with wm0 = 128 (wave & 1), wn0 = 64 (wave >> 1).
+__device__ __forceinline__ void mainloop_big(const DirectKC& la, const DirectKC& lb, int nk, uint16_t* smem,
+                                             f32x4 (&acc)[8][4]) {
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nk <= 0) return;
+    la.issue(0, smem);
+    lb.issue(0, smem + SmemBig::A);
+    wait_copies();
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+        const uint16_t* cur = smem + (kt & 1) * SmemBig::STAGE;
+        uint16_t* nxt = smem + ((kt + 1) & 1) * SmemBig::STAGE;
+        const bool more = kt + 1 < nk;
+        const uint16_t* sA = cur;
+        const uint16_t* sB = cur + SmemBig::A;
+#pragma unroll
+        for (int ks = 0; ks < kTK; ks += 32) {
+            bf16x8 fb[8];
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) fb[mb] = frag_kc(sA, 0, wm0 + mb * 16, ks);
+            bf16x8 fa0 = frag_kc(sB, 0, wn0, ks), fa1;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                if (nb + 1 < 4) {
+                    if (nb & 1) fa0 = frag_kc(sB, 0, wn0 + (nb + 1) * 16, ks);
+                    else fa1 = frag_kc(sB, 0, wn0 + (nb + 1) * 16, ks);
+                }
+                const int li = (ks / 32) * 4 + nb;       // 0..7: the next step's eight copies
+                if (more) {
+                    if (li < DirectKC::PER) la.issue1(li, kt + 1, nxt);
+                    else lb.issue1(li - DirectKC::PER, kt + 1, nxt + SmemBig::A);
+                }
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma_16x16x32((nb & 1) ? fa1 : fa0, fb[mb], acc[mb][nb]);
+            }
+        }
+        wait_copies();
+        __syncthreads();
+    }
+}
+
 // accumulator (mb, nb, r) -> tile coordinates
 template <int TM, int TN>
 struct AccPos {
@@ -595,6 +698,34 @@ __device__ __forceinline__ bool map_mtile(const GroupRows& g, int nNt, int b, in
     e = a;
     lo = g.offsets[e] + (mt - g.tile_off[e]) * TM;
     hi = min(lo + TM, g.offsets[e + 1]);
+    return true;
+}
+
+// M-grouped with 256-row tiles: the groups of at least kBigRows rows, over
+// their own tile prefix (g.tile_big); a dense group takes them whole.
+__device__ __forceinline__ bool map_mtile_big(const GroupRows& g, int nNt, int b, int& e, int& lo, int& hi,
+                                              int& nt) {
+    const int ntiles = g.tile_off ? g.tile_big[g.E] : (g.dense_rows + kBig - 1) / kBig;
+    const int total = ntiles * nNt;
+    if (b >= total) return false;
+    const int L = xcd_remap(b, total);
+    const int mt = L / nNt;
+    nt = L - mt * nNt;
+    if (!g.tile_off) {
+        e = 0;
+        lo = mt * kBig;
+        hi = min(lo + kBig, g.dense_rows);
+        return true;
+    }
+    int a = 0, z = g.E;
+    while (z - a > 1) {
+        const int mid = (a + z) >> 1;
+        if (g.tile_big[mid] <= mt) a = mid;
+        else z = mid;
+    }
+    e = a;
+    lo = g.offsets[e] + (mt - g.tile_big[e]) * kBig;
+    hi = min(lo + kBig, g.offsets[e + 1]);
     return true;
 }
 

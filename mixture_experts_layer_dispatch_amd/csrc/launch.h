@@ -14,6 +14,11 @@ constexpr int kBlockSlots = 512;   // slots per schedule block
 
 // Row groups of one macrobatch.  offsets == nullptr: a single dense group of
 // dense_rows rows (the shared expert).
+// 256 x 256 output tiles (eight-wave blocks) for the groups of at least
+// kBigRows rows, in the GEMMs that have that form
+constexpr int kBig = 256;
+constexpr int kBigRows = 256;
+
 struct GroupRows {
     const int32_t* offsets;   // [E+1] macrobatch-local row offsets
     const int32_t* tile_off;  // [E+1] prefix of row tiles (M-grouped GEMMs)
@@ -27,6 +32,10 @@ struct GroupRows {
     const int32_t* deep;
     int deep_thr;
     int tm;                   // M-grouped GEMMs: row tile of tile_off (64 or 128; 0 = 64)
+    // [E+1] prefix of 256-row tiles over the groups of at least kBigRows rows
+    // (GEMMs with a 256 x 256 tile form; null: none).  tile_off then counts
+    // only the other groups.
+    const int32_t* tile_big;
 };
 
 struct GemmGateUpArgs {
@@ -311,6 +320,11 @@ int launch_softmax_bwd(const float* part, int P, const int32_t* row_of_slot, con
                        float* dw, float* d_logits, int32_t* err, hipStream_t st);
 int launch_tile_prefix(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
                        int32_t* err, hipStream_t st);
+// the same, plus the prefixes over the groups below big_rows rows (TM-row
+// tiles) and over the rest (big_tm-row tiles)
+int launch_tile_prefix_split(const int32_t* offsets, int E, int rows, int TM, int32_t* tile_off,
+                             int big_rows, int big_tm, int32_t* small, int32_t* big, int32_t* err,
+                             hipStream_t st);
 int launch_deep_list(const int32_t* offsets, int E, int rows, int thr, int32_t* list, hipStream_t st);
 
 // mx.hip

@@ -49,6 +49,16 @@ SMALL = {
     # directly (no combine or reverse-dispatch pass)
     "top1_ring": si.custom_shape("top1_ring", T=512, H=256, I=256, E=8, k=1, seed=34,
                                  macrobatch=128, minibatch=64),
+    # groups of several hundred rows over two macrobatches, with a dense
+    # shared expert of 512 rows per macrobatch: the down projection's
+    # 256 x 256 tiles (groups of at least 256 rows, ragged tails) beside the
+    # 128-row tiles of the smaller groups
+    "big_tiles": si.custom_shape("big_tiles", T=1024, H=512, I=256, E=4, k=2, seed=36,
+                                 n_shared=1, macrobatch=512, minibatch=256),
+    # Zipf-skewed groups: a few hot experts in 256-row tiles, the rest in
+    # 128-row tiles, top-1 (rows written straight to y)
+    "big_zipf_top1": si.custom_shape("big_zipf_top1", T=4096, H=256, I=128, E=16, k=1, seed=37,
+                                     zipf=True),
 }
 
 
