@@ -763,9 +763,9 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
-        // the down GEMM takes groups of at least kBigRows rows in 256 x 256
-        // tiles when groups are large on average
-        const bool big = tm == 128 && g.H % kBig == 0;
+        // the gate/up and down GEMMs take groups of at least kBigRows rows in
+        // 256 x 256 tiles when groups are large on average
+        const bool big = tm == 128 && g.H % kBig == 0 && g.I % (kBig / 2) == 0;
         int32_t* tsmall = (int32_t*)((char*)workspace + L.tile_split) + (size_t)m * 2 * (g.E + 1);
         int32_t* tbig = tsmall + (g.E + 1);
         if (big ? launch_tile_prefix_split(off, g.E, g.Sm, tm, toff, kBigRows, kBig, tsmall, tbig, err, st)
@@ -774,17 +774,16 @@ moe_status moe_forward(const moe_config* cfg, const moe_sched* sched, const void
         // dispatch fused into the gate/up GEMM: its operand loads gather each
         // routed row from the row of its token
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
-        GroupRows grp_down = grp;
         if (big) {
-            grp_down.tile_off = tsmall;
-            grp_down.tile_big = tbig;
+            grp.tile_off = tsmall;
+            grp.tile_big = tbig;
         }
         const GU keep = gu_routed(g, L, P, saved, m, true);
         GemmGateUpArgs a1{grp, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
                           (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
                           (uint16_t*)keep.g, (uint16_t*)keep.u, keep.row0, hbuf};
         if (launch_gemm_gate_up(a1, st)) return MOE_ERR_HIP;
-        GemmDownArgs a2{grp_down, hbuf, (const uint16_t*)w->w_down, g.H, g.I, top1_direct(g) ? (uint16_t*)y : obuf,
+        GemmDownArgs a2{grp, hbuf, (const uint16_t*)w->w_down, g.H, g.I, top1_direct(g) ? (uint16_t*)y : obuf,
                         {sched->topk_w, sched->slot_of_row, grow0, g.S}, token_rows(g, sched, grow0)};
         if (launch_gemm_down(a2, st)) return MOE_ERR_HIP;
         const uint16_t* sh_o = nullptr;

@@ -106,6 +106,55 @@ __global__ __launch_bounds__(GateUpShape<TM>::NTHR, TM == 64 ? 2 : 1) void k_gem
     }
 }
 
+// The groups of at least kBigRows rows in 256 x 256 tiles (mainloop_big):
+// 256 rows x (128 gate + 128 up columns); wave w holds gate columns
+// i0 + 32 (w >> 1) + 0..31 in acc[.][0..1] and the matching up columns in
+// acc[.][2..3] (RowsGateUp's quarters).  Same bits as the 128-row tiles.
+__global__ __launch_bounds__(kBigThreads, 1) void k_gemm_gate_up_big(GemmGateUpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t smem[SmemBig::TOTAL];
+    int e, lo, hi, nt;
+    if (!map_mtile_big(a.g, a.I / (kBig / 2), blockIdx.x, e, lo, hi, nt)) return;
+    const int i0 = nt * (kBig / 2);
+    f32x4 acc[8][4];
+    {
+        const RowsGateUp sb{a.w_gate + (int64_t)e * a.I * a.H, a.w_up + (int64_t)e * a.I * a.H, a.H, i0};
+        const DirectKC lb(sb);
+        if (a.x_gather) {
+            const RowsGather sa{a.x, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
+            const DirectKC la(sa);
+            mainloop_big(la, lb, a.H / kTK, smem, acc);
+        } else {
+            const RowsDirect sa{a.x, a.H, a.xrow0 + lo, hi - lo};
+            const DirectKC la(sa);
+            mainloop_big(la, lb, a.H / kTK, smem, acc);
+        }
+    }
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wq = w >> 1;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int rl = lo + wm0 + mb * 16 + (lane & 15);
+        if (rl >= hi) continue;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int i = i0 + 32 * wq + nb * 16 + 4 * (lane >> 4);
+            float gq[4], uq[4], hq[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                gq[r] = bf2f(f2bf(acc[mb][nb][r]));
+                uq[r] = bf2f(f2bf(acc[mb][nb + 2][r]));
+                hq[r] = swiglu_h(gq[r], uq[r]);
+            }
+            if (a.g_out) {
+                const int64_t srow = (int64_t)(a.save_row0 + rl) * a.I + i;
+                *(uint2*)(a.g_out + srow) = pack4(gq[0], gq[1], gq[2], gq[3]);
+                *(uint2*)(a.u_out + srow) = pack4(uq[0], uq[1], uq[2], uq[3]);
+            }
+            *(uint2*)(a.h_out + (int64_t)rl * a.I + i) = pack4(hq[0], hq[1], hq[2], hq[3]);
+        }
+    }
+}
+
 // ================================================================ forward GEMM 2
 // o = w * (h W_down^T), each row scaled by its slot's router weight in fp32
 // before the one rounding to bf16.  alphalab.site "Mixture-of-Kittens" keeps
@@ -568,20 +617,12 @@ static inline int row_tile(const GroupRows& g) { return g.tm == 128 ? 128 : 64; 
         return hipGetLastError() == hipSuccess ? 0 : -1;                           \
     } while (0)
 
-int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
-    ProfScope prof_(st, "gemm_gate_up");
-    const int tm_ = row_tile(a.g);
-    const int grid_ = mgroup_grid(a.g, tm_) * (a.I / (tm_ == 128 ? 128 : 64));
-    if (grid_ <= 0) return 0;
-    if (tm_ == 128) k_gemm_gate_up<128><<<grid_, GateUpShape<128>::NTHR, 0, st>>>(a);
-    else k_gemm_gate_up<64><<<grid_, GateUpShape<64>::NTHR, 0, st>>>(a);
-    return hipGetLastError() == hipSuccess ? 0 : -1;
-}
-
 // 256 x 256 tiles: the routed groups of tile_big, or a dense group of at
 // least kBigRows rows (then alone)
-static inline bool dense_big(const GroupRows& g, int ncols) {
-    return !g.tile_off && g.tm == 128 && g.dense_rows >= kBigRows && ncols % kBig == 0;
+// (routed groups: the caller builds tile_big only when every GEMM that takes
+// it has a 256 x 256 form for its sizes; a launcher that cannot take it fails)
+static inline bool dense_big(const GroupRows& g, bool dims_ok) {
+    return !g.tile_off && g.tm == 128 && g.dense_rows >= kBigRows && dims_ok;
 }
 
 static inline int big_grid(const GroupRows& g) {
@@ -591,11 +632,33 @@ static inline int big_grid(const GroupRows& g) {
     return (int)(a < b ? a : b);
 }
 
+int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
+    ProfScope prof_(st, "gemm_gate_up");
+    const bool dims_ok = a.I % (kBig / 2) == 0 && a.H % kTK == 0;
+    const bool dbig = dense_big(a.g, dims_ok);
+    if (a.g.tile_big || dbig) {
+        if (!dims_ok) return -1;
+        const int grid = big_grid(a.g) * (a.I / (kBig / 2));
+        if (grid > 0) {
+            k_gemm_gate_up_big<<<grid, kBigThreads, 0, st>>>(a);
+            if (hipGetLastError() != hipSuccess) return -1;
+        }
+        if (dbig) return 0;
+    }
+    const int tm_ = row_tile(a.g);
+    const int grid_ = mgroup_grid(a.g, tm_) * (a.I / (tm_ == 128 ? 128 : 64));
+    if (grid_ <= 0) return 0;
+    if (tm_ == 128) k_gemm_gate_up<128><<<grid_, GateUpShape<128>::NTHR, 0, st>>>(a);
+    else k_gemm_gate_up<64><<<grid_, GateUpShape<64>::NTHR, 0, st>>>(a);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down");
-    const bool dbig = dense_big(a.g, a.H);
+    const bool dims_ok = a.H % kBig == 0 && a.I % kTK == 0;
+    const bool dbig = dense_big(a.g, dims_ok);
     if (a.g.tile_big || dbig) {
-        if (a.H % kBig != 0 || a.I % kTK != 0) return -1;
+        if (!dims_ok) return -1;
         const int grid = big_grid(a.g) * (a.H / kBig);
         if (grid > 0) {
             k_gemm_down_big<<<grid, kBigThreads, 0, st>>>(a);
