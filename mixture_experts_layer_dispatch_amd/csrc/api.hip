@@ -864,13 +864,25 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
+        // the gate/up GEMMs take groups of at least kBigRows rows in 256 x 256
+        // tiles when groups are large on average (the down dgrad has no such form)
+        const bool big = tm == 128 && g.H % kBig == 0 && g.I % (kBig / 2) == 0;
+        int32_t* tsmall = (int32_t*)((char*)workspace + L.tile_split) + (size_t)m * 2 * (g.E + 1);
+        int32_t* tbig = tsmall + (g.E + 1);
+        if (big ? launch_tile_prefix_split(off, g.E, g.Sm, tm, toff, kBigRows, kBig, tsmall, tbig, err, st)
+                : launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st))
+            return MOE_ERR_HIP;
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
+        GroupRows grp_split = grp;
+        if (big) {
+            grp_split.tile_off = tsmall;
+            grp_split.tile_big = tbig;
+        }
         const GU gu = gu_routed(g, L, P, saved, m, false);
         if (g.recompute && m != g.n_macro - 1) {
             // recompute this macrobatch's g, u (h goes to the hw rows, which
             // the dgrad below overwrites)
-            GemmGateUpArgs r1{grp, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
+            GemmGateUpArgs r1{grp_split, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
                               (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
                               (uint16_t*)gu.g, (uint16_t*)gu.u, 0, hw};
             if (launch_gemm_gate_up(r1, st)) return MOE_ERR_HIP;
@@ -880,7 +892,7 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                              (const uint16_t*)w->w_down, g.H, g.I, (const uint16_t*)gu.g,
                              (const uint16_t*)gu.u, gu.row0, dgu, hw, part, g.P};
         if (launch_gemm_down_dgrad(b1, st)) return MOE_ERR_HIP;
-        GemmGuDgradArgs b2{grp, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
+        GemmGuDgradArgs b2{grp_split, dgu, (const uint16_t*)w->w_gate, (const uint16_t*)w->w_up, g.H, g.I,
                            top1_direct(g) ? (uint16_t*)dx : dxd, token_rows(g, sched, grow0)};
         if (launch_gemm_gu_dgrad(b2, st)) return MOE_ERR_HIP;
         // the shared expert's input gradient, then reverse-dispatch and the

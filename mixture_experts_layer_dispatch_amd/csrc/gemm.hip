@@ -111,7 +111,8 @@ __global__ __launch_bounds__(GateUpShape<TM>::NTHR, TM == 64 ? 2 : 1) void k_gem
 // i0 + 32 (w >> 1) + 0..31 in acc[.][0..1] and the matching up columns in
 // acc[.][2..3] (RowsGateUp's quarters).  Same bits as the 128-row tiles.
 __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_gate_up_big(GemmGateUpArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[SmemBig::TOTAL];
+    __shared__ __attribute__((aligned(16))) uint16_t st0[SmemBig::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[SmemBig::STAGE];
     int e, lo, hi, nt;
     if (!map_mtile_big(a.g, a.I / (kBig / 2), blockIdx.x, e, lo, hi, nt)) return;
     const int i0 = nt * (kBig / 2);
@@ -122,11 +123,11 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_gate_up_big(GemmGateUpA
         if (a.x_gather) {
             const RowsGather sa{a.x, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
             const DirectKC la(sa);
-            mainloop_big(la, lb, a.H / kTK, smem, acc);
+            mainloop_big(la, lb, a.H / kTK, st0, st1, acc);
         } else {
             const RowsDirect sa{a.x, a.H, a.xrow0 + lo, hi - lo};
             const DirectKC la(sa);
-            mainloop_big(la, lb, a.H / kTK, smem, acc);
+            mainloop_big(la, lb, a.H / kTK, st0, st1, acc);
         }
     }
     const int w = threadIdx.x >> 6, lane = lane_id();
@@ -211,7 +212,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down(GemmDownArgs a) {
 // the same rows, scaled by their router weights, and the same bits (K steps
 // ascend and each MFMA sums in a fixed order, whatever the tile shape).
 __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_down_big(GemmDownArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t smem[SmemBig::TOTAL];
+    __shared__ __attribute__((aligned(16))) uint16_t st0[SmemBig::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[SmemBig::STAGE];
     int e, lo, hi, nt;
     if (!map_mtile_big(a.g, a.H / kBig, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * kBig;
@@ -220,7 +222,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_down_big(GemmDownArgs a
         const RowsDirect sa{a.h, a.I, lo, hi - lo};
         const RowsDirect sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0, kBig};
         const DirectKC la(sa), lb(sb);
-        mainloop_big(la, lb, a.I / kTK, smem, acc);
+        mainloop_big(la, lb, a.I / kTK, st0, st1, acc);
     }
     const int w = threadIdx.x >> 6, lane = lane_id();
     const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
@@ -372,6 +374,39 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gu_dgrad(GemmGuDgradArgs a) {
         epi(0, acc);
     } else {
         mainloop_tiles<TM, G4_TN, false, true>(la, lb, 2 * a.I / kTK, ntl, G4_TN, smem, acc, epi);
+    }
+}
+
+// The groups of at least kBigRows rows in 256 x 256 tiles (mainloop_big with
+// [W_gate; W_up] as a KS operand); same bits as the 128-row tiles.
+__global__ __launch_bounds__(kBigThreads, 1) void k_gemm_gu_dgrad_big(GemmGuDgradArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t st0[SmemBig::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[SmemBig::STAGE];
+    int e, lo, hi, nt;
+    if (!map_mtile_big(a.g, a.H / kBig, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * kBig;
+    f32x4 acc[8][4];
+    {
+        const RowsDirect sa{a.dgu, 2 * a.I, lo, hi - lo};
+        const DirectKC la(sa);
+        const StepGateUp sb{a.w_gate + (int64_t)e * a.I * a.H, a.w_up + (int64_t)e * a.I * a.H, a.H, n0, a.I};
+        const DirectKS lb(a.H);
+        mainloop_big(la, lb, sb, 2 * a.I / kTK, st0, st1, acc);
+    }
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int rl = lo + wm0 + mb * 16 + (lane & 15);
+        if (rl >= hi) continue;
+        const int64_t orow = a.dest.row(rl, a.g.err);
+        if (orow < 0) continue;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int col = n0 + wn0 + nb * 16 + 4 * (lane >> 4);
+            const f32x4 v = acc[mb][nb];
+            *(uint2*)(a.dx + orow * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
+        }
     }
 }
 
@@ -678,6 +713,17 @@ int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st) {
 
 int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gu_dgrad");
+    const bool dims_ok = a.H % kBig == 0 && a.I % kTK == 0;
+    const bool dbig = dense_big(a.g, dims_ok);
+    if (a.g.tile_big || dbig) {
+        if (!dims_ok) return -1;
+        const int grid = big_grid(a.g) * (a.H / kBig);
+        if (grid > 0) {
+            k_gemm_gu_dgrad_big<<<grid, kBigThreads, 0, st>>>(a);
+            if (hipGetLastError() != hipSuccess) return -1;
+        }
+        if (dbig) return 0;
+    }
     const int ncol = a.H / G4_TN;
     MOE_LAUNCH_TM2(k_gemm_gu_dgrad, (ncol + short_k_tiles_per_block<64>() - 1) / short_k_tiles_per_block<64>(),
                    (ncol + short_k_tiles_per_block<128>() - 1) / short_k_tiles_per_block<128>());

@@ -598,10 +598,66 @@ struct DirectKC {
     }
 };
 
+// KS tile of kTK k-rows by kBig columns, unpadded 512-byte k-rows whose
+// 16-byte chunks are XOR-swizzled by k: chunk c of k-row k sits at slot
+// c ^ (2 (k & 7)).  The transpose load of a fragment reads 32 bytes (two
+// chunks c, c + 1, c even) from each of 8 consecutive k-rows per half-wave;
+// the swizzle moves the pair to 8 different 32-byte bank windows.  Chunk
+// g = q * 512 + wave * 64 + lane (k-row g / 32, slot g % 32) is copied by that
+// lane.  src.step(kt) points at column col0 of k-row kt * kTK; the step's k-rows
+// follow at stride src.ld.
+struct DirectKS {
+    static constexpr int PER = kTK * (kBig / 8) / kBigThreads;
+    int off[PER];
+    __device__ explicit DirectKS(int64_t ld) {
+        const int lane = lane_id(), w = threadIdx.x >> 6;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int g = q * kBigThreads + w * 64 + lane;
+            const int k = g >> 5, c = (g & 31) ^ ((k & 7) << 1);
+            off[q] = (int)(k * ld) + c * 8;
+        }
+    }
+    __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint16_t* tile) const {
+        const int w = threadIdx.x >> 6;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[q]),
+                                         (lds_void_t*)(tile + (q * kBigThreads + w * 64) * 8), 16, 0, 0);
+    }
+};
+
+// element offset of (k-row k, column col) in a DirectKS tile
+__device__ __forceinline__ int ks_sw_off(int k, int col) {
+    return k * kBig + ((((col >> 3) ^ ((k & 7) << 1))) << 3) + (col & 7);
+}
+
+// the B-side fragment of frag_ks from a DirectKS tile (same lanes and k order)
+__device__ __forceinline__ bf16x8 frag_ks_sw(const uint16_t* s, int rbase, int ks) {
+    const int lane = lane_id();
+    const int g = lane >> 4, j = lane & 15;
+    const int k1 = ks + 4 * g + (j >> 2), col = rbase + 4 * (j & 3);
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(s + ks_sw_off(k1, col)));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(s + ks_sw_off(k1 + 16, col)));
+    const uint4 v = make_uint4(__builtin_bit_cast(uint2, a).x, __builtin_bit_cast(uint2, a).y,
+                               __builtin_bit_cast(uint2, b).x, __builtin_bit_cast(uint2, b).y);
+    return *(const bf16x8*)&v;
+}
+
+// K-step bases of [W_gate; W_up] read with k as the memory row (k < I: W_gate
+// row k, else W_up row k - I; I a multiple of kTK), at column col0
+struct StepGateUp {
+    const uint16_t* wg;
+    const uint16_t* wu;
+    int64_t ld;
+    int col0, I;
+    __device__ const uint16_t* step(int kt) const {
+        const int k = kt * kTK;
+        return (k < I ? wg + (int64_t)k * ld : wu + (int64_t)(k - I) * ld) + col0;
+    }
+};
+
 struct SmemBig {
     static constexpr int A = Tile<kBig, false>::SIZE;     // uint16 per operand tile
-    static constexpr int STAGE = 2 * A;
-    static constexpr int TOTAL = 2 * STAGE;               // 128 KB
+    static constexpr int STAGE = 2 * A;                   // A then B; two stages: 128 KB
 };
 
 // wait for every copy this thread issued (vmcnt 0; the expcnt and lgkmcnt
@@ -610,8 +666,20 @@ __device__ __forceinline__ void wait_copies() { __builtin_amdgcn_s_waitcnt(0x007
 
 // acc[mb][nb]: output rows wm0 + 16 mb + (lane & 15), columns wn0 + 16 nb +
 // 4 (lane >> 4) + r, with wm0 = 128 (wave & 1), wn0 = 64 (wave >> 1).
-__device__ __forceinline__ void mainloop_big(const DirectKC& la, const DirectKC& lb, int nk, uint16_t* smem,
-                                             f32x4 (&acc)[8][4]) {
+// B is a DirectKC tile (LB = DirectKC), or a DirectKS tile over the k-rows
+// of src (LB = DirectKS, src.step(kt)); with a KS operand both operands use
+// the permuted K order of frag_kc_perm / frag_ks (the 128-row kernels' order,
+// so the bits are theirs).
+template <class LB, class SrcB>
+__device__ __forceinline__ void big_issue_b(const LB& lb, const SrcB& sb, int q, int kt, uint16_t* tile) {
+    if constexpr (__is_same(LB, DirectKC)) lb.issue1(q, kt, tile);
+    else lb.issue1(q, sb.step(kt), tile);
+}
+
+template <class LB, class SrcB>
+__device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, const SrcB& sb, int nk,
+                                             uint16_t* st0, uint16_t* st1, f32x4 (&acc)[8][4]) {
+    constexpr bool BKS = __is_same(LB, DirectKS);
     const int w = threadIdx.x >> 6;
     const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
 #pragma unroll
@@ -619,13 +687,20 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const DirectKC&
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (nk <= 0) return;
-    la.issue(0, smem);
-    lb.issue(0, smem + SmemBig::A);
+    la.issue(0, st0);
+#pragma unroll
+    for (int q = 0; q < LB::PER; ++q) big_issue_b(lb, sb, q, 0, st0 + SmemBig::A);
     wait_copies();
     __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-        const uint16_t* cur = smem + (kt & 1) * SmemBig::STAGE;
-        uint16_t* nxt = smem + ((kt + 1) & 1) * SmemBig::STAGE;
+    auto fa_of = [&](const uint16_t* sB, int nb, int ks) {
+        if constexpr (BKS) return frag_ks_sw(sB, wn0 + nb * 16, ks);
+        else return frag_kc(sB, 0, wn0 + nb * 16, ks);
+    };
+    // one K step on cur while the next step's copies go to nxt; the two
+    // stages are separate LDS arrays, so the compiler can tell the copies
+    // into one from the reads of the other (it waits for every copy in flight
+    // before an LDS read it cannot tell apart from them)
+    auto step = [&](const uint16_t* cur, uint16_t* nxt, int kt) {
         const bool more = kt + 1 < nk;
         const uint16_t* sA = cur;
         const uint16_t* sB = cur + SmemBig::A;
@@ -633,18 +708,21 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const DirectKC&
         for (int ks = 0; ks < kTK; ks += 32) {
             bf16x8 fb[8];
 #pragma unroll
-            for (int mb = 0; mb < 8; ++mb) fb[mb] = frag_kc(sA, 0, wm0 + mb * 16, ks);
-            bf16x8 fa0 = frag_kc(sB, 0, wn0, ks), fa1;
+            for (int mb = 0; mb < 8; ++mb) {
+                if constexpr (BKS) fb[mb] = frag_kc_perm(sA, 0, wm0 + mb * 16, ks);
+                else fb[mb] = frag_kc(sA, 0, wm0 + mb * 16, ks);
+            }
+            bf16x8 fa0 = fa_of(sB, 0, ks), fa1;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) {
                 if (nb + 1 < 4) {
-                    if (nb & 1) fa0 = frag_kc(sB, 0, wn0 + (nb + 1) * 16, ks);
-                    else fa1 = frag_kc(sB, 0, wn0 + (nb + 1) * 16, ks);
+                    if (nb & 1) fa0 = fa_of(sB, nb + 1, ks);
+                    else fa1 = fa_of(sB, nb + 1, ks);
                 }
                 const int li = (ks / 32) * 4 + nb;       // 0..7: the next step's eight copies
                 if (more) {
                     if (li < DirectKC::PER) la.issue1(li, kt + 1, nxt);
-                    else lb.issue1(li - DirectKC::PER, kt + 1, nxt + SmemBig::A);
+                    else big_issue_b(lb, sb, li - DirectKC::PER, kt + 1, nxt + SmemBig::A);
                 }
 #pragma unroll
                 for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma_16x16x32((nb & 1) ? fa1 : fa0, fb[mb], acc[mb][nb]);
@@ -652,7 +730,18 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const DirectKC&
         }
         wait_copies();
         __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(st0, st1, kt);
+        if (kt + 1 < nk) step(st1, st0, kt + 1);
     }
+}
+
+// both operands DirectKC
+struct NoSrc {};
+__device__ __forceinline__ void mainloop_big(const DirectKC& la, const DirectKC& lb, int nk, uint16_t* st0,
+                                             uint16_t* st1, f32x4 (&acc)[8][4]) {
+    mainloop_big(la, lb, NoSrc{}, nk, st0, st1, acc);
 }
 
 // accumulator (mb, nb, r) -> tile coordinates
