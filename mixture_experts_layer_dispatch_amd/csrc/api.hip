@@ -31,7 +31,7 @@ struct Geom {
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct Layout {
-    size_t err, hist, base, tile_off, tile_split, deep, ring, ring_half, sh, wacc, total;
+    size_t err, hist, base, tile_off, tile_split, deep, deep_big, zero, ring, ring_half, sh, wacc, total;
     // offsets inside one ring half (bytes)
     size_t f_h, f_o;                  // forward
     size_t f_hs;                      // MXFP8 forward: h scales after the codes (codes at f_h)
@@ -110,6 +110,8 @@ Layout make_layout(const Geom& g) {
     // of the others (256-row tiles), for the down GEMM's two tile forms
     L.tile_split = take((size_t)g.n_macro * 2 * (g.E + 1) * 4);
     L.deep = take((size_t)(g.E + 1) * 4);        // deep weight-gradient groups of one macrobatch
+    L.deep_big = take((size_t)(g.E + 1) * 4);    // ... and those in 256 x 256 tiles
+    L.zero = take(1024);                         // zeros the 256 x 256 weight gradients read past a group
     const size_t Sm = (size_t)g.Sm, H = g.H, I = g.I;
     // the forward's ring rows: h and the weighted o of the macrobatch (the
     // dispatched x rows are gathered by the gate/up GEMM's loads, never stored)
@@ -233,6 +235,7 @@ bool device_ok() {
 }
 
 __global__ void k_clear_word(int32_t* p) { *p = 0; }
+__global__ void k_clear_words(int32_t* p) { p[threadIdx.x] = 0; }
 
 moe_status common_checks(const moe_config* cfg, Geom& g, Layout& L, void* ws, size_t ws_bytes) {
     moe_status s = make_geom(cfg, g);
@@ -852,6 +855,14 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
     const uint16_t* xb = (const uint16_t*)x;
     const uint16_t* dyb = (const uint16_t*)dy;
     const int tm = gemm_row_tile(g.Sm, g.E);            // row tile of the M-grouped GEMMs
+    // weight gradients of groups of at least wgrad_big_rows() rows in 256 x 256
+    // tiles; rows past a group's end are read from a zero row
+    const bool wbig = g.H % kBig == 0 && g.I % kBig == 0;
+    const uint16_t* zero = (const uint16_t*)((char*)workspace + L.zero);
+    if (wbig) {
+        k_clear_words<<<1, 256, 0, st>>>((int32_t*)((char*)workspace + L.zero));
+        if (hipGetLastError() != hipSuccess) return MOE_ERR_HIP;
+    }
     for (int m = g.n_macro - 1; m >= 0; --m) {
         // weight-gradient accumulation across the reverse walk
         int mode = 0;
@@ -928,24 +939,32 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                                t0 + g.M, g.k, g.E, grow0, g.Sm, dw, d_logits, err, st))
             return MOE_ERR_HIP;
         int32_t* deep = (int32_t*)((char*)workspace + L.deep);
-        if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows(), deep, st)) return MOE_ERR_HIP;
+        int32_t* deep_big = (int32_t*)((char*)workspace + L.deep_big);
+        if (wbig ? launch_deep_list_split(off, g.E, g.Sm, wgrad_deep_rows(), deep, wgrad_big_rows(), deep_big, st)
+                 : launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows(), deep, st))
+            return MOE_ERR_HIP;
         GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err, deep, wgrad_deep_rows()};
+        if (wbig) {
+            kgrp.deep_big = deep_big;
+            kgrp.big_thr = wgrad_big_rows();
+            dense.big_thr = wgrad_big_rows();
+        }
         const int32_t* cnts = g.n_macro > 1 ? sched->counts : nullptr;   // per-expert modes
         const int32_t* sl = g.n_macro > 1 ? P.acc_slot() : nullptr;
         WgradDownArgs b3{kgrp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, hw, g.H, g.I,
-                         {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode, cnts, m, g.n_macro, g.E, sl}};
+                         {(uint16_t*)gr->d_w_down, P.wacc(L.wacc_d), mode, cnts, m, g.n_macro, g.E, sl}, zero};
         if (launch_wgrad_down(b3, st)) return MOE_ERR_HIP;
         WgradGateUpArgs b4{kgrp, dgu, xb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, g.H, g.I,
                            {(uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), mode, cnts, m, g.n_macro, g.E, sl},
-                           {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode, cnts, m, g.n_macro, g.E, sl}};
+                           {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode, cnts, m, g.n_macro, g.E, sl}, zero};
         if (launch_wgrad_gate_up(b4, st)) return MOE_ERR_HIP;
         if (g.shared) {
             WgradDownArgs c3{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, shw, g.H, g.I,
-                             {(uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), mode}};
+                             {(uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), mode}, zero};
             if (launch_wgrad_down(c3, st)) return MOE_ERR_HIP;
             WgradGateUpArgs c4{dense, sdgu, xb, 0, t0, nullptr, 0, g.k, g.S, g.H, g.I,
                                {(uint16_t*)gr->d_s_gate, P.wacc(L.wacc_sg), mode},
-                               {(uint16_t*)gr->d_s_up, P.wacc(L.wacc_su), mode}};
+                               {(uint16_t*)gr->d_s_up, P.wacc(L.wacc_su), mode}, zero};
             if (launch_wgrad_gate_up(c4, st)) return MOE_ERR_HIP;
         }
     }

@@ -248,15 +248,7 @@ __global__ __launch_bounds__(1024) void k_tile_prefix(const int32_t* __restrict_
 // Experts whose group has more than thr rows, in ascending order:
 // list[0] = their count, list[1..] = their ids.  Bad offsets count as empty
 // (the tile prefix reports them).
-__global__ __launch_bounds__(1024) void k_deep_list(const int32_t* __restrict__ offsets, int E,
-                                                    int rows, int thr, int32_t* __restrict__ list) {
-    __shared__ int32_t wsum[16];
-    const int e = threadIdx.x;
-    int f = 0;
-    if (e < E) {
-        const int a = offsets[e], b = offsets[e + 1];
-        f = (a >= 0 && b >= a && b <= rows && b - a > thr) ? 1 : 0;
-    }
+__device__ __forceinline__ void flag_list(int f, int e, int32_t* wsum, int32_t* list) {
     const int lane = lane_id(), wv = threadIdx.x >> 6;
     const unsigned long long m = __ballot(f);
     const int incl = __popcll(m & ((2ull << lane) - 1ull));
@@ -270,6 +262,24 @@ __global__ __launch_bounds__(1024) void k_deep_list(const int32_t* __restrict__ 
         for (int q = 0; q < 16; ++q) tot += wsum[q];
         list[0] = tot;
     }
+    __syncthreads();                       // wsum is reused by the next list
+}
+
+// With a second list (big), the groups of at least big_thr rows go there
+// instead of to list.
+__global__ __launch_bounds__(1024) void k_deep_list(const int32_t* __restrict__ offsets, int E,
+                                                    int rows, int thr, int32_t* __restrict__ list,
+                                                    int big_thr, int32_t* __restrict__ big) {
+    __shared__ int32_t wsum[16];
+    const int e = threadIdx.x;
+    int n = -1;
+    if (e < E) {
+        const int a = offsets[e], b = offsets[e + 1];
+        if (a >= 0 && b >= a && b <= rows) n = b - a;
+    }
+    const bool is_big = big && n >= big_thr;
+    flag_list(n > thr && !is_big ? 1 : 0, e, wsum, list);
+    if (big) flag_list(is_big ? 1 : 0, e, wsum, big);
 }
 
 // ============================================================== launchers
@@ -313,10 +323,18 @@ int launch_tile_prefix_split(const int32_t* offsets, int E, int rows, int TM, in
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
+int launch_deep_list_split(const int32_t* offsets, int E, int rows, int thr, int32_t* list, int big_thr,
+                           int32_t* big, hipStream_t st) {
+    ProfScope prof_(st, "deep_list");
+    if (E > 1024 || !big || big_thr <= thr) return -1;
+    k_deep_list<<<1, 1024, 0, st>>>(offsets, E, rows, thr, list, big_thr, big);
+    return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+
 int launch_deep_list(const int32_t* offsets, int E, int rows, int thr, int32_t* list, hipStream_t st) {
     ProfScope prof_(st, "deep_list");
     if (E > 1024) return -1;
-    k_deep_list<<<1, 1024, 0, st>>>(offsets, E, rows, thr, list);
+    k_deep_list<<<1, 1024, 0, st>>>(offsets, E, rows, thr, list, 0, nullptr);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

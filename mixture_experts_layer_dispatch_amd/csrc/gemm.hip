@@ -535,10 +535,14 @@ __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
 // tile) so that a hot expert's tiles spread over the whole chip.
 constexpr int D_TM = 128, D_TN = 128, D_GRID = 512;
 
+__device__ __forceinline__ bool dense_wgrad_big(const GroupRows& g) {
+    return g.big_thr > 0 && g.dense_rows >= g.big_thr;
+}
+
 __device__ __forceinline__ int deep_count(const GroupRows& g) {
     if (g.deep_thr <= 0) return 0;
     if (g.offsets) return g.deep[0];
-    return g.dense_rows > g.deep_thr ? 1 : 0;
+    return g.dense_rows > g.deep_thr && !dense_wgrad_big(g) ? 1 : 0;
 }
 
 // group d of the deep list -> (expert, first row, rows)
@@ -617,6 +621,107 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_gate_up_deep(WgradGateUpArgs a
         WgradOut o = up ? a.out_up : a.out_gate;
         if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) >= 0)
             deep_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
+    }
+}
+
+// ---------------------------------------------------------------- large groups
+// Groups of at least big_thr rows (the GEMM is then MFMA work: each output
+// element sums hundreds of products): 256 x 256 output tiles (eight waves,
+// operands copied straight into LDS as swizzled K-major tiles), a persistent
+// grid over the items (big group, tile); consecutive items of a round go to
+// the blocks of one XCD, so the tiles that share an operand strip share its L2.
+constexpr int B_GRID = 256;
+
+__device__ __forceinline__ int big_count(const GroupRows& g) {
+    if (g.big_thr <= 0) return 0;
+    if (g.offsets) return g.deep_big[0];
+    return dense_wgrad_big(g) ? 1 : 0;
+}
+
+__device__ __forceinline__ void big_group(const GroupRows& g, int d, int& e, int& lo, int& n) {
+    if (!g.offsets) {
+        e = 0;
+        lo = 0;
+        n = g.dense_rows;
+        return;
+    }
+    e = g.deep_big[1 + d];
+    lo = g.offsets[e];
+    n = g.offsets[e + 1] - lo;          // validated when the list was built
+}
+
+__device__ __forceinline__ void big_wgrad_store(const WgradOut& out, int64_t ebase, int64_t ld, int r0, int n0,
+                                                const f32x4 (&acc)[8][4]) {
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            wgrad_store(out, ebase + (int64_t)(r0 + wm0 + mb * 16 + (lane & 15)) * ld + n0 + wn0 + nb * 16 +
+                                 4 * (lane >> 4),
+                        acc[mb][nb]);
+}
+
+__device__ __forceinline__ int big_item(int r) {
+    return r * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+}
+
+__global__ __launch_bounds__(kBigThreads, 1) void k_wgrad_down_big(WgradDownArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t st0[SmemBig::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[SmemBig::STAGE];
+    const int nNt = a.I / kBig, per = (a.H / kBig) * nNt;
+    const int total = big_count(a.g) * per;
+    for (int r = 0;; ++r) {
+        const int item = big_item(r);
+        if (item >= total) break;
+        const int d = item / per, tile = item - d * per;
+        int e, lo, n;
+        big_group(a.g, d, e, lo, n);
+        const int m0 = (tile / nNt) * kBig, n0 = (tile % nNt) * kBig;
+        const int nk = (n + kTK - 1) / kTK;
+        DirectKSRows<KRowsGroup> lb(KRowsGroup{a.hw, a.I, lo, n, n0}, a.zero);
+        f32x4 acc[8][4];
+        if (a.dy_gather) {
+            DirectKSRows<KRowsGroupGather> la(
+                KRowsGroupGather{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err}, a.zero);
+            mainloop_big_kk(la, lb, nk, st0, st1, acc);
+        } else {
+            DirectKSRows<KRowsGroup> la(KRowsGroup{a.dy, a.H, a.dyrow0 + lo, n, m0}, a.zero);
+            mainloop_big_kk(la, lb, nk, st0, st1, acc);
+        }
+        WgradOut o = a.out;
+        if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) >= 0) big_wgrad_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
+    }
+}
+
+__global__ __launch_bounds__(kBigThreads, 1) void k_wgrad_gate_up_big(WgradGateUpArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t st0[SmemBig::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[SmemBig::STAGE];
+    const int nNt = a.H / kBig, per = (2 * a.I / kBig) * nNt;
+    const int total = big_count(a.g) * per;
+    for (int r = 0;; ++r) {
+        const int item = big_item(r);
+        if (item >= total) break;
+        const int d = item / per, tile = item - d * per;
+        int e, lo, n;
+        big_group(a.g, d, e, lo, n);
+        const int m0 = (tile / nNt) * kBig, n0 = (tile % nNt) * kBig;
+        const int nk = (n + kTK - 1) / kTK;
+        const bool up = m0 >= a.I;
+        DirectKSRows<KRowsGroup> la(KRowsGroup{a.dgu, 2 * a.I, lo, n, m0}, a.zero);
+        f32x4 acc[8][4];
+        if (a.x_gather) {
+            DirectKSRows<KRowsGroupGather> lb(
+                KRowsGroupGather{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, n0, a.k, a.S, a.g.err}, a.zero);
+            mainloop_big_kk(la, lb, nk, st0, st1, acc);
+        } else {
+            DirectKSRows<KRowsGroup> lb(KRowsGroup{a.x, a.H, a.xrow0 + lo, n, n0}, a.zero);
+            mainloop_big_kk(la, lb, nk, st0, st1, acc);
+        }
+        WgradOut o = up ? a.out_up : a.out_gate;
+        if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) >= 0)
+            big_wgrad_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
     }
 }
 
@@ -731,6 +836,12 @@ int launch_gemm_gu_dgrad(const GemmGuDgradArgs& a, hipStream_t st) {
 
 int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_down");
+    if (a.g.big_thr > 0) {
+        if (a.H % kBig != 0 || a.I % kBig != 0 || !a.zero || a.g.deep_thr <= 0 || a.g.big_thr <= a.g.deep_thr)
+            return -1;
+        k_wgrad_down_big<<<B_GRID, kBigThreads, 0, st>>>(a);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     if (a.g.deep_thr > 0) {
         k_wgrad_down_deep<<<D_GRID, 256, 0, st>>>(a);
         if (hipGetLastError() != hipSuccess) return -1;
@@ -742,6 +853,12 @@ int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
 
 int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "wgrad_gate_up");
+    if (a.g.big_thr > 0) {
+        if (a.H % kBig != 0 || a.I % kBig != 0 || !a.zero || a.g.deep_thr <= 0 || a.g.big_thr <= a.g.deep_thr)
+            return -1;
+        k_wgrad_gate_up_big<<<B_GRID, kBigThreads, 0, st>>>(a);
+        if (hipGetLastError() != hipSuccess) return -1;
+    }
     if (a.g.deep_thr > 0) {
         k_wgrad_gate_up_deep<<<D_GRID, 256, 0, st>>>(a);
         if (hipGetLastError() != hipSuccess) return -1;
@@ -755,6 +872,8 @@ int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
 // are MFMA work rather than weight streaming)
 int gemm_row_tile(int rows, int E) { return (int64_t)rows >= 192LL * E ? 128 : 64; }
 int wgrad_deep_rows() { return kTK; }
+// bf16 weight gradients: groups of at least this many rows take the 256 x 256 tiles
+int wgrad_big_rows() { return 512; }
 int dgrad_col_tiles(int I) { return I / G3_TN; }
 
 }  // namespace moe

@@ -737,6 +737,117 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
     }
 }
 
+// ---------------------------------------------------------------- 256 x 256, K-grouped
+// KS tile of kTK k-rows by kBig columns whose k-rows come one by one from a
+// K-row source (src.pre / src.at: the k-th row of a group at column col0, or
+// null past the group's end or for a bad slot).  Missing rows are copied from
+// a zero row, so they add exact zeros, as the zero-filled tiles of the
+// 128 x 128 kernels do.  src.pre(k) (a gathered row's slot) is fetched two K
+// steps before the copy that needs it: prime(kt) fills pn for step kt,
+// ahead(kt) fills pn2, advance() moves pn2 to pn.
+template <class Src>
+struct DirectKSRows {
+    static constexpr int PER = kTK * (kBig / 8) / kBigThreads;
+    // copy q of a lane covers k-row k0 + 16 q; its chunk slot (lane & 31) and
+    // the k-row's swizzle ((k0 & 7), the same for every q) fix the column
+    Src src;
+    const uint16_t* zero;             // kBig zero elements
+    int k0, co, pn[PER], pn2[PER];
+    __device__ DirectKSRows(const Src& s, const uint16_t* z) : src(s), zero(z) {
+        const int lane = lane_id(), w = threadIdx.x >> 6;
+        k0 = (w * 64 + lane) >> 5;
+        co = ((lane & 31) ^ ((k0 & 7) << 1)) * 8;
+    }
+    __device__ __forceinline__ void prime(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) pn[q] = src.pre(kt * kTK + k0 + 16 * q);
+    }
+    __device__ __forceinline__ void ahead(int kt) {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) pn2[q] = src.pre(kt * kTK + k0 + 16 * q);
+    }
+    __device__ __forceinline__ void advance() {
+#pragma unroll
+        for (int q = 0; q < PER; ++q) pn[q] = pn2[q];
+    }
+    __device__ __forceinline__ void issue1(int q, int kt, uint16_t* tile) const {
+        const int w = threadIdx.x >> 6;
+        const uint16_t* r = src.at(kt * kTK + k0 + 16 * q, pn[q]);
+        const uint16_t* p = global_select(r == nullptr, r, zero) + co;
+        __builtin_amdgcn_global_load_lds((glb_void_t*)p, (lds_void_t*)(tile + (q * kBigThreads + w * 64) * 8),
+                                         16, 0, 0);
+    }
+};
+
+// C[256 x 256] = sum over the group's rows of A[r, m0 + .] (x) B[r, n0 + .],
+// both operands DirectKSRows tiles read with the transpose load (the K order
+// and the bits of the 128 x 128 kernels).  acc as in mainloop_big.
+template <class LA, class LB>
+__device__ __forceinline__ void mainloop_big_kk(LA& la, LB& lb, int nk, uint16_t* st0, uint16_t* st1,
+                                                f32x4 (&acc)[8][4]) {
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nk <= 0) return;
+    la.prime(0);
+    lb.prime(0);
+#pragma unroll
+    for (int q = 0; q < LA::PER; ++q) la.issue1(q, 0, st0);
+#pragma unroll
+    for (int q = 0; q < LB::PER; ++q) lb.issue1(q, 0, st0 + SmemBig::A);
+    if (nk > 1) {
+        la.prime(1);
+        lb.prime(1);
+    }
+    wait_copies();
+    __syncthreads();
+    auto step = [&](const uint16_t* cur, uint16_t* nxt, int kt) {
+        const bool more = kt + 1 < nk, ahead = kt + 2 < nk;
+        if (ahead) {
+            la.ahead(kt + 2);
+            lb.ahead(kt + 2);
+        }
+        const uint16_t* sA = cur;
+        const uint16_t* sB = cur + SmemBig::A;
+        // the row blocks outermost: four B fragments and two A fragments live
+        // at a time (each accumulator still sees its MFMAs in K order)
+#pragma unroll
+        for (int ks = 0; ks < kTK; ks += 32) {
+            bf16x8 fa[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) fa[nb] = frag_ks_sw(sB, wn0 + nb * 16, ks);
+            bf16x8 fb0 = frag_ks_sw(sA, wm0, ks), fb1;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+                if (mb + 1 < 8) {
+                    if (mb & 1) fb0 = frag_ks_sw(sA, wm0 + (mb + 1) * 16, ks);
+                    else fb1 = frag_ks_sw(sA, wm0 + (mb + 1) * 16, ks);
+                }
+                const int li = (ks / 32) * 8 + mb;          // copies on the even slots
+                if (more && !(li & 1)) {
+                    if (li / 2 < LA::PER) la.issue1(li / 2, kt + 1, nxt);
+                    else lb.issue1(li / 2 - LA::PER, kt + 1, nxt + SmemBig::A);
+                }
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], (mb & 1) ? fb1 : fb0, acc[mb][nb]);
+            }
+        }
+        if (ahead) {
+            la.advance();
+            lb.advance();
+        }
+        wait_copies();
+        __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(st0, st1, kt);
+        if (kt + 1 < nk) step(st1, st0, kt + 1);
+    }
+}
+
 // both operands DirectKC
 struct NoSrc {};
 __device__ __forceinline__ void mainloop_big(const DirectKC& la, const DirectKC& lb, int nk, uint16_t* st0,

@@ -36,6 +36,11 @@ struct GroupRows {
     // (GEMMs with a 256 x 256 tile form; null: none).  tile_off then counts
     // only the other groups.
     const int32_t* tile_big;
+    // weight gradients: groups of at least big_thr rows (big_thr > 0) go to
+    // the 256 x 256 kernels instead, deep_big = [count, expert ids...] (a
+    // dense group when dense_rows >= big_thr); deep then lists the others
+    const int32_t* deep_big;
+    int big_thr;
 };
 
 struct GemmGateUpArgs {
@@ -181,6 +186,7 @@ struct WgradDownArgs {
     const uint16_t* hw;
     int H, I;
     WgradOut out;
+    const uint16_t* zero;     // kBig zero bf16 values (groups in 256 x 256 tiles)
 };
 
 struct WgradGateUpArgs {
@@ -192,6 +198,7 @@ struct WgradGateUpArgs {
     int grow0, k, S;
     int H, I;
     WgradOut out_gate, out_up;
+    const uint16_t* zero;     // kBig zero bf16 values (groups in 256 x 256 tiles)
 };
 
 struct GemmGateUpMXArgs {
@@ -326,6 +333,9 @@ int launch_tile_prefix_split(const int32_t* offsets, int E, int rows, int TM, in
                              int big_rows, int big_tm, int32_t* small, int32_t* big, int32_t* err,
                              hipStream_t st);
 int launch_deep_list(const int32_t* offsets, int E, int rows, int thr, int32_t* list, hipStream_t st);
+// the same, with the groups of at least big_thr rows in a list of their own
+int launch_deep_list_split(const int32_t* offsets, int E, int rows, int thr, int32_t* list, int big_thr,
+                           int32_t* big, hipStream_t st);
 
 // mx.hip
 int launch_mx_quant_rows(const void* x, int64_t rows, int K, void* codes, void* scales, hipStream_t st,
@@ -361,6 +371,7 @@ int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st);
 int gemm_row_tile(int rows, int E);   // M-grouped row tile for a macrobatch of rows over E groups
 int dgrad_col_tiles(int I);
 int wgrad_deep_rows();        // bf16 weight gradients: groups above this go to the deep kernels
+int wgrad_big_rows();         // ... and groups of at least this many rows to the 256 x 256 kernels
 int wgrad_deep_rows_mx();     // MXFP8 weight gradients: the same, in rows
 
 }  // namespace moe

@@ -59,6 +59,15 @@ SMALL = {
     # 128-row tiles, top-1 (rows written straight to y)
     "big_zipf_top1": si.custom_shape("big_zipf_top1", T=4096, H=256, I=128, E=16, k=1, seed=37,
                                      zipf=True),
+    # groups of ~500 rows over two macrobatches: an expert's weight gradient
+    # moves between the 256 x 256 kernels (>= 512 rows) and the 128 x 128
+    # deep kernels from one macrobatch to the next, through its fp32 sums
+    "big_wgrad": si.custom_shape("big_wgrad", T=2048, H=256, I=256, E=4, k=2, seed=38,
+                                 macrobatch=1024, minibatch=512),
+    # Zipf-skewed groups with a dense shared expert of 768 rows: every weight
+    # gradient form in one macrobatch (256 x 256, deep 128 x 128, slabs)
+    "big_wgrad_zipf": si.custom_shape("big_wgrad_zipf", T=1536, H=256, I=256, E=6, k=3, seed=39,
+                                      n_shared=1, macrobatch=768, minibatch=256, zipf=True),
 }
 
 
