@@ -875,9 +875,9 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)((char*)workspace + L.tile_off) + (size_t)m * (g.E + 1);
-        // the gate/up GEMMs take groups of at least kBigRows rows in 256 x 256
-        // tiles when groups are large on average (the down dgrad has no such form)
-        const bool big = tm == 128 && g.H % kBig == 0 && g.I % (kBig / 2) == 0;
+        // the M-grouped GEMMs take groups of at least kBigRows rows in 256 x 256
+        // tiles when groups are large on average
+        const bool big = tm == 128 && g.H % kBig == 0 && g.I % kBig == 0;
         int32_t* tsmall = (int32_t*)((char*)workspace + L.tile_split) + (size_t)m * 2 * (g.E + 1);
         int32_t* tbig = tsmall + (g.E + 1);
         if (big ? launch_tile_prefix_split(off, g.E, g.Sm, tm, toff, kBigRows, kBig, tsmall, tbig, err, st)
@@ -899,7 +899,11 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
             if (launch_gemm_gate_up(r1, st)) return MOE_ERR_HIP;
         }
         // reverse-combine (dy gathered on load) + down dgrad + SwiGLU backward + dw partials
-        GemmDownDgradArgs b1{grp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, sched->topk_w,
+        // the down dgrad has few column tiles (I / 256): its 256 x 256 form
+        // needs a macrobatch of at least ~two rounds of such tiles over the chip
+        // (the expert-parallel share's 320 tiles ran 0.33 -> 0.37 ms in it)
+        const bool big_dd = big && (int64_t)(g.Sm / kBig) * (g.I / kBig) >= kBigDgradTiles;
+        GemmDownDgradArgs b1{big_dd ? grp_split : grp, dyb, 1, 0, sched->slot_of_row, grow0, g.k, g.S, sched->topk_w,
                              (const uint16_t*)w->w_down, g.H, g.I, (const uint16_t*)gu.g,
                              (const uint16_t*)gu.u, gu.row0, dgu, hw, part, g.P};
         if (launch_gemm_down_dgrad(b1, st)) return MOE_ERR_HIP;

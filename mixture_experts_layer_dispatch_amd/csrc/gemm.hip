@@ -333,6 +333,91 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad(GemmDownDgradArgs a)
     }
 }
 
+// The groups of at least kBigRows rows in 256 x 256 tiles (two of the
+// 128-column tiles above; mainloop_big with W_down as a KS operand).  The
+// epilogue is the one above, per 128-column tile: each wave's 64 columns are
+// one half of one such tile, so the dw partials (lane sums, the two shuffles,
+// then half 0 + half 1) and every other output keep their bits.
+__global__ __launch_bounds__(kBigThreads, 1) void k_gemm_down_dgrad_big(GemmDownDgradArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t st0[SmemBig::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[SmemBig::STAGE];
+    __shared__ float red[2][2][kBig];                     // [128-column tile][half][row]
+    int e, lo, hi, nt;
+    if (!map_mtile_big(a.g, a.I / kBig, blockIdx.x, e, lo, hi, nt)) return;
+    const int n0 = nt * kBig;
+    f32x4 acc[8][4];
+    {
+        const StepRows sb{a.w_down + (int64_t)e * a.H * a.I, a.I, n0};
+        const DirectKS lb(a.I);
+        if (a.dy_gather) {
+            const RowsGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S, a.g.err};
+            const DirectKC la(sa);
+            mainloop_big(la, lb, sb, a.H / kTK, st0, st1, acc);
+        } else {
+            const RowsDirect sa{a.dy, a.H, a.dyrow0 + lo, hi - lo};
+            const DirectKC la(sa);
+            mainloop_big(la, lb, sb, a.H / kTK, st0, st1, acc);
+        }
+    }
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wq = w >> 1;           // columns n0 + 64 wq: tile wq / 2, half wq % 2
+    float dot[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) dot[mb] = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int rl = lo + wm0 + mb * 16 + (lane & 15);
+        const bool ok = rl < hi;
+        float wr = 1.0f;
+        if (ok && a.topk_w) {
+            const int s = a.slot_of_row[a.grow0 + rl];
+            wr = (unsigned)s < (unsigned)a.S ? a.topk_w[s] : 0.f;
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            if (!ok) continue;
+            const int i = n0 + 64 * wq + nb * 16 + 4 * (lane >> 4);
+            const int64_t srow = (int64_t)(a.save_row0 + rl) * a.I + i;
+            const uint2 gb = *(const uint2*)(a.g_saved + srow);
+            const uint2 ub = *(const uint2*)(a.u_saved + srow);
+            const float gq[4] = {lo_bf(gb.x), hi_bf(gb.x), lo_bf(gb.y), hi_bf(gb.y)};
+            const float uq[4] = {lo_bf(ub.x), hi_bf(ub.x), lo_bf(ub.y), hi_bf(ub.y)};
+            float dg[4], du[4], hw[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float av = acc[mb][nb][r];
+                const float h = bf2f(f2bf(swiglu_h(gq[r], uq[r])));
+                dot[mb] += av * h;
+                const float dh = wr * av;
+                const float s = sigmoidf_(gq[r]);
+                du[r] = dh * (gq[r] * s);
+                dg[r] = dh * uq[r] * s * (1.0f + gq[r] * (1.0f - s));
+                hw[r] = wr * h;
+            }
+            const int64_t drow = (int64_t)rl * (2 * a.I);
+            *(uint2*)(a.dgu + drow + i) = pack4(dg[0], dg[1], dg[2], dg[3]);
+            *(uint2*)(a.dgu + drow + a.I + i) = pack4(du[0], du[1], du[2], du[3]);
+            *(uint2*)(a.hw + (int64_t)rl * a.I + i) = pack4(hw[0], hw[1], hw[2], hw[3]);
+        }
+    }
+    if (!a.dw_part) return;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        dot[mb] += __shfl_xor(dot[mb], 16);
+        dot[mb] += __shfl_xor(dot[mb], 32);
+    }
+    if (lane < 16) {
+#pragma unroll
+        for (int mb = 0; mb < 8; ++mb) red[wq >> 1][wq & 1][wm0 + 16 * mb + lane] = dot[mb];
+    }
+    __syncthreads();
+    {
+        const int t = threadIdx.x >> 8, m = threadIdx.x & 255;        // 512 threads: 2 tiles x 256 rows
+        const int rl = lo + m;
+        if (rl < hi) a.dw_part[(int64_t)rl * a.P + 2 * nt + t] = red[t][0][m] + red[t][1][m];
+    }
+}
+
 // ================================================================ backward: gate/up dgrad
 // dX = dg W_gate + du W_up: A = [dg | du] rows (K = 2I), B = [W_gate; W_up]
 // read with k as the memory row.  Tile TM rows x 128 columns of H; with
@@ -813,6 +898,17 @@ int launch_gemm_down(const GemmDownArgs& a, hipStream_t st) {
 
 int launch_gemm_down_dgrad(const GemmDownDgradArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_down_dgrad");
+    const bool dims_ok = a.I % kBig == 0 && a.H % kTK == 0;
+    const bool dbig = dense_big(a.g, dims_ok);
+    if (a.g.tile_big || dbig) {
+        if (!dims_ok || a.P != a.I / G3_TN) return -1;
+        const int grid = big_grid(a.g) * (a.I / kBig);
+        if (grid > 0) {
+            k_gemm_down_dgrad_big<<<grid, kBigThreads, 0, st>>>(a);
+            if (hipGetLastError() != hipSuccess) return -1;
+        }
+        if (dbig) return 0;
+    }
     MOE_LAUNCH_TM(k_gemm_down_dgrad, a.I / G3_TN);
 }
 

@@ -642,6 +642,14 @@ __device__ __forceinline__ bf16x8 frag_ks_sw(const uint16_t* s, int rbase, int k
     return *(const bf16x8*)&v;
 }
 
+// K-step bases of a matrix read with k as the memory row, at column col0
+struct StepRows {
+    const uint16_t* base;
+    int64_t ld;
+    int col0;
+    __device__ const uint16_t* step(int kt) const { return base + (int64_t)kt * kTK * ld + col0; }
+};
+
 // K-step bases of [W_gate; W_up] read with k as the memory row (k < I: W_gate
 // row k, else W_up row k - I; I a multiple of kTK), at column col0
 struct StepGateUp {

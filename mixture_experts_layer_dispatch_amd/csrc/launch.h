@@ -18,6 +18,7 @@ constexpr int kBlockSlots = 512;   // slots per schedule block
 // kBigRows rows, in the GEMMs that have that form
 constexpr int kBig = 256;
 constexpr int kBigRows = 256;
+constexpr int kBigDgradTiles = 512;   // down dgrad: least macrobatch rows / 256 x I / 256 for that form
 
 struct GroupRows {
     const int32_t* offsets;   // [E+1] macrobatch-local row offsets

@@ -320,3 +320,36 @@ def test_forward_backward_ep_share_full_size_sampled():
         assert_close(f"dW_gate[{e}]", f32(case.grads["d_w_gate"][e]), rb["dWg"][e])
         assert_close(f"dW_up[{e}]", f32(case.grads["d_w_up"][e]), rb["dWu"][e])
         assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])
+
+
+def test_forward_backward_many_big_tiles_sampled():
+    """A macrobatch of 131 072 routed rows over eight experts (I = 512): enough
+    256 x 256 tiles of the down dgrad (512 row tiles x 2 column tiles) for its
+    256 x 256 form, with router weights, gathered dy and the dw partials of its
+    two 128-column halves per tile, checked on sampled tokens and experts."""
+    shape = si.custom_shape("many_big_tiles", T=32768, H=256, I=512, E=8, k=4, seed=40)
+    case = Case(shape)
+    case.schedule()
+    idx, w, sch = _check_schedule(case)
+    case.forward()
+    case.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(case.ws) == 0
+    rng = np.random.default_rng(9)
+    tokens = np.sort(rng.choice(shape.T, size=24, replace=False))
+    tokens[0], tokens[-1] = 0, shape.T - 1
+    x, dy = f32(case.x), f32(case.dy)
+    wgv, wuv, wdv = case.expert_view(case.wg), case.expert_view(case.wu), case.expert_view(case.wd)
+    ref = oracle.forward(x, wgv, wuv, wdv, idx, w, tokens=tokens)
+    assert_close("y[sampled]", f32(case.y)[tokens], ref["y"])
+    rb = oracle.backward(x, wgv, wuv, wdv, idx, w, dy, tokens=tokens, experts=[1, 3])
+    assert_close("dx[sampled]", f32(case.dx)[tokens], rb["dx"])
+    assert_close("dw[sampled]", case.dw.cpu().numpy()[tokens], rb["dw"])
+    dl = oracle.ffn.d_logits_dense(idx, rb["dl_sel"], shape.E, tokens=tokens)
+    assert_close("d_logits[sampled]", case.dlogits.cpu().numpy()[tokens], dl)
+    for e in (1, 3):
+        assert_close(f"dW_gate[{e}]", f32(case.grads["d_w_gate"][e]), rb["dWg"][e])
+        assert_close(f"dW_up[{e}]", f32(case.grads["d_w_up"][e]), rb["dWu"][e])
+        assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])
+    assert_rerun_bitwise(case)
