@@ -341,10 +341,22 @@ moe_status forward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_s
         const int grow0 = m * g.Sm, t0 = m * g.M;
         const int32_t* off = sched->offsets + (size_t)m * (g.E + 1);
         int32_t* toff = (int32_t*)(P.ws + L.tile_off) + (size_t)m * (g.E + 1);
-        if (launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st)) return MOE_ERR_HIP;
+        // MXFP8 weights: the gate/up GEMM takes groups of at least kBigRows
+        // rows in 256 x 256 tiles when groups are large on average
+        const bool big = !g.w4 && tm == 128 && g.I % (kBig / 2) == 0;
+        int32_t* tsmall = (int32_t*)(P.ws + L.tile_split) + (size_t)m * 2 * (g.E + 1);
+        int32_t* tbig = tsmall + (g.E + 1);
+        if (big ? launch_tile_prefix_split(off, g.E, g.Sm, tm, toff, kBigRows, kBig, tsmall, tbig, err, st)
+                : launch_tile_prefix(off, g.E, g.Sm, tm, toff, err, st))
+            return MOE_ERR_HIP;
         GroupRows grp{off, toff, g.E, g.Sm, 0, err, nullptr, 0, tm};
+        GroupRows grp_split = grp;
+        if (big) {
+            grp_split.tile_off = tsmall;
+            grp_split.tile_big = tbig;
+        }
         const GU keep = gu_routed(g, L, P, saved, m, true);
-        GemmGateUpMXArgs a1{grp, w4, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
+        GemmGateUpMXArgs a1{grp_split, w4, xq, xs, 0, 1, sched->slot_of_row, grow0, g.k, g.S,
                             (const uint8_t*)fw.gq, (const uint8_t*)fw.gs, (const uint8_t*)fw.uq,
                             (const uint8_t*)fw.us, g.H, g.I, (float*)keep.g, (float*)keep.u, keep.row0,
                             hq, hs};

@@ -64,6 +64,10 @@ __device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
 // ---------------------------------------------------------------- wave ops
 __device__ __forceinline__ int lane_id() { return threadIdx.x & (kWave - 1); }
 
+// the wave's index in its block, as a wave-uniform (scalar) value: LDS
+// addresses built from it alone stay in scalar registers
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
 __device__ __forceinline__ uint64_t lanemask_lt() {
     int l = lane_id();
     return l == 0 ? 0ull : (~0ull >> (64 - l));

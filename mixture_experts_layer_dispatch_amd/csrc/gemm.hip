@@ -842,21 +842,6 @@ static inline int row_tile(const GroupRows& g) { return g.tm == 128 ? 128 : 64; 
         return hipGetLastError() == hipSuccess ? 0 : -1;                           \
     } while (0)
 
-// 256 x 256 tiles: the routed groups of tile_big, or a dense group of at
-// least kBigRows rows (then alone)
-// (routed groups: the caller builds tile_big only when every GEMM that takes
-// it has a 256 x 256 form for its sizes; a launcher that cannot take it fails)
-static inline bool dense_big(const GroupRows& g, bool dims_ok) {
-    return !g.tile_off && g.tm == 128 && g.dense_rows >= kBigRows && dims_ok;
-}
-
-static inline int big_grid(const GroupRows& g) {
-    if (!g.tile_off) return (g.dense_rows + kBig - 1) / kBig;
-    // groups of n >= kBigRows rows take ceil(n / kBig) <= n / 128 tiles
-    const int64_t a = (int64_t)g.rows / 128, b = ((int64_t)g.rows + (int64_t)g.E * (kBig - 1)) / kBig;
-    return (int)(a < b ? a : b);
-}
-
 int launch_gemm_gate_up(const GemmGateUpArgs& a, hipStream_t st) {
     ProfScope prof_(st, "gemm_gate_up");
     const bool dims_ok = a.I % (kBig / 2) == 0 && a.H % kTK == 0;

@@ -588,7 +588,7 @@ struct DirectKC {
         }
     }
     __device__ __forceinline__ void issue1(int q, int kt, uint16_t* tile) const {
-        const int w = threadIdx.x >> 6;
+        const int w = wave_id();
         __builtin_amdgcn_global_load_lds((glb_void_t*)(p[q] + (int64_t)kt * kTK),
                                          (lds_void_t*)(tile + (q * kBigThreads + w * 64) * 8), 16, 0, 0);
     }
@@ -619,7 +619,7 @@ struct DirectKS {
         }
     }
     __device__ __forceinline__ void issue1(int q, const uint16_t* base, uint16_t* tile) const {
-        const int w = threadIdx.x >> 6;
+        const int w = wave_id();
         __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off[q]),
                                          (lds_void_t*)(tile + (q * kBigThreads + w * 64) * 8), 16, 0, 0);
     }
@@ -745,6 +745,21 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
     }
 }
 
+// 256 x 256 tiles: the routed groups of tile_big, or a dense group of at
+// least kBigRows rows (then alone)
+// (routed groups: the caller builds tile_big only when every GEMM that takes
+// it has a 256 x 256 form for its sizes; a launcher that cannot take it fails)
+static inline bool dense_big(const GroupRows& g, bool dims_ok) {
+    return !g.tile_off && g.tm == 128 && g.dense_rows >= kBigRows && dims_ok;
+}
+
+static inline int big_grid(const GroupRows& g) {
+    if (!g.tile_off) return (g.dense_rows + kBig - 1) / kBig;
+    // groups of n >= kBigRows rows take ceil(n / kBig) <= n / 128 tiles
+    const int64_t a = (int64_t)g.rows / 128, b = ((int64_t)g.rows + (int64_t)g.E * (kBig - 1)) / kBig;
+    return (int)(a < b ? a : b);
+}
+
 // ---------------------------------------------------------------- 256 x 256, K-grouped
 // KS tile of kTK k-rows by kBig columns whose k-rows come one by one from a
 // K-row source (src.pre / src.at: the k-th row of a group at column col0, or
@@ -779,7 +794,7 @@ struct DirectKSRows {
         for (int q = 0; q < PER; ++q) pn[q] = pn2[q];
     }
     __device__ __forceinline__ void issue1(int q, int kt, uint16_t* tile) const {
-        const int w = threadIdx.x >> 6;
+        const int w = wave_id();
         const uint16_t* r = src.at(kt * kTK + k0 + 16 * q, pn[q]);
         const uint16_t* p = global_select(r == nullptr, r, zero) + co;
         __builtin_amdgcn_global_load_lds((glb_void_t*)p, (lds_void_t*)(tile + (q * kBigThreads + w * 64) * 8),

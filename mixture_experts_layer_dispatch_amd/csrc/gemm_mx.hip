@@ -392,6 +392,139 @@ __device__ __forceinline__ void mainloop_mx(LA& la, LB& lb, SA& sa, SB& sb, int 
     }
 }
 
+// ================================================================ 256 x 256 tiles
+// Groups of at least kBigRows rows (see mainloop_big): a 128-code K step is
+// 128 bytes per row, the row of a bf16 KC tile, so code tiles are DirectKC
+// copies; each row's scale word (four E8M0 scales) is one 4-byte copy, waves
+// 0-3 copying A rows 64 (wave & 3) + lane, waves 4-7 the B rows.
+// Stage: A codes, B codes, A scale words, B scale words (66 KB).
+struct SmemBigMX {
+    static constexpr int A = Tile<kBig, false>::SIZE;      // uint16 per code tile
+    static constexpr int SC = 2 * kBig;                     // uint16 per kBig scale words
+    static constexpr int STAGE = 2 * A + 2 * SC;
+};
+
+struct DirectScales {
+    const uint32_t* p;             // this lane's row, K step 0
+    int kst;                       // words between K steps
+    template <class SA, class SB>
+    __device__ DirectScales(const SA& sa, const SB& sb, const uint32_t* safe) {
+        const int w = threadIdx.x >> 6, r = 64 * (w & 3) + lane_id();
+        const uint32_t* b;
+        if (w < 4) {
+            b = sa.row(r);
+            kst = sa.kstride();
+        } else {
+            b = sb.row(r);
+            kst = sb.kstride();
+        }
+        p = global_select(b == nullptr, b, safe);
+    }
+    __device__ __forceinline__ void issue(int kt, uint16_t* stage) const {
+        const int w = wave_id();
+        uint32_t* sc = (uint32_t*)(stage + 2 * SmemBigMX::A) + (w < 4 ? 0 : kBig) + 64 * (w & 3);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(p + (int64_t)kt * kst), (lds_void_t*)sc, 4, 0, 0);
+    }
+};
+
+// MODE MX_BF16: codes decoded exactly to bf16 (four 32-code sub-steps per K
+// step, mma_tile_mx_precise's order); MX_ACC: the scaled fp8 MFMA, one per
+// K step (mma_tile_mx_at's).  acc as in mainloop_big.
+template <int MODE>
+__device__ __forceinline__ void mainloop_big_mx(const DirectKC& la, const DirectKC& lb, const DirectScales& ls,
+                                                int nk, uint16_t* st0, uint16_t* st1, f32x4 (&acc)[8][4]) {
+    const int w = threadIdx.x >> 6;
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (nk <= 0) return;
+    la.issue(0, st0);
+    lb.issue(0, st0 + SmemBigMX::A);
+    ls.issue(0, st0);
+    wait_copies();
+    __syncthreads();
+    // copy slot li of a step (0 .. 8): A codes, B codes, then the scale word
+    auto copy = [&](int li, int kt, uint16_t* nxt) {
+        if (li < DirectKC::PER) la.issue1(li, kt, nxt);
+        else if (li < 2 * DirectKC::PER) lb.issue1(li - DirectKC::PER, kt, nxt + SmemBigMX::A);
+        else if (li == 2 * DirectKC::PER) ls.issue(kt, nxt);
+    };
+    auto step = [&](const uint16_t* cur, uint16_t* nxt, int kt) {
+        const bool more = kt + 1 < nk;
+        const uint16_t* sA = cur;
+        const uint16_t* sB = cur + SmemBigMX::A;
+        const uint32_t* cA = (const uint32_t*)(cur + 2 * SmemBigMX::A);
+        const uint32_t* cB = cA + kBig;
+        if constexpr (MODE == MX_BF16) {
+            // row blocks outermost: four B and two A fragments live.  The
+            // sub-steps stay a loop (unrolled, the decode of all four is
+            // hoisted and spills); the first one, which issues the copies,
+            // is peeled so that every copy slot is static.
+            auto sub = [&](int ks, bool copies) {
+                bf16x8 fa[4];
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) fa[nb] = frag_mx_bf16(sB, cB, wn0 + nb * 16, ks);
+                bf16x8 fb0 = frag_mx_bf16(sA, cA, wm0, ks), fb1;
+#pragma unroll
+                for (int mb = 0; mb < 8; ++mb) {
+                    if (mb + 1 < 8) {
+                        if (mb & 1) fb0 = frag_mx_bf16(sA, cA, wm0 + (mb + 1) * 16, ks);
+                        else fb1 = frag_mx_bf16(sA, cA, wm0 + (mb + 1) * 16, ks);
+                    }
+                    if (copies) {
+                        copy(mb, kt + 1, nxt);
+                        if (mb == 7) copy(8, kt + 1, nxt);
+                    }
+#pragma unroll
+                    for (int nb = 0; nb < 4; ++nb)
+                        acc[mb][nb] = mfma_16x16x32(fa[nb], (mb & 1) ? fb1 : fb0, acc[mb][nb]);
+                }
+            };
+            sub(0, more);
+#pragma unroll 1
+            for (int ks = 1; ks < 4; ++ks) sub(ks, false);
+        } else {
+            v8i32 fa[4];
+            int xa[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                fa[nb] = frag_mx(sB, wn0 + nb * 16);
+                xa[nb] = scale_mx(cB, wn0 + nb * 16);
+            }
+            v8i32 fb0 = frag_mx(sA, wm0), fb1;
+            int xb0 = scale_mx(cA, wm0), xb1;
+#pragma unroll
+            for (int mb = 0; mb < 8; ++mb) {
+                if (mb + 1 < 8) {
+                    if (mb & 1) {
+                        fb0 = frag_mx(sA, wm0 + (mb + 1) * 16);
+                        xb0 = scale_mx(cA, wm0 + (mb + 1) * 16);
+                    } else {
+                        fb1 = frag_mx(sA, wm0 + (mb + 1) * 16);
+                        xb1 = scale_mx(cA, wm0 + (mb + 1) * 16);
+                    }
+                }
+                if (more) {
+                    copy(mb, kt + 1, nxt);
+                    if (mb == 7) copy(8, kt + 1, nxt);
+                }
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        fa[nb], (mb & 1) ? fb1 : fb0, acc[mb][nb], 0, 0, 0, xa[nb], 0, (mb & 1) ? xb1 : xb0);
+            }
+        }
+        wait_copies();
+        __syncthreads();
+    };
+    for (int kt = 0; kt < nk; kt += 2) {
+        step(st0, st1, kt);
+        if (kt + 1 < nk) step(st1, st0, kt + 1);
+    }
+}
+
 // One or two column tiles of one row tile in a single K loop (as
 // mainloop_kc_tiles): tile 1's B codes lie bstride uint16 further, its B
 // scales bstride_s words further.
@@ -510,6 +643,77 @@ __global__ __launch_bounds__(256, 2) void k_gemm_gate_up_mx(GemmGateUpMXArgs a) 
         const int s = mx_scale_exp(amax);
         if (rl < hi) {
             const int ib = i0 + 32 * wn;                     // first column of the block
+            uint8_t* hrow = a.h_q + (int64_t)rl * I;
+            *(uint32_t*)(hrow + ib + 4 * (lane >> 4)) = e4m3_pack4(hq, s);
+            *(uint32_t*)(hrow + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(hq + 4, s);
+            if ((lane >> 4) == 0) a.h_s[(int64_t)rl * (I / 32) + ib / 32] = (uint8_t)(s + 127);
+        }
+    }
+}
+
+// The groups of at least kBigRows rows in 256 x 256 tiles (MXFP8 weights):
+// 256 rows x (128 gate + 128 up columns), each wave's 64 columns the gate and
+// up columns of one 32-wide h block, so the epilogue is the one above.
+__global__ __launch_bounds__(kBigThreads, 1) void k_gemm_gate_up_mx_big(GemmGateUpMXArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t st0[SmemBigMX::STAGE];
+    __shared__ __attribute__((aligned(16))) uint16_t st1[SmemBigMX::STAGE];
+    int e, lo, hi, nt;
+    if (!map_mtile_big(a.g, a.I / (kBig / 2), blockIdx.x, e, lo, hi, nt)) return;
+    const int i0 = nt * (kBig / 2);
+    const int H = a.H, I = a.I;
+    f32x4 acc[8][4];
+    {
+        const uint16_t* wg = (const uint16_t*)(a.wg_q + (int64_t)e * I * H);
+        const uint16_t* wu = (const uint16_t*)(a.wu_q + (int64_t)e * I * H);
+        const uint32_t* wgs = (const uint32_t*)(a.wg_s + (int64_t)e * I * (H / 32));
+        const uint32_t* wus = (const uint32_t*)(a.wu_s + (int64_t)e * I * (H / 32));
+        const RowsGateUp db{wg, wu, H / 2, i0};
+        const ScalesGateUp ds{wgs, wus, I, i0};
+        const DirectKC lb(db);
+        const uint32_t* safe = (const uint32_t*)a.x_s;
+        if (a.x_gather) {
+            const RowsGather da{(const uint16_t*)a.x_q, H / 2, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S,
+                                a.g.err};
+            const ScalesGather dsa{(const uint32_t*)a.x_s, H / 128, a.slot_of_row, a.grow0 + lo, hi - lo, a.k, a.S};
+            const DirectKC la(da);
+            const DirectScales ls(dsa, ds, safe);
+            mainloop_big_mx<MX_BF16>(la, lb, ls, H / 128, st0, st1, acc);
+        } else {
+            const RowsDirect da{(const uint16_t*)a.x_q, H / 2, a.xrow0 + lo, hi - lo};
+            const ScalesDirect dsa{(const uint32_t*)a.x_s, H / 128, a.xrow0 + lo, hi - lo};
+            const DirectKC la(da);
+            const DirectScales ls(dsa, ds, safe);
+            mainloop_big_mx<MX_BF16>(la, lb, ls, H / 128, st0, st1, acc);
+        }
+    }
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wq = w >> 1;
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int rl = lo + wm0 + mb * 16 + (lane & 15);
+        float hq[8];
+        float amax = 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hq[4 * nb + r] = swiglu_h(acc[mb][nb][r], acc[mb][nb + 2][r]);
+                amax = fmaxf(amax, fabsf(hq[4 * nb + r]));
+            }
+            if (rl < hi && a.g_out) {
+                const int i = i0 + 32 * wq + nb * 16 + 4 * (lane >> 4);
+                const int64_t srow = (int64_t)(a.save_row0 + rl) * I + i;
+                *(float4*)(a.g_out + srow) = make_float4(acc[mb][nb][0], acc[mb][nb][1],
+                                                         acc[mb][nb][2], acc[mb][nb][3]);
+                *(float4*)(a.u_out + srow) = make_float4(acc[mb][nb + 2][0], acc[mb][nb + 2][1],
+                                                         acc[mb][nb + 2][2], acc[mb][nb + 2][3]);
+            }
+        }
+        amax = fmaxf(amax, __shfl_xor(amax, 16));
+        amax = fmaxf(amax, __shfl_xor(amax, 32));
+        const int s = mx_scale_exp(amax);
+        if (rl < hi) {
+            const int ib = i0 + 32 * wq;                     // first column of the block
             uint8_t* hrow = a.h_q + (int64_t)rl * I;
             *(uint32_t*)(hrow + ib + 4 * (lane >> 4)) = e4m3_pack4(hq, s);
             *(uint32_t*)(hrow + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(hq + 4, s);
@@ -1033,6 +1237,17 @@ static inline int mgroup_grid_mx(const GroupRows& g, int TM) {
 
 int launch_gemm_gate_up_mx(const GemmGateUpMXArgs& a, hipStream_t st) {
     ProfScope prof_(st, a.w4 ? "gemm_gate_up_mx4" : "gemm_gate_up_mx");
+    const bool dims_ok = !a.w4 && a.I % (kBig / 2) == 0 && a.H % 128 == 0;
+    const bool dbig = dense_big(a.g, dims_ok);
+    if (a.g.tile_big || dbig) {
+        if (!dims_ok) return -1;
+        const int grid = big_grid(a.g) * (a.I / (kBig / 2));
+        if (grid > 0) {
+            k_gemm_gate_up_mx_big<<<grid, kBigThreads, 0, st>>>(a);
+            if (hipGetLastError() != hipSuccess) return -1;
+        }
+        if (dbig) return 0;
+    }
     const int tm_ = a.g.tm == 128 ? 128 : 64;
     const int grid_ = mgroup_grid_mx(a.g, tm_) * (a.I / 64);
     if (grid_ <= 0) return 0;

@@ -46,6 +46,10 @@ SHAPES = {
     "max_e": si.custom_shape("max_e_mx", T=256, H=128, I=128, E=1024, k=8, seed=33),
     "top1_ring": si.custom_shape("top1_ring_mx", T=512, H=256, I=256, E=8, k=1, seed=35,
                                  macrobatch=128, minibatch=64),
+    # groups of ~256 rows over two macrobatches with a dense shared expert of
+    # 512 rows: the gate/up GEMM's 256 x 256 tiles beside its 128-row tiles
+    "big_tiles": si.custom_shape("big_tiles_mx", T=1024, H=512, I=256, E=4, k=2, seed=41,
+                                 n_shared=1, macrobatch=512, minibatch=256),
 }
 
 
