@@ -561,8 +561,10 @@ __device__ __forceinline__ void mainloop_ks_pipe(LA& la, LB& lb, int nk, uint16_
 // fragments from LDS for 64 MFMAs.  Operands go from global memory straight
 // into LDS (gfx950's global_load_lds, 16 bytes per lane, no register
 // staging) in the swizzled KC layout, two stages of 64 KB; the copies of the
-// next step are issued one per column block inside the MFMA loop, so they
-// fly while the current step computes.
+// next step go out together after the step's first fragment reads, so they
+// fly while the current step computes (spread one per column block, the
+// gate/up input gradient took 0.40 instead of 0.37 ms on the expert-parallel
+// share).
 constexpr int kBigThreads = 512;       // kBig, kBigRows: launch.h
 
 typedef __attribute__((address_space(3))) void lds_void_t;
@@ -727,10 +729,12 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
                     if (nb & 1) fa0 = fa_of(sB, nb + 1, ks);
                     else fa1 = fa_of(sB, nb + 1, ks);
                 }
-                const int li = (ks / 32) * 4 + nb;       // 0..7: the next step's eight copies
-                if (more) {
-                    if (li < DirectKC::PER) la.issue1(li, kt + 1, nxt);
-                    else big_issue_b(lb, sb, li - DirectKC::PER, kt + 1, nxt + SmemBig::A);
+                if (more && ks == 0 && nb == 0) {         // the next step's eight copies
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) {
+                        if (q < DirectKC::PER) la.issue1(q, kt + 1, nxt);
+                        else big_issue_b(lb, sb, q - DirectKC::PER, kt + 1, nxt + SmemBig::A);
+                    }
                 }
 #pragma unroll
                 for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma_16x16x32((nb & 1) ? fa1 : fa0, fb[mb], acc[mb][nb]);
@@ -849,10 +853,12 @@ __device__ __forceinline__ void mainloop_big_kk(LA& la, LB& lb, int nk, uint16_t
                     if (mb & 1) fb0 = frag_ks_sw(sA, wm0 + (mb + 1) * 16, ks);
                     else fb1 = frag_ks_sw(sA, wm0 + (mb + 1) * 16, ks);
                 }
-                const int li = (ks / 32) * 8 + mb;          // copies on the even slots
-                if (more && !(li & 1)) {
-                    if (li / 2 < LA::PER) la.issue1(li / 2, kt + 1, nxt);
-                    else lb.issue1(li / 2 - LA::PER, kt + 1, nxt + SmemBig::A);
+                if (more && ks == 0 && mb == 0) {      // the next step's copies, together
+#pragma unroll
+                    for (int q = 0; q < LA::PER + LB::PER; ++q) {
+                        if (q < LA::PER) la.issue1(q, kt + 1, nxt);
+                        else lb.issue1(q - LA::PER, kt + 1, nxt + SmemBig::A);
+                    }
                 }
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], (mb & 1) ? fb1 : fb0, acc[mb][nb]);
