@@ -714,22 +714,26 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
         const bool more = kt + 1 < nk;
         const uint16_t* sA = cur;
         const uint16_t* sB = cur + SmemBig::A;
+        // row blocks outermost: four B fragments and two A fragments live at a
+        // time (B outermost, with all eight A fragments loaded first, ran the
+        // gate/up input gradient 0.343 -> 0.365 ms on the expert-parallel share)
 #pragma unroll
         for (int ks = 0; ks < kTK; ks += 32) {
-            bf16x8 fb[8];
+            bf16x8 fa[4];
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) fa[nb] = fa_of(sB, nb, ks);
+            auto fbm = [&](int mb) {
+                if constexpr (BKS) return frag_kc_perm(sA, 0, wm0 + mb * 16, ks);
+                else return frag_kc(sA, 0, wm0 + mb * 16, ks);
+            };
+            bf16x8 fb0 = fbm(0), fb1;
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
-                if constexpr (BKS) fb[mb] = frag_kc_perm(sA, 0, wm0 + mb * 16, ks);
-                else fb[mb] = frag_kc(sA, 0, wm0 + mb * 16, ks);
-            }
-            bf16x8 fa0 = fa_of(sB, 0, ks), fa1;
-#pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
-                if (nb + 1 < 4) {
-                    if (nb & 1) fa0 = fa_of(sB, nb + 1, ks);
-                    else fa1 = fa_of(sB, nb + 1, ks);
+                if (mb + 1 < 8) {
+                    if (mb & 1) fb0 = fbm(mb + 1);
+                    else fb1 = fbm(mb + 1);
                 }
-                if (more && ks == 0 && nb == 0) {         // the next step's eight copies
+                if (more && ks == 0 && mb == 0) {       // the next step's eight copies
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
                         if (q < DirectKC::PER) la.issue1(q, kt + 1, nxt);
@@ -737,7 +741,7 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
                     }
                 }
 #pragma unroll
-                for (int mb = 0; mb < 8; ++mb) acc[mb][nb] = mfma_16x16x32((nb & 1) ? fa1 : fa0, fb[mb], acc[mb][nb]);
+                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], (mb & 1) ? fb1 : fb0, acc[mb][nb]);
             }
         }
         wait_copies();
