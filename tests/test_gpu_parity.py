@@ -353,3 +353,29 @@ def test_forward_backward_many_big_tiles_sampled():
         assert_close(f"dW_up[{e}]", f32(case.grads["d_w_up"][e]), rb["dWu"][e])
         assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])
     assert_rerun_bitwise(case)
+
+
+@pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
+def test_256_row_tiles_give_the_bits_of_the_smaller_tiles(precision):
+    """The same tokens as one macrobatch (groups of ~512 rows, a 1024-row shared
+    expert: the 256 x 256 tile forms) and as eight macrobatches (groups of ~64
+    rows: 64-row tiles).  Every output whose rows do not mix across
+    macrobatches (y, dx, the router-weight and logit gradients) is bit for bit
+    the same: each row's products are summed in the same order in every tile
+    form."""
+    from mixture_experts_layer_dispatch_amd import binding as B
+    prec = B.PREC_BF16 if precision == "bf16" else B.PREC_MXFP8
+    kw = dict(T=1024, H=512, I=256, E=4, k=2, seed=42, n_shared=1)
+    one = Case(si.custom_shape("tiles_one_macrobatch", **kw), precision=prec)
+    many = Case(si.custom_shape("tiles_eight_macrobatches", macrobatch=128, minibatch=64, **kw),
+                precision=prec)
+    for c in (one, many):
+        c.schedule()
+        c.forward()
+        c.backward()
+    torch.cuda.synchronize()
+    assert B.moe_check_device_error(one.ws) == 0 and B.moe_check_device_error(many.ws) == 0
+    _, _, sch = one.oracle_schedule()
+    assert (sch["counts"] >= 256).any()                      # the large form runs in `one`
+    for name in ("y", "dx", "dw", "dlogits"):
+        assert torch.equal(getattr(one, name), getattr(many, name)), name
