@@ -643,16 +643,6 @@ __device__ __forceinline__ void deep_group(const GroupRows& g, int d, int& e, in
     n = g.offsets[e + 1] - lo;          // validated when the list was built
 }
 
-__device__ __forceinline__ void deep_store(const WgradOut& out, int64_t ebase, int64_t ld, int r0, int n0,
-                                           const f32x4 (&acc)[D_TM / 32][D_TN / 32]) {
-    AccPos<D_TM, D_TN> pos;
-#pragma unroll
-    for (int mb = 0; mb < D_TM / 32; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < D_TN / 32; ++nb)
-            wgrad_store(out, ebase + (int64_t)(r0 + pos.m(mb)) * ld + n0 + pos.n(nb), acc[mb][nb]);
-}
-
 __global__ __launch_bounds__(256, 2) void k_wgrad_down_deep(WgradDownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<D_TM, D_TN, true, true>::STAGE];
     const int nNt = a.I / D_TN, per = (a.H / D_TM) * nNt;
@@ -676,7 +666,8 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_down_deep(WgradDownArgs a) {
             mainloop_ks_pipe<D_TM, D_TN>(la, lb, nk, smem, acc);
         }
         WgradOut o = a.out;
-        if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) >= 0) deep_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
+        if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) >= 0)
+            staged_tile_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc, (float*)smem);
     }
 }
 
@@ -705,7 +696,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_gate_up_deep(WgradGateUpArgs a
         }
         WgradOut o = up ? a.out_up : a.out_gate;
         if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) >= 0)
-            deep_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
+            staged_tile_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc, (float*)smem);
     }
 }
 
@@ -735,17 +726,39 @@ __device__ __forceinline__ void big_group(const GroupRows& g, int d, int& e, int
     n = g.offsets[e + 1] - lo;          // validated when the list was built
 }
 
+// A 256 x 256 tile (mainloop_big_kk's layout) stored through LDS 64 rows at a
+// time, the rounds alternating the two stage arrays (64 rows x 256 floats,
+// 64 KB, 16-byte chunks XOR-swizzled by row so that 16 rows of one chunk, or
+// 16 chunks of one row, hit 16 bank groups): every global access is a whole
+// 1 KB (fp32) or 512-byte (bf16) row piece.  Ends with a barrier (the stage
+// arrays are free for the next item's copies).
 __device__ __forceinline__ void big_wgrad_store(const WgradOut& out, int64_t ebase, int64_t ld, int r0, int n0,
-                                                const f32x4 (&acc)[8][4]) {
+                                                const f32x4 (&acc)[8][4], float* b0, float* b1) {
     const int w = threadIdx.x >> 6, lane = lane_id();
-    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+    const int wn0 = (w >> 1) * 64;
 #pragma unroll
-    for (int mb = 0; mb < 8; ++mb)
+    for (int rd = 0; rd < 4; ++rd) {                 // rows 64 rd .. 64 rd + 63 of the tile
+        float* buf = (rd & 1) ? b1 : b0;
+        if ((w & 1) == (rd >> 1)) {
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-            wgrad_store(out, ebase + (int64_t)(r0 + wm0 + mb * 16 + (lane & 15)) * ld + n0 + wn0 + nb * 16 +
-                                 4 * (lane >> 4),
-                        acc[mb][nb]);
+            for (int mbl = 0; mbl < 4; ++mbl) {
+                const int rl = mbl * 16 + (lane & 15);
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) {
+                    const int ch = (wn0 + nb * 16) / 4 + (lane >> 4);
+                    *(f32x4*)(buf + rl * 256 + 4 * (ch ^ (rl & 15))) = acc[(rd & 1) * 4 + mbl][nb];
+                }
+            }
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int q = 0; q < 64 * 64 / kBigThreads; ++q) {
+            const int c = threadIdx.x + kBigThreads * q, r = c >> 6, cc = c & 63;
+            const f32x4 v = *(const f32x4*)(buf + r * 256 + 4 * (cc ^ (r & 15)));
+            wgrad_store(out, ebase + (int64_t)(r0 + 64 * rd + r) * ld + n0 + 4 * cc, v);
+        }
+    }
+    __syncthreads();
 }
 
 __device__ __forceinline__ int big_item(int r) {
@@ -776,7 +789,8 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_wgrad_down_big(WgradDownArgs
             mainloop_big_kk(la, lb, nk, st0, st1, acc);
         }
         WgradOut o = a.out;
-        if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) >= 0) big_wgrad_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc);
+        if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) >= 0)
+            big_wgrad_store(o, (int64_t)e * a.H * a.I, a.I, m0, n0, acc, (float*)st0, (float*)st1);
     }
 }
 
@@ -806,7 +820,7 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_wgrad_gate_up_big(WgradGateU
         }
         WgradOut o = up ? a.out_up : a.out_gate;
         if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) >= 0)
-            big_wgrad_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc);
+            big_wgrad_store(o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0, n0, acc, (float*)st0, (float*)st1);
     }
 }
 

@@ -1014,7 +1014,9 @@ __host__ __device__ __forceinline__ int wgrad_group_tiles(int ntiles, int ng, in
 // LDS of a weight-gradient block: the resident A tile, then a region that
 // holds the B tile during the MFMAs and the bf16 output tile afterwards.
 constexpr int W_SP = W_TN + 8;                                    // staging pitch
+constexpr int W_FP = W_TN + 4;        // fp32 staging pitch: 16 rows of 16 bytes hit 16 bank groups
 constexpr int W_REGION = (W_TM * W_SP > Tile<W_TN, true>::SIZE) ? W_TM * W_SP : Tile<W_TN, true>::SIZE;
+static_assert(64 * W_FP * 2 <= W_REGION, "half a slab of fp32 sums fits the staging region");
 constexpr int W_SMEM = Tile<W_TM, true>::SIZE + W_REGION;
 
 // mode: 0 write bf16; 1 write fp32 partial; 2 add to fp32 partial;
@@ -1031,6 +1033,30 @@ __device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, cons
     }
     if (o.mode == 1 || o.mode == 2) *(float4*)(o.acc + idx) = make_float4(x0, x1, x2, x3);
     else *(uint2*)(o.out + idx) = pack4(x0, x1, x2, x3);
+}
+
+// A 128 x 128 output tile of a four-wave block (AccPos<128, 128> layout)
+// stored through LDS, so that every global access is a whole row piece (512
+// bytes of fp32 sums, 256 of bf16) rather than each lane's 16 bytes of a
+// 64-byte piece.  fst: 128 x W_TFP floats of LDS the block no longer reads
+// (the caller has passed a barrier since its last reads); ends with a barrier,
+// after which the LDS may be reused.
+constexpr int W_TFP = 128 + 4;       // 16 rows of 16 bytes per pass hit 16 bank groups
+__device__ __forceinline__ void staged_tile_store(const WgradOut& out, int64_t ebase, int64_t ld, int r0, int n0,
+                                                  const f32x4 (&acc)[4][4], float* fst) {
+    AccPos<128, 128> pos;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) *(f32x4*)(fst + pos.m(mb) * W_TFP + pos.n(nb)) = acc[mb][nb];
+    __syncthreads();
+#pragma unroll 2
+    for (int q = 0; q < 128 * 32 / 256; ++q) {
+        const int c = threadIdx.x + 256 * q, r = c >> 5, cc = c & 31;
+        const f32x4 v = *(const f32x4*)(fst + r * W_TFP + 4 * cc);
+        wgrad_store(out, ebase + (int64_t)(r0 + r) * ld + n0 + 4 * cc, v);
+    }
+    __syncthreads();
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -1054,11 +1080,31 @@ struct WgradEpi {
         AccPos<W_TM, W_TN> pos;
         const int n0 = nt * W_TN;
         if (!BF16_ONLY && out.mode != 0) {
+            // fp32 running sums: staged in LDS half a slab (64 rows) at a time so
+            // that every global access is a whole 256-byte row piece (each
+            // lane's own four sums are 16 bytes of a 64-byte piece: the
+            // 65 536-token stream's cold experts ran at ~1 TB/s that way)
+            float* fst = (float*)stage;
+            const int w = threadIdx.x >> 6;
 #pragma unroll
-            for (int mb = 0; mb < W_TM / 32; ++mb)
+            for (int half = 0; half < 2; ++half) {
+                if (half) __syncthreads();                 // the first half is written out
+                if ((w & 1) == half) {
 #pragma unroll
-                for (int nb = 0; nb < W_TN / 32; ++nb)
-                    wgrad_store(out, ebase + (int64_t)(m0 + pos.m(mb)) * ld + n0 + pos.n(nb), acc[mb][nb]);
+                    for (int mb = 0; mb < W_TM / 32; ++mb)
+#pragma unroll
+                        for (int nb = 0; nb < W_TN / 32; ++nb)
+                            *(f32x4*)(fst + (pos.m(mb) - 64 * half) * W_FP + pos.n(nb)) = acc[mb][nb];
+                }
+                __syncthreads();
+#pragma unroll 1
+                for (int q = 0; q < 64 * (W_TN / 4) / 256; ++q) {
+                    const int c = threadIdx.x + 256 * q;
+                    const int r = c / (W_TN / 4), cc = c % (W_TN / 4);
+                    const f32x4 v = *(const f32x4*)(fst + r * W_FP + 4 * cc);
+                    wgrad_store(out, ebase + (int64_t)(m0 + 64 * half + r) * ld + n0 + 4 * cc, v);
+                }
+            }
             return;
         }
 #pragma unroll

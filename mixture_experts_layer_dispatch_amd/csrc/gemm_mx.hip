@@ -1050,6 +1050,7 @@ constexpr int X_CA = X_TM * X_P;                          // A scales: X_TM word
 constexpr int X_CB = X_CA + 2 * X_TM;                     // B scales: X_TN words
 constexpr int X_REG = X_CB + 2 * X_TN;
 constexpr int X_SMEM = X_REG + (X_TM * W_SP > X_TN * X_P ? X_TM * W_SP : X_TN * X_P);
+static_assert(X_TM == W_TM && X_TN == W_TN && 64 * W_FP * 2 <= X_TM * W_SP, "WgradEpi's staging fits the region");
 
 // The column-tile walk of one weight-gradient block (A: 128 rows, B: the
 // current 64-row column tile).
@@ -1209,12 +1210,8 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx_deep(WgradMXArgs a) {
         if (wgrad_bind(out, e, g.blk_off ? g.off[e + 1] - g.off[e] : g.dense_rows, mat) < 0) continue;
         const int64_t ebase = (int64_t)e * mat;
         const int r0 = hi_part ? m0 - a.msplit : m0;
-        AccPos<XD_T, XD_T> pos;
-#pragma unroll
-        for (int mb = 0; mb < XD_T / 32; ++mb)
-#pragma unroll
-            for (int nb = 0; nb < XD_T / 32; ++nb)
-                wgrad_store(out, ebase + (int64_t)(r0 + pos.m(mb)) * a.N + n0 + pos.n(nb), acc[mb][nb]);
+        static_assert(XD_T == 128 && 128 * W_TFP * 4 <= 2 * SmemMX<XD_T, XD_T>::STAGE * 2, "staging fits");
+        staged_tile_store(out, ebase, a.N, r0, n0, acc, (float*)smem);
     }
 }
 
