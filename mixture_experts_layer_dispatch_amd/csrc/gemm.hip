@@ -736,9 +736,13 @@ __device__ __forceinline__ void big_wgrad_store(const WgradOut& out, int64_t eba
                                                 const f32x4 (&acc)[8][4], float* b0, float* b1) {
     const int w = threadIdx.x >> 6, lane = lane_id();
     const int wn0 = (w >> 1) * 64;
+    // readout: chunk q of a round is row 8 q + threadIdx.x / 64 of the round's
+    // 64, column chunk threadIdx.x % 64
+    const int rr = threadIdx.x >> 6, cc = threadIdx.x & 63;
 #pragma unroll
     for (int rd = 0; rd < 4; ++rd) {                 // rows 64 rd .. 64 rd + 63 of the tile
         float* buf = (rd & 1) ? b1 : b0;
+        const int64_t base = ebase + (int64_t)(r0 + 64 * rd + rr) * ld + n0 + 4 * cc;
         if ((w & 1) == (rd >> 1)) {
 #pragma unroll
             for (int mbl = 0; mbl < 4; ++mbl) {
@@ -750,12 +754,25 @@ __device__ __forceinline__ void big_wgrad_store(const WgradOut& out, int64_t eba
                 }
             }
         }
+        // the old sums in two batches of four (eight at once spill)
+        f32x4 old[4];
+        if (out.mode >= 2) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) old[q] = wgrad_old(out, base + 8 * q * ld);
+        }
         __syncthreads();
-#pragma unroll 2
-        for (int q = 0; q < 64 * 64 / kBigThreads; ++q) {
-            const int c = threadIdx.x + kBigThreads * q, r = c >> 6, cc = c & 63;
-            const f32x4 v = *(const f32x4*)(buf + r * 256 + 4 * (cc ^ (r & 15)));
-            wgrad_store(out, ebase + (int64_t)(r0 + 64 * rd + r) * ld + n0 + 4 * cc, v);
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            if (hb && out.mode >= 2) {
+#pragma unroll
+                for (int q = 0; q < 4; ++q) old[q] = wgrad_old(out, base + 8 * (4 + q) * ld);
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int r = rr + 8 * (4 * hb + q);
+                wgrad_put(out, base + 8 * (4 * hb + q) * ld, *(const f32x4*)(buf + r * 256 + 4 * (cc ^ (r & 15))),
+                          old[q]);
+            }
         }
     }
     __syncthreads();

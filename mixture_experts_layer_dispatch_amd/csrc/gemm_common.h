@@ -1025,14 +1025,26 @@ constexpr int W_SMEM = Tile<W_TM, true>::SIZE + W_REGION;
 // bf16 output: half the workspace, but the 8-byte accesses to two arrays
 // made the 65 536-token stream's weight gradients 15-20 % slower than one
 // 16-byte access to an fp32 array.)
-__device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, const f32x4& v) {
+__device__ __forceinline__ f32x4 wgrad_old(const WgradOut& o, int64_t idx) {
+    return *(const f32x4*)(o.acc + idx);
+}
+__device__ __forceinline__ void wgrad_put(const WgradOut& o, int64_t idx, const f32x4& v, const f32x4& old) {
     float x0 = v[0], x1 = v[1], x2 = v[2], x3 = v[3];
     if (o.mode >= 2) {
-        const float4 p = *(const float4*)(o.acc + idx);
-        x0 = p.x + x0; x1 = p.y + x1; x2 = p.z + x2; x3 = p.w + x3;
+        x0 = old[0] + x0; x1 = old[1] + x1; x2 = old[2] + x2; x3 = old[3] + x3;
     }
     if (o.mode == 1 || o.mode == 2) *(float4*)(o.acc + idx) = make_float4(x0, x1, x2, x3);
     else *(uint2*)(o.out + idx) = pack4(x0, x1, x2, x3);
+}
+// wgrad_old then wgrad_put.  Callers that store several chunks issue the
+// wgrad_old loads of all of them first: with one load before each store, each
+// store waits for its load's round trip (a thread storing eight chunks paid
+// eight in a row; the 65 536-token stream's accumulating weight gradients
+// were bound by that latency rather than by HBM).
+__device__ __forceinline__ void wgrad_store(const WgradOut& o, int64_t idx, const f32x4& v) {
+    f32x4 old = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (o.mode >= 2) old = wgrad_old(o, idx);
+    wgrad_put(o, idx, v, old);
 }
 
 // A 128 x 128 output tile of a four-wave block (AccPos<128, 128> layout)
@@ -1049,13 +1061,18 @@ __device__ __forceinline__ void staged_tile_store(const WgradOut& out, int64_t e
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) *(f32x4*)(fst + pos.m(mb) * W_TFP + pos.n(nb)) = acc[mb][nb];
-    __syncthreads();
-#pragma unroll 2
-    for (int q = 0; q < 128 * 32 / 256; ++q) {
-        const int c = threadIdx.x + 256 * q, r = c >> 5, cc = c & 31;
-        const f32x4 v = *(const f32x4*)(fst + r * W_TFP + 4 * cc);
-        wgrad_store(out, ebase + (int64_t)(r0 + r) * ld + n0 + 4 * cc, v);
+    constexpr int N = 128 * 32 / 256;
+    const int r = threadIdx.x >> 5, cc = threadIdx.x & 31;      // chunk q: row r + 8 q, column chunk cc
+    const int64_t base = ebase + (int64_t)(r0 + r) * ld + n0 + 4 * cc;
+    f32x4 old[N];
+    if (out.mode >= 2) {                   // the old sums of all the thread's chunks in one batch
+#pragma unroll
+        for (int q = 0; q < N; ++q) old[q] = wgrad_old(out, base + 8 * q * ld);
     }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < N; ++q)
+        wgrad_put(out, base + 8 * q * ld, *(const f32x4*)(fst + (r + 8 * q) * W_TFP + 4 * cc), old[q]);
     __syncthreads();
 }
 
@@ -1083,9 +1100,12 @@ struct WgradEpi {
             // fp32 running sums: staged in LDS half a slab (64 rows) at a time so
             // that every global access is a whole 256-byte row piece (each
             // lane's own four sums are 16 bytes of a 64-byte piece: the
-            // 65 536-token stream's cold experts ran at ~1 TB/s that way)
+            // 65 536-token stream's cold experts ran at ~1 TB/s that way); a
+            // half's old sums are loaded in one batch (wgrad_store)
             float* fst = (float*)stage;
             const int w = threadIdx.x >> 6;
+            constexpr int CPR = W_TN / 4, N = 64 * CPR / 256;
+            const int r = threadIdx.x / CPR, cc = threadIdx.x % CPR;    // chunk q: row r + 16 q
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 if (half) __syncthreads();                 // the first half is written out
@@ -1096,14 +1116,17 @@ struct WgradEpi {
                         for (int nb = 0; nb < W_TN / 32; ++nb)
                             *(f32x4*)(fst + (pos.m(mb) - 64 * half) * W_FP + pos.n(nb)) = acc[mb][nb];
                 }
-                __syncthreads();
-#pragma unroll 1
-                for (int q = 0; q < 64 * (W_TN / 4) / 256; ++q) {
-                    const int c = threadIdx.x + 256 * q;
-                    const int r = c / (W_TN / 4), cc = c % (W_TN / 4);
-                    const f32x4 v = *(const f32x4*)(fst + r * W_FP + 4 * cc);
-                    wgrad_store(out, ebase + (int64_t)(m0 + 64 * half + r) * ld + n0 + 4 * cc, v);
+                const int64_t base = ebase + (int64_t)(m0 + 64 * half + r) * ld + n0 + 4 * cc;
+                f32x4 old[N];
+                if (out.mode >= 2) {
+#pragma unroll
+                    for (int q = 0; q < N; ++q) old[q] = wgrad_old(out, base + 256 / CPR * q * ld);
                 }
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < N; ++q)
+                    wgrad_put(out, base + 256 / CPR * q * ld,
+                              *(const f32x4*)(fst + (r + 256 / CPR * q) * W_FP + 4 * cc), old[q]);
             }
             return;
         }
