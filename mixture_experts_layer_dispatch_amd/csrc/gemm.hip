@@ -561,56 +561,103 @@ __device__ __forceinline__ void wgrad_tiles(LoadKS<W_TM, SA>& la, LoadKS<W_TN, S
     else wgrad_tiles_<true, false>(la, lb, nk, g, ntn, ng, smem, epi);
 }
 
+// The slab kernels' two grids.  One block per (expert, 128-row slab, column
+// group) of every expert (one macrobatch, or the dense group); or, LISTED (a
+// walk over several macrobatches, modes chosen per expert), a persistent grid
+// over the items of the experts that have work (block_list), three blocks per
+// CU.
+__device__ __forceinline__ int slab_list(const GroupRows& g, const WgradOut& o, int16_t* list) {
+    return block_list(g.E, [&](int e) {
+        const int a = g.offsets[e], z = g.offsets[e + 1];
+        if (a < 0 || z < a || z > g.rows) {
+            raise_err(g.err, ERR_BAD_OFFSETS);
+            return false;
+        }
+        const int n = z - a;
+        return (g.deep_thr <= 0 || n <= g.deep_thr) && wgrad_mode(o, e, n) >= 0;
+    }, list);
+}
+template <bool LISTED, class Item>
+__device__ __forceinline__ void slab_blocks(const GroupRows& g, const WgradOut& o, int nMt, int nng,
+                                            const Item& item_fn) {
+    if constexpr (LISTED) {
+        __shared__ int16_t list[1024];
+        const int per = nMt * nng, total = slab_list(g, o, list) * per;
+        for (int r = 0;; ++r) {
+            const int item = r * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+            if (item >= total) break;
+            if (r) __syncthreads();                 // the previous item's staged tile has been read
+            const int d = item / per, rem = item - d * per;
+            const int e = list[d];
+            const int lo = g.offsets[e];
+            item_fn(e, rem / nng, rem % nng, lo, g.offsets[e + 1] - lo);    // validated by the list
+        }
+    } else {
+        int e, mt, ng, lo, n;
+        if (!map_ktile(g, nMt, nng, blockIdx.x, e, mt, ng, lo, n)) return;
+        item_fn(e, mt, ng, lo, n);
+    }
+}
+constexpr int SLAB_LISTED_PER_CU = 3;
+// the listed form: a walk over several macrobatches of routed groups
+static inline bool slab_listed(const GroupRows& g, const WgradOut& o) { return g.offsets && o.counts; }
+static inline int slab_grid(const GroupRows& g, const WgradOut& o, int nMt, int nng) {
+    const int all = (g.offsets ? g.E : 1) * nMt * nng;
+    return slab_listed(g, o) ? std::min(all, SLAB_LISTED_PER_CU * 256) : all;
+}
+
 // dW_down[e][h, i] = sum over e's rows r of dy[tok(r), h] * hw[r, i].
-__global__ __launch_bounds__(256, 4) void k_wgrad_down(WgradDownArgs a) {
+template <bool LISTED>
+__global__ __launch_bounds__(256, LISTED ? SLAB_LISTED_PER_CU : 4) void k_wgrad_down(WgradDownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[W_SMEM];
     const int ntiles = a.I / W_TN, nng = wgrad_groups(ntiles);
-    int e, mt, ng, lo, n;
-    if (!map_ktile(a.g, a.H / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
-    if (a.g.deep_thr > 0 && n > a.g.deep_thr) return;          // the deep kernel's group
-    const int m0 = mt * W_TM;
-    const int nk = (n + kTK - 1) / kTK;
-    KRowsGroup sb{a.hw, a.I, lo, n, 0};
-    LoadKS<W_TN, KRowsGroup> lb(sb);
-    WgradOut o = a.out;
-    if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) < 0) return;   // nothing to add for this expert
-    WgradEpi epi{o, (int64_t)e * a.H * a.I, a.I, m0};
-    if (a.dy_gather) {
-        KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
-        LoadKS<W_TM, KRowsGroupGather> la(sa);
-        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
-    } else {
-        KRowsGroup sa{a.dy, a.H, a.dyrow0 + lo, n, m0};
-        LoadKS<W_TM, KRowsGroup> la(sa);
-        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
-    }
+    slab_blocks<LISTED>(a.g, a.out, a.H / W_TM, nng, [&](int e, int mt, int ng, int lo, int n) {
+        if (a.g.deep_thr > 0 && n > a.g.deep_thr) return;          // the deep kernel's group
+        const int m0 = mt * W_TM;
+        const int nk = (n + kTK - 1) / kTK;
+        KRowsGroup sb{a.hw, a.I, lo, n, 0};
+        LoadKS<W_TN, KRowsGroup> lb(sb);
+        WgradOut o = a.out;
+        if (wgrad_bind(o, e, n, (int64_t)a.H * a.I) < 0) return;   // nothing to add for this expert
+        WgradEpi epi{o, (int64_t)e * a.H * a.I, a.I, m0};
+        if (a.dy_gather) {
+            KRowsGroupGather sa{a.dy, a.H, a.slot_of_row, a.grow0 + lo, n, m0, a.k, a.S, a.g.err};
+            LoadKS<W_TM, KRowsGroupGather> la(sa);
+            wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
+        } else {
+            KRowsGroup sa{a.dy, a.H, a.dyrow0 + lo, n, m0};
+            LoadKS<W_TM, KRowsGroup> la(sa);
+            wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
+        }
+    });
 }
 
 // dW_gate[e][i, h] = sum_r dg[r, i] x[tok(r), h]; dW_up likewise with du.
 // M runs over the 2I columns of [dg | du].
+template <bool LISTED>
 __global__ __launch_bounds__(256, 3) void k_wgrad_gate_up(WgradGateUpArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[W_SMEM];
     const int ntiles = a.H / W_TN, nng = wgrad_groups(ntiles);
-    int e, mt, ng, lo, n;
-    if (!map_ktile(a.g, 2 * a.I / W_TM, nng, blockIdx.x, e, mt, ng, lo, n)) return;
-    if (a.g.deep_thr > 0 && n > a.g.deep_thr) return;          // the deep kernel's group
-    const int m0 = mt * W_TM;
-    const int nk = (n + kTK - 1) / kTK;
-    const bool up = m0 >= a.I;
-    KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};
-    LoadKS<W_TM, KRowsGroup> la(sa);
-    WgradOut o = up ? a.out_up : a.out_gate;
-    if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) < 0) return;   // nothing to add for this expert
-    WgradEpi epi{o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0};
-    if (a.x_gather) {
-        KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, 0, a.k, a.S, a.g.err};
-        LoadKS<W_TN, KRowsGroupGather> lb(sb);
-        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
-    } else {
-        KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, 0};
-        LoadKS<W_TN, KRowsGroup> lb(sb);
-        wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
-    }
+    slab_blocks<LISTED>(a.g, a.out_gate, 2 * a.I / W_TM, nng, [&](int e, int mt, int ng, int lo, int n) {
+        if (a.g.deep_thr > 0 && n > a.g.deep_thr) return;          // the deep kernel's group
+        const int m0 = mt * W_TM;
+        const int nk = (n + kTK - 1) / kTK;
+        const bool up = m0 >= a.I;
+        KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};
+        LoadKS<W_TM, KRowsGroup> la(sa);
+        WgradOut o = up ? a.out_up : a.out_gate;
+        if (wgrad_bind(o, e, n, (int64_t)a.I * a.H) < 0) return;   // nothing to add for this expert
+        WgradEpi epi{o, (int64_t)e * a.I * a.H, a.H, up ? m0 - a.I : m0};
+        if (a.x_gather) {
+            KRowsGroupGather sb{a.x, a.H, a.slot_of_row, a.grow0 + lo, n, 0, a.k, a.S, a.g.err};
+            LoadKS<W_TN, KRowsGroupGather> lb(sb);
+            wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
+        } else {
+            KRowsGroup sb{a.x, a.H, a.xrow0 + lo, n, 0};
+            LoadKS<W_TN, KRowsGroup> lb(sb);
+            wgrad_tiles(la, lb, nk, ntiles, ng, nng, smem, epi);
+        }
+    });
 }
 
 // ---------------------------------------------------------------- deep groups
@@ -958,8 +1005,10 @@ int launch_wgrad_down(const WgradDownArgs& a, hipStream_t st) {
         k_wgrad_down_deep<<<D_GRID, 256, 0, st>>>(a);
         if (hipGetLastError() != hipSuccess) return -1;
     }
-    const int grid = (a.g.offsets ? a.g.E : 1) * (a.H / W_TM) * wgrad_groups(a.I / W_TN);
-    k_wgrad_down<<<grid, 256, 0, st>>>(a);
+    if (a.g.offsets && a.g.E > 1024) return -1;               // the block list's bound
+    const int grid = slab_grid(a.g, a.out, a.H / W_TM, wgrad_groups(a.I / W_TN));
+    if (slab_listed(a.g, a.out)) k_wgrad_down<true><<<grid, 256, 0, st>>>(a);
+    else k_wgrad_down<false><<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
@@ -975,8 +1024,10 @@ int launch_wgrad_gate_up(const WgradGateUpArgs& a, hipStream_t st) {
         k_wgrad_gate_up_deep<<<D_GRID, 256, 0, st>>>(a);
         if (hipGetLastError() != hipSuccess) return -1;
     }
-    const int grid = (a.g.offsets ? a.g.E : 1) * (2 * a.I / W_TM) * wgrad_groups(a.H / W_TN);
-    k_wgrad_gate_up<<<grid, 256, 0, st>>>(a);
+    if (a.g.offsets && a.g.E > 1024) return -1;               // the block list's bound
+    const int grid = slab_grid(a.g, a.out_gate, 2 * a.I / W_TM, wgrad_groups(a.H / W_TN));
+    if (slab_listed(a.g, a.out_gate)) k_wgrad_gate_up<true><<<grid, 256, 0, st>>>(a);
+    else k_wgrad_gate_up<false><<<grid, 256, 0, st>>>(a);
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 

@@ -963,6 +963,32 @@ __device__ __forceinline__ bool map_mtile_big(const GroupRows& g, int nNt, int b
 }
 
 // K-grouped: block b -> (expert, M tile, N tile) and the expert's rows.
+// The experts for which pred(e) holds, ascending, into LDS (list[0 .. count));
+// a 256-thread block.  The slab weight-gradient kernels of a macrobatch walk
+// build it once per block and run a persistent grid over its items: most
+// experts of a skewed stream have no rows in a macrobatch, and a block per
+// (expert, slab, column group) of all E experts cost ~0.5 ms per launch in
+// dispatching blocks that had nothing to do.
+template <class Pred>
+__device__ __forceinline__ int block_list(int E, const Pred& pred, int16_t* list) {
+    __shared__ int wc[4];
+    const int lane = lane_id(), wv = threadIdx.x >> 6;
+    int base = 0;
+    for (int j = 0; j < E; j += 256) {
+        const int e = j + threadIdx.x;
+        const bool f = e < E && pred(e);
+        const uint64_t m = __ballot(f);
+        if (lane == 0) wc[wv] = __popcll(m);
+        __syncthreads();
+        int pre = base;
+        for (int w = 0; w < wv; ++w) pre += wc[w];
+        if (f) list[pre + __popcll(m & lanemask_lt())] = (int16_t)e;
+        base += wc[0] + wc[1] + wc[2] + wc[3];
+        __syncthreads();
+    }
+    return base;
+}
+
 __device__ __forceinline__ bool map_ktile(const GroupRows& g, int nMt, int nNt, int b, int& e, int& mt,
                                           int& nt, int& lo, int& n) {
     const int per = nMt * nNt;

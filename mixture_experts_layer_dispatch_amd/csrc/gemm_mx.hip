@@ -1120,54 +1120,76 @@ __device__ __forceinline__ void wgrad_mx_tiles(LoadKCPad<X_TM>& la, LoadScalesPa
 
 // STREAM: the slabs' column tiles are dealt over several blocks (streaming
 // bf16 stores); a template parameter of the kernel, so that each kernel holds
-// two instantiations of the tile walk.
-template <bool STREAM>
-__global__ __launch_bounds__(256, 4) void k_wgrad_mx(WgradMXArgs a) {
+// two instantiations of the tile walk.  LISTED: the persistent grid of a walk
+// over several macrobatches (three blocks per CU) instead of a block per item.
+template <bool STREAM, bool LISTED>
+__global__ __launch_bounds__(256, LISTED ? 3 : 4) void k_wgrad_mx(WgradMXArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[X_SMEM];
     const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
     const int nMt = a.M / X_TM;
     const int per = nMt * nng;
-    const int total = (a.g.blk_off ? a.g.E : 1) * per;
-    const int b = blockIdx.x;
-    if (b >= total) return;
-    const int L = xcd_remap(b, total);
-    const int e = L / per;
-    const int mt = (L - e * per) / nng;
-    const int ng = L - e * per - mt * nng;
-    // the group's operands are contiguous [rows][kcodes] blocks (group-major)
-    int64_t blk0 = 0;
-    int kcodes = 0, rows = 0;
-    if (a.g.blk_off) {
-        const int lo = a.g.off[e], hi = a.g.off[e + 1];
-        if (lo >= 0 && hi >= lo && hi <= a.g.rows) {
-            blk0 = a.g.blk_off[e];
-            kcodes = 32 * (a.g.blk_off[e + 1] - a.g.blk_off[e]);
-            rows = hi - lo;
+    const int64_t mat = (int64_t)(a.msplit == a.M ? a.M : a.msplit) * a.N;   // elements per expert
+    // one (expert, slab, column group) item; the group's operands are
+    // contiguous [rows][kcodes] blocks (group-major)
+    auto item_fn = [&](int e, int mt, int ng) {
+        int64_t blk0 = 0;
+        int kcodes = 0, rows = 0;
+        if (a.g.blk_off) {
+            const int lo = a.g.off[e], hi = a.g.off[e + 1];
+            if (lo >= 0 && hi >= lo && hi <= a.g.rows) {
+                blk0 = a.g.blk_off[e];
+                kcodes = 32 * (a.g.blk_off[e + 1] - a.g.blk_off[e]);
+                rows = hi - lo;
+            }
+        } else {
+            kcodes = 32 * ((a.g.dense_rows + 31) / 32);
+        }
+        if (a.g.deep_thr > 0 && kcodes > a.g.deep_thr) return;     // the deep kernel's group
+        const int nk = (kcodes + 127) / 128;
+        const int m0 = mt * X_TM;
+        const bool hi_part = m0 >= a.msplit;
+        WgradOut o = hi_part ? a.out_hi : a.out_lo;
+        if (wgrad_bind(o, e, rows, mat) < 0) return;               // nothing to add for this expert
+        WgradEpi epi{o, (int64_t)e * mat, a.N, hi_part ? m0 - a.msplit : m0};
+        const uint8_t* aq = a.at_q + 32 * blk0 * a.M;
+        const uint8_t* as_ = a.at_s + blk0 * a.M;
+        const uint8_t* bq = a.bt_q + 32 * blk0 * a.N;
+        const uint8_t* bs = a.bt_s + blk0 * a.N;
+        RowsPadK ra{aq, kcodes, m0, 0};
+        LoadKCPad<X_TM> la(ra, kcodes);
+        LoadScalesPad<X_TM> sa(as_, kcodes / 32, m0, 0, kcodes / 32);
+        const int nt0 = ng, ntn = wgrad_group_tiles(ntiles, nng, ng);
+        RowsPadK rb{bq, kcodes, nt0 * X_TN, 0};
+        LoadKCPad<X_TN> lb(rb, kcodes);
+        LoadScalesPad<X_TN> sb(bs, kcodes / 32, nt0 * X_TN, 0, kcodes / 32);
+        if (epi.out.mode == 0) wgrad_mx_tiles<true, STREAM>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
+        else wgrad_mx_tiles<false, false>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
+    };
+    if constexpr (LISTED) {
+        // a walk over several macrobatches: a persistent grid over the items
+        // of the experts with work (block_list; most experts of a skewed
+        // stream have no rows in a macrobatch)
+        __shared__ int16_t list[1024];
+        const int total = per * block_list(a.g.E, [&](int e) {
+            const int lo = a.g.off[e], hi = a.g.off[e + 1];
+            if (lo < 0 || hi < lo || hi > a.g.rows) return false;
+            const int kcodes = 32 * (a.g.blk_off[e + 1] - a.g.blk_off[e]);
+            return (a.g.deep_thr <= 0 || kcodes <= a.g.deep_thr) && wgrad_mode(a.out_lo, e, hi - lo) >= 0;
+        }, list);
+        for (int r = 0;; ++r) {
+            const int item = r * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+            if (item >= total) break;
+            if (r) __syncthreads();             // the previous item's staged tile has been read
+            const int d = item / per, rem = item - d * per;
+            item_fn(list[d], rem / nng, rem % nng);
         }
     } else {
-        kcodes = 32 * ((a.g.dense_rows + 31) / 32);
+        const int total = (a.g.blk_off ? a.g.E : 1) * per;
+        if ((int)blockIdx.x >= total) return;
+        const int L = xcd_remap(blockIdx.x, total);
+        const int e = L / per, rem = L - e * per;
+        item_fn(e, rem / nng, rem % nng);
     }
-    if (a.g.deep_thr > 0 && kcodes > a.g.deep_thr) return;     // the deep kernel's group
-    const int nk = (kcodes + 127) / 128;
-    const int m0 = mt * X_TM;
-    const bool hi_part = m0 >= a.msplit;
-    WgradOut o = hi_part ? a.out_hi : a.out_lo;
-    const int64_t mat = (int64_t)(a.msplit == a.M ? a.M : a.msplit) * a.N;   // elements per expert
-    if (wgrad_bind(o, e, rows, mat) < 0) return;               // nothing to add for this expert
-    WgradEpi epi{o, (int64_t)e * mat, a.N, hi_part ? m0 - a.msplit : m0};
-    const uint8_t* aq = a.at_q + 32 * blk0 * a.M;
-    const uint8_t* as_ = a.at_s + blk0 * a.M;
-    const uint8_t* bq = a.bt_q + 32 * blk0 * a.N;
-    const uint8_t* bs = a.bt_s + blk0 * a.N;
-    RowsPadK ra{aq, kcodes, m0, 0};
-    LoadKCPad<X_TM> la(ra, kcodes);
-    LoadScalesPad<X_TM> sa(as_, kcodes / 32, m0, 0, kcodes / 32);
-    const int nt0 = ng, ntn = wgrad_group_tiles(ntiles, nng, ng);
-    RowsPadK rb{bq, kcodes, nt0 * X_TN, 0};
-    LoadKCPad<X_TN> lb(rb, kcodes);
-    LoadScalesPad<X_TN> sb(bs, kcodes / 32, nt0 * X_TN, 0, kcodes / 32);
-    if (epi.out.mode == 0) wgrad_mx_tiles<true, STREAM>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
-    else wgrad_mx_tiles<false, false>(la, sa, lb, sb, nk, nt0, ntn, nng, smem, epi);
 }
 
 // ---------------------------------------------------------------- deep groups
@@ -1299,10 +1321,18 @@ int launch_wgrad_mx(const WgradMXArgs& a, hipStream_t st) {
         if (hipGetLastError() != hipSuccess) return -1;
     }
     const int ntiles = a.N / X_TN, nng = wgrad_groups(ntiles);
-    const int grid = (a.g.blk_off ? a.g.E : 1) * (a.M / X_TM) * nng;
+    const bool listed = a.g.blk_off && a.out_lo.counts;        // persistent grid (k_wgrad_mx)
+    if (listed && a.g.E > 1024) return -1;                      // the block list's bound
+    const int all = (a.g.blk_off ? a.g.E : 1) * (a.M / X_TM) * nng;
+    const int grid = listed ? std::min(all, 3 * 256) : all;
     if (grid <= 0) return 0;
-    if (nng > 1) k_wgrad_mx<true><<<grid, 256, 0, st>>>(a);
-    else k_wgrad_mx<false><<<grid, 256, 0, st>>>(a);
+    if (nng > 1) {
+        if (listed) k_wgrad_mx<true, true><<<grid, 256, 0, st>>>(a);
+        else k_wgrad_mx<true, false><<<grid, 256, 0, st>>>(a);
+    } else {
+        if (listed) k_wgrad_mx<false, true><<<grid, 256, 0, st>>>(a);
+        else k_wgrad_mx<false, false><<<grid, 256, 0, st>>>(a);
+    }
     return hipGetLastError() == hipSuccess ? 0 : -1;
 }
 
