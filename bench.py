@@ -130,15 +130,16 @@ def kernel_bytes(shape, counts: np.ndarray) -> dict:
         # MXFP8 leg (x quantised once per token by mx_quant_rows, gathered on load)
         "gemm_gate_up_mx": int(w_gu / 2 * q + T * H * q + 2 * S * I * 4 + S * I * q),
         "gemm_down_mx": int(w_d / 2 * q + S * I * q + S * H * 2 + S * 8),
-        "gemm_down_dgrad_mx": int(w_d / 2 * q + T * H * q + 4 * S * I * 4 + S * I * 4
-                                  + 2 * S * I * q + S * P * 4),
+        # g, u read; dg | du quantised along I; h, dg, du quantised along the
+        # group's rows and written transposed (the weight gradients' operands)
+        "gemm_down_dgrad_mx": int(w_d / 2 * q + T * H * q + 2 * S * I * 4 + 2 * S * I * q
+                                  + 3 * S * I * q + S * P * 4),
         "gemm_gu_dgrad_mx": int(w_gu / 2 * q + 2 * S * I * q + S * H * 2),
         "wgrad_down_mx": int(E * H * I * 2 + (H + I) * S * q),
         "wgrad_gate_up_mx": int(E * 2 * I * H * 2 + (2 * I + H) * S * q),
         "mx_quant_rows": int(T * H * 2 + T * H * q),       # x (forward) and dy (backward)
         "mx_qt_wdy": int(T * H * 2 + S * H * q),
         "mx_qt_x": int(T * H * 2 + S * H * q),
-        "mx_qt_f32": int((3 * S * I * 4 + 3 * S * I * q) / 2),   # mean of its two launches
     }
 
 

@@ -42,10 +42,11 @@ struct Layout {
     size_t xq, xs;                    // MXFP8 forward: x codes / scales [T, H] (quantised once)
     // MXFP8 backward
     size_t dyq, dys;                  // dy codes / scales [T, H]
-    size_t x_dgu32, x_h32, x_dguq, x_dgus, x_dx, x_part;    // inside a ring half
+    size_t x_dguq, x_dgus, x_dx, x_part;                    // inside a ring half
     size_t tr, tr_wdy, tr_wdys, tr_h, tr_hs, tr_dgu, tr_dgus, tr_x, tr_xs, blk_off;
+    size_t tr_sh, tr_shs, tr_sdgu, tr_sdgus;               // the shared expert's h, dg | du
     int64_t kcap;
-    size_t s_dgu32, s_h32, s_dguq, s_dgus, s_dxm;          // shared expert
+    size_t s_dguq, s_dgus, s_dxm;                          // shared expert
     size_t wacc_g, wacc_u, wacc_d, wacc_sg, wacc_su, wacc_sd;
     size_t acc_slot;                  // int32 [E]: each routed expert's accumulator slot
     size_t rc_g, rc_u, rc_sg, rc_su;  // recompute mode: one macrobatch's g, u (and the shared expert's)
@@ -127,9 +128,7 @@ Layout make_layout(const Geom& g) {
     const size_t bwd_end = align_up(L.b_part + Sm * g.P * 4, 256);
     L.ring_half = fwd_end > bwd_end ? fwd_end : bwd_end;
     if (g.mx) {
-        L.x_dgu32 = 0;
-        L.x_h32 = align_up(Sm * 2 * I * 4, 256);
-        L.x_dguq = align_up(L.x_h32 + Sm * I * 4, 256);
+        L.x_dguq = 0;
         L.x_dgus = align_up(L.x_dguq + Sm * 2 * I, 256);
         L.x_dx = align_up(L.x_dgus + Sm * 2 * I / 32, 256);
         L.x_part = align_up(L.x_dx + Sm * H * 2, 256);
@@ -169,15 +168,20 @@ Layout make_layout(const Geom& g) {
         L.s_dx = align_up(L.s_hw + M * I * 2, 256);
         size_t be = align_up(L.s_dx + M * H * 2, 256);
         if (g.mx) {
-            L.s_dgu32 = 0;
-            L.s_h32 = align_up(M * 2 * I * 4, 256);
-            L.s_dguq = align_up(L.s_h32 + M * I * 4, 256);
+            L.s_dguq = 0;
             L.s_dgus = align_up(L.s_dguq + M * 2 * I, 256);
             L.s_dxm = align_up(L.s_dgus + M * 2 * I / 32, 256);
             const size_t me = align_up(L.s_dxm + M * H * 2, 256);
             if (me > be) be = me;
         }
         L.sh = take(fe > be ? fe : be);
+        if (g.mx) {                  // its transposed h and dg | du (one dense group of M rows)
+            const size_t kcs = align_up(M, 128);
+            L.tr_sh = take(I * kcs);
+            L.tr_shs = take(I * kcs / 32 + 16);
+            L.tr_sdgu = take(2 * I * kcs);
+            L.tr_sdgus = take(2 * I * kcs / 32 + 16);
+        }
     }
     L.dl16 = take((size_t)g.T * router_padded_experts(g.E) * 2);
     if (g.recompute) {
@@ -422,14 +426,15 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
     int32_t* blk = (int32_t*)(ws + L.blk_off);
     // counts: the schedule's [n_macro, E] counts for routed groups over several
     // macrobatches (per-expert modes), nullptr otherwise
-    auto wgrads = [&](const PadGroups& pg, int mode, const int32_t* counts, int m, uint16_t* dwd,
+    auto wgrads = [&](const PadGroups& pg, const uint8_t* ah, const uint8_t* ahs, const uint8_t* adgu,
+                      const uint8_t* adgus, int mode, const int32_t* counts, int m, uint16_t* dwd,
                       float* accd, uint16_t* dwg, float* accg, uint16_t* dwu, float* accu) -> bool {
         const int32_t* sl = counts ? P.acc_slot() : nullptr;
-        WgradMXArgs d{pg, twdy, twdys, th, ths, g.H, g.I, g.H,
+        WgradMXArgs d{pg, twdy, twdys, ah, ahs, g.H, g.I, g.H,
                       {dwd, accd, mode, counts, m, g.n_macro, g.E, sl},
                       {dwd, accd, mode, counts, m, g.n_macro, g.E, sl}};
         if (launch_wgrad_mx(d, st)) return false;
-        WgradMXArgs gu{pg, tdgu, tdgus, tx, txs, 2 * g.I, g.H, g.I,
+        WgradMXArgs gu{pg, adgu, adgus, tx, txs, 2 * g.I, g.H, g.I,
                        {dwg, accg, mode, counts, m, g.n_macro, g.E, sl},
                        {dwu, accu, mode, counts, m, g.n_macro, g.E, sl}};
         return launch_wgrad_mx(gu, st) == 0;
@@ -439,8 +444,6 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         int mode = 0;
         if (g.n_macro > 1) mode = (m == g.n_macro - 1) ? 1 : (m == 0 ? 3 : 2);
         char* half = P.half(m, g.halves);
-        float* dgu32 = (float*)(half + L.x_dgu32);
-        float* h32 = (float*)(half + L.x_h32);
         uint8_t* dguq = (uint8_t*)(half + L.x_dguq);
         uint8_t* dgus = (uint8_t*)(half + L.x_dgus);
         uint16_t* dxd = (uint16_t*)(half + L.x_dx);
@@ -464,7 +467,8 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         GemmDownDgradMXArgs b1{grp, dyq, dys, 1, 0, sched->slot_of_row, grow0, g.k, g.S,
                                sched->topk_w, (const uint8_t*)wq->w_down_tq,
                                (const uint8_t*)wq->w_down_ts, g.H, g.I, (const float*)gu.g,
-                               (const float*)gu.u, gu.row0, dgu32, h32, dguq, dgus, part, g.P};
+                               (const float*)gu.u, gu.row0, blk, th, ths, tdgu, tdgus, dguq, dgus,
+                               part, g.P};
         if (launch_gemm_down_dgrad_mx(b1, st)) return MOE_ERR_HIP;
         GemmGuDgradMXArgs b2{grp, dguq, dgus, (const uint8_t*)wq->w_gate_tq,
                              (const uint8_t*)wq->w_gate_ts, (const uint8_t*)wq->w_up_tq,
@@ -478,8 +482,6 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         char* sh = g.shared ? P.sh() : nullptr;
         GroupRows dense{nullptr, nullptr, 1, g.M, g.M, err, nullptr, 0, gemm_row_tile(g.M, 1)};
         if (g.shared) {
-            float* sdgu32 = (float*)(sh + L.s_dgu32);
-            float* sh32 = (float*)(sh + L.s_h32);
             uint8_t* sdguq = (uint8_t*)(sh + L.s_dguq);
             uint8_t* sdgus = (uint8_t*)(sh + L.s_dgus);
             uint16_t* sdx = (uint16_t*)(sh + L.s_dxm);
@@ -493,8 +495,10 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
             }
             GemmDownDgradMXArgs c1{dense, dyq, dys, 0, t0, nullptr, 0, g.k, g.S, nullptr,
                                    (const uint8_t*)wq->s_down_tq, (const uint8_t*)wq->s_down_ts, g.H,
-                                   g.I, (const float*)sgu.g, (const float*)sgu.u, sgu.row0, sdgu32,
-                                   sh32, sdguq, sdgus, nullptr, g.P};
+                                   g.I, (const float*)sgu.g, (const float*)sgu.u, sgu.row0, nullptr,
+                                   (uint8_t*)(ws + L.tr_sh), (uint8_t*)(ws + L.tr_shs),
+                                   (uint8_t*)(ws + L.tr_sdgu), (uint8_t*)(ws + L.tr_sdgus), sdguq, sdgus,
+                                   nullptr, g.P};
             if (launch_gemm_down_dgrad_mx(c1, st)) return MOE_ERR_HIP;
             GemmGuDgradMXArgs c2{dense, sdguq, sdgus, (const uint8_t*)wq->s_gate_tq,
                                  (const uint8_t*)wq->s_gate_ts, (const uint8_t*)wq->s_up_tq,
@@ -511,33 +515,25 @@ moe_status backward_mx(const Geom& g, const Layout& L, const Ptrs& P, const moe_
         int32_t* deep = (int32_t*)(ws + L.deep);
         if (launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows_mx(), deep, st)) return MOE_ERR_HIP;
         PadGroups pg{off, blk, g.E, g.Sm, 0, err, deep, wgrad_deep_rows_mx()};
+        // (h and dg | du were quantised and transposed by the down input gradient)
         QtSrc qwdy{0, dyb, nullptr, g.H, sched->slot_of_row, sched->topk_w, grow0, 0, g.k, g.S};
-        QtSrc qh{1, nullptr, h32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
-        QtSrc qdgu{1, nullptr, dgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
         QtSrc qx{2, xb, nullptr, g.H, sched->slot_of_row, nullptr, grow0, 0, g.k, g.S};
         if (launch_mx_quant_group_t(pg, qwdy, g.H, twdy, twdys, st) ||
-            launch_mx_quant_group_t(pg, qh, g.I, th, ths, st) ||
-            launch_mx_quant_group_t(pg, qdgu, 2 * g.I, tdgu, tdgus, st) ||
             launch_mx_quant_group_t(pg, qx, g.H, tx, txs, st))
             return MOE_ERR_HIP;
         const int32_t* cnts = g.n_macro > 1 ? sched->counts : nullptr;
-        if (!wgrads(pg, mode, cnts, m, (uint16_t*)gr->d_w_down, P.wacc(L.wacc_d),
+        if (!wgrads(pg, th, ths, tdgu, tdgus, mode, cnts, m, (uint16_t*)gr->d_w_down, P.wacc(L.wacc_d),
                     (uint16_t*)gr->d_w_gate, P.wacc(L.wacc_g), (uint16_t*)gr->d_w_up, P.wacc(L.wacc_u)))
             return MOE_ERR_HIP;
         if (g.shared) {
-            float* sdgu32 = (float*)(sh + L.s_dgu32);
-            float* sh32 = (float*)(sh + L.s_h32);
             PadGroups pd{nullptr, nullptr, 1, g.M, g.M, err, nullptr, wgrad_deep_rows_mx()};
             QtSrc sdy{3, dyb, nullptr, g.H, nullptr, nullptr, 0, t0, g.k, g.S};
-            QtSrc shh{1, nullptr, sh32, g.I, nullptr, nullptr, 0, 0, g.k, g.S};
-            QtSrc sdg{1, nullptr, sdgu32, 2 * g.I, nullptr, nullptr, 0, 0, g.k, g.S};
             QtSrc sxx{3, xb, nullptr, g.H, nullptr, nullptr, 0, t0, g.k, g.S};
             if (launch_mx_quant_group_t(pd, sdy, g.H, twdy, twdys, st) ||
-                launch_mx_quant_group_t(pd, shh, g.I, th, ths, st) ||
-                launch_mx_quant_group_t(pd, sdg, 2 * g.I, tdgu, tdgus, st) ||
                 launch_mx_quant_group_t(pd, sxx, g.H, tx, txs, st))
                 return MOE_ERR_HIP;
-            if (!wgrads(pd, mode, nullptr, m, (uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd),
+            if (!wgrads(pd, (uint8_t*)(ws + L.tr_sh), (uint8_t*)(ws + L.tr_shs), (uint8_t*)(ws + L.tr_sdgu),
+                        (uint8_t*)(ws + L.tr_sdgus), mode, nullptr, m, (uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd),
                         (uint16_t*)gr->d_s_gate, P.wacc(L.wacc_sg), (uint16_t*)gr->d_s_up,
                         P.wacc(L.wacc_su)))
                 return MOE_ERR_HIP;

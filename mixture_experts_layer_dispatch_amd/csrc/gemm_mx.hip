@@ -820,73 +820,150 @@ __global__ __launch_bounds__(256, 2) void k_gemm_down_dgrad_mx(GemmDownDgradMXAr
     AccPos<TM, M3_TN> pos;
     const int lane = lane_id();
     const int wv = threadIdx.x >> 6, wm = wv & 1, wn = wv >> 1;
-    float dot[TM / 32];
+    float dot[TM / 32], wr[TM / 32];
 #pragma unroll
-    for (int mb = 0; mb < TM / 32; ++mb) dot[mb] = 0.f;
+    for (int mb = 0; mb < TM / 32; ++mb) {
+        dot[mb] = 0.f;
+        wr[mb] = 1.0f;
+        const int rl = lo + pos.m(mb);
+        if (rl < hi && a.topk_w) {
+            const int s = a.slot_of_row[a.grow0 + rl];
+            wr[mb] = (unsigned)s < (unsigned)a.S ? a.topk_w[s] : 0.f;
+        }
+    }
+    // The weight gradients' operands h, dg, du are quantised here along the
+    // rows of the group (32-row blocks; a tile's rows start on a block of
+    // its group) and written transposed, group by group, as
+    // launch_mx_quant_group_t lays them out: each quantity in turn is staged
+    // in LDS as fp32 (rows past the group as zeros), then each thread takes
+    // one column of one 32-row block.
+    int gs = 0, np = 32 * ((a.g.dense_rows + 31) / 32);
+    int64_t gb = 0;                                  // the group's first 32-row block
+    if (a.blk_off) {
+        gs = a.g.offsets[e];
+        gb = a.blk_off[e];
+        np = 32 * (a.blk_off[e + 1] - a.blk_off[e]);
+    }
+    const int lr0 = lo - gs;                         // the tile's first row in its group
+    constexpr int FP = M3_TN + 4;                    // 16 rows of 16 bytes hit 16 bank groups
+    static_assert(TM * FP * 4 <= 2 * SmemMX<TM, M3_TN>::STAGE * 2, "the fp32 tile fits the operand stages");
+    float* fst = (float*)smem;
+    // quantise R staged rows (tile rows rb0 .. rb0 + R - 1) of columns c0 ..
+    // c0 + 127 of a matrix of C columns
+    auto colquant = [&](const float* src, int R, int rb0, uint8_t* codes, uint8_t* scales, int C, int c0) {
+#pragma unroll 1
+        for (int u = threadIdx.x; u < M3_TN * (R / 32); u += 256) {
+            const int cl = u % M3_TN, b = u / M3_TN;
+            const int lr = lr0 + rb0 + 32 * b;       // the block's first row in its group
+            if (lr >= np) continue;                  // past the group's padded rows
+            const float* col = src + 32 * b * FP + cl;
+            float amax = 0.f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(col[j * FP]));
+            const int sx = mx_scale_exp(amax);
+            const int c = c0 + cl;
+            uint8_t* q = codes + 32 * gb * C + (int64_t)c * np + lr;
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {             // 16 rows at a time (registers)
+                float v[16];
+#pragma unroll
+                for (int j = 0; j < 16; ++j) v[j] = col[(16 * hb + j) * FP];
+                *(uint4*)(q + 16 * hb) = make_uint4(e4m3_pack4(v, sx), e4m3_pack4(v + 4, sx),
+                                                    e4m3_pack4(v + 8, sx), e4m3_pack4(v + 12, sx));
+            }
+            scales[gb * C + (int64_t)c * (np / 32) + lr / 32] = (uint8_t)(sx + 127);
+        }
+    };
+    auto load_gu = [&](int rl, int i, float (&gq)[4], float (&uq)[4]) {
+        float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f), u4 = g4;
+        if (rl < hi) {
+            const int64_t srow = (int64_t)(a.save_row0 + rl) * I + i;
+            g4 = *(const float4*)(a.g_saved + srow);
+            u4 = *(const float4*)(a.u_saved + srow);
+        }
+        gq[0] = g4.x; gq[1] = g4.y; gq[2] = g4.z; gq[3] = g4.w;
+        uq[0] = u4.x; uq[1] = u4.y; uq[2] = u4.z; uq[3] = u4.w;
+    };
+    // h (and the router-weight gradient's per-row dots): the whole tile
 #pragma unroll
     for (int mb = 0; mb < TM / 32; ++mb) {
         const int rl = lo + pos.m(mb);
-        const bool ok = rl < hi;
-        float wr = 1.0f;
-        if (ok && a.topk_w) {
-            const int s = a.slot_of_row[a.grow0 + rl];
-            wr = (unsigned)s < (unsigned)a.S ? a.topk_w[s] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            float gq[4], uq[4], hv[4];
+            load_gu(rl, n0 + pos.n(nb), gq, uq);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                hv[r] = swiglu_h(gq[r], uq[r]);
+                dot[mb] += acc[mb][nb][r] * hv[r];
+            }
+            *(f32x4*)(fst + pos.m(mb) * FP + pos.n(nb)) = f32x4{hv[0], hv[1], hv[2], hv[3]};
         }
+    }
+    __syncthreads();
+    colquant(fst, TM, 0, a.th, a.ths, I, n0);
+    // dg and du, the rows of one wave row (TM / 2 rows) at a time (both then
+    // fit the LDS); each is also quantised along I for the gate/up input
+    // gradient (a 32-column block is 4 lanes x 2 accumulators of one row)
+    float* fdg = fst;
+    float* fdu = fst + (TM / 2) * FP;
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {          // two 32-column blocks of the wave
-            float dgv[8], duv[8];
-            float mg = 0.f, mu = 0.f;
+    for (int half = 0; half < 2; ++half) {
+        __syncthreads();                             // the staging area has been read
+        if (wm == half) {
 #pragma unroll
-            for (int nbb = 0; nbb < 2; ++nbb) {
-                const int nb = 2 * blk + nbb;
-                const int i = n0 + pos.n(nb);
-                float4 g4 = make_float4(0.f, 0.f, 0.f, 0.f), u4 = g4;
-                if (ok) {
-                    const int64_t srow = (int64_t)(a.save_row0 + rl) * I + i;
-                    g4 = *(const float4*)(a.g_saved + srow);
-                    u4 = *(const float4*)(a.u_saved + srow);
-                }
-                const float gq[4] = {g4.x, g4.y, g4.z, g4.w};
-                const float uq[4] = {u4.x, u4.y, u4.z, u4.w};
-                float hv[4];
+            for (int mb = 0; mb < TM / 32; ++mb) {
+                const int rl = lo + pos.m(mb);
+                const int rs = pos.m(mb) - half * (TM / 2);      // row in the staging area
+                const bool ok = rl < hi;
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float av = acc[mb][nb][r];
-                    hv[r] = swiglu_h(gq[r], uq[r]);
-                    dot[mb] += av * hv[r];
-                    const float dh = wr * av;
-                    const float sg = sigmoidf_(gq[r]);
-                    duv[4 * nbb + r] = dh * (gq[r] * sg);
-                    dgv[4 * nbb + r] = dh * uq[r] * sg * (1.0f + gq[r] * (1.0f - sg));
-                    mg = fmaxf(mg, fabsf(dgv[4 * nbb + r]));
-                    mu = fmaxf(mu, fabsf(duv[4 * nbb + r]));
-                }
-                if (ok) {
-                    *(float4*)(a.h32 + (int64_t)rl * I + i) = make_float4(hv[0], hv[1], hv[2], hv[3]);
-                    float* drow = a.dgu32 + (int64_t)rl * (2 * I);
-                    *(float4*)(drow + i) = make_float4(dgv[4 * nbb], dgv[4 * nbb + 1], dgv[4 * nbb + 2], dgv[4 * nbb + 3]);
-                    *(float4*)(drow + I + i) = make_float4(duv[4 * nbb], duv[4 * nbb + 1], duv[4 * nbb + 2], duv[4 * nbb + 3]);
+                for (int blk = 0; blk < 2; ++blk) {          // two 32-column blocks of the wave
+                    float dgv[8], duv[8];
+                    float mg = 0.f, mu = 0.f;
+#pragma unroll
+                    for (int nbb = 0; nbb < 2; ++nbb) {
+                        const int nb = 2 * blk + nbb;
+                        float gq[4], uq[4];
+                        load_gu(rl, n0 + pos.n(nb), gq, uq);
+#pragma unroll
+                        for (int r = 0; r < 4; ++r) {
+                            const float dh = wr[mb] * acc[mb][nb][r];
+                            const float sg = sigmoidf_(gq[r]);
+                            duv[4 * nbb + r] = dh * (gq[r] * sg);
+                            dgv[4 * nbb + r] = dh * uq[r] * sg * (1.0f + gq[r] * (1.0f - sg));
+                            mg = fmaxf(mg, fabsf(dgv[4 * nbb + r]));
+                            mu = fmaxf(mu, fabsf(duv[4 * nbb + r]));
+                        }
+                        const float z = ok ? 1.f : 0.f;        // rows past the group stage as zeros
+                        *(f32x4*)(fdg + rs * FP + pos.n(nb)) =
+                            f32x4{z * dgv[4 * nbb], z * dgv[4 * nbb + 1], z * dgv[4 * nbb + 2], z * dgv[4 * nbb + 3]};
+                        *(f32x4*)(fdu + rs * FP + pos.n(nb)) =
+                            f32x4{z * duv[4 * nbb], z * duv[4 * nbb + 1], z * duv[4 * nbb + 2], z * duv[4 * nbb + 3]};
+                    }
+                    mg = fmaxf(mg, __shfl_xor(mg, 16));
+                    mg = fmaxf(mg, __shfl_xor(mg, 32));
+                    mu = fmaxf(mu, __shfl_xor(mu, 16));
+                    mu = fmaxf(mu, __shfl_xor(mu, 32));
+                    const int sgx = mx_scale_exp(mg), sux = mx_scale_exp(mu);
+                    if (ok) {
+                        const int ib = n0 + wn * 64 + blk * 32;     // first column of the block
+                        uint8_t* qrow = a.dgu_q + (int64_t)rl * (2 * I);
+                        *(uint32_t*)(qrow + ib + 4 * (lane >> 4)) = e4m3_pack4(dgv, sgx);
+                        *(uint32_t*)(qrow + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(dgv + 4, sgx);
+                        *(uint32_t*)(qrow + I + ib + 4 * (lane >> 4)) = e4m3_pack4(duv, sux);
+                        *(uint32_t*)(qrow + I + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(duv + 4, sux);
+                        if ((lane >> 4) == 0) {
+                            uint8_t* srow = a.dgu_s + (int64_t)rl * (2 * I / 32);
+                            srow[ib / 32] = (uint8_t)(sgx + 127);
+                            srow[(I + ib) / 32] = (uint8_t)(sux + 127);
+                        }
+                    }
                 }
             }
-            mg = fmaxf(mg, __shfl_xor(mg, 16));
-            mg = fmaxf(mg, __shfl_xor(mg, 32));
-            mu = fmaxf(mu, __shfl_xor(mu, 16));
-            mu = fmaxf(mu, __shfl_xor(mu, 32));
-            const int sgx = mx_scale_exp(mg), sux = mx_scale_exp(mu);
-            if (ok) {
-                const int ib = n0 + wn * 64 + blk * 32;     // first column of the block
-                uint8_t* qrow = a.dgu_q + (int64_t)rl * (2 * I);
-                *(uint32_t*)(qrow + ib + 4 * (lane >> 4)) = e4m3_pack4(dgv, sgx);
-                *(uint32_t*)(qrow + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(dgv + 4, sgx);
-                *(uint32_t*)(qrow + I + ib + 4 * (lane >> 4)) = e4m3_pack4(duv, sux);
-                *(uint32_t*)(qrow + I + ib + 16 + 4 * (lane >> 4)) = e4m3_pack4(duv + 4, sux);
-                if ((lane >> 4) == 0) {
-                    uint8_t* srow = a.dgu_s + (int64_t)rl * (2 * I / 32);
-                    srow[ib / 32] = (uint8_t)(sgx + 127);
-                    srow[(I + ib) / 32] = (uint8_t)(sux + 127);
-                }
-            }
         }
+        __syncthreads();
+        colquant(fdg, TM / 2, half * (TM / 2), a.tdgu, a.tdgus, 2 * I, n0);
+        colquant(fdu, TM / 2, half * (TM / 2), a.tdgu, a.tdgus, 2 * I, I + n0);
     }
     if (!a.dw_part) return;
 #pragma unroll

@@ -274,8 +274,13 @@ struct GemmDownDgradMXArgs {
     const float* g_saved;     // fp32
     const float* u_saved;
     int save_row0;
-    float* dgu32;             // ring [rows, 2I] fp32 dg | du
-    float* h32;               // ring [rows, I] fp32 h
+    // h and [dg | du], quantised along the rows of each group and written
+    // transposed, group by group (launch_mx_quant_group_t's layout)
+    const int32_t* blk_off;   // [E+1] prefix of each group's 32-row blocks (null: one dense group)
+    uint8_t* th;
+    uint8_t* ths;
+    uint8_t* tdgu;
+    uint8_t* tdgus;
     uint8_t* dgu_q;           // ring [rows, 2I] codes along I
     uint8_t* dgu_s;           // ring [rows, 2I/32]
     float* dw_part;
