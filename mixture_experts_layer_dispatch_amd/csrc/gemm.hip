@@ -217,6 +217,22 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_down_big(GemmDownArgs a
     int e, lo, hi, nt;
     if (!map_mtile_big(a.g, a.H / kBig, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * kBig;
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+    // the epilogue's row look-ups (destination row, router weight) go out
+    // before the K loop, so that their round trips hide behind it
+    int64_t orow[8];
+    float wr[8];
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int rl = lo + wm0 + mb * 16 + (lane & 15);
+        orow[mb] = -1;
+        wr[mb] = 0.f;
+        if (rl < hi) {
+            orow[mb] = a.dest.row(rl, a.g.err);
+            wr[mb] = a.rw.at(rl);
+        }
+    }
     f32x4 acc[8][4];
     {
         const RowsDirect sa{a.h, a.I, lo, hi - lo};
@@ -224,40 +240,16 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_down_big(GemmDownArgs a
         const DirectKC la(sa), lb(sb);
         mainloop_big(la, lb, a.I / kTK, st0, st1, acc);
     }
-    // the tile goes out through LDS (rows 0-127 in st0, 128-255 in st1; 16-byte
-    // chunk c of row r at slot c ^ (r & 31)) so that each global store is a
-    // whole 512-byte row piece; the rows' destinations are kept in orow_s
-    __shared__ int64_t orow_s[kBig];
-    const int w = threadIdx.x >> 6, lane = lane_id();
-    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
-    uint16_t* sbuf = (w & 1) ? st1 : st0;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-        const int r = wm0 + mb * 16 + (lane & 15), rl = lo + r;
-        int64_t orow = -1;
-        float wr = 0.f;
-        if (rl < hi) {
-            orow = a.dest.row(rl, a.g.err);
-            wr = a.rw.at(rl);
-        }
-        if (lane < 16) orow_s[r] = orow;
-        const int rr = r & 127;
+        if (orow[mb] < 0) continue;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-            const int col = wn0 + nb * 16 + 4 * (lane >> 4);
+            const int col = n0 + wn0 + nb * 16 + 4 * (lane >> 4);
             const f32x4 v = acc[mb][nb];
-            *(uint2*)(sbuf + rr * kBig + 8 * ((col >> 3) ^ (rr & 31)) + (col & 7)) =
-                pack4(wr * v[0], wr * v[1], wr * v[2], wr * v[3]);
+            *(uint2*)(a.o + orow[mb] * a.H + col) =
+                pack4(wr[mb] * v[0], wr[mb] * v[1], wr[mb] * v[2], wr[mb] * v[3]);
         }
-    }
-    __syncthreads();
-#pragma unroll 4
-    for (int q = 0; q < kBig * 32 / kBigThreads; ++q) {
-        const int c = threadIdx.x + kBigThreads * q, r = c >> 5, cc = c & 31;
-        const int64_t orow = orow_s[r];
-        if (orow < 0) continue;
-        const uint16_t* sb = (r < 128 ? st0 : st1) + (r & 127) * kBig;
-        *(uint4*)(a.o + orow * a.H + n0 + 8 * cc) = *(const uint4*)(sb + 8 * (cc ^ (r & 31)));
     }
 }
 
@@ -489,6 +481,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_gu_dgrad_big(GemmGuDgra
     int e, lo, hi, nt;
     if (!map_mtile_big(a.g, a.H / kBig, blockIdx.x, e, lo, hi, nt)) return;
     const int n0 = nt * kBig;
+    const int w = threadIdx.x >> 6, lane = lane_id();
+    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
+    int64_t orow[8];                    // destination rows, looked up before the K loop
+#pragma unroll
+    for (int mb = 0; mb < 8; ++mb) {
+        const int rl = lo + wm0 + mb * 16 + (lane & 15);
+        orow[mb] = rl < hi ? a.dest.row(rl, a.g.err) : -1;
+    }
     f32x4 acc[8][4];
     {
         const RowsDirect sa{a.dgu, 2 * a.I, lo, hi - lo};
@@ -497,19 +497,14 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_gemm_gu_dgrad_big(GemmGuDgra
         const DirectKS lb(a.H);
         mainloop_big(la, lb, sb, 2 * a.I / kTK, st0, st1, acc);
     }
-    const int w = threadIdx.x >> 6, lane = lane_id();
-    const int wm0 = (w & 1) * 128, wn0 = (w >> 1) * 64;
 #pragma unroll
     for (int mb = 0; mb < 8; ++mb) {
-        const int rl = lo + wm0 + mb * 16 + (lane & 15);
-        if (rl >= hi) continue;
-        const int64_t orow = a.dest.row(rl, a.g.err);
-        if (orow < 0) continue;
+        if (orow[mb] < 0) continue;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
             const int col = n0 + wn0 + nb * 16 + 4 * (lane >> 4);
             const f32x4 v = acc[mb][nb];
-            *(uint2*)(a.dx + orow * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
+            *(uint2*)(a.dx + orow[mb] * a.H + col) = pack4(v[0], v[1], v[2], v[3]);
         }
     }
 }
