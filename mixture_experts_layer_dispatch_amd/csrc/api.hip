@@ -956,10 +956,16 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                  : launch_deep_list(off, g.E, g.Sm, wgrad_deep_rows(), deep, st))
             return MOE_ERR_HIP;
         GroupRows kgrp{off, nullptr, g.E, g.Sm, 0, err, deep, wgrad_deep_rows()};
+        // the dense group takes the 256 x 256 form only where its tiles fill
+        // the persistent grid (a 16 384-row shared expert's dW_gate | dW_up has
+        // 128 such tiles for 256 blocks, its dW_down 64; the 128 x 128 deep
+        // kernel then keeps the chip busy)
+        GroupRows dense_d = dense, dense_gu = dense;
         if (wbig) {
             kgrp.deep_big = deep_big;
             kgrp.big_thr = wgrad_big_rows();
-            dense.big_thr = wgrad_big_rows();
+            if ((g.H / kBig) * (g.I / kBig) >= wgrad_big_grid()) dense_d.big_thr = wgrad_big_rows();
+            if ((2 * g.I / kBig) * (g.H / kBig) >= wgrad_big_grid()) dense_gu.big_thr = wgrad_big_rows();
         }
         const int32_t* cnts = g.n_macro > 1 ? sched->counts : nullptr;   // per-expert modes
         const int32_t* sl = g.n_macro > 1 ? P.acc_slot() : nullptr;
@@ -971,10 +977,10 @@ moe_status moe_backward(const moe_config* cfg, const moe_sched* sched, const moe
                            {(uint16_t*)gr->d_w_up, P.wacc(L.wacc_u), mode, cnts, m, g.n_macro, g.E, sl}, zero};
         if (launch_wgrad_gate_up(b4, st)) return MOE_ERR_HIP;
         if (g.shared) {
-            WgradDownArgs c3{dense, dyb, 0, t0, nullptr, 0, g.k, g.S, shw, g.H, g.I,
+            WgradDownArgs c3{dense_d, dyb, 0, t0, nullptr, 0, g.k, g.S, shw, g.H, g.I,
                              {(uint16_t*)gr->d_s_down, P.wacc(L.wacc_sd), mode}, zero};
             if (launch_wgrad_down(c3, st)) return MOE_ERR_HIP;
-            WgradGateUpArgs c4{dense, sdgu, xb, 0, t0, nullptr, 0, g.k, g.S, g.H, g.I,
+            WgradGateUpArgs c4{dense_gu, sdgu, xb, 0, t0, nullptr, 0, g.k, g.S, g.H, g.I,
                                {(uint16_t*)gr->d_s_gate, P.wacc(L.wacc_sg), mode},
                                {(uint16_t*)gr->d_s_up, P.wacc(L.wacc_su), mode}, zero};
             if (launch_wgrad_gate_up(c4, st)) return MOE_ERR_HIP;

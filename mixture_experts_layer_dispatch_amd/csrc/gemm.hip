@@ -1051,6 +1051,7 @@ int gemm_row_tile(int rows, int E) { return (int64_t)rows >= 192LL * E ? 128 : 6
 int wgrad_deep_rows() { return kTK; }
 // bf16 weight gradients: groups of at least this many rows take the 256 x 256 tiles
 int wgrad_big_rows() { return 512; }
+int wgrad_big_grid() { return B_GRID; }
 int dgrad_col_tiles(int I) { return I / G3_TN; }
 
 }  // namespace moe

@@ -378,6 +378,8 @@ int gemm_row_tile(int rows, int E);   // M-grouped row tile for a macrobatch of 
 int dgrad_col_tiles(int I);
 int wgrad_deep_rows();        // bf16 weight gradients: groups above this go to the deep kernels
 int wgrad_big_rows();         // ... and groups of at least this many rows to the 256 x 256 kernels
+// blocks of the 256 x 256 weight-gradient kernels' persistent grid
+int wgrad_big_grid();
 int wgrad_deep_rows_mx();     // MXFP8 weight gradients: the same, in rows
 
 }  // namespace moe

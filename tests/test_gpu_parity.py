@@ -355,6 +355,32 @@ def test_forward_backward_many_big_tiles_sampled():
     assert_rerun_bitwise(case)
 
 
+def test_dense_shared_expert_big_weight_gradient_tiles():
+    """A shared expert whose weight gradients have enough 256 x 256 tiles to
+    fill their persistent grid (H = I = 4096: 256 tiles of dW_down, 512 of
+    dW_gate | dW_up) takes that form; smaller dense groups take the 128 x 128
+    tiles.  Checked in full against the oracle (about 20 s of float64 on the
+    host)."""
+    shape = si.custom_shape("dense_big_wgrad", T=512, H=4096, I=4096, E=2, k=1, seed=41, n_shared=1)
+    case = Case(shape)
+    case.schedule()
+    idx, w, sch = _check_schedule(case)
+    case.forward()
+    case.backward()
+    torch.cuda.synchronize()
+    from mixture_experts_layer_dispatch_amd import binding as B
+    assert B.moe_check_device_error(case.ws) == 0
+    x, dy = f32(case.x), f32(case.dy)
+    wgv, wuv, wdv = case.expert_view(case.wg), case.expert_view(case.wu), case.expert_view(case.wd)
+    rb = oracle.backward(x, wgv, wuv, wdv, idx, w, dy, shared=case.shared_np())
+    assert_close("dx", f32(case.dx), rb["dx"])
+    assert_close("dW_shared_gate", f32(case.grads["d_s_gate"]), rb["dW_sg"])
+    assert_close("dW_shared_up", f32(case.grads["d_s_up"]), rb["dW_su"])
+    assert_close("dW_shared_down", f32(case.grads["d_s_down"]), rb["dW_sd"])
+    for e in (0, 1):
+        assert_close(f"dW_down[{e}]", f32(case.grads["d_w_down"][e]), rb["dWd"][e])
+
+
 @pytest.mark.parametrize("precision", ["bf16", "mxfp8"])
 def test_256_row_tiles_give_the_bits_of_the_smaller_tiles(precision):
     """The same tokens as one macrobatch (groups of ~512 rows, a 1024-row shared
