@@ -839,8 +839,13 @@ __device__ __forceinline__ void big_wgrad_store(const WgradOut& out, int64_t eba
     __syncthreads();
 }
 
+// Items of round r: consecutive ones on the blocks of one XCD; odd rounds
+// deal them in reverse, so that a block that took a tile of a larger group
+// (the list ascends by expert, a skewed stream's groups mostly shrink along
+// it) takes one of a smaller group next.
 __device__ __forceinline__ int big_item(int r) {
-    return r * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+    const int l = xcd_remap(blockIdx.x, gridDim.x);
+    return r * (int)gridDim.x + ((r & 1) ? (int)gridDim.x - 1 - l : l);
 }
 
 __global__ __launch_bounds__(kBigThreads, 1) void k_wgrad_down_big(WgradDownArgs a) {
