@@ -708,11 +708,13 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_down_deep(WgradDownArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<D_TM, D_TN, true, true>::STAGE];
     const int nNt = a.I / D_TN, per = (a.H / D_TM) * nNt;
     const int total = deep_count(a.g) * per;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    for (int r = 0, item = deep_item(0); item < total; item = deep_item(++r)) {
         const int d = item / per, tile = item - d * per;
         int e, lo, n;
         deep_group(a.g, d, e, lo, n);
-        const int m0 = (tile / nNt) * D_TM, n0 = (tile % nNt) * D_TN;
+        int mt, nt;
+        band_tile(tile, per / nNt, nNt, mt, nt);
+        const int m0 = mt * D_TM, n0 = nt * D_TN;
         const int nk = (n + kTK - 1) / kTK;
         KRowsGroup sb{a.hw, a.I, lo, n, n0};
         LoadKS<D_TN, KRowsGroup> lb(sb);
@@ -736,11 +738,13 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_gate_up_deep(WgradGateUpArgs a
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * Smem<D_TM, D_TN, true, true>::STAGE];
     const int nNt = a.H / D_TN, per = (2 * a.I / D_TM) * nNt;
     const int total = deep_count(a.g) * per;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    for (int r = 0, item = deep_item(0); item < total; item = deep_item(++r)) {
         const int d = item / per, tile = item - d * per;
         int e, lo, n;
         deep_group(a.g, d, e, lo, n);
-        const int m0 = (tile / nNt) * D_TM, n0 = (tile % nNt) * D_TN;
+        int mt, nt;
+        band_tile(tile, per / nNt, nNt, mt, nt);
+        const int m0 = mt * D_TM, n0 = nt * D_TN;
         const int nk = (n + kTK - 1) / kTK;
         const bool up = m0 >= a.I;
         KRowsGroup sa{a.dgu, 2 * a.I, lo, n, m0};

@@ -905,6 +905,29 @@ __device__ __forceinline__ uint2 pack4(float a, float b, float c, float d) {
     return make_uint2(pack_bf2(a, b), pack_bf2(c, d));
 }
 
+// Item of round r of the 128 x 128 weight-gradient kernels' persistent grid:
+// a round's consecutive items, the tiles of one row strip that share its
+// operand, go to the blocks of one XCD (one L2).
+__device__ __forceinline__ int deep_item(int r) {
+    return r * (int)gridDim.x + xcd_remap(blockIdx.x, gridDim.x);
+}
+// Tile t of a group with nNt column tiles, in bands of 8 column tiles (row
+// tiles within a band, 8 columns within a row tile), so that 64 consecutive
+// items, one XCD's share of a round, are an 8 x 8 square of tiles: 8 row and
+// 8 column operand strips (row-major order gave a share of 2 x 32 tiles,
+// needing 34 strips in its L2, where the gate/up weight gradient has 32
+// column tiles).  nNt not a multiple of 8: row-major.
+__device__ __forceinline__ void band_tile(int t, int nMt, int nNt, int& mt, int& nt) {
+    if (nNt % 8 != 0) {
+        mt = t / nNt;
+        nt = t - mt * nNt;
+        return;
+    }
+    const int band = t / (8 * nMt), r = t - band * 8 * nMt;
+    mt = r >> 3;
+    nt = 8 * band + (r & 7);
+}
+
 // ================================================================ tile maps
 // M-grouped: find (expert, row range, column tile) of block b.
 template <int TM>

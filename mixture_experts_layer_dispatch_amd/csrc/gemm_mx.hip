@@ -1281,7 +1281,7 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx_deep(WgradMXArgs a) {
                   : g.blk_off ? g.deep[0] : (32 * ((g.dense_rows + 31) / 32) > g.deep_thr ? 1 : 0);
     const int nNt = a.N / XD_T, per = (a.M / XD_T) * nNt;
     const int total = cnt * per;
-    for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    for (int r = 0, item = deep_item(0); item < total; item = deep_item(++r)) {
         const int d = item / per, tile = item - d * per;
         const int e = g.blk_off ? g.deep[1 + d] : 0;
         int64_t blk0 = 0;
@@ -1290,7 +1290,9 @@ __global__ __launch_bounds__(256, 2) void k_wgrad_mx_deep(WgradMXArgs a) {
             blk0 = g.blk_off[e];
             kcodes = 32 * (g.blk_off[e + 1] - g.blk_off[e]);
         }
-        const int m0 = (tile / nNt) * XD_T, n0 = (tile % nNt) * XD_T;
+        int mt, nt;
+        band_tile(tile, per / nNt, nNt, mt, nt);
+        const int m0 = mt * XD_T, n0 = nt * XD_T;
         const uint8_t* aq = a.at_q + 32 * blk0 * a.M;
         const uint8_t* as_ = a.at_s + blk0 * a.M;
         const uint8_t* bq = a.bt_q + 32 * blk0 * a.N;
