@@ -863,7 +863,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_wgrad_down_big(WgradDownArgs
         const int d = item / per, tile = item - d * per;
         int e, lo, n;
         big_group(a.g, d, e, lo, n);
-        const int m0 = (tile / nNt) * kBig, n0 = (tile % nNt) * kBig;
+        int mt, nt;
+        band_tile(tile, per / nNt, nNt, mt, nt);
+        const int m0 = mt * kBig, n0 = nt * kBig;
         const int nk = (n + kTK - 1) / kTK;
         DirectKSRows<KRowsGroup> lb(KRowsGroup{a.hw, a.I, lo, n, n0}, a.zero);
         f32x4 acc[8][4];
@@ -892,7 +894,9 @@ __global__ __launch_bounds__(kBigThreads, 1) void k_wgrad_gate_up_big(WgradGateU
         const int d = item / per, tile = item - d * per;
         int e, lo, n;
         big_group(a.g, d, e, lo, n);
-        const int m0 = (tile / nNt) * kBig, n0 = (tile % nNt) * kBig;
+        int mt, nt;
+        band_tile(tile, per / nNt, nNt, mt, nt);
+        const int m0 = mt * kBig, n0 = nt * kBig;
         const int nk = (n + kTK - 1) / kTK;
         const bool up = m0 >= a.I;
         DirectKSRows<KRowsGroup> la(KRowsGroup{a.dgu, 2 * a.I, lo, n, m0}, a.zero);
