@@ -714,9 +714,11 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
         const bool more = kt + 1 < nk;
         const uint16_t* sA = cur;
         const uint16_t* sB = cur + SmemBig::A;
-        // row blocks outermost: four B fragments and two A fragments live at a
-        // time (B outermost, with all eight A fragments loaded first, ran the
-        // gate/up input gradient 0.343 -> 0.365 ms on the expert-parallel share)
+        // row blocks outermost: four B fragments and three A fragments live at
+        // a time, each A fragment fetched two row blocks ahead (B outermost,
+        // with all eight A fragments loaded first, ran the gate/up input
+        // gradient 0.343 -> 0.365 ms on the expert-parallel share; one row
+        // block ahead, 1-2 % slower than two)
 #pragma unroll
         for (int ks = 0; ks < kTK; ks += 32) {
             bf16x8 fa[4];
@@ -726,13 +728,12 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
                 if constexpr (BKS) return frag_kc_perm(sA, 0, wm0 + mb * 16, ks);
                 else return frag_kc(sA, 0, wm0 + mb * 16, ks);
             };
-            bf16x8 fb0 = fbm(0), fb1;
+            bf16x8 fbr[3];
+            fbr[0] = fbm(0);
+            fbr[1] = fbm(1);
 #pragma unroll
             for (int mb = 0; mb < 8; ++mb) {
-                if (mb + 1 < 8) {
-                    if (mb & 1) fb0 = fbm(mb + 1);
-                    else fb1 = fbm(mb + 1);
-                }
+                if (mb + 2 < 8) fbr[(mb + 2) % 3] = fbm(mb + 2);
                 if (more && ks == 0 && mb == 0) {       // the next step's eight copies
 #pragma unroll
                     for (int q = 0; q < 8; ++q) {
@@ -741,7 +742,7 @@ __device__ __forceinline__ void mainloop_big(const DirectKC& la, const LB& lb, c
                     }
                 }
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], (mb & 1) ? fb1 : fb0, acc[mb][nb]);
+                for (int nb = 0; nb < 4; ++nb) acc[mb][nb] = mfma_16x16x32(fa[nb], fbr[mb % 3], acc[mb][nb]);
             }
         }
         wait_copies();
